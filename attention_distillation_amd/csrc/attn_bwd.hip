@@ -1,0 +1,153 @@
+// Gradient of the distillation loss with respect to the compressed keys, gfx950.
+//
+// With G = 2 (Yhat - Y), e = lhat - l and crow_i = -G_i.Yhat_i + 2 lam e_i
+// (all produced by the forward merge), and A = exp(St - e) rebuilt from the
+// stored shifted scores:
+//     dA = G Vc^T,   dS = A * (dA + crow 1^T),   dL/dKc = scale * dS^T Q.
+// One workgroup = 4 wave64s = 64 keys (16 per wave) x one chunk of queries.
+// Each wave keeps its 16 value rows in VGPRs (B operand of dA), the query
+// tile is staged in LDS twice: G row-major (A operand of dA) and Q transposed
+// (B operand of dK).  dA comes out with query rows 4g+r and key column lq,
+// which is the A-operand layout of dK = dS^T Q, so dS never leaves VGPRs.
+// Partial dK per query chunk is written out and summed in a fixed order by
+// grad_reduce_kernel (no float atomics).
+#include "kvs_internal.h"
+
+namespace kvs {
+
+__device__ __forceinline__ f32x4 mfma_f32b(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int k = pi.k;
+  const int kt0 = blockIdx.x * 64;
+  if (kt0 >= k) return;
+  const int n = a.n, npad = (n + 3) & ~3;
+  const int nq = ((((n + a.Cn - 1) / a.Cn) + 63) / 64) * 64;
+  const int qbeg = blockIdx.z * nq;
+  const int qend = min(n, qbeg + nq);
+
+  __shared__ float Gs[64][D + 4];
+  __shared__ float Qt[D][64 + 4];
+  __shared__ float es[64], cs[64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, lq = lane & 15;
+  const int key = kt0 + wave * 16 + lq;
+  const bool kok = key < k;
+
+  float vr[D / 4];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (kok) v = *(const f32x4*)(a.V + (size_t)(pi.koff + key) * D + 16 * j + 4 * g);
+    vr[4 * j + 0] = v.x; vr[4 * j + 1] = v.y; vr[4 * j + 2] = v.z; vr[4 * j + 3] = v.w;
+  }
+  f32x4 dk[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t prow = (size_t)p * n;
+  const float* strow = a.St + pi.soff + (size_t)(kok ? key : 0) * npad;
+
+  for (int qt = qbeg; qt < qend; qt += 64) {
+    __syncthreads();
+    for (int i = tid; i < 64 * (D / 4); i += 256) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
+      const int qq = qt + r;
+      f32x4 gv = {0.f, 0.f, 0.f, 0.f}, qv = {0.f, 0.f, 0.f, 0.f};
+      if (qq < qend) {
+        gv = *(const f32x4*)(a.G + (prow + qq) * D + 4 * c4);
+        qv = *(const f32x4*)(a.Q + (prow + qq) * D + 4 * c4);
+      }
+      *(f32x4*)&Gs[r][4 * c4] = gv;
+      Qt[4 * c4 + 0][r] = qv.x;
+      Qt[4 * c4 + 1][r] = qv.y;
+      Qt[4 * c4 + 2][r] = qv.z;
+      Qt[4 * c4 + 3][r] = qv.w;
+    }
+    if (tid < 64) {
+      const int qq = qt + tid;
+      es[tid] = qq < qend ? a.e[prow + qq] : 0.f;
+      cs[tid] = qq < qend ? a.crow[prow + qq] : 0.f;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int qrow = qt + 16 * qb + 4 * g;    // first of this lane's 4 queries
+      f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+      if (kok && qrow < qend) sv = *(const f32x4*)(strow + qrow);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const f32x4 gv = *(const f32x4*)&Gs[16 * qb + lq][16 * j + 4 * g];
+        acc = mfma_f32b(gv.x, vr[4 * j + 0], acc);
+        acc = mfma_f32b(gv.y, vr[4 * j + 1], acc);
+        acc = mfma_f32b(gv.z, vr[4 * j + 2], acc);
+        acc = mfma_f32b(gv.w, vr[4 * j + 3], acc);
+      }
+      float ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int li = 16 * qb + 4 * g + r;
+        const bool ok = kok && (qt + li) < qend;
+        ds[r] = ok ? expf(sv[r] - es[li]) * (acc[r] + cs[li]) : 0.f;
+      }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const f32x4 qv = *(const f32x4*)&Qt[16 * db + lq][16 * qb + 4 * g];
+        dk[db] = mfma_f32b(ds[0], qv.x, dk[db]);
+        dk[db] = mfma_f32b(ds[1], qv.y, dk[db]);
+        dk[db] = mfma_f32b(ds[2], qv.z, dk[db]);
+        dk[db] = mfma_f32b(ds[3], qv.w, dk[db]);
+      }
+    }
+  }
+
+  // dk[db][r] = dK[key = kt0 + 16 wave + 4g + r][dim = 16 db + lq]
+  float* out = a.dKpart + (size_t)blockIdx.z * a.ktot * D;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int kr = kt0 + wave * 16 + 4 * g + r;
+    if (kr < k) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) out[(size_t)(pi.koff + kr) * D + 16 * db + lq] = dk[db][r];
+    }
+  }
+}
+
+void launch_attn_bwd(const BwdArgs& a, int d, hipStream_t s) {
+  dim3 grid((a.kmax + 63) / 64, a.P, a.Cn);
+  if (d == 128) hipLaunchKernelGGL((attn_bwd_kernel<128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((attn_bwd_kernel<64>), grid, dim3(256), 0, s, a);
+}
+
+// grad = scale * sum_c dKpart[c], c in increasing order
+__global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceArgs a, int d) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const long long nel = (long long)pi.k * d;
+  const long long base = (long long)pi.koff * d;
+  const float sc = (float)a.scale;
+  for (long long i4 = (blockIdx.x * 256LL + threadIdx.x) * 4; i4 < nel; i4 += (long long)gridDim.x * 256 * 4) {
+    f32x4 acc = *(const f32x4*)(a.dKpart + base + i4);
+    for (int c = 1; c < a.Cn; ++c) acc += *(const f32x4*)(a.dKpart + (size_t)c * a.ktot * d + base + i4);
+    *(f32x4*)(a.grad + base + i4) = acc * sc;
+  }
+}
+
+void launch_grad_reduce(const GradReduceArgs& a, int d, hipStream_t s) {
+  int kmax = 0;
+  (void)kmax;
+  dim3 grid(64, a.P);
+  hipLaunchKernelGGL(grad_reduce_kernel, grid, dim3(256), 0, s, a, d);
+}
+
+}  // namespace kvs

@@ -1,0 +1,408 @@
+// Forward attention over compressed (or compress-zone) keys, gfx950.
+//
+// One workgroup = 4 wave64s = 64 training queries of one problem and one
+// chunk of its keys.  Each wave owns 16 queries: their rows stay in VGPRs as
+// the B operand of S^T = K Q^T (16x16x4 MFMA, keys as rows), so the score
+// tile comes out with one query per lane column, which is exactly the B
+// operand layout that O^T += V^T P^T needs next.  K and V tiles (64 keys)
+// are staged in LDS; V transposed, with the key order inside each 16-key
+// block permuted to match the score layout of the MFMA variant in use.
+//
+// Scores (logits) optionally run on fp64 MFMA and are shifted by a per-row
+// value (the target log-sum-exp) before rounding to fp32: the stored
+// St = scale*q.k - shift keeps small magnitudes, so the exp() of later
+// kernels sees a well-conditioned argument.  Softmax is online (running max
+// per query, per-lane partial sums), partial O / max / sum per key chunk are
+// merged by merge_kernel.
+#include "kvs_internal.h"
+
+namespace kvs {
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// Key (row) index held in register r by lane group g of a 16x16 MFMA result.
+template <bool F64>
+__device__ __forceinline__ constexpr int out_row(int g, int r) {
+  return F64 ? (g + 4 * r) : (4 * g + r);
+}
+// LDS column of key kk (0..15) inside its 16-key block of the transposed V
+// tile, so that lane group g finds its four keys (r = 0..3) contiguous.
+template <bool F64>
+__device__ __forceinline__ int vt_col(int kk) {
+  return F64 ? ((kk & 3) * 4 + (kk >> 2)) : kk;
+}
+
+template <int D, bool STORE, bool F64>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
+  const int p = blockIdx.y, c = blockIdx.z;
+  float alpha = 0.f;
+  if (a.st) {
+    const LbState& s = a.st[p];
+    if (!((1 << s.status) & a.active_mask)) return;
+    alpha = (float)s.alpha;
+  }
+  int k, koff;
+  long long soff;
+  if (a.info) {
+    k = a.info[p].k; koff = a.info[p].koff; soff = a.info[p].soff;
+  } else {
+    k = a.kuni; koff = p * a.kuni; soff = 0;
+  }
+  const int n = a.n;
+  const int npad = (n + 3) & ~3;
+  const int chunk = (((k + a.C - 1) / a.C) + 63) & ~63;
+  const int kbeg = c * chunk;
+  const int kend = min(k, kbeg + chunk);
+
+  __shared__ float Ks[64][D + 4];
+  __shared__ float Vt[D][64 + 4];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, lq = lane & 15;
+  const int q = blockIdx.x * 64 + wave * 16 + lq;
+  const bool qok = q < n;
+  const size_t prow = (size_t)p * n;
+
+  // query rows as MFMA B operand: lane (g, lq) holds dims 16j+4g..+3 of query lq
+  float qf[D / 4];
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (qok) v = *(const f32x4*)(a.Q + (prow + q) * D + 16 * j + 4 * g);
+    qf[4 * j + 0] = v.x; qf[4 * j + 1] = v.y; qf[4 * j + 2] = v.z; qf[4 * j + 3] = v.w;
+  }
+  const double shift = (a.shift && qok) ? (double)a.shift[prow + q] : 0.0;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kt = kbeg; kt < kend; kt += 64) {
+    __syncthreads();
+    for (int i = tid; i < 64 * (D / 4); i += 256) {
+      const int row = i / (D / 4), c4 = i % (D / 4);
+      const int key = kt + row;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (key < kend) {
+        const size_t off = (size_t)(koff + key) * D + 4 * c4;
+        kv = *(const f32x4*)(a.K + off);
+        if (a.dir) {
+          const f32x4 dv = *(const f32x4*)(a.dir + off);
+          kv.x = __fmaf_rn(alpha, dv.x, kv.x);
+          kv.y = __fmaf_rn(alpha, dv.y, kv.y);
+          kv.z = __fmaf_rn(alpha, dv.z, kv.z);
+          kv.w = __fmaf_rn(alpha, dv.w, kv.w);
+        }
+        vv = *(const f32x4*)(a.V + off);
+      }
+      *(f32x4*)&Ks[row][4 * c4] = kv;
+      const int col = (row & ~15) | vt_col<F64>(row & 15);
+      Vt[4 * c4 + 0][col] = vv.x;
+      Vt[4 * c4 + 1][col] = vv.y;
+      Vt[4 * c4 + 2][col] = vv.z;
+      Vt[4 * c4 + 3][col] = vv.w;
+    }
+    __syncthreads();
+
+    float sv[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if constexpr (F64) {
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          const f32x4 kv = *(const f32x4*)&Ks[16 * b + lq][16 * j + 4 * g];
+          acc = mfma_f64((double)kv.x, (double)qf[4 * j + 0], acc);
+          acc = mfma_f64((double)kv.y, (double)qf[4 * j + 1], acc);
+          acc = mfma_f64((double)kv.z, (double)qf[4 * j + 2], acc);
+          acc = mfma_f64((double)kv.w, (double)qf[4 * j + 3], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[b][r] = (float)(acc[r] * a.scale - shift);
+      } else {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          const f32x4 kv = *(const f32x4*)&Ks[16 * b + lq][16 * j + 4 * g];
+          acc = mfma_f32(kv.x, qf[4 * j + 0], acc);
+          acc = mfma_f32(kv.y, qf[4 * j + 1], acc);
+          acc = mfma_f32(kv.z, qf[4 * j + 2], acc);
+          acc = mfma_f32(kv.w, qf[4 * j + 3], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[b][r] = (float)((double)acc[r] * a.scale - shift);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt + 16 * b + out_row<F64>(g, r);
+        if (key >= kend) {
+          sv[b][r] = -INFINITY;
+        } else if (STORE && qok) {
+          a.St[soff + (size_t)key * npad + q] = sv[b][r];
+        }
+      }
+    }
+
+    float tmax = sv[0][0];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[b][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);   // finite: the tile holds a valid key
+    const float corr = expf(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[b][r] = expf(sv[b][r] - m_new);
+        l_run += sv[b][r];
+      }
+    m_run = m_new;
+
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const f32x4 vv = *(const f32x4*)&Vt[16 * db + lq][16 * b + 4 * g];
+        oacc[db] = mfma_f32(vv.x, sv[b][0], oacc[db]);
+        oacc[db] = mfma_f32(vv.y, sv[b][1], oacc[db]);
+        oacc[db] = mfma_f32(vv.z, sv[b][2], oacc[db]);
+        oacc[db] = mfma_f32(vv.w, sv[b][3], oacc[db]);
+      }
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (qok) {
+    const size_t orow = (size_t)c * a.P * n + prow + q;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *(f32x4*)(a.Opart + orow * D + 16 * db + 4 * g) = oacc[db];
+    if (g == 0) {
+      a.Mpart[orow] = m_run;
+      a.Lpart[orow] = l_run;
+    }
+  }
+}
+
+void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s) {
+  dim3 grid((a.n + 63) / 64, a.P, a.C);
+  const bool store = a.St != nullptr;
+#define KVS_FWD(DD, SS, FF) hipLaunchKernelGGL((attn_fwd_kernel<DD, SS, FF>), grid, dim3(256), 0, s, a)
+  if (d == 128) {
+    if (store) { if (logit_f64) KVS_FWD(128, true, true); else KVS_FWD(128, true, false); }
+    else { if (logit_f64) KVS_FWD(128, false, true); else KVS_FWD(128, false, false); }
+  } else {
+    if (store) { if (logit_f64) KVS_FWD(64, true, true); else KVS_FWD(64, true, false); }
+    else { if (logit_f64) KVS_FWD(64, false, true); else KVS_FWD(64, false, false); }
+  }
+#undef KVS_FWD
+}
+
+// --------------------------------------------------------------------------
+// merge of key-chunk partials + epilogue.  16 queries per workgroup, 16
+// threads per query, each owning d/16 consecutive dims.
+//   reference mode: Y = O, lse = m + log l
+//   loss mode (scores were shifted by the target lse, so m + log l = lhat - l):
+//     R = O - Y, G = 2R, e = lhat - l, crow = -G.O + 2 lam e,
+//     per-WG partials of sum(R^2) + lam sum(e^2) and of sum(R^2).
+template <int D, bool LOSS>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  constexpr int DPT = D / 16;
+  const int tid = threadIdx.x, qi = tid >> 4, part = tid & 15;
+  const int n = a.n;
+  const int q = blockIdx.x * 16 + qi;
+  const bool ok = q < n;
+  const size_t row = (size_t)p * n + q;
+  const size_t plane = (size_t)a.P * n;
+
+  float m = -INFINITY;
+  for (int c = 0; c < a.C; ++c) m = ok ? fmaxf(m, a.Mpart[c * plane + row]) : m;
+  float l = 0.f;
+  float o[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) o[i] = 0.f;
+  if (ok) {
+    for (int c = 0; c < a.C; ++c) {
+      const float w = expf(a.Mpart[c * plane + row] - m);
+      l += w * a.Lpart[c * plane + row];
+      const float* src = a.Opart + (c * plane + row) * D + part * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4) {
+        const f32x4 v = *(const f32x4*)(src + i);
+        o[i] += w * v.x; o[i + 1] += w * v.y; o[i + 2] += w * v.z; o[i + 3] += w * v.w;
+      }
+    }
+  }
+  const float inv = ok ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) o[i] *= inv;
+  const float lse = ok ? m + logf(l) : 0.f;
+
+  if constexpr (!LOSS) {
+    if (ok) {
+      float* dst = a.Yout + row * D + part * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4) *(f32x4*)(dst + i) = f32x4{o[i], o[i + 1], o[i + 2], o[i + 3]};
+      if (part == 0) a.lse_out[row] = lse;
+    }
+  } else {
+    __shared__ double red[2][256];
+    float rr = 0.f, dl = 0.f;
+    if (ok) {
+      const float* y = a.Y + row * D + part * DPT;
+      float* gout = a.G + row * D + part * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4) {
+        const f32x4 yv = *(const f32x4*)(y + i);
+        f32x4 gv;
+        const float r0 = o[i] - yv.x, r1 = o[i + 1] - yv.y, r2 = o[i + 2] - yv.z, r3 = o[i + 3] - yv.w;
+        rr += r0 * r0 + r1 * r1 + r2 * r2 + r3 * r3;
+        gv.x = 2.f * r0; gv.y = 2.f * r1; gv.z = 2.f * r2; gv.w = 2.f * r3;
+        dl += gv.x * o[i] + gv.y * o[i + 1] + gv.z * o[i + 2] + gv.w * o[i + 3];
+        *(f32x4*)(gout + i) = gv;
+      }
+    }
+    // reduce over the 16 threads of this query (fixed xor tree)
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      rr += __shfl_xor(rr, off);
+      dl += __shfl_xor(dl, off);
+    }
+    const float e = lse;   // lhat - l
+    if (ok && part == 0) {
+      a.e[row] = e;
+      a.crow[row] = -dl + (float)(2.0 * a.lambda) * e;
+    }
+    const double lrow = ok ? (double)rr + a.lambda * (double)e * (double)e : 0.0;
+    const double orow = ok ? (double)rr : 0.0;
+    red[0][tid] = (part == 0) ? lrow : 0.0;
+    red[1][tid] = (part == 0) ? orow : 0.0;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) {
+        red[0][tid] += red[0][tid + off];
+        red[1][tid] += red[1][tid + off];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      double* dst = a.part + ((size_t)p * gridDim.x + blockIdx.x) * 2;
+      dst[0] = red[0][0];
+      dst[1] = red[1][0];
+    }
+  }
+}
+
+int merge_blocks(int n) { return (n + 15) / 16; }
+
+void launch_merge(const MergeArgs& a, int d, bool loss_mode, hipStream_t s) {
+  dim3 grid(merge_blocks(a.n), a.P);
+#define KVS_MERGE(DD, LL) hipLaunchKernelGGL((merge_kernel<DD, LL>), grid, dim3(256), 0, s, a)
+  if (d == 128) { if (loss_mode) KVS_MERGE(128, true); else KVS_MERGE(128, false); }
+  else { if (loss_mode) KVS_MERGE(64, true); else KVS_MERGE(64, false); }
+#undef KVS_MERGE
+}
+
+// --------------------------------------------------------------------------
+// per-problem loss finalisation (fixed-order double sums) and, in trial
+// mode, the Armijo test of the backtracking search.
+__global__ __launch_bounds__(64) void finalize_kernel(FinalizeArgs a) {
+  const int p = blockIdx.x;
+  LbState* st = a.st ? a.st + p : nullptr;
+  if (a.mode == 1 && st->status != ST_SEARCH) {
+    if (threadIdx.x == 0 && a.status_host_view) a.status_host_view[p] = st->status;
+    return;
+  }
+  const int t = threadIdx.x;
+  double sL = 0.0, sO = 0.0;
+  for (int i = t; i < a.nblk; i += 64) {
+    sL += a.part[((size_t)p * a.nblk + i) * 2 + 0];
+    sO += a.part[((size_t)p * a.nblk + i) * 2 + 1];
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    sL += __shfl_xor(sL, off);
+    sO += __shfl_xor(sO, off);
+  }
+  if (t != 0) return;
+  if (a.mode == 0) {
+    if (a.loss) a.loss[p] = (float)sL;
+    if (a.mse) a.mse[p] = (float)(sO / ((double)a.n * a.d));
+    if (st) {
+      st->L = sL;
+      st->st_valid = 1;
+    }
+  } else if (a.mode == 1) {
+    st->Ltrial = sL;
+    if (sL <= st->L + a.c1 * st->alpha * st->gtp) {
+      st->status = ST_ACCEPT;
+      st->L = sL;
+      st->st_valid = 1;
+    } else {
+      st->st_valid = 0;
+      st->trials += 1;
+      st->alpha *= a.shrink;
+      if (st->trials >= a.max_bt) st->status = ST_FAIL;
+    }
+    if (a.status_host_view) a.status_host_view[p] = st->status;
+  } else {
+    st->L = sL;
+    st->st_valid = 1;
+    if (a.loss) a.loss[p] = (float)sL;
+    if (a.mse) a.mse[p] = (float)(sO / ((double)a.n * a.d));
+  }
+}
+
+void launch_finalize(const FinalizeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.P), dim3(64), 0, s, a);
+}
+
+// --------------------------------------------------------------------------
+__global__ void fill_i32_kernel(int* p, int v, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void fill_f32_kernel(float* p, float v, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) p[i] = v;
+}
+void launch_fill_i32(int* p, int v, long long n, hipStream_t s) {
+  if (n <= 0) return;
+  int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
+}
+void launch_fill_f32(float* p, float v, long long n, hipStream_t s) {
+  if (n <= 0) return;
+  int blocks = (int)std::min<long long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(blocks), dim3(256), 0, s, p, v, n);
+}
+
+struct InfoChunk {
+  int first, count;
+  ProbInfo e[48];
+};
+__global__ void write_info_kernel(ProbInfo* dst, InfoChunk c) {
+  const int i = threadIdx.x;
+  if (i < c.count) dst[c.first + i] = c.e[i];
+}
+void launch_write_info(ProbInfo* dst, const ProbInfo* src, int P, hipStream_t s) {
+  for (int first = 0; first < P; first += 48) {
+    InfoChunk c;
+    c.first = first;
+    c.count = std::min(48, P - first);
+    for (int i = 0; i < c.count; ++i) c.e[i] = src[first + i];
+    hipLaunchKernelGGL(write_info_kernel, dim3(1), dim3(64), 0, s, dst, c);
+  }
+}
+
+}  // namespace kvs

@@ -1,0 +1,184 @@
+// Internal declarations shared by the HIP kernels and the host driver of the
+// KVSculpt library (gfx950 only).  Nothing here is part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHistMax = 16;            // L-BFGS pairs kept at most
+constexpr int kSlots = kHistMax + 1;    // ring slots (history + one staging slot)
+constexpr int kTile = 64;               // key/query tile edge used across kernels
+
+// Per-problem geometry, uploaded once per call into the workspace.
+struct ProbInfo {
+  int k;        // compressed pairs
+  int kpad;     // k rounded up to kTile (Gram / Cholesky edge)
+  int koff;     // first row of the problem in packed [sum k][d] arrays
+  int pad0;
+  long long soff;   // offset (floats) of the problem's stored scores [k][n]
+  long long moff;   // offset (floats) of the problem's augmented Gram [(kpad+d)][kpad]
+  long long xoff;   // offset (floats) of the problem's padded solve rows [kpad][d]
+};
+
+// L-BFGS / line-search status of one problem.
+enum : int { ST_READY = 0, ST_SEARCH = 1, ST_ACCEPT = 2, ST_FAIL = 3 };
+
+// Per-problem optimizer state, kept in device memory between kernels.
+struct LbState {
+  double L;          // loss at the current keys x
+  double Ltrial;     // loss at the last trial point
+  double gtp;        // g^T p of the current direction
+  double alpha;      // step of the current trial
+  double gg;         // g^T g
+  int status;        // ST_*
+  int trials;        // trials used in the current search
+  int flags;         // accumulated KVS_FLAG_* bits
+  int count;         // pairs in the history
+  int stage;         // ring slot receiving the next (s, y)
+  int st_valid;      // stored scores belong to x (not to a rejected trial)
+  int order[kHistMax];          // history slots, oldest first
+  double rho[kSlots];
+  double SY[kSlots][kSlots];    // s_i . y_j by slot
+  double YY[kSlots][kSlots];    // y_i . y_j by slot
+  double Sg[kSlots], Yg[kSlots];
+  double coef_g;                // direction p = coef_g g + sum cs s + sum cy y
+  double cs[kSlots], cy[kSlots];
+};
+
+// Number of dot products each WG of the history kernel emits per problem.
+constexpr int kDots = 5 * kSlots + 4;
+
+// ---- launchers (device code in the .hip files) ----------------------------
+
+struct FwdArgs {
+  const float* Q; const float* K; const float* V;
+  const float* dir;        // trial direction (NULL: keys are K itself)
+  const LbState* st;       // per-problem state (step alpha, status); NULL = all active
+  int active_mask;         // bit (1 << status) selects the problems processed
+  const float* shift;      // [P][n] per-row score shift, NULL = none
+  float* St;               // stored shifted scores (NULL = do not store)
+  float* Opart; float* Mpart; float* Lpart;
+  const ProbInfo* info;    // NULL: uniform k = kuni rows at K + p*kuni*d
+  int P, n, C, kuni, kmax;
+  double scale;
+};
+void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s);
+
+struct MergeArgs {
+  const float* Opart; const float* Mpart; const float* Lpart;
+  const LbState* st; int active_mask;
+  const float* Y; const float* lse;   // loss mode: targets; ref mode: NULL
+  float* Yout; float* lse_out;        // ref mode outputs
+  float* G; float* e; float* crow;    // loss mode outputs
+  double* part;                       // [P][nblk][2] loss / output-term partials
+  int P, n, C;
+  double lambda;
+};
+void launch_merge(const MergeArgs& a, int d, bool loss_mode, hipStream_t s);
+int merge_blocks(int n);
+
+struct FinalizeArgs {
+  const double* part; int nblk; int P;
+  LbState* st;            // NULL: plain loss_grad output
+  float* loss; float* mse;
+  int n, d;
+  int mode;               // 0 = write outputs, 1 = Armijo trial, 2 = refresh L at x
+  double c1, shrink; int max_bt;
+  int* status_host_view;  // device int[P] copy of the status (for the host)
+};
+void launch_finalize(const FinalizeArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const float* Q; const float* St; const float* G; const float* e; const float* crow;
+  const float* K; const float* V;
+  const LbState* st; int active_mask;
+  float* dKpart;           // [Cn][sum k][d]
+  const ProbInfo* info;
+  int P, n, Cn, kmax, ktot;
+};
+void launch_attn_bwd(const BwdArgs& a, int d, hipStream_t s);
+
+struct GradReduceArgs {
+  const float* dKpart; float* grad; const LbState* st; int active_mask;
+  const ProbInfo* info; int P, Cn, ktot; double scale;
+};
+void launch_grad_reduce(const GradReduceArgs& a, int d, hipStream_t s);
+
+struct GramArgs {
+  const float* St; const float* e; const float* Y;
+  const LbState* st; int active_mask;
+  float* Mpart;            // [Cg][sum M]
+  const ProbInfo* info;
+  int P, n, Cg, kpadmax; long long mtot;
+};
+void launch_gram(const GramArgs& a, int d, hipStream_t s);
+
+struct GramReduceArgs {
+  const float* Mpart; float* M; double* trpart; const LbState* st; int active_mask;
+  const ProbInfo* info; int P, Cg, kpadmax; long long mtot;
+};
+void launch_gram_reduce(const GramReduceArgs& a, int d, hipStream_t s);
+
+struct CholArgs {
+  float* M; const double* trpart; double* mu; int* info_out;
+  const LbState* st; int active_mask;
+  const ProbInfo* info; int P, kpadmax; double ridge_rel;
+};
+void launch_mu(const CholArgs& a, hipStream_t s);
+void launch_potrf_panel(const CholArgs& a, int d, int panel, hipStream_t s);
+void launch_trailing(const CholArgs& a, int d, int panel, hipStream_t s);
+
+struct BackArgs {
+  const float* M; float* X; float* Vc; const int* info_out; int* flags;
+  LbState* st; int active_mask;
+  const ProbInfo* info; int P;
+};
+void launch_back_subst(const BackArgs& a, int d, hipStream_t s);
+
+struct ImpArgs {
+  const float* Q; const float* Kz; const float* lse;
+  float* Mpart; float* Spart;   // [Cq][P][Z]
+  int P, n, Z, Cq; double scale;
+};
+void launch_importance(const ImpArgs& a, int d, hipStream_t s);
+
+struct TopkArgs {
+  const float* Mpart; const float* Spart; const float* Kz;
+  int* idx; float* Kc; const ProbInfo* info;
+  int P, Z, Cq, d;
+};
+void launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct HistArgs {
+  float* x; const float* p; float* g; const float* gnew;
+  float* S; float* Yh;          // [kSlots][sum k][d]
+  LbState* st; int active_mask;
+  double* part;                 // [P][nwg][kDots]
+  const ProbInfo* info;
+  int P, d, ktot, nwg; int mode;  // mode 0 = accept (x, s, y, g), 1 = refresh (g only)
+};
+void launch_hist_dots(const HistArgs& a, hipStream_t s);
+struct PrepArgs {
+  LbState* st; const double* part; int nwg; int P; int mode; int history; double curv_eps;
+  int select_status;     // process problems in this status
+  int* flags;
+};
+void launch_prepare(const PrepArgs& a, hipStream_t s);
+struct DirArgs {
+  float* p; const float* g; const float* S; const float* Yh; const LbState* st;
+  const ProbInfo* info; int P, d, ktot, nwg;
+};
+void launch_direction(const DirArgs& a, hipStream_t s);
+
+void launch_write_info(ProbInfo* dst, const ProbInfo* src, int P, hipStream_t s);
+void launch_fill_i32(int* p, int v, long long n, hipStream_t s);
+void launch_fill_f32(float* p, float v, long long n, hipStream_t s);
+void launch_state_init(LbState* st, int P, int clear, hipStream_t s);
+void launch_state_flags_out(const LbState* st, int* flags, float* loss, int P, hipStream_t s);
+
+}  // namespace kvs

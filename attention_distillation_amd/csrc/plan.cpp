@@ -1,0 +1,134 @@
+// Workspace layout and launch split factors for a batch of problems.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstdio>
+
+namespace kvs {
+
+namespace {
+
+constexpr int kTargetWG = 1024;   // ~4 workgroups per CU on a 256-CU part
+
+int split_for(long long base_wgs, int max_split) {
+  if (base_wgs <= 0) return 1;
+  long long c = (kTargetWG + base_wgs - 1) / base_wgs;
+  if (c < 1) c = 1;
+  if (c > max_split) c = max_split;
+  return (int)c;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
+  if (!b) return "batch is NULL";
+  if (b->P < 1) return "P must be >= 1";
+  if (b->d != 64 && b->d != 128) return "d must be 64 or 128";
+  if (b->Z < 1) return "Z must be >= 1";
+  if (b->n < 1) return "n must be >= 1";
+  if (!(b->scale > 0.0)) return "scale must be > 0";
+  if (!(b->lambda >= 0.0)) return "lambda must be >= 0";
+  if (!(b->ridge_rel >= 0.0)) return "ridge_rel must be >= 0";
+  int H = 10;
+  if (o) {
+    if (o->history < 1 || o->history > kHistMax) return "history must be in [1, 16]";
+    if (o->iters < 0) return "iters must be >= 0";
+    if (o->vc_every < 1) return "vc_every must be >= 1";
+    if (o->max_backtracks < 0) return "max_backtracks must be >= 0";
+    if (!(o->shrink > 0.0 && o->shrink < 1.0)) return "shrink must be in (0, 1)";
+    H = o->history;
+  }
+  Plan& p = *pl;
+  p = Plan();
+  p.P = b->P; p.d = b->d; p.Z = b->Z; p.n = b->n; p.npad = (b->n + 3) & ~3; p.H = H;
+  p.info.resize(p.P);
+  long long koff = 0, soff = 0, moff = 0, xoff = 0;
+  for (int i = 0; i < p.P; ++i) {
+    int k = b->k ? b->k[i] : b->Z;
+    if (k < 1 || k > b->Z) return "k[p] must be in [1, Z]";
+    ProbInfo& q = p.info[i];
+    q.k = k;
+    q.kpad = (k + kTile - 1) / kTile * kTile;
+    q.koff = (int)koff;
+    q.pad0 = 0;
+    q.soff = soff;
+    q.moff = moff;
+    q.xoff = xoff;
+    koff += k;
+    soff += (long long)k * p.npad;
+    moff += (long long)(q.kpad + p.d) * q.kpad;
+    xoff += (long long)q.kpad * p.d;
+    p.kmax = std::max(p.kmax, k);
+    p.kpadmax = std::max(p.kpadmax, q.kpad);
+  }
+  if (koff > 0x7fffffffLL) return "sum of k too large";
+  p.ktot = koff; p.stot = soff; p.mtot = moff; p.kpadtot = xoff / p.d;
+
+  const long long qtiles = (p.n + 63) / 64;
+  p.Cref = split_for((long long)p.P * qtiles, (p.Z + 63) / 64);
+  p.C = split_for((long long)p.P * qtiles, (p.kmax + 63) / 64);
+  p.Cn = split_for((long long)p.P * ((p.kmax + 63) / 64), (int)qtiles);
+  const int KT = p.kpadmax / kTile;
+  const long long gtiles = (long long)KT * (KT + 1) / 2 + (long long)(p.d / kTile) * KT;
+  p.Cg = split_for((long long)p.P * gtiles, (int)qtiles);
+  p.Cq = split_for((long long)p.P * ((p.Z + 63) / 64), (int)qtiles);
+  p.nblk = merge_blocks(p.n);
+  {
+    // L-BFGS vector kernels: ~4096 floats per workgroup per problem
+    long long per = (p.kmax * (long long)p.d + 4095) / 4096;
+    p.nwg = (int)std::max<long long>(1, std::min<long long>(per, 64));
+  }
+
+  const int Cmax = std::max(p.Cref, p.C);
+  const size_t f = 4;
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off = align256(off + bytes);
+  };
+  take(p.r_info, sizeof(ProbInfo) * p.P);
+  take(p.r_state, sizeof(LbState) * p.P);
+  take(p.r_status, sizeof(int) * p.P);
+  take(p.r_flags, sizeof(int) * p.P);
+  take(p.r_loss, sizeof(float) * p.P);
+  take(p.r_yref, f * p.P * p.n * p.d);
+  take(p.r_lseref, f * p.P * p.n);
+  take(p.r_St, f * p.stot);
+  take(p.r_Opart, f * Cmax * (size_t)p.P * p.n * p.d);
+  take(p.r_Mpart, f * Cmax * (size_t)p.P * p.n);
+  take(p.r_Lpart, f * Cmax * (size_t)p.P * p.n);
+  take(p.r_G, f * (size_t)p.P * p.n * p.d);
+  take(p.r_e, f * (size_t)p.P * p.n);
+  take(p.r_crow, f * (size_t)p.P * p.n);
+  take(p.r_part, sizeof(double) * 2 * (size_t)p.P * p.nblk);
+  take(p.r_dK, f * (size_t)p.Cn * p.ktot * p.d);
+  take(p.r_grad, f * (size_t)p.ktot * p.d);
+  take(p.r_Mg, p.Cg > 1 ? f * (size_t)p.Cg * p.mtot : 0);
+  take(p.r_M, f * (size_t)p.mtot);
+  take(p.r_tr, sizeof(double) * (size_t)p.P * KT);
+  take(p.r_mu, sizeof(double) * p.P);
+  take(p.r_cinfo, sizeof(int) * p.P);
+  take(p.r_X, f * (size_t)p.kpadtot * p.d);
+  take(p.r_imp, f * 2 * (size_t)p.Cq * p.P * p.Z);
+  take(p.r_idx, sizeof(int) * (size_t)p.ktot);
+  take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nwg * kDots);
+  take(p.r_g, f * (size_t)p.ktot * p.d);
+  take(p.r_p, f * (size_t)p.ktot * p.d);
+  take(p.r_S, f * (size_t)(H + 1) * p.ktot * p.d);
+  take(p.r_Yh, f * (size_t)(H + 1) * p.ktot * p.d);
+  p.ws_bytes = off;
+
+  off = 0;
+  take(p.s_state, sizeof(LbState) * p.P);
+  take(p.s_g, f * (size_t)p.ktot * p.d);
+  take(p.s_p, f * (size_t)p.ktot * p.d);
+  take(p.s_S, f * (size_t)(H + 1) * p.ktot * p.d);
+  take(p.s_Yh, f * (size_t)(H + 1) * p.ktot * p.d);
+  p.state_bytes = off;
+  return std::string();
+}
+
+}  // namespace kvs

@@ -1,0 +1,201 @@
+/*
+ * kvsculpt.h -- C ABI of the MI355X (gfx950) KVSculpt cache-distillation library.
+ *
+ * The method (KVSculpt: KV Cache Compression as Distillation; arXiv abstract
+ * and the gist.science page, section 2 "Methodology"): for every (layer,
+ * KV-head) problem, the oldest Z = N - m RoPE'd key/value pairs of a cache
+ * (the compress zone) are replaced by k free pairs (Kc, Vc) that minimise
+ *     L = ||Yhat - Y||_F^2 + lambda * ||lhat - l||^2
+ * over a set of training queries Q, where (Y, l) are the compress zone's
+ * attention output and log-sum-exp for those queries and (Yhat, lhat) the
+ * compressed pairs'.  Kc is updated by L-BFGS; Vc is re-solved in closed
+ * form by ridge regression every few iterations; Kc starts at the top-k keys
+ * by attention importance.  A short pilot run at uniform k redistributes the
+ * total budget across problems in proportion to sqrt(pilot MSE).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Problems p = 0..P-1 (p = layer * kv_heads + head) are batched in one call.
+ *  - All tensors are float32, C-contiguous, caller-owned DEVICE pointers with
+ *    16-byte alignment, unless marked HOST.
+ *      Q   [P][n][d]   training queries (already RoPE'd)
+ *      Kz  [P][Z][d]   compress-zone keys     Vz [P][Z][d] values
+ *      Y   [P][n][d]   reference attention output over the compress zone
+ *      lse [P][n]      reference log-sum-exp (natural log) over the zone
+ *      Kc, Vc          packed ragged [sum_p k_p][d]; problem p starts at row
+ *                      off_p = k_0 + ... + k_{p-1}
+ *  - d is 64 or 128; 1 <= k_p <= Z; n >= 1; Z >= 1.
+ *  - Work is enqueued on the context's HIP stream and is complete when that
+ *    stream is synchronised.  Only kvs_pilot_allocate synchronises itself.
+ *  - The library never allocates device memory: calls that need scratch
+ *    take a caller workspace of at least kvs_workspace_bytes() bytes
+ *    (256-byte aligned).  Calls on one context must not overlap in time
+ *    with other users of the same workspace.
+ *  - Errors: every call returns a kvs_status.  Argument errors are found on
+ *    the host before anything is enqueued; nothing throws, aborts or prints.
+ *    Numerical failures are per problem, reported in a device flags[P] word
+ *    (KVS_FLAG_*), and a flagged problem keeps its last good state.
+ *  - Results are deterministic: reductions use fixed orders, no float atomics.
+ */
+#ifndef KVSCULPT_H
+#define KVSCULPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvs_status;
+#define KVS_OK                 0
+#define KVS_ERR_INVALID      (-1)  /* null pointer, bad size or option        */
+#define KVS_ERR_ALIGN        (-2)  /* pointer not 16-byte (workspace 256-byte) aligned */
+#define KVS_ERR_WORKSPACE    (-3)  /* workspace smaller than required          */
+#define KVS_ERR_HIP          (-4)  /* HIP runtime/launch error (see kvs_last_error) */
+
+/* per-problem numerical status bits (device int32 flags[P]) */
+#define KVS_FLAG_NONFINITE     1   /* non-finite loss or gradient             */
+#define KVS_FLAG_CHOLESKY      2   /* Gram + mu I not positive definite       */
+#define KVS_FLAG_LINESEARCH    4   /* no Armijo step found: no move, history cleared */
+#define KVS_FLAG_NONDESCENT    8   /* L-BFGS direction not a descent: reset   */
+
+typedef struct kvs_ctx_s* kvs_ctx;
+
+/* Create a context bound to a borrowed HIP stream (hipStream_t; NULL = the
+ * null stream) on the current device.  The context owns no device memory. */
+kvs_status  kvs_create(kvs_ctx* out, void* hip_stream);
+kvs_status  kvs_destroy(kvs_ctx ctx);
+const char* kvs_status_string(kvs_status s);
+/* Text of the last failing call on ctx (empty if none). */
+const char* kvs_last_error(kvs_ctx ctx);
+
+/* Problem batch description.  k points to HOST int32[P]. */
+typedef struct {
+  int32_t P, d, Z, n;
+  const int32_t* k;     /* HOST [P], 1 <= k[p] <= Z (ragged)                    */
+  double  scale;        /* score scale, 1/sqrt(d)                               */
+  double  lambda;       /* weight of the LSE term (1.0)                         */
+  double  ridge_rel;    /* mu = ridge_rel * trace(A^T A) / k  (1e-3)            */
+} kvs_batch;
+
+/* Optimizer schedule. */
+typedef struct {
+  int32_t iters;          /* L-BFGS iterations T                               */
+  int32_t vc_every;       /* Vc re-solved after iterations vc_every, 2*vc_every.. (5) */
+  int32_t history;        /* L-BFGS pairs kept, 1..16 (10)                     */
+  int32_t max_backtracks; /* Armijo trials per iteration (30)                  */
+  double  c1;             /* Armijo constant (1e-4)                            */
+  double  shrink;         /* step factor per failed trial (0.5)                */
+} kvs_opts;
+
+/* Defaults: iters 20, vc_every 5, history 10, max_backtracks 30, c1 1e-4,
+ * shrink 0.5; lambda 1, ridge_rel 1e-3, scale 1/sqrt(d). */
+void kvs_default_opts(kvs_opts* o);
+
+/* Workspace that every call below needs for this batch and schedule. */
+size_t kvs_workspace_bytes(const kvs_batch* b, const kvs_opts* o);
+/* Persistent L-BFGS state for kvs_lbfgs_init / kvs_lbfgs_step. */
+size_t kvs_lbfgs_state_bytes(const kvs_batch* b, const kvs_opts* o);
+
+/* Reference chunk attention (gist page, section 2 "Problem Formulation" and
+ * "Loss Function"): for each training query, the softmax attention output Y
+ * over the compress zone alone and its natural-log log-sum-exp lse, with
+ * scores scale * q.k.  Kz/Vz have Z rows per problem; b->k is ignored. */
+kvs_status kvs_reference_attn(kvs_ctx ctx, const kvs_batch* b, const float* Q,
+                              const float* Kz, const float* Vz, float* Y, float* lse,
+                              void* ws, size_t ws_bytes);
+
+/* Select+Fit warm start (arXiv abstract: attention-score eviction with
+ * least-squares value fitting; gist page, "Optimization Strategy",
+ * Initialization).  importance_j = sum_i exp(scale*q_i.kz_j - lse_i); the
+ * k_p largest (ties to the lower position) are taken in ascending position
+ * order: idx [sum k] int32 (positions within the problem's zone), Kc = Kz[idx],
+ * then Vc = ridge solve at Kc (see kvs_value_solve).  flags [P] device int32
+ * gets KVS_FLAG_CHOLESKY where the solve failed (Vc then zero). */
+kvs_status kvs_init_topk(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Kz,
+                         const float* Y, const float* lse, int32_t* idx, float* Kc,
+                         float* Vc, int32_t* flags, void* ws, size_t ws_bytes);
+
+/* Loss and key gradient (gist page, "Loss Function"): per problem
+ * loss[p] = sum_i ||Yhat_i - Y_i||^2 + lambda * sum_i (lhat_i - lse_i)^2 with
+ * Yhat = softmax(scale Q Kc^T) Vc and lhat its log-sum-exp; grad = dL/dKc
+ * [sum k][d] (NULL to skip); mse[p] = ||Yhat - Y||_F^2 / (n d) (NULL to skip).
+ * loss and mse are device float[P]. */
+kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
+                         const float* lse, const float* Kc, const float* Vc, float* loss,
+                         float* grad, float* mse, void* ws, size_t ws_bytes);
+
+/* Closed-form values (gist page, "Optimization Strategy", Value Optimization:
+ * ridge regression given the attention weights of the current keys):
+ * A = softmax(scale Q Kc^T), mu = ridge_rel * trace(A^T A) / k,
+ * (A^T A + mu I) Vc = A^T Y by Cholesky and two triangular solves.
+ * lse [P][n] is only used as a per-row shift of the scores (it does not
+ * change A); NULL means no shift.  flags [P] (device, may be NULL) gets
+ * KVS_FLAG_CHOLESKY where the factorisation failed; Vc of that problem is
+ * left unchanged. */
+kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
+                           const float* lse, const float* Kc, float* Vc, int32_t* flags,
+                           void* ws, size_t ws_bytes);
+
+/* L-BFGS on the keys (gist page, "Optimization Strategy", Key Optimization).
+ * kvs_lbfgs_init evaluates loss and gradient at Kc with the given Vc into the
+ * persistent state (clear_history != 0 also empties the history; 0 keeps it,
+ * as after a value re-solve).  kvs_lbfgs_step performs one iteration per
+ * problem: two-loop direction over the stored pairs (empty history: -g with
+ * first step 1/max(1,||g||)), backtracking Armijo search
+ * L(x + a p) <= L(x) + c1 a g^T p halving a up to max_backtracks times, then
+ * the curvature-guarded pair update (s^T y > 1e-10 ||s|| ||y||).  Kc is
+ * updated in place; loss [P] (device float) receives the loss at the new
+ * point; flags [P] (device int32) accumulates KVS_FLAG_* bits.  state is
+ * caller memory of kvs_lbfgs_state_bytes() bytes, valid between calls with
+ * the same batch, Q, Y, lse and Vc.  kvs_lbfgs_step synchronises the stream
+ * once per Armijo trial round to decide whether another round is needed. */
+kvs_status kvs_lbfgs_init(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                          const float* Y, const float* lse, const float* Kc, const float* Vc,
+                          int32_t clear_history, float* loss, int32_t* flags,
+                          void* state, size_t state_bytes, void* ws, size_t ws_bytes);
+kvs_status kvs_lbfgs_step(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                          const float* Y, const float* lse, float* Kc, const float* Vc,
+                          float* loss, int32_t* flags, void* state, size_t state_bytes,
+                          void* ws, size_t ws_bytes);
+
+/* The whole alternating schedule (arXiv abstract: keys by L-BFGS, values in
+ * closed form, alternating every few steps), batched over all problems with
+ * ragged k: reference attention, Select+Fit init, then for t = 1..iters one
+ * L-BFGS iteration and, when t % vc_every == 0, a value re-solve followed by
+ * loss and gradient at the same keys (history kept).  Outputs Kc, Vc packed
+ * [sum k][d]; loss [P] final loss; mse [P] final output MSE (may be NULL);
+ * init_loss [P] loss at the Select+Fit start (may be NULL); flags [P].
+ * All outputs are device memory. */
+kvs_status kvs_compress(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                        const float* Kz, const float* Vz, float* Kc, float* Vc, float* loss,
+                        float* mse, float* init_loss, int32_t* flags, void* ws, size_t ws_bytes);
+
+/* Pilot run and budget (gist page, "Adaptive Budget Allocation"): kvs_compress
+ * at the batch's uniform k for pilot_iters iterations (60), per-problem output
+ * MSE into pilot_mse [P] (device float), then kvs_allocate_budget with
+ * K_total = sum of the batch's k.  k_out is HOST int32[P].  Synchronises the
+ * stream.  The workspace must fit the pilot batch. */
+kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o,
+                              int32_t pilot_iters, double alpha, int32_t k_min, int32_t k_max,
+                              const float* Q, const float* Kz, const float* Vz,
+                              float* pilot_mse, int32_t* k_out, void* ws, size_t ws_bytes);
+
+/* Budget split (gist page, "Adaptive Budget Allocation": total budget
+ * redistributed in proportion to the square root of the pilot MSE), pure
+ * host, IEEE double: weights w_p = sqrt(mse_p) (alpha = 0.5; alpha = 1 uses
+ * mse_p; other alpha pow), x_p = clamp(t w_p, k_min, k_max) with sum K_total
+ * (bounded water-filling), then floors plus largest remainders, ties to the
+ * lower p.  Sums run in problem order so the result is reproducible bit for
+ * bit.  mse and k_out are HOST arrays of P entries.  All-zero weights mean a
+ * uniform split.  Errors: KVS_ERR_INVALID if P < 1, a weight is negative or
+ * not finite, k_min < 1, k_min > k_max or K_total outside
+ * [P k_min, P k_max]. */
+kvs_status kvs_allocate_budget(const double* mse, int32_t P, int64_t K_total, double alpha,
+                               int32_t k_min, int32_t k_max, int32_t* k_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSCULPT_H */
