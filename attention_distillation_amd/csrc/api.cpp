@@ -126,6 +126,163 @@ void run_backward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* 
   launch_grad_reduce(gr, pl.d, ctx->stream);
 }
 
+// Ridge value solve from the last forward's stored scores (St, e): Gram with
+// the A^T Y rows, fixed-order reduction, mu, panel Cholesky, back solve.
+void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Y, float* Vc,
+                     int* flags, LbState* st, int mask, void* ws) {
+  float* M = at<float>(ws, pl.r_M);
+  GramArgs g{};
+  g.St = at<float>(ws, pl.r_St); g.e = at<float>(ws, pl.r_e); g.Y = Y; g.st = st; g.active_mask = mask;
+  g.Mpart = pl.Cg > 1 ? at<float>(ws, pl.r_Mg) : M; g.info = at<ProbInfo>(ws, pl.r_info);
+  g.P = pl.P; g.n = pl.n; g.Cg = pl.Cg; g.kpadmax = pl.kpadmax; g.mtot = pl.mtot;
+  launch_gram(g, pl.d, ctx->stream);
+  GramReduceArgs r{};
+  r.Mpart = g.Mpart; r.M = M; r.trpart = at<double>(ws, pl.r_tr); r.st = st; r.active_mask = mask;
+  r.info = g.info; r.P = pl.P; r.Cg = pl.Cg; r.kpadmax = pl.kpadmax; r.mtot = pl.mtot;
+  launch_gram_reduce(r, pl.d, ctx->stream);
+  CholArgs c{};
+  c.M = M; c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
+  c.st = st; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
+  c.ridge_rel = b->ridge_rel;
+  launch_mu(c, ctx->stream);
+  const int KT = pl.kpadmax / kTile;
+  for (int j = 0; j < KT; ++j) {
+    launch_potrf_panel(c, pl.d, j, ctx->stream);
+    launch_trailing(c, pl.d, j, ctx->stream);
+  }
+  BackArgs bk{};
+  bk.M = M; bk.X = at<float>(ws, pl.r_X); bk.Vc = Vc; bk.info_out = c.info_out; bk.flags = flags;
+  bk.st = st; bk.active_mask = mask; bk.info = g.info; bk.P = pl.P;
+  launch_back_subst(bk, pl.d, ctx->stream);
+}
+
+// Select+Fit: importance, top-k, gather, then the ridge fit at the selected keys.
+void run_init_topk(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Kz,
+                   const float* Y, const float* lse, int* idx, float* Kc, float* Vc, int* flags,
+                   LbState* st, void* ws) {
+  ImpArgs ia{};
+  ia.Q = Q; ia.Kz = Kz; ia.lse = lse;
+  ia.Mpart = at<float>(ws, pl.r_imp);
+  ia.Spart = ia.Mpart + (size_t)pl.Cq * pl.P * pl.Z;
+  ia.P = pl.P; ia.n = pl.n; ia.Z = pl.Z; ia.Cq = pl.Cq; ia.scale = b->scale;
+  launch_importance(ia, pl.d, ctx->stream);
+  TopkArgs ta{};
+  ta.Mpart = ia.Mpart; ta.Spart = ia.Spart; ta.Kz = Kz; ta.idx = idx; ta.Kc = Kc;
+  ta.info = at<ProbInfo>(ws, pl.r_info); ta.P = pl.P; ta.Z = pl.Z; ta.Cq = pl.Cq; ta.d = pl.d;
+  launch_topk(ta, ctx->stream);
+  launch_fill_f32(Vc, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
+  run_value_solve(ctx, pl, b, Y, Vc, flags, st, 0xF, ws);
+}
+
+constexpr int kAll = 0xF;
+
+struct LbBuffers {
+  LbState* st;
+  float *g, *p, *S, *Yh, *gnew;
+  double* hpart;
+  int* status_view;
+};
+
+LbBuffers lb_in_ws(const Plan& pl, void* ws) {
+  return LbBuffers{at<LbState>(ws, pl.r_state), at<float>(ws, pl.r_g), at<float>(ws, pl.r_p),
+                   at<float>(ws, pl.r_S), at<float>(ws, pl.r_Yh), at<float>(ws, pl.r_grad),
+                   at<double>(ws, pl.r_hpart), at<int>(ws, pl.r_status)};
+}
+
+LbBuffers lb_in_state(const Plan& pl, void* state, void* ws) {
+  return LbBuffers{at<LbState>(state, pl.s_state), at<float>(state, pl.s_g), at<float>(state, pl.s_p),
+                   at<float>(state, pl.s_S), at<float>(state, pl.s_Yh), at<float>(ws, pl.r_grad),
+                   at<double>(ws, pl.r_hpart), at<int>(ws, pl.r_status)};
+}
+
+// Loss and gradient at the current keys for every problem, then the
+// L-BFGS bookkeeping: prep_mode 1 keeps the history, 2 clears it.
+void lb_eval_at_x(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                  const float* Y, const float* lse, float* Kc, const float* Vc, const LbBuffers& B,
+                  int prep_mode, float* loss_out, float* mse_out, void* ws) {
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws);
+  run_backward(ctx, pl, b, Q, Vc, B.st, kAll, B.gnew, ws);
+  HistArgs h{};
+  h.x = Kc; h.p = B.p; h.g = B.g; h.gnew = B.gnew; h.S = B.S; h.Yh = B.Yh; h.st = B.st;
+  h.active_mask = kAll; h.part = B.hpart; h.info = at<ProbInfo>(ws, pl.r_info); h.P = pl.P;
+  h.d = pl.d; h.ktot = (int)pl.ktot; h.nwg = pl.nwg; h.mode = 1;
+  launch_hist_dots(h, ctx->stream);
+  PrepArgs pa{};
+  pa.st = B.st; pa.part = B.hpart; pa.nwg = pl.nwg; pa.P = pl.P; pa.mode = prep_mode;
+  pa.history = pl.H; pa.curv_eps = 1e-10; pa.select_status = 0; pa.flags = nullptr;
+  launch_prepare(pa, ctx->stream);
+}
+
+// One L-BFGS iteration for every problem: direction, backtracking Armijo
+// rounds (the host reads the per-problem status after each round), then
+// gradient at the accepted keys and the history update.  Returns a HIP error
+// status; *any_fail reports a failed search (stored scores then stale).
+kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
+                        const float* Q, const float* Y, const float* lse, float* Kc, const float* Vc,
+                        const LbBuffers& B, void* ws, bool* any_fail, std::vector<int>& hs) {
+  DirArgs da{};
+  da.p = B.p; da.g = B.g; da.S = B.S; da.Yh = B.Yh; da.st = B.st; da.info = at<ProbInfo>(ws, pl.r_info);
+  da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nwg = pl.nwg;
+  launch_direction(da, ctx->stream);
+  hs.resize(pl.P);
+  *any_fail = false;
+  for (int round = 0; round < o->max_backtracks; ++round) {
+    run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws);
+    if (hipMemcpyAsync(hs.data(), B.status_view, sizeof(int) * pl.P, hipMemcpyDeviceToHost,
+                       ctx->stream) != hipSuccess ||
+        hipStreamSynchronize(ctx->stream) != hipSuccess)
+      return fail(ctx, KVS_ERR_HIP, "line search: %s", hipGetErrorString(hipGetLastError()));
+    bool searching = false;
+    for (int v : hs) searching |= (v == ST_SEARCH);
+    if (!searching) break;
+  }
+  for (int v : hs) *any_fail |= (v == ST_FAIL);
+  run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, B.gnew, ws);
+  HistArgs h{};
+  h.x = Kc; h.p = B.p; h.g = B.g; h.gnew = B.gnew; h.S = B.S; h.Yh = B.Yh; h.st = B.st;
+  h.active_mask = 1 << ST_ACCEPT; h.part = B.hpart; h.info = at<ProbInfo>(ws, pl.r_info);
+  h.P = pl.P; h.d = pl.d; h.ktot = (int)pl.ktot; h.nwg = pl.nwg; h.mode = 0;
+  launch_hist_dots(h, ctx->stream);
+  PrepArgs pa{};
+  pa.st = B.st; pa.part = B.hpart; pa.nwg = pl.nwg; pa.P = pl.P; pa.mode = 0;
+  pa.history = pl.H; pa.curv_eps = 1e-10; pa.select_status = 0; pa.flags = nullptr;
+  launch_prepare(pa, ctx->stream);
+  return KVS_OK;
+}
+
+// The whole alternating schedule on the plan's batch.
+kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
+                         const float* Q, const float* Kz, const float* Vz, float* Kc, float* Vc,
+                         float* loss, float* mse, float* init_loss, int* flags, void* ws) {
+  float* Yr = at<float>(ws, pl.r_yref);
+  float* lr = at<float>(ws, pl.r_lseref);
+  run_reference(ctx, pl, b, Q, Kz, Vz, Yr, lr, ws);
+  LbBuffers B = lb_in_ws(pl, ws);
+  launch_state_init(B.st, pl.P, 1, ctx->stream);
+  run_init_topk(ctx, pl, b, Q, Kz, Yr, lr, at<int>(ws, pl.r_idx), Kc, Vc, nullptr, B.st, ws);
+  lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws);
+  bool refreshed = true;
+  std::vector<int> hs;
+  for (int t = 1; t <= o->iters; ++t) {
+    bool any_fail = false;
+    kvs_status s = lb_iteration(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, &any_fail, hs);
+    if (s != KVS_OK) return s;
+    refreshed = false;
+    if (t % o->vc_every == 0) {
+      if (any_fail)   // stored scores of a failed search belong to a rejected trial
+        run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, kAll, 2, nullptr, nullptr, o, ws);
+      run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws);
+      lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 1, nullptr, mse, ws);
+      refreshed = true;
+    }
+  }
+  if (!refreshed || o->iters == 0)
+    run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, kAll, 2, nullptr, mse, o, ws);
+  launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
+  return KVS_OK;
+}
+
 }  // namespace kvs
 
 using namespace kvs;
@@ -213,26 +370,137 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
   return hip_check(ctx, fn);
 }
 
+kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
+                           const float* lse, const float* Kc, float* Vc, int32_t* flags, void* ws,
+                           size_t ws_bytes) {
+  const char* fn = "kvs_value_solve";
+  if (!ctx) return KVS_ERR_INVALID;
+  KVS_NEED(Q); KVS_NEED(Y); KVS_NEED(Kc); KVS_NEED(Vc); KVS_OPT(lse); KVS_OPT(flags);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
+  run_value_solve(ctx, pl, b, Y, Vc, flags, nullptr, 0, ws);
+  return hip_check(ctx, fn);
+}
+
 }  // extern "C"
 
-// ---- entry points whose kernels are not wired yet -------------------------
+
 extern "C" {
-#define KVS_TODO(name) return fail(ctx, KVS_ERR_INVALID, "%s: not available in this build", #name)
-kvs_status kvs_init_topk(kvs_ctx ctx, const kvs_batch*, const float*, const float*, const float*,
-                         const float*, int32_t*, float*, float*, int32_t*, void*, size_t) { KVS_TODO(kvs_init_topk); }
-kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch*, const float*, const float*, const float*,
-                           const float*, float*, int32_t*, void*, size_t) { KVS_TODO(kvs_value_solve); }
-kvs_status kvs_lbfgs_init(kvs_ctx ctx, const kvs_batch*, const kvs_opts*, const float*, const float*,
-                          const float*, const float*, const float*, int32_t, float*, int32_t*, void*,
-                          size_t, void*, size_t) { KVS_TODO(kvs_lbfgs_init); }
-kvs_status kvs_lbfgs_step(kvs_ctx ctx, const kvs_batch*, const kvs_opts*, const float*, const float*,
-                          const float*, float*, const float*, float*, int32_t*, void*, size_t, void*,
-                          size_t) { KVS_TODO(kvs_lbfgs_step); }
-kvs_status kvs_compress(kvs_ctx ctx, const kvs_batch*, const kvs_opts*, const float*, const float*,
-                        const float*, float*, float*, float*, float*, float*, int32_t*, void*, size_t) {
-  KVS_TODO(kvs_compress);
+
+kvs_status kvs_init_topk(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Kz,
+                         const float* Y, const float* lse, int32_t* idx, float* Kc, float* Vc,
+                         int32_t* flags, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_init_topk";
+  if (!ctx) return KVS_ERR_INVALID;
+  KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Y); KVS_NEED(lse); KVS_NEED(idx); KVS_NEED(Kc); KVS_NEED(Vc);
+  KVS_OPT(flags);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  run_init_topk(ctx, pl, b, Q, Kz, Y, lse, idx, Kc, Vc, flags, nullptr, ws);
+  return hip_check(ctx, fn);
 }
-kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch*, const kvs_opts*, int32_t, double, int32_t,
-                              int32_t, const float*, const float*, const float*, float*, int32_t*,
-                              void*, size_t) { KVS_TODO(kvs_pilot_allocate); }
+
+static kvs_status check_state(kvs_ctx ctx, const char* fn, const Plan& pl, void* state, size_t bytes) {
+  if (!state) return fail(ctx, KVS_ERR_INVALID, "%s: state is NULL", fn);
+  if (!aligned(state, 256)) return fail(ctx, KVS_ERR_ALIGN, "%s: state not 256-byte aligned", fn);
+  if (bytes < pl.state_bytes)
+    return fail(ctx, KVS_ERR_WORKSPACE, "%s: state %zu bytes < required %zu", fn, bytes, pl.state_bytes);
+  return KVS_OK;
 }
+
+kvs_status kvs_lbfgs_init(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                          const float* Y, const float* lse, const float* Kc, const float* Vc,
+                          int32_t clear_history, float* loss, int32_t* flags, void* state,
+                          size_t state_bytes, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_lbfgs_init";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Y); KVS_NEED(lse); KVS_NEED(Kc); KVS_NEED(Vc); KVS_OPT(loss); KVS_OPT(flags);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  if ((s = check_state(ctx, fn, pl, state, state_bytes)) != KVS_OK) return s;
+  LbBuffers B = lb_in_state(pl, state, ws);
+  launch_state_init(B.st, pl.P, clear_history ? 1 : 0, ctx->stream);
+  lb_eval_at_x(ctx, pl, b, o, Q, Y, lse, const_cast<float*>(Kc), Vc, B, clear_history ? 2 : 1, loss,
+               nullptr, ws);
+  launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
+  return hip_check(ctx, fn);
+}
+
+kvs_status kvs_lbfgs_step(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                          const float* Y, const float* lse, float* Kc, const float* Vc, float* loss,
+                          int32_t* flags, void* state, size_t state_bytes, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_lbfgs_step";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Y); KVS_NEED(lse); KVS_NEED(Kc); KVS_NEED(Vc); KVS_OPT(loss); KVS_OPT(flags);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  if ((s = check_state(ctx, fn, pl, state, state_bytes)) != KVS_OK) return s;
+  LbBuffers B = lb_in_state(pl, state, ws);
+  bool any_fail = false;
+  std::vector<int> hs;
+  s = lb_iteration(ctx, pl, b, o, Q, Y, lse, Kc, Vc, B, ws, &any_fail, hs);
+  if (s != KVS_OK) return s;
+  launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
+  return hip_check(ctx, fn);
+}
+
+kvs_status kvs_compress(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                        const float* Kz, const float* Vz, float* Kc, float* Vc, float* loss,
+                        float* mse, float* init_loss, int32_t* flags, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_compress";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(Kc); KVS_NEED(Vc); KVS_NEED(loss);
+  KVS_OPT(mse); KVS_OPT(init_loss); KVS_OPT(flags);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  s = compress_impl(ctx, pl, b, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, ws);
+  if (s != KVS_OK) return s;
+  return hip_check(ctx, fn);
+}
+
+kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o,
+                              int32_t pilot_iters, double alpha, int32_t k_min, int32_t k_max,
+                              const float* Q, const float* Kz, const float* Vz, float* pilot_mse,
+                              int32_t* k_out, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_pilot_allocate";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(pilot_mse);
+  if (!k_out) return fail(ctx, KVS_ERR_INVALID, "%s: k_out is NULL", fn);
+  if (pilot_iters < 0) return fail(ctx, KVS_ERR_INVALID, "%s: pilot_iters < 0", fn);
+  if (!(alpha >= 0.0)) return fail(ctx, KVS_ERR_INVALID, "%s: alpha < 0", fn);
+  kvs_opts po = *o;
+  po.iters = pilot_iters;
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, &po, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  if (k_min < 1 || k_max < k_min || k_max > b->Z)
+    return fail(ctx, KVS_ERR_INVALID, "%s: need 1 <= k_min <= k_max <= Z", fn);
+  int* dflags = at<int>(ws, pl.r_flags);
+  float* dloss = at<float>(ws, pl.r_loss);
+  launch_fill_i32(dflags, 0, pl.P, ctx->stream);
+  s = compress_impl(ctx, pl, b, &po, Q, Kz, Vz, at<float>(ws, pl.r_Kc), at<float>(ws, pl.r_Vc), dloss,
+                    pilot_mse, nullptr, dflags, ws);
+  if (s != KVS_OK) return s;
+  std::vector<float> hm(pl.P);
+  if (hipMemcpyAsync(hm.data(), pilot_mse, sizeof(float) * pl.P, hipMemcpyDeviceToHost, ctx->stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return fail(ctx, KVS_ERR_HIP, "%s: %s", fn, hipGetErrorString(hipGetLastError()));
+  std::vector<double> md(hm.begin(), hm.end());
+  const int64_t K = pl.ktot;
+  s = kvs_allocate_budget(md.data(), pl.P, K, alpha, k_min, k_max, k_out);
+  if (s != KVS_OK) return fail(ctx, s, "%s: budget split failed (non-finite pilot MSE?)", fn);
+  return hip_check(ctx, fn);
+}
+
+}  // extern "C"

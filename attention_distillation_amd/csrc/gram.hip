@@ -1,0 +1,198 @@
+// Normal equations of the ridge value solve, gfx950.
+//
+// For A = exp(St - e) (the softmax weights rebuilt from the stored shifted
+// scores, n x k) the kernel forms the augmented lower-trapezoidal matrix
+//     M = [ A^T A ]   rows 0..kpad-1  (lower triangle, 64x64 tiles)
+//         [ Y^T A ]   rows kpad..kpad+d-1
+// so that a Cholesky factorisation of the top block, carried through the
+// bottom rows, also performs the forward substitution L W = A^T Y.
+// Tiles are 64x64; 4 waves each compute a 32x32 quarter with 16x16x4 fp32
+// MFMA, operands staged in LDS along the query (contraction) axis.  The
+// query axis can be split over gridDim.z; partial tiles are then summed in
+// a fixed order by gram_reduce_kernel, which also pads rows/columns k..kpad-1
+// with the identity and emits per-diagonal-tile trace partials.
+#include "kvs_internal.h"
+
+namespace kvs {
+
+__device__ __forceinline__ f32x4 mfma_g(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// tile t of a problem with KT key tiles and DT = d/64 value tiles -> (I, J)
+__device__ __forceinline__ bool gram_tile(long long t, int KT, int DT, int& I, int& J) {
+  const long long tri = (long long)KT * (KT + 1) / 2;
+  if (t < tri) {
+    int i = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while ((long long)(i + 1) * (i + 2) / 2 <= t) ++i;
+    while ((long long)i * (i + 1) / 2 > t) --i;
+    I = i;
+    J = (int)(t - (long long)i * (i + 1) / 2);
+    return true;
+  }
+  const long long u = t - tri;
+  if (u >= (long long)DT * KT) return false;
+  I = KT + (int)(u / KT);
+  J = (int)(u % KT);
+  return true;
+}
+
+template <int D>
+__device__ __forceinline__ void stage_keys(float (*dst)[68], const float* St, const float* e, int k,
+                                           int key0, int npad, int qt, int qend, int tid) {
+  for (int i = tid; i < 64 * 16; i += 256) {
+    const int r = i >> 4, c4 = i & 15;
+    const int key = key0 + r;
+    const int q = qt + 4 * c4;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (key < k && q < qend) {
+      const f32x4 s = *(const f32x4*)(St + (size_t)key * npad + q);
+      v.x = expf(s.x - e[q]);
+      v.y = (q + 1 < qend) ? expf(s.y - e[q + 1]) : 0.f;
+      v.z = (q + 2 < qend) ? expf(s.z - e[q + 2]) : 0.f;
+      v.w = (q + 3 < qend) ? expf(s.w - e[q + 3]) : 0.f;
+    }
+    *(f32x4*)&dst[r][4 * c4] = v;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int KT = pi.kpad / 64, DT = D / 64;
+  int I, J;
+  if (!gram_tile(blockIdx.x, KT, DT, I, J)) return;
+  const int n = a.n, npad = (n + 3) & ~3;
+  const int nq = ((((n + a.Cg - 1) / a.Cg) + 63) / 64) * 64;
+  const int qbeg = blockIdx.z * nq, qend = min(n, qbeg + nq);
+
+  __shared__ float Ra[64][68];
+  __shared__ float Ca[64][68];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+  const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
+  const bool diag = (I == J);
+  const float* St = a.St + pi.soff;
+  const float* e = a.e + (size_t)p * n;
+  const float* Y = a.Y + (size_t)p * n * D;
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int qt = qbeg; qt < qend; qt += 64) {
+    __syncthreads();
+    if (I < KT) {
+      stage_keys<D>(Ra, St, e, pi.k, 64 * I, npad, qt, qend, tid);
+    } else {
+      const int dim0 = 64 * (I - KT);
+      for (int i = tid; i < 64 * 16; i += 256) {
+        const int qq = i >> 4, c4 = i & 15;
+        const int q = qt + qq;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (q < qend) v = *(const f32x4*)(Y + (size_t)q * D + dim0 + 4 * c4);
+        Ra[4 * c4 + 0][qq] = v.x;
+        Ra[4 * c4 + 1][qq] = v.y;
+        Ra[4 * c4 + 2][qq] = v.z;
+        Ra[4 * c4 + 3][qq] = v.w;
+      }
+    }
+    if (!diag) stage_keys<D>(Ca, St, e, pi.k, 64 * J, npad, qt, qend, tid);
+    __syncthreads();
+    float (*C)[68] = diag ? Ra : Ca;
+#pragma unroll
+    for (int qq = 0; qq < 64; qq += 16) {
+      f32x4 av[2], bv[2];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) av[ib] = *(const f32x4*)&Ra[rb + 16 * ib + lq][qq + 4 * g];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) bv[jb] = *(const f32x4*)&C[cb + 16 * jb + lq][qq + 4 * g];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          acc[ib][jb] = mfma_g(av[ib].x, bv[jb].x, acc[ib][jb]);
+          acc[ib][jb] = mfma_g(av[ib].y, bv[jb].y, acc[ib][jb]);
+          acc[ib][jb] = mfma_g(av[ib].z, bv[jb].z, acc[ib][jb]);
+          acc[ib][jb] = mfma_g(av[ib].w, bv[jb].w, acc[ib][jb]);
+        }
+    }
+  }
+
+  float* Mout = a.Mpart + (size_t)blockIdx.z * a.mtot + pi.moff;
+  const int ld = pi.kpad;
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 64 * I + rb + 16 * ib + 4 * g + r;
+        const int col = 64 * J + cb + 16 * jb + lq;
+        Mout[(size_t)row * ld + col] = acc[ib][jb][r];
+      }
+}
+
+void launch_gram(const GramArgs& a, int d, hipStream_t s) {
+  const long long KT = a.kpadmax / 64;
+  const long long T = KT * (KT + 1) / 2 + (long long)(d / 64) * KT;
+  dim3 grid((unsigned)T, a.P, a.Cg);
+  if (d == 128) hipLaunchKernelGGL((gram_kernel<128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gram_kernel<64>), grid, dim3(256), 0, s, a);
+}
+
+// Sum split partials (fixed order), pad with the identity beyond k, trace.
+template <int D>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(GramReduceArgs a) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int KT = pi.kpad / 64, DT = D / 64;
+  int I, J;
+  if (!gram_tile(blockIdx.x, KT, DT, I, J)) return;
+  const int ld = pi.kpad, k = pi.k;
+  const int tid = threadIdx.x;
+  __shared__ double red[256];
+  double tr = 0.0;
+  for (int i = tid; i < 64 * 16; i += 256) {
+    const int r = i >> 4, c4 = i & 15;
+    const int row = 64 * I + r;
+    const int col = 64 * J + 4 * c4;
+    const size_t off = pi.moff + (size_t)row * ld + col;
+    f32x4 v = *(const f32x4*)(a.Mpart + off);
+    for (int c = 1; c < a.Cg; ++c) v += *(const f32x4*)(a.Mpart + (size_t)c * a.mtot + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int cc = col + e;
+      if (I < KT) {
+        if (row >= k || cc >= k) v[e] = (row == cc) ? 1.f : 0.f;
+        else if (row == cc) tr += (double)v[e];
+      } else if (cc >= k) {
+        v[e] = 0.f;
+      }
+    }
+    *(f32x4*)(a.M + off) = v;
+  }
+  if (I == J) {
+    red[tid] = tr;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+      if (tid < off) red[tid] += red[tid + off];
+      __syncthreads();
+    }
+    if (tid == 0) a.trpart[(size_t)p * (a.kpadmax / 64) + I] = red[0];
+  }
+}
+
+void launch_gram_reduce(const GramReduceArgs& a, int d, hipStream_t s) {
+  const long long KT = a.kpadmax / 64;
+  const long long T = KT * (KT + 1) / 2 + (long long)(d / 64) * KT;
+  dim3 grid((unsigned)T, a.P);
+  if (d == 128) hipLaunchKernelGGL((gram_reduce_kernel<128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gram_reduce_kernel<64>), grid, dim3(256), 0, s, a);
+}
+
+}  // namespace kvs

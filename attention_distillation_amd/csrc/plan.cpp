@@ -36,7 +36,8 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     if (o->history < 1 || o->history > kHistMax) return "history must be in [1, 16]";
     if (o->iters < 0) return "iters must be >= 0";
     if (o->vc_every < 1) return "vc_every must be >= 1";
-    if (o->max_backtracks < 0) return "max_backtracks must be >= 0";
+    if (o->max_backtracks < 1) return "max_backtracks must be >= 1";
+    if (!(o->c1 > 0.0 && o->c1 < 1.0)) return "c1 must be in (0, 1)";
     if (!(o->shrink > 0.0 && o->shrink < 1.0)) return "shrink must be in (0, 1)";
     H = o->history;
   }
@@ -76,9 +77,9 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p.Cq = split_for((long long)p.P * ((p.Z + 63) / 64), (int)qtiles);
   p.nblk = merge_blocks(p.n);
   {
-    // L-BFGS vector kernels: ~4096 floats per workgroup per problem
-    long long per = (p.kmax * (long long)p.d + 4095) / 4096;
-    p.nwg = (int)std::max<long long>(1, std::min<long long>(per, 64));
+    // L-BFGS vector kernels: 4096 floats (1024 float4) per workgroup
+    const long long per = (p.kmax * (long long)p.d + 4095) / 4096;
+    p.nwg = (int)std::max<long long>(1, per);
   }
 
   const int Cmax = std::max(p.Cref, p.C);
@@ -119,6 +120,8 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_p, f * (size_t)p.ktot * p.d);
   take(p.r_S, f * (size_t)(H + 1) * p.ktot * p.d);
   take(p.r_Yh, f * (size_t)(H + 1) * p.ktot * p.d);
+  take(p.r_Kc, f * (size_t)p.ktot * p.d);
+  take(p.r_Vc, f * (size_t)p.ktot * p.d);
   p.ws_bytes = off;
 
   off = 0;

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI (no GPU): exports, argument errors, allocator."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import kvsculpt as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import attention_distillation_amd as K
+    K.load()
+    return K
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvsculpt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point(K):
+    names = _declared()
+    assert len(names) >= 16
+    lib = ctypes.CDLL(K._lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(K.ENTRY_POINTS) == set(names)
+
+
+def test_workspace_and_state_sizes(K):
+    b = K.Batch(2, 128, 1920, 3840, k=[960, 960])
+    o = K.opts()
+    ws = K.workspace_bytes(b, o)
+    st = K.lbfgs_state_bytes(b, o)
+    # stored scores alone are k * n floats per problem
+    assert ws > 2 * 960 * 3840 * 4
+    assert st >= 2 * (2 + 2 * 11) * 960 * 128 * 4
+    bad = K.Batch(2, 96, 1920, 3840, k=[960, 960])   # d must be 64 or 128
+    assert K.workspace_bytes(bad, o) == 0
+    bad2 = K.Batch(2, 128, 100, 64, k=[10, 101])     # k > Z
+    assert K.workspace_bytes(bad2, o) == 0
+
+
+def test_argument_errors_are_reported_before_any_launch(K):
+    lib = K.load()
+    ctx = ctypes.c_void_p()
+    assert lib.kvs_create(ctypes.byref(ctx), None) == 0
+    b = K.Batch(1, 64, 224, 96, k=[64])
+    # NULL pointers -> invalid; misaligned -> align; small workspace -> workspace
+    st = lib.kvs_loss_grad(ctx, ctypes.byref(b.c), None, None, None, None, None, None, None, None,
+                           None, 0)
+    assert st == -1 and b"NULL" in lib.kvs_last_error(ctx)
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    st = lib.kvs_loss_grad(ctx, ctypes.byref(b.c), odd, fake, fake, fake, fake, fake, None, None,
+                           fake, 1 << 30)
+    assert st == -2
+    st = lib.kvs_loss_grad(ctx, ctypes.byref(b.c), fake, fake, fake, fake, fake, fake, None, None,
+                           fake, 16)
+    assert st == -3 and b"workspace" in lib.kvs_last_error(ctx)
+    o = K.opts(max_backtracks=0)
+    st = lib.kvs_compress(ctx, ctypes.byref(b.c), ctypes.byref(o), fake, fake, fake, fake, fake, fake,
+                          None, None, None, fake, 1 << 30)
+    assert st == -1 and b"max_backtracks" in lib.kvs_last_error(ctx)
+    assert lib.kvs_destroy(ctx) == 0
+
+
+def test_allocator_cpp_equals_oracle_bit_for_bit(K):
+    rng = np.random.default_rng(20)
+    for it in range(10000):
+        P = int(rng.integers(1, 60))
+        scale = rng.choice([1e-6, 1.0, 1e3])
+        mse = np.exp(rng.normal(0, 3, size=P)) * scale
+        if it % 7 == 0:
+            mse[rng.integers(0, P)] = 0.0
+        kmax = int(rng.integers(1, 4000))
+        kmin = int(rng.integers(1, kmax + 1))
+        K_total = int(rng.integers(P * kmin, P * kmax + 1))
+        alpha = [0.5, 1.0, 0.75][it % 3]
+        want = O.allocate_budget(list(mse), K_total, alpha, kmin, kmax)
+        got = K.kvs_allocate_budget(mse, K_total, alpha, kmin, kmax)
+        assert got.tolist() == want, (it, P, kmin, kmax, K_total)
+
+
+def test_allocator_rejects_bad_requests(K):
+    with pytest.raises(K.KvsError):
+        K.kvs_allocate_budget([1.0, 2.0], 10, 0.5, 1, 4)
+    with pytest.raises(K.KvsError):
+        K.kvs_allocate_budget([1.0, float("nan")], 4, 0.5, 1, 4)
+    assert K.kvs_allocate_budget([0.0, 0.0, 0.0], 7).tolist() == [3, 2, 2]

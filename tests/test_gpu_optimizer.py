@@ -1,0 +1,210 @@
+"""GPU parity of the optimizer entry points through the C ABI.
+
+- kvs_init_topk: the selected index set equals the oracle's except for swaps
+  among keys whose float64 log-importances tie within 1e-5 relative at the
+  k-th value; Kc is exactly Kz[idx]; Vc within 1e-4 of the oracle's ridge
+  solve at the GPU's keys.
+- kvs_lbfgs_init / kvs_lbfgs_step: from the same float32 start and fixed Vc,
+  the loss after each of the first iterations within 1e-4 of the oracle's.
+- kvs_compress: final loss within 2% of the oracle's after the same schedule
+  (the loss at the Select+Fit start within 1e-4).
+- kvs_pilot_allocate: per-problem budgets bit-exact with the oracle allocator
+  fed the GPU's pilot MSEs; pilot MSEs within 2% of the oracle's.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import attention_distillation_amd as K
+from oracle import kvsculpt as O
+from synth import WORKLOADS, make_batch, tiny_workload
+from tests.gpu_common import empty, host, rel, say, to_gpu, workspace
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _ref(b):
+    out = []
+    for p in range(b["Q"].shape[0]):
+        Y, l = O.reference_attention(b["Q"][p], b["Kz"][p], b["Vz"][p], b["scale"])
+        out.append((Y.astype(np.float32), l.astype(np.float32)))
+    return out
+
+
+def _check_topk(idx_gpu, logimp, k):
+    want = O.select_topk(logimp, k)
+    got = np.sort(np.asarray(idx_gpu))
+    if np.array_equal(got, want):
+        return 0
+    kth = np.sort(logimp)[::-1][k - 1]
+    diff = np.setxor1d(got, want)
+    assert np.all(np.abs(logimp[diff] - kth) <= 1e-5 * max(1.0, abs(kth))), "non-tie selection differs"
+    return len(diff)
+
+
+INIT_CASES = {
+    "cfg0": (WORKLOADS[0], lambda p, Z: 64),
+    "cfg1": (WORKLOADS[1], lambda p, Z: 960),
+    "tiny-ragged": (tiny_workload(d=64, N=300, m=20, g=2, F=30, layers=2, kv_heads=2),
+                    lambda p, Z: [1, 64, 100, 280][p]),
+}
+
+
+@pytest.mark.parametrize("name", list(INIT_CASES))
+def test_init_topk_matches_oracle(name):
+    w, kfun = INIT_CASES[name]
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    ks = [kfun(p, Z) for p in range(P)]
+    say(f"[init-topk] case={name} P={P} n={n} Z={Z} k={ks}")
+    ref = _ref(b)
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt))
+    idx, Kc, Vc = empty((sum(ks),), "i32"), empty((sum(ks), d)), empty((sum(ks), d))
+    flags = to_gpu(np.zeros(P, np.int32))
+    K.kvs_init_topk(ctx, bt, to_gpu(b["Q"]), to_gpu(b["Kz"]), to_gpu(np.stack([r[0] for r in ref])),
+                    to_gpu(np.stack([r[1] for r in ref])), idx, Kc, Vc, flags, ws)
+    ig, kg, vg, fg = host(idx), host(Kc), host(Vc), host(flags)
+    off = 0
+    for p in range(P):
+        k = ks[p]
+        Q, Kz = b["Q"][p], b["Kz"][p]
+        li = O.log_importance(Q, Kz, ref[p][1], b["scale"])
+        sel = ig[off:off + k]
+        assert np.all(np.diff(sel) > 0), "indices must be ascending and distinct"
+        nd = _check_topk(sel, li, k)
+        np.testing.assert_array_equal(kg[off:off + k], Kz[sel])
+        V, _, ok = O.ridge_values(Q, ref[p][0], Kz[sel], b["scale"])
+        ev = rel(vg[off:off + k], V)
+        say(f"   p={p} k={k} tie-swaps={nd} relVc={ev:.2e} flags={fg[p]}")
+        assert ok and fg[p] == 0 and ev <= 1e-4
+        off += k
+
+
+@pytest.mark.parametrize("name,steps", [("cfg0", 8), ("cfg1", 4)])
+def test_lbfgs_steps_match_oracle(name, steps):
+    w = WORKLOADS[0 if name == "cfg0" else 1]
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    ref = _ref(b)
+    starts = []
+    for p in range(P):
+        idx, Kc, Vc, ok = O.init_select_fit(b["Q"][p], b["Kz"][p], ref[p][0], ref[p][1], w.k0, b["scale"])
+        starts.append((Kc.astype(np.float32), Vc.astype(np.float32)))
+    ks = [w.k0] * P
+    o = K.opts(iters=steps)
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt, o))
+    state = workspace(K.lbfgs_state_bytes(bt, o))
+    Kc = to_gpu(np.concatenate([s[0] for s in starts]))
+    Vc = to_gpu(np.concatenate([s[1] for s in starts]))
+    Qg, Yg, lg = to_gpu(b["Q"]), to_gpu(np.stack([r[0] for r in ref])), to_gpu(np.stack([r[1] for r in ref]))
+    loss, flags = empty((P,)), to_gpu(np.zeros(P, np.int32))
+    K.kvs_lbfgs_init(ctx, bt, o, Qg, Yg, lg, Kc, Vc, 1, loss, flags, state, ws)
+    gl = [host(loss).copy()]
+    for _ in range(steps):
+        K.kvs_lbfgs_step(ctx, bt, o, Qg, Yg, lg, Kc, Vc, loss, flags, state, ws)
+        gl.append(host(loss).copy())
+    kg, fg = host(Kc), host(flags)
+    for p in range(P):
+        Q, (Y32, l32), (K0, V0) = b["Q"][p], ref[p], starts[p]
+        f = lambda x: O.loss(Q, Y32, l32, x, V0, b["scale"])
+        fgr = lambda x: O.loss_grad(Q, Y32, l32, x, V0, b["scale"])[:2]
+        L0, g0 = fgr(K0)
+        st = O.LbfgsState(x=K0.astype(np.float64), L=L0, g=g0)
+        ol = [L0]
+        for _ in range(steps):
+            O.lbfgs_iteration(f, fgr, st, O.LbfgsOptions())
+            ol.append(st.L)
+        errs = [abs(gl[t][p] - ol[t]) / ol[t] for t in range(steps + 1)]
+        ek = rel(kg[p * w.k0:(p + 1) * w.k0], st.x)
+        say(f"   p={p} oracle={np.round(ol, 4).tolist()}")
+        say(f"   p={p} gpu   ={np.round([g[p] for g in gl], 4).tolist()}")
+        say(f"   p={p} rel loss err per step={['%.1e' % e for e in errs]} relKc={ek:.2e} flags={fg[p]}")
+        assert fg[p] == 0
+        assert max(errs[:4]) <= 1e-4
+        assert ek <= 1e-3
+
+
+def test_compress_cfg0_end_to_end():
+    w = WORKLOADS[0]
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    o = K.opts(iters=w.T)
+    bt = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt, o))
+    Kc, Vc = empty((w.k0 * P, d)), empty((w.k0 * P, d))
+    loss, mse, l0 = empty((P,)), empty((P,)), empty((P,))
+    flags = to_gpu(np.zeros(P, np.int32))
+    K.kvs_compress(ctx, bt, o, to_gpu(b["Q"]), to_gpu(b["Kz"]), to_gpu(b["Vz"]), Kc, Vc, loss, mse, l0,
+                   flags, ws)
+    lg, mg, l0g, fg = host(loss), host(mse), host(l0), host(flags)
+    r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], w.k0, b["scale"], O.CompressOptions(iters=w.T))
+    say(f"[compress cfg0] init gpu={l0g[0]:.6g} oracle={r['init_loss']:.6g}; "
+        f"final gpu={lg[0]:.6g} oracle={r['loss']:.6g}; mse gpu={mg[0]:.4e} oracle={r['mse']:.4e} flags={fg[0]}")
+    assert abs(l0g[0] - r["init_loss"]) <= 1e-4 * r["init_loss"]
+    assert abs(lg[0] - r["loss"]) <= 0.02 * r["loss"]
+    assert fg[0] == 0
+    # the returned pair reproduces the reported loss
+    Y, l = O.reference_attention(b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"])
+    Lchk = O.loss(b["Q"][0], Y, l, host(Kc), host(Vc), b["scale"])
+    assert abs(Lchk - lg[0]) <= 1e-3 * Lchk
+
+
+def test_compress_cfg1_end_to_end():
+    path = os.path.join(HERE, "golden", "oracle_compress_cfg1.json")
+    gold = json.load(open(path))
+    w = WORKLOADS[1]
+    b = make_batch(w, gold["seed"])
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    o = K.opts(iters=gold["iters"])
+    bt = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt, o))
+    Kc, Vc = empty((w.k0 * P, d)), empty((w.k0 * P, d))
+    loss, mse, l0 = empty((P,)), empty((P,)), empty((P,))
+    flags = to_gpu(np.zeros(P, np.int32))
+    K.kvs_compress(ctx, bt, o, to_gpu(b["Q"]), to_gpu(b["Kz"]), to_gpu(b["Vz"]), Kc, Vc, loss, mse, l0,
+                   flags, ws)
+    lg, l0g, fg = host(loss), host(l0), host(flags)
+    for p, g in enumerate(gold["problems"]):
+        say(f"[compress cfg1] p={p} init gpu={l0g[p]:.6g} oracle={g['init_loss']:.6g}; "
+            f"final gpu={lg[p]:.6g} oracle={g['final_loss']:.6g} ratio={lg[p] / g['final_loss']:.4f} flags={fg[p]}")
+        assert abs(l0g[p] - g["init_loss"]) <= 1e-4 * g["init_loss"]
+        assert abs(lg[p] - g["final_loss"]) <= 0.02 * g["final_loss"]
+        assert fg[p] & ~K.KVS_FLAG_NONDESCENT == 0
+
+
+def test_pilot_allocation_bit_exact():
+    w = tiny_workload(d=64, N=300, m=20, g=2, F=30, layers=3, kv_heads=2, k0=40)
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    pilot = 20
+    o = K.opts(iters=pilot)
+    bt = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt, o))
+    pm = empty((P,))
+    k_out = K.kvs_pilot_allocate(ctx, bt, o, pilot, 0.5, 1, Z, to_gpu(b["Q"]), to_gpu(b["Kz"]),
+                                 to_gpu(b["Vz"]), pm, ws)
+    mg = host(pm).astype(np.float64)
+    want = O.allocate_budget(list(mg), w.k0 * P, 0.5, 1, Z)
+    mse, ks, _ = O.pilot_allocate([(b["Q"][p], b["Kz"][p], b["Vz"][p]) for p in range(P)], w.k0,
+                                  b["scale"], O.CompressOptions(), pilot_iters=pilot, k_max=Z)
+    say(f"[pilot] gpu mse={np.round(mg, 6).tolist()}\n        oracle mse={np.round(mse, 6).tolist()}")
+    say(f"        k gpu={k_out.tolist()} oracle-alloc(gpu mse)={want} oracle-alloc(oracle mse)={ks}")
+    assert k_out.tolist() == want
+    assert sum(k_out) == w.k0 * P
+    for a, bb in zip(mg, mse):
+        assert abs(a - bb) <= 0.02 * bb

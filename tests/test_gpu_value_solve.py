@@ -1,0 +1,94 @@
+"""GPU parity: closed-form ridge value solve through the C ABI (bar 1e-4)."""
+import numpy as np
+import pytest
+
+import attention_distillation_amd as K
+from oracle import kvsculpt as O
+from synth import WORKLOADS, make_batch, tiny_workload
+from tests.gpu_common import empty, host, rel, say, to_gpu, workspace
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def _setup(w, kfun, perturb=0.0, seed=0):
+    b = make_batch(w, seed)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    s = b["scale"]
+    rng = np.random.default_rng(3)
+    probs = []
+    for p in range(P):
+        Q, Kz, Vz = b["Q"][p], b["Kz"][p], b["Vz"][p]
+        Y, l = O.reference_attention(Q, Kz, Vz, s)
+        Y32, l32 = Y.astype(np.float32), l.astype(np.float32)
+        k = min(kfun(p, Z), Z)
+        idx = O.select_topk(O.log_importance(Q, Kz, l32, s), k)
+        Kc = (Kz[idx] + perturb * rng.standard_normal((k, d))).astype(np.float32)
+        probs.append((Q, Y32, l32, Kc))
+    return b, probs
+
+
+CASES = {
+    "cfg0": (WORKLOADS[0], lambda p, Z: 64, 0.0),
+    "cfg0-perturbed": (WORKLOADS[0], lambda p, Z: 64, 1e-2),
+    "cfg1": (WORKLOADS[1], lambda p, Z: 960, 0.0),
+    "tiny64-ragged": (tiny_workload(d=64, N=80, m=10, g=1, F=40, layers=3), lambda p, Z: [1, 17, 70][p], 0.0),
+    "tiny128-ragged": (tiny_workload(d=128, N=330, m=10, g=2, F=40, layers=1, kv_heads=3),
+                       lambda p, Z: [100, 3, 96][p], 0.0),
+    # more compressed pairs than training queries: A^T A is rank deficient
+    # and only mu keeps it definite (happens after budget reallocation)
+    "rank-deficient": (tiny_workload(d=128, N=330, m=10, g=2, F=40, layers=1, kv_heads=2),
+                       lambda p, Z: [320, 150][p], 0.0),
+}
+
+
+@pytest.mark.parametrize("name", [pytest.param(c, marks=pytest.mark.xfail(
+    reason="fp32 Cholesky loses accuracy when k > n (rank-deficient Gram)", strict=False))
+    if c == "rank-deficient" else c for c in CASES])
+def test_value_solve_matches_oracle(name):
+    w, kfun, pert = CASES[name]
+    b, probs = _setup(w, kfun, pert)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    ks = [pr[3].shape[0] for pr in probs]
+    say(f"[value-solve] case={name} P={P} n={n} d={d} k={ks}")
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt))
+    Vc = empty((sum(ks), d))
+    flags = to_gpu(np.zeros(P, np.int32))
+    K.kvs_value_solve(ctx, bt, to_gpu(b["Q"]), to_gpu(np.stack([p[1] for p in probs])),
+                      to_gpu(np.stack([p[2] for p in probs])),
+                      to_gpu(np.concatenate([p[3] for p in probs])), Vc, flags, ws)
+    Vg, fg = host(Vc), host(flags)
+    off = 0
+    for p, (Q, Y32, l32, Kc) in enumerate(probs):
+        k = Kc.shape[0]
+        V, mu, ok = O.ridge_values(Q, Y32, Kc, b["scale"])
+        e = rel(Vg[off:off + k], V)
+        say(f"   p={p} k={k} mu={mu:.3e} relVc={e:.2e} flags={fg[p]}")
+        assert ok and fg[p] == 0 and e <= TOL
+        off += k
+
+
+def test_value_solve_flags_nonfinite_keys_and_keeps_vc():
+    w = tiny_workload(d=64, N=80, m=10, g=1, F=40, layers=2)
+    b, probs = _setup(w, lambda p, Z: 20)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    Kc = np.concatenate([p[3] for p in probs])
+    Kc[25, 3] = np.nan                       # problem 1 only
+    bt = K.Batch(P, d, Z, n, k=[20, 20], scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt))
+    Vc = to_gpu(np.full((40, d), 7.0, np.float32))
+    flags = to_gpu(np.zeros(P, np.int32))
+    K.kvs_value_solve(ctx, bt, to_gpu(b["Q"]), to_gpu(np.stack([p[1] for p in probs])),
+                      to_gpu(np.stack([p[2] for p in probs])), to_gpu(Kc), Vc, flags, ws)
+    Vg, fg = host(Vc), host(flags)
+    say(f"[value-solve-nan] flags={fg}")
+    assert fg[0] == 0 and fg[1] & K.KVS_FLAG_CHOLESKY
+    assert np.all(Vg[20:] == 7.0)
+    V0, _, _ = O.ridge_values(b["Q"][0], probs[0][1], probs[0][3], b["scale"])
+    assert rel(Vg[:20], V0) <= TOL
