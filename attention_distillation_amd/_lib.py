@@ -24,7 +24,7 @@ ENTRY_POINTS = (
     "kvs_create", "kvs_destroy", "kvs_status_string", "kvs_last_error", "kvs_default_opts",
     "kvs_workspace_bytes", "kvs_lbfgs_state_bytes", "kvs_reference_attn", "kvs_init_topk",
     "kvs_loss_grad", "kvs_value_solve", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_compress",
-    "kvs_pilot_allocate", "kvs_allocate_budget",
+    "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_profile_enable", "kvs_profile_read",
 )
 
 
@@ -38,6 +38,11 @@ class KvsBatch(ctypes.Structure):
     _fields_ = [("P", c_int32), ("d", c_int32), ("Z", c_int32), ("n", c_int32),
                 ("k", POINTER(c_int32)), ("scale", c_double), ("lambda_", c_double),
                 ("ridge_rel", c_double)]
+
+
+class KvsKernelStats(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", c_int64), ("total_ms", c_double),
+                ("flops", c_double), ("bytes", c_double)]
 
 
 class KvsOpts(ctypes.Structure):
@@ -81,6 +86,8 @@ def load(path: str | None = None):
                                          V, V, c_size_t]),
         "kvs_allocate_budget": (c_int32, [POINTER(c_double), c_int32, c_int64, c_double, c_int32,
                                           c_int32, POINTER(c_int32)]),
+        "kvs_profile_enable": (c_int32, [V, c_int32]),
+        "kvs_profile_read": (c_int32, [V, POINTER(KvsKernelStats), c_int32, POINTER(c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -241,3 +248,25 @@ def kvs_allocate_budget(mse, K_total, alpha=0.5, k_min=1, k_max=1 << 30):
     if st != 0:
         raise KvsError("kvs_allocate_budget", st, "invalid budget request")
     return out
+
+
+PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",
+                   "hist_dots", "direction", "importance", "ref_attn_fwd", "merge")
+
+
+def kvs_profile_enable(ctx, enable=True, kernels=None):
+    """Enable per-kernel event timing (all kernels, or the named ones)."""
+    mask = 0
+    if enable:
+        mask = -1 if kernels is None else sum(1 << PROFILE_CLASSES.index(k) for k in kernels)
+    ctx.check("kvs_profile_enable", ctx.lib.kvs_profile_enable(ctx.handle, mask))
+
+
+def kvs_profile_read(ctx):
+    """Per-kernel totals since the last enable: {name: dict(launches, ms, flops, bytes)}."""
+    arr = (KvsKernelStats * 32)()
+    cnt = c_int32(0)
+    ctx.check("kvs_profile_read", ctx.lib.kvs_profile_read(ctx.handle, arr, 32, ctypes.byref(cnt)))
+    return {arr[i].name.decode(): dict(launches=int(arr[i].launches), ms=float(arr[i].total_ms),
+                                       flops=float(arr[i].flops), bytes=float(arr[i].bytes))
+            for i in range(cnt.value)}

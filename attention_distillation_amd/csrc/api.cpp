@@ -14,11 +14,39 @@
 #include "kvs_internal.h"
 #include "plan.h"
 
+namespace kvs {
+enum ProfClass {
+  PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
+  PROF_IMP, PROF_REF, PROF_MERGE, PROF_NCLASS
+};
+const char* const kProfNames[PROF_NCLASS] = {
+    "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
+    "direction", "importance", "ref_attn_fwd", "merge"};
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct ProfAcc {
+  long long launches = 0;
+  double ms = 0, flops = 0, bytes = 0;
+};
+}  // namespace kvs
+
 struct kvs_ctx_s {
   hipStream_t stream = nullptr;
   std::string err;
   int device = 0;
   bool logit_f64 = true;
+  bool prof = false;
+  int prof_mask = 0;
+  std::vector<hipEvent_t> pool;
+  std::vector<kvs::ProfRec> pending;
+  kvs::ProfAcc acc[kvs::PROF_NCLASS];
+  ~kvs_ctx_s() {
+    for (auto& r : pending) { pool.push_back(r.a); pool.push_back(r.b); }
+    for (auto e : pool) hipEventDestroy(e);
+  }
 };
 
 namespace kvs {
@@ -39,6 +67,65 @@ kvs_status hip_check(kvs_ctx c, const char* where) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(c, KVS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
   return KVS_OK;
+}
+
+hipEvent_t prof_event(kvs_ctx c) {
+  if (!c->pool.empty()) {
+    hipEvent_t e = c->pool.back();
+    c->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Fold completed launch timings into the per-class totals (stream must be idle
+// or the events complete).
+void prof_drain(kvs_ctx c) {
+  for (auto& r : c->pending) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      ProfAcc& a = c->acc[r.cls];
+      a.launches += 1;
+      a.ms += ms;
+      a.flops += r.flops;
+      a.bytes += r.bytes;
+    }
+    c->pool.push_back(r.a);
+    c->pool.push_back(r.b);
+  }
+  c->pending.clear();
+}
+
+// RAII timer around one kernel launch on the context stream (no-op unless
+// profiling is enabled).
+struct Prof {
+  kvs_ctx c;
+  ProfRec r{};
+  bool on;
+  Prof(kvs_ctx ctx, int cls, double flops, double bytes)
+      : c(ctx), on(ctx->prof && ((ctx->prof_mask >> cls) & 1)) {
+    if (!on) return;
+    r.cls = cls; r.flops = flops; r.bytes = bytes;
+    r.a = prof_event(c);
+    r.b = prof_event(c);
+    if (!r.a || !r.b) { on = false; return; }
+    hipEventRecord(r.a, c->stream);
+  }
+  ~Prof() {
+    if (!on) return;
+    hipEventRecord(r.b, c->stream);
+    c->pending.push_back(r);
+  }
+};
+
+// Algorithmic work of the contraction kernels over the active problems.
+double sum_k(const Plan& pl, const std::vector<int>* hs, int want) {
+  double s = 0;
+  for (int p = 0; p < pl.P; ++p)
+    if (!hs || (*hs)[p] == want) s += pl.info[p].k;
+  return s;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -77,7 +164,10 @@ void run_reference(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
   f.shift = nullptr; f.St = nullptr;
   f.Opart = at<float>(ws, pl.r_Opart); f.Mpart = at<float>(ws, pl.r_Mpart); f.Lpart = at<float>(ws, pl.r_Lpart);
   f.info = nullptr; f.P = pl.P; f.n = pl.n; f.C = pl.Cref; f.kuni = pl.Z; f.kmax = pl.Z; f.scale = b->scale;
-  launch_attn_fwd(f, pl.d, false, ctx->stream);
+  {
+    Prof pr(ctx, PROF_REF, 4.0 * pl.n * pl.Z * pl.d * pl.P, 4.0 * pl.P * (2.0 * pl.n * pl.d + 2.0 * pl.Z * pl.d));
+    launch_attn_fwd(f, pl.d, false, ctx->stream);
+  }
   MergeArgs m{};
   m.Opart = f.Opart; m.Mpart = f.Mpart; m.Lpart = f.Lpart; m.st = nullptr; m.active_mask = 0;
   m.Yout = Y; m.lse_out = lse; m.P = pl.P; m.n = pl.n; m.C = pl.Cref; m.lambda = b->lambda;
@@ -89,14 +179,21 @@ void run_reference(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
 // partials, then finalises per-problem losses in the given mode.
 void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Y,
                  const float* lse, const float* K, const float* dir, const float* V, LbState* st,
-                 int mask, int fin_mode, float* loss, float* mse, const kvs_opts* o, void* ws) {
+                 int mask, int fin_mode, float* loss, float* mse, const kvs_opts* o, void* ws,
+                 const std::vector<int>* hs = nullptr, int want = 0) {
   FwdArgs f{};
   f.Q = Q; f.K = K; f.V = V; f.dir = dir; f.st = st; f.active_mask = mask;
   f.shift = lse; f.St = at<float>(ws, pl.r_St);
   f.Opart = at<float>(ws, pl.r_Opart); f.Mpart = at<float>(ws, pl.r_Mpart); f.Lpart = at<float>(ws, pl.r_Lpart);
   f.info = at<ProbInfo>(ws, pl.r_info); f.P = pl.P; f.n = pl.n; f.C = pl.C; f.kuni = 0; f.kmax = pl.kmax;
   f.scale = b->scale;
-  launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+  {
+    const double ks = sum_k(pl, hs, want);
+    const double np = hs ? 0 : pl.P;
+    Prof pr(ctx, PROF_FWD, 4.0 * pl.n * pl.d * ks,
+            4.0 * (ks * pl.d * (dir ? 3.0 : 2.0) + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
+    launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+  }
   MergeArgs m{};
   m.Opart = f.Opart; m.Mpart = f.Mpart; m.Lpart = f.Lpart; m.st = st; m.active_mask = mask;
   m.Y = Y; m.lse = lse; m.G = at<float>(ws, pl.r_G); m.e = at<float>(ws, pl.r_e);
@@ -113,13 +210,18 @@ void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q
 
 // Backward from the last forward's stored scores into grad (scaled, reduced).
 void run_backward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* V,
-                  LbState* st, int mask, float* grad, void* ws) {
+                  LbState* st, int mask, float* grad, void* ws, const std::vector<int>* hs = nullptr,
+                  int want = 0) {
   BwdArgs bw{};
   bw.Q = Q; bw.St = at<float>(ws, pl.r_St); bw.G = at<float>(ws, pl.r_G); bw.e = at<float>(ws, pl.r_e);
   bw.crow = at<float>(ws, pl.r_crow); bw.K = nullptr; bw.V = V; bw.st = st; bw.active_mask = mask;
   bw.dKpart = at<float>(ws, pl.r_dK); bw.info = at<ProbInfo>(ws, pl.r_info);
   bw.P = pl.P; bw.n = pl.n; bw.Cn = pl.Cn; bw.kmax = pl.kmax; bw.ktot = (int)pl.ktot;
-  launch_attn_bwd(bw, pl.d, ctx->stream);
+  {
+    const double ks = sum_k(pl, hs, want);
+    Prof pr(ctx, PROF_BWD, 4.0 * pl.n * pl.d * ks, 4.0 * (ks * pl.npad + ks * pl.d * (1.0 + pl.Cn)));
+    launch_attn_bwd(bw, pl.d, ctx->stream);
+  }
   GradReduceArgs gr{};
   gr.dKpart = bw.dKpart; gr.grad = grad; gr.st = st; gr.active_mask = mask; gr.info = bw.info;
   gr.P = pl.P; gr.Cn = pl.Cn; gr.ktot = (int)pl.ktot; gr.scale = b->scale;
@@ -135,7 +237,15 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   g.St = at<float>(ws, pl.r_St); g.e = at<float>(ws, pl.r_e); g.Y = Y; g.st = st; g.active_mask = mask;
   g.Mpart = pl.Cg > 1 ? at<float>(ws, pl.r_Mg) : M; g.info = at<ProbInfo>(ws, pl.r_info);
   g.P = pl.P; g.n = pl.n; g.Cg = pl.Cg; g.kpadmax = pl.kpadmax; g.mtot = pl.mtot;
-  launch_gram(g, pl.d, ctx->stream);
+  {
+    double fl = 0, by = 0;
+    for (const auto& q : pl.info) {
+      fl += (double)pl.n * q.k * (q.k + 1) + 2.0 * pl.n * q.k * pl.d;
+      by += 4.0 * ((double)q.k * pl.npad + (double)pl.n * pl.d + (double)(q.kpad + pl.d) * q.kpad * pl.Cg);
+    }
+    Prof pr(ctx, PROF_GRAM, fl, by);
+    launch_gram(g, pl.d, ctx->stream);
+  }
   GramReduceArgs r{};
   r.Mpart = g.Mpart; r.M = M; r.trpart = at<double>(ws, pl.r_tr); r.st = st; r.active_mask = mask;
   r.info = g.info; r.P = pl.P; r.Cg = pl.Cg; r.kpadmax = pl.kpadmax; r.mtot = pl.mtot;
@@ -147,13 +257,31 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   launch_mu(c, ctx->stream);
   const int KT = pl.kpadmax / kTile;
   for (int j = 0; j < KT; ++j) {
-    launch_potrf_panel(c, pl.d, j, ctx->stream);
-    launch_trailing(c, pl.d, j, ctx->stream);
+    {
+      Prof pr(ctx, PROF_POTRF, 0, 0);
+      launch_potrf_panel(c, pl.d, j, ctx->stream);
+    }
+    {
+      double fl = 0;
+      for (const auto& q : pl.info) {
+        const int KTp = q.kpad / kTile;
+        if (j >= KTp) continue;
+        const double rows = (double)(q.kpad + pl.d) - 64.0 * (j + 1), cols = (double)q.kpad - 64.0 * (j + 1);
+        fl += 2.0 * 64.0 * (rows * cols - cols * (cols - 64.0) / 2.0);
+      }
+      Prof pr(ctx, PROF_TRAIL, fl, 0);
+      launch_trailing(c, pl.d, j, ctx->stream);
+    }
   }
   BackArgs bk{};
   bk.M = M; bk.X = at<float>(ws, pl.r_X); bk.Vc = Vc; bk.info_out = c.info_out; bk.flags = flags;
   bk.st = st; bk.active_mask = mask; bk.info = g.info; bk.P = pl.P;
-  launch_back_subst(bk, pl.d, ctx->stream);
+  {
+    double fl = 0;
+    for (const auto& q : pl.info) fl += 1.0 * q.kpad * q.kpad * pl.d;
+    Prof pr(ctx, PROF_BACK, fl, 0);
+    launch_back_subst(bk, pl.d, ctx->stream);
+  }
 }
 
 // Select+Fit: importance, top-k, gather, then the ridge fit at the selected keys.
@@ -165,7 +293,10 @@ void run_init_topk(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
   ia.Mpart = at<float>(ws, pl.r_imp);
   ia.Spart = ia.Mpart + (size_t)pl.Cq * pl.P * pl.Z;
   ia.P = pl.P; ia.n = pl.n; ia.Z = pl.Z; ia.Cq = pl.Cq; ia.scale = b->scale;
-  launch_importance(ia, pl.d, ctx->stream);
+  {
+    Prof pr(ctx, PROF_IMP, 2.0 * pl.n * pl.Z * pl.d * pl.P, 4.0 * pl.P * ((double)pl.n * pl.d + (double)pl.Z * pl.d));
+    launch_importance(ia, pl.d, ctx->stream);
+  }
   TopkArgs ta{};
   ta.Mpart = ia.Mpart; ta.Spart = ia.Spart; ta.Kz = Kz; ta.idx = idx; ta.Kc = Kc;
   ta.info = at<ProbInfo>(ws, pl.r_info); ta.P = pl.P; ta.Z = pl.Z; ta.Cq = pl.Cq; ta.d = pl.d;
@@ -207,7 +338,10 @@ void lb_eval_at_x(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opt
   h.x = Kc; h.p = B.p; h.g = B.g; h.gnew = B.gnew; h.S = B.S; h.Yh = B.Yh; h.st = B.st;
   h.active_mask = kAll; h.part = B.hpart; h.info = at<ProbInfo>(ws, pl.r_info); h.P = pl.P;
   h.d = pl.d; h.ktot = (int)pl.ktot; h.nwg = pl.nwg; h.mode = 1;
-  launch_hist_dots(h, ctx->stream);
+  {
+    Prof pr(ctx, PROF_HIST, 0, 0);
+    launch_hist_dots(h, ctx->stream);
+  }
   PrepArgs pa{};
   pa.st = B.st; pa.part = B.hpart; pa.nwg = pl.nwg; pa.P = pl.P; pa.mode = prep_mode;
   pa.history = pl.H; pa.curv_eps = 1e-10; pa.select_status = 0; pa.flags = nullptr;
@@ -224,26 +358,34 @@ kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const k
   DirArgs da{};
   da.p = B.p; da.g = B.g; da.S = B.S; da.Yh = B.Yh; da.st = B.st; da.info = at<ProbInfo>(ws, pl.r_info);
   da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nwg = pl.nwg;
-  launch_direction(da, ctx->stream);
+  {
+    Prof pr(ctx, PROF_DIR, 0, 0);
+    launch_direction(da, ctx->stream);
+  }
   hs.resize(pl.P);
   *any_fail = false;
   for (int round = 0; round < o->max_backtracks; ++round) {
-    run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws);
+    run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws,
+                round ? &hs : nullptr, ST_SEARCH);
     if (hipMemcpyAsync(hs.data(), B.status_view, sizeof(int) * pl.P, hipMemcpyDeviceToHost,
                        ctx->stream) != hipSuccess ||
         hipStreamSynchronize(ctx->stream) != hipSuccess)
       return fail(ctx, KVS_ERR_HIP, "line search: %s", hipGetErrorString(hipGetLastError()));
+    if (ctx->prof) prof_drain(ctx);
     bool searching = false;
     for (int v : hs) searching |= (v == ST_SEARCH);
     if (!searching) break;
   }
   for (int v : hs) *any_fail |= (v == ST_FAIL);
-  run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, B.gnew, ws);
+  run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, B.gnew, ws, &hs, ST_ACCEPT);
   HistArgs h{};
   h.x = Kc; h.p = B.p; h.g = B.g; h.gnew = B.gnew; h.S = B.S; h.Yh = B.Yh; h.st = B.st;
   h.active_mask = 1 << ST_ACCEPT; h.part = B.hpart; h.info = at<ProbInfo>(ws, pl.r_info);
   h.P = pl.P; h.d = pl.d; h.ktot = (int)pl.ktot; h.nwg = pl.nwg; h.mode = 0;
-  launch_hist_dots(h, ctx->stream);
+  {
+    Prof pr(ctx, PROF_HIST, 0, 0);
+    launch_hist_dots(h, ctx->stream);
+  }
   PrepArgs pa{};
   pa.st = B.st; pa.part = B.hpart; pa.nwg = pl.nwg; pa.P = pl.P; pa.mode = 0;
   pa.history = pl.H; pa.curv_eps = 1e-10; pa.select_status = 0; pa.flags = nullptr;
@@ -501,6 +643,41 @@ kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o
   s = kvs_allocate_budget(md.data(), pl.P, K, alpha, k_min, k_max, k_out);
   if (s != KVS_OK) return fail(ctx, s, "%s: budget split failed (non-finite pilot MSE?)", fn);
   return hip_check(ctx, fn);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+kvs_status kvs_profile_enable(kvs_ctx ctx, int32_t enable) {
+  if (!ctx) return KVS_ERR_INVALID;
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return fail(ctx, KVS_ERR_HIP, "kvs_profile_enable: %s", hipGetErrorString(hipGetLastError()));
+  prof_drain(ctx);
+  for (auto& a : ctx->acc) a = ProfAcc();
+  ctx->prof = enable != 0;
+  ctx->prof_mask = enable;
+  return KVS_OK;
+}
+
+kvs_status kvs_profile_read(kvs_ctx ctx, kvs_kernel_stats* out, int32_t max, int32_t* count) {
+  if (!ctx || !count || (max > 0 && !out)) return KVS_ERR_INVALID;
+  if (hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return fail(ctx, KVS_ERR_HIP, "kvs_profile_read: %s", hipGetErrorString(hipGetLastError()));
+  prof_drain(ctx);
+  int n = 0;
+  for (int c = 0; c < PROF_NCLASS && n < max; ++c) {
+    if (ctx->acc[c].launches == 0) continue;
+    kvs_kernel_stats& o = out[n++];
+    memset(&o, 0, sizeof o);
+    snprintf(o.name, sizeof o.name, "%s", kProfNames[c]);
+    o.launches = ctx->acc[c].launches;
+    o.total_ms = ctx->acc[c].ms;
+    o.flops = ctx->acc[c].flops;
+    o.bytes = ctx->acc[c].bytes;
+  }
+  *count = n;
+  return KVS_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,208 @@
+"""Throughput of the KVSculpt optimizer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+A step is one whole kvs_compress call on one batch of synthetic problems:
+compress-zone reference attention, Select+Fit init (importance, top-k, ridge
+fit), then T L-BFGS iterations (direction, Armijo trials, loss/gradient) with
+the ridge value re-solve every 5 iterations.  With --config 2..4 the step
+also runs the 60-iteration pilot and the budget reallocation before the main
+run at ragged k.  The metric is problem-iterations per second,
+P * T * K / (wall time of the K timed steps), inputs resident in HBM.
+
+Printed: one JSON line (stdout).  It carries the live roofline of the
+dominant kernel (HIP events on the library's stream over the timed steps)
+and the float64 oracle timed on a bounded sample on the host CPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks
+PEAK_FP32_MFMA = 157.3e12
+PEAK_FP64_MFMA = 78.6e12
+PEAK_HBM = 8.0e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def mixed_fwd_peak():
+    """Forward kernel: half its flops (Q Kc^T) on fp64 MFMA, half (A Vc) on fp32."""
+    return 1.0 / (0.5 / PEAK_FP64_MFMA + 0.5 / PEAK_FP32_MFMA)
+
+
+def cpu_baseline(w, b, seconds):
+    """Float64 oracle on problem 0 of the same workload (host cores)."""
+    from oracle import kvsculpt as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
+    Y, l = O.reference_attention(Q, Kz, Vz, s)
+    t0 = time.perf_counter()
+    O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=0), Y=Y, lse=l)
+    t_init = time.perf_counter() - t0
+    # size the sample to roughly `seconds` of iteration work (multiple of 5: whole value-solve periods)
+    t0 = time.perf_counter()
+    O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=5), Y=Y, lse=l)
+    t5 = time.perf_counter() - t0 - t_init
+    iters = int(max(5, min(w.T, 5 * round(seconds / max(t5, 1e-3)))))
+    if iters > 5:
+        t0 = time.perf_counter()
+        O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=iters), Y=Y, lse=l)
+        t_it = time.perf_counter() - t0 - t_init
+    else:
+        t_it = t5
+    return {"value": iters / t_it, "unit": "problem-iterations/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{w.name} problem 0 of {w.P}, {iters} L-BFGS iterations with value "
+                      f"solves every 5 (Select+Fit init excluded), float64 NumPy/SciPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--ratio", type=float, default=None, help="compression ratio r (configs 2..4)")
+    ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py measures one GPU: the problems of a batch are independent and this build "
+            "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
+        sys.exit(2)
+
+    import torch
+    import attention_distillation_amd as K
+    from synth import WORKLOADS, make_batch
+
+    w = WORKLOADS[args.config]
+    if args.ratio is not None:
+        w = w.with_ratio(args.ratio)
+    T = w.T if args.iters is None else args.iters
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}: P={w.P} n={w.n} Z={w.Z} d={w.d} k0={w.k0} T={T}")
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    Q = torch.from_numpy(b["Q"]).to(dev)
+    Kz = torch.from_numpy(b["Kz"]).to(dev)
+    Vz = torch.from_numpy(b["Vz"]).to(dev)
+
+    ctx = K.Context()
+    o = K.opts(iters=T)
+    pilot = w.pilot if w.pilot else 0
+    kmax_bytes = 0
+    if pilot:
+        # budget the workspace for the widest ragged split the allocator can return
+        bt_pilot = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
+        kmax_bytes = K.workspace_bytes(bt_pilot, K.opts(iters=pilot))
+    bt = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
+    ktot = w.k0 * P
+
+    def alloc(batch):
+        nb = max(K.workspace_bytes(batch, o), kmax_bytes)
+        return torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    ws = alloc(bt)
+    Kc = torch.empty((ktot, d), dtype=torch.float32, device=dev)
+    Vc = torch.empty((ktot, d), dtype=torch.float32, device=dev)
+    loss = torch.empty(P, dtype=torch.float32, device=dev)
+    mse = torch.empty(P, dtype=torch.float32, device=dev)
+    l0 = torch.empty(P, dtype=torch.float32, device=dev)
+    flags = torch.zeros(P, dtype=torch.int32, device=dev)
+    pm = torch.empty(P, dtype=torch.float32, device=dev)
+    state = {"ws": ws, "k": None}
+
+    def step():
+        batch = bt
+        if pilot:
+            k_out = K.kvs_pilot_allocate(ctx, bt, K.opts(iters=pilot), pilot, 0.5, 1, Z, Q, Kz, Vz, pm,
+                                         state["ws"])
+            batch = K.Batch(P, d, Z, n, k=k_out, scale=b["scale"])
+            need = K.workspace_bytes(batch, o)
+            if need > state["ws"].numel():
+                state["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+            state["k"] = k_out
+        flags.zero_()
+        K.kvs_compress(ctx, batch, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, state["ws"])
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dominant = ["attn_fwd", "attn_bwd"]
+    K.kvs_profile_enable(ctx, True, kernels=dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = K.kvs_profile_read(ctx)
+    K.kvs_profile_enable(ctx, False)
+
+    # per-kernel breakdown of one further (untimed) step
+    K.kvs_profile_enable(ctx, True)
+    step()
+    breakdown = K.kvs_profile_read(ctx)
+    K.kvs_profile_enable(ctx, False)
+    lg, l0g, fg = loss.cpu().numpy(), l0.cpu().numpy(), flags.cpu().numpy()
+
+    iters_total = P * T * args.steps
+    value = iters_total / elapsed
+    ms_step = 1e3 * elapsed / args.steps
+    # dominant kernel = the contraction kernel with the most time in the timed region
+    name = max(stats, key=lambda k: stats[k]["ms"])
+    st = stats[name]
+    avg_s = st["ms"] / st["launches"] / 1e3
+    fl_launch = st["flops"] / st["launches"]
+    peak = mixed_fwd_peak() if name == "attn_fwd" else PEAK_FP32_MFMA
+    achieved = fl_launch / avg_s
+    roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": name, "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
+    for k2 in breakdown:
+        bd = breakdown[k2]
+        log(f"[bench] {k2:14s} launches={bd['launches']:6d} ms={bd['ms']:9.3f} "
+            f"TF/s={bd['flops'] / max(bd['ms'], 1e-9) / 1e9:8.2f}")
+    log(f"[bench] loss init={l0g.tolist()} final={lg.tolist()} flags={fg.tolist()} k={state['k']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        cpu = cpu_baseline(w, b, args.cpu_seconds)
+
+    out = {
+        "metric": "KVSculpt L-BFGS iterations/sec over all layer×KV-head problems; % fp32 MFMA",
+        "value": round(value, 2), "unit": "problem-iterations/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "problems": P, "d": d, "n": n, "Z": Z, "k": w.k0,
+                   "iters": T, "vc_every": 5, "history": 10, "pilot": pilot,
+                   "logits": "fp64 MFMA (stored fp32)", "contractions": "fp32 MFMA"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -195,6 +195,26 @@ kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o
 kvs_status kvs_allocate_budget(const double* mse, int32_t P, int64_t K_total, double alpha,
                                int32_t k_min, int32_t k_max, int32_t* k_out);
 
+/* Opt-in kernel timing, for measurement tools.  While enabled, the library
+ * records a HIP event pair on the context stream around each launch of its
+ * main kernels and accumulates, per kernel, the launch count, the summed
+ * event time and the algorithmic flops / HBM bytes of those launches (the
+ * method's own work, not hardware counters; zero where not tracked).
+ * kvs_profile_enable clears the totals; its argument is 0 (off), -1 (all
+ * kernels) or a bitmask over attn_fwd (bit 0), attn_bwd, gram, potrf_panel,
+ * trailing, back_subst, hist_dots, direction, importance, ref_attn_fwd,
+ * merge (bit 10).  kvs_profile_read synchronises the stream and writes up to
+ * max entries (kernels with launches) to out. */
+typedef struct {
+  char    name[32];
+  int64_t launches;
+  double  total_ms;
+  double  flops;
+  double  bytes;
+} kvs_kernel_stats;
+kvs_status kvs_profile_enable(kvs_ctx ctx, int32_t enable);
+kvs_status kvs_profile_read(kvs_ctx ctx, kvs_kernel_stats* out, int32_t max, int32_t* count);
+
 #ifdef __cplusplus
 }
 #endif
