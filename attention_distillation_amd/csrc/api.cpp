@@ -151,6 +151,7 @@ kvs_status prepare(kvs_ctx ctx, const char* fn, const kvs_batch* b, const kvs_op
   if (ws_bytes < pl->ws_bytes)
     return fail(ctx, KVS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, pl->ws_bytes);
   launch_write_info(at<ProbInfo>(ws, pl->r_info), pl->info.data(), pl->P, ctx->stream);
+  launch_fill_i32(at<int>(ws, pl->r_cnt), 0, 2LL * pl->P, ctx->stream);
   return KVS_OK;
 }
 
@@ -198,20 +199,21 @@ void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q
   m.Opart = f.Opart; m.Mpart = f.Mpart; m.Lpart = f.Lpart; m.st = st; m.active_mask = mask;
   m.Y = Y; m.lse = lse; m.G = at<float>(ws, pl.r_G); m.e = at<float>(ws, pl.r_e);
   m.crow = at<float>(ws, pl.r_crow); m.part = at<double>(ws, pl.r_part);
+  m.counter = at<unsigned>(ws, pl.r_cnt);
   m.P = pl.P; m.n = pl.n; m.C = pl.C; m.lambda = b->lambda;
-  launch_merge(m, pl.d, true, ctx->stream);
-  FinalizeArgs fa{};
-  fa.part = m.part; fa.nblk = pl.nblk; fa.P = pl.P; fa.st = st; fa.loss = loss; fa.mse = mse;
-  fa.n = pl.n; fa.d = pl.d; fa.mode = fin_mode;
-  fa.c1 = o ? o->c1 : 1e-4; fa.shrink = o ? o->shrink : 0.5; fa.max_bt = o ? o->max_backtracks : 30;
-  fa.status_host_view = at<int>(ws, pl.r_status);
-  launch_finalize(fa, ctx->stream);
+  m.fin_mode = fin_mode; m.c1 = o ? o->c1 : 1e-4; m.shrink = o ? o->shrink : 0.5;
+  m.max_bt = o ? o->max_backtracks : 30; m.loss = loss; m.mse = mse;
+  m.status_view = at<int>(ws, pl.r_status);
+  {
+    Prof pr(ctx, PROF_MERGE, 0, 0);
+    launch_merge(m, pl.d, true, ctx->stream);
+  }
 }
 
-// Backward from the last forward's stored scores into grad (scaled, reduced).
+// Backward from the last forward's stored scores: split-n partials of dL/dKc
+// (reduced by the gradient pass that follows).
 void run_backward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* V,
-                  LbState* st, int mask, float* grad, void* ws, const std::vector<int>* hs = nullptr,
-                  int want = 0) {
+                  LbState* st, int mask, void* ws, const std::vector<int>* hs = nullptr, int want = 0) {
   BwdArgs bw{};
   bw.Q = Q; bw.St = at<float>(ws, pl.r_St); bw.G = at<float>(ws, pl.r_G); bw.e = at<float>(ws, pl.r_e);
   bw.crow = at<float>(ws, pl.r_crow); bw.K = nullptr; bw.V = V; bw.st = st; bw.active_mask = mask;
@@ -222,10 +224,14 @@ void run_backward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* 
     Prof pr(ctx, PROF_BWD, 4.0 * pl.n * pl.d * ks, 4.0 * (ks * pl.npad + ks * pl.d * (1.0 + pl.Cn)));
     launch_attn_bwd(bw, pl.d, ctx->stream);
   }
-  GradReduceArgs gr{};
-  gr.dKpart = bw.dKpart; gr.grad = grad; gr.st = st; gr.active_mask = mask; gr.info = bw.info;
-  gr.P = pl.P; gr.Cn = pl.Cn; gr.ktot = (int)pl.ktot; gr.scale = b->scale;
-  launch_grad_reduce(gr, pl.d, ctx->stream);
+}
+
+GradUpdArgs grad_args(const Plan& pl, const kvs_batch* b, void* ws, LbState* st, int mask, int mode) {
+  GradUpdArgs g{};
+  g.dKpart = at<float>(ws, pl.r_dK); g.Cn = pl.Cn; g.scale = b->scale; g.st = st; g.active_mask = mask;
+  g.mode = mode; g.info = at<ProbInfo>(ws, pl.r_info); g.P = pl.P; g.d = pl.d; g.ktot = (int)pl.ktot;
+  g.nch = pl.nchv;
+  return g;
 }
 
 // Ridge value solve from the last forward's stored scores (St, e): Gram with
@@ -251,31 +257,19 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   r.info = g.info; r.P = pl.P; r.Cg = pl.Cg; r.kpadmax = pl.kpadmax; r.mtot = pl.mtot;
   launch_gram_reduce(r, pl.d, ctx->stream);
   CholArgs c{};
-  c.M = M; c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
+  c.M = M; c.Ldiag = at<float>(ws, pl.r_Ldiag); c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
   c.st = st; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
   c.ridge_rel = b->ridge_rel;
   launch_mu(c, ctx->stream);
   const int KT = pl.kpadmax / kTile;
   for (int j = 0; j < KT; ++j) {
-    {
-      Prof pr(ctx, PROF_POTRF, 0, 0);
-      launch_potrf_panel(c, pl.d, j, ctx->stream);
-    }
-    {
-      double fl = 0;
-      for (const auto& q : pl.info) {
-        const int KTp = q.kpad / kTile;
-        if (j >= KTp) continue;
-        const double rows = (double)(q.kpad + pl.d) - 64.0 * (j + 1), cols = (double)q.kpad - 64.0 * (j + 1);
-        fl += 2.0 * 64.0 * (rows * cols - cols * (cols - 64.0) / 2.0);
-      }
-      Prof pr(ctx, PROF_TRAIL, fl, 0);
-      launch_trailing(c, pl.d, j, ctx->stream);
-    }
+    Prof pr(ctx, PROF_POTRF, 0, 0);
+    launch_chol_step(c, pl.d, j, ctx->stream);
   }
   BackArgs bk{};
-  bk.M = M; bk.X = at<float>(ws, pl.r_X); bk.Vc = Vc; bk.info_out = c.info_out; bk.flags = flags;
-  bk.st = st; bk.active_mask = mask; bk.info = g.info; bk.P = pl.P;
+  bk.M = M; bk.Ldiag = c.Ldiag; bk.X = at<float>(ws, pl.r_X); bk.Dinv = at<float>(ws, pl.r_Dinv); bk.Vc = Vc;
+  bk.info_out = c.info_out; bk.flags = flags; bk.st = st; bk.active_mask = mask; bk.info = g.info;
+  bk.P = pl.P; bk.d = pl.d; bk.kpadmax = pl.kpadmax;
   {
     double fl = 0;
     for (const auto& q : pl.info) fl += 1.0 * q.kpad * q.kpad * pl.d;
@@ -310,21 +304,30 @@ constexpr int kAll = 0xF;
 
 struct LbBuffers {
   LbState* st;
-  float *g, *p, *S, *Yh, *gnew;
+  float *g, *p, *S, *Yh;
   double* hpart;
   int* status_view;
 };
 
 LbBuffers lb_in_ws(const Plan& pl, void* ws) {
   return LbBuffers{at<LbState>(ws, pl.r_state), at<float>(ws, pl.r_g), at<float>(ws, pl.r_p),
-                   at<float>(ws, pl.r_S), at<float>(ws, pl.r_Yh), at<float>(ws, pl.r_grad),
-                   at<double>(ws, pl.r_hpart), at<int>(ws, pl.r_status)};
+                   at<float>(ws, pl.r_S), at<float>(ws, pl.r_Yh), at<double>(ws, pl.r_hpart),
+                   at<int>(ws, pl.r_status)};
 }
 
 LbBuffers lb_in_state(const Plan& pl, void* state, void* ws) {
   return LbBuffers{at<LbState>(state, pl.s_state), at<float>(state, pl.s_g), at<float>(state, pl.s_p),
-                   at<float>(state, pl.s_S), at<float>(state, pl.s_Yh), at<float>(ws, pl.r_grad),
-                   at<double>(ws, pl.r_hpart), at<int>(ws, pl.r_status)};
+                   at<float>(state, pl.s_S), at<float>(state, pl.s_Yh), at<double>(ws, pl.r_hpart),
+                   at<int>(ws, pl.r_status)};
+}
+
+void lb_dots(kvs_ctx ctx, const Plan& pl, const LbBuffers& B, void* ws, int mode, int mask) {
+  DotsArgs d{};
+  d.g = B.g; d.S = B.S; d.Yh = B.Yh; d.st = B.st; d.active_mask = mask; d.mode = mode;
+  d.history = pl.H; d.curv_eps = 1e-10; d.part = B.hpart; d.counter = at<unsigned>(ws, pl.r_cnt) + pl.P;
+  d.info = at<ProbInfo>(ws, pl.r_info); d.P = pl.P; d.d = pl.d; d.ktot = (int)pl.ktot; d.nch = pl.nchd;
+  Prof pr(ctx, PROF_HIST, 0, 0);
+  launch_dots(d, ctx->stream);
 }
 
 // Loss and gradient at the current keys for every problem, then the
@@ -333,19 +336,11 @@ void lb_eval_at_x(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opt
                   const float* Y, const float* lse, float* Kc, const float* Vc, const LbBuffers& B,
                   int prep_mode, float* loss_out, float* mse_out, void* ws) {
   run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws);
-  run_backward(ctx, pl, b, Q, Vc, B.st, kAll, B.gnew, ws);
-  HistArgs h{};
-  h.x = Kc; h.p = B.p; h.g = B.g; h.gnew = B.gnew; h.S = B.S; h.Yh = B.Yh; h.st = B.st;
-  h.active_mask = kAll; h.part = B.hpart; h.info = at<ProbInfo>(ws, pl.r_info); h.P = pl.P;
-  h.d = pl.d; h.ktot = (int)pl.ktot; h.nwg = pl.nwg; h.mode = 1;
-  {
-    Prof pr(ctx, PROF_HIST, 0, 0);
-    launch_hist_dots(h, ctx->stream);
-  }
-  PrepArgs pa{};
-  pa.st = B.st; pa.part = B.hpart; pa.nwg = pl.nwg; pa.P = pl.P; pa.mode = prep_mode;
-  pa.history = pl.H; pa.curv_eps = 1e-10; pa.select_status = 0; pa.flags = nullptr;
-  launch_prepare(pa, ctx->stream);
+  run_backward(ctx, pl, b, Q, Vc, B.st, kAll, ws);
+  GradUpdArgs g = grad_args(pl, b, ws, B.st, kAll, 1);
+  g.g = B.g;
+  launch_grad_update(g, ctx->stream);
+  lb_dots(ctx, pl, B, ws, prep_mode, kAll);
 }
 
 // One L-BFGS iteration for every problem: direction, backtracking Armijo
@@ -357,7 +352,7 @@ kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const k
                         const LbBuffers& B, void* ws, bool* any_fail, std::vector<int>& hs) {
   DirArgs da{};
   da.p = B.p; da.g = B.g; da.S = B.S; da.Yh = B.Yh; da.st = B.st; da.info = at<ProbInfo>(ws, pl.r_info);
-  da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nwg = pl.nwg;
+  da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nch = pl.nchv;
   {
     Prof pr(ctx, PROF_DIR, 0, 0);
     launch_direction(da, ctx->stream);
@@ -376,20 +371,18 @@ kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const k
     for (int v : hs) searching |= (v == ST_SEARCH);
     if (!searching) break;
   }
-  for (int v : hs) *any_fail |= (v == ST_FAIL);
-  run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, B.gnew, ws, &hs, ST_ACCEPT);
-  HistArgs h{};
-  h.x = Kc; h.p = B.p; h.g = B.g; h.gnew = B.gnew; h.S = B.S; h.Yh = B.Yh; h.st = B.st;
-  h.active_mask = 1 << ST_ACCEPT; h.part = B.hpart; h.info = at<ProbInfo>(ws, pl.r_info);
-  h.P = pl.P; h.d = pl.d; h.ktot = (int)pl.ktot; h.nwg = pl.nwg; h.mode = 0;
-  {
-    Prof pr(ctx, PROF_HIST, 0, 0);
-    launch_hist_dots(h, ctx->stream);
+  bool any_accept = false;
+  for (int v : hs) {
+    *any_fail |= (v == ST_FAIL);
+    any_accept |= (v == ST_ACCEPT);
   }
-  PrepArgs pa{};
-  pa.st = B.st; pa.part = B.hpart; pa.nwg = pl.nwg; pa.P = pl.P; pa.mode = 0;
-  pa.history = pl.H; pa.curv_eps = 1e-10; pa.select_status = 0; pa.flags = nullptr;
-  launch_prepare(pa, ctx->stream);
+  if (any_accept) {
+    run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, ws, &hs, ST_ACCEPT);
+    GradUpdArgs g = grad_args(pl, b, ws, B.st, 1 << ST_ACCEPT, 0);
+    g.x = Kc; g.p = B.p; g.g = B.g; g.S = B.S; g.Yh = B.Yh;
+    launch_grad_update(g, ctx->stream);
+  }
+  lb_dots(ctx, pl, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL));
   return KVS_OK;
 }
 
@@ -508,7 +501,12 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
   kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
   run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, loss, mse, nullptr, ws);
-  if (grad) run_backward(ctx, pl, b, Q, Vc, nullptr, 0, grad, ws);
+  if (grad) {
+    run_backward(ctx, pl, b, Q, Vc, nullptr, 0, ws);
+    GradUpdArgs g = grad_args(pl, b, ws, nullptr, 0, 2);
+    g.gout = grad;
+    launch_grad_update(g, ctx->stream);
+  }
   return hip_check(ctx, fn);
 }
 

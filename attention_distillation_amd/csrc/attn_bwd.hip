@@ -10,7 +10,7 @@
 // (B operand of dK).  dA comes out with query rows 4g+r and key column lq,
 // which is the A-operand layout of dK = dS^T Q, so dS never leaves VGPRs.
 // Partial dK per query chunk is written out and summed in a fixed order by
-// grad_reduce_kernel (no float atomics).
+// the gradient pass of the optimizer (no float atomics).
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -126,28 +126,6 @@ void launch_attn_bwd(const BwdArgs& a, int d, hipStream_t s) {
   dim3 grid((a.kmax + 63) / 64, a.P, a.Cn);
   if (d == 128) hipLaunchKernelGGL((attn_bwd_kernel<128>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((attn_bwd_kernel<64>), grid, dim3(256), 0, s, a);
-}
-
-// grad = scale * sum_c dKpart[c], c in increasing order
-__global__ __launch_bounds__(256) void grad_reduce_kernel(GradReduceArgs a, int d) {
-  const int p = blockIdx.y;
-  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
-  const ProbInfo pi = a.info[p];
-  const long long nel = (long long)pi.k * d;
-  const long long base = (long long)pi.koff * d;
-  const float sc = (float)a.scale;
-  for (long long i4 = (blockIdx.x * 256LL + threadIdx.x) * 4; i4 < nel; i4 += (long long)gridDim.x * 256 * 4) {
-    f32x4 acc = *(const f32x4*)(a.dKpart + base + i4);
-    for (int c = 1; c < a.Cn; ++c) acc += *(const f32x4*)(a.dKpart + (size_t)c * a.ktot * d + base + i4);
-    *(f32x4*)(a.grad + base + i4) = acc * sc;
-  }
-}
-
-void launch_grad_reduce(const GradReduceArgs& a, int d, hipStream_t s) {
-  int kmax = 0;
-  (void)kmax;
-  dim3 grid(64, a.P);
-  hipLaunchKernelGGL(grad_reduce_kernel, grid, dim3(256), 0, s, a, d);
 }
 
 }  // namespace kvs

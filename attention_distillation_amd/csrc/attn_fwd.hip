@@ -215,7 +215,58 @@ void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s) {
 //   reference mode: Y = O, lse = m + log l
 //   loss mode (scores were shifted by the target lse, so m + log l = lhat - l):
 //     R = O - Y, G = 2R, e = lhat - l, crow = -G.O + 2 lam e,
-//     per-WG partials of sum(R^2) + lam sum(e^2) and of sum(R^2).
+//     per-WG partials of sum(R^2) + lam sum(e^2) and of sum(R^2); the last
+//     workgroup of a problem (arrival counter) sums them in block order and
+//     finalises: loss / mse outputs, or the Armijo test of a line-search trial.
+
+// Fixed-order sum of the per-block partials, then the per-problem decision.
+template <int D>
+__device__ void finalize_problem(const MergeArgs& a, int p, int nblk) {
+  __shared__ double r0[256], r1[256];
+  const int t = threadIdx.x;
+  double sL = 0.0, sO = 0.0;
+  for (int i = t; i < nblk; i += 256) {
+    const double* src = a.part + ((size_t)p * nblk + i) * 2;
+    sL += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sO += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  r0[t] = sL;
+  r1[t] = sO;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) {
+      r0[t] += r0[t + off];
+      r1[t] += r1[t + off];
+    }
+    __syncthreads();
+  }
+  if (t != 0) return;
+  sL = r0[0];
+  sO = r1[0];
+  LbState* st = a.st ? a.st + p : nullptr;
+  if (a.fin_mode == 1) {
+    st->Ltrial = sL;
+    if (sL <= st->L + a.c1 * st->alpha * st->gtp) {
+      st->status = ST_ACCEPT;
+      st->L = sL;
+      st->st_valid = 1;
+    } else {
+      st->st_valid = 0;
+      st->trials += 1;
+      st->alpha *= a.shrink;
+      if (st->trials >= a.max_bt) st->status = ST_FAIL;
+    }
+    if (a.status_view) a.status_view[p] = st->status;
+  } else {
+    if (st) {
+      st->L = sL;
+      st->st_valid = 1;
+    }
+    if (a.loss) a.loss[p] = (float)sL;
+    if (a.mse) a.mse[p] = (float)(sO / ((double)a.n * (double)D));
+  }
+}
+
 template <int D, bool LOSS>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int p = blockIdx.y;
@@ -260,6 +311,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
   } else {
     __shared__ double red[2][256];
+    __shared__ int s_last;
     float rr = 0.f, dl = 0.f;
     if (ok) {
       const float* y = a.Y + row * D + part * DPT;
@@ -302,7 +354,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       double* dst = a.part + ((size_t)p * gridDim.x + blockIdx.x) * 2;
       dst[0] = red[0][0];
       dst[1] = red[1][0];
+      __threadfence();
+      const unsigned prev = atomicAdd(a.counter + p, 1u);
+      s_last = (prev == gridDim.x - 1);
     }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    finalize_problem<D>(a, p, gridDim.x);
+    if (tid == 0) a.counter[p] = 0u;
   }
 }
 
@@ -314,59 +374,6 @@ void launch_merge(const MergeArgs& a, int d, bool loss_mode, hipStream_t s) {
   if (d == 128) { if (loss_mode) KVS_MERGE(128, true); else KVS_MERGE(128, false); }
   else { if (loss_mode) KVS_MERGE(64, true); else KVS_MERGE(64, false); }
 #undef KVS_MERGE
-}
-
-// --------------------------------------------------------------------------
-// per-problem loss finalisation (fixed-order double sums) and, in trial
-// mode, the Armijo test of the backtracking search.
-__global__ __launch_bounds__(64) void finalize_kernel(FinalizeArgs a) {
-  const int p = blockIdx.x;
-  LbState* st = a.st ? a.st + p : nullptr;
-  if (a.mode == 1 && st->status != ST_SEARCH) {
-    if (threadIdx.x == 0 && a.status_host_view) a.status_host_view[p] = st->status;
-    return;
-  }
-  const int t = threadIdx.x;
-  double sL = 0.0, sO = 0.0;
-  for (int i = t; i < a.nblk; i += 64) {
-    sL += a.part[((size_t)p * a.nblk + i) * 2 + 0];
-    sO += a.part[((size_t)p * a.nblk + i) * 2 + 1];
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    sL += __shfl_xor(sL, off);
-    sO += __shfl_xor(sO, off);
-  }
-  if (t != 0) return;
-  if (a.mode == 0) {
-    if (a.loss) a.loss[p] = (float)sL;
-    if (a.mse) a.mse[p] = (float)(sO / ((double)a.n * a.d));
-    if (st) {
-      st->L = sL;
-      st->st_valid = 1;
-    }
-  } else if (a.mode == 1) {
-    st->Ltrial = sL;
-    if (sL <= st->L + a.c1 * st->alpha * st->gtp) {
-      st->status = ST_ACCEPT;
-      st->L = sL;
-      st->st_valid = 1;
-    } else {
-      st->st_valid = 0;
-      st->trials += 1;
-      st->alpha *= a.shrink;
-      if (st->trials >= a.max_bt) st->status = ST_FAIL;
-    }
-    if (a.status_host_view) a.status_host_view[p] = st->status;
-  } else {
-    st->L = sL;
-    st->st_valid = 1;
-    if (a.loss) a.loss[p] = (float)sL;
-    if (a.mse) a.mse[p] = (float)(sO / ((double)a.n * a.d));
-  }
-}
-
-void launch_finalize(const FinalizeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.P), dim3(64), 0, s, a);
 }
 
 // --------------------------------------------------------------------------

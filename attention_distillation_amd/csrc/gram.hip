@@ -1,5 +1,8 @@
 // Normal equations of the ridge value solve, gfx950.
 //
+// The stored shifted scores are first turned into the softmax weights in
+// place (weights_kernel), then tiled.
+//
 // For A = exp(St - e) (the softmax weights rebuilt from the stored shifted
 // scores, n x k) the kernel forms the augmented lower-trapezoidal matrix
 //     M = [ A^T A ]   rows 0..kpad-1  (lower triangle, 64x64 tiles)
@@ -37,21 +40,36 @@ __device__ __forceinline__ bool gram_tile(long long t, int KT, int DT, int& I, i
   return true;
 }
 
-template <int D>
-__device__ __forceinline__ void stage_keys(float (*dst)[68], const float* St, const float* e, int k,
-                                           int key0, int npad, int qt, int qend, int tid) {
+// A = exp(St - e), in place over the stored scores (zero for q >= n), so the
+// Gram tiles stage plain copies instead of recomputing exp per tile.
+__global__ __launch_bounds__(256) void weights_kernel(GramArgs a) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int n = a.n, npad = (n + 3) & ~3, n4 = npad / 4;
+  const long long tot4 = (long long)pi.k * n4;
+  f32x4* A = reinterpret_cast<f32x4*>(const_cast<float*>(a.St) + pi.soff);
+  const float* e = a.e + (size_t)p * n;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < tot4; i += (long long)gridDim.x * 256) {
+    const int q = (int)(i % n4) * 4;
+    const f32x4 sv = A[i];
+    f32x4 v;
+    v.x = expf(sv.x - e[q]);
+    v.y = (q + 1 < n) ? expf(sv.y - e[q + 1]) : 0.f;
+    v.z = (q + 2 < n) ? expf(sv.z - e[q + 2]) : 0.f;
+    v.w = (q + 3 < n) ? expf(sv.w - e[q + 3]) : 0.f;
+    A[i] = v;
+  }
+}
+
+__device__ __forceinline__ void stage_keys(float (*dst)[68], const float* A, int k, int key0, int npad,
+                                           int qt, int qend, int tid) {
   for (int i = tid; i < 64 * 16; i += 256) {
     const int r = i >> 4, c4 = i & 15;
     const int key = key0 + r;
     const int q = qt + 4 * c4;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (key < k && q < qend) {
-      const f32x4 s = *(const f32x4*)(St + (size_t)key * npad + q);
-      v.x = expf(s.x - e[q]);
-      v.y = (q + 1 < qend) ? expf(s.y - e[q + 1]) : 0.f;
-      v.z = (q + 2 < qend) ? expf(s.z - e[q + 2]) : 0.f;
-      v.w = (q + 3 < qend) ? expf(s.w - e[q + 3]) : 0.f;
-    }
+    if (key < k && q < qend) v = *(const f32x4*)(A + (size_t)key * npad + q);
     *(f32x4*)&dst[r][4 * c4] = v;
   }
 }
@@ -73,8 +91,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
   const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
   const bool diag = (I == J);
-  const float* St = a.St + pi.soff;
-  const float* e = a.e + (size_t)p * n;
+  const float* St = a.St + pi.soff;      // softmax weights after weights_kernel
   const float* Y = a.Y + (size_t)p * n * D;
 
   f32x4 acc[2][2];
@@ -86,7 +103,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   for (int qt = qbeg; qt < qend; qt += 64) {
     __syncthreads();
     if (I < KT) {
-      stage_keys<D>(Ra, St, e, pi.k, 64 * I, npad, qt, qend, tid);
+      stage_keys(Ra, St, pi.k, 64 * I, npad, qt, qend, tid);
     } else {
       const int dim0 = 64 * (I - KT);
       for (int i = tid; i < 64 * 16; i += 256) {
@@ -100,7 +117,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
         Ra[4 * c4 + 3][qq] = v.w;
       }
     }
-    if (!diag) stage_keys<D>(Ca, St, e, pi.k, 64 * J, npad, qt, qend, tid);
+    if (!diag) stage_keys(Ca, St, pi.k, 64 * J, npad, qt, qend, tid);
     __syncthreads();
     float (*C)[68] = diag ? Ra : Ca;
 #pragma unroll
@@ -137,6 +154,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
 }
 
 void launch_gram(const GramArgs& a, int d, hipStream_t s) {
+  hipLaunchKernelGGL(weights_kernel, dim3(256, a.P), dim3(256), 0, s, a);
   const long long KT = a.kpadmax / 64;
   const long long T = KT * (KT + 1) / 2 + (long long)(d / 64) * KT;
   dim3 grid((unsigned)T, a.P, a.Cg);

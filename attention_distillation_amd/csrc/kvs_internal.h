@@ -71,27 +71,23 @@ void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s);
 
 struct MergeArgs {
   const float* Opart; const float* Mpart; const float* Lpart;
-  const LbState* st; int active_mask;
+  LbState* st; int active_mask;
   const float* Y; const float* lse;   // loss mode: targets; ref mode: NULL
   float* Yout; float* lse_out;        // ref mode outputs
   float* G; float* e; float* crow;    // loss mode outputs
   double* part;                       // [P][nblk][2] loss / output-term partials
+  unsigned* counter;                  // [P] arrival counters (zero between launches)
   int P, n, C;
   double lambda;
+  // per-problem finalisation, done by the last workgroup of each problem:
+  //   0 = write loss / mse, 1 = Armijo trial, 2 = refresh L at the keys
+  int fin_mode;
+  double c1, shrink; int max_bt;
+  float* loss; float* mse;
+  int* status_view;                   // device int[P] copy of the status for the host
 };
 void launch_merge(const MergeArgs& a, int d, bool loss_mode, hipStream_t s);
 int merge_blocks(int n);
-
-struct FinalizeArgs {
-  const double* part; int nblk; int P;
-  LbState* st;            // NULL: plain loss_grad output
-  float* loss; float* mse;
-  int n, d;
-  int mode;               // 0 = write outputs, 1 = Armijo trial, 2 = refresh L at x
-  double c1, shrink; int max_bt;
-  int* status_host_view;  // device int[P] copy of the status (for the host)
-};
-void launch_finalize(const FinalizeArgs& a, hipStream_t s);
 
 struct BwdArgs {
   const float* Q; const float* St; const float* G; const float* e; const float* crow;
@@ -102,12 +98,6 @@ struct BwdArgs {
   int P, n, Cn, kmax, ktot;
 };
 void launch_attn_bwd(const BwdArgs& a, int d, hipStream_t s);
-
-struct GradReduceArgs {
-  const float* dKpart; float* grad; const LbState* st; int active_mask;
-  const ProbInfo* info; int P, Cn, ktot; double scale;
-};
-void launch_grad_reduce(const GradReduceArgs& a, int d, hipStream_t s);
 
 struct GramArgs {
   const float* St; const float* e; const float* Y;
@@ -125,18 +115,17 @@ struct GramReduceArgs {
 void launch_gram_reduce(const GramReduceArgs& a, int d, hipStream_t s);
 
 struct CholArgs {
-  float* M; const double* trpart; double* mu; int* info_out;
+  float* M; float* Ldiag; const double* trpart; double* mu; int* info_out;
   const LbState* st; int active_mask;
   const ProbInfo* info; int P, kpadmax; double ridge_rel;
 };
 void launch_mu(const CholArgs& a, hipStream_t s);
-void launch_potrf_panel(const CholArgs& a, int d, int panel, hipStream_t s);
-void launch_trailing(const CholArgs& a, int d, int panel, hipStream_t s);
+void launch_chol_step(const CholArgs& a, int d, int panel, hipStream_t s);
 
 struct BackArgs {
-  const float* M; float* X; float* Vc; const int* info_out; int* flags;
+  const float* M; const float* Ldiag; float* X; float* Dinv; float* Vc; const int* info_out; int* flags;
   LbState* st; int active_mask;
-  const ProbInfo* info; int P;
+  const ProbInfo* info; int P, d, kpadmax;
 };
 void launch_back_subst(const BackArgs& a, int d, hipStream_t s);
 
@@ -154,24 +143,38 @@ struct TopkArgs {
 };
 void launch_topk(const TopkArgs& a, hipStream_t s);
 
-struct HistArgs {
-  float* x; const float* p; float* g; const float* gnew;
-  float* S; float* Yh;          // [kSlots][sum k][d]
-  LbState* st; int active_mask;
-  double* part;                 // [P][nwg][kDots]
-  const ProbInfo* info;
-  int P, d, ktot, nwg; int mode;  // mode 0 = accept (x, s, y, g), 1 = refresh (g only)
+// Gradient reduction fused with the L-BFGS vector updates.
+//   mode 0 (accepted step, problems in ACCEPT): g_new = scale * sum_c dKpart[c],
+//          x <- x + alpha p, s = x_new - x, y = g_new - g into the staging slot, g <- g_new
+//   mode 1 (refresh, every problem): g <- g_new
+//   mode 2 (plain output): gout <- g_new
+struct GradUpdArgs {
+  const float* dKpart; int Cn; double scale;
+  LbState* st; int active_mask; int mode;
+  float* x; const float* p; float* g; float* S; float* Yh; float* gout;
+  const ProbInfo* info; int P, d, ktot, nch;
 };
-void launch_hist_dots(const HistArgs& a, hipStream_t s);
-struct PrepArgs {
-  LbState* st; const double* part; int nwg; int P; int mode; int history; double curv_eps;
-  int select_status;     // process problems in this status
-  int* flags;
+void launch_grad_update(const GradUpdArgs& a, hipStream_t s);
+
+// Inner products of the history with the staged pair and the gradient, one
+// workgroup per (chunk, slot); the last workgroup of each problem then runs
+// the scalar L-BFGS logic (history update, two-loop coefficients, first step).
+//   mode 0: after a search (ACCEPT: push + coefficients, FAIL: reset)
+//   mode 1: gradient refreshed at the same keys; mode 2: history cleared
+struct DotsArgs {
+  const float* g; const float* S; const float* Yh;
+  LbState* st; int active_mask; int mode; int history; double curv_eps;
+  double* part;                 // [P][nch][kDots]
+  unsigned* counter;            // [P]
+  const ProbInfo* info; int P, d, ktot, nch;
 };
-void launch_prepare(const PrepArgs& a, hipStream_t s);
+void launch_dots(const DotsArgs& a, hipStream_t s);
+int dots_chunks(long long kmax_d);
+int vec_chunks(long long kmax_d);
+
 struct DirArgs {
   float* p; const float* g; const float* S; const float* Yh; const LbState* st;
-  const ProbInfo* info; int P, d, ktot, nwg;
+  const ProbInfo* info; int P, d, ktot, nch;
 };
 void launch_direction(const DirArgs& a, hipStream_t s);
 

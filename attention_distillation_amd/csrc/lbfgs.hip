@@ -3,303 +3,431 @@
 // The two-loop recursion (Nocedal & Wright, Numerical Optimization,
 // Algorithm 7.4) is evaluated from inner products: every scalar it needs is
 // a combination of s_i.y_j, y_i.y_j, s_i.g and y_i.g, so the recursion runs
-// in a few hundred scalar flops per problem (prepare_kernel) and the vectors
-// are touched in two streaming passes per iteration:
-//   hist_dots_kernel   accepted step: x <- x + a p, s = x_new - x, y = g_new - g,
-//                      g <- g_new, and the new inner products (fixed-order
-//                      partials per workgroup, double accumulation);
-//   direction_kernel   p = c_g g + sum_j (cs_j s_j + cy_j y_j).
+// in a few hundred scalar flops per problem and the vectors are streamed in
+// three bandwidth-bound passes per iteration:
+//   grad_update_kernel  g_new = scale * sum of the backward's split partials,
+//                       and for an accepted step x <- x + a p, s = x_new - x,
+//                       y = g_new - g (into the staging slot), g <- g_new;
+//   dots_kernel         one workgroup per chunk: the five inner products of
+//                       every history slot with the staged pair and g, kept
+//                       in registers; the last workgroup of each problem
+//                       (arrival counter) reduces them in chunk order and runs
+//                       the scalar logic (curvature test, ring update, two-loop
+//                       coefficients, descent check, first step) on a copy of
+//                       the state in LDS, lane-parallel over the history;
+//   direction_kernel    p = c_g g + sum_j (cs_j s_j + cy_j y_j).
 // Pairs live in a ring of history+1 slots; the spare slot stages the next
 // (s, y) before the curvature test decides whether it enters the history.
-#include <float.h>
-
 #include "../../include/kvsculpt.h"
 #include "kvs_internal.h"
 
 namespace kvs {
 
-constexpr int kVecPerWG = 1024;   // float4 per workgroup in the vector passes
+static_assert(sizeof(LbState) % 8 == 0, "state is copied to LDS in 8-byte words");
 
-__device__ __forceinline__ double dsum_wave(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+constexpr int kVec4PerWG = 256;     // float4 per workgroup in the streaming passes
+constexpr int kDotVec4PerWG = 256;  // float4 per workgroup in the dot pass (one per thread)
+
+int vec_chunks(long long kmax_d) {
+  const long long v4 = (kmax_d + 3) / 4;
+  return (int)std::max<long long>(1, (v4 + kVec4PerWG - 1) / kVec4PerWG);
 }
-
-// Sum of NV doubles over the 256-thread workgroup (fixed tree), result in out[0..NV).
-template <int NV>
-__device__ __forceinline__ void wg_sum(double (&v)[NV], double* out, double (*sh)[NV]) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = dsum_wave(v[i]);
-  if (lane == 0)
-#pragma unroll
-    for (int i = 0; i < NV; ++i) sh[wave][i] = v[i];
-  __syncthreads();
-  if (tid == 0)
-#pragma unroll
-    for (int i = 0; i < NV; ++i) out[i] = ((sh[0][i] + sh[1][i]) + sh[2][i]) + sh[3][i];
-  __syncthreads();
+int dots_chunks(long long kmax_d) {
+  const long long v4 = (kmax_d + 3) / 4;
+  return (int)std::max<long long>(1, (v4 + kDotVec4PerWG - 1) / kDotVec4PerWG);
 }
 
 __device__ __forceinline__ double dot4(f32x4 a, f32x4 b) {
   return (double)a.x * b.x + (double)a.y * b.y + (double)a.z * b.z + (double)a.w * b.w;
 }
 
-__global__ __launch_bounds__(256) void hist_dots_kernel(HistArgs a) {
+__device__ __forceinline__ bool active(const LbState* st, int mask) {
+  return (1 << st->status) & mask;
+}
+
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void grad_update_kernel(GradUpdArgs a) {
   const int p = blockIdx.y;
-  LbState* st = a.st + p;
-  if (!((1 << st->status) & a.active_mask)) return;
+  LbState* st = a.st ? a.st + p : nullptr;
+  if (st && !active(st, a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const long long n4 = (long long)pi.k * a.d / 4;
+  const long long e = (long long)blockIdx.x * kVec4PerWG + threadIdx.x;
+  if (e >= n4) return;
+  const long long base4 = (long long)pi.koff * a.d / 4;
+  const long long stride4 = (long long)a.ktot * a.d / 4;
+  const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
+  f32x4 gn = dK[e];
+  for (int c = 1; c < a.Cn; ++c) gn += dK[(size_t)c * stride4 + e];
+  gn *= (float)a.scale;
+  if (a.mode == 2) {
+    reinterpret_cast<f32x4*>(a.gout)[base4 + e] = gn;
+    return;
+  }
+  f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
+  if (a.mode == 0) {
+    f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
+    const f32x4* Pd = reinterpret_cast<const f32x4*>(a.p) + base4;
+    const float alpha = (float)st->alpha;
+    const int stg = st->stage;
+    const f32x4 xv = X[e], pv = Pd[e], go = G[e];
+    f32x4 xn;
+    xn.x = __fmaf_rn(alpha, pv.x, xv.x);
+    xn.y = __fmaf_rn(alpha, pv.y, xv.y);
+    xn.z = __fmaf_rn(alpha, pv.z, xv.z);
+    xn.w = __fmaf_rn(alpha, pv.w, xv.w);
+    X[e] = xn;
+    reinterpret_cast<f32x4*>(a.S)[(size_t)stg * stride4 + base4 + e] = xn - xv;
+    reinterpret_cast<f32x4*>(a.Yh)[(size_t)stg * stride4 + base4 + e] = gn - go;
+  }
+  G[e] = gn;
+}
+
+void launch_grad_update(const GradUpdArgs& a, hipStream_t s) {
+  dim3 grid(a.nch, a.P);
+  hipLaunchKernelGGL(grad_update_kernel, grid, dim3(256), 0, s, a);
+}
+
+// --------------------------------------------------------------------------
+// Scalar L-BFGS logic of one problem on the LDS copy of its state, spread
+// over the first wave of the workgroup (lane i owns history position i).
+// d holds the reduced inner products by history position: 5 t + r for
+// position t (t < count: order[t]; t == count: the staged pair), r = 0..4 as
+// in dots_kernel, then g.g at 5 MS and s.s at 5 MS + 1.
+// Every thread of the workgroup calls it (barriers), lanes of wave 0 work.
+template <int MS>
+__device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, double curv_eps) {
+  const int tid = threadIdx.x;
+  const bool w0 = tid < 64;
+  const int lane = tid & 63;
+  __syncthreads();
+  const int status = st->status;
+  const bool use_dots = !(mode == 0 && status == ST_FAIL);
+  const bool reset = (mode == 2 || (mode == 0 && status == ST_FAIL));
+  const bool accept = (mode == 0 && status == ST_ACCEPT);
+  const int cnt0 = st->count, stg0 = st->stage;
+  __syncthreads();
+  // inner products with g, by slot id (taken before the ring moves)
+  if (use_dots && w0 && lane <= cnt0 && (lane < cnt0 || accept)) {
+    const int j = (lane < cnt0) ? st->order[lane] : stg0;
+    st->Sg[j] = d[5 * lane + 3];
+    st->Yg[j] = d[5 * lane + 4];
+  }
+  if (use_dots && tid == 0) st->gg = d[5 * MS];
+  __syncthreads();
+  if (reset && tid == 0) {
+    if (mode == 0) st->flags |= KVS_FLAG_LINESEARCH;
+    st->count = 0;
+    st->stage = 0;
+  }
+  __syncthreads();
+  if (accept) {
+    const int stg = stg0, cnt = cnt0;
+    const double sy = d[5 * cnt + 0], yy = d[5 * cnt + 2], ss = d[5 * MS + 1];
+    const bool push = sy > curv_eps * sqrt(ss) * sqrt(yy);
+    if (push) {
+      if (w0 && lane < cnt) {
+        const int j = st->order[lane];
+        st->SY[stg][j] = d[5 * lane + 0];
+        st->SY[j][stg] = d[5 * lane + 1];
+        st->YY[stg][j] = d[5 * lane + 2];
+        st->YY[j][stg] = d[5 * lane + 2];
+      }
+      __syncthreads();
+      if (tid == 0) {
+        st->rho[stg] = 1.0 / sy;
+        st->SY[stg][stg] = sy;
+        st->YY[stg][stg] = yy;
+        if (cnt < H) {
+          st->order[cnt] = stg;
+          st->count = cnt + 1;
+          int fr = 0;                         // smallest slot not in the history
+          for (; fr < kSlots; ++fr) {
+            bool used = false;
+            for (int t = 0; t <= cnt; ++t) used |= (st->order[t] == fr);
+            if (!used) break;
+          }
+          st->stage = fr;
+        } else {
+          const int old = st->order[0];
+          for (int t = 1; t < H; ++t) st->order[t - 1] = st->order[t];
+          st->order[H - 1] = stg;
+          st->stage = old;
+        }
+      }
+    }
+  }
+  if (w0 && lane < kSlots) { st->cs[lane] = 0.0; st->cy[lane] = 0.0; }
+  __syncthreads();
+
+  // two-loop recursion through inner products: two triangular solves of
+  // size m <= 16 with lane-parallel updates
+  const int m = st->count;
+  const double gg = st->gg;
+  double gtp = -gg, coef_g = -1.0;
+  bool nondescent = false;
+  if (m > 0 && w0) {
+    const bool mine = lane < m;
+    const int oi = mine ? st->order[lane] : 0;
+    double row[kHistMax], col[kHistMax], yyr[kHistMax];
+#pragma unroll
+    for (int j = 0; j < kHistMax; ++j) {
+      const int oj = (j < m) ? st->order[j] : 0;
+      row[j] = (mine && j < m) ? st->SY[oi][oj] : 0.0;   // s_i . y_j
+      col[j] = (mine && j < m) ? st->SY[oj][oi] : 0.0;   // s_j . y_i
+      yyr[j] = (mine && j < m) ? st->YY[oi][oj] : 0.0;
+    }
+    const double rho = mine ? st->rho[oi] : 0.0;
+    const double sg = mine ? st->Sg[oi] : 0.0, yg = mine ? st->Yg[oi] : 0.0;
+    double al[kHistMax], be[kHistMax];
+    // newest -> oldest: a_i = rho_i (s_i.g - sum_{j>i} a_j s_i.y_j)
+    double acc = sg;
+#pragma unroll
+    for (int j = kHistMax - 1; j >= 0; --j) {
+      al[j] = 0.0;
+      if (j < m) {
+        const double mine_al = rho * acc;
+        al[j] = __shfl(mine_al, j);
+        if (lane < j) acc -= al[j] * row[j];
+      }
+    }
+    const int on = st->order[m - 1];
+    const double gamma = st->SY[on][on] / st->YY[on][on];
+    // oldest -> newest: b_i = rho_i y_i.r, r = gamma (g - sum a_j y_j) + sum_{j<i} (a_j - b_j) s_j
+    double c = yg;
+#pragma unroll
+    for (int j = 0; j < kHistMax; ++j)
+      if (j < m) c -= al[j] * yyr[j];
+    c *= gamma;
+    double acc2 = 0.0;
+#pragma unroll
+    for (int j = 0; j < kHistMax; ++j) {
+      be[j] = 0.0;
+      if (j < m) {
+        const double mine_be = rho * (c + acc2);
+        be[j] = __shfl(mine_be, j);
+        if (lane > j) acc2 += (al[j] - be[j]) * col[j];
+      }
+    }
+    double my_al = 0.0, my_be = 0.0;
+#pragma unroll
+    for (int j = 0; j < kHistMax; ++j)
+      if (j == lane) { my_al = al[j]; my_be = be[j]; }
+    double term = mine ? (-gamma * my_al * yg + (my_al - my_be) * sg) : 0.0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) term += __shfl_xor(term, off);
+    gtp = -(gamma * gg + term);
+    coef_g = -gamma;
+    if (gtp < 0.0) {
+      if (mine) {
+        st->cy[oi] = gamma * my_al;
+        st->cs[oi] = -(my_al - my_be);
+      }
+    } else {
+      nondescent = true;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double a0 = 1.0;
+    if (nondescent) {
+      st->flags |= KVS_FLAG_NONDESCENT;
+      st->count = 0;
+      st->stage = 0;
+    }
+    if (st->count == 0) {
+      coef_g = -1.0;
+      gtp = -gg;
+      a0 = 1.0 / fmax(1.0, sqrt(gg));
+    }
+    st->coef_g = coef_g;
+    st->gtp = gtp;
+    st->alpha = a0;
+    st->trials = 0;
+    st->status = ST_SEARCH;
+  }
+  __syncthreads();
+}
+
+// One workgroup per 256-float4 chunk of a problem's vectors, one float4 per
+// thread: the loads of every history slot are issued together, the five
+// inner products per slot (by history position) are reduced once per
+// workgroup.  The last workgroup of the problem sums the chunk partials
+// (folded to 64 rows, then a fixed pairwise tree in LDS) and runs the scalar
+// logic.  MS = history bound + 1 positions (history plus the staged pair).
+template <int MS>
+__global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
+  constexpr int E = 5 * MS + 2;            // partial entries per chunk
+  const int p = blockIdx.y;
+  LbState* gst = a.st + p;
+  const int status = gst->status;
+  if (!((1 << status) & a.active_mask)) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const ProbInfo pi = a.info[p];
   const long long n4 = (long long)pi.k * a.d / 4;
   const long long base4 = (long long)pi.koff * a.d / 4;
   const long long stride4 = (long long)a.ktot * a.d / 4;
-  const long long beg = (long long)blockIdx.x * kVecPerWG;
-  if (beg >= n4) {
-    // keep the partial layout complete: zero contributions
-    if (threadIdx.x < kDots) a.part[((size_t)p * a.nwg + blockIdx.x) * kDots + threadIdx.x] = 0.0;
-    return;
-  }
-  const int tid = threadIdx.x;
-  const int stg = st->stage;
-  const float alpha = (float)st->alpha;
-  f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
-  const f32x4* Pd = reinterpret_cast<const f32x4*>(a.p) + base4;
-  f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
-  const f32x4* Gn = reinterpret_cast<const f32x4*>(a.gnew) + base4;
-  f32x4* S = reinterpret_cast<f32x4*>(a.S) + base4;
-  f32x4* Yv = reinterpret_cast<f32x4*>(a.Yh) + base4;
+  const int cnt = gst->count, stg = gst->stage;
+  const bool accept = (a.mode == 0 && status == ST_ACCEPT);
+  const bool compute = !(a.mode == 0 && status == ST_FAIL);
+  const int nvis = cnt + (accept ? 1 : 0);
+  double* out = a.part + ((size_t)p * a.nch + blockIdx.x) * E;
+  constexpr int NV = (E + 63) / 64;       // reduced values per lane
+  __shared__ double red[4][64 * NV];
+  __shared__ int s_last;
 
-  constexpr int PER = kVecPerWG / 256;
-  f32x4 sv[PER], yv[PER], gv[PER];
-  bool ok[PER];
-  double gg = 0.0, ss = 0.0;
+  if (compute) {
+    const long long e = (long long)blockIdx.x * 256 + tid;
+    const bool ok = e < n4;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
+    const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
+    const f32x4 gv = ok ? reinterpret_cast<const f32x4*>(a.g)[base4 + e] : z;
+    const f32x4 sv = (ok && accept) ? S[(size_t)stg * stride4 + e] : z;
+    const f32x4 yv = (ok && accept) ? Yv[(size_t)stg * stride4 + e] : z;
+    int slot[MS];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const long long e = beg + tid + 256 * i;
-    ok[i] = e < n4;
-    sv[i] = yv[i] = gv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!ok[i]) continue;
-    const f32x4 gn = Gn[e];
-    if (a.mode == 0) {
-      const f32x4 xv = X[e], pv = Pd[e], go = G[e];
-      f32x4 xn;
-      xn.x = __fmaf_rn(alpha, pv.x, xv.x);
-      xn.y = __fmaf_rn(alpha, pv.y, xv.y);
-      xn.z = __fmaf_rn(alpha, pv.z, xv.z);
-      xn.w = __fmaf_rn(alpha, pv.w, xv.w);
-      sv[i] = xn - xv;
-      yv[i] = gn - go;
-      X[e] = xn;
-      S[(size_t)stg * stride4 + e] = sv[i];
-      Yv[(size_t)stg * stride4 + e] = yv[i];
-    }
-    G[e] = gn;
-    gv[i] = gn;
-    gg += dot4(gn, gn);
-    ss += dot4(sv[i], sv[i]);
-  }
-  __shared__ double sh5[4][5];
-  __shared__ double sh2[4][2];
-  double* out = a.part + ((size_t)p * a.nwg + blockIdx.x) * kDots;
-  {
-    double v[2] = {gg, ss};
-    wg_sum<2>(v, out + 5 * kSlots, sh2);
-  }
-  // slots to visit: the history plus (accept mode) the staged pair
-  const int cnt = st->count;
-  const int nvis = cnt + (a.mode == 0 ? 1 : 0);
-  for (int t = 0; t < nvis; ++t) {
-    const int j = (t < cnt) ? st->order[t] : stg;
-    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int t = 0; t < MS; ++t) slot[t] = (t < cnt) ? gst->order[t < kHistMax ? t : 0] : stg;
+    f32x4 sj[MS], yj[MS];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (!ok[i]) continue;
-      const long long e = beg + tid + 256 * i;
-      const f32x4 sj = S[(size_t)j * stride4 + e];
-      const f32x4 yj = Yv[(size_t)j * stride4 + e];
-      v[0] += dot4(sv[i], yj);   // s_stage . y_j
-      v[1] += dot4(sj, yv[i]);   // s_j . y_stage
-      v[2] += dot4(yv[i], yj);   // y_stage . y_j
-      v[3] += dot4(gv[i], sj);   // g . s_j
-      v[4] += dot4(gv[i], yj);   // g . y_j
+    for (int t = 0; t < MS; ++t) {
+      const bool use = ok && t < nvis;
+      sj[t] = use ? S[(size_t)slot[t] * stride4 + e] : z;
+      yj[t] = use ? Yv[(size_t)slot[t] * stride4 + e] : z;
     }
-    wg_sum<5>(v, out + 5 * j, sh5);
+    // all E values of this lane, padded to a multiple of 64, then a
+    // butterfly reduction per group of 64: at each level a lane keeps one
+    // half of its values and adds the partner's copy of that half, so lane l
+    // ends with the wave total of value l of the group (63 exchanges per
+    // group instead of a full reduction per value)
+    double v[64 * NV];
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
+      const bool use = t < nvis;
+      v[5 * t + 0] = use ? dot4(sv, yj[t]) : 0.0;   // s_stage . y_t
+      v[5 * t + 1] = use ? dot4(sj[t], yv) : 0.0;   // s_t . y_stage
+      v[5 * t + 2] = use ? dot4(yv, yj[t]) : 0.0;   // y_stage . y_t
+      v[5 * t + 3] = use ? dot4(gv, sj[t]) : 0.0;   // g . s_t
+      v[5 * t + 4] = use ? dot4(gv, yj[t]) : 0.0;   // g . y_t
+    }
+    v[5 * MS] = dot4(gv, gv);
+    v[5 * MS + 1] = dot4(sv, sv);
+#pragma unroll
+    for (int i = E; i < 64 * NV; ++i) v[i] = 0.0;
+#pragma unroll
+    for (int gi = 0; gi < NV; ++gi) {
+      double* w = v + 64 * gi;
+#pragma unroll
+      for (int L = 32; L > 0; L >>= 1) {
+        const bool hi = (lane & L) != 0;
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+          const double send = hi ? w[i] : w[i + L];
+          const double keep = hi ? w[i + L] : w[i];
+          w[i] = keep + __shfl_xor(send, L);
+        }
+      }
+      red[wave][64 * gi + lane] = w[0];
+    }
+    __syncthreads();
+    if (tid < 5 * nvis || (tid >= 5 * MS && tid < E))
+      out[tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
   }
-}
-
-void launch_hist_dots(const HistArgs& a, hipStream_t s) {
-  dim3 grid(a.nwg, a.P);
-  hipLaunchKernelGGL(hist_dots_kernel, grid, dim3(256), 0, s, a);
-}
-
-// Scalar L-BFGS logic per problem: reduce the inner products, update the
-// history, and derive the next direction's coefficients from the two-loop
-// recursion; sets status = SEARCH with the first trial step.
-//   mode 0: after an accepted (or failed) search; 1: gradient refreshed at
-//   the same keys; 2: start (history cleared).
-__global__ __launch_bounds__(64) void prepare_kernel(PrepArgs a) {
-  const int p = blockIdx.x;
-  LbState* st = a.st + p;
-  const int status = st->status;
-  if (a.mode == 0 && status != ST_ACCEPT && status != ST_FAIL) return;
-  __shared__ double d[kDots];
-  const int tid = threadIdx.x;
-  const bool use_dots = !(a.mode == 0 && status == ST_FAIL);
-  if (use_dots) {
-    for (int i = tid; i < kDots; i += 64) {
-      double s = 0.0;
-      for (int b = 0; b < a.nwg; ++b) s += a.part[((size_t)p * a.nwg + b) * kDots + i];
-      d[i] = s;
-    }
+  // arrival: the last workgroup of this problem runs the scalar logic
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    const unsigned prev = atomicAdd(a.counter + p, 1u);
+    s_last = (prev == gridDim.x - 1);
   }
   __syncthreads();
-  if (tid != 0) return;
-  const int H = a.history;
-  if (a.mode == 2 || (a.mode == 0 && status == ST_FAIL)) {
-    if (a.mode == 0) st->flags |= KVS_FLAG_LINESEARCH;
-    st->count = 0;
-    st->stage = 0;
-  }
-  if (a.mode == 0 && status == ST_ACCEPT) {
-    const int stg = st->stage;
-    const double sy = d[5 * stg + 0], yy = d[5 * stg + 2], ss = d[5 * kSlots + 1];
-    if (sy > a.curv_eps * sqrt(ss) * sqrt(yy)) {
-      st->rho[stg] = 1.0 / sy;
-      for (int t = 0; t < st->count; ++t) {
-        const int j = st->order[t];
-        st->SY[stg][j] = d[5 * j + 0];
-        st->SY[j][stg] = d[5 * j + 1];
-        st->YY[stg][j] = d[5 * j + 2];
-        st->YY[j][stg] = d[5 * j + 2];
-      }
-      st->SY[stg][stg] = sy;
-      st->YY[stg][stg] = yy;
-      if (st->count < H) {
-        st->order[st->count++] = stg;
-        // next free slot: the smallest not in the history
-        int fr = 0;
-        for (; fr < kSlots; ++fr) {
-          bool used = false;
-          for (int t = 0; t < st->count; ++t) used |= (st->order[t] == fr);
-          if (!used) break;
+  if (!s_last) return;
+  __threadfence();
+
+  __shared__ double tree[64][E];
+  __shared__ double d[E];
+  __shared__ LbState ls;
+  if (compute) {
+    // fold chunk c, c+64, c+128, ... (in that order) into row c of the tree;
+    // entries not written this launch read as zero
+    constexpr int PERT = (64 * E + 255) / 256;
+    const double* src = a.part + (size_t)p * a.nch * E;
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < 64 * E) {
+        const int c = idx / E, i = idx % E;
+        const bool wanted = (i < 5 * nvis) || (i >= 5 * MS);
+        double s = 0.0;
+        if (wanted) {
+          // straight-line first two chunks so all loads of a thread issue together
+          const double s0 = (c < a.nch) ? src[(size_t)c * E + i] : 0.0;
+          const double s1 = (c + 64 < a.nch) ? src[(size_t)(c + 64) * E + i] : 0.0;
+          s = s0 + s1;
+          for (int cc = c + 128; cc < a.nch; cc += 64) s += src[(size_t)cc * E + i];
         }
-        st->stage = fr;
-      } else {
-        const int old = st->order[0];
-        for (int t = 1; t < H; ++t) st->order[t - 1] = st->order[t];
-        st->order[H - 1] = stg;
-        st->stage = old;
+        tree[c][i] = s;
       }
     }
+    __syncthreads();
+    for (int half = 32; half > 0; half >>= 1) {
+      for (int idx = tid; idx < half * E; idx += 256) {
+        const int c = idx / E, i = idx % E;
+        tree[c][i] += tree[c + half][i];
+      }
+      __syncthreads();
+    }
+    if (tid < E) d[tid] = tree[0][tid];
   }
-  if (use_dots) {
-    for (int j = 0; j < kSlots; ++j) {
-      st->Sg[j] = d[5 * j + 3];
-      st->Yg[j] = d[5 * j + 4];
-    }
-    st->gg = d[5 * kSlots];
+  {
+    const unsigned long long* s8 = reinterpret_cast<const unsigned long long*>(gst);
+    unsigned long long* d8 = reinterpret_cast<unsigned long long*>(&ls);
+    for (int i = tid; i < (int)(sizeof(LbState) / 8); i += 256) d8[i] = s8[i];
   }
-
-  // two-loop recursion through inner products
-  const int m = st->count;
-  const double gg = st->gg;
-  double gtp, a0;
-  for (int j = 0; j < kSlots; ++j) { st->cs[j] = 0.0; st->cy[j] = 0.0; }
-  if (m > 0) {
-    double al[kHistMax], be[kHistMax];
-    for (int i = m - 1; i >= 0; --i) {
-      const int oi = st->order[i];
-      double t = st->Sg[oi];
-      for (int j = i + 1; j < m; ++j) t -= al[j] * st->SY[oi][st->order[j]];
-      al[i] = st->rho[oi] * t;
-    }
-    const int on = st->order[m - 1];
-    const double gamma = st->SY[on][on] / st->YY[on][on];
-    for (int i = 0; i < m; ++i) {
-      const int oi = st->order[i];
-      double t = st->Yg[oi];
-      for (int j = 0; j < m; ++j) t -= al[j] * st->YY[oi][st->order[j]];
-      double yr = gamma * t;
-      for (int j = 0; j < i; ++j) yr += (al[j] - be[j]) * st->SY[st->order[j]][oi];
-      be[i] = st->rho[oi] * yr;
-    }
-    double gtr = gamma * gg;
-    for (int j = 0; j < m; ++j) {
-      const int oj = st->order[j];
-      gtr += -gamma * al[j] * st->Yg[oj] + (al[j] - be[j]) * st->Sg[oj];
-      st->cy[oj] = gamma * al[j];
-      st->cs[oj] = -(al[j] - be[j]);
-    }
-    st->coef_g = -gamma;
-    gtp = -gtr;
-    a0 = 1.0;
-    if (!(gtp < 0.0)) {
-      st->flags |= KVS_FLAG_NONDESCENT;
-      st->count = 0;
-      st->stage = 0;
-      for (int j = 0; j < kSlots; ++j) { st->cs[j] = 0.0; st->cy[j] = 0.0; }
-    }
+  lbfgs_scalar<MS>(&ls, d, a.mode, a.history, a.curv_eps);
+  {
+    const unsigned long long* s8 = reinterpret_cast<const unsigned long long*>(&ls);
+    unsigned long long* d8 = reinterpret_cast<unsigned long long*>(gst);
+    for (int i = tid; i < (int)(sizeof(LbState) / 8); i += 256) d8[i] = s8[i];
   }
-  if (st->count == 0) {
-    st->coef_g = -1.0;
-    gtp = -gg;
-    a0 = 1.0 / fmax(1.0, sqrt(gg));
-  }
-  st->gtp = gtp;
-  st->alpha = a0;
-  st->trials = 0;
-  st->status = ST_SEARCH;
+  if (tid == 0) a.counter[p] = 0u;
 }
 
-void launch_prepare(const PrepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(prepare_kernel, dim3(a.P), dim3(64), 0, s, a);
+void launch_dots(const DotsArgs& a, hipStream_t s) {
+  dim3 grid(a.nch, a.P);
+  if (a.history <= 10) hipLaunchKernelGGL((dots_kernel<11>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((dots_kernel<kSlots>), grid, dim3(256), 0, s, a);
 }
 
+// --------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void direction_kernel(DirArgs a) {
   const int p = blockIdx.y;
   const LbState* st = a.st + p;
   if (st->status != ST_SEARCH) return;
   const ProbInfo pi = a.info[p];
   const long long n4 = (long long)pi.k * a.d / 4;
+  const long long e = (long long)blockIdx.x * kVec4PerWG + threadIdx.x;
+  if (e >= n4) return;
   const long long base4 = (long long)pi.koff * a.d / 4;
   const long long stride4 = (long long)a.ktot * a.d / 4;
-  const long long beg = (long long)blockIdx.x * kVecPerWG;
-  if (beg >= n4) return;
   const int m = st->count;
-  const float cg = (float)st->coef_g;
-  f32x4* Pd = reinterpret_cast<f32x4*>(a.p) + base4;
   const f32x4* G = reinterpret_cast<const f32x4*>(a.g) + base4;
   const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
   const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
-  constexpr int PER = kVecPerWG / 256;
-  f32x4 acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const long long e = beg + threadIdx.x + 256 * i;
-    acc[i] = (e < n4) ? G[e] * cg : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  f32x4 acc = G[e] * (float)st->coef_g;
   for (int t = 0; t < m; ++t) {
     const int j = st->order[t];
-    const float cs = (float)st->cs[j], cy = (float)st->cy[j];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const long long e = beg + threadIdx.x + 256 * i;
-      if (e < n4) acc[i] += S[(size_t)j * stride4 + e] * cs + Yv[(size_t)j * stride4 + e] * cy;
-    }
+    acc += S[(size_t)j * stride4 + e] * (float)st->cs[j] + Yv[(size_t)j * stride4 + e] * (float)st->cy[j];
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const long long e = beg + threadIdx.x + 256 * i;
-    if (e < n4) Pd[e] = acc[i];
-  }
+  reinterpret_cast<f32x4*>(a.p)[base4 + e] = acc;
 }
 
 void launch_direction(const DirArgs& a, hipStream_t s) {
-  dim3 grid(a.nwg, a.P);
+  dim3 grid(a.nch, a.P);
   hipLaunchKernelGGL(direction_kernel, grid, dim3(256), 0, s, a);
 }
 
+// --------------------------------------------------------------------------
 __global__ void state_init_kernel(LbState* st, int P, int clear) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= P) return;

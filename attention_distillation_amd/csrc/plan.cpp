@@ -70,18 +70,14 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   const long long qtiles = (p.n + 63) / 64;
   p.Cref = split_for((long long)p.P * qtiles, (p.Z + 63) / 64);
   p.C = split_for((long long)p.P * qtiles, (p.kmax + 63) / 64);
-  p.Cn = split_for((long long)p.P * ((p.kmax + 63) / 64), (int)qtiles);
+  p.Cn = std::max(1, split_for((long long)p.P * ((p.kmax + 63) / 64), (int)qtiles) / 2);
   const int KT = p.kpadmax / kTile;
   const long long gtiles = (long long)KT * (KT + 1) / 2 + (long long)(p.d / kTile) * KT;
   p.Cg = split_for((long long)p.P * gtiles, (int)qtiles);
   p.Cq = split_for((long long)p.P * ((p.Z + 63) / 64), (int)qtiles);
   p.nblk = merge_blocks(p.n);
-  {
-    // L-BFGS vector kernels: 4096 floats (1024 float4) per workgroup
-    const long long per = (p.kmax * (long long)p.d + 4095) / 4096;
-    p.nwg = (int)std::max<long long>(1, per);
-  }
-
+  p.nchv = vec_chunks((long long)p.kmax * p.d);
+  p.nchd = dots_chunks((long long)p.kmax * p.d);
   const int Cmax = std::max(p.Cref, p.C);
   const size_t f = 4;
   size_t off = 0;
@@ -95,6 +91,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_status, sizeof(int) * p.P);
   take(p.r_flags, sizeof(int) * p.P);
   take(p.r_loss, sizeof(float) * p.P);
+  take(p.r_cnt, sizeof(unsigned) * 2 * p.P);
   take(p.r_yref, f * p.P * p.n * p.d);
   take(p.r_lseref, f * p.P * p.n);
   take(p.r_St, f * p.stot);
@@ -113,9 +110,11 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_mu, sizeof(double) * p.P);
   take(p.r_cinfo, sizeof(int) * p.P);
   take(p.r_X, f * (size_t)p.kpadtot * p.d);
+  take(p.r_Dinv, f * (size_t)p.kpadtot * kTile);
+  take(p.r_Ldiag, f * (size_t)p.kpadtot * kTile);
   take(p.r_imp, f * 2 * (size_t)p.Cq * p.P * p.Z);
   take(p.r_idx, sizeof(int) * (size_t)p.ktot);
-  take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nwg * kDots);
+  take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nchd * kDots);
   take(p.r_g, f * (size_t)p.ktot * p.d);
   take(p.r_p, f * (size_t)p.ktot * p.d);
   take(p.r_S, f * (size_t)(H + 1) * p.ktot * p.d);
