@@ -37,6 +37,7 @@ struct kvs_ctx_s {
   hipStream_t stream = nullptr;
   std::string err;
   int device = 0;
+  int lds_max = 0;          // dynamic LDS bytes per workgroup on this device
   bool logit_f64 = true;
   bool prof = false;
   int prof_mask = 0;
@@ -257,7 +258,7 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   r.info = g.info; r.P = pl.P; r.Cg = pl.Cg; r.kpadmax = pl.kpadmax; r.mtot = pl.mtot;
   launch_gram_reduce(r, pl.d, ctx->stream);
   CholArgs c{};
-  c.M = M; c.Ldiag = at<float>(ws, pl.r_Ldiag); c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
+  c.M = M; c.Dinv = at<float>(ws, pl.r_Dinv); c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
   c.st = st; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
   c.ridge_rel = b->ridge_rel;
   launch_mu(c, ctx->stream);
@@ -267,9 +268,9 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
     launch_chol_step(c, pl.d, j, ctx->stream);
   }
   BackArgs bk{};
-  bk.M = M; bk.Ldiag = c.Ldiag; bk.X = at<float>(ws, pl.r_X); bk.Dinv = at<float>(ws, pl.r_Dinv); bk.Vc = Vc;
+  bk.M = M; bk.X = at<float>(ws, pl.r_X); bk.Dinv = c.Dinv; bk.Vc = Vc;
   bk.info_out = c.info_out; bk.flags = flags; bk.st = st; bk.active_mask = mask; bk.info = g.info;
-  bk.P = pl.P; bk.d = pl.d; bk.kpadmax = pl.kpadmax;
+  bk.P = pl.P; bk.d = pl.d; bk.kpadmax = pl.kpadmax; bk.lds_max = ctx->lds_max;
   {
     double fl = 0;
     for (const auto& q : pl.info) fl += 1.0 * q.kpad * q.kpad * pl.d;
@@ -430,6 +431,10 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
   if (!c) return KVS_ERR_INVALID;
   c->stream = static_cast<hipStream_t>(hip_stream);
   if (hipGetDevice(&c->device) != hipSuccess) c->device = 0;
+  int lds = 0;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) == hipSuccess)
+    c->lds_max = lds;
+  (void)hipGetLastError();
   const char* env = getenv("KVS_LOGITS_FP32");
   c->logit_f64 = !(env && env[0] == '1');
   *out = c;

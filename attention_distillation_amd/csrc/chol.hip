@@ -5,8 +5,8 @@
 // the batch (problems whose kpad is exhausted exit at once); see
 // chol_step_kernel.  The panel solves of the rows below kpad (the Y^T A rows)
 // are the forward substitution L W = A^T Y.
-// diag_inv_kernel inverts the 64x64 diagonal blocks of L in parallel, then
-// back_subst_kernel solves L^T X = W for 16 value columns per workgroup,
+// The workgroup that factors a diagonal block also inverts it (for the back
+// substitution); back_subst_kernel solves L^T X = W for 16 value columns per workgroup,
 // 64-row blocks from the bottom up, every block step on MFMA.
 #include "../../include/kvsculpt.h"
 #include "kvs_internal.h"
@@ -108,9 +108,10 @@ __device__ __forceinline__ void tile_updated_to_lds(const float* __restrict__ Mp
 //    block j.  Each applies the update of panel j-1 to its tile and to the
 //    diagonal block (redundantly; nobody writes the diagonal block of M in
 //    this launch), factors the diagonal block in one wave (lane r owns row r,
-//    each factored column broadcast through LDS), then solves X L_jj^T = tile (right-looking,
-//    independent updates per step).  The factored diagonal block goes to
-//    Ldiag; the panel tiles are overwritten in place.
+//    each column broadcast through LDS), then solves X L_jj^T = tile (right-looking,
+//    independent updates per step).  The panel tiles are overwritten in
+//    place; the diagonal workgroup solves against the identity instead and
+//    writes inv(L_jj) to Dinv.
 //  - trailing workgroups: the update of panel j-1 for the tiles (I, J) with
 //    J >= j+1, which no panel workgroup touches.
 template <int D>
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   __shared__ float Dl[64][65];
   __shared__ float Tl[64][65];
   __shared__ float Lt[64][68];      // Lt[c][t] = L[t][c]: column c as a contiguous row
+  __shared__ float Rd[64];          // 1 / L[c][c]
   tile_updated_to_lds(Mp, ld, 64 * j, 64 * j, 64 * j, j, Dl);
   if (I != j) tile_updated_to_lds(Mp, ld, rowof(I), 64 * j, 64 * j, j, Tl);
   __syncthreads();
@@ -174,58 +176,76 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   for (int c = 0; c < 64; ++c)
     if (c == r && real_row) L[c] += mu;
 
+  // Right-looking factorisation with one LDS round trip per column: every
+  // lane publishes its entry of the unscaled column c, reads the whole column
+  // back (pivot included), and applies a_rt -= a_rc a_tc / a_cc.
   int badcol = -1;
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
     Lt[c][r] = L[c];
     wave_sync();
-    const float piv = Lt[c][c];
+    const int c4 = c & ~3;
+    f32x4 col[16];
+#pragma unroll
+    for (int t4 = c4; t4 < 64; t4 += 4) col[t4 / 4] = *(const f32x4*)&Lt[c][t4];
+    const float piv = col[c / 4][c % 4];
     if (!(piv > 0.f) && badcol < 0) badcol = c;
     const float dgn = sqrtf(piv);
     const float inv = __frcp_rn(dgn);
-    L[c] = (r == c) ? dgn : ((r > c) ? L[c] * inv : L[c]);
-    Lt[c][r] = L[c];
-    wave_sync();
-    // rank-1 update of the columns to the right with the broadcast column c
+    const float f = L[c] * (inv * inv);
 #pragma unroll
-    for (int t4 = (c + 1) & ~3; t4 < 64; t4 += 4) {
-      const f32x4 lc = *(const f32x4*)&Lt[c][t4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (t4 + e > c) L[t4 + e] = fmaf(-L[c], lc[e], L[t4 + e]);
-    }
+    for (int t = c + 1; t < 64; ++t) L[t] = fmaf(-f, col[t / 4][t % 4], L[t]);
+    L[c] = (r == c) ? dgn : L[c] * inv;
+    __builtin_amdgcn_sched_barrier(0);
   }
-
-  if (I == j) {
-    float* dst = a.Ldiag + ((size_t)pi.xoff / D + 64 * j + r) * 64;
+  // the factor (zero above the diagonal), column c as row c of Lt
 #pragma unroll
-    for (int c = 0; c < 64; c += 4) {
-      f32x4 v;
-      v.x = (c + 0 <= r) ? L[c + 0] : 0.f;
-      v.y = (c + 1 <= r) ? L[c + 1] : 0.f;
-      v.z = (c + 2 <= r) ? L[c + 2] : 0.f;
-      v.w = (c + 3 <= r) ? L[c + 3] : 0.f;
-      *(f32x4*)(dst + c) = v;
-    }
-    if (r == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * j + badcol + 1;
-    return;
-  }
+  for (int c = 0; c < 64; ++c) Lt[c][r] = (c <= r) ? L[c] : 0.f;
+  wave_sync();
+  Rd[r] = __frcp_rn(Lt[r][r]);
+  wave_sync();
 
-  // X L^T = T, right-looking: x_c = t_c / L_cc, then t_t -= x_c L_tc (t > c);
-  // Lt holds the factored columns
+  // X L^T = T, right-looking: x_c = t_c / L_cc, then t_t -= x_c L_tc (t > c).
+  // Software-pipelined by hand: the reads of column c+1 are issued at the
+  // start of step c (nothing in the loop writes LDS).
   float x[64];
+  if (I == j) {
+    // diagonal workgroup: T = identity, so lane r ends with row r of
+    // inv(L)^T, i.e. column r of inv(L)
 #pragma unroll
-  for (int c = 0; c < 64; ++c) x[c] = Tl[r][c];
+    for (int c = 0; c < 64; ++c) x[c] = (c == r) ? 1.f : 0.f;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 64; ++c) x[c] = Tl[r][c];
+  }
+  f32x4 cur[16];
+  float rcur = Rd[0];
+#pragma unroll
+  for (int t4 = 0; t4 < 64; t4 += 4) cur[t4 / 4] = *(const f32x4*)&Lt[0][t4];
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
-    x[c] = x[c] * __frcp_rn(Lt[c][c]);
+    f32x4 nxt[16];
+    float rnxt = 0.f;
+    if (c + 1 < 64) {
+      rnxt = Rd[c + 1];
 #pragma unroll
-    for (int t4 = (c + 1) & ~3; t4 < 64; t4 += 4) {
-      const f32x4 lc = *(const f32x4*)&Lt[c][t4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (t4 + e > c) x[t4 + e] = fmaf(-x[c], lc[e], x[t4 + e]);
+      for (int t4 = (c + 2) & ~3; t4 < 64; t4 += 4) nxt[t4 / 4] = *(const f32x4*)&Lt[c + 1][t4];
     }
+    x[c] = x[c] * rcur;
+#pragma unroll
+    for (int t = c + 1; t < 64; ++t) x[t] = fmaf(-x[c], cur[t / 4][t % 4], x[t]);
+#pragma unroll
+    for (int t4 = (c + 2) & ~3; t4 < 64; t4 += 4) cur[t4 / 4] = nxt[t4 / 4];
+    rcur = rnxt;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (I == j) {
+    // Dinv block j, row-major: Dinv[c][r] = inv(L)[c][r] = x[c] of lane r
+    float* dst = a.Dinv + ((size_t)pi.xoff / D + 64 * j) * 64;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) dst[c * 64 + r] = x[c];
+    if (r == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * j + badcol + 1;
+    return;
   }
   float* xr = Mp + (size_t)(rowof(I) + r) * ld + 64 * j;
 #pragma unroll
@@ -240,47 +260,6 @@ void launch_chol_step(const CholArgs& a, int d, int j, hipStream_t s) {
   dim3 grid(Rmax + ntrail, a.P);
   if (d == 128) hipLaunchKernelGGL((chol_step_kernel<128>), grid, dim3(256), 0, s, a, j, Rmax, nJ > 0 ? nJ : 1);
   else hipLaunchKernelGGL((chol_step_kernel<64>), grid, dim3(256), 0, s, a, j, Rmax, nJ > 0 ? nJ : 1);
-}
-
-// Inverse of every 64x64 diagonal block of L (one wave per block, lane c
-// computes column c by forward substitution; the block is broadcast from
-// LDS).  Padding blocks are the identity.  Dinv is [sum KT][64][64].
-__global__ __launch_bounds__(64) void diag_inv_kernel(BackArgs a) {
-  const int p = blockIdx.y;
-  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
-  const ProbInfo pi = a.info[p];
-  const int KT = pi.kpad / 64;
-  const int blk = blockIdx.x;
-  if (blk >= KT) return;
-  __shared__ float Ls[64][65];
-  const int c = threadIdx.x;
-  const float* Lb = a.Ldiag + ((size_t)pi.xoff / a.d + 64 * blk) * 64;
-  for (int e = c; e < 64 * 64; e += 64) Ls[e >> 6][e & 63] = Lb[e];
-  __syncthreads();
-  // column c of inv(L): forward substitution L x = e_c; each row's sum is
-  // split over four independent accumulators to shorten the dependency chain
-  float x[64];
-#pragma unroll
-  for (int r = 0; r < 64; ++r) {
-    float s0 = (r == c) ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-    for (int t = 0; t + 3 < r; t += 4) {
-      s0 = fmaf(-Ls[r][t], x[t], s0);
-      s1 = fmaf(-Ls[r][t + 1], x[t + 1], s1);
-      s2 = fmaf(-Ls[r][t + 2], x[t + 2], s2);
-      s3 = fmaf(-Ls[r][t + 3], x[t + 3], s3);
-    }
-#pragma unroll
-    for (int t = r & ~3; t < r; ++t) s0 = fmaf(-Ls[r][t], x[t], s0);
-    x[r] = ((s0 + s1) + (s2 + s3)) / Ls[r][r];
-    __asm__ __volatile__("" ::: "memory");   // keep each row's LDS reads in its own step
-  }
-  // one wave: every lane has finished reading Ls, so it can hold the result
-#pragma unroll
-  for (int r = 0; r < 64; ++r) Ls[r][c] = x[r];
-  __syncthreads();
-  float* dst = a.Dinv + ((size_t)pi.xoff / a.d / 64 + blk) * 64 * 64;
-  for (int e = c; e < 64 * 64; e += 64) dst[e] = Ls[e >> 6][e & 63];
 }
 
 // Solve L^T X = W for 16 value columns per workgroup, 64-row blocks from the
@@ -370,9 +349,116 @@ __global__ __launch_bounds__(256) void back_subst_kernel(BackArgs a) {
   }
 }
 
+// Same solve with the right-hand side W held in LDS ([kpad][16] floats,
+// dynamic shared memory) for the whole back substitution: only the L blocks
+// and inv(L_ii) come from global memory, and the L-block loads of a step are
+// issued before its diagonal solve so their latency overlaps it.
+template <int D>
+__global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
+  extern __shared__ float Wl[];          // [kpadmax][16], then Xs [64][16]
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int KT = pi.kpad / 64, ld = pi.kpad;
+  const float* __restrict__ Mp = a.M + pi.moff;
+  const int dim0 = 16 * blockIdx.x;
+  const float* __restrict__ Dinv = a.Dinv + (size_t)pi.xoff / D / 64 * 64 * 64;
+  float* Xs = Wl + (size_t)a.kpadmax * 16;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+
+  // W[row][c] = M[kpad + dim0 + c][row]: coalesced float4 reads along the row
+  for (int e = tid; e < pi.kpad * 4; e += 256) {
+    const int c = e / (pi.kpad / 4), r4 = e % (pi.kpad / 4);
+    const f32x4 v = *(const f32x4*)(Mp + (size_t)(pi.kpad + dim0 + c) * ld + 4 * r4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Wl[(4 * r4 + u) * 16 + c] = v[u];
+  }
+  __syncthreads();
+
+  auto load_block = [&](float (&av)[4][16], int i, int rb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2)
+        av[q][s2] = -Mp[(size_t)(64 * i + 4 * s2 + g) * ld + 64 * rb + 16 * q + lq];
+  };
+  // W_rb += (-L_{i,rb})^T X_i, accumulator seeded with W_rb
+  auto update_block = [&](const float (&av)[4][16], const float (&bx)[16], int rb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = Wl[(64 * rb + 16 * q + 4 * g + r) * 16 + lq];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q][s2], bx[s2], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Wl[(64 * rb + 16 * q + 4 * g + r) * 16 + lq] = acc[r];
+    }
+  };
+
+  for (int i = KT - 1; i >= 0; --i) {
+    float av0[4][16], av1[4][16];
+    const int rb0 = wave, rb1 = wave + 4;
+    if (rb0 < i) load_block(av0, i, rb0);
+    if (rb1 < i) load_block(av1, i, rb1);
+    // X_i rows b = 16 wave + (4g + r): sum_a inv(L_ii)[a][b] W_i[a][c]
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    {
+      const float* Di = Dinv + (size_t)i * 64 * 64;
+      float dv[16], wv[16];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        dv[s2] = Di[(4 * s2 + g) * 64 + 16 * wave + lq];
+        wv[s2] = Wl[(64 * i + 4 * s2 + g) * 16 + lq];
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) x = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[s2], wv[s2], x, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Xs[(16 * wave + 4 * g + r) * 16 + lq] = x[r];
+    }
+    __syncthreads();
+    // every wave has read W_i: it now holds X_i
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Wl[(64 * i + 16 * wave + 4 * g + r) * 16 + lq] = x[r];
+    if (i > 0) {
+      float bx[16];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) bx[s2] = Xs[(4 * s2 + g) * 16 + lq];
+      if (rb0 < i) update_block(av0, bx, rb0);
+      if (rb1 < i) update_block(av1, bx, rb1);
+      for (int rb = wave + 8; rb < i; rb += 8) {
+        load_block(av0, i, rb);
+        if (rb + 4 < i) load_block(av1, i, rb + 4);
+        update_block(av0, bx, rb);
+        if (rb + 4 < i) update_block(av1, bx, rb + 4);
+      }
+    }
+    __syncthreads();
+  }
+
+  const bool ok = a.info_out[p] == 0;
+  if (ok) {
+    for (int e = tid; e < pi.k * 16; e += 256) {
+      const int row = e >> 4, c = e & 15;
+      a.Vc[(size_t)(pi.koff + row) * D + dim0 + c] = Wl[row * 16 + c];
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0 && !ok) {
+    if (a.flags) a.flags[p] |= KVS_FLAG_CHOLESKY;
+    if (a.st) a.st[p].flags |= KVS_FLAG_CHOLESKY;
+  }
+}
+
+size_t back_subst_lds_bytes(int kpadmax) { return ((size_t)kpadmax * 16 + 64 * 16) * sizeof(float); }
+
 void launch_back_subst(const BackArgs& a, int d, hipStream_t s) {
-  hipLaunchKernelGGL(diag_inv_kernel, dim3(a.kpadmax / 64, a.P), dim3(64), 0, s, a);
   dim3 grid(d / 16, a.P);
+  const size_t lds = back_subst_lds_bytes(a.kpadmax);
+  if (lds <= (size_t)a.lds_max) {
+    if (d == 128) hipLaunchKernelGGL((back_subst_lds_kernel<128>), grid, dim3(256), lds, s, a);
+    else hipLaunchKernelGGL((back_subst_lds_kernel<64>), grid, dim3(256), lds, s, a);
+    return;
+  }
   if (d == 128) hipLaunchKernelGGL((back_subst_kernel<128>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((back_subst_kernel<64>), grid, dim3(256), 0, s, a);
 }

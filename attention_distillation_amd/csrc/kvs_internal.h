@@ -115,7 +115,7 @@ struct GramReduceArgs {
 void launch_gram_reduce(const GramReduceArgs& a, int d, hipStream_t s);
 
 struct CholArgs {
-  float* M; float* Ldiag; const double* trpart; double* mu; int* info_out;
+  float* M; float* Dinv; const double* trpart; double* mu; int* info_out;
   const LbState* st; int active_mask;
   const ProbInfo* info; int P, kpadmax; double ridge_rel;
 };
@@ -123,10 +123,12 @@ void launch_mu(const CholArgs& a, hipStream_t s);
 void launch_chol_step(const CholArgs& a, int d, int panel, hipStream_t s);
 
 struct BackArgs {
-  const float* M; const float* Ldiag; float* X; float* Dinv; float* Vc; const int* info_out; int* flags;
+  const float* M; float* X; const float* Dinv; float* Vc; const int* info_out; int* flags;
   LbState* st; int active_mask;
   const ProbInfo* info; int P, d, kpadmax;
+  int lds_max;   // dynamic LDS bytes a workgroup may use (0: solve in global memory)
 };
+size_t back_subst_lds_bytes(int kpadmax);
 void launch_back_subst(const BackArgs& a, int d, hipStream_t s);
 
 struct ImpArgs {

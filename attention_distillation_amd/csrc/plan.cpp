@@ -111,7 +111,6 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_cinfo, sizeof(int) * p.P);
   take(p.r_X, f * (size_t)p.kpadtot * p.d);
   take(p.r_Dinv, f * (size_t)p.kpadtot * kTile);
-  take(p.r_Ldiag, f * (size_t)p.kpadtot * kTile);
   take(p.r_imp, f * 2 * (size_t)p.Cq * p.P * p.Z);
   take(p.r_idx, sizeof(int) * (size_t)p.ktot);
   take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nchd * kDots);

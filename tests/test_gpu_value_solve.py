@@ -11,8 +11,8 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
 
-def _setup(w, kfun, perturb=0.0, seed=0):
-    b = make_batch(w, seed)
+def _setup(w, kfun, perturb=0.0, seed=0, problems=None):
+    b = make_batch(w, seed, problems=problems)
     P, n, d = b["Q"].shape
     Z = b["Kz"].shape[1]
     s = b["scale"]
@@ -40,6 +40,11 @@ CASES = {
     # and only mu keeps it definite (happens after budget reallocation)
     "rank-deficient": (tiny_workload(d=128, N=330, m=10, g=2, F=40, layers=1, kv_heads=2),
                        lambda p, Z: [320, 150][p], 0.0),
+    # llama3-8b-shaped head (n=5120, Z=7936) at its uniform k0 = 2381 and
+    # above it: the right-hand side of the back substitution fits in one
+    # workgroup's LDS for the first and not for the second
+    "llama3-8b-k2381": (WORKLOADS[3], lambda p, Z: 2381, 0.0, [0]),
+    "llama3-8b-k2600": (WORKLOADS[3], lambda p, Z: 2600, 0.0, [5]),
 }
 
 
@@ -47,8 +52,8 @@ CASES = {
     reason="fp32 Cholesky loses accuracy when k > n (rank-deficient Gram)", strict=False))
     if c == "rank-deficient" else c for c in CASES])
 def test_value_solve_matches_oracle(name):
-    w, kfun, pert = CASES[name]
-    b, probs = _setup(w, kfun, pert)
+    w, kfun, pert, *sel = CASES[name]
+    b, probs = _setup(w, kfun, pert, problems=sel[0] if sel else None)
     P, n, d = b["Q"].shape
     Z = b["Kz"].shape[1]
     ks = [pr[3].shape[0] for pr in probs]
