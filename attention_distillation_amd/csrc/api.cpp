@@ -122,8 +122,11 @@ struct Prof {
 };
 
 // Algorithmic work of the contraction kernels over the active problems.
+// want < 0: the active set is not known at launch (device-driven slots);
+// the work is added afterwards from the per-problem trial counters.
 double sum_k(const Plan& pl, const std::vector<int>* hs, int want) {
   double s = 0;
+  if (want < 0) return 0;
   for (int p = 0; p < pl.P; ++p)
     if (!hs || (*hs)[p] == want) s += pl.info[p].k;
   return s;
@@ -298,10 +301,10 @@ void run_init_topk(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
   launch_topk(ta, ctx->stream);
   launch_fill_f32(Vc, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
   run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
-  run_value_solve(ctx, pl, b, Y, Vc, flags, st, 0xF, ws);
+  run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws);
 }
 
-constexpr int kAll = 0xF;
+constexpr int kAll = kAllStates;
 
 struct LbBuffers {
   LbState* st;
@@ -322,8 +325,10 @@ LbBuffers lb_in_state(const Plan& pl, void* state, void* ws) {
                    at<int>(ws, pl.r_status)};
 }
 
-void lb_dots(kvs_ctx ctx, const Plan& pl, const LbBuffers& B, void* ws, int mode, int mask) {
+void lb_dots(kvs_ctx ctx, const Plan& pl, const LbBuffers& B, void* ws, int mode, int mask,
+             int target = 0x7fffffff) {
   DotsArgs d{};
+  d.target = target; d.status_view = B.status_view;
   d.g = B.g; d.S = B.S; d.Yh = B.Yh; d.st = B.st; d.active_mask = mask; d.mode = mode;
   d.history = pl.H; d.curv_eps = 1e-10; d.part = B.hpart; d.counter = at<unsigned>(ws, pl.r_cnt) + pl.P;
   d.info = at<ProbInfo>(ws, pl.r_info); d.P = pl.P; d.d = pl.d; d.ktot = (int)pl.ktot; d.nch = pl.nchd;
@@ -387,7 +392,52 @@ kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const k
   return KVS_OK;
 }
 
-// The whole alternating schedule on the plan's batch.
+// One device-driven slot of the L-BFGS schedule: every kernel acts only on
+// the problems whose status asks for it, so a slot advances each problem by
+// one step of its own state machine (direction and first trial, or a further
+// trial; gradient and history after an accepted or failed search).  A slot
+// needs no host decision, so slots are enqueued back to back.
+void lb_slot(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o, const float* Q,
+             const float* Y, const float* lse, float* Kc, const float* Vc, const LbBuffers& B, void* ws,
+             int target) {
+  DirArgs da{};
+  da.p = B.p; da.g = B.g; da.S = B.S; da.Yh = B.Yh; da.st = B.st; da.info = at<ProbInfo>(ws, pl.r_info);
+  da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nch = pl.nchv;
+  {
+    Prof pr(ctx, PROF_DIR, 0, 0);
+    launch_direction(da, ctx->stream);
+  }
+  std::vector<int> none;
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws, &none, -1);
+  run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, ws, &none, -1);
+  GradUpdArgs g = grad_args(pl, b, ws, B.st, 1 << ST_ACCEPT, 0);
+  g.x = Kc; g.p = B.p; g.g = B.g; g.S = B.S; g.Yh = B.Yh;
+  launch_grad_update(g, ctx->stream);
+  lb_dots(ctx, pl, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL), target);
+}
+
+// Contraction work of the device-driven slots, from the per-problem trial and
+// accept counters (profiling only: one state read-back per call).
+void prof_add_slot_work(kvs_ctx ctx, const Plan& pl, const LbState* st) {
+  if (!ctx->prof) return;
+  std::vector<LbState> h(pl.P);
+  if (hipMemcpyAsync(h.data(), st, sizeof(LbState) * pl.P, hipMemcpyDeviceToHost, ctx->stream) != hipSuccess ||
+      hipStreamSynchronize(ctx->stream) != hipSuccess)
+    return;
+  double fw = 0, bw = 0;
+  for (int p = 0; p < pl.P; ++p) {
+    fw += (double)h[p].n_trial * pl.info[p].k;
+    bw += (double)h[p].n_accept * pl.info[p].k;
+  }
+  ctx->acc[PROF_FWD].flops += 4.0 * pl.n * pl.d * fw;
+  ctx->acc[PROF_BWD].flops += 4.0 * pl.n * pl.d * bw;
+}
+
+// The whole alternating schedule on the plan's batch.  Iterations run in
+// blocks that end at the value solves: each block enqueues one slot per
+// iteration, then reads the per-problem status once; problems that needed
+// extra line-search trials get further slots until every problem has done
+// the block's iterations.
 kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
                          const float* Q, const float* Kz, const float* Vz, float* Kc, float* Vc,
                          float* loss, float* mse, float* init_loss, int* flags, void* ws) {
@@ -399,15 +449,39 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
   run_init_topk(ctx, pl, b, Q, Kz, Yr, lr, at<int>(ws, pl.r_idx), Kc, Vc, nullptr, B.st, ws);
   lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws);
   bool refreshed = true;
-  std::vector<int> hs;
-  for (int t = 1; t <= o->iters; ++t) {
+  std::vector<int> hs(pl.P);
+  int done = 0;
+  while (done < o->iters) {
+    const int blk = std::min(o->vc_every - done % o->vc_every, o->iters - done);
+    int slots = 0;
+    for (; slots < blk; ++slots) lb_slot(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, blk);
     bool any_fail = false;
-    kvs_status s = lb_iteration(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, &any_fail, hs);
-    if (s != KVS_OK) return s;
+    for (;;) {
+      if (hipMemcpyAsync(hs.data(), B.status_view, sizeof(int) * pl.P, hipMemcpyDeviceToHost,
+                         ctx->stream) != hipSuccess ||
+          hipStreamSynchronize(ctx->stream) != hipSuccess)
+        return fail(ctx, KVS_ERR_HIP, "schedule: %s", hipGetErrorString(hipGetLastError()));
+      if (ctx->prof) prof_drain(ctx);
+      bool all = true;
+      any_fail = false;
+      for (int v : hs) {
+        all &= (v == ST_DONE || v == ST_DONE_FAIL);
+        any_fail |= (v == ST_DONE_FAIL);
+      }
+      if (all) break;
+      // every slot moves each unfinished problem forward, and a search ends
+      // within max_backtracks trials
+      if (slots >= blk * (o->max_backtracks + 1))
+        return fail(ctx, KVS_ERR_HIP, "schedule: block did not finish in %d slots", slots);
+      lb_slot(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, blk);
+      ++slots;
+    }
+    done += blk;
     refreshed = false;
-    if (t % o->vc_every == 0) {
+    if (done % o->vc_every == 0) {
       if (any_fail)   // stored scores of a failed search belong to a rejected trial
-        run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, kAll, 2, nullptr, nullptr, o, ws);
+        run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, 1 << ST_DONE_FAIL, 2, nullptr, nullptr, o,
+                    ws);
       run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws);
       lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 1, nullptr, mse, ws);
       refreshed = true;
@@ -416,6 +490,7 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
   if (!refreshed || o->iters == 0)
     run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, kAll, 2, nullptr, mse, o, ws);
   launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
+  prof_add_slot_work(ctx, pl, B.st);
   return KVS_OK;
 }
 

@@ -246,7 +246,9 @@ __device__ void finalize_problem(const MergeArgs& a, int p, int nblk) {
   LbState* st = a.st ? a.st + p : nullptr;
   if (a.fin_mode == 1) {
     st->Ltrial = sL;
+    st->n_trial += 1;
     if (sL <= st->L + a.c1 * st->alpha * st->gtp) {
+      st->n_accept += 1;
       st->status = ST_ACCEPT;
       st->L = sL;
       st->st_valid = 1;

@@ -26,7 +26,10 @@ struct ProbInfo {
 };
 
 // L-BFGS / line-search status of one problem.
-enum : int { ST_READY = 0, ST_SEARCH = 1, ST_ACCEPT = 2, ST_FAIL = 3 };
+// ST_DONE / ST_DONE_FAIL: the problem finished the iterations of the current
+// block (the last one accepted / failed its search) and waits for the rest.
+enum : int { ST_READY = 0, ST_SEARCH = 1, ST_ACCEPT = 2, ST_FAIL = 3, ST_DONE = 4, ST_DONE_FAIL = 5 };
+constexpr int kAllStates = 0x3F;   // active_mask selecting every status
 
 // Per-problem optimizer state, kept in device memory between kernels.
 struct LbState {
@@ -41,6 +44,10 @@ struct LbState {
   int count;         // pairs in the history
   int stage;         // ring slot receiving the next (s, y)
   int st_valid;      // stored scores belong to x (not to a rejected trial)
+  int iter;          // iterations finished in the current block
+  int n_trial;       // line-search trial evaluations since the state was cleared
+  int n_accept;      // accepted trials since the state was cleared
+  int pad_;
   int order[kHistMax];          // history slots, oldest first
   double rho[kSlots];
   double SY[kSlots][kSlots];    // s_i . y_j by slot
@@ -49,6 +56,8 @@ struct LbState {
   double coef_g;                // direction p = coef_g g + sum cs s + sum cy y
   double cs[kSlots], cy[kSlots];
 };
+
+static_assert(sizeof(LbState) % 8 == 0, "LbState is copied in 8-byte words");
 
 // Number of dot products each WG of the history kernel emits per problem.
 constexpr int kDots = 5 * kSlots + 4;
@@ -169,6 +178,8 @@ struct DotsArgs {
   double* part;                 // [P][nch][kDots]
   unsigned* counter;            // [P]
   const ProbInfo* info; int P, d, ktot, nch;
+  int target;                   // iterations per block: a problem reaching it becomes ST_DONE*
+  int* status_view;             // [P] copy of the new status (host-readable), or NULL
 };
 void launch_dots(const DotsArgs& a, hipStream_t s);
 int dots_chunks(long long kmax_d);

@@ -96,7 +96,7 @@ void launch_grad_update(const GradUpdArgs& a, hipStream_t s) {
 // in dots_kernel, then g.g at 5 MS and s.s at 5 MS + 1.
 // Every thread of the workgroup calls it (barriers), lanes of wave 0 work.
 template <int MS>
-__device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, double curv_eps) {
+__device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, double curv_eps, int target) {
   const int tid = threadIdx.x;
   const bool w0 = tid < 64;
   const int lane = tid & 63;
@@ -244,7 +244,14 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
     st->gtp = gtp;
     st->alpha = a0;
     st->trials = 0;
-    st->status = ST_SEARCH;
+    int next = ST_SEARCH;
+    if (mode == 0) {
+      st->iter += 1;
+      if (st->iter >= target) next = (status == ST_FAIL) ? ST_DONE_FAIL : ST_DONE;
+    } else {
+      st->iter = 0;
+    }
+    st->status = next;
   }
   __syncthreads();
 }
@@ -384,13 +391,16 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
     unsigned long long* d8 = reinterpret_cast<unsigned long long*>(&ls);
     for (int i = tid; i < (int)(sizeof(LbState) / 8); i += 256) d8[i] = s8[i];
   }
-  lbfgs_scalar<MS>(&ls, d, a.mode, a.history, a.curv_eps);
+  lbfgs_scalar<MS>(&ls, d, a.mode, a.history, a.curv_eps, a.target);
   {
     const unsigned long long* s8 = reinterpret_cast<const unsigned long long*>(&ls);
     unsigned long long* d8 = reinterpret_cast<unsigned long long*>(gst);
     for (int i = tid; i < (int)(sizeof(LbState) / 8); i += 256) d8[i] = s8[i];
   }
-  if (tid == 0) a.counter[p] = 0u;
+  if (tid == 0) {
+    if (a.status_view) a.status_view[p] = ls.status;
+    a.counter[p] = 0u;
+  }
 }
 
 void launch_dots(const DotsArgs& a, hipStream_t s) {
@@ -403,7 +413,7 @@ void launch_dots(const DotsArgs& a, hipStream_t s) {
 __global__ __launch_bounds__(256) void direction_kernel(DirArgs a) {
   const int p = blockIdx.y;
   const LbState* st = a.st + p;
-  if (st->status != ST_SEARCH) return;
+  if (st->status != ST_SEARCH || st->trials != 0) return;   // once per iteration
   const ProbInfo pi = a.info[p];
   const long long n4 = (long long)pi.k * a.d / 4;
   const long long e = (long long)blockIdx.x * kVec4PerWG + threadIdx.x;
@@ -434,10 +444,13 @@ __global__ void state_init_kernel(LbState* st, int P, int clear) {
   st[p].status = ST_READY;
   st[p].trials = 0;
   st[p].alpha = 0.0;
+  st[p].iter = 0;
   if (clear) {
     st[p].count = 0;
     st[p].stage = 0;
     st[p].flags = 0;
+    st[p].n_trial = 0;
+    st[p].n_accept = 0;
   }
 }
 
