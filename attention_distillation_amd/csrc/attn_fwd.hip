@@ -227,8 +227,8 @@ __device__ void finalize_problem(const MergeArgs& a, int p, int nblk) {
   double sL = 0.0, sO = 0.0;
   for (int i = t; i < nblk; i += 256) {
     const double* src = a.part + ((size_t)p * nblk + i) * 2;
-    sL += __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sO += __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sL += coherent_load(src);
+    sO += coherent_load(src + 1);
   }
   r0[t] = sL;
   r1[t] = sO;
@@ -269,8 +269,10 @@ __device__ void finalize_problem(const MergeArgs& a, int p, int nblk) {
   }
 }
 
+// waves_per_eu: let the scheduler keep the batched loads in flight instead
+// of trading them for occupancy
 template <int D, bool LOSS>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void merge_kernel(MergeArgs a) {
   const int p = blockIdx.y;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
   constexpr int DPT = D / 16;
@@ -281,21 +283,44 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const size_t row = (size_t)p * n + q;
   const size_t plane = (size_t)a.P * n;
 
+  // all chunk maxima and sums first, then the partial outputs four chunks at
+  // a time; loads are branch-free (rows past n read row 0 and are dropped)
+  const size_t rrow = ok ? row : (size_t)p * n;
+  float mv[kMaxChunks], lv[kMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const size_t o = (c < a.C ? c : 0) * plane + rrow;
+    mv[c] = a.Mpart[o];
+    lv[c] = a.Lpart[o];
+  }
   float m = -INFINITY;
-  for (int c = 0; c < a.C; ++c) m = ok ? fmaxf(m, a.Mpart[c * plane + row]) : m;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    if (c < a.C) m = fmaxf(m, mv[c]);
   float l = 0.f;
   float o[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) o[i] = 0.f;
-  if (ok) {
-    for (int c = 0; c < a.C; ++c) {
-      const float w = expf(a.Mpart[c * plane + row] - m);
-      l += w * a.Lpart[c * plane + row];
-      const float* src = a.Opart + (c * plane + row) * D + part * DPT;
 #pragma unroll
-      for (int i = 0; i < DPT; i += 4) {
-        const f32x4 v = *(const f32x4*)(src + i);
-        o[i] += w * v.x; o[i + 1] += w * v.y; o[i + 2] += w * v.z; o[i + 3] += w * v.w;
+  for (int c0 = 0; c0 < kMaxChunks; c0 += 4) {
+    if (c0 >= a.C) break;
+    f32x4 ov[4][DPT / 4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = c0 + cc < a.C ? c0 + cc : 0;
+      const float* src = a.Opart + (c * plane + rrow) * D + part * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT / 4; ++i) ov[cc][i] = *(const f32x4*)(src + 4 * i);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = c0 + cc;
+      const float w = (c < a.C) ? expf(mv[c] - m) : 0.f;
+      l += w * ((c < a.C) ? lv[c] : 0.f);
+#pragma unroll
+      for (int i = 0; i < DPT / 4; ++i) {
+        o[4 * i + 0] += w * ov[cc][i].x; o[4 * i + 1] += w * ov[cc][i].y;
+        o[4 * i + 2] += w * ov[cc][i].z; o[4 * i + 3] += w * ov[cc][i].w;
       }
     }
   }
@@ -354,15 +379,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
     if (tid == 0) {
       double* dst = a.part + ((size_t)p * gridDim.x + blockIdx.x) * 2;
-      dst[0] = red[0][0];
-      dst[1] = red[1][0];
-      __threadfence();
-      const unsigned prev = atomicAdd(a.counter + p, 1u);
-      s_last = (prev == gridDim.x - 1);
+      coherent_store(dst, red[0][0]);
+      coherent_store(dst + 1, red[1][0]);
+      wait_own_stores();
+      s_last = arrive_last(a.counter + p, gridDim.x);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     finalize_problem<D>(a, p, gridDim.x);
     if (tid == 0) a.counter[p] = 0u;
   }

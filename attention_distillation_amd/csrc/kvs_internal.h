@@ -30,6 +30,7 @@ struct ProbInfo {
 // block (the last one accepted / failed its search) and waits for the rest.
 enum : int { ST_READY = 0, ST_SEARCH = 1, ST_ACCEPT = 2, ST_FAIL = 3, ST_DONE = 4, ST_DONE_FAIL = 5 };
 constexpr int kAllStates = 0x3F;   // active_mask selecting every status
+constexpr int kMaxChunks = 16;     // key chunks of the split forward (merge unrolls over them)
 
 // Per-problem optimizer state, kept in device memory between kernels.
 struct LbState {
@@ -58,6 +59,25 @@ struct LbState {
 };
 
 static_assert(sizeof(LbState) % 8 == 0, "LbState is copied in 8-byte words");
+
+// Cross-workgroup partial sums ("last workgroup finalises" reductions).
+// Partials are written and read with device-scope relaxed atomics, which are
+// coherent across the XCDs' L2 caches, and each wave waits for its own
+// stores before the arrival counter is bumped; no workgroup needs a
+// device-wide release fence (an L2 write-back on this part).
+__device__ __forceinline__ void coherent_store(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double coherent_load(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all memory operations this wave issued have completed
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+// arrival on a per-problem counter; true for the last of `total` arrivals
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned total) {
+  const unsigned prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return prev == total - 1;
+}
 
 // Number of dot products each WG of the history kernel emits per problem.
 constexpr int kDots = 5 * kSlots + 4;

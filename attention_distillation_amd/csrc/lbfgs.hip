@@ -46,7 +46,7 @@ __device__ __forceinline__ bool active(const LbState* st, int mask) {
 }
 
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void grad_update_kernel(GradUpdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void grad_update_kernel(GradUpdArgs a) {
   const int p = blockIdx.y;
   LbState* st = a.st ? a.st + p : nullptr;
   if (st && !active(st, a.active_mask)) return;
@@ -57,8 +57,16 @@ __global__ __launch_bounds__(256) void grad_update_kernel(GradUpdArgs a) {
   const long long base4 = (long long)pi.koff * a.d / 4;
   const long long stride4 = (long long)a.ktot * a.d / 4;
   const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
+  // split partials in a fixed order, loads issued eight at a time
   f32x4 gn = dK[e];
-  for (int c = 1; c < a.Cn; ++c) gn += dK[(size_t)c * stride4 + e];
+  for (int c0 = 1; c0 < a.Cn; c0 += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < a.Cn) gn += t[j];
+  }
   gn *= (float)a.scale;
   if (a.mode == 2) {
     reinterpret_cast<f32x4*>(a.gout)[base4 + e] = gn;
@@ -338,18 +346,14 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
     }
     __syncthreads();
     if (tid < 5 * nvis || (tid >= 5 * MS && tid < E))
-      out[tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      coherent_store(out + tid, ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
   }
   // arrival: the last workgroup of this problem runs the scalar logic
+  wait_own_stores();
   __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const unsigned prev = atomicAdd(a.counter + p, 1u);
-    s_last = (prev == gridDim.x - 1);
-  }
+  if (tid == 0) s_last = arrive_last(a.counter + p, gridDim.x);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   __shared__ double tree[64][E];
   __shared__ double d[E];
@@ -359,19 +363,29 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
     // entries not written this launch read as zero
     constexpr int PERT = (64 * E + 255) / 256;
     const double* src = a.part + (size_t)p * a.nch * E;
+    // branch-free: every load of the thread is issued before the first use
+    // (masked entries load element 0 and are dropped)
+    double v0[PERT], v1[PERT];
+#pragma unroll
+    for (int u = 0; u < PERT; ++u) {
+      const int idx = tid + 256 * u;
+      const int c = idx / E, i = idx % E;
+      const bool use = idx < 64 * E && ((i < 5 * nvis) || (i >= 5 * MS));
+      const size_t o0 = (use && c < a.nch) ? (size_t)c * E + i : 0;
+      const size_t o1 = (use && c + 64 < a.nch) ? (size_t)(c + 64) * E + i : 0;
+      v0[u] = coherent_load(src + o0);
+      v1[u] = coherent_load(src + o1);
+    }
 #pragma unroll
     for (int u = 0; u < PERT; ++u) {
       const int idx = tid + 256 * u;
       if (idx < 64 * E) {
         const int c = idx / E, i = idx % E;
-        const bool wanted = (i < 5 * nvis) || (i >= 5 * MS);
+        const bool use = (i < 5 * nvis) || (i >= 5 * MS);
         double s = 0.0;
-        if (wanted) {
-          // straight-line first two chunks so all loads of a thread issue together
-          const double s0 = (c < a.nch) ? src[(size_t)c * E + i] : 0.0;
-          const double s1 = (c + 64 < a.nch) ? src[(size_t)(c + 64) * E + i] : 0.0;
-          s = s0 + s1;
-          for (int cc = c + 128; cc < a.nch; cc += 64) s += src[(size_t)cc * E + i];
+        if (use) {
+          s = ((c < a.nch) ? v0[u] : 0.0) + ((c + 64 < a.nch) ? v1[u] : 0.0);
+          for (int cc = c + 128; cc < a.nch; cc += 64) s += coherent_load(src + (size_t)cc * E + i);
         }
         tree[c][i] = s;
       }

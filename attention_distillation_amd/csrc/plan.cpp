@@ -68,8 +68,15 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p.ktot = koff; p.stot = soff; p.mtot = moff; p.kpadtot = xoff / p.d;
 
   const long long qtiles = (p.n + 63) / 64;
-  p.Cref = split_for((long long)p.P * qtiles, (p.Z + 63) / 64);
-  p.C = split_for((long long)p.P * qtiles, (p.kmax + 63) / 64);
+  // key chunks of the split forward: at most kMaxChunks, and no chunk left
+  // empty by rounding the chunk length up to whole 64-key tiles
+  auto chunks = [&](int keys) {
+    const int c = std::min(split_for((long long)p.P * qtiles, (keys + 63) / 64), kMaxChunks);
+    const int len = (((keys + c - 1) / c) + 63) / 64 * 64;
+    return (keys + len - 1) / len;
+  };
+  p.Cref = chunks(p.Z);
+  p.C = chunks(p.kmax);
   p.Cn = std::max(1, split_for((long long)p.P * ((p.kmax + 63) / 64), (int)qtiles) / 2);
   const int KT = p.kpadmax / kTile;
   const long long gtiles = (long long)KT * (KT + 1) / 2 + (long long)(p.d / kTile) * KT;
