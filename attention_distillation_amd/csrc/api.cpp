@@ -561,10 +561,10 @@ kvs_status kvs_reference_attn(kvs_ctx ctx, const kvs_batch* b, const float* Q, c
   const char* fn = "kvs_reference_attn";
   if (!ctx) return KVS_ERR_INVALID;
   KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(Y); KVS_NEED(lse);
-  kvs_batch bb = *b;
-  bb.k = nullptr;   // k is not used here: every problem attends over its Z keys
+  // every problem attends over its Z zone keys; b->k only sizes the plan, so
+  // a workspace of kvs_workspace_bytes(b) serves this call as any other
   Plan pl;
-  kvs_status s = prepare(ctx, fn, &bb, nullptr, ws, ws_bytes, &pl);
+  kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
   run_reference(ctx, pl, b, Q, Kz, Vz, Y, lse, ws);
   return hip_check(ctx, fn);

@@ -141,6 +141,7 @@ def main():
     dev = torch.device("cuda:0")
     log(f"[bench] generating {w.name}: P={w.P} n={w.n} Z={w.Z} d={w.d} k0={w.k0} T={T}")
     b = make_batch(w, 0)
+    log("[bench] inputs ready")
     P, n, d = b["Q"].shape
     Z = b["Kz"].shape[1]
     Q = torch.from_numpy(b["Q"]).to(dev)
@@ -182,8 +183,12 @@ def main():
             if need > state["ws"].numel():
                 state["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
             state["k"] = k_out
+            log(f"[bench] pilot done: k in [{min(k_out)}, {max(k_out)}], sum {sum(k_out)}")
         flags.zero_()
         K.kvs_compress(ctx, batch, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, state["ws"])
+        if pilot:
+            torch.cuda.synchronize()
+            log("[bench] main run done")
 
     for i in range(args.warmup):
         step()

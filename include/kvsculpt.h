@@ -101,7 +101,9 @@ size_t kvs_lbfgs_state_bytes(const kvs_batch* b, const kvs_opts* o);
 /* Reference chunk attention (gist page, section 2 "Problem Formulation" and
  * "Loss Function"): for each training query, the softmax attention output Y
  * over the compress zone alone and its natural-log log-sum-exp lse, with
- * scores scale * q.k.  Kz/Vz have Z rows per problem; b->k is ignored. */
+ * scores scale * q.k.  Kz/Vz have Z rows per problem.  b->k does not change
+ * the result (it may be NULL, meaning k = Z); when given it is validated as
+ * for the other calls, and kvs_workspace_bytes(b) is enough for this call. */
 kvs_status kvs_reference_attn(kvs_ctx ctx, const kvs_batch* b, const float* Q,
                               const float* Kz, const float* Vz, float* Y, float* lse,
                               void* ws, size_t ws_bytes);
