@@ -266,7 +266,7 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   c.ridge_rel = b->ridge_rel;
   launch_mu(c, ctx->stream);
   const int KT = pl.kpadmax / kTile;
-  for (int j = 0; j < KT; ++j) {
+  for (int j = -1; j < KT; ++j) {
     Prof pr(ctx, PROF_POTRF, 0, 0);
     launch_chol_step(c, pl.d, j, ctx->stream);
   }

@@ -1,12 +1,12 @@
 // Batched blocked Cholesky of (A^T A + mu I) carried through the A^T Y rows,
 // then the back substitution for Vc, gfx950.
 //
-// Right-looking, 64-column panels, one launch per panel for every problem of
-// the batch (problems whose kpad is exhausted exit at once); see
-// chol_step_kernel.  The panel solves of the rows below kpad (the Y^T A rows)
-// are the forward substitution L W = A^T Y.
-// The workgroup that factors a diagonal block also inverts it (for the back
-// substitution); back_subst_kernel solves L^T X = W for 16 value columns per workgroup,
+// Right-looking, 64-column panels with a one-block look-ahead, one launch per
+// panel for every problem of the batch (problems whose kpad is exhausted exit
+// at once); see chol_step_kernel.  The panel solves of the rows below kpad
+// (the Y^T A rows) are the forward substitution L W = A^T Y.  The inverted
+// diagonal blocks serve the panel solves and the back substitution;
+// back_subst_kernel solves L^T X = W for 16 value columns per workgroup,
 // 64-row blocks from the bottom up, every block step on MFMA.
 #include "../../include/kvsculpt.h"
 #include "kvs_internal.h"
@@ -77,43 +77,40 @@ __device__ __forceinline__ void tile_aat(const float* __restrict__ Mp, int ld, i
   }
 }
 
-// Tile of M (rows row0.., columns col0..) minus the update of panel j-1
-// (when j > 0), into LDS.
-__device__ __forceinline__ void tile_updated_to_lds(const float* __restrict__ Mp, int ld, int row0,
-                                                    int rowJ, int col0, int j, float (*T)[65]) {
+// acc += A B^T for 64x64 tiles, A from LDS ([64][65], row-major), B row-major
+// with leading dimension ldb; same result layout as tile_aat.
+__device__ __forceinline__ void tile_abt_acc(const float (*A)[65], const float* B, int ldb,
+                                             f32x4 (&acc)[2][2]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
   const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
-  f32x4 acc[2][2];
-  if (j > 0) {
-    tile_aat(Mp, ld, row0, rowJ, 64 * (j - 1), acc);
-  } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < 16; ++t) {
+    float av[2], bv[2];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ib = 0; ib < 2; ++ib) av[ib] = A[rb + 16 * ib + lq][4 * t + g];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) bv[jb] = B[(size_t)(cb + 16 * jb + lq) * ldb + 4 * t + g];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma_c(av[ib], bv[jb], acc[ib][jb]);
   }
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
-        T[rr][cc] = Mp[(size_t)(row0 + rr) * ld + col0 + cc] - acc[ib][jb][r];
-      }
 }
 
-// One step of the right-looking factorisation, per problem, in one launch:
-//  - panel workgroups (blockIdx.x < R): row tile I = j + blockIdx.x of column
-//    block j.  Each applies the update of panel j-1 to its tile and to the
-//    diagonal block (redundantly; nobody writes the diagonal block of M in
-//    this launch), factors the diagonal block in one wave (lane r owns row r,
-//    each column broadcast through LDS), then solves X L_jj^T = tile (right-looking,
-//    independent updates per step).  The panel tiles are overwritten in
-//    place; the diagonal workgroup solves against the identity instead and
-//    writes inv(L_jj) to Dinv.
+// Launch j of the right-looking factorisation with look-ahead (j = -1 .. KT-1),
+// all problems of the batch at once:
+//  - panel workgroups: row tile I = j+1+blockIdx.x of column block j.  Each
+//    applies the update of panel j-1 to its tile, solves it against L_jj by
+//    one MFMA product with inv(L_jj) (computed one launch earlier) and stores
+//    L_Ij in place.  Rows below kpad are the A^T Y rows: their panel solves are
+//    the forward substitution L W = A^T Y.
+//  - the workgroup of I = j+1 (a diagonal block) also applies the updates of
+//    panels j-1 and j to the diagonal tile (j+1, j+1), factors it and writes
+//    inv(L_{j+1,j+1}) for the next launch and the back substitution.  Launch
+//    -1 does only this for block 0.
 //  - trailing workgroups: the update of panel j-1 for the tiles (I, J) with
-//    J >= j+1, which no panel workgroup touches.
+//    J >= j+1, except the diagonal tile (j+1, j+1), which the look-ahead
+//    workgroup updates itself.
 template <int D>
 __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int Rmax, int nJ) {
   const int p = blockIdx.y;
@@ -123,17 +120,17 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   if (j >= KT) return;
   const int ld = pi.kpad;
   float* __restrict__ Mp = a.M + pi.moff;
-  const int tid = threadIdx.x;
+  float* __restrict__ Dinv = a.Dinv + (size_t)pi.xoff / D * 64;   // [KT][64][64]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+  const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
   auto rowof = [&](int I) { return (I < KT) ? 64 * I : pi.kpad + 64 * (I - KT); };
 
   if ((int)blockIdx.x >= Rmax) {
     // trailing update from panel j-1
-    if (j == 0) return;
+    if (j <= 0) return;
     const int t = blockIdx.x - Rmax;
     const int I = j + 1 + t / nJ, J = j + 1 + t % nJ;
-    if (J >= KT || I >= RT || J > I) return;
-    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
-    const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
+    if (J >= KT || I >= RT || J > I || (I == j + 1 && J == j + 1)) return;
     f32x4 acc[2][2];
     tile_aat(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
 #pragma unroll
@@ -148,19 +145,148 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
     return;
   }
 
-  const int I = j + blockIdx.x;
+  const int I = j + 1 + blockIdx.x;
   if (I >= RT) return;
-  __shared__ float Dl[64][65];
-  __shared__ float Tl[64][65];
-  __shared__ float Lt[64][68];      // Lt[c][t] = L[t][c]: column c as a contiguous row
-  __shared__ float Rd[64];          // 1 / L[c][c]
-  tile_updated_to_lds(Mp, ld, 64 * j, 64 * j, 64 * j, j, Dl);
-  if (I != j) tile_updated_to_lds(Mp, ld, rowof(I), 64 * j, 64 * j, j, Tl);
+  const bool look = (I == j + 1) && (I < KT);
+  __shared__ float Tl[64][65];      // panel tile, then L_Ij
+  __shared__ float Dl[64][65];      // diagonal tile of the look-ahead
+  __shared__ float Lt[64][68];
+
+  const int rowI = rowof(I);
+  if (j >= 0) {
+    // every global load of the workgroup is issued here, before any use:
+    // the panel tile (I, j), for the look-ahead the diagonal tile (I, I), the
+    // panel j-1 operands of their updates, and inv(L_jj) as MFMA B operand
+    const bool upd = j > 0;
+    float tv[2][2][4], dv[2][2][4], dj[16][2];
+    f32x4 av[4][2], bt[4][2], bd[4][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
+          tv[ib][jb][r] = Mp[(size_t)(rowI + rr) * ld + 64 * j + cc];
+          dv[ib][jb][r] = look ? Mp[(size_t)(rowI + rr) * ld + 64 * I + cc] : 0.f;
+        }
+    if (upd) {
+      const int c0 = 64 * (j - 1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+          av[t][ib] = *(const f32x4*)(Mp + (size_t)(rowI + rb + 16 * ib + lq) * ld + c0 + 16 * t + 4 * g);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          bt[t][jb] = *(const f32x4*)(Mp + (size_t)(64 * j + cb + 16 * jb + lq) * ld + c0 + 16 * t + 4 * g);
+          if (look) bd[t][jb] = *(const f32x4*)(Mp + (size_t)(rowI + cb + 16 * jb + lq) * ld + c0 + 16 * t + 4 * g);
+        }
+      }
+    }
+    const float* Dj = Dinv + (size_t)j * 64 * 64;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) dj[t][jb] = Dj[(cb + 16 * jb + lq) * 64 + 4 * t + g];
+
+    // updates of panel j-1: T -= L_{I,j-1} L_{j,j-1}^T, D -= L_{I,j-1} L_{I,j-1}^T
+    f32x4 accT[2][2], accD[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        accT[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accD[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    if (upd) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              accT[ib][jb] = mfma_c(av[t][ib][e], bt[t][jb][e], accT[ib][jb]);
+              if (look) accD[ib][jb] = mfma_c(av[t][ib][e], bd[t][jb][e], accD[ib][jb]);
+            }
+    }
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
+          Tl[rr][cc] = tv[ib][jb][r] - accT[ib][jb][r];
+          if (look) Dl[rr][cc] = dv[ib][jb][r] - accD[ib][jb][r];
+        }
+    __syncthreads();
+
+    // L_Ij = T inv(L_jj)^T
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float a2[2];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) a2[ib] = Tl[rb + 16 * ib + lq][4 * t + g];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma_c(a2[ib], dj[t][jb], acc[ib][jb]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
+          Tl[rr][cc] = acc[ib][jb][r];
+          Mp[(size_t)(rowI + rr) * ld + 64 * j + cc] = acc[ib][jb][r];
+        }
+  }
+  if (!look) return;
+
+  if (j < 0) {
+    // block 0: nothing to update
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
+          Dl[rr][cc] = Mp[(size_t)rr * ld + cc];
+        }
+  }
   __syncthreads();
+  if (j >= 0) {
+    // D -= L_Ij L_Ij^T (panel j)
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    tile_abt_acc(Tl, &Tl[0][0], 65, acc);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Dl[rb + 16 * ib + 4 * g + r][cb + 16 * jb + lq] -= acc[ib][jb][r];
+    __syncthreads();
+  }
   if (tid >= 64) return;
 
-  // one wave from here on: LDS traffic between lanes is ordered by
-  // wavefront-scope release/acquire fences
+  // factor and invert the diagonal tile; one wave from here on: LDS traffic
+  // between lanes is ordered by wavefront-scope release/acquire fences
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -171,14 +297,22 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   float L[64];
 #pragma unroll
   for (int c = 0; c < 64; ++c) L[c] = Dl[r][c];
-  const bool real_row = (64 * j + r) < pi.k;
+  const bool real_row = (64 * I + r) < pi.k;
 #pragma unroll
   for (int c = 0; c < 64; ++c)
     if (c == r && real_row) L[c] += mu;
 
-  // Right-looking factorisation with one LDS round trip per column: every
-  // lane publishes its entry of the unscaled column c, reads the whole column
-  // back (pivot included), and applies a_rt -= a_rc a_tc / a_cc.
+  // Right-looking factorisation with one LDS round trip per column, fused
+  // with the right-looking solve of X L^T = I: every lane publishes its entry
+  // of the unscaled column c and reads the whole column back (pivot
+  // included).  With inv = 1 / sqrt(pivot), the column below the pivot times
+  // inv is column c of L, so the same registers serve
+  //   factor:  a_rt -= a_rc a_tc / a_cc                      (t > c)
+  //   solve:   x_c *= inv,  x_t -= (x_c inv) a_tc            (t > c)
+  // and lane r ends with row r of inv(L)^T, i.e. column r of inv(L).
+  float x[64];
+#pragma unroll
+  for (int c = 0; c < 64; ++c) x[c] = (c == r) ? 1.f : 0.f;
   int badcol = -1;
 #pragma unroll
   for (int c = 0; c < 64; ++c) {
@@ -190,72 +324,29 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
     for (int t4 = c4; t4 < 64; t4 += 4) col[t4 / 4] = *(const f32x4*)&Lt[c][t4];
     const float piv = col[c / 4][c % 4];
     if (!(piv > 0.f) && badcol < 0) badcol = c;
-    const float dgn = sqrtf(piv);
-    const float inv = __frcp_rn(dgn);
+    const float dgn = __builtin_amdgcn_sqrtf(piv);   // hardware sqrt / reciprocal (about 1 ulp)
+    const float inv = __builtin_amdgcn_rcpf(dgn);
     const float f = L[c] * (inv * inv);
+    x[c] = x[c] * inv;
+    const float xf = x[c] * inv;
 #pragma unroll
-    for (int t = c + 1; t < 64; ++t) L[t] = fmaf(-f, col[t / 4][t % 4], L[t]);
-    L[c] = (r == c) ? dgn : L[c] * inv;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the factor (zero above the diagonal), column c as row c of Lt
-#pragma unroll
-  for (int c = 0; c < 64; ++c) Lt[c][r] = (c <= r) ? L[c] : 0.f;
-  wave_sync();
-  Rd[r] = __frcp_rn(Lt[r][r]);
-  wave_sync();
-
-  // X L^T = T, right-looking: x_c = t_c / L_cc, then t_t -= x_c L_tc (t > c).
-  // Software-pipelined by hand: the reads of column c+1 are issued at the
-  // start of step c (nothing in the loop writes LDS).
-  float x[64];
-  if (I == j) {
-    // diagonal workgroup: T = identity, so lane r ends with row r of
-    // inv(L)^T, i.e. column r of inv(L)
-#pragma unroll
-    for (int c = 0; c < 64; ++c) x[c] = (c == r) ? 1.f : 0.f;
-  } else {
-#pragma unroll
-    for (int c = 0; c < 64; ++c) x[c] = Tl[r][c];
-  }
-  f32x4 cur[16];
-  float rcur = Rd[0];
-#pragma unroll
-  for (int t4 = 0; t4 < 64; t4 += 4) cur[t4 / 4] = *(const f32x4*)&Lt[0][t4];
-#pragma unroll
-  for (int c = 0; c < 64; ++c) {
-    f32x4 nxt[16];
-    float rnxt = 0.f;
-    if (c + 1 < 64) {
-      rnxt = Rd[c + 1];
-#pragma unroll
-      for (int t4 = (c + 2) & ~3; t4 < 64; t4 += 4) nxt[t4 / 4] = *(const f32x4*)&Lt[c + 1][t4];
+    for (int t = c + 1; t < 64; ++t) {
+      L[t] = fmaf(-f, col[t / 4][t % 4], L[t]);
+      x[t] = fmaf(-xf, col[t / 4][t % 4], x[t]);
     }
-    x[c] = x[c] * rcur;
-#pragma unroll
-    for (int t = c + 1; t < 64; ++t) x[t] = fmaf(-x[c], cur[t / 4][t % 4], x[t]);
-#pragma unroll
-    for (int t4 = (c + 2) & ~3; t4 < 64; t4 += 4) cur[t4 / 4] = nxt[t4 / 4];
-    rcur = rnxt;
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (I == j) {
-    // Dinv block j, row-major: Dinv[c][r] = inv(L)[c][r] = x[c] of lane r
-    float* dst = a.Dinv + ((size_t)pi.xoff / D + 64 * j) * 64;
+  // Dinv block I, row-major: Dinv[c][r] = inv(L)[c][r] = x[c] of lane r
+  float* dst = Dinv + (size_t)I * 64 * 64;
 #pragma unroll
-    for (int c = 0; c < 64; ++c) dst[c * 64 + r] = x[c];
-    if (r == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * j + badcol + 1;
-    return;
-  }
-  float* xr = Mp + (size_t)(rowof(I) + r) * ld + 64 * j;
-#pragma unroll
-  for (int c = 0; c < 64; c += 4) *(f32x4*)(xr + c) = f32x4{x[c], x[c + 1], x[c + 2], x[c + 3]};
+  for (int c = 0; c < 64; ++c) dst[c * 64 + r] = x[c];
+  if (r == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * I + badcol + 1;
 }
 
 void launch_chol_step(const CholArgs& a, int d, int j, hipStream_t s) {
-  const int KT = a.kpadmax / 64;
-  const int Rmax = KT + d / 64 - j;
-  const int nI = KT + d / 64 - j - 1, nJ = KT - j - 1;
+  const int KT = a.kpadmax / 64, RT = KT + d / 64;
+  const int Rmax = (j < 0) ? 1 : RT - j - 1;
+  const int nI = RT - j - 1, nJ = KT - j - 1;
   const int ntrail = (j > 0 && nI > 0 && nJ > 0) ? nI * nJ : 0;
   dim3 grid(Rmax + ntrail, a.P);
   if (d == 128) hipLaunchKernelGGL((chol_step_kernel<128>), grid, dim3(256), 0, s, a, j, Rmax, nJ > 0 ? nJ : 1);
