@@ -19,17 +19,59 @@ __device__ __forceinline__ f32x4 mfma_f32b(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 4x4 transpose across the lanes of a quad: lane 4m+l holds row l of the
+// block on entry and column l on exit.  Two exchange rounds (partners l^1,
+// then l^2) with DPP quad permutations; a round swaps the elements whose
+// column bit differs from the lane bit.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+// The DPP reads must run with every lane of the quad active: each exchanged
+// value is computed unconditionally and pinned (empty asm) before the
+// per-lane selection, so the compiler cannot move it under a branch.
+__device__ __forceinline__ float pinned(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int lane) {
+  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
+  // round 1: element c <-> partner's element c^1 where bit0(c) != bit0(lane)
+  const float x0 = pinned(dpp_xor1(v[1])), x1 = pinned(dpp_xor1(v[0]));
+  const float x2 = pinned(dpp_xor1(v[3])), x3 = pinned(dpp_xor1(v[2]));
+  f32x4 t;
+  t[0] = b0 ? x0 : v[0];
+  t[1] = b0 ? v[1] : x1;
+  t[2] = b0 ? x2 : v[2];
+  t[3] = b0 ? v[3] : x3;
+  // round 2: element c <-> partner's element c^2 where bit1(c) != bit1(lane)
+  const float y0 = pinned(dpp_xor2(t[2])), y1 = pinned(dpp_xor2(t[3]));
+  const float y2 = pinned(dpp_xor2(t[0])), y3 = pinned(dpp_xor2(t[1]));
+  f32x4 w;
+  w[0] = b1 ? y0 : t[0];
+  w[1] = b1 ? y1 : t[1];
+  w[2] = b1 ? t[2] : y2;
+  w[3] = b1 ? t[3] : y3;
+  return w;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
-  const int p = blockIdx.y;
+  // logical block: key tile bx of problem p, query chunk bz; the key tiles of
+  // one query chunk (same G, Q and score rows) share an XCD
+  unsigned bx, by, bz;
+  xcd_block(bx, by, bz);
+  const int p = by;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
   const ProbInfo pi = a.info[p];
   const int k = pi.k;
-  const int kt0 = blockIdx.x * 64;
+  const int kt0 = bx * 64;
   if (kt0 >= k) return;
   const int n = a.n, npad = (n + 3) & ~3;
   const int nq = ((((n + a.Cn - 1) / a.Cn) + 63) / 64) * 64;
-  const int qbeg = blockIdx.z * nq;
+  const int qbeg = bz * nq;
   const int qend = min(n, qbeg + nq);
 
   __shared__ float Gs[64][D + 4];
@@ -55,34 +97,63 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   const size_t prow = (size_t)p * n;
   const float* strow = a.St + pi.soff + (size_t)(kok ? key : 0) * npad;
 
-  for (int qt = qbeg; qt < qend; qt += 64) {
-    __syncthreads();
-    for (int i = tid; i < 64 * (D / 4); i += 256) {
-      const int r = i / (D / 4), c4 = i % (D / 4);
-      const int qq = qt + r;
-      f32x4 gv = {0.f, 0.f, 0.f, 0.f}, qv = {0.f, 0.f, 0.f, 0.f};
-      if (qq < qend) {
-        gv = *(const f32x4*)(a.G + (prow + qq) * D + 4 * c4);
-        qv = *(const f32x4*)(a.Q + (prow + qq) * D + 4 * c4);
-      }
-      *(f32x4*)&Gs[r][4 * c4] = gv;
-      Qt[4 * c4 + 0][r] = qv.x;
-      Qt[4 * c4 + 1][r] = qv.y;
-      Qt[4 * c4 + 2][r] = qv.z;
-      Qt[4 * c4 + 3][r] = qv.w;
+  // Software-pipelined over query tiles: the global loads of tile t+1 (G, Q,
+  // the stored scores and the row terms) are issued before tile t is
+  // computed; rows past qend read the last valid row and are zeroed when
+  // staged.  G is staged row-major; Q transposed, each quad of lanes holding
+  // 4 consecutive rows of 4 columns that it transposes in registers, so every
+  // lane writes 4 rows of one column with one conflict-free 16-byte store.
+  constexpr int NL = 64 * (D / 4) / 256;   // float4 of G (and of Q) per thread per tile
+  const float* Gp = a.G + prow * D;
+  const float* Qp = a.Q + prow * D;
+  f32x4 gpre[NL], qpre[NL], spre[4];
+  float epre = 0.f, cpre = 0.f;
+  auto prefetch = [&](int qt) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int rg = i / (D / 4), cg = i % (D / 4);
+      gpre[u] = *(const f32x4*)(Gp + (unsigned)(min(qt + rg, qend - 1) * D + 4 * cg));
+      const int rq = 4 * (i / (4 * (D / 4))) + (i & 3), cq = (i >> 2) % (D / 4);
+      qpre[u] = *(const f32x4*)(Qp + (unsigned)(min(qt + rq, qend - 1) * D + 4 * cq));
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int qrow = qt + 16 * qb + 4 * g;
+      spre[qb] = *(const f32x4*)(strow + (qrow < qend ? qrow : 0));
     }
     if (tid < 64) {
-      const int qq = qt + tid;
-      es[tid] = qq < qend ? a.e[prow + qq] : 0.f;
-      cs[tid] = qq < qend ? a.crow[prow + qq] : 0.f;
+      const int qq = min(qt + tid, qend - 1);
+      epre = a.e[prow + qq];
+      cpre = a.crow[prow + qq];
     }
+  };
+  if (qbeg < qend) prefetch(qbeg);
+  for (int qt = qbeg; qt < qend; qt += 64) {
     __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int rg = i / (D / 4), cg = i % (D / 4);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)&Gs[rg][4 * cg] = (qt + rg < qend) ? gpre[u] : z;
+      const int rq = 4 * (i / (4 * (D / 4))) + (i & 3), cq = (i >> 2) % (D / 4);
+      const f32x4 qv = (qt + rq < qend) ? qpre[u] : z;
+      *(f32x4*)&Qt[4 * cq + (lane & 3)][rq & ~3] = quad_transpose(qv, lane);
+    }
+    if (tid < 64) {
+      es[tid] = epre;
+      cs[tid] = cpre;
+    }
+    f32x4 svv[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) svv[qb] = spre[qb];
+    __syncthreads();
+    if (qt + 64 < qend) prefetch(qt + 64);
 
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const int qrow = qt + 16 * qb + 4 * g;    // first of this lane's 4 queries
-      f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-      if (kok && qrow < qend) sv = *(const f32x4*)(strow + qrow);
+      const f32x4 sv = svv[qb];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
@@ -111,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   }
 
   // dk[db][r] = dK[key = kt0 + 16 wave + 4g + r][dim = 16 db + lq]
-  float* out = a.dKpart + (size_t)blockIdx.z * a.ktot * D;
+  float* out = a.dKpart + (size_t)bz * a.ktot * D;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int kr = kt0 + wave * 16 + 4 * g + r;

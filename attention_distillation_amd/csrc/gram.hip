@@ -76,15 +76,19 @@ __device__ __forceinline__ void stage_keys(float (*dst)[68], const float* A, int
 
 template <int D>
 __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
-  const int p = blockIdx.y;
+  // logical block: tile bx of problem p, query split bz; consecutive tiles
+  // (same row block of A) share an XCD
+  unsigned bx, by, bz;
+  xcd_block(bx, by, bz);
+  const int p = by;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
   const ProbInfo pi = a.info[p];
   const int KT = pi.kpad / 64, DT = D / 64;
   int I, J;
-  if (!gram_tile(blockIdx.x, KT, DT, I, J)) return;
+  if (!gram_tile(bx, KT, DT, I, J)) return;
   const int n = a.n, npad = (n + 3) & ~3;
   const int nq = ((((n + a.Cg - 1) / a.Cg) + 63) / 64) * 64;
-  const int qbeg = blockIdx.z * nq, qend = min(n, qbeg + nq);
+  const int qbeg = bz * nq, qend = min(n, qbeg + nq);
 
   __shared__ float Ra[64][68];
   __shared__ float Ca[64][68];
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     }
   }
 
-  float* Mout = a.Mpart + (size_t)blockIdx.z * a.mtot + pi.moff;
+  float* Mout = a.Mpart + (size_t)bz * a.mtot + pi.moff;
   const int ld = pi.kpad;
 #pragma unroll
   for (int ib = 0; ib < 2; ++ib)

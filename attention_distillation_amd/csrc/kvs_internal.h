@@ -60,6 +60,26 @@ struct LbState {
 
 static_assert(sizeof(LbState) % 8 == 0, "LbState is copied in 8-byte words");
 
+// Workgroups of a launch go to the 8 XCDs (each with its own L2) round-robin
+// by linear index.  xcd_remap turns the hardware linear index into a logical
+// one such that each XCD receives a contiguous range of logical indices, so
+// neighbouring logical workgroups (which share operands) share an L2.  It is
+// a bijection on [0, total).
+__device__ __forceinline__ unsigned xcd_remap(unsigned L, unsigned total) {
+  const unsigned q = total / 8, r = total % 8;
+  const unsigned xcd = L % 8, slot = L / 8;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+// Logical (x, y, z) of this workgroup under xcd_remap, x fastest.
+__device__ __forceinline__ void xcd_block(unsigned& x, unsigned& y, unsigned& z) {
+  const unsigned nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+  const unsigned L = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const unsigned Lp = xcd_remap(L, total);
+  x = Lp % nx;
+  y = (Lp / nx) % ny;
+  z = Lp / (nx * ny);
+}
+
 // Cross-workgroup partial sums ("last workgroup finalises" reductions).
 // Partials are written and read with device-scope relaxed atomics, which are
 // coherent across the XCDs' L2 caches, and each wave waits for its own
