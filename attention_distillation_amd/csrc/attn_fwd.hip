@@ -83,30 +83,50 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K/V tile staging: the loads of a batch of NB rows-chunks per thread are
+  // issued together (rows past kend read the last valid row and are zeroed),
+  // then written to LDS; two batches keep the registers of one batch small
+  // enough for two waves per SIMD.
+  constexpr int NL = 64 * (D / 4) / 256;     // float4 of K (and V) per thread per tile
+  constexpr int NB = NL >= 4 ? NL / 2 : NL;  // per batch
+  const float* Kp = a.K + (size_t)koff * D;
+  const float* Vp = a.V + (size_t)koff * D;
+  const float* Dp = a.dir ? a.dir + (size_t)koff * D : nullptr;
   for (int kt = kbeg; kt < kend; kt += 64) {
     __syncthreads();
-    for (int i = tid; i < 64 * (D / 4); i += 256) {
-      const int row = i / (D / 4), c4 = i % (D / 4);
-      const int key = kt + row;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (key < kend) {
-        const size_t off = (size_t)(koff + key) * D + 4 * c4;
-        kv = *(const f32x4*)(a.K + off);
-        if (a.dir) {
-          const f32x4 dv = *(const f32x4*)(a.dir + off);
-          kv.x = __fmaf_rn(alpha, dv.x, kv.x);
-          kv.y = __fmaf_rn(alpha, dv.y, kv.y);
-          kv.z = __fmaf_rn(alpha, dv.z, kv.z);
-          kv.w = __fmaf_rn(alpha, dv.w, kv.w);
-        }
-        vv = *(const f32x4*)(a.V + off);
+#pragma unroll
+    for (int u0 = 0; u0 < NL; u0 += NB) {
+      f32x4 kv[NB], vv[NB], dv[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = tid + 256 * (u0 + u);
+        const int row = i / (D / 4), c4 = i % (D / 4);
+        const unsigned off = (unsigned)(min(kt + row, kend - 1) * D + 4 * c4);
+        kv[u] = *(const f32x4*)(Kp + off);
+        vv[u] = *(const f32x4*)(Vp + off);
+        if (Dp) dv[u] = *(const f32x4*)(Dp + off);
       }
-      *(f32x4*)&Ks[row][4 * c4] = kv;
-      const int col = (row & ~15) | vt_col<F64>(row & 15);
-      Vt[4 * c4 + 0][col] = vv.x;
-      Vt[4 * c4 + 1][col] = vv.y;
-      Vt[4 * c4 + 2][col] = vv.z;
-      Vt[4 * c4 + 3][col] = vv.w;
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = tid + 256 * (u0 + u);
+        const int row = i / (D / 4), c4 = i % (D / 4);
+        const bool ok = kt + row < kend;
+        f32x4 k4 = kv[u];
+        if (Dp) {
+          k4.x = __fmaf_rn(alpha, dv[u].x, k4.x);
+          k4.y = __fmaf_rn(alpha, dv[u].y, k4.y);
+          k4.z = __fmaf_rn(alpha, dv[u].z, k4.z);
+          k4.w = __fmaf_rn(alpha, dv[u].w, k4.w);
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)&Ks[row][4 * c4] = ok ? k4 : z;
+        const f32x4 v4 = ok ? vv[u] : z;
+        const int col = (row & ~15) | vt_col<F64>(row & 15);
+        Vt[4 * c4 + 0][col] = v4.x;
+        Vt[4 * c4 + 1][col] = v4.y;
+        Vt[4 * c4 + 2][col] = v4.z;
+        Vt[4 * c4 + 3][col] = v4.w;
+      }
     }
     __syncthreads();
 
