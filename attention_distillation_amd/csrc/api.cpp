@@ -325,10 +325,15 @@ LbBuffers lb_in_state(const Plan& pl, void* state, void* ws) {
                    at<int>(ws, pl.r_status)};
 }
 
-void lb_dots(kvs_ctx ctx, const Plan& pl, const LbBuffers& B, void* ws, int mode, int mask,
-             int target = 0x7fffffff) {
+// History inner products and the scalar L-BFGS logic; with grad set, the
+// gradient pass (reduction of the backward's split partials, and for an
+// accepted step the move of Kc and the staged pair) runs in the same kernel.
+void lb_dots(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const LbBuffers& B, void* ws, int mode,
+             int mask, bool grad, float* Kc, int target = 0x7fffffff) {
   DotsArgs d{};
   d.target = target; d.status_view = B.status_view;
+  d.grad = grad ? 1 : 0; d.dKpart = at<float>(ws, pl.r_dK); d.Cn = pl.Cn; d.gscale = b->scale;
+  d.x = Kc; d.pdir = B.p;
   d.g = B.g; d.S = B.S; d.Yh = B.Yh; d.st = B.st; d.active_mask = mask; d.mode = mode;
   d.history = pl.H; d.curv_eps = 1e-10; d.part = B.hpart; d.counter = at<unsigned>(ws, pl.r_cnt) + pl.P;
   d.info = at<ProbInfo>(ws, pl.r_info); d.P = pl.P; d.d = pl.d; d.ktot = (int)pl.ktot; d.nch = pl.nchd;
@@ -343,10 +348,7 @@ void lb_eval_at_x(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opt
                   int prep_mode, float* loss_out, float* mse_out, void* ws) {
   run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws);
   run_backward(ctx, pl, b, Q, Vc, B.st, kAll, ws);
-  GradUpdArgs g = grad_args(pl, b, ws, B.st, kAll, 1);
-  g.g = B.g;
-  launch_grad_update(g, ctx->stream);
-  lb_dots(ctx, pl, B, ws, prep_mode, kAll);
+  lb_dots(ctx, pl, b, B, ws, prep_mode, kAll, true, Kc);
 }
 
 // One L-BFGS iteration for every problem: direction, backtracking Armijo
@@ -382,13 +384,8 @@ kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const k
     *any_fail |= (v == ST_FAIL);
     any_accept |= (v == ST_ACCEPT);
   }
-  if (any_accept) {
-    run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, ws, &hs, ST_ACCEPT);
-    GradUpdArgs g = grad_args(pl, b, ws, B.st, 1 << ST_ACCEPT, 0);
-    g.x = Kc; g.p = B.p; g.g = B.g; g.S = B.S; g.Yh = B.Yh;
-    launch_grad_update(g, ctx->stream);
-  }
-  lb_dots(ctx, pl, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL));
+  if (any_accept) run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, ws, &hs, ST_ACCEPT);
+  lb_dots(ctx, pl, b, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL), true, Kc);
   return KVS_OK;
 }
 
@@ -410,10 +407,7 @@ void lb_slot(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
   std::vector<int> none;
   run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws, &none, -1);
   run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, ws, &none, -1);
-  GradUpdArgs g = grad_args(pl, b, ws, B.st, 1 << ST_ACCEPT, 0);
-  g.x = Kc; g.p = B.p; g.g = B.g; g.S = B.S; g.Yh = B.Yh;
-  launch_grad_update(g, ctx->stream);
-  lb_dots(ctx, pl, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL), target);
+  lb_dots(ctx, pl, b, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL), true, Kc, target);
 }
 
 // Contraction work of the device-driven slots, from the per-problem trial and

@@ -213,13 +213,19 @@ void launch_grad_update(const GradUpdArgs& a, hipStream_t s);
 //   mode 0: after a search (ACCEPT: push + coefficients, FAIL: reset)
 //   mode 1: gradient refreshed at the same keys; mode 2: history cleared
 struct DotsArgs {
-  const float* g; const float* S; const float* Yh;
+  float* g; float* S; float* Yh;   // written by the fused gradient pass
   LbState* st; int active_mask; int mode; int history; double curv_eps;
   double* part;                 // [P][nch][kDots]
   unsigned* counter;            // [P]
   const ProbInfo* info; int P, d, ktot, nch;
   int target;                   // iterations per block: a problem reaching it becomes ST_DONE*
   int* status_view;             // [P] copy of the new status (host-readable), or NULL
+  // gradient pass fused in front of the inner products (grad != 0): g is
+  // rebuilt as gscale * sum of the backward's Cn split partials; for an
+  // accepted step also x <- x + alpha p and the staged s = x_new - x,
+  // y = g_new - g.  Applied to the problems the kernel computes for.
+  int grad;
+  const float* dKpart; int Cn; double gscale; float* x; const float* pdir;
 };
 void launch_dots(const DotsArgs& a, hipStream_t s);
 int dots_chunks(long long kmax_d);

@@ -5,10 +5,10 @@
 // a combination of s_i.y_j, y_i.y_j, s_i.g and y_i.g, so the recursion runs
 // in a few hundred scalar flops per problem and the vectors are streamed in
 // three bandwidth-bound passes per iteration:
-//   grad_update_kernel  g_new = scale * sum of the backward's split partials,
+//   dots_kernel         g_new = scale * sum of the backward's split partials,
 //                       and for an accepted step x <- x + a p, s = x_new - x,
 //                       y = g_new - g (into the staging slot), g <- g_new;
-//   dots_kernel         one workgroup per chunk: the five inner products of
+//                       then, one workgroup per chunk, the five inner products of
 //                       every history slot with the staged pair and g, kept
 //                       in registers; the last workgroup of each problem
 //                       (arrival counter) reduces them in chunk order and runs
@@ -297,18 +297,60 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
     const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
-    const f32x4 gv = ok ? reinterpret_cast<const f32x4*>(a.g)[base4 + e] : z;
-    const f32x4 sv = (ok && accept) ? S[(size_t)stg * stride4 + e] : z;
-    const f32x4 yv = (ok && accept) ? Yv[(size_t)stg * stride4 + e] : z;
+    f32x4 gv = z, sv = z, yv = z;
+    if (a.grad) {
+      if (ok) {
+        // gradient from the split partials (fixed order, loads issued eight
+        // at a time), then the accepted step and its (s, y) pair
+        const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
+        f32x4 gn = dK[e];
+        for (int c0 = 1; c0 < a.Cn; c0 += 8) {
+          f32x4 t[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + e];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j < a.Cn) gn += t[j];
+        }
+        gn *= (float)a.gscale;
+        f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
+        if (accept) {
+          f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
+          const f32x4 pv = reinterpret_cast<const f32x4*>(a.pdir)[base4 + e];
+          const float alpha = (float)gst->alpha;
+          const f32x4 xv = X[e], go = G[e];
+          f32x4 xn;
+          xn.x = __fmaf_rn(alpha, pv.x, xv.x);
+          xn.y = __fmaf_rn(alpha, pv.y, xv.y);
+          xn.z = __fmaf_rn(alpha, pv.z, xv.z);
+          xn.w = __fmaf_rn(alpha, pv.w, xv.w);
+          X[e] = xn;
+          sv = xn - xv;
+          yv = gn - go;
+          reinterpret_cast<f32x4*>(a.S)[(size_t)stg * stride4 + base4 + e] = sv;
+          reinterpret_cast<f32x4*>(a.Yh)[(size_t)stg * stride4 + base4 + e] = yv;
+        }
+        G[e] = gn;
+        gv = gn;
+      }
+    } else {
+      gv = ok ? reinterpret_cast<const f32x4*>(a.g)[base4 + e] : z;
+      sv = (ok && accept) ? S[(size_t)stg * stride4 + e] : z;
+      yv = (ok && accept) ? Yv[(size_t)stg * stride4 + e] : z;
+    }
     int slot[MS];
 #pragma unroll
     for (int t = 0; t < MS; ++t) slot[t] = (t < cnt) ? gst->order[t < kHistMax ? t : 0] : stg;
     f32x4 sj[MS], yj[MS];
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
-      const bool use = ok && t < nvis;
+      const bool use = ok && t < cnt;
       sj[t] = use ? S[(size_t)slot[t] * stride4 + e] : z;
       yj[t] = use ? Yv[(size_t)slot[t] * stride4 + e] : z;
+      if (t == cnt && accept) {   // the staged pair, already in registers
+        sj[t] = sv;
+        yj[t] = yv;
+      }
     }
     // all E values of this lane, padded to a multiple of 64, then a
     // butterfly reduction per group of 64: at each level a lane keeps one
