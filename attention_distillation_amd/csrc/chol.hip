@@ -101,16 +101,16 @@ __device__ __forceinline__ void tile_abt_acc(const float (*A)[65], const float* 
 // all problems of the batch at once:
 //  - panel workgroups: row tile I = j+1+blockIdx.x of column block j.  Each
 //    applies the update of panel j-1 to its tile, solves it against L_jj by
-//    one MFMA product with inv(L_jj) (computed one launch earlier) and stores
-//    L_Ij in place.  Rows below kpad are the A^T Y rows: their panel solves are
-//    the forward substitution L W = A^T Y.
-//  - the workgroup of I = j+1 (a diagonal block) also applies the updates of
-//    panels j-1 and j to the diagonal tile (j+1, j+1), factors it and writes
+//    one MFMA product with inv(L_jj) (computed one launch earlier), stores
+//    L_Ij in place and subtracts L_Ij L_Ij^T from its row's diagonal tile
+//    (I, I).  Rows below kpad are the A^T Y rows: their panel solves are the
+//    forward substitution L W = A^T Y.
+//  - the workgroup of I = j+1 keeps that diagonal tile in LDS instead (all
+//    earlier panels are already applied), factors it and writes
 //    inv(L_{j+1,j+1}) for the next launch and the back substitution.  Launch
 //    -1 does only this for block 0.
 //  - trailing workgroups: the update of panel j-1 for the tiles (I, J) with
-//    J >= j+1, except the diagonal tile (j+1, j+1), which the look-ahead
-//    workgroup updates itself.
+//    I > J >= j+1 (diagonal tiles are left to the panel workgroups).
 template <int D>
 __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int Rmax, int nJ) {
   const int p = blockIdx.y;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
     if (j <= 0) return;
     const int t = blockIdx.x - Rmax;
     const int I = j + 1 + t / nJ, J = j + 1 + t % nJ;
-    if (J >= KT || I >= RT || J > I || (I == j + 1 && J == j + 1)) return;
+    if (J >= KT || I >= RT || J >= I) return;   // diagonal tiles: panel workgroups
     f32x4 acc[2][2];
     tile_aat(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
 #pragma unroll
@@ -153,13 +153,19 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   __shared__ float Lt[64][68];
 
   const int rowI = rowof(I);
+  // The diagonal tile (I, I) receives the update of panel j from the panel
+  // workgroup of row I in launch j (it holds the fresh L_Ij); trailing
+  // workgroups never touch diagonal tiles.  So the look-ahead workgroup finds
+  // panels 0..j-1 already applied and subtracts only panel j.
+  const bool diag = (I < KT) && j >= 0;      // row I has a diagonal tile to update
+  float dv[2][2][4];
   if (j >= 0) {
     // every global load of the workgroup is issued here, before any use:
-    // the panel tile (I, j), for the look-ahead the diagonal tile (I, I), the
-    // panel j-1 operands of their updates, and inv(L_jj) as MFMA B operand
+    // the panel tile (I, j), the diagonal tile (I, I), the panel j-1
+    // operands of the panel tile's update, and inv(L_jj) as MFMA B operand
     const bool upd = j > 0;
-    float tv[2][2][4], dv[2][2][4], dj[16][2];
-    f32x4 av[4][2], bt[4][2], bd[4][2];
+    float tv[2][2][4], dj[16][2];
+    f32x4 av[4][2], bt[4][2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
         for (int r = 0; r < 4; ++r) {
           const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
           tv[ib][jb][r] = Mp[(size_t)(rowI + rr) * ld + 64 * j + cc];
-          dv[ib][jb][r] = look ? Mp[(size_t)(rowI + rr) * ld + 64 * I + cc] : 0.f;
+          dv[ib][jb][r] = diag ? Mp[(size_t)(rowI + rr) * ld + 64 * I + cc] : 0.f;
         }
     if (upd) {
       const int c0 = 64 * (j - 1);
@@ -178,10 +184,8 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
         for (int ib = 0; ib < 2; ++ib)
           av[t][ib] = *(const f32x4*)(Mp + (size_t)(rowI + rb + 16 * ib + lq) * ld + c0 + 16 * t + 4 * g);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        for (int jb = 0; jb < 2; ++jb)
           bt[t][jb] = *(const f32x4*)(Mp + (size_t)(64 * j + cb + 16 * jb + lq) * ld + c0 + 16 * t + 4 * g);
-          if (look) bd[t][jb] = *(const f32x4*)(Mp + (size_t)(rowI + cb + 16 * jb + lq) * ld + c0 + 16 * t + 4 * g);
-        }
       }
     }
     const float* Dj = Dinv + (size_t)j * 64 * 64;
@@ -190,15 +194,12 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) dj[t][jb] = Dj[(cb + 16 * jb + lq) * 64 + 4 * t + g];
 
-    // updates of panel j-1: T -= L_{I,j-1} L_{j,j-1}^T, D -= L_{I,j-1} L_{I,j-1}^T
-    f32x4 accT[2][2], accD[2][2];
+    // update of panel j-1: T -= L_{I,j-1} L_{j,j-1}^T
+    f32x4 accT[2][2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        accT[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accD[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int jb = 0; jb < 2; ++jb) accT[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (upd) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -207,10 +208,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              accT[ib][jb] = mfma_c(av[t][ib][e], bt[t][jb][e], accT[ib][jb]);
-              if (look) accD[ib][jb] = mfma_c(av[t][ib][e], bd[t][jb][e], accD[ib][jb]);
-            }
+            for (int e = 0; e < 4; ++e) accT[ib][jb] = mfma_c(av[t][ib][e], bt[t][jb][e], accT[ib][jb]);
     }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -220,7 +218,6 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
         for (int r = 0; r < 4; ++r) {
           const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
           Tl[rr][cc] = tv[ib][jb][r] - accT[ib][jb][r];
-          if (look) Dl[rr][cc] = dv[ib][jb][r] - accD[ib][jb][r];
         }
     __syncthreads();
 
@@ -251,6 +248,27 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
           Tl[rr][cc] = acc[ib][jb][r];
           Mp[(size_t)(rowI + rr) * ld + 64 * j + cc] = acc[ib][jb][r];
         }
+    if (diag) {
+      // D_II -= L_Ij L_Ij^T: into LDS for the look-ahead factor, else back to M
+      __syncthreads();
+      f32x4 acc2[2][2];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) acc2[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tile_abt_acc(Tl, &Tl[0][0], 65, acc2);
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = rb + 16 * ib + 4 * g + r, cc = cb + 16 * jb + lq;
+            const float v = dv[ib][jb][r] - acc2[ib][jb][r];
+            if (look) Dl[rr][cc] = v;
+            else Mp[(size_t)(rowI + rr) * ld + 64 * I + cc] = v;
+          }
+    }
   }
   if (!look) return;
 
@@ -267,22 +285,6 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
         }
   }
   __syncthreads();
-  if (j >= 0) {
-    // D -= L_Ij L_Ij^T (panel j)
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    tile_abt_acc(Tl, &Tl[0][0], 65, acc);
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Dl[rb + 16 * ib + 4 * g + r][cb + 16 * jb + lq] -= acc[ib][jb][r];
-    __syncthreads();
-  }
   if (tid >= 64) return;
 
   // factor and invert the diagonal tile; one wave from here on: LDS traffic
