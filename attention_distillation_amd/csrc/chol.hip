@@ -149,8 +149,8 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   if (I >= RT) return;
   const bool look = (I == j + 1) && (I < KT);
   __shared__ float Tl[64][65];      // panel tile, then L_Ij
-  __shared__ float Dl[64][65];      // diagonal tile of the look-ahead
-  __shared__ float Lt[64][68];
+  __shared__ float Dl[64][68];      // diagonal tile of the look-ahead, then its factor
+  __shared__ float Xr[4][16][20];   // inverses of the factor's 16x16 diagonal blocks
 
   const int rowI = rowof(I);
   // The diagonal tile (I, I) receives the update of panel j from the panel
@@ -285,64 +285,152 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
         }
   }
   __syncthreads();
-  if (tid >= 64) return;
 
-  // factor and invert the diagonal tile; one wave from here on: LDS traffic
-  // between lanes is ordered by wavefront-scope release/acquire fences
+  // Factor the diagonal tile and invert the factor, in 16-column panels.
+  //  - wave 0 factors panel b (rows 16b..63, columns 16b..16b+15) in
+  //    registers, one row per lane: the pivot column is broadcast by readlane
+  //    (by symmetry, entry c of the rows below the pivot), and the 16x16
+  //    diagonal block is inverted in the same sweep (X L_bb^T = I, lane r
+  //    keeping column r of inv(L_bb)).  It then applies panel b to the tiles
+  //    of panel b+1 on MFMA and goes on with that panel.
+  //  - waves 1..3 meanwhile apply panel b to the rest of the trailing tiles
+  //    and carry block column q = wave-1 of X = inv(L) by blocked forward
+  //    substitution: X_bq = inv(L_bb) B_bq, then B_iq -= L_ib X_bq for i > b,
+  //    with B starting as the identity.  Block column 3 is inv(L_33) itself.
+  // One barrier per panel; every tile is 16x16 and MFMA operands are read
+  // four k at a time (k = 4 g + s in step s), results of one product feeding
+  // the next as its B operand in the same k order.
+  const float mu = (float)a.mu[p];
+  if (tid < 64 && 64 * I + tid < pi.k) Dl[tid][tid] += mu;
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  const int r = tid;
-  const float mu = (float)a.mu[p];
-  float L[64];
+  // Dl tile (ti, tj) -= L_{ti,b} L_{tj,b}^T
+  auto tile_update = [&](int ti, int tj, int b) {
+    const f32x4 av = *(const f32x4*)&Dl[16 * ti + lq][16 * b + 4 * g];
+    const f32x4 bv = *(const f32x4*)&Dl[16 * tj + lq][16 * b + 4 * g];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < 64; ++c) L[c] = Dl[r][c];
-  const bool real_row = (64 * I + r) < pi.k;
+    for (int s = 0; s < 4; ++s) acc = mfma_c(av[s], bv[s], acc);
 #pragma unroll
-  for (int c = 0; c < 64; ++c)
-    if (c == r && real_row) L[c] += mu;
-
-  // Right-looking factorisation with one LDS round trip per column, fused
-  // with the right-looking solve of X L^T = I: every lane publishes its entry
-  // of the unscaled column c and reads the whole column back (pivot
-  // included).  With inv = 1 / sqrt(pivot), the column below the pivot times
-  // inv is column c of L, so the same registers serve
-  //   factor:  a_rt -= a_rc a_tc / a_cc                      (t > c)
-  //   solve:   x_c *= inv,  x_t -= (x_c inv) a_tc            (t > c)
-  // and lane r ends with row r of inv(L)^T, i.e. column r of inv(L).
-  float x[64];
+    for (int r = 0; r < 4; ++r) Dl[16 * ti + 4 * g + r][16 * tj + lq] -= acc[r];
+  };
+  float* dst = Dinv + (size_t)I * 64 * 64;   // inv(L_II), row-major
+  const int q = wave - 1;                    // block column carried by waves 1..3
+  f32x4 Bq[4];
 #pragma unroll
-  for (int c = 0; c < 64; ++c) x[c] = (c == r) ? 1.f : 0.f;
-  int badcol = -1;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-  for (int c = 0; c < 64; ++c) {
-    Lt[c][r] = L[c];
-    wave_sync();
-    const int c4 = c & ~3;
-    f32x4 col[16];
+    for (int r = 0; r < 4; ++r) Bq[i][r] = (i == q && 4 * g + r == lq) ? 1.f : 0.f;
+  // X_bq from B_bq, then B_iq -= L_ib X_bq (i > b)
+  auto column_step = [&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const f32x4 xa = *(const f32x4*)&Xr[b][lq][4 * g];
+    f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t4 = c4; t4 < 64; t4 += 4) col[t4 / 4] = *(const f32x4*)&Lt[c][t4];
-    const float piv = col[c / 4][c % 4];
-    if (!(piv > 0.f) && badcol < 0) badcol = c;
-    const float dgn = __builtin_amdgcn_sqrtf(piv);   // hardware sqrt / reciprocal (about 1 ulp)
-    const float inv = __builtin_amdgcn_rcpf(dgn);
-    const float f = L[c] * (inv * inv);
-    x[c] = x[c] * inv;
-    const float xf = x[c] * inv;
+    for (int s = 0; s < 4; ++s) X = mfma_c(xa[s], Bq[b][s], X);
 #pragma unroll
-    for (int t = c + 1; t < 64; ++t) {
-      L[t] = fmaf(-f, col[t / 4][t % 4], L[t]);
-      x[t] = fmaf(-xf, col[t / 4][t % 4], x[t]);
+    for (int r = 0; r < 4; ++r) dst[(16 * b + 4 * g + r) * 64 + 16 * q + lq] = X[r];
+#pragma unroll
+    for (int i = b + 1; i < 4; ++i) {
+      const f32x4 la = *(const f32x4*)&Dl[16 * i + lq][16 * b + 4 * g];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Bq[i] = mfma_c(-la[s], X[s], Bq[i]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // Dinv block I, row-major: Dinv[c][r] = inv(L)[c][r] = x[c] of lane r
-  float* dst = Dinv + (size_t)I * 64 * 64;
+  };
+  int badcol = -1;
+  auto panel_step = [&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    if (wave == 0) {
+      if constexpr (b > 0) {
+        // panel b-1 applied to the tiles of panel b
 #pragma unroll
-  for (int c = 0; c < 64; ++c) dst[c * 64 + r] = x[c];
-  if (r == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * I + badcol + 1;
+        for (int ti = b; ti < 4; ++ti) tile_update(ti, b, b - 1);
+      }
+      wave_sync();
+      const int rw = min(16 * b + lane, 63);
+      float P[16], x[16], iv[16];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f32x4 v = *(const f32x4*)&Dl[rw][16 * b + 4 * c4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P[4 * c4 + e] = v[e];
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) x[c] = (c == lane) ? 1.f : 0.f;
+      // right-looking sweep: with inv = 1/sqrt(pivot) and col the unscaled
+      // pivot column, a_rt -= a_rc col_t / pivot and x_c *= inv,
+      // x_t -= x_c inv col_t (t > c); row r of L is P_c inv_c
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const float piv = bcast(P[c], c);
+        if (!(piv > 0.f) && badcol < 0) badcol = 16 * b + c;
+        const float inv = __builtin_amdgcn_rsqf(piv);   // hardware 1/sqrt (about 1 ulp)
+        iv[c] = inv;
+        const float f = P[c] * (inv * inv);
+        x[c] = x[c] * inv;
+        const float xf = x[c] * inv;
+#pragma unroll
+        for (int t = c + 1; t < 16; ++t) {
+          const float col = bcast(P[c], t);
+          P[t] = fmaf(-f, col, P[t]);
+          x[t] = fmaf(-xf, col, x[t]);
+        }
+        // each broadcast column is consumed in its own step (none kept live
+        // in scalar registers across steps): x_c is final here, and pinning
+        // it keeps the inverse's updates from sinking into the store below
+        asm volatile("" : "+v"(x[c]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (16 * b + lane < 64) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          *(f32x4*)&Dl[16 * b + lane][16 * b + 4 * c4] =
+              f32x4{P[4 * c4] * iv[4 * c4], P[4 * c4 + 1] * iv[4 * c4 + 1], P[4 * c4 + 2] * iv[4 * c4 + 2],
+                    P[4 * c4 + 3] * iv[4 * c4 + 3]};
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) Xr[b][c][lane] = x[c];
+        if constexpr (b == 3) {
+#pragma unroll
+          for (int c = 0; c < 16; ++c) dst[(48 + c) * 64 + 48 + lane] = x[c];
+        }
+      }
+    } else if constexpr (b == 0) {
+      // blocks above the diagonal of inv(L_II) are zero
+      const int t = tid - 64;                 // 0..191
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int u = t + 192 * e;            // 384 float4 = 6 blocks of 16x16
+        if (u < 384) {
+          const int blk = u / 64, w = u % 64, row = w / 4, c4 = w % 4;
+          const int rbk = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+          const int cbk = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+          *(f32x4*)&dst[(16 * rbk + row) * 64 + 16 * cbk + 4 * c4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    } else {
+      // panel b-1 applied to the tiles right of panel b, then block column q
+      constexpr int pb = b - 1;
+      int k = 0;
+#pragma unroll
+      for (int tj = pb + 2; tj < 4; ++tj)
+#pragma unroll
+        for (int ti = tj; ti < 4; ++ti, ++k)
+          if (k == q) tile_update(ti, tj, pb);
+      if (q <= pb) column_step(std::integral_constant<int, pb>{});
+    }
+    __syncthreads();
+  };
+  panel_step(std::integral_constant<int, 0>{});
+  panel_step(std::integral_constant<int, 1>{});
+  panel_step(std::integral_constant<int, 2>{});
+  panel_step(std::integral_constant<int, 3>{});
+  if (wave > 0) column_step(std::integral_constant<int, 3>{});
+  if (tid == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * I + badcol + 1;
 }
 
 void launch_chol_step(const CholArgs& a, int d, int j, hipStream_t s) {
