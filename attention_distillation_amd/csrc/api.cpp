@@ -243,8 +243,11 @@ GradUpdArgs grad_args(const Plan& pl, const kvs_batch* b, void* ws, LbState* st,
 void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Y, float* Vc,
                      int* flags, LbState* st, int mask, void* ws) {
   float* M = at<float>(ws, pl.r_M);
+  // kernels that read the status only to select problems skip that load
+  // when every status is selected
+  LbState* sel = (mask == kAllStates) ? nullptr : st;
   GramArgs g{};
-  g.St = at<float>(ws, pl.r_St); g.e = at<float>(ws, pl.r_e); g.Y = Y; g.st = st; g.active_mask = mask;
+  g.St = at<float>(ws, pl.r_St); g.e = at<float>(ws, pl.r_e); g.Y = Y; g.st = sel; g.active_mask = mask;
   g.Mpart = pl.Cg > 1 ? at<float>(ws, pl.r_Mg) : M; g.info = at<ProbInfo>(ws, pl.r_info);
   g.P = pl.P; g.n = pl.n; g.Cg = pl.Cg; g.kpadmax = pl.kpadmax; g.mtot = pl.mtot;
   {
@@ -257,12 +260,12 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
     launch_gram(g, pl.d, ctx->stream);
   }
   GramReduceArgs r{};
-  r.Mpart = g.Mpart; r.M = M; r.trpart = at<double>(ws, pl.r_tr); r.st = st; r.active_mask = mask;
+  r.Mpart = g.Mpart; r.M = M; r.trpart = at<double>(ws, pl.r_tr); r.st = sel; r.active_mask = mask;
   r.info = g.info; r.P = pl.P; r.Cg = pl.Cg; r.kpadmax = pl.kpadmax; r.mtot = pl.mtot;
   launch_gram_reduce(r, pl.d, ctx->stream);
   CholArgs c{};
   c.M = M; c.Dinv = at<float>(ws, pl.r_Dinv); c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
-  c.st = st; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
+  c.st = sel; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
   c.ridge_rel = b->ridge_rel;
   launch_mu(c, ctx->stream);
   const int KT = pl.kpadmax / kTile;

@@ -20,6 +20,20 @@ __device__ __forceinline__ float bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// value of lane T of this lane's 16-lane row (DPP row_newbcast)
+template <int T>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + T, 0xF, 0xF, true));
+}
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 __device__ __forceinline__ bool chol_active(const LbState* st, int mask, int p) {
   return !st || ((1 << st[p].status) & mask);
 }
@@ -77,23 +91,25 @@ __device__ __forceinline__ void tile_aat(const float* __restrict__ Mp, int ld, i
   }
 }
 
-// acc += A B^T for 64x64 tiles, A from LDS ([64][65], row-major), B row-major
-// with leading dimension ldb; same result layout as tile_aat.
-__device__ __forceinline__ void tile_abt_acc(const float (*A)[65], const float* B, int ldb,
-                                             f32x4 (&acc)[2][2]) {
+// acc += A B^T for 64x64 tiles held in LDS ([64][68], row-major); same
+// result layout as tile_aat.  Operands are read four k at a time: step t
+// takes k = 16 (t / 4) + 4 g + t % 4 on both sides.
+__device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (*B)[68], f32x4 (&acc)[2][2]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
   const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    float av[2], bv[2];
+  for (int t4 = 0; t4 < 4; ++t4) {
+    f32x4 av[2], bv[2];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) av[ib] = A[rb + 16 * ib + lq][4 * t + g];
+    for (int ib = 0; ib < 2; ++ib) av[ib] = *(const f32x4*)&A[rb + 16 * ib + lq][16 * t4 + 4 * g];
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) bv[jb] = B[(size_t)(cb + 16 * jb + lq) * ldb + 4 * t + g];
+    for (int jb = 0; jb < 2; ++jb) bv[jb] = *(const f32x4*)&B[cb + 16 * jb + lq][16 * t4 + 4 * g];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma_c(av[ib], bv[jb], acc[ib][jb]);
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma_c(av[ib][e], bv[jb][e], acc[ib][jb]);
   }
 }
 
@@ -148,7 +164,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   const int I = j + 1 + blockIdx.x;
   if (I >= RT) return;
   const bool look = (I == j + 1) && (I < KT);
-  __shared__ float Tl[64][65];      // panel tile, then L_Ij
+  __shared__ float Tl[64][68];      // panel tile, then L_Ij
   __shared__ float Dl[64][68];      // diagonal tile of the look-ahead, then its factor
   __shared__ float Xr[4][16][20];   // inverses of the factor's 16x16 diagonal blocks
 
@@ -188,11 +204,17 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
           bt[t][jb] = *(const f32x4*)(Mp + (size_t)(64 * j + cb + 16 * jb + lq) * ld + c0 + 16 * t + 4 * g);
       }
     }
+    // inv(L_jj) as B operand, four k per load: step t takes
+    // k = 16 (t / 4) + 4 g + t % 4 (the A operand below uses the same order)
     const float* Dj = Dinv + (size_t)j * 64 * 64;
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
+    for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) dj[t][jb] = Dj[(cb + 16 * jb + lq) * 64 + 4 * t + g];
+      for (int jb = 0; jb < 2; ++jb) {
+        const f32x4 v = *(const f32x4*)&Dj[(cb + 16 * jb + lq) * 64 + 16 * t4 + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dj[4 * t4 + e][jb] = v[e];
+      }
 
     // update of panel j-1: T -= L_{I,j-1} L_{j,j-1}^T
     f32x4 accT[2][2];
@@ -228,14 +250,16 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float a2[2];
+    for (int t4 = 0; t4 < 4; ++t4) {
+      f32x4 a4[2];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) a2[ib] = Tl[rb + 16 * ib + lq][4 * t + g];
+      for (int ib = 0; ib < 2; ++ib) a4[ib] = *(const f32x4*)&Tl[rb + 16 * ib + lq][16 * t4 + 4 * g];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma_c(a2[ib], dj[t][jb], acc[ib][jb]);
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma_c(a4[ib][e], dj[4 * t4 + e][jb], acc[ib][jb]);
     }
     __syncthreads();
 #pragma unroll
@@ -256,7 +280,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) acc2[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      tile_abt_acc(Tl, &Tl[0][0], 65, acc2);
+      tile_abt_acc(Tl, Tl, acc2);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -350,53 +374,66 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
         for (int ti = b; ti < 4; ++ti) tile_update(ti, b, b - 1);
       }
       wave_sync();
-      const int rw = min(16 * b + lane, 63);
-      float P[16], x[16], iv[16];
+      // Lane layout: li = lane % 16 names a row of the 16x16 diagonal block,
+      // held by every 16-lane row of the wave (Db) so that entry t of any
+      // column is one row broadcast away.  Each lane also carries one row
+      // of the augmented panel (P): a row below the block (lane < nb) or
+      // row li of the identity (nb <= lane < nb + 16).  The sweep turns the
+      // rows below into L_ib and the identity rows into inv(L_bb)^T.
+      constexpr int nb = 48 - 16 * b;
+      float Db[16], P[16], iv[16];
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const f32x4 v = *(const f32x4*)&Dl[rw][16 * b + 4 * c4];
+        const f32x4 v = *(const f32x4*)&Dl[16 * b + lq][16 * b + 4 * c4];
+        const f32x4 w = *(const f32x4*)&Dl[min(16 * (b + 1) + lane, 63)][16 * b + 4 * c4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) P[4 * c4 + e] = v[e];
-      }
-#pragma unroll
-      for (int c = 0; c < 16; ++c) x[c] = (c == lane) ? 1.f : 0.f;
-      // right-looking sweep: with inv = 1/sqrt(pivot) and col the unscaled
-      // pivot column, a_rt -= a_rc col_t / pivot and x_c *= inv,
-      // x_t -= x_c inv col_t (t > c); row r of L is P_c inv_c
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const float piv = bcast(P[c], c);
-        if (!(piv > 0.f) && badcol < 0) badcol = 16 * b + c;
-        const float inv = __builtin_amdgcn_rsqf(piv);   // hardware 1/sqrt (about 1 ulp)
-        iv[c] = inv;
-        const float f = P[c] * (inv * inv);
-        x[c] = x[c] * inv;
-        const float xf = x[c] * inv;
-#pragma unroll
-        for (int t = c + 1; t < 16; ++t) {
-          const float col = bcast(P[c], t);
-          P[t] = fmaf(-f, col, P[t]);
-          x[t] = fmaf(-xf, col, x[t]);
+        for (int e = 0; e < 4; ++e) {
+          Db[4 * c4 + e] = v[e];
+          P[4 * c4 + e] = (lane < nb) ? w[e] : ((lane < nb + 16 && 4 * c4 + e == lq) ? 1.f : 0.f);
         }
-        // each broadcast column is consumed in its own step (none kept live
-        // in scalar registers across steps): x_c is final here, and pinning
-        // it keeps the inverse's updates from sinking into the store below
-        asm volatile("" : "+v"(x[c]));
-        __builtin_amdgcn_sched_barrier(0);
       }
-      if (16 * b + lane < 64) {
+      // right-looking sweep: with col the pivot column (unscaled) and
+      // inv = 1/sqrt(pivot), a_t -= a_c col_t / pivot (t > c) for every row;
+      // row r of the result is P_c inv_c
+      // Column c+1 is updated first and its pivot's 1/sqrt started before
+      // the rest of step c, so that latency hides behind step c's updates.
+      float piv = row_bcast<0>(Db[0]);
+      float inv = __builtin_amdgcn_rsqf(piv);   // hardware 1/sqrt (about 1 ulp)
+      static_for<16>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        if (!(piv > 0.f) && badcol < 0) badcol = 16 * b + c;
+        iv[c] = inv;
+        const float i2 = inv * inv;
+        const float fD = Db[c] * i2, fP = P[c] * i2;
+        if constexpr (c + 1 < 16) {
+          const float col = row_bcast<c + 1>(Db[c]);
+          Db[c + 1] = fmaf(-fD, col, Db[c + 1]);
+          P[c + 1] = fmaf(-fP, col, P[c + 1]);
+          piv = row_bcast<c + 1>(Db[c + 1]);
+          inv = __builtin_amdgcn_rsqf(piv);
+        }
+        static_for<16>([&](auto tt) {
+          constexpr int t = decltype(tt)::value;
+          if constexpr (t > c + 1) {
+            const float col = row_bcast<t>(Db[c]);
+            Db[t] = fmaf(-fD, col, Db[t]);
+            P[t] = fmaf(-fP, col, P[t]);
+          }
+        });
+      });
+      if (lane < nb) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
-          *(f32x4*)&Dl[16 * b + lane][16 * b + 4 * c4] =
+          *(f32x4*)&Dl[16 * (b + 1) + lane][16 * b + 4 * c4] =
               f32x4{P[4 * c4] * iv[4 * c4], P[4 * c4 + 1] * iv[4 * c4 + 1], P[4 * c4 + 2] * iv[4 * c4 + 2],
                     P[4 * c4 + 3] * iv[4 * c4 + 3]};
-      }
-      if (lane < 16) {
+      } else if (lane < nb + 16) {
+        // identity row li became column li of inv(L_bb)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) Xr[b][c][lane] = x[c];
+        for (int c = 0; c < 16; ++c) Xr[b][c][lq] = P[c] * iv[c];
         if constexpr (b == 3) {
 #pragma unroll
-          for (int c = 0; c < 16; ++c) dst[(48 + c) * 64 + 48 + lane] = x[c];
+          for (int c = 0; c < 16; ++c) dst[(48 + c) * 64 + 48 + lq] = P[c] * iv[c];
         }
       }
     } else if constexpr (b == 0) {
