@@ -44,9 +44,20 @@ struct kvs_ctx_s {
   std::vector<hipEvent_t> pool;
   std::vector<kvs::ProfRec> pending;
   kvs::ProfAcc acc[kvs::PROF_NCLASS];
+  // pinned host copies of the per-problem status (two buffers of hstat_cap
+  // entries) and their completion events, for the pipelined block schedule
+  int* hstat = nullptr;
+  int hstat_cap = 0;
+  hipEvent_t sev[2] = {nullptr, nullptr};
   ~kvs_ctx_s() {
     for (auto& r : pending) { pool.push_back(r.a); pool.push_back(r.b); }
     for (auto e : pool) hipEventDestroy(e);
+    if (hstat) {
+      hipStreamSynchronize(stream);   // a status copy may still target it
+      hipHostFree(hstat);
+    }
+    for (auto e : sev)
+      if (e) hipEventDestroy(e);
   }
 };
 
@@ -430,11 +441,34 @@ void prof_add_slot_work(kvs_ctx ctx, const Plan& pl, const LbState* st) {
   ctx->acc[PROF_BWD].flops += 4.0 * pl.n * pl.d * bw;
 }
 
+// Two pinned status buffers of P entries and their events.
+kvs_status status_buffers(kvs_ctx ctx, int P) {
+  if (ctx->hstat_cap < P) {
+    if (ctx->hstat) {
+      if (hipStreamSynchronize(ctx->stream) != hipSuccess)
+        return fail(ctx, KVS_ERR_HIP, "status buffers: %s", hipGetErrorString(hipGetLastError()));
+      hipHostFree(ctx->hstat);
+      ctx->hstat = nullptr;
+      ctx->hstat_cap = 0;
+    }
+    if (hipHostMalloc((void**)&ctx->hstat, sizeof(int) * 2 * (size_t)P, hipHostMallocDefault) != hipSuccess)
+      return fail(ctx, KVS_ERR_HIP, "status buffers: %s", hipGetErrorString(hipGetLastError()));
+    ctx->hstat_cap = P;
+  }
+  for (auto& e : ctx->sev)
+    if (!e && hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+      return fail(ctx, KVS_ERR_HIP, "status events: %s", hipGetErrorString(hipGetLastError()));
+  return KVS_OK;
+}
+
 // The whole alternating schedule on the plan's batch.  Iterations run in
 // blocks that end at the value solves: each block enqueues one slot per
-// iteration, then reads the per-problem status once; problems that needed
-// extra line-search trials get further slots until every problem has done
-// the block's iterations.
+// iteration; problems that needed extra line-search trials get further slots
+// until every problem has done the block's iterations.  The status check is
+// pipelined: after each copy of the per-problem status one more slot is
+// enqueued before the host waits for that copy, so the device keeps working
+// while the host decides (a slot leaves a problem that finished its block
+// untouched, so the last of these slots runs empty).
 kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
                          const float* Q, const float* Kz, const float* Vz, float* Kc, float* Vc,
                          float* loss, float* mse, float* init_loss, int* flags, void* ws) {
@@ -446,32 +480,41 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
   run_init_topk(ctx, pl, b, Q, Kz, Yr, lr, at<int>(ws, pl.r_idx), Kc, Vc, nullptr, B.st, ws);
   lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws);
   bool refreshed = true;
-  std::vector<int> hs(pl.P);
+  if (kvs_status s = status_buffers(ctx, pl.P); s != KVS_OK) return s;
+  int* hbuf[2] = {ctx->hstat, ctx->hstat + pl.P};
+  auto copy_status = [&](int i) {
+    return hipMemcpyAsync(hbuf[i], B.status_view, sizeof(int) * pl.P, hipMemcpyDeviceToHost, ctx->stream) ==
+               hipSuccess &&
+           hipEventRecord(ctx->sev[i], ctx->stream) == hipSuccess;
+  };
   int done = 0;
   while (done < o->iters) {
     const int blk = std::min(o->vc_every - done % o->vc_every, o->iters - done);
     int slots = 0;
     for (; slots < blk; ++slots) lb_slot(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, blk);
     bool any_fail = false;
+    int cur = 0;                 // buffer holding the status after `slots` slots
+    if (!copy_status(cur)) return fail(ctx, KVS_ERR_HIP, "schedule: %s", hipGetErrorString(hipGetLastError()));
     for (;;) {
-      if (hipMemcpyAsync(hs.data(), B.status_view, sizeof(int) * pl.P, hipMemcpyDeviceToHost,
-                         ctx->stream) != hipSuccess ||
-          hipStreamSynchronize(ctx->stream) != hipSuccess)
+      const int checked = slots;
+      lb_slot(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, blk);
+      ++slots;
+      if (!copy_status(cur ^ 1) || hipEventSynchronize(ctx->sev[cur]) != hipSuccess)
         return fail(ctx, KVS_ERR_HIP, "schedule: %s", hipGetErrorString(hipGetLastError()));
       if (ctx->prof) prof_drain(ctx);
       bool all = true;
       any_fail = false;
-      for (int v : hs) {
+      for (int p = 0; p < pl.P; ++p) {
+        const int v = hbuf[cur][p];
         all &= (v == ST_DONE || v == ST_DONE_FAIL);
         any_fail |= (v == ST_DONE_FAIL);
       }
       if (all) break;
       // every slot moves each unfinished problem forward, and a search ends
       // within max_backtracks trials
-      if (slots >= blk * (o->max_backtracks + 1))
-        return fail(ctx, KVS_ERR_HIP, "schedule: block did not finish in %d slots", slots);
-      lb_slot(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, blk);
-      ++slots;
+      if (checked >= blk * (o->max_backtracks + 1))
+        return fail(ctx, KVS_ERR_HIP, "schedule: block did not finish in %d slots", checked);
+      cur ^= 1;
     }
     done += blk;
     refreshed = false;

@@ -97,11 +97,18 @@ void launch_grad_update(const GradUpdArgs& a, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------------
+// value of v in lane `src` (uniform), through two 32-bit readlanes
+__device__ __forceinline__ double lane_value(double v, int src) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffLL), src);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), src);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 // Scalar L-BFGS logic of one problem on the LDS copy of its state, spread
 // over the first wave of the workgroup (lane i owns history position i).
-// d holds the reduced inner products by history position: 5 t + r for
-// position t (t < count: order[t]; t == count: the staged pair), r = 0..4 as
-// in dots_kernel, then g.g at 5 MS and s.s at 5 MS + 1.
+// d holds the reduced inner products by ring slot: 5 j + r for slot j,
+// r = 0..4 as in dots_kernel, then g.g at 5 MS and s.s at 5 MS + 1.
 // Every thread of the workgroup calls it (barriers), lanes of wave 0 work.
 template <int MS>
 __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, double curv_eps, int target) {
@@ -115,11 +122,11 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
   const bool accept = (mode == 0 && status == ST_ACCEPT);
   const int cnt0 = st->count, stg0 = st->stage;
   __syncthreads();
-  // inner products with g, by slot id (taken before the ring moves)
-  if (use_dots && w0 && lane <= cnt0 && (lane < cnt0 || accept)) {
-    const int j = (lane < cnt0) ? st->order[lane] : stg0;
-    st->Sg[j] = d[5 * lane + 3];
-    st->Yg[j] = d[5 * lane + 4];
+  // inner products with g, by slot (slots outside the history are
+  // rewritten before they are read)
+  if (use_dots && w0 && lane < MS) {
+    st->Sg[lane] = d[5 * lane + 3];
+    st->Yg[lane] = d[5 * lane + 4];
   }
   if (use_dots && tid == 0) st->gg = d[5 * MS];
   __syncthreads();
@@ -131,15 +138,15 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
   __syncthreads();
   if (accept) {
     const int stg = stg0, cnt = cnt0;
-    const double sy = d[5 * cnt + 0], yy = d[5 * cnt + 2], ss = d[5 * MS + 1];
+    const double sy = d[5 * stg + 0], yy = d[5 * stg + 2], ss = d[5 * MS + 1];
     const bool push = sy > curv_eps * sqrt(ss) * sqrt(yy);
     if (push) {
       if (w0 && lane < cnt) {
         const int j = st->order[lane];
-        st->SY[stg][j] = d[5 * lane + 0];
-        st->SY[j][stg] = d[5 * lane + 1];
-        st->YY[stg][j] = d[5 * lane + 2];
-        st->YY[j][stg] = d[5 * lane + 2];
+        st->SY[stg][j] = d[5 * j + 0];
+        st->SY[j][stg] = d[5 * j + 1];
+        st->YY[stg][j] = d[5 * j + 2];
+        st->YY[j][stg] = d[5 * j + 2];
       }
       __syncthreads();
       if (tid == 0) {
@@ -149,13 +156,9 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
         if (cnt < H) {
           st->order[cnt] = stg;
           st->count = cnt + 1;
-          int fr = 0;                         // smallest slot not in the history
-          for (; fr < kSlots; ++fr) {
-            bool used = false;
-            for (int t = 0; t <= cnt; ++t) used |= (st->order[t] == fr);
-            if (!used) break;
-          }
-          st->stage = fr;
+          unsigned used = 0;                  // smallest slot not in the history
+          for (int t = 0; t <= cnt; ++t) used |= 1u << st->order[t];
+          st->stage = __builtin_ctz(~used);
         } else {
           const int old = st->order[0];
           for (int t = 1; t < H; ++t) st->order[t - 1] = st->order[t];
@@ -195,7 +198,7 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
       al[j] = 0.0;
       if (j < m) {
         const double mine_al = rho * acc;
-        al[j] = __shfl(mine_al, j);
+        al[j] = lane_value(mine_al, j);
         if (lane < j) acc -= al[j] * row[j];
       }
     }
@@ -213,7 +216,7 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
       be[j] = 0.0;
       if (j < m) {
         const double mine_be = rho * (c + acc2);
-        be[j] = __shfl(mine_be, j);
+        be[j] = lane_value(mine_be, j);
         if (lane > j) acc2 += (al[j] - be[j]) * col[j];
       }
     }
@@ -265,27 +268,29 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
 }
 
 // One workgroup per 256-float4 chunk of a problem's vectors, one float4 per
-// thread: the loads of every history slot are issued together, the five
-// inner products per slot (by history position) are reduced once per
-// workgroup.  The last workgroup of the problem sums the chunk partials
-// (folded to 64 rows, then a fixed pairwise tree in LDS) and runs the scalar
-// logic.  MS = history bound + 1 positions (history plus the staged pair).
+// thread.  The five inner products are taken per ring slot (not per history
+// position), so no vector load waits for the history order: the problem
+// table and the state header are read together, then every vector load of
+// the thread is issued at once.  The last workgroup of the problem sums the
+// chunk partials in a fixed order and runs the scalar logic.  MS bounds the
+// ring slots in use (history + 1).
 template <int MS>
 __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   constexpr int E = 5 * MS + 2;            // partial entries per chunk
   const int p = blockIdx.y;
   LbState* gst = a.st + p;
+  const ProbInfo pi = a.info[p];
   const int status = gst->status;
+  const int stg = gst->stage;
+  const float alpha = (float)gst->alpha;
   if (!((1 << status) & a.active_mask)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const ProbInfo pi = a.info[p];
   const long long n4 = (long long)pi.k * a.d / 4;
   const long long base4 = (long long)pi.koff * a.d / 4;
   const long long stride4 = (long long)a.ktot * a.d / 4;
-  const int cnt = gst->count, stg = gst->stage;
+  const int nslot = a.history + 1;         // ring slots in use
   const bool accept = (a.mode == 0 && status == ST_ACCEPT);
   const bool compute = !(a.mode == 0 && status == ST_FAIL);
-  const int nvis = cnt + (accept ? 1 : 0);
   double* out = a.part + ((size_t)p * a.nch + blockIdx.x) * E;
   constexpr int NV = (E + 63) / 64;       // reduced values per lane
   __shared__ double red[4][64 * NV];
@@ -294,31 +299,45 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   if (compute) {
     const long long e = (long long)blockIdx.x * 256 + tid;
     const bool ok = e < n4;
+    const long long ec = ok ? e : 0;       // in-range index for the loads of idle lanes
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
     const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
+    f32x4 sj[MS], yj[MS];
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
+      const bool use = t < nslot;
+      sj[t] = use ? S[(size_t)t * stride4 + ec] : z;
+      yj[t] = use ? Yv[(size_t)t * stride4 + ec] : z;
+    }
     f32x4 gv = z, sv = z, yv = z;
     if (a.grad) {
+      // gradient from the split partials (fixed order), then the accepted
+      // step and its (s, y) pair, staged in slot stg
+      const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
+      f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
+      f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
+      const f32x4 go = G[ec];
+      const f32x4 xv = accept ? X[ec] : z;
+      const f32x4 pv = accept ? reinterpret_cast<const f32x4*>(a.pdir)[base4 + ec] : z;
+      f32x4 t0[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t0[j] = dK[(size_t)(j < a.Cn ? j : 0) * stride4 + ec];
+      f32x4 gn = t0[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j)
+        if (j < a.Cn) gn += t0[j];
+      for (int c0 = 8; c0 < a.Cn; c0 += 8) {
+        f32x4 t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + ec];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (c0 + j < a.Cn) gn += t[j];
+      }
+      gn *= (float)a.gscale;
       if (ok) {
-        // gradient from the split partials (fixed order, loads issued eight
-        // at a time), then the accepted step and its (s, y) pair
-        const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
-        f32x4 gn = dK[e];
-        for (int c0 = 1; c0 < a.Cn; c0 += 8) {
-          f32x4 t[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + e];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (c0 + j < a.Cn) gn += t[j];
-        }
-        gn *= (float)a.gscale;
-        f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
         if (accept) {
-          f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
-          const f32x4 pv = reinterpret_cast<const f32x4*>(a.pdir)[base4 + e];
-          const float alpha = (float)gst->alpha;
-          const f32x4 xv = X[e], go = G[e];
           f32x4 xn;
           xn.x = __fmaf_rn(alpha, pv.x, xv.x);
           xn.y = __fmaf_rn(alpha, pv.y, xv.y);
@@ -338,20 +357,18 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
       sv = (ok && accept) ? S[(size_t)stg * stride4 + e] : z;
       yv = (ok && accept) ? Yv[(size_t)stg * stride4 + e] : z;
     }
-    int slot[MS];
+    if (!ok) {
 #pragma unroll
-    for (int t = 0; t < MS; ++t) slot[t] = (t < cnt) ? gst->order[t < kHistMax ? t : 0] : stg;
-    f32x4 sj[MS], yj[MS];
+      for (int t = 0; t < MS; ++t) sj[t] = yj[t] = z;
+    }
+    // the staged slot holds the new pair (its loads above may predate the
+    // stores): take it from registers
 #pragma unroll
-    for (int t = 0; t < MS; ++t) {
-      const bool use = ok && t < cnt;
-      sj[t] = use ? S[(size_t)slot[t] * stride4 + e] : z;
-      yj[t] = use ? Yv[(size_t)slot[t] * stride4 + e] : z;
-      if (t == cnt && accept) {   // the staged pair, already in registers
+    for (int t = 0; t < MS; ++t)
+      if (accept && t == stg) {
         sj[t] = sv;
         yj[t] = yv;
       }
-    }
     // all E values of this lane, padded to a multiple of 64, then a
     // butterfly reduction per group of 64: at each level a lane keeps one
     // half of its values and adds the partner's copy of that half, so lane l
@@ -360,12 +377,11 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
     double v[64 * NV];
 #pragma unroll
     for (int t = 0; t < MS; ++t) {
-      const bool use = t < nvis;
-      v[5 * t + 0] = use ? dot4(sv, yj[t]) : 0.0;   // s_stage . y_t
-      v[5 * t + 1] = use ? dot4(sj[t], yv) : 0.0;   // s_t . y_stage
-      v[5 * t + 2] = use ? dot4(yv, yj[t]) : 0.0;   // y_stage . y_t
-      v[5 * t + 3] = use ? dot4(gv, sj[t]) : 0.0;   // g . s_t
-      v[5 * t + 4] = use ? dot4(gv, yj[t]) : 0.0;   // g . y_t
+      v[5 * t + 0] = dot4(sv, yj[t]);   // s_new . y_t
+      v[5 * t + 1] = dot4(sj[t], yv);   // s_t . y_new
+      v[5 * t + 2] = dot4(yv, yj[t]);   // y_new . y_t
+      v[5 * t + 3] = dot4(gv, sj[t]);   // g . s_t
+      v[5 * t + 4] = dot4(gv, yj[t]);   // g . y_t
     }
     v[5 * MS] = dot4(gv, gv);
     v[5 * MS + 1] = dot4(sv, sv);
@@ -387,8 +403,7 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
       red[wave][64 * gi + lane] = w[0];
     }
     __syncthreads();
-    if (tid < 5 * nvis || (tid >= 5 * MS && tid < E))
-      coherent_store(out + tid, ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
+    if (tid < E) coherent_store(out + tid, ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
   }
   // arrival: the last workgroup of this problem runs the scalar logic
   wait_own_stores();
@@ -397,55 +412,43 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  __shared__ double tree[64][E];
+  __shared__ double fold[256];
   __shared__ double d[E];
   __shared__ LbState ls;
-  if (compute) {
-    // fold chunk c, c+64, c+128, ... (in that order) into row c of the tree;
-    // entries not written this launch read as zero
-    constexpr int PERT = (64 * E + 255) / 256;
-    const double* src = a.part + (size_t)p * a.nch * E;
-    // branch-free: every load of the thread is issued before the first use
-    // (masked entries load element 0 and are dropped)
-    double v0[PERT], v1[PERT];
-#pragma unroll
-    for (int u = 0; u < PERT; ++u) {
-      const int idx = tid + 256 * u;
-      const int c = idx / E, i = idx % E;
-      const bool use = idx < 64 * E && ((i < 5 * nvis) || (i >= 5 * MS));
-      const size_t o0 = (use && c < a.nch) ? (size_t)c * E + i : 0;
-      const size_t o1 = (use && c + 64 < a.nch) ? (size_t)(c + 64) * E + i : 0;
-      v0[u] = coherent_load(src + o0);
-      v1[u] = coherent_load(src + o1);
-    }
-#pragma unroll
-    for (int u = 0; u < PERT; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < 64 * E) {
-        const int c = idx / E, i = idx % E;
-        const bool use = (i < 5 * nvis) || (i >= 5 * MS);
-        double s = 0.0;
-        if (use) {
-          s = ((c < a.nch) ? v0[u] : 0.0) + ((c + 64 < a.nch) ? v1[u] : 0.0);
-          for (int cc = c + 128; cc < a.nch; cc += 64) s += coherent_load(src + (size_t)cc * E + i);
-        }
-        tree[c][i] = s;
-      }
-    }
-    __syncthreads();
-    for (int half = 32; half > 0; half >>= 1) {
-      for (int idx = tid; idx < half * E; idx += 256) {
-        const int c = idx / E, i = idx % E;
-        tree[c][i] += tree[c + half][i];
-      }
-      __syncthreads();
-    }
-    if (tid < E) d[tid] = tree[0][tid];
-  }
+  // state copy to LDS; its loads go out together with the partial loads below
   {
     const unsigned long long* s8 = reinterpret_cast<const unsigned long long*>(gst);
     unsigned long long* d8 = reinterpret_cast<unsigned long long*>(&ls);
     for (int i = tid; i < (int)(sizeof(LbState) / 8); i += 256) d8[i] = s8[i];
+  }
+  if (compute) {
+    // value i is summed by G threads, thread q over chunks q, q + G, ...
+    // (up to 32 loads in flight), then the G sums in order of q
+    constexpr int G = 256 / E;
+    const int i = tid % E, q = tid / E;
+    const double* src = a.part + (size_t)p * a.nch * E;
+    double acc = 0.0;
+    if (q < G) {
+      for (int c0 = q; c0 < a.nch; c0 += 32 * G) {
+        double t[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int c = c0 + j * G;
+          t[j] = coherent_load(src + (size_t)(c < a.nch ? c : 0) * E + i);
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if (c0 + j * G < a.nch) acc += t[j];
+      }
+      fold[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < E) {
+      double sum = fold[tid];
+#pragma unroll
+      for (int r = 1; r < G; ++r) sum += fold[tid + r * E];
+      d[tid] = sum;
+    }
   }
   lbfgs_scalar<MS>(&ls, d, a.mode, a.history, a.curv_eps, a.target);
   {
