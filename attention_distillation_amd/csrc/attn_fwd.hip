@@ -37,6 +37,22 @@ __device__ __forceinline__ int vt_col(int kk) {
   return F64 ? ((kk & 3) * 4 + (kk >> 2)) : kk;
 }
 
+// V staging by lane quads: element i of a tile (i = thread + 256 u) belongs to
+// quad i / 4, which holds dims 4 c4 .. 4 c4 + 3 (c4 = quad % (D/4)) of four
+// keys of one 16-key block; lane l = i % 4 loads key vt_key(i).  The keys of
+// a quad are the four that vt_col places in consecutive LDS columns, so
+// after a quad transpose each lane writes one 16-byte row segment of Vt.
+template <int D>
+__device__ __forceinline__ int vt_c4(int i) {
+  return (i >> 2) % (D / 4);
+}
+template <int D, bool F64>
+__device__ __forceinline__ int vt_key(int i) {
+  const int vg = (i >> 2) / (D / 4);   // 4-key group: 16-key block vg / 4, slot vg % 4
+  const int l = i & 3;
+  return 16 * (vg >> 2) + (F64 ? (vg & 3) + 4 * l : 4 * (vg & 3) + l);
+}
+
 template <int D, bool STORE, bool F64>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   const int p = blockIdx.y, c = blockIdx.z;
@@ -103,8 +119,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
         const int row = i / (D / 4), c4 = i % (D / 4);
         const unsigned off = (unsigned)(min(kt + row, kend - 1) * D + 4 * c4);
         kv[u] = *(const f32x4*)(Kp + off);
-        vv[u] = *(const f32x4*)(Vp + off);
         if (Dp) dv[u] = *(const f32x4*)(Dp + off);
+        const int vkey = vt_key<D, F64>(i);
+        vv[u] = *(const f32x4*)(Vp + (unsigned)(min(kt + vkey, kend - 1) * D + 4 * vt_c4<D>(i)));
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
@@ -120,12 +137,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
         }
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         *(f32x4*)&Ks[row][4 * c4] = ok ? k4 : z;
-        const f32x4 v4 = ok ? vv[u] : z;
-        const int col = (row & ~15) | vt_col<F64>(row & 15);
-        Vt[4 * c4 + 0][col] = v4.x;
-        Vt[4 * c4 + 1][col] = v4.y;
-        Vt[4 * c4 + 2][col] = v4.z;
-        Vt[4 * c4 + 3][col] = v4.w;
+        // V: the quad's four keys of dims 4 c4v.. are transposed in
+        // registers, lane l then stores dim 4 c4v + l of the four keys
+        const int vc4 = vt_c4<D>(i), vg = (i >> 2) / (D / 4);
+        const f32x4 v4 = (kt + vt_key<D, F64>(i) < kend) ? vv[u] : z;
+        *(f32x4*)&Vt[4 * vc4 + (lane & 3)][16 * (vg >> 2) + 4 * (vg & 3)] = quad_transpose(v4, lane);
       }
     }
     __syncthreads();
