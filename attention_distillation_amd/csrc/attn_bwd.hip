@@ -26,8 +26,10 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   unsigned bx, by, bz;
   xcd_block(bx, by, bz);
   const int p = by;
-  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  // the problem table is read before the status test, which uses it, so the
+  // two loads share one round trip
   const ProbInfo pi = a.info[p];
+  if ((a.st && !((1 << a.st[p].status) & a.active_mask)) || pi.k < 0) return;
   const int k = pi.k;
   const int kt0 = bx * 64;
   if (kt0 >= k) return;
@@ -111,10 +113,11 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) svv[qb] = spre[qb];
     __syncthreads();
-    if (qt + 64 < qend) prefetch(qt + 64);
 
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
+      // the next tile's loads are issued inside the MFMA work of this one
+      if (qb == 1 && qt + 64 < qend) prefetch(qt + 64);
       const f32x4 sv = svv[qb];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

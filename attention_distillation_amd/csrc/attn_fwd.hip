@@ -56,18 +56,20 @@ __device__ __forceinline__ int vt_key(int i) {
 template <int D, bool STORE, bool F64>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   const int p = blockIdx.y, c = blockIdx.z;
-  float alpha = 0.f;
-  if (a.st) {
-    const LbState& s = a.st[p];
-    if (!((1 << s.status) & a.active_mask)) return;
-    alpha = (float)s.alpha;
-  }
+  // the problem table and the state are read before the status test, which
+  // uses both, so the two loads share one round trip
   int k, koff;
   long long soff;
   if (a.info) {
     k = a.info[p].k; koff = a.info[p].koff; soff = a.info[p].soff;
   } else {
     k = a.kuni; koff = p * a.kuni; soff = 0;
+  }
+  float alpha = 0.f;
+  if (a.st) {
+    const LbState& s = a.st[p];
+    if (!((1 << s.status) & a.active_mask) || k < 0) return;
+    alpha = (float)s.alpha;
   }
   const int n = a.n;
   const int npad = (n + 3) & ~3;
@@ -91,6 +93,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (qok) v = *(const f32x4*)(a.Q + (prow + q) * D + 16 * j + 4 * g);
     qf[4 * j + 0] = v.x; qf[4 * j + 1] = v.y; qf[4 * j + 2] = v.z; qf[4 * j + 3] = v.w;
+  }
+  // fp64 query operands of the score MFMA, converted once
+  double qd[F64 ? D / 4 : 1];
+  if constexpr (F64) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) qd[i] = (double)qf[i];
   }
   const double shift = (a.shift && qok) ? (double)a.shift[prow + q] : 0.0;
 
@@ -154,10 +162,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           const f32x4 kv = *(const f32x4*)&Ks[16 * b + lq][16 * j + 4 * g];
-          acc = mfma_f64((double)kv.x, (double)qf[4 * j + 0], acc);
-          acc = mfma_f64((double)kv.y, (double)qf[4 * j + 1], acc);
-          acc = mfma_f64((double)kv.z, (double)qf[4 * j + 2], acc);
-          acc = mfma_f64((double)kv.w, (double)qf[4 * j + 3], acc);
+          acc = mfma_f64((double)kv.x, qd[4 * j + 0], acc);
+          acc = mfma_f64((double)kv.y, qd[4 * j + 1], acc);
+          acc = mfma_f64((double)kv.z, qd[4 * j + 2], acc);
+          acc = mfma_f64((double)kv.w, qd[4 * j + 3], acc);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[b][r] = (float)(acc[r] * a.scale - shift);

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   const int status = gst->status;
   const int stg = gst->stage;
   const float alpha = (float)gst->alpha;
-  if (!((1 << status) & a.active_mask)) return;
+  if (!((1 << status) & a.active_mask) || pi.k < 0) return;   // both loads before the test
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const long long n4 = (long long)pi.k * a.d / 4;
   const long long base4 = (long long)pi.koff * a.d / 4;
@@ -472,8 +472,9 @@ void launch_dots(const DotsArgs& a, hipStream_t s) {
 __global__ __launch_bounds__(256) void direction_kernel(DirArgs a) {
   const int p = blockIdx.y;
   const LbState* st = a.st + p;
-  if (st->status != ST_SEARCH || st->trials != 0) return;   // once per iteration
   const ProbInfo pi = a.info[p];
+  // once per iteration; the table load joins the state load before the test
+  if (st->status != ST_SEARCH || st->trials != 0 || pi.k < 0) return;
   const long long n4 = (long long)pi.k * a.d / 4;
   const long long e = (long long)blockIdx.x * kVec4PerWG + threadIdx.x;
   if (e >= n4) return;
