@@ -48,9 +48,9 @@ def mixed_fwd_peak():
 # plain copy's known bytes to what the same counter reads for it.  Valid only
 # for the kernel source they were taken on (sha256 of that file).
 MEASURED_TRAFFIC = {
-    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 14345.6 KiB x 1.99980
-    # + WRITE 60000.0 KiB x 1.00000 per dispatch
-    "attn_fwd": {"bytes": 90816893, "source": "attn_fwd.hip", "sha": "2a7b34b62ba62a26"},
+    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 12970.7 KiB x 1.99977
+    # + WRITE 54000.0 KiB x 1.00000 per dispatch
+    "attn_fwd": {"bytes": 81857049, "source": "attn_fwd.hip", "sha": "786d74eb12f60d46"},
 }
 
 
