@@ -176,7 +176,7 @@ kvs_status prepare(kvs_ctx ctx, const char* fn, const kvs_batch* b, const kvs_op
 void run_reference(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Kz,
                    const float* Vz, float* Y, float* lse, void* ws) {
   FwdArgs f{};
-  f.Q = Q; f.K = Kz; f.V = Vz; f.dir = nullptr; f.st = nullptr; f.active_mask = 0;
+  f.Q = Q; f.K = Kz; f.V = Vz; f.st = nullptr; f.active_mask = 0;
   f.shift = nullptr; f.St = nullptr;
   f.Opart = at<float>(ws, pl.r_Opart); f.Mpart = at<float>(ws, pl.r_Mpart); f.Lpart = at<float>(ws, pl.r_Lpart);
   f.info = nullptr; f.P = pl.P; f.n = pl.n; f.C = pl.Cref; f.kuni = pl.Z; f.kmax = pl.Z; f.scale = b->scale;
@@ -194,11 +194,11 @@ void run_reference(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
 // (st, mask): stores shifted scores, merges, writes G / e / crow and the loss
 // partials, then finalises per-problem losses in the given mode.
 void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Y,
-                 const float* lse, const float* K, const float* dir, const float* V, LbState* st,
+                 const float* lse, const float* K, const float* V, LbState* st,
                  int mask, int fin_mode, float* loss, float* mse, const kvs_opts* o, void* ws,
                  const std::vector<int>* hs = nullptr, int want = 0) {
   FwdArgs f{};
-  f.Q = Q; f.K = K; f.V = V; f.dir = dir; f.st = st; f.active_mask = mask;
+  f.Q = Q; f.K = K; f.V = V; f.st = st; f.active_mask = mask;
   f.shift = lse; f.St = at<float>(ws, pl.r_St);
   f.Opart = at<float>(ws, pl.r_Opart); f.Mpart = at<float>(ws, pl.r_Mpart); f.Lpart = at<float>(ws, pl.r_Lpart);
   f.info = at<ProbInfo>(ws, pl.r_info); f.P = pl.P; f.n = pl.n; f.C = pl.C; f.kuni = 0; f.kmax = pl.kmax;
@@ -207,7 +207,7 @@ void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q
     const double ks = sum_k(pl, hs, want);
     const double np = hs ? 0 : pl.P;
     Prof pr(ctx, PROF_FWD, 4.0 * pl.n * pl.d * ks,
-            4.0 * (ks * pl.d * (dir ? 3.0 : 2.0) + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
+            4.0 * (ks * pl.d * 2.0 + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
     launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
   }
   MergeArgs m{};
@@ -314,7 +314,7 @@ void run_init_topk(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
   ta.info = at<ProbInfo>(ws, pl.r_info); ta.P = pl.P; ta.Z = pl.Z; ta.Cq = pl.Cq; ta.d = pl.d;
   launch_topk(ta, ctx->stream);
   launch_fill_f32(Vc, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
-  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
   run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws);
 }
 
@@ -360,7 +360,7 @@ void lb_dots(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const LbBuffers& B
 void lb_eval_at_x(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o, const float* Q,
                   const float* Y, const float* lse, float* Kc, const float* Vc, const LbBuffers& B,
                   int prep_mode, float* loss_out, float* mse_out, void* ws) {
-  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws);
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws);
   run_backward(ctx, pl, b, Q, Vc, B.st, kAll, ws);
   lb_dots(ctx, pl, b, B, ws, prep_mode, kAll, true, Kc);
 }
@@ -374,15 +374,17 @@ kvs_status lb_iteration(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const k
                         const LbBuffers& B, void* ws, bool* any_fail, std::vector<int>& hs) {
   DirArgs da{};
   da.p = B.p; da.g = B.g; da.S = B.S; da.Yh = B.Yh; da.st = B.st; da.info = at<ProbInfo>(ws, pl.r_info);
+  da.x = Kc; da.kt = at<float>(ws, pl.r_Kt);
   da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nch = pl.nchv;
-  {
-    Prof pr(ctx, PROF_DIR, 0, 0);
-    launch_direction(da, ctx->stream);
-  }
   hs.resize(pl.P);
   *any_fail = false;
   for (int round = 0; round < o->max_backtracks; ++round) {
-    run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws,
+    {
+      // direction on the first round; trial keys at the current step on every round
+      Prof pr(ctx, PROF_DIR, 0, 0);
+      launch_direction(da, ctx->stream);
+    }
+    run_forward(ctx, pl, b, Q, Y, lse, at<float>(ws, pl.r_Kt), Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws,
                 round ? &hs : nullptr, ST_SEARCH);
     if (hipMemcpyAsync(hs.data(), B.status_view, sizeof(int) * pl.P, hipMemcpyDeviceToHost,
                        ctx->stream) != hipSuccess ||
@@ -413,13 +415,14 @@ void lb_slot(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
              int target) {
   DirArgs da{};
   da.p = B.p; da.g = B.g; da.S = B.S; da.Yh = B.Yh; da.st = B.st; da.info = at<ProbInfo>(ws, pl.r_info);
+  da.x = Kc; da.kt = at<float>(ws, pl.r_Kt);
   da.P = pl.P; da.d = pl.d; da.ktot = (int)pl.ktot; da.nch = pl.nchv;
   {
     Prof pr(ctx, PROF_DIR, 0, 0);
     launch_direction(da, ctx->stream);
   }
   std::vector<int> none;
-  run_forward(ctx, pl, b, Q, Y, lse, Kc, B.p, Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws, &none, -1);
+  run_forward(ctx, pl, b, Q, Y, lse, at<float>(ws, pl.r_Kt), Vc, B.st, 1 << ST_SEARCH, 1, nullptr, nullptr, o, ws, &none, -1);
   run_backward(ctx, pl, b, Q, Vc, B.st, 1 << ST_ACCEPT, ws, &none, -1);
   lb_dots(ctx, pl, b, B, ws, 0, (1 << ST_ACCEPT) | (1 << ST_FAIL), true, Kc, target);
 }
@@ -520,7 +523,7 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
     refreshed = false;
     if (done % o->vc_every == 0) {
       if (any_fail)   // stored scores of a failed search belong to a rejected trial
-        run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, 1 << ST_DONE_FAIL, 2, nullptr, nullptr, o,
+        run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, 1 << ST_DONE_FAIL, 2, nullptr, nullptr, o,
                     ws);
       run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws);
       lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 1, nullptr, mse, ws);
@@ -528,7 +531,7 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
     }
   }
   if (!refreshed || o->iters == 0)
-    run_forward(ctx, pl, b, Q, Yr, lr, Kc, nullptr, Vc, B.st, kAll, 2, nullptr, mse, o, ws);
+    run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, kAll, 2, nullptr, mse, o, ws);
   launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
   prof_add_slot_work(ctx, pl, B.st);
   return KVS_OK;
@@ -620,7 +623,7 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
   Plan pl;
   kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
-  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, loss, mse, nullptr, ws);
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, loss, mse, nullptr, ws);
   if (grad) {
     run_backward(ctx, pl, b, Q, Vc, nullptr, 0, ws);
     GradUpdArgs g = grad_args(pl, b, ws, nullptr, 0, 2);
@@ -639,7 +642,7 @@ kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, cons
   Plan pl;
   kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
-  run_forward(ctx, pl, b, Q, Y, lse, Kc, nullptr, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
   run_value_solve(ctx, pl, b, Y, Vc, flags, nullptr, 0, ws);
   return hip_check(ctx, fn);
 }

@@ -37,20 +37,13 @@ __device__ __forceinline__ int vt_col(int kk) {
   return F64 ? ((kk & 3) * 4 + (kk >> 2)) : kk;
 }
 
-// V staging by lane quads: element i of a tile (i = thread + 256 u) belongs to
-// quad i / 4, which holds dims 4 c4 .. 4 c4 + 3 (c4 = quad % (D/4)) of four
-// keys of one 16-key block; lane l = i % 4 loads key vt_key(i).  The keys of
-// a quad are the four that vt_col places in consecutive LDS columns, so
-// after a quad transpose each lane writes one 16-byte row segment of Vt.
-template <int D>
-__device__ __forceinline__ int vt_c4(int i) {
-  return (i >> 2) % (D / 4);
-}
-template <int D, bool F64>
-__device__ __forceinline__ int vt_key(int i) {
-  const int vg = (i >> 2) / (D / 4);   // 4-key group: 16-key block vg / 4, slot vg % 4
-  const int l = i & 3;
-  return 16 * (vg >> 2) + (F64 ? (vg & 3) + 4 * l : 4 * (vg & 3) + l);
+// V staging: a quad of lanes covers dims 4 c4 .. 4 c4 + 3 of four keys of one
+// 16-key block (group vg: block vg / 4, slot vg % 4).  The keys are the four
+// that vt_col places in consecutive LDS columns, so each lane writes one
+// 16-byte row segment of Vt.
+template <bool F64>
+__device__ __forceinline__ int vt_key(int vg, int j) {
+  return 16 * (vg >> 2) + (F64 ? (vg & 3) + 4 * j : 4 * (vg & 3) + j);
 }
 
 template <int D, bool STORE, bool F64>
@@ -65,12 +58,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   } else {
     k = a.kuni; koff = p * a.kuni; soff = 0;
   }
-  float alpha = 0.f;
-  if (a.st) {
-    const LbState& s = a.st[p];
-    if (!((1 << s.status) & a.active_mask) || k < 0) return;
-    alpha = (float)s.alpha;
-  }
+  if (a.st && (!((1 << a.st[p].status) & a.active_mask) || k < 0)) return;
   const int n = a.n;
   const int npad = (n + 3) & ~3;
   const int chunk = (((k + a.C - 1) / a.C) + 63) & ~63;
@@ -107,49 +95,39 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K/V tile staging: the loads of a batch of NB rows-chunks per thread are
-  // issued together (rows past kend read the last valid row and are zeroed),
-  // then written to LDS; two batches keep the registers of one batch small
-  // enough for two waves per SIMD.
+  // K/V tile staging: the loads of a batch of NB float4 per thread are issued
+  // together, then written to LDS; two batches keep the registers of one
+  // batch small enough for two waves per SIMD.  Rows past kend read the last
+  // valid row: their scores are replaced by -inf, so their softmax weights
+  // are exactly zero and the values they carry never count.
   constexpr int NL = 64 * (D / 4) / 256;     // float4 of K (and V) per thread per tile
   constexpr int NB = NL >= 4 ? NL / 2 : NL;  // per batch
   const float* Kp = a.K + (size_t)koff * D;
   const float* Vp = a.V + (size_t)koff * D;
-  const float* Dp = a.dir ? a.dir + (size_t)koff * D : nullptr;
   for (int kt = kbeg; kt < kend; kt += 64) {
     __syncthreads();
 #pragma unroll
     for (int u0 = 0; u0 < NL; u0 += NB) {
-      f32x4 kv[NB], vv[NB], dv[NB];
+      f32x4 kv[NB], vv[NB];
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int i = tid + 256 * (u0 + u);
         const int row = i / (D / 4), c4 = i % (D / 4);
-        const unsigned off = (unsigned)(min(kt + row, kend - 1) * D + 4 * c4);
-        kv[u] = *(const f32x4*)(Kp + off);
-        if (Dp) dv[u] = *(const f32x4*)(Dp + off);
-        const int vkey = vt_key<D, F64>(i);
-        vv[u] = *(const f32x4*)(Vp + (unsigned)(min(kt + vkey, kend - 1) * D + 4 * vt_c4<D>(i)));
+        kv[u] = *(const f32x4*)(Kp + (unsigned)(min(kt + row, kend - 1) * D + 4 * c4));
+        // V: lane l of quad i / 4 reads dim 4 c4v + l of the quad's four keys
+        // (four coalesced 4-byte loads), i.e. one 16-byte row segment of Vt
+        const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vv[u][j] = Vp[(unsigned)(min(kt + vt_key<F64>(vg, j), kend - 1) * D + dim)];
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int i = tid + 256 * (u0 + u);
         const int row = i / (D / 4), c4 = i % (D / 4);
-        const bool ok = kt + row < kend;
-        f32x4 k4 = kv[u];
-        if (Dp) {
-          k4.x = __fmaf_rn(alpha, dv[u].x, k4.x);
-          k4.y = __fmaf_rn(alpha, dv[u].y, k4.y);
-          k4.z = __fmaf_rn(alpha, dv[u].z, k4.z);
-          k4.w = __fmaf_rn(alpha, dv[u].w, k4.w);
-        }
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        *(f32x4*)&Ks[row][4 * c4] = ok ? k4 : z;
-        // V: the quad's four keys of dims 4 c4v.. are transposed in
-        // registers, lane l then stores dim 4 c4v + l of the four keys
-        const int vc4 = vt_c4<D>(i), vg = (i >> 2) / (D / 4);
-        const f32x4 v4 = (kt + vt_key<D, F64>(i) < kend) ? vv[u] : z;
-        *(f32x4*)&Vt[4 * vc4 + (lane & 3)][16 * (vg >> 2) + 4 * (vg & 3)] = quad_transpose(v4, lane);
+        *(f32x4*)&Ks[row][4 * c4] = kv[u];
+        const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
+        *(f32x4*)&Vt[dim][16 * (vg >> 2) + 4 * (vg & 3)] = vv[u];
       }
     }
     __syncthreads();

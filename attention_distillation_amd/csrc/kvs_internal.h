@@ -144,8 +144,7 @@ constexpr int kDots = 5 * kSlots + 4;
 
 struct FwdArgs {
   const float* Q; const float* K; const float* V;
-  const float* dir;        // trial direction (NULL: keys are K itself)
-  const LbState* st;       // per-problem state (step alpha, status); NULL = all active
+  const LbState* st;       // per-problem state (status); NULL = all active
   int active_mask;         // bit (1 << status) selects the problems processed
   const float* shift;      // [P][n] per-row score shift, NULL = none
   float* St;               // stored shifted scores (NULL = do not store)
@@ -269,8 +268,11 @@ void launch_dots(const DotsArgs& a, hipStream_t s);
 int dots_chunks(long long kmax_d);
 int vec_chunks(long long kmax_d);
 
+// For every problem in search: on its first trial the direction
+// p = c_g g + sum (c_s s + c_y y); on every trial the trial keys kt = x + alpha p.
 struct DirArgs {
   float* p; const float* g; const float* S; const float* Yh; const LbState* st;
+  const float* x; float* kt;
   const ProbInfo* info; int P, d, ktot, nch;
 };
 void launch_direction(const DirArgs& a, hipStream_t s);

@@ -15,7 +15,8 @@
 //                       the scalar logic (curvature test, ring update, two-loop
 //                       coefficients, descent check, first step) on a copy of
 //                       the state in LDS, lane-parallel over the history;
-//   direction_kernel    p = c_g g + sum_j (cs_j s_j + cy_j y_j).
+//   direction_kernel    p = c_g g + sum_j (cs_j s_j + cy_j y_j) on a search's first
+//                       trial, and the trial keys x + alpha p on every trial.
 // Pairs live in a ring of history+1 slots; the spare slot stages the next
 // (s, y) before the curvature test decides whether it enters the history.
 #include "../../include/kvsculpt.h"
@@ -473,23 +474,39 @@ __global__ __launch_bounds__(256) void direction_kernel(DirArgs a) {
   const int p = blockIdx.y;
   const LbState* st = a.st + p;
   const ProbInfo pi = a.info[p];
-  // once per iteration; the table load joins the state load before the test
-  if (st->status != ST_SEARCH || st->trials != 0 || pi.k < 0) return;
+  // problems in search; the table load joins the state load before the test
+  if (st->status != ST_SEARCH || pi.k < 0) return;
   const long long n4 = (long long)pi.k * a.d / 4;
   const long long e = (long long)blockIdx.x * kVec4PerWG + threadIdx.x;
   if (e >= n4) return;
   const long long base4 = (long long)pi.koff * a.d / 4;
   const long long stride4 = (long long)a.ktot * a.d / 4;
-  const int m = st->count;
-  const f32x4* G = reinterpret_cast<const f32x4*>(a.g) + base4;
-  const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
-  const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
-  f32x4 acc = G[e] * (float)st->coef_g;
-  for (int t = 0; t < m; ++t) {
-    const int j = st->order[t];
-    acc += S[(size_t)j * stride4 + e] * (float)st->cs[j] + Yv[(size_t)j * stride4 + e] * (float)st->cy[j];
+  f32x4* Pd = reinterpret_cast<f32x4*>(a.p) + base4;
+  f32x4 pv;
+  if (st->trials == 0) {   // once per iteration
+    const int m = st->count;
+    const f32x4* G = reinterpret_cast<const f32x4*>(a.g) + base4;
+    const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
+    const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
+    f32x4 acc = G[e] * (float)st->coef_g;
+    for (int t = 0; t < m; ++t) {
+      const int j = st->order[t];
+      acc += S[(size_t)j * stride4 + e] * (float)st->cs[j] + Yv[(size_t)j * stride4 + e] * (float)st->cy[j];
+    }
+    Pd[e] = acc;
+    pv = acc;
+  } else {
+    pv = Pd[e];
   }
-  reinterpret_cast<f32x4*>(a.p)[base4 + e] = acc;
+  // trial keys at the current step (the same fma the accepted step applies)
+  const float alpha = (float)st->alpha;
+  const f32x4 xv = reinterpret_cast<const f32x4*>(a.x)[base4 + e];
+  f32x4 kv;
+  kv.x = __fmaf_rn(alpha, pv.x, xv.x);
+  kv.y = __fmaf_rn(alpha, pv.y, xv.y);
+  kv.z = __fmaf_rn(alpha, pv.z, xv.z);
+  kv.w = __fmaf_rn(alpha, pv.w, xv.w);
+  reinterpret_cast<f32x4*>(a.kt)[base4 + e] = kv;
 }
 
 void launch_direction(const DirArgs& a, hipStream_t s) {

@@ -123,6 +123,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nchd * kDots);
   take(p.r_g, f * (size_t)p.ktot * p.d);
   take(p.r_p, f * (size_t)p.ktot * p.d);
+  take(p.r_Kt, f * (size_t)p.ktot * p.d);
   take(p.r_S, f * (size_t)(H + 1) * p.ktot * p.d);
   take(p.r_Yh, f * (size_t)(H + 1) * p.ktot * p.d);
   take(p.r_Kc, f * (size_t)p.ktot * p.d);
