@@ -62,11 +62,12 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   const float* strow = a.St + pi.soff + (size_t)(kok ? key : 0) * npad;
 
   // Software-pipelined over query tiles: the global loads of tile t+1 (G, Q,
-  // the stored scores and the row terms) are issued before tile t is
-  // computed; rows past qend read the last valid row and are zeroed when
-  // staged.  G is staged row-major; Q transposed, each quad of lanes holding
-  // 4 consecutive rows of 4 columns that it transposes in registers, so every
-  // lane writes 4 rows of one column with one conflict-free 16-byte store.
+  // the stored scores and the row terms) are issued inside the MFMA work of
+  // tile t.  Rows past qend read the last valid row; their dS is zero, so
+  // they never count.  G is staged row-major; Q transposed: lane l of a quad
+  // covering rows 4 m .. 4 m + 3 and dims 4 c .. 4 c + 3 reads dim 4 c + l of
+  // the four rows (coalesced 4-byte loads across the quads of a wave) and
+  // writes them as one 16-byte row segment of Qt.
   constexpr int NL = 64 * (D / 4) / 256;   // float4 of G (and of Q) per thread per tile
   const float* Gp = a.G + prow * D;
   const float* Qp = a.Q + prow * D;
@@ -78,8 +79,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
       const int i = tid + 256 * u;
       const int rg = i / (D / 4), cg = i % (D / 4);
       gpre[u] = *(const f32x4*)(Gp + (unsigned)(min(qt + rg, qend - 1) * D + 4 * cg));
-      const int rq = 4 * (i / (4 * (D / 4))) + (i & 3), cq = (i >> 2) % (D / 4);
-      qpre[u] = *(const f32x4*)(Qp + (unsigned)(min(qt + rq, qend - 1) * D + 4 * cq));
+      const int rq = 4 * (i / (4 * (D / 4))), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qpre[u][j] = Qp[(unsigned)(min(qt + rq + j, qend - 1) * D + dq)];
     }
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -99,11 +101,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
     for (int u = 0; u < NL; ++u) {
       const int i = tid + 256 * u;
       const int rg = i / (D / 4), cg = i % (D / 4);
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)&Gs[rg][4 * cg] = (qt + rg < qend) ? gpre[u] : z;
-      const int rq = 4 * (i / (4 * (D / 4))) + (i & 3), cq = (i >> 2) % (D / 4);
-      const f32x4 qv = (qt + rq < qend) ? qpre[u] : z;
-      *(f32x4*)&Qt[4 * cq + (lane & 3)][rq & ~3] = quad_transpose(qv, lane);
+      *(f32x4*)&Gs[rg][4 * cg] = gpre[u];
+      const int rq = 4 * (i / (4 * (D / 4))), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
+      *(f32x4*)&Qt[dq][rq] = qpre[u];
     }
     if (tid < 64) {
       es[tid] = epre;

@@ -80,44 +80,6 @@ __device__ __forceinline__ void xcd_block(unsigned& x, unsigned& y, unsigned& z)
   z = Lp / (nx * ny);
 }
 
-// 4x4 transpose across the lanes of a quad: lane 4m+l holds row l of the
-// block on entry and column l on exit.  Two exchange rounds (partners l^1,
-// then l^2) with DPP quad permutations; a round swaps the elements whose
-// column bit differs from the lane bit.
-__device__ __forceinline__ float dpp_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-}
-// The DPP reads must run with every lane of the quad active: each exchanged
-// value is computed unconditionally and pinned (empty asm) before the
-// per-lane selection, so the compiler cannot move it under a branch.
-__device__ __forceinline__ float pinned(float v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-__device__ __forceinline__ f32x4 quad_transpose(f32x4 v, int lane) {
-  const bool b0 = lane & 1, b1 = (lane >> 1) & 1;
-  // round 1: element c <-> partner's element c^1 where bit0(c) != bit0(lane)
-  const float x0 = pinned(dpp_xor1(v[1])), x1 = pinned(dpp_xor1(v[0]));
-  const float x2 = pinned(dpp_xor1(v[3])), x3 = pinned(dpp_xor1(v[2]));
-  f32x4 t;
-  t[0] = b0 ? x0 : v[0];
-  t[1] = b0 ? v[1] : x1;
-  t[2] = b0 ? x2 : v[2];
-  t[3] = b0 ? v[3] : x3;
-  // round 2: element c <-> partner's element c^2 where bit1(c) != bit1(lane)
-  const float y0 = pinned(dpp_xor2(t[2])), y1 = pinned(dpp_xor2(t[3]));
-  const float y2 = pinned(dpp_xor2(t[0])), y3 = pinned(dpp_xor2(t[1]));
-  f32x4 w;
-  w[0] = b1 ? y0 : t[0];
-  w[1] = b1 ? y1 : t[1];
-  w[2] = b1 ? t[2] : y2;
-  w[3] = b1 ? t[3] : y3;
-  return w;
-}
-
 // Cross-workgroup partial sums ("last workgroup finalises" reductions).
 // Partials are written and read with device-scope relaxed atomics, which are
 // coherent across the XCDs' L2 caches, and each wave waits for its own
