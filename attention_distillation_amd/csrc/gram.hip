@@ -62,18 +62,6 @@ __global__ __launch_bounds__(256) void weights_kernel(GramArgs a) {
   }
 }
 
-__device__ __forceinline__ void stage_keys(float (*dst)[68], const float* A, int k, int key0, int npad,
-                                           int qt, int qend, int tid) {
-  for (int i = tid; i < 64 * 16; i += 256) {
-    const int r = i >> 4, c4 = i & 15;
-    const int key = key0 + r;
-    const int q = qt + 4 * c4;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (key < k && q < qend) v = *(const f32x4*)(A + (size_t)key * npad + q);
-    *(f32x4*)&dst[r][4 * c4] = v;
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   // logical block: tile bx of problem p, query split bz; consecutive tiles
@@ -104,25 +92,56 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Operand tiles of 64 queries, software-pipelined: the loads of the next
+  // tile are issued before the MFMA work of this one.  Element u of a thread
+  // (i = tid + 256 u) is, for a key tile, key i / 16 and queries 4 (i % 16)
+  // .. + 3 (one 16-byte load); for the value rows of YᵀA, dim i % 64 and
+  // queries 4 (i / 64) .. + 3, read as four 4-byte loads (consecutive lanes,
+  // consecutive dims) so that the tile lands transposed with one 16-byte LDS
+  // store.  Keys past k read the last key (their rows and columns are
+  // replaced by the identity later); queries past qend are zeroed.
+  const bool yrows = I >= KT;
+  const int keyR = 64 * I, keyC = 64 * J;
+  const int dim0 = 64 * (I - KT);
+  f32x4 pr[4], pc[4];
+  auto prefetch = [&](int qt) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i >> 4, q4 = 4 * (i & 15);
+      if (yrows) {
+        const int qy = qt + 4 * (i >> 6);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[u][j] = Y[(size_t)min(qy + j, n - 1) * D + dim0 + (i & 63)];
+      } else {
+        pr[u] = *(const f32x4*)(St + (size_t)min(keyR + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
+      }
+      if (!diag) pc[u] = *(const f32x4*)(St + (size_t)min(keyC + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
+    }
+  };
+  if (qbeg < qend) prefetch(qbeg);
   for (int qt = qbeg; qt < qend; qt += 64) {
     __syncthreads();
-    if (I < KT) {
-      stage_keys(Ra, St, pi.k, 64 * I, npad, qt, qend, tid);
-    } else {
-      const int dim0 = 64 * (I - KT);
-      for (int i = tid; i < 64 * 16; i += 256) {
-        const int qq = i >> 4, c4 = i & 15;
-        const int q = qt + qq;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (q < qend) v = *(const f32x4*)(Y + (size_t)q * D + dim0 + 4 * c4);
-        Ra[4 * c4 + 0][qq] = v.x;
-        Ra[4 * c4 + 1][qq] = v.y;
-        Ra[4 * c4 + 2][qq] = v.z;
-        Ra[4 * c4 + 3][qq] = v.w;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u;
+      const int r = yrows ? (i & 63) : (i >> 4), q4 = yrows ? 4 * (i >> 6) : 4 * (i & 15);
+      f32x4 v = pr[u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (qt + q4 + j >= qend) v[j] = 0.f;
+      *(f32x4*)&Ra[r][q4] = v;
+      if (!diag) {
+        const int rc = i >> 4, qc = 4 * (i & 15);
+        f32x4 w = pc[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (qt + qc + j >= qend) w[j] = 0.f;
+        *(f32x4*)&Ca[rc][qc] = w;
       }
     }
-    if (!diag) stage_keys(Ca, St, pi.k, 64 * J, npad, qt, qend, tid);
     __syncthreads();
+    if (qt + 64 < qend) prefetch(qt + 64);
     float (*C)[68] = diag ? Ra : Ca;
 #pragma unroll
     for (int qq = 0; qq < 64; qq += 16) {
