@@ -614,6 +614,14 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
     }
   };
 
+  // inv(L_ii) as A operand of X_i, loaded one step ahead
+  auto load_dinv = [&](float (&dv)[16], int i) {
+    const float* Di = Dinv + (size_t)i * 64 * 64;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) dv[s2] = Di[(4 * s2 + g) * 64 + 16 * wave + lq];
+  };
+  float dv[16];
+  load_dinv(dv, KT - 1);
   for (int i = KT - 1; i >= 0; --i) {
     float av0[4][16], av1[4][16];
     const int rb0 = wave, rb1 = wave + 4;
@@ -622,18 +630,15 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
     // X_i rows b = 16 wave + (4g + r): sum_a inv(L_ii)[a][b] W_i[a][c]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     {
-      const float* Di = Dinv + (size_t)i * 64 * 64;
-      float dv[16], wv[16];
+      float wv[16];
 #pragma unroll
-      for (int s2 = 0; s2 < 16; ++s2) {
-        dv[s2] = Di[(4 * s2 + g) * 64 + 16 * wave + lq];
-        wv[s2] = Wl[(64 * i + 4 * s2 + g) * 16 + lq];
-      }
+      for (int s2 = 0; s2 < 16; ++s2) wv[s2] = Wl[(64 * i + 4 * s2 + g) * 16 + lq];
 #pragma unroll
       for (int s2 = 0; s2 < 16; ++s2) x = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[s2], wv[s2], x, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Xs[(16 * wave + 4 * g + r) * 16 + lq] = x[r];
     }
+    if (i > 0) load_dinv(dv, i - 1);
     __syncthreads();
     // every wave has read W_i: it now holds X_i
 #pragma unroll
