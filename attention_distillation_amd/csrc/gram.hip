@@ -1,7 +1,7 @@
 // Normal equations of the ridge value solve, gfx950.
 //
-// The stored shifted scores are first turned into the softmax weights in
-// place (weights_kernel), then tiled.
+// The softmax weights are rebuilt from the stored shifted scores while the
+// Gram tiles are staged (the scores themselves stay untouched).
 //
 // For A = exp(St - e) (the softmax weights rebuilt from the stored shifted
 // scores, n x k) the kernel forms the augmented lower-trapezoidal matrix
@@ -40,28 +40,6 @@ __device__ __forceinline__ bool gram_tile(long long t, int KT, int DT, int& I, i
   return true;
 }
 
-// A = exp(St - e), in place over the stored scores (zero for q >= n), so the
-// Gram tiles stage plain copies instead of recomputing exp per tile.
-__global__ __launch_bounds__(256) void weights_kernel(GramArgs a) {
-  const int p = blockIdx.y;
-  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
-  const ProbInfo pi = a.info[p];
-  const int n = a.n, npad = (n + 3) & ~3, n4 = npad / 4;
-  const long long tot4 = (long long)pi.k * n4;
-  f32x4* A = reinterpret_cast<f32x4*>(const_cast<float*>(a.St) + pi.soff);
-  const float* e = a.e + (size_t)p * n;
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < tot4; i += (long long)gridDim.x * 256) {
-    const int q = (int)(i % n4) * 4;
-    const f32x4 sv = A[i];
-    f32x4 v;
-    v.x = expf(sv.x - e[q]);
-    v.y = (q + 1 < n) ? expf(sv.y - e[q + 1]) : 0.f;
-    v.z = (q + 2 < n) ? expf(sv.z - e[q + 2]) : 0.f;
-    v.w = (q + 3 < n) ? expf(sv.w - e[q + 3]) : 0.f;
-    A[i] = v;
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   // logical block: tile bx of problem p, query split bz; consecutive tiles
@@ -83,7 +61,8 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
   const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
   const bool diag = (I == J);
-  const float* St = a.St + pi.soff;      // softmax weights after weights_kernel
+  const float* St = a.St + pi.soff;      // stored shifted scores
+  const float* E = a.e + (size_t)p * n;
   const float* Y = a.Y + (size_t)p * n * D;
 
   f32x4 acc[2][2];
@@ -103,8 +82,11 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
   const bool yrows = I >= KT;
   const int keyR = 64 * I, keyC = 64 * J;
   const int dim0 = 64 * (I - KT);
-  f32x4 pr[4], pc[4];
+  f32x4 pr[4], pc[4], ev;
   auto prefetch = [&](int qt) {
+    // e of this thread's four key-tile queries (clamped past n)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ev[j] = E[min(qt + 4 * (tid & 15) + j, n - 1)];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = tid + 256 * u;
@@ -119,6 +101,14 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
       if (!diag) pc[u] = *(const f32x4*)(St + (size_t)min(keyC + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
     }
   };
+  // softmax weights A = exp(St - e) of staged scores (queries past qend: 0);
+  // exp in its hardware exp2 form: the arguments are <= 0 up to rounding
+  auto weights = [&](f32x4 v, int q0) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (q0 + j < qend) ? __expf(v[j] - ev[j]) : 0.f;
+    return w;
+  };
   if (qbeg < qend) prefetch(qbeg);
   for (int qt = qbeg; qt < qend; qt += 64) {
     __syncthreads();
@@ -126,19 +116,17 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     for (int u = 0; u < 4; ++u) {
       const int i = tid + 256 * u;
       const int r = yrows ? (i & 63) : (i >> 4), q4 = yrows ? 4 * (i >> 6) : 4 * (i & 15);
-      f32x4 v = pr[u];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (qt + q4 + j >= qend) v[j] = 0.f;
-      *(f32x4*)&Ra[r][q4] = v;
-      if (!diag) {
-        const int rc = i >> 4, qc = 4 * (i & 15);
-        f32x4 w = pc[u];
+      f32x4 v;
+      if (yrows) {
+        v = pr[u];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (qt + qc + j >= qend) w[j] = 0.f;
-        *(f32x4*)&Ca[rc][qc] = w;
+          if (qt + q4 + j >= qend) v[j] = 0.f;
+      } else {
+        v = weights(pr[u], qt + q4);
       }
+      *(f32x4*)&Ra[r][q4] = v;
+      if (!diag) *(f32x4*)&Ca[i >> 4][4 * (i & 15)] = weights(pc[u], qt + 4 * (i & 15));
     }
     __syncthreads();
     if (qt + 64 < qend) prefetch(qt + 64);
@@ -177,7 +165,6 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
 }
 
 void launch_gram(const GramArgs& a, int d, hipStream_t s) {
-  hipLaunchKernelGGL(weights_kernel, dim3(256, a.P), dim3(256), 0, s, a);
   const long long KT = a.kpadmax / 64;
   const long long T = KT * (KT + 1) / 2 + (long long)(d / 64) * KT;
   dim3 grid((unsigned)T, a.P, a.Cg);
