@@ -487,3 +487,67 @@ def pilot_allocate(problems, k0, scale, opt: CompressOptions, pilot_iters=60,
     kmax = Z if k_max is None else k_max
     ks = allocate_budget(mse, k0 * len(problems), alpha, k_min, kmax)
     return mse, ks, res
+
+
+# --------------------------------------------------------------------------
+# training-query construction
+# --------------------------------------------------------------------------
+
+def rotary(x, pos, theta):
+    """Rotary position embedding of the rows of ``x`` at integer positions ``pos``.
+
+    [gist] "Training Query Construction" speaks of RoPE'd queries without
+    fixing the convention.  Reading: the half-split pairing of the Llama /
+    Qwen families -- channel c and channel c + d/2 (c < d/2) form a plane,
+    turned counter-clockwise by pos * theta**(-2c/d), positions 0-based.
+    ``x`` is [..., d]; ``pos`` broadcasts against x's leading axes.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    h = d // 2
+    freq = np.power(float(theta), -2.0 * np.arange(h, dtype=np.float64) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * freq
+    cos, sin = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)))
+    out[..., :h] = a * cos - b * sin
+    out[..., h:] = a * sin + b * cos
+    return out
+
+
+def de_rotary(x, pos, theta):
+    """Remove the rotary embedding applied at ``pos`` (the De-RoPE step)."""
+    return rotary(x, -np.asarray(pos, dtype=np.float64), theta)
+
+
+def training_queries(Qctx, src, m, theta):
+    """Training queries of one KV head from its query heads' context queries.
+
+    [gist] "Training Query Construction": the real queries of the recent
+    context, plus synthetic future queries whose content is taken from the
+    context by undoing RoPE and which are embedded again at future positions,
+    the sources drawn uniformly over the context.  Readings:
+      * ``Qctx`` [g][N][d] holds the RoPE'd queries of the g query heads that
+        share the KV head, at context positions 0..N-1;
+      * retain queries are the rows at the retain-zone positions N-m..N-1
+        ([gist] "Problem Formulation": the most recent m pairs);
+      * ``src`` [g][F] holds the uniformly drawn source positions (the draw is
+        an input); synthetic query j of head h is the row at src[h][j] with its
+        rotation at src[h][j] removed, rotated again at position N + j;
+      * rows are ordered: retain block (head 0's m rows, head 1's, ...), then
+        the future block (head 0's F rows, head 1's, ...).
+    Returns Q [g(m+F)][d] in float64.
+    """
+    Qctx = _f64(Qctx)
+    src = np.asarray(src, dtype=np.int64)
+    g, N, d = Qctx.shape
+    F = src.shape[1] if src.ndim == 2 else 0
+    if src.size and (src.min() < 0 or src.max() >= N):
+        raise ValueError("source positions must lie in [0, N)")
+    retain = [Qctx[h, N - m:N] for h in range(g)]
+    future = []
+    for h in range(g):
+        content = de_rotary(Qctx[h, src[h]], src[h], theta)     # De-RoPE at the source
+        future.append(rotary(content, N + np.arange(F), theta))  # future positions
+    rows = retain + future
+    return np.concatenate(rows, axis=0) if rows else np.zeros((0, d))

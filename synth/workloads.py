@@ -132,19 +132,11 @@ def layer_temperatures(w: Workload, seed: int = 0) -> np.ndarray:
     return np.exp(rng.uniform(lo, hi, size=w.layers))
 
 
-def make_head(w: Workload, layer: int, head: int, seed: int = 0,
-              temperature: float = 1.0) -> dict:
-    """Build one KV head's problem in float64 (rounded to float32 by callers).
-
-    Returns a dict with
-      Kz, Vz   [Z, d]  compress zone (RoPE'd keys, plain values)
-      Kr, Vr   [m, d]  retain zone
-      Q        [n, d]  training queries: query head 0..g-1 retain rows, then
-                       query head 0..g-1 future rows
-      n_retain         number of retain rows (g*m)
-    """
-    rng = np.random.default_rng(np.random.SeedSequence([seed, w.cid, layer, head]))
-    d, N, m, Z, g, F = w.d, w.N, w.m, w.Z, w.g, w.F
+def _head_base(w: Workload, rng) -> dict:
+    """Draws shared by every view of one KV head, in a fixed order: channel
+    scales, key content (with outlier channels), values, the mean key
+    direction and the future queries' source positions."""
+    d, N, g, F = w.d, w.N, w.g, w.F
     sigma = np.exp(0.5 * rng.standard_normal(d))
     sigma_k = sigma.copy()
     if w.outliers:
@@ -158,7 +150,25 @@ def make_head(w: Workload, layer: int, head: int, seed: int = 0,
     mean_dir = kc.mean(axis=0)
     mean_dir = mean_dir / np.linalg.norm(mean_dir)
     fut_src = rng.integers(0, N, size=(g, F))
+    return dict(sigma=sigma, kc=kc, vals=vals, mean_dir=mean_dir, fut_src=fut_src)
 
+
+def make_head(w: Workload, layer: int, head: int, seed: int = 0,
+              temperature: float = 1.0) -> dict:
+    """Build one KV head's problem in float64 (rounded to float32 by callers).
+
+    Returns a dict with
+      Kz, Vz   [Z, d]  compress zone (RoPE'd keys, plain values)
+      Kr, Vr   [m, d]  retain zone
+      Q        [n, d]  training queries: query head 0..g-1 retain rows, then
+                       query head 0..g-1 future rows
+      n_retain         number of retain rows (g*m)
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([seed, w.cid, layer, head]))
+    d, N, m, Z, g, F = w.d, w.N, w.m, w.Z, w.g, w.F
+    base = _head_base(w, rng)
+    sigma, kc, vals = base["sigma"], base["kc"], base["vals"]
+    mean_dir, fut_src = base["mean_dir"], base["fut_src"]
     pos_all = np.arange(N)
     keys = rope(kc, pos_all, w.theta)
 
@@ -177,6 +187,50 @@ def make_head(w: Workload, layer: int, head: int, seed: int = 0,
     Q = np.concatenate(retain_rows + future_rows, axis=0)
     return dict(Kz=keys[:Z], Vz=vals[:Z], Kr=keys[Z:], Vr=vals[Z:], Q=Q,
                 n_retain=g * m)
+
+
+def make_context(w: Workload, layer: int, head: int, seed: int = 0,
+                 temperature: float = 1.0) -> dict:
+    """One KV head's context queries, for building training queries on device.
+
+    Keys, values and source positions are those of :func:`make_head` (same
+    stream, same draw order); the query content is then drawn at every
+    context position.  Returns
+      Qctx  [g, N, d]  RoPE'd queries of the g query heads at positions 0..N-1
+      src   [g, F]     source positions of the synthetic future queries,
+                       uniform over [0, N)
+      Kz, Vz, Kr, Vr   as in :func:`make_head`
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([seed, w.cid, layer, head]))
+    d, N, Z, g = w.d, w.N, w.Z, w.g
+    base = _head_base(w, rng)
+    keys = rope(base["kc"], np.arange(N), w.theta)
+    vals = base["vals"]
+    qctx = np.empty((g, N, d))
+    for h in range(g):
+        content = 0.5 * base["mean_dir"] + rng.standard_normal((N, d)) * base["sigma"]
+        qctx[h] = rope(content / temperature, np.arange(N), w.theta)
+    return dict(Qctx=qctx, src=base["fut_src"], Kz=keys[:Z], Vz=vals[:Z], Kr=keys[Z:],
+                Vr=vals[Z:])
+
+
+def make_context_batch(w: Workload, seed: int = 0,
+                       problems: Sequence[int] | None = None) -> dict:
+    """Stack :func:`make_context` over problems: Qctx [P, g, N, d] float32,
+    src [P, g, F] int32, Kz/Vz [P, Z, d] float32."""
+    temps = layer_temperatures(w, seed)
+    plist = problem_list(w, problems)
+    out = {k: [] for k in ("Qctx", "src", "Kz", "Vz")}
+    for p in plist:
+        layer, head = divmod(p, w.kv_heads)
+        hd = make_context(w, layer, head, seed, float(temps[layer]))
+        for k in out:
+            out[k].append(hd[k])
+    res = {k: np.ascontiguousarray(np.stack(v).astype(np.int32 if k == "src" else np.float32))
+           for k, v in out.items()}
+    res["problems"] = np.array(plist, dtype=np.int64)
+    res["scale"] = 1.0 / math.sqrt(w.d)
+    return res
 
 
 def problem_list(w: Workload, problems: Iterable[int] | None = None) -> list:
