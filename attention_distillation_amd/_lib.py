@@ -19,12 +19,14 @@ KVS_FLAG_NONFINITE = 1
 KVS_FLAG_CHOLESKY = 2
 KVS_FLAG_LINESEARCH = 4
 KVS_FLAG_NONDESCENT = 8
+KVS_FLAG_BADINDEX = 16
 
 ENTRY_POINTS = (
     "kvs_create", "kvs_destroy", "kvs_status_string", "kvs_last_error", "kvs_default_opts",
     "kvs_workspace_bytes", "kvs_lbfgs_state_bytes", "kvs_reference_attn", "kvs_init_topk",
     "kvs_loss_grad", "kvs_value_solve", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_compress",
-    "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_profile_enable", "kvs_profile_read",
+    "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_build_queries", "kvs_profile_enable",
+    "kvs_profile_read",
 )
 
 
@@ -38,6 +40,11 @@ class KvsBatch(ctypes.Structure):
     _fields_ = [("P", c_int32), ("d", c_int32), ("Z", c_int32), ("n", c_int32),
                 ("k", POINTER(c_int32)), ("scale", c_double), ("lambda_", c_double),
                 ("ridge_rel", c_double)]
+
+
+class KvsQueryGeom(ctypes.Structure):
+    _fields_ = [("P", c_int32), ("g", c_int32), ("N", c_int32), ("m", c_int32), ("F", c_int32),
+                ("d", c_int32), ("theta", c_double)]
 
 
 class KvsKernelStats(ctypes.Structure):
@@ -86,6 +93,7 @@ def load(path: str | None = None):
                                          V, V, c_size_t]),
         "kvs_allocate_budget": (c_int32, [POINTER(c_double), c_int32, c_int64, c_double, c_int32,
                                           c_int32, POINTER(c_int32)]),
+        "kvs_build_queries": (c_int32, [V, POINTER(KvsQueryGeom), V, V, V, V]),
         "kvs_profile_enable": (c_int32, [V, c_int32]),
         "kvs_profile_read": (c_int32, [V, POINTER(KvsKernelStats), c_int32, POINTER(c_int32)]),
     }
@@ -250,8 +258,15 @@ def kvs_allocate_budget(mse, K_total, alpha=0.5, k_min=1, k_max=1 << 30):
     return out
 
 
+def kvs_build_queries(ctx, P, g, N, m, F, d, theta, Qctx, src, Q, flags=None):
+    geom = KvsQueryGeom(P, g, N, m, F, d, float(theta))
+    ctx.check("kvs_build_queries", ctx.lib.kvs_build_queries(
+        ctx.handle, ctypes.byref(geom), _ptr(Qctx), _ptr(src), _ptr(Q), _ptr(flags)))
+
+
 PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",
-                   "hist_dots", "direction", "importance", "ref_attn_fwd", "merge")
+                   "hist_dots", "direction", "importance", "ref_attn_fwd", "merge",
+                   "build_queries")
 
 
 def kvs_profile_enable(ctx, enable=True, kernels=None):

@@ -17,11 +17,11 @@
 namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
-  PROF_IMP, PROF_REF, PROF_MERGE, PROF_NCLASS
+  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
-    "direction", "importance", "ref_attn_fwd", "merge"};
+    "direction", "importance", "ref_attn_fwd", "merge", "build_queries"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -769,6 +769,44 @@ kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o
 }  // extern "C"
 
 extern "C" {
+
+kvs_status kvs_build_queries(kvs_ctx ctx, const kvs_query_geom* q, const float* Qctx,
+                             const int32_t* src, float* Q, int32_t* flags) {
+  const char* fn = "kvs_build_queries";
+  if (!ctx) return KVS_ERR_INVALID;
+  ctx->err.clear();
+  if (!q) return fail(ctx, KVS_ERR_INVALID, "%s: geometry is NULL", fn);
+  const int d = q->d;
+  if (q->P < 1 || q->g < 1 || q->N < 1 || q->m < 0 || q->m > q->N || q->F < 0)
+    return fail(ctx, KVS_ERR_INVALID, "%s: bad sizes P=%d g=%d N=%d m=%d F=%d", fn, q->P, q->g,
+                q->N, q->m, q->F);
+  if (d != 8 && d != 16 && d != 32 && d != 64 && d != 128 && d != 256)
+    return fail(ctx, KVS_ERR_INVALID, "%s: d=%d is not a power of two in [8, 256]", fn, d);
+  if (!(q->theta > 1.0) || !std::isfinite(q->theta))
+    return fail(ctx, KVS_ERR_INVALID, "%s: theta must be finite and > 1", fn);
+  const long long per_p = (long long)q->g * (q->m + q->F);
+  if (per_p < 1) return fail(ctx, KVS_ERR_INVALID, "%s: no queries to build (g (m + F) = 0)", fn);
+  if ((long long)q->N + q->F > (1LL << 30))
+    return fail(ctx, KVS_ERR_INVALID, "%s: positions beyond 2^30", fn);
+  KVS_NEED(Qctx); KVS_NEED(Q);
+  if (q->F > 0 && !src) return fail(ctx, KVS_ERR_INVALID, "%s: argument 'src' is NULL", fn);
+  if (src && !aligned(src, 4)) return fail(ctx, KVS_ERR_ALIGN, "%s: 'src' not 4-byte aligned", fn);
+  if (flags && !aligned(flags, 4)) return fail(ctx, KVS_ERR_ALIGN, "%s: 'flags' not 4-byte aligned", fn);
+  QueryArgs a{};
+  a.Qctx = Qctx; a.src = src; a.Q = Q; a.flags = flags;
+  a.P = q->P; a.g = q->g; a.N = q->N; a.m = q->m; a.F = q->F; a.d = d;
+  a.bad_flag = KVS_FLAG_BADINDEX;
+  a.log2_theta = std::log2(q->theta);
+  a.freq_ratio = std::exp2(-2.0 / d * a.log2_theta);
+  {
+    // every output element is read once and written once; the future rows
+    // also read their source index
+    const double rows = (double)q->P * per_p;
+    Prof pr(ctx, PROF_QUERIES, 0.0, rows * d * 8.0 + (double)q->P * q->g * q->F * 4.0);
+    launch_build_queries(a, ctx->stream);
+  }
+  return hip_check(ctx, fn);
+}
 
 kvs_status kvs_profile_enable(kvs_ctx ctx, int32_t enable) {
   if (!ctx) return KVS_ERR_INVALID;

@@ -239,6 +239,19 @@ struct DirArgs {
 };
 void launch_direction(const DirArgs& a, hipStream_t s);
 
+// Training queries: retain rows copied, future rows rotated by (N + j - s).
+struct QueryArgs {
+  const float* Qctx;       // [P][g][N][d]
+  const int* src;          // [P][g][F]
+  float* Q;                // [P][g(m+F)][d]
+  int* flags;              // [P] or NULL: bad_flag set on an invalid source
+  int P, g, N, m, F, d;
+  int bad_flag;
+  double log2_theta;       // log2 of the RoPE base
+  double freq_ratio;       // theta^(-2/d): frequency of plane c+1 over plane c
+};
+void launch_build_queries(const QueryArgs& a, hipStream_t s);
+
 void launch_write_info(ProbInfo* dst, const ProbInfo* src, int P, hipStream_t s);
 void launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 void launch_fill_f32(float* p, float v, long long n, hipStream_t s);

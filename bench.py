@@ -10,6 +10,12 @@ also runs the 60-iteration pilot and the budget reallocation before the main
 run at ragged k.  The metric is problem-iterations per second,
 P * T * K / (wall time of the K timed steps), inputs resident in HBM.
 
+With --row queries the step is instead one kvs_build_queries call over the
+workload's problems: retain queries copied and synthetic future queries
+re-embedded from context queries sampled uniformly over the context (the
+step just before the optimizer); the metric is training queries built per
+second.
+
 Printed: one JSON line (stdout).  It carries the live roofline of the
 dominant kernel (HIP events on the library's stream over the timed steps)
 and the float64 oracle timed on a bounded sample on the host CPU.
@@ -109,6 +115,76 @@ def cpu_baseline(w, b, seconds):
                       f"solves every 5 (Select+Fit init excluded), float64 NumPy/SciPy"}
 
 
+def cpu_queries(w, b, seconds):
+    """Float64 oracle of the training-query construction on whole problems."""
+    from oracle import kvsculpt as O
+    P = b["Qctx"].shape[0]
+    done, rows, t0 = 0, 0, time.perf_counter()
+    while True:
+        p = done % P
+        Qo = O.training_queries(b["Qctx"][p], b["src"][p], w.m, w.theta)
+        rows += Qo.shape[0]
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rows / el, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name}: {done} problems' training queries "
+                      f"({rows} rows of d={w.d}), float64 NumPy"}
+
+
+def bench_queries(args, torch, K):
+    """Training-query construction alone: one launch per step."""
+    from synth import WORKLOADS, make_context_batch
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating context queries of {w.name}: P={w.P} g={w.g} N={w.N} d={w.d}")
+    b = make_context_batch(w, 0)
+    P, g, N, d = b["Qctx"].shape
+    F, m = b["src"].shape[2], w.m
+    n = g * (m + F)
+    Qctx = torch.from_numpy(b["Qctx"]).to(dev)
+    src = torch.from_numpy(b["src"]).to(dev)
+    Q = torch.empty((P, n, d), dtype=torch.float32, device=dev)
+    ctx = K.Context()
+
+    def step():
+        K.kvs_build_queries(ctx, P, g, N, m, F, d, w.theta, Qctx, src, Q, None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kvs_profile_enable(ctx, True, kernels=["build_queries"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = K.kvs_profile_read(ctx)["build_queries"]
+    K.kvs_profile_enable(ctx, False)
+    avg_s = st["ms"] / st["launches"] / 1e3
+    bytes_launch = st["bytes"] / st["launches"]
+    achieved = bytes_launch / avg_s
+    roofline = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+                "traffic": traffic_for("build_queries"), "kernel": "build_queries",
+                "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
+    cpu = None if args.no_cpu_baseline else cpu_queries(w, b, min(args.cpu_seconds, 10.0))
+    out = {
+        "metric": "training queries built/sec (retain copies + De-RoPE/RoPE future queries)",
+        "value": round(P * n * args.steps / elapsed, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (angles f64)", "data": "synthetic",
+        "config": {"workload": w.name, "row": "queries", "problems": P, "g": g, "N": N, "m": m,
+                   "F": F, "d": d, "theta": w.theta},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +195,8 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row", choices=["compress", "queries"], default="compress",
+                    help="compress: the optimizer (default); queries: training-query construction")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this size (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -133,6 +211,9 @@ def main():
         return
     import attention_distillation_amd as K
     from synth import WORKLOADS, make_batch
+    if args.row == "queries":
+        bench_queries(args, torch, K)
+        return
 
     w = WORKLOADS[args.config]
     if args.ratio is not None:

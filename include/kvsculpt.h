@@ -197,6 +197,38 @@ kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o
 kvs_status kvs_allocate_budget(const double* mse, int32_t P, int64_t K_total, double alpha,
                                int32_t k_min, int32_t k_max, int32_t* k_out);
 
+/* Training queries (gist page, section 2 "Training Query Construction": real
+ * queries of the recent context plus synthetic future queries whose content
+ * is taken from the context by undoing RoPE and embedded again at future
+ * positions, the sources sampled uniformly over the context).
+ *   Qctx [P][g][N][d]  device: RoPE'd queries of the g query heads sharing
+ *                      KV head p, at context positions 0..N-1
+ *   src  [P][g][F]     device int32: source positions of the synthetic
+ *                      queries (the caller's uniform draw over [0, N));
+ *                      may be NULL when F == 0
+ *   Q    [P][g(m+F)][d] device output: per problem the retain block
+ *                      (head 0's rows at positions N-m..N-1, head 1's, ...)
+ *                      then the future block (head h's query j at row
+ *                      g m + h F + j): row Qctx[p][h][s] with s = src[p][h][j],
+ *                      turned back by its rotation at s and forward by the
+ *                      rotation at position N + j.
+ * RoPE: channel c and c + d/2 (c < d/2) form a plane turned by
+ * pos * theta^(-2c/d).  Retain rows are exact copies; future rows carry
+ * float32 rounding of the turned values (the angle itself is reduced in
+ * float64).  A source outside [0, N) gives a zero row and sets
+ * KVS_FLAG_BADINDEX in flags[p] (device int32[P], may be NULL; bits are OR'ed
+ * in, never cleared).  Errors: KVS_ERR_INVALID for P, g < 1, N < 1, m outside
+ * [0, N], F < 0, g (m + F) < 1, d not one of 8, 16, 32, 64, 128, 256 or
+ * theta <= 1; KVS_ERR_ALIGN for Qctx or Q not 16-byte aligned.  No workspace
+ * is needed. */
+#define KVS_FLAG_BADINDEX     16   /* a training-query source outside [0, N)  */
+typedef struct {
+  int32_t P, g, N, m, F, d;
+  double  theta;        /* RoPE base (1e4 .. 1e6 in the Llama / Qwen families) */
+} kvs_query_geom;
+kvs_status kvs_build_queries(kvs_ctx ctx, const kvs_query_geom* q, const float* Qctx,
+                             const int32_t* src, float* Q, int32_t* flags);
+
 /* Opt-in kernel timing, for measurement tools.  While enabled, the library
  * records a HIP event pair on the context stream around each launch of its
  * main kernels and accumulates, per kernel, the launch count, the summed
@@ -205,8 +237,8 @@ kvs_status kvs_allocate_budget(const double* mse, int32_t P, int64_t K_total, do
  * kvs_profile_enable clears the totals; its argument is 0 (off), -1 (all
  * kernels) or a bitmask over attn_fwd (bit 0), attn_bwd, gram, potrf_panel,
  * trailing, back_subst, hist_dots, direction, importance, ref_attn_fwd,
- * merge (bit 10).  kvs_profile_read synchronises the stream and writes up to
- * max entries (kernels with launches) to out. */
+ * merge, build_queries (bit 11).  kvs_profile_read synchronises the stream
+ * and writes up to max entries (kernels with launches) to out. */
 typedef struct {
   char    name[32];
   int64_t launches;

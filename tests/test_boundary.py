@@ -71,6 +71,33 @@ def test_argument_errors_are_reported_before_any_launch(K):
     assert lib.kvs_destroy(ctx) == 0
 
 
+def test_build_queries_argument_errors(K):
+    lib = K.load()
+    ctx = ctypes.c_void_p()
+    assert lib.kvs_create(ctypes.byref(ctx), None) == 0
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    G = K._lib.KvsQueryGeom
+
+    def call(geom, qctx=fake, src=fake, q=fake):
+        return lib.kvs_build_queries(ctx, ctypes.byref(geom), qctx, src, q, None)
+
+    # bad sizes, head dims and bases are refused with a message
+    for geom, word in [(G(0, 6, 2048, 128, 512, 128, 1e6), b"sizes"),
+                       (G(2, 6, 2048, 2049, 512, 128, 1e6), b"sizes"),
+                       (G(2, 6, 2048, 128, -1, 128, 1e6), b"sizes"),
+                       (G(2, 6, 2048, 128, 512, 96, 1e6), b"power of two"),
+                       (G(2, 6, 2048, 128, 512, 128, 1.0), b"theta"),
+                       (G(2, 6, 2048, 0, 0, 128, 1e6), b"no queries")]:
+        assert call(geom) == -1 and word in lib.kvs_last_error(ctx), geom
+    good = G(2, 6, 2048, 128, 512, 128, 1e6)
+    assert call(good, qctx=None) == -1
+    assert call(good, src=None) == -1 and b"src" in lib.kvs_last_error(ctx)
+    assert call(good, q=odd) == -2
+    assert lib.kvs_build_queries(ctx, None, fake, fake, fake, None) == -1
+    assert lib.kvs_destroy(ctx) == 0
+
+
 def test_allocator_cpp_equals_oracle_bit_for_bit(K):
     rng = np.random.default_rng(20)
     for it in range(10000):
