@@ -5,18 +5,18 @@ ABI, declared in include/kvsculpt.h); this package is the thin ctypes
 binding with the same entry-point names.  Importing it does not touch the
 GPU; calling an entry point needs the built library and a GPU.
 """
-from ._lib import (ENTRY_POINTS, KVS_FLAG_CHOLESKY, KVS_FLAG_LINESEARCH, KVS_FLAG_NONDESCENT,
-                   KVS_FLAG_NONFINITE, Batch, Context, KvsBatch, KvsError, KvsOpts,
-                   kvs_allocate_budget, kvs_compress, kvs_init_topk, kvs_lbfgs_init,
-                   kvs_lbfgs_step, kvs_loss_grad, kvs_pilot_allocate, kvs_profile_enable,
-                   kvs_profile_read, kvs_reference_attn,
+from ._lib import (ENTRY_POINTS, KVS_FLAG_BADINDEX, KVS_FLAG_CHOLESKY, KVS_FLAG_LINESEARCH,
+                   KVS_FLAG_NONDESCENT, KVS_FLAG_NONFINITE, Batch, Context, KvsBatch, KvsError,
+                   KvsOpts, KvsQueryGeom, kvs_allocate_budget, kvs_build_queries, kvs_compress,
+                   kvs_init_topk, kvs_lbfgs_init, kvs_lbfgs_step, kvs_loss_grad,
+                   kvs_pilot_allocate, kvs_profile_enable, kvs_profile_read, kvs_reference_attn,
                    kvs_value_solve, lbfgs_state_bytes, load, opts, workspace_bytes)
 
 __all__ = [
-    "ENTRY_POINTS", "KVS_FLAG_CHOLESKY", "KVS_FLAG_LINESEARCH", "KVS_FLAG_NONDESCENT",
-    "KVS_FLAG_NONFINITE", "Batch", "Context", "KvsBatch", "KvsError", "KvsOpts",
-    "kvs_allocate_budget", "kvs_compress", "kvs_init_topk", "kvs_lbfgs_init", "kvs_lbfgs_step",
-    "kvs_loss_grad", "kvs_pilot_allocate", "kvs_profile_enable", "kvs_profile_read",
-    "kvs_reference_attn", "kvs_value_solve",
+    "ENTRY_POINTS", "KVS_FLAG_BADINDEX", "KVS_FLAG_CHOLESKY", "KVS_FLAG_LINESEARCH",
+    "KVS_FLAG_NONDESCENT", "KVS_FLAG_NONFINITE", "Batch", "Context", "KvsBatch", "KvsError",
+    "KvsOpts", "KvsQueryGeom", "kvs_allocate_budget", "kvs_build_queries", "kvs_compress",
+    "kvs_init_topk", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_loss_grad", "kvs_pilot_allocate",
+    "kvs_profile_enable", "kvs_profile_read", "kvs_reference_attn", "kvs_value_solve",
     "lbfgs_state_bytes", "load", "opts", "workspace_bytes",
 ]

@@ -54,9 +54,12 @@ def mixed_fwd_peak():
 # plain copy's known bytes to what the same counter reads for it.  Valid only
 # for the kernel source they were taken on (sha256 of that file).
 MEASURED_TRAFFIC = {
-    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 12970.7 KiB x 1.99977
+    # qwen2.5-1.5b-full-cache training queries: FETCH 53517.7 KiB x 1.99978
+    # + WRITE 107520.0 KiB x 1.00000 per dispatch
+    "build_queries": {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
+    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 10054.6 KiB x 1.99978
     # + WRITE 54000.0 KiB x 1.00000 per dispatch
-    "attn_fwd": {"bytes": 81857049, "source": "attn_fwd.hip", "sha": "786d74eb12f60d46"},
+    "attn_fwd": {"bytes": 75885543, "source": "attn_fwd.hip", "sha": "de425ab819f1f1df"},
 }
 
 
