@@ -30,6 +30,11 @@ normal-equation residual and the stacked least-squares routine for the
 ridge solve, dense BFGS inverse-Hessian recursion for the two-loop output,
 Rosenbrock and convex least squares for the optimizer, brute-force search
 on a tiny instance, and hand cases plus invariants for the allocator.
+Training-query construction (tests/test_oracle_queries.py): a complex-
+exponential closed form, textbook trigonometric values, norm and relative-
+position invariants, layout.  Use-side evaluation (tests/test_oracle_use.py):
+the LSE merge of per-chunk attention, hand arithmetic, a mass-preserving
+exact merge of duplicate keys, degenerate caches.
 """
 from __future__ import annotations
 
@@ -551,3 +556,38 @@ def training_queries(Qctx, src, m, theta):
         future.append(rotary(content, N + np.arange(F), theta))  # future positions
     rows = retain + future
     return np.concatenate(rows, axis=0) if rows else np.zeros((0, d))
+
+
+# --------------------------------------------------------------------------
+# use-side evaluation
+# --------------------------------------------------------------------------
+
+def use_side_outputs(Qh, Kz, Vz, Kr, Vr, Kc, Vc, scale):
+    """Attention outputs at use time over the full and the compressed cache.
+
+    [gist] "Problem Formulation": the compressed cache (k free pairs in place
+    of the compress zone, retain zone unchanged) should give the full cache's
+    attention output for future queries; "Loss Function": the LSE term keeps
+    the chunk's attention mass right when it is combined with the other
+    tokens.  Reading: a use-time query attends over [Kz; Kr] (full cache) or
+    [Kc; Kr] (compressed cache) in one softmax -- the plain definition, no
+    chunk merging -- with scores scale * q.k and no mask (every held-out
+    query comes after the whole context).  ``Kr`` may have zero rows.
+    Returns dict(full [nh, d], comp [nh, d], mse, rel) with
+    mse = ||comp - full||_F^2 / (nh d) and rel = ||comp - full||_F / ||full||_F.
+    """
+    Qh = _f64(Qh)
+    d = Qh.shape[1]
+    Kr = _f64(Kr).reshape(-1, d)
+    Vr = _f64(Vr).reshape(-1, d)
+
+    def attend(K, V):
+        W, _ = softmax_rows(logits(Qh, K, scale))
+        return W @ V
+
+    full = attend(np.concatenate([_f64(Kz), Kr]), np.concatenate([_f64(Vz), Vr]))
+    comp = attend(np.concatenate([_f64(Kc), Kr]), np.concatenate([_f64(Vc), Vr]))
+    D = comp - full
+    sq = float(np.sum(D * D))
+    nf = float(np.sqrt(np.sum(full * full)))
+    return dict(full=full, comp=comp, mse=sq / D.size, rel=math.sqrt(sq) / nf if nf > 0 else 0.0)

@@ -233,6 +233,42 @@ def make_context_batch(w: Workload, seed: int = 0,
     return res
 
 
+def make_use_batch(w: Workload, seed: int = 0, problems: Sequence[int] | None = None,
+                   per_head: int | None = None) -> dict:
+    """Held-out future queries with the caches of :func:`make_batch`.
+
+    Keys and values are those of :func:`make_head` (same stream, same draw
+    order).  The held-out queries come from a stream of their own: per query
+    head, ``per_head`` (default F) fresh query contents of the same
+    distribution as the context's (0.5 * mean key direction + N(0, sigma^2),
+    over the layer temperature), RoPE'd at the future positions N, N+1, ...
+    Returns Qh [P, g*per_head, d], Kz/Vz [P, Z, d], Kr/Vr [P, m, d] float32.
+    """
+    temps = layer_temperatures(w, seed)
+    plist = problem_list(w, problems)
+    per = w.F if per_head is None else int(per_head)
+    out = {k: [] for k in ("Qh", "Kz", "Vz", "Kr", "Vr")}
+    for p in plist:
+        layer, head = divmod(p, w.kv_heads)
+        rng = np.random.default_rng(np.random.SeedSequence([seed, w.cid, layer, head]))
+        base = _head_base(w, rng)
+        keys = rope(base["kc"], np.arange(w.N), w.theta)
+        hrng = np.random.default_rng(np.random.SeedSequence([seed, w.cid, layer, head, 2]))
+        rows = []
+        for _ in range(w.g):
+            content = 0.5 * base["mean_dir"] + hrng.standard_normal((per, w.d)) * base["sigma"]
+            rows.append(rope(content / float(temps[layer]), w.N + np.arange(per), w.theta))
+        out["Qh"].append(np.concatenate(rows, axis=0))
+        out["Kz"].append(keys[:w.Z])
+        out["Vz"].append(base["vals"][:w.Z])
+        out["Kr"].append(keys[w.Z:])
+        out["Vr"].append(base["vals"][w.Z:])
+    res = {k: np.ascontiguousarray(np.stack(v).astype(np.float32)) for k, v in out.items()}
+    res["problems"] = np.array(plist, dtype=np.int64)
+    res["scale"] = 1.0 / math.sqrt(w.d)
+    return res
+
+
 def problem_list(w: Workload, problems: Iterable[int] | None = None) -> list:
     P = w.P
     return list(range(P)) if problems is None else [int(p) for p in problems]
