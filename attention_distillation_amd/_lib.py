@@ -25,8 +25,8 @@ ENTRY_POINTS = (
     "kvs_create", "kvs_destroy", "kvs_status_string", "kvs_last_error", "kvs_default_opts",
     "kvs_workspace_bytes", "kvs_lbfgs_state_bytes", "kvs_reference_attn", "kvs_init_topk",
     "kvs_loss_grad", "kvs_value_solve", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_compress",
-    "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_build_queries", "kvs_profile_enable",
-    "kvs_profile_read",
+    "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_build_queries", "kvs_use_eval_workspace_bytes",
+    "kvs_use_eval", "kvs_profile_enable", "kvs_profile_read",
 )
 
 
@@ -94,6 +94,8 @@ def load(path: str | None = None):
         "kvs_allocate_budget": (c_int32, [POINTER(c_double), c_int32, c_int64, c_double, c_int32,
                                           c_int32, POINTER(c_int32)]),
         "kvs_build_queries": (c_int32, [V, POINTER(KvsQueryGeom), V, V, V, V]),
+        "kvs_use_eval_workspace_bytes": (c_size_t, [B, c_int32]),
+        "kvs_use_eval": (c_int32, [V, B, c_int32, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t]),
         "kvs_profile_enable": (c_int32, [V, c_int32]),
         "kvs_profile_read": (c_int32, [V, POINTER(KvsKernelStats), c_int32, POINTER(c_int32)]),
     }
@@ -264,9 +266,20 @@ def kvs_build_queries(ctx, P, g, N, m, F, d, theta, Qctx, src, Q, flags=None):
         ctx.handle, ctypes.byref(geom), _ptr(Qctx), _ptr(src), _ptr(Q), _ptr(flags)))
 
 
+def use_eval_workspace_bytes(batch: Batch, m: int) -> int:
+    return load().kvs_use_eval_workspace_bytes(ctypes.byref(batch.c), int(m))
+
+
+def kvs_use_eval(ctx, batch, m, Qh, Kz, Vz, Kr, Vr, Kc, Vc, Ofull, Ocomp, mse, rel, ws):
+    w, nb = _ws(ws)
+    ctx.check("kvs_use_eval", ctx.lib.kvs_use_eval(
+        ctx.handle, ctypes.byref(batch.c), int(m), _ptr(Qh), _ptr(Kz), _ptr(Vz), _ptr(Kr),
+        _ptr(Vr), _ptr(Kc), _ptr(Vc), _ptr(Ofull), _ptr(Ocomp), _ptr(mse), _ptr(rel), w, nb))
+
+
 PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",
                    "hist_dots", "direction", "importance", "ref_attn_fwd", "merge",
-                   "build_queries")
+                   "build_queries", "use_attn_fwd")
 
 
 def kvs_profile_enable(ctx, enable=True, kernels=None):

@@ -17,11 +17,11 @@
 namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
-  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_NCLASS
+  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
-    "direction", "importance", "ref_attn_fwd", "merge", "build_queries"};
+    "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -805,6 +805,75 @@ kvs_status kvs_build_queries(kvs_ctx ctx, const kvs_query_geom* q, const float* 
     Prof pr(ctx, PROF_QUERIES, 0.0, rows * d * 8.0 + (double)q->P * q->g * q->F * 4.0);
     launch_build_queries(a, ctx->stream);
   }
+  return hip_check(ctx, fn);
+}
+
+size_t kvs_use_eval_workspace_bytes(const kvs_batch* b, int32_t m) {
+  UsePlan u;
+  if (!make_use_plan(b, m, &u).empty()) return 0;
+  return u.ws_bytes;
+}
+
+kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float* Qh,
+                        const float* Kz, const float* Vz, const float* Kr, const float* Vr,
+                        const float* Kc, const float* Vc, float* Ofull, float* Ocomp, float* mse,
+                        float* rel, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_use_eval";
+  if (!ctx) return KVS_ERR_INVALID;
+  ctx->err.clear();
+  UsePlan u;
+  std::string e = make_use_plan(b, m, &u);
+  if (!e.empty()) return fail(ctx, KVS_ERR_INVALID, "%s: %s", fn, e.c_str());
+  KVS_NEED(Qh); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(Kc); KVS_NEED(Vc); KVS_NEED(mse);
+  if (m > 0) { KVS_NEED(Kr); KVS_NEED(Vr); }
+  KVS_OPT(Ofull); KVS_OPT(Ocomp); KVS_OPT(rel);
+  if (!ws) return fail(ctx, KVS_ERR_INVALID, "%s: workspace is NULL", fn);
+  if (!aligned(ws, 256)) return fail(ctx, KVS_ERR_ALIGN, "%s: workspace not 256-byte aligned", fn);
+  if (ws_bytes < u.ws_bytes)
+    return fail(ctx, KVS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes,
+                u.ws_bytes);
+  launch_write_info(at<ProbInfo>(ws, u.r_info), u.info.data(), u.P, ctx->stream);
+
+  const size_t pn = (size_t)u.P * u.n;
+  float* Opart = at<float>(ws, u.r_Opart);
+  float* Mpart = at<float>(ws, u.r_Mpart);
+  float* Lpart = at<float>(ws, u.r_Lpart);
+  // split-key partials of one cache into planes [c0, c0 + C)
+  auto chunk_fwd = [&](const float* K, const float* V, const ProbInfo* info, int kuni, int kmax,
+                       int C, int c0, double keys) {
+    FwdArgs f{};
+    f.Q = Qh; f.K = K; f.V = V; f.st = nullptr; f.active_mask = 0; f.shift = nullptr;
+    f.St = nullptr;
+    f.Opart = Opart + (size_t)c0 * pn * u.d;
+    f.Mpart = Mpart + (size_t)c0 * pn;
+    f.Lpart = Lpart + (size_t)c0 * pn;
+    f.info = info; f.P = u.P; f.n = u.n; f.C = C; f.kuni = kuni; f.kmax = kmax;
+    f.scale = b->scale;
+    Prof pr(ctx, PROF_USE, 4.0 * u.n * u.d * keys, 4.0 * (keys * u.d * 2.0 + (double)pn * u.d));
+    launch_attn_fwd(f, u.d, ctx->logit_f64, ctx->stream);
+  };
+  chunk_fwd(Kz, Vz, nullptr, u.Z, u.Z, u.Cz, 0, (double)u.P * u.Z);
+  if (u.Cr) chunk_fwd(Kr, Vr, nullptr, m, m, u.Cr, u.Cz, (double)u.P * m);
+  chunk_fwd(Kc, Vc, at<ProbInfo>(ws, u.r_info), 0, u.kmax, u.Cc, u.Cz + u.Cr, (double)u.ktot);
+
+  float* Of = Ofull ? Ofull : at<float>(ws, u.r_Of);
+  float* Oc = Ocomp ? Ocomp : at<float>(ws, u.r_Oc);
+  auto merge = [&](int c0, int C, float* Y, float* lse) {
+    MergeArgs mg{};
+    mg.Opart = Opart + (size_t)c0 * pn * u.d;
+    mg.Mpart = Mpart + (size_t)c0 * pn;
+    mg.Lpart = Lpart + (size_t)c0 * pn;
+    mg.st = nullptr; mg.active_mask = 0; mg.Yout = Y; mg.lse_out = lse;
+    mg.P = u.P; mg.n = u.n; mg.C = C; mg.lambda = b->lambda;
+    launch_merge(mg, u.d, false, ctx->stream);
+  };
+  merge(0, u.Cz + u.Cr, Of, at<float>(ws, u.r_lf));            // [Kz; Kr]
+  merge(u.Cz, u.Cr + u.Cc, Oc, at<float>(ws, u.r_lc));         // [Kr; Kc]
+
+  UseErrArgs ea{};
+  ea.Of = Of; ea.Oc = Oc; ea.part = at<double>(ws, u.r_part); ea.mse = mse; ea.rel = rel;
+  ea.P = u.P; ea.n = u.n; ea.d = u.d; ea.nblk = u.nblk;
+  launch_use_err(ea, ctx->stream);
   return hip_check(ctx, fn);
 }
 

@@ -252,6 +252,16 @@ struct QueryArgs {
 };
 void launch_build_queries(const QueryArgs& a, hipStream_t s);
 
+// Use-side error: per problem sum (Oc - Of)^2 and sum Of^2 over [n][d] rows.
+struct UseErrArgs {
+  const float* Of; const float* Oc;
+  double* part;            // [P][nblk][2]
+  float* mse; float* rel;  // [P]; rel may be NULL
+  int P, n, d, nblk;
+};
+int use_err_blocks(int n);
+void launch_use_err(const UseErrArgs& a, hipStream_t s);
+
 void launch_write_info(ProbInfo* dst, const ProbInfo* src, int P, hipStream_t s);
 void launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 void launch_fill_f32(float* p, float v, long long n, hipStream_t s);

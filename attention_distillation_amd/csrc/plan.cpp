@@ -22,6 +22,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+int key_chunks(int P, int n, int keys, int cap) {
+  if (keys <= 0) return 0;
+  const long long qtiles = (n + 63) / 64;
+  const int c = std::max(1, std::min(split_for((long long)P * qtiles, (keys + 63) / 64), cap));
+  const int len = (((keys + c - 1) / c) + 63) / 64 * 64;
+  return (keys + len - 1) / len;
+}
+
 std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   if (!b) return "batch is NULL";
   if (b->P < 1) return "P must be >= 1";
@@ -68,15 +76,8 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p.ktot = koff; p.stot = soff; p.mtot = moff; p.kpadtot = xoff / p.d;
 
   const long long qtiles = (p.n + 63) / 64;
-  // key chunks of the split forward: at most kMaxChunks, and no chunk left
-  // empty by rounding the chunk length up to whole 64-key tiles
-  auto chunks = [&](int keys) {
-    const int c = std::min(split_for((long long)p.P * qtiles, (keys + 63) / 64), kMaxChunks);
-    const int len = (((keys + c - 1) / c) + 63) / 64 * 64;
-    return (keys + len - 1) / len;
-  };
-  p.Cref = chunks(p.Z);
-  p.C = chunks(p.kmax);
+  p.Cref = key_chunks(p.P, p.n, p.Z, kMaxChunks);
+  p.C = key_chunks(p.P, p.n, p.kmax, kMaxChunks);
   p.Cn = std::max(1, split_for((long long)p.P * ((p.kmax + 63) / 64), (int)qtiles) / 2);
   const int KT = p.kpadmax / kTile;
   const long long gtiles = (long long)KT * (KT + 1) / 2 + (long long)(p.d / kTile) * KT;
@@ -137,6 +138,42 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.s_S, f * (size_t)(H + 1) * p.ktot * p.d);
   take(p.s_Yh, f * (size_t)(H + 1) * p.ktot * p.d);
   p.state_bytes = off;
+  return std::string();
+}
+
+std::string make_use_plan(const kvs_batch* b, int m, UsePlan* up) {
+  Plan base;
+  std::string e = make_plan(b, nullptr, &base);
+  if (!e.empty()) return e;
+  if (m < 0) return "m must be >= 0";
+  UsePlan& u = *up;
+  u = UsePlan();
+  u.P = base.P; u.d = base.d; u.Z = base.Z; u.n = base.n; u.m = m; u.kmax = base.kmax;
+  u.ktot = base.ktot;
+  u.info = base.info;
+  // the two merges read planes [0, Cz + Cr) and [Cz, Cz + Cr + Cc): each at
+  // most kMaxChunks
+  u.Cr = m > 0 ? key_chunks(u.P, u.n, m, 4) : 0;
+  u.Cz = key_chunks(u.P, u.n, u.Z, kMaxChunks - u.Cr);
+  u.Cc = key_chunks(u.P, u.n, u.kmax, kMaxChunks - u.Cr);
+  u.nblk = use_err_blocks(u.n);
+  const size_t f = 4, planes = (size_t)(u.Cz + u.Cr + u.Cc), pn = (size_t)u.P * u.n;
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off = align256(off + bytes);
+  };
+  take(u.r_info, sizeof(ProbInfo) * u.P);
+  take(u.r_Opart, f * planes * pn * u.d);
+  take(u.r_Mpart, f * planes * pn);
+  take(u.r_Lpart, f * planes * pn);
+  take(u.r_Of, f * pn * u.d);
+  take(u.r_Oc, f * pn * u.d);
+  take(u.r_lf, f * pn);
+  take(u.r_lc, f * pn);
+  take(u.r_part, sizeof(double) * 2 * (size_t)u.P * u.nblk);
+  u.ws_bytes = off;
   return std::string();
 }
 

@@ -30,6 +30,24 @@ struct Plan {
 // Fills plan from the batch; returns an error text or empty.
 std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* plan);
 
+// Key chunks of the split forward for `keys` keys: at most `cap`, enough
+// workgroups for the part, and no chunk left empty by rounding the chunk
+// length up to whole 64-key tiles.
+int key_chunks(int P, int n, int keys, int cap);
+
+// Workspace of the use-side evaluation: split-key partials of the three
+// caches (compress zone, retain zone, compressed pairs) in adjacent planes,
+// the two merged outputs and the error partials.
+struct UsePlan {
+  int P = 0, d = 0, Z = 0, n = 0, m = 0, kmax = 0;
+  long long ktot = 0;
+  int Cz = 0, Cr = 0, Cc = 0, nblk = 0;
+  std::vector<ProbInfo> info;
+  Region r_info, r_Opart, r_Mpart, r_Lpart, r_Of, r_Oc, r_lf, r_lc, r_part;
+  size_t ws_bytes = 0;
+};
+std::string make_use_plan(const kvs_batch* b, int m, UsePlan* plan);
+
 template <typename T>
 inline T* at(void* base, const Region& r) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + r.off);

@@ -14,7 +14,10 @@ With --row queries the step is instead one kvs_build_queries call over the
 workload's problems: retain queries copied and synthetic future queries
 re-embedded from context queries sampled uniformly over the context (the
 step just before the optimizer); the metric is training queries built per
-second.
+second.  With --row use it is one kvs_use_eval call: held-out future
+queries over the full and the compressed cache (the step just after the
+optimizer); the metric is held-out queries evaluated per second.  Both
+default to the 56-problem full-cache workload (--config 2).
 
 Printed: one JSON line (stdout).  It carries the live roofline of the
 dominant kernel (HIP events on the library's stream over the timed steps)
@@ -88,14 +91,18 @@ def copy_probe(torch, mib):
     log(f"[bench] copied {mib} MiB three times")
 
 
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(w, b, seconds):
     """Float64 oracle on problem 0 of the same workload (host cores)."""
     from oracle import kvsculpt as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _threads()
     Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
     Y, l = O.reference_attention(Q, Kz, Vz, s)
     t0 = time.perf_counter()
@@ -188,21 +195,104 @@ def bench_queries(args, torch, K):
     print(json.dumps(out), flush=True)
 
 
+def cpu_use(w, u, Kc, Vc, k, seconds):
+    """Float64 oracle of the use-side evaluation on whole problems."""
+    from oracle import kvsculpt as O
+    P = u["Qh"].shape[0]
+    done, rows, t0 = 0, 0, time.perf_counter()
+    while True:
+        p = done % P
+        O.use_side_outputs(u["Qh"][p], u["Kz"][p], u["Vz"][p], u["Kr"][p], u["Vr"][p],
+                           Kc[p * k:(p + 1) * k], Vc[p * k:(p + 1) * k], u["scale"])
+        rows += u["Qh"].shape[1]
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rows / el, "unit": "queries/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{w.name}: {done} problems' use-side outputs ({rows} held-out queries "
+                      f"over Z={w.Z} + m={w.m} and k={k} + m keys), float64 NumPy"}
+
+
+def bench_use(args, torch, K):
+    """Use-side evaluation alone: held-out queries over the full and the compressed cache."""
+    from synth import WORKLOADS, make_use_batch
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating held-out queries of {w.name}: P={w.P} g={w.g} per head {w.F}")
+    u = make_use_batch(w, 0)
+    P, n, d = u["Qh"].shape
+    k = w.k0
+    rng = np.random.default_rng(0)
+    idx = [np.sort(rng.choice(w.Z, size=k, replace=False)) for _ in range(P)]
+    Kc = np.concatenate([u["Kz"][p, idx[p]] for p in range(P)])
+    Vc = np.concatenate([u["Vz"][p, idx[p]] for p in range(P)])
+    g = {key: torch.from_numpy(u[key]).to(dev) for key in ("Qh", "Kz", "Vz", "Kr", "Vr")}
+    Kcg, Vcg = torch.from_numpy(Kc).to(dev), torch.from_numpy(Vc).to(dev)
+    bt = K.Batch(P, d, w.Z, n, k=[k] * P, scale=u["scale"])
+    ws = torch.empty(K.use_eval_workspace_bytes(bt, w.m), dtype=torch.uint8, device=dev)
+    mse = torch.empty(P, dtype=torch.float32, device=dev)
+    rl = torch.empty(P, dtype=torch.float32, device=dev)
+    ctx = K.Context()
+
+    def step():
+        K.kvs_use_eval(ctx, bt, w.m, g["Qh"], g["Kz"], g["Vz"], g["Kr"], g["Vr"], Kcg, Vcg, None,
+                       None, mse, rl, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kvs_profile_enable(ctx, True, kernels=["use_attn_fwd"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = K.kvs_profile_read(ctx)["use_attn_fwd"]
+    K.kvs_profile_enable(ctx, False)
+    avg_s = st["ms"] / st["launches"] / 1e3
+    achieved = st["flops"] / st["launches"] / avg_s
+    peak = mixed_fwd_peak()
+    roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_for("use_attn_fwd"), "kernel": "use_attn_fwd",
+                "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
+    log(f"[bench] use-side rel error per problem: {rl.cpu().numpy()[:8].tolist()} ...")
+    cpu = None if args.no_cpu_baseline else cpu_use(w, u, Kc, Vc, k, min(args.cpu_seconds, 10.0))
+    out = {
+        "metric": "held-out queries evaluated/sec over the full and the compressed cache",
+        "value": round(P * n * args.steps / elapsed, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (scores f64)", "data": "synthetic",
+        "config": {"workload": w.name, "row": "use", "problems": P, "n_heldout": n, "Z": w.Z,
+                   "m": w.m, "k": k, "d": d},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=None,
+                    help="workload (default 1; 2 for --row queries / use)")
     ap.add_argument("--ratio", type=float, default=None, help="compression ratio r (configs 2..4)")
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--row", choices=["compress", "queries"], default="compress",
-                    help="compress: the optimizer (default); queries: training-query construction")
+    ap.add_argument("--row", choices=["compress", "queries", "use"], default="compress",
+                    help="compress: the optimizer (default); queries: training-query "
+                         "construction; use: use-side evaluation")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this size (HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.config is None:
+        args.config = 1 if args.row == "compress" else 2
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the problems of a batch are independent and this build "
             "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
@@ -216,6 +306,9 @@ def main():
     from synth import WORKLOADS, make_batch
     if args.row == "queries":
         bench_queries(args, torch, K)
+        return
+    if args.row == "use":
+        bench_use(args, torch, K)
         return
 
     w = WORKLOADS[args.config]

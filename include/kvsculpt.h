@@ -229,6 +229,28 @@ typedef struct {
 kvs_status kvs_build_queries(kvs_ctx ctx, const kvs_query_geom* q, const float* Qctx,
                              const int32_t* src, float* Q, int32_t* flags);
 
+/* Use-side evaluation (gist page, section 2 "Problem Formulation": the
+ * compressed cache should give the full cache's attention output for future
+ * queries, the retain zone kept as is; "Loss Function": the LSE term keeps
+ * the chunk's attention mass right when it is combined with other tokens).
+ * For held-out queries Qh [P][n][d] (b->n rows per problem, b->k the
+ * compressed sizes):
+ *   Ofull = softmax(scale Qh [Kz; Kr]^T) [Vz; Vr]    (full cache)
+ *   Ocomp = softmax(scale Qh [Kc; Kr]^T) [Vc; Vr]    (compressed cache)
+ *   mse[p] = ||Ocomp - Ofull||_F^2 / (n d),  rel[p] = ||Ocomp - Ofull||_F / ||Ofull||_F
+ * one softmax over each whole cache, no mask.  Kr, Vr [P][m][d] are the
+ * retain zone (m >= 0; may be NULL when m == 0); Kc, Vc packed [sum k][d].
+ * Ofull, Ocomp [P][n][d] are optional outputs (NULL: kept in the
+ * workspace); mse [P] is required, rel [P] optional (device float).  Scores
+ * are formed as for the loss (float64 products), outputs accumulate in
+ * float32, the norms in float64 in a fixed order.  The workspace is
+ * kvs_use_eval_workspace_bytes(b, m) bytes (0: invalid batch or m). */
+size_t kvs_use_eval_workspace_bytes(const kvs_batch* b, int32_t m);
+kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float* Qh,
+                        const float* Kz, const float* Vz, const float* Kr, const float* Vr,
+                        const float* Kc, const float* Vc, float* Ofull, float* Ocomp,
+                        float* mse, float* rel, void* ws, size_t ws_bytes);
+
 /* Opt-in kernel timing, for measurement tools.  While enabled, the library
  * records a HIP event pair on the context stream around each launch of its
  * main kernels and accumulates, per kernel, the launch count, the summed
@@ -237,8 +259,9 @@ kvs_status kvs_build_queries(kvs_ctx ctx, const kvs_query_geom* q, const float* 
  * kvs_profile_enable clears the totals; its argument is 0 (off), -1 (all
  * kernels) or a bitmask over attn_fwd (bit 0), attn_bwd, gram, potrf_panel,
  * trailing, back_subst, hist_dots, direction, importance, ref_attn_fwd,
- * merge, build_queries (bit 11).  kvs_profile_read synchronises the stream
- * and writes up to max entries (kernels with launches) to out. */
+ * merge, build_queries, use_attn_fwd (bit 12).  kvs_profile_read
+ * synchronises the stream and writes up to max entries (kernels with
+ * launches) to out. */
 typedef struct {
   char    name[32];
   int64_t launches;

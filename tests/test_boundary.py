@@ -98,6 +98,35 @@ def test_build_queries_argument_errors(K):
     assert lib.kvs_destroy(ctx) == 0
 
 
+def test_use_eval_workspace_and_argument_errors(K):
+    b = K.Batch(2, 128, 1920, 3072, k=[960, 700])
+    ws = K.use_eval_workspace_bytes(b, 128)
+    # two merged outputs alone are 2 * P * n * d floats; partials add more
+    assert ws > 2 * 2 * 3072 * 128 * 4
+    assert K.use_eval_workspace_bytes(b, -1) == 0
+    assert K.use_eval_workspace_bytes(K.Batch(2, 96, 1920, 3072, k=[960, 700]), 128) == 0
+    lib = K.load()
+    ctx = ctypes.c_void_p()
+    assert lib.kvs_create(ctypes.byref(ctx), None) == 0
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    args = [fake] * 6
+    # retain zone pointers are required when m > 0
+    st = lib.kvs_use_eval(ctx, ctypes.byref(b.c), 128, fake, fake, fake, None, None, fake, fake,
+                          None, None, fake, None, fake, 1 << 40)
+    assert st == -1 and b"Kr" in lib.kvs_last_error(ctx)
+    st = lib.kvs_use_eval(ctx, ctypes.byref(b.c), 0, fake, fake, fake, None, None, fake, fake,
+                          None, None, None, None, fake, 1 << 40)
+    assert st == -1 and b"mse" in lib.kvs_last_error(ctx)
+    st = lib.kvs_use_eval(ctx, ctypes.byref(b.c), 128, fake, fake, fake, fake, fake, fake, fake,
+                          odd, None, fake, None, fake, 1 << 40)
+    assert st == -2
+    st = lib.kvs_use_eval(ctx, ctypes.byref(b.c), 128, *args, fake, None, None, fake, None,
+                          fake, ws - 256)
+    assert st == -3 and b"workspace" in lib.kvs_last_error(ctx)
+    assert lib.kvs_destroy(ctx) == 0
+
+
 def test_allocator_cpp_equals_oracle_bit_for_bit(K):
     rng = np.random.default_rng(20)
     for it in range(10000):
