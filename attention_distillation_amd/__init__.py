@@ -7,7 +7,8 @@ GPU; calling an entry point needs the built library and a GPU.
 """
 from ._lib import (ENTRY_POINTS, KVS_FLAG_BADINDEX, KVS_FLAG_CHOLESKY, KVS_FLAG_LINESEARCH,
                    KVS_FLAG_NONDESCENT, KVS_FLAG_NONFINITE, Batch, Context, KvsBatch, KvsError,
-                   KvsOpts, KvsQueryGeom, kvs_allocate_budget, kvs_build_queries, kvs_compress,
+                   KvsAdamOpts, KvsOpts, KvsQueryGeom, adam_opts, kvs_allocate_budget,
+                   kvs_build_queries, kvs_compress, kvs_compress_adam, kvs_compress_from_keys,
                    kvs_init_topk, kvs_lbfgs_init, kvs_lbfgs_step, kvs_loss_grad,
                    kvs_pilot_allocate, kvs_profile_enable, kvs_profile_read, kvs_reference_attn,
                    kvs_use_eval, kvs_value_solve, lbfgs_state_bytes, load, opts,
@@ -16,7 +17,8 @@ from ._lib import (ENTRY_POINTS, KVS_FLAG_BADINDEX, KVS_FLAG_CHOLESKY, KVS_FLAG_
 __all__ = [
     "ENTRY_POINTS", "KVS_FLAG_BADINDEX", "KVS_FLAG_CHOLESKY", "KVS_FLAG_LINESEARCH",
     "KVS_FLAG_NONDESCENT", "KVS_FLAG_NONFINITE", "Batch", "Context", "KvsBatch", "KvsError",
-    "KvsOpts", "KvsQueryGeom", "kvs_allocate_budget", "kvs_build_queries", "kvs_compress",
+    "KvsAdamOpts", "KvsOpts", "KvsQueryGeom", "adam_opts", "kvs_allocate_budget",
+    "kvs_build_queries", "kvs_compress", "kvs_compress_adam", "kvs_compress_from_keys",
     "kvs_init_topk", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_loss_grad", "kvs_pilot_allocate",
     "kvs_profile_enable", "kvs_profile_read", "kvs_reference_attn", "kvs_use_eval",
     "kvs_value_solve", "lbfgs_state_bytes", "load", "opts", "use_eval_workspace_bytes",

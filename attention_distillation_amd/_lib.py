@@ -26,7 +26,8 @@ ENTRY_POINTS = (
     "kvs_workspace_bytes", "kvs_lbfgs_state_bytes", "kvs_reference_attn", "kvs_init_topk",
     "kvs_loss_grad", "kvs_value_solve", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_compress",
     "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_build_queries", "kvs_use_eval_workspace_bytes",
-    "kvs_use_eval", "kvs_profile_enable", "kvs_profile_read",
+    "kvs_use_eval", "kvs_compress_from_keys", "kvs_default_adam_opts", "kvs_compress_adam",
+    "kvs_profile_enable", "kvs_profile_read",
 )
 
 
@@ -40,6 +41,10 @@ class KvsBatch(ctypes.Structure):
     _fields_ = [("P", c_int32), ("d", c_int32), ("Z", c_int32), ("n", c_int32),
                 ("k", POINTER(c_int32)), ("scale", c_double), ("lambda_", c_double),
                 ("ridge_rel", c_double)]
+
+
+class KvsAdamOpts(ctypes.Structure):
+    _fields_ = [("lr", c_double), ("beta1", c_double), ("beta2", c_double), ("eps", c_double)]
 
 
 class KvsQueryGeom(ctypes.Structure):
@@ -95,6 +100,10 @@ def load(path: str | None = None):
                                           c_int32, POINTER(c_int32)]),
         "kvs_build_queries": (c_int32, [V, POINTER(KvsQueryGeom), V, V, V, V]),
         "kvs_use_eval_workspace_bytes": (c_size_t, [B, c_int32]),
+        "kvs_compress_from_keys": (c_int32, [V, B, O, V, V, V, V, V, V, V, V, V, V, c_size_t]),
+        "kvs_default_adam_opts": (None, [POINTER(KvsAdamOpts)]),
+        "kvs_compress_adam": (c_int32, [V, B, O, POINTER(KvsAdamOpts), c_int32, V, V, V, V, V, V, V,
+                                        V, V, V, c_size_t]),
         "kvs_use_eval": (c_int32, [V, B, c_int32, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t]),
         "kvs_profile_enable": (c_int32, [V, c_int32]),
         "kvs_profile_read": (c_int32, [V, POINTER(KvsKernelStats), c_int32, POINTER(c_int32)]),
@@ -235,6 +244,26 @@ def kvs_compress(ctx, batch, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, 
     ctx.check("kvs_compress", ctx.lib.kvs_compress(
         ctx.handle, ctypes.byref(batch.c), ctypes.byref(o), _ptr(Q), _ptr(Kz), _ptr(Vz), _ptr(Kc),
         _ptr(Vc), _ptr(loss), _ptr(mse), _ptr(init_loss), _ptr(flags), w, nb))
+
+
+def kvs_compress_from_keys(ctx, batch, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, ws):
+    w, nb = _ws(ws)
+    ctx.check("kvs_compress_from_keys", ctx.lib.kvs_compress_from_keys(
+        ctx.handle, ctypes.byref(batch.c), ctypes.byref(o), _ptr(Q), _ptr(Kz), _ptr(Vz), _ptr(Kc),
+        _ptr(Vc), _ptr(loss), _ptr(mse), _ptr(init_loss), _ptr(flags), w, nb))
+
+
+def adam_opts(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8):
+    return KvsAdamOpts(lr, beta1, beta2, eps)
+
+
+def kvs_compress_adam(ctx, batch, o, a, keys_given, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss,
+                      flags, ws):
+    w, nb = _ws(ws)
+    ctx.check("kvs_compress_adam", ctx.lib.kvs_compress_adam(
+        ctx.handle, ctypes.byref(batch.c), ctypes.byref(o), ctypes.byref(a), int(keys_given),
+        _ptr(Q), _ptr(Kz), _ptr(Vz), _ptr(Kc), _ptr(Vc), _ptr(loss), _ptr(mse), _ptr(init_loss),
+        _ptr(flags), w, nb))
 
 
 def kvs_pilot_allocate(ctx, batch, o, pilot_iters, alpha, k_min, k_max, Q, Kz, Vz, pilot_mse, ws):

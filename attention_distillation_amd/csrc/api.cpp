@@ -472,15 +472,30 @@ kvs_status status_buffers(kvs_ctx ctx, int P) {
 // enqueued before the host waits for that copy, so the device keeps working
 // while the host decides (a slot leaves a problem that finished its block
 // untouched, so the last of these slots runs empty).
+// Starting point of a run: Select+Fit, or the caller's keys in Kc with
+// ridge-fitted values.
+void run_init(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Kz,
+              const float* Y, const float* lse, float* Kc, float* Vc, int* flags, LbState* st,
+              bool keys_given, void* ws) {
+  if (!keys_given) {
+    run_init_topk(ctx, pl, b, Q, Kz, Y, lse, at<int>(ws, pl.r_idx), Kc, Vc, flags, st, ws);
+    return;
+  }
+  launch_fill_f32(Vc, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
+  run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws);
+}
+
 kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
                          const float* Q, const float* Kz, const float* Vz, float* Kc, float* Vc,
-                         float* loss, float* mse, float* init_loss, int* flags, void* ws) {
+                         float* loss, float* mse, float* init_loss, int* flags, void* ws,
+                         bool keys_given = false) {
   float* Yr = at<float>(ws, pl.r_yref);
   float* lr = at<float>(ws, pl.r_lseref);
   run_reference(ctx, pl, b, Q, Kz, Vz, Yr, lr, ws);
   LbBuffers B = lb_in_ws(pl, ws);
   launch_state_init(B.st, pl.P, 1, ctx->stream);
-  run_init_topk(ctx, pl, b, Q, Kz, Yr, lr, at<int>(ws, pl.r_idx), Kc, Vc, nullptr, B.st, ws);
+  run_init(ctx, pl, b, Q, Kz, Yr, lr, Kc, Vc, nullptr, B.st, keys_given, ws);
   lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws);
   bool refreshed = true;
   if (kvs_status s = status_buffers(ctx, pl.P); s != KVS_OK) return s;
@@ -534,6 +549,51 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
     run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, kAll, 2, nullptr, mse, o, ws);
   launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
   prof_add_slot_work(ctx, pl, B.st);
+  return KVS_OK;
+}
+
+// The alternating schedule with Adam on the keys: per iteration loss and
+// gradient at the current keys, one Adam step; values re-solved after
+// iterations vc_every, 2 vc_every, ... (moments kept).  The moments live in
+// the history region, which Adam does not otherwise use.
+kvs_status adam_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
+                     const kvs_adam_opts* ad, const float* Q, const float* Kz, const float* Vz,
+                     float* Kc, float* Vc, float* loss, float* mse, float* init_loss, int* flags,
+                     bool keys_given, void* ws) {
+  float* Yr = at<float>(ws, pl.r_yref);
+  float* lr = at<float>(ws, pl.r_lseref);
+  launch_fill_i32(flags, 0, pl.P, ctx->stream);
+  run_reference(ctx, pl, b, Q, Kz, Vz, Yr, lr, ws);
+  run_init(ctx, pl, b, Q, Kz, Yr, lr, Kc, Vc, flags, nullptr, keys_given, ws);
+  float* g = at<float>(ws, pl.r_g);
+  float* m = at<float>(ws, pl.r_S);
+  float* v = at<float>(ws, pl.r_Yh);
+  launch_fill_f32(m, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
+  launch_fill_f32(v, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
+  // loss at the start; its stored scores serve the first gradient
+  run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, init_loss, nullptr, o, ws);
+  AdamArgs aa{};
+  aa.x = Kc; aa.g = g; aa.m = m; aa.v = v; aa.flags = flags; aa.nonfinite_flag = KVS_FLAG_NONFINITE;
+  aa.info = at<ProbInfo>(ws, pl.r_info); aa.P = pl.P; aa.d = pl.d;
+  aa.b1 = (float)ad->beta1; aa.b2 = (float)ad->beta2; aa.eps = (float)ad->eps;
+  double p1 = 1.0, p2 = 1.0;
+  for (int t = 1; t <= o->iters; ++t) {
+    if (t > 1) run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, o, ws);
+    run_backward(ctx, pl, b, Q, Vc, nullptr, 0, ws);
+    GradUpdArgs ga = grad_args(pl, b, ws, nullptr, 0, 2);
+    ga.gout = g;
+    launch_grad_update(ga, ctx->stream);
+    p1 *= ad->beta1;
+    p2 *= ad->beta2;
+    aa.step = (float)(ad->lr / (1.0 - p1));
+    aa.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - p2));
+    launch_adam(aa, pl.kmax, ctx->stream);
+    if (t % o->vc_every == 0) {
+      run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, o, ws);
+      run_value_solve(ctx, pl, b, Yr, Vc, flags, nullptr, kAllStates, ws);
+    }
+  }
+  run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, loss, mse, o, ws);
   return KVS_OK;
 }
 
@@ -726,6 +786,53 @@ kvs_status kvs_compress(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, cons
   kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
   s = compress_impl(ctx, pl, b, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, ws);
+  if (s != KVS_OK) return s;
+  return hip_check(ctx, fn);
+}
+
+kvs_status kvs_compress_from_keys(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o,
+                                  const float* Q, const float* Kz, const float* Vz, float* Kc,
+                                  float* Vc, float* loss, float* mse, float* init_loss,
+                                  int32_t* flags, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_compress_from_keys";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(Kc); KVS_NEED(Vc); KVS_NEED(loss);
+  KVS_OPT(mse); KVS_OPT(init_loss); KVS_OPT(flags);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  s = compress_impl(ctx, pl, b, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, ws, true);
+  if (s != KVS_OK) return s;
+  return hip_check(ctx, fn);
+}
+
+void kvs_default_adam_opts(kvs_adam_opts* a) {
+  if (!a) return;
+  a->lr = 1e-2;
+  a->beta1 = 0.9;
+  a->beta2 = 0.999;
+  a->eps = 1e-8;
+}
+
+kvs_status kvs_compress_adam(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o,
+                             const kvs_adam_opts* a, int32_t keys_given, const float* Q,
+                             const float* Kz, const float* Vz, float* Kc, float* Vc, float* loss,
+                             float* mse, float* init_loss, int32_t* flags, void* ws,
+                             size_t ws_bytes) {
+  const char* fn = "kvs_compress_adam";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  if (!a) return fail(ctx, KVS_ERR_INVALID, "%s: adam opts is NULL", fn);
+  if (!(a->lr > 0.0) || !(a->beta1 >= 0.0 && a->beta1 < 1.0) || !(a->beta2 >= 0.0 && a->beta2 < 1.0) ||
+      !(a->eps > 0.0))
+    return fail(ctx, KVS_ERR_INVALID, "%s: adam needs lr > 0, beta1 and beta2 in [0, 1), eps > 0", fn);
+  KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(Kc); KVS_NEED(Vc); KVS_NEED(loss);
+  KVS_NEED(flags); KVS_OPT(mse); KVS_OPT(init_loss);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  s = adam_impl(ctx, pl, b, o, a, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, keys_given != 0, ws);
   if (s != KVS_OK) return s;
   return hip_check(ctx, fn);
 }

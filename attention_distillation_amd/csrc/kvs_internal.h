@@ -262,6 +262,17 @@ struct UseErrArgs {
 int use_err_blocks(int n);
 void launch_use_err(const UseErrArgs& a, hipStream_t s);
 
+// One Adam step on the packed keys of every problem.
+struct AdamArgs {
+  float* x; const float* g; float* m; float* v;
+  int* flags; int nonfinite_flag;     // flags [P] or NULL
+  const ProbInfo* info; int P, d;
+  float b1, b2, eps;
+  float step;           // lr / (1 - b1^t)
+  float inv_sqrt_bc2;   // 1 / sqrt(1 - b2^t)
+};
+void launch_adam(const AdamArgs& a, int kmax, hipStream_t s);
+
 void launch_write_info(ProbInfo* dst, const ProbInfo* src, int P, hipStream_t s);
 void launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 void launch_fill_f32(float* p, float v, long long n, hipStream_t s);

@@ -174,6 +174,44 @@ kvs_status kvs_compress(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, cons
                         const float* Kz, const float* Vz, float* Kc, float* Vc, float* loss,
                         float* mse, float* init_loss, int32_t* flags, void* ws, size_t ws_bytes);
 
+/* kvs_compress from the caller's starting keys: Kc holds them on entry
+ * (packed [sum k][d]) and the result on return; the values start as the
+ * ridge fit at those keys instead of the Select+Fit choice.  Everything else
+ * as kvs_compress.  It serves the comparison with a search over random
+ * restarts (gist page, section 4 "Optimizer Efficacy": a single L-BFGS run
+ * against the best of 100 restarts): a restart is one more problem of the
+ * batch whose starting keys are the caller's random draw. */
+kvs_status kvs_compress_from_keys(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o,
+                                  const float* Q, const float* Kz, const float* Vz, float* Kc,
+                                  float* Vc, float* loss, float* mse, float* init_loss,
+                                  int32_t* flags, void* ws, size_t ws_bytes);
+
+/* The schedule with Adam in place of L-BFGS on the keys (gist page, section 4
+ * "Optimizer Efficacy": the ablation that replaces L-BFGS by Adam; section 2
+ * "Optimization Strategy": first-order methods get trapped).  Per iteration
+ * t = 1..iters: loss and gradient at (Kc, Vc), then the Adam step (Kingma &
+ * Ba 2015, Algorithm 1) m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2,
+ * Kc -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps), in float32; values
+ * re-solved after iterations vc_every, 2 vc_every, ... with the moments
+ * kept.  The start is Select+Fit (keys_given = 0) or the caller's keys in Kc
+ * with ridge values (keys_given != 0).  history, max_backtracks, c1 and
+ * shrink of o are validated but unused.  flags [P] (required) is cleared,
+ * then gets KVS_FLAG_NONFINITE for a non-finite gradient element (left
+ * unchanged) and KVS_FLAG_CHOLESKY for a failed value solve.  Outputs as for
+ * kvs_compress. */
+typedef struct {
+  double lr;      /* step size (1e-2)   */
+  double beta1;   /* 0.9                */
+  double beta2;   /* 0.999              */
+  double eps;     /* 1e-8               */
+} kvs_adam_opts;
+void kvs_default_adam_opts(kvs_adam_opts* a);
+kvs_status kvs_compress_adam(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o,
+                             const kvs_adam_opts* a, int32_t keys_given, const float* Q,
+                             const float* Kz, const float* Vz, float* Kc, float* Vc, float* loss,
+                             float* mse, float* init_loss, int32_t* flags, void* ws,
+                             size_t ws_bytes);
+
 /* Pilot run and budget (gist page, "Adaptive Budget Allocation"): kvs_compress
  * at the batch's uniform k for pilot_iters iterations (60), per-problem output
  * MSE into pilot_mse [P] (device float), then kvs_allocate_budget with
