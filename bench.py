@@ -17,7 +17,12 @@ step just before the optimizer); the metric is training queries built per
 second.  With --row use it is one kvs_use_eval call: held-out future
 queries over the full and the compressed cache (the step just after the
 optimizer); the metric is held-out queries evaluated per second.  Both
-default to the 56-problem full-cache workload (--config 2).
+default to the 56-problem full-cache workload (--config 2).  --row adam runs
+the schedule with Adam on the keys and reports its final output MSE over
+L-BFGS's; --row restarts runs R random restarts of one problem as one batch
+(kvs_compress_from_keys) and reports the single Select+Fit run's final loss
+over the best restart's.  The ablation rows carry no CPU baseline (the
+oracle of the whole schedule is timed by the default row).
 
 Printed: one JSON line (stdout).  It carries the live roofline of the
 dominant kernel (HIP events on the library's stream over the timed steps)
@@ -274,6 +279,137 @@ def bench_use(args, torch, K):
     print(json.dumps(out), flush=True)
 
 
+def _fwd_roofline(stats):
+    st = stats["attn_fwd"]
+    avg_s = st["ms"] / st["launches"] / 1e3
+    achieved = st["flops"] / st["launches"] / avg_s
+    peak = mixed_fwd_peak()
+    return {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_for("attn_fwd"),
+            "kernel": "attn_fwd", "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
+
+
+def bench_adam(args, torch, K):
+    """The schedule with Adam on the keys, and its final MSE against L-BFGS's."""
+    from synth import WORKLOADS, make_batch
+    w = WORKLOADS[args.config]
+    T = w.T if args.iters is None else args.iters
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}: P={w.P} n={w.n} Z={w.Z} k={w.k0} T={T}")
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Q, Kz, Vz = (torch.from_numpy(b[key]).to(dev) for key in ("Q", "Kz", "Vz"))
+    bt = K.Batch(P, d, w.Z, n, k=[w.k0] * P, scale=b["scale"])
+    o = K.opts(iters=T)
+    a = K.adam_opts(lr=args.adam_lr)
+    ws = torch.empty(K.workspace_bytes(bt, o), dtype=torch.uint8, device=dev)
+    Kc = torch.empty((w.k0 * P, d), dtype=torch.float32, device=dev)
+    Vc = torch.empty_like(Kc)
+    loss, mse, l0 = (torch.empty(P, dtype=torch.float32, device=dev) for _ in range(3))
+    flags = torch.zeros(P, dtype=torch.int32, device=dev)
+    ctx = K.Context()
+
+    def step():
+        K.kvs_compress_adam(ctx, bt, o, a, 0, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kvs_profile_enable(ctx, True, kernels=["attn_fwd"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = K.kvs_profile_read(ctx)
+    K.kvs_profile_enable(ctx, False)
+    mse_adam, fl = mse.cpu().numpy().copy(), flags.cpu().numpy().copy()
+    K.kvs_compress(ctx, bt, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, ws)
+    mse_lb = mse.cpu().numpy().copy()
+    ratio = [float(x) for x in mse_adam / mse_lb]
+    log(f"[bench] final output MSE Adam {mse_adam.tolist()} L-BFGS {mse_lb.tolist()} flags {fl.tolist()}")
+    out = {
+        "metric": "Adam-on-keys schedule: problem-iterations/sec (ablation of L-BFGS)",
+        "value": round(P * T * args.steps / elapsed, 2), "unit": "problem-iterations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "row": "adam", "problems": P, "n": n, "Z": w.Z,
+                   "k": w.k0, "iters": T, "vc_every": 5, "lr": args.adam_lr,
+                   "mse_adam_over_lbfgs": [round(r, 3) for r in ratio]},
+        "roofline": _fwd_roofline(stats),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_restarts(args, torch, K):
+    """A search over random restarts of one problem, batched, against one run."""
+    from synth import WORKLOADS, make_batch
+    w = WORKLOADS[args.config]
+    T = w.T if args.iters is None else args.iters
+    R = args.restarts
+    dev = torch.device("cuda:0")
+    b = make_batch(w, 0, problems=[0])
+    _, n, d = b["Q"].shape
+    log(f"[bench] {R} restarts of {w.name} problem 0: n={n} Z={w.Z} k={w.k0} T={T}")
+    rng = np.random.default_rng(0)
+    draws = [np.sort(rng.choice(w.Z, w.k0, replace=False)) for _ in range(R)]
+    Kc0 = np.concatenate([b["Kz"][0][ix] for ix in draws])
+    rep = {key: torch.from_numpy(b[key]).to(dev).expand(R, -1, -1).contiguous()
+           for key in ("Q", "Kz", "Vz")}
+    bt = K.Batch(R, d, w.Z, n, k=[w.k0] * R, scale=b["scale"])
+    o = K.opts(iters=T)
+    ws = torch.empty(K.workspace_bytes(bt, o), dtype=torch.uint8, device=dev)
+    Kc0g = torch.from_numpy(Kc0).to(dev)
+    Kc = torch.empty_like(Kc0g)
+    Vc = torch.empty_like(Kc0g)
+    loss, mse, l0 = (torch.empty(R, dtype=torch.float32, device=dev) for _ in range(3))
+    flags = torch.zeros(R, dtype=torch.int32, device=dev)
+    ctx = K.Context()
+
+    def step():
+        Kc.copy_(Kc0g)
+        K.kvs_compress_from_keys(ctx, bt, o, rep["Q"], rep["Kz"], rep["Vz"], Kc, Vc, loss, mse, l0,
+                                 flags, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kvs_profile_enable(ctx, True, kernels=["attn_fwd"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = K.kvs_profile_read(ctx)
+    K.kvs_profile_enable(ctx, False)
+    lr_ = loss.cpu().numpy().copy()
+    # the single Select+Fit run of the same problem
+    b1 = K.Batch(1, d, w.Z, n, k=[w.k0], scale=b["scale"])
+    K.kvs_compress(ctx, b1, o, rep["Q"][:1], rep["Kz"][:1], rep["Vz"][:1], Kc[:w.k0], Vc[:w.k0],
+                   loss[:1], mse[:1], l0[:1], flags[:1], ws)
+    single = float(loss[:1].cpu().numpy()[0])
+    best = float(lr_.min())
+    log(f"[bench] restart losses min {best:.6g} median {float(np.median(lr_)):.6g} "
+        f"max {float(lr_.max()):.6g}; single Select+Fit run {single:.6g}")
+    out = {
+        "metric": "random-restart search: problem-iterations/sec over R restarts batched",
+        "value": round(R * T * args.steps / elapsed, 2), "unit": "problem-iterations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "row": "restarts", "problem": 0, "restarts": R, "n": n,
+                   "Z": w.Z, "k": w.k0, "iters": T,
+                   "single_run_over_best_restart": round(single / best, 4)},
+        "roofline": _fwd_roofline(stats),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,14 +421,18 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--row", choices=["compress", "queries", "use"], default="compress",
+    ap.add_argument("--row", choices=["compress", "queries", "use", "adam", "restarts"],
+                    default="compress",
                     help="compress: the optimizer (default); queries: training-query "
-                         "construction; use: use-side evaluation")
+                         "construction; use: use-side evaluation; adam / restarts: the "
+                         "optimizer ablations")
+    ap.add_argument("--adam-lr", type=float, default=1e-2)
+    ap.add_argument("--restarts", type=int, default=100)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this size (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.config is None:
-        args.config = 1 if args.row == "compress" else 2
+        args.config = 2 if args.row in ("queries", "use") else 1
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the problems of a batch are independent and this build "
             "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
@@ -309,6 +449,12 @@ def main():
         return
     if args.row == "use":
         bench_use(args, torch, K)
+        return
+    if args.row == "adam":
+        bench_adam(args, torch, K)
+        return
+    if args.row == "restarts":
+        bench_restarts(args, torch, K)
         return
 
     w = WORKLOADS[args.config]
