@@ -38,6 +38,9 @@ exact merge of duplicate keys, degenerate caches.  Optimizer ablations
 (tests/test_oracle_ablations.py): the Adam update against torch.optim.Adam
 and a constant-gradient closed form, the Adam schedule without value solves
 against torch.optim.Adam on the loss, restarts against the Select+Fit run.
+Allocation variants (tests/test_oracle_alloc_variants.py): two-level split
+by hand and by its reductions to the flat split; value-norm signal by hand
+and invariances.
 """
 from __future__ import annotations
 
@@ -481,6 +484,46 @@ def allocate_budget(mse: Sequence[float], K_total: int, alpha: float = 0.5,
             k[p] += 1
             left -= 1
     return k
+
+
+def allocate_budget_two_level(mse: Sequence[float], layers: int, heads: int, K_total: int,
+                              alpha: float = 0.5, k_min: int = 1, k_max: int = 1 << 30) -> List[int]:
+    """Two-level split: layers first, then the heads of each layer.
+
+    [gist] "Adaptive Budget Allocation": allocation is done at both the layer
+    and the KV-head level.  Reading: problem p = layer * heads + head; a
+    layer's signal is the mean of its heads' MSE (the MSE of the layer's
+    concatenated head outputs), summed in head order and divided by
+    ``heads``; the layer budgets split K_total by :func:`allocate_budget`
+    with bounds [heads * k_min, min(heads * k_max, K_total)]; each layer's
+    budget is then split over its heads by :func:`allocate_budget` on the
+    heads' own MSE.  Same exponent alpha at both levels.
+    """
+    if layers < 1 or heads < 1 or len(mse) != layers * heads:
+        raise ValueError("mse must hold layers * heads entries")
+    lmse = []
+    for l in range(layers):
+        acc = 0.0
+        for h in range(heads):
+            acc += float(mse[l * heads + h])
+        lmse.append(acc / heads)
+    lmax = min(heads * k_max, K_total)
+    if lmax > (1 << 31) - 1:
+        raise ValueError("per-layer bound too large")
+    kl = allocate_budget(lmse, K_total, alpha, heads * k_min, lmax)
+    out = []
+    for l in range(layers):
+        out += allocate_budget(mse[l * heads:(l + 1) * heads], kl[l], alpha, k_min, k_max)
+    return out
+
+
+def value_norm_signal(Vz):
+    """Static allocation signal: the mean Euclidean norm of the compress
+    zone's value rows.  [gist] "Adaptive Budget Allocation" contrasts pilot
+    MSE with static signals "like value norms"; reading: this per-problem
+    mean, used as the allocation weight in place of the pilot MSE."""
+    V = _f64(Vz)
+    return float(np.mean(np.sqrt(np.sum(V * V, axis=1))))
 
 
 def pilot_allocate(problems, k0, scale, opt: CompressOptions, pilot_iters=60,
