@@ -27,6 +27,7 @@ ENTRY_POINTS = (
     "kvs_loss_grad", "kvs_value_solve", "kvs_lbfgs_init", "kvs_lbfgs_step", "kvs_compress",
     "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_build_queries", "kvs_use_eval_workspace_bytes",
     "kvs_use_eval", "kvs_compress_from_keys", "kvs_default_adam_opts", "kvs_compress_adam",
+    "kvs_allocate_budget_two_level", "kvs_value_norms_workspace_bytes", "kvs_value_norms",
     "kvs_profile_enable", "kvs_profile_read",
 )
 
@@ -100,6 +101,10 @@ def load(path: str | None = None):
                                           c_int32, POINTER(c_int32)]),
         "kvs_build_queries": (c_int32, [V, POINTER(KvsQueryGeom), V, V, V, V]),
         "kvs_use_eval_workspace_bytes": (c_size_t, [B, c_int32]),
+        "kvs_allocate_budget_two_level": (c_int32, [POINTER(c_double), c_int32, c_int32, c_int64,
+                                                    c_double, c_int32, c_int32, POINTER(c_int32)]),
+        "kvs_value_norms_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+        "kvs_value_norms": (c_int32, [V, c_int32, c_int32, c_int32, V, V, V, c_size_t]),
         "kvs_compress_from_keys": (c_int32, [V, B, O, V, V, V, V, V, V, V, V, V, V, c_size_t]),
         "kvs_default_adam_opts": (None, [POINTER(KvsAdamOpts)]),
         "kvs_compress_adam": (c_int32, [V, B, O, POINTER(KvsAdamOpts), c_int32, V, V, V, V, V, V, V,
@@ -304,6 +309,28 @@ def kvs_use_eval(ctx, batch, m, Qh, Kz, Vz, Kr, Vr, Kc, Vc, Ofull, Ocomp, mse, r
     ctx.check("kvs_use_eval", ctx.lib.kvs_use_eval(
         ctx.handle, ctypes.byref(batch.c), int(m), _ptr(Qh), _ptr(Kz), _ptr(Vz), _ptr(Kr),
         _ptr(Vr), _ptr(Kc), _ptr(Vc), _ptr(Ofull), _ptr(Ocomp), _ptr(mse), _ptr(rel), w, nb))
+
+
+def kvs_allocate_budget_two_level(mse, layers, heads, K_total, alpha=0.5, k_min=1, k_max=1 << 30):
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(mse, dtype=np.float64))
+    out = np.zeros(m.size, dtype=np.int32)
+    st = load().kvs_allocate_budget_two_level(m.ctypes.data_as(POINTER(c_double)), int(layers),
+                                              int(heads), int(K_total), float(alpha), int(k_min),
+                                              int(k_max), out.ctypes.data_as(POINTER(c_int32)))
+    if st != 0:
+        raise KvsError("kvs_allocate_budget_two_level", st, "invalid budget request")
+    return out
+
+
+def value_norms_workspace_bytes(P, Z):
+    return load().kvs_value_norms_workspace_bytes(int(P), int(Z))
+
+
+def kvs_value_norms(ctx, P, Z, d, Vz, signal, ws):
+    w, nb = _ws(ws)
+    ctx.check("kvs_value_norms", ctx.lib.kvs_value_norms(ctx.handle, int(P), int(Z), int(d),
+                                                         _ptr(Vz), _ptr(signal), w, nb))
 
 
 PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",

@@ -6,6 +6,7 @@
 // multiply-add is fused: every sum runs over problems in increasing order and
 // every share is (R * w) / S, which makes the result reproducible bit for bit
 // by any implementation that performs the same operations.
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -99,4 +100,39 @@ extern "C" kvs_status kvs_allocate_budget(const double* mse, int32_t P, int64_t 
     }
   }
   return left == 0 ? KVS_OK : KVS_ERR_INVALID;
+}
+
+// Two-level split (the same page and section: allocation at the layer and
+// the KV-head level): layer signal = mean of its heads' MSE (summed in head
+// order, divided by the head count), layer budgets by the flat split with
+// bounds [heads k_min, min(heads k_max, K_total)], then each layer's budget
+// over its heads by the flat split on their own MSE.
+extern "C" kvs_status kvs_allocate_budget_two_level(const double* mse, int32_t layers,
+                                                    int32_t heads, int64_t K_total, double alpha,
+                                                    int32_t k_min, int32_t k_max, int32_t* k_out) {
+  if (!mse || !k_out || layers < 1 || heads < 1 || k_min < 1 || k_min > k_max) return KVS_ERR_INVALID;
+  const int64_t P = (int64_t)layers * heads;
+  if (P > 0x7fffffff || K_total < P * k_min || K_total > P * k_max) return KVS_ERR_INVALID;
+  const int64_t lmax = std::min<int64_t>((int64_t)heads * k_max, K_total);
+  if (lmax > 0x7fffffff || (int64_t)heads * k_min > 0x7fffffff) return KVS_ERR_INVALID;
+  std::vector<double> lmse(layers);
+  for (int l = 0; l < layers; ++l) {
+    double acc = 0.0;
+    for (int h = 0; h < heads; ++h) {
+      const double v = mse[(int64_t)l * heads + h];
+      if (!(v >= 0.0) || std::isinf(v)) return KVS_ERR_INVALID;
+      acc += v;
+    }
+    lmse[l] = acc / (double)heads;
+  }
+  std::vector<int32_t> kl(layers);
+  kvs_status s = kvs_allocate_budget(lmse.data(), layers, K_total, alpha, heads * k_min, (int32_t)lmax,
+                                     kl.data());
+  if (s != KVS_OK) return s;
+  for (int l = 0; l < layers; ++l) {
+    s = kvs_allocate_budget(mse + (int64_t)l * heads, heads, kl[l], alpha, k_min, k_max,
+                            k_out + (int64_t)l * heads);
+    if (s != KVS_OK) return s;
+  }
+  return KVS_OK;
 }

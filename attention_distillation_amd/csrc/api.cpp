@@ -984,6 +984,34 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
   return hip_check(ctx, fn);
 }
 
+size_t kvs_value_norms_workspace_bytes(int32_t P, int32_t Z) {
+  if (P < 1 || Z < 1) return 0;
+  const size_t b = (size_t)P * value_norm_chunks(P, Z) * sizeof(double);
+  return (b + 255) & ~(size_t)255;
+}
+
+kvs_status kvs_value_norms(kvs_ctx ctx, int32_t P, int32_t Z, int32_t d, const float* Vz,
+                           double* signal, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_value_norms";
+  if (!ctx) return KVS_ERR_INVALID;
+  ctx->err.clear();
+  if (P < 1 || Z < 1 || (d != 64 && d != 128))
+    return fail(ctx, KVS_ERR_INVALID, "%s: bad sizes P=%d Z=%d d=%d", fn, P, Z, d);
+  KVS_NEED(Vz);
+  if (!signal) return fail(ctx, KVS_ERR_INVALID, "%s: argument 'signal' is NULL", fn);
+  if (!aligned(signal, 8)) return fail(ctx, KVS_ERR_ALIGN, "%s: 'signal' not 8-byte aligned", fn);
+  if (!ws) return fail(ctx, KVS_ERR_INVALID, "%s: workspace is NULL", fn);
+  if (!aligned(ws, 256)) return fail(ctx, KVS_ERR_ALIGN, "%s: workspace not 256-byte aligned", fn);
+  const size_t need = kvs_value_norms_workspace_bytes(P, Z);
+  if (ws_bytes < need)
+    return fail(ctx, KVS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
+  VnormArgs a{};
+  a.V = Vz; a.part = static_cast<double*>(ws); a.out = signal; a.P = P; a.Z = Z;
+  a.C = value_norm_chunks(P, Z);
+  launch_value_norms(a, d, ctx->stream);
+  return hip_check(ctx, fn);
+}
+
 kvs_status kvs_profile_enable(kvs_ctx ctx, int32_t enable) {
   if (!ctx) return KVS_ERR_INVALID;
   if (hipStreamSynchronize(ctx->stream) != hipSuccess)

@@ -273,6 +273,16 @@ struct AdamArgs {
 };
 void launch_adam(const AdamArgs& a, int kmax, hipStream_t s);
 
+// Mean value-row norm per problem: chunk partials, then the per-problem sum.
+struct VnormArgs {
+  const float* V;          // [P][Z][d]
+  double* part;            // [P][C]
+  double* out;             // [P]
+  int P, Z, C;
+};
+int value_norm_chunks(int P, int Z);
+void launch_value_norms(const VnormArgs& a, int d, hipStream_t s);
+
 void launch_write_info(ProbInfo* dst, const ProbInfo* src, int P, hipStream_t s);
 void launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 void launch_fill_f32(float* p, float v, long long n, hipStream_t s);

@@ -22,7 +22,10 @@ the schedule with Adam on the keys and reports its final output MSE over
 L-BFGS's; --row restarts runs R random restarts of one problem as one batch
 (kvs_compress_from_keys) and reports the single Select+Fit run's final loss
 over the best restart's.  The ablation rows carry no CPU baseline (the
-oracle of the whole schedule is timed by the default row).
+oracle of the whole schedule is timed by the default row).  --row alloc
+times the value-norm signal kernel on a llama3-8b-shaped zone and compares
+the main run's final MSE under uniform, pilot (flat, two-level, alpha 1)
+and value-norm allocations of the same total budget.
 
 Printed: one JSON line (stdout).  It carries the live roofline of the
 dominant kernel (HIP events on the library's stream over the timed steps)
@@ -410,6 +413,97 @@ def bench_restarts(args, torch, K):
     print(json.dumps(out), flush=True)
 
 
+def bench_alloc(args, torch, K):
+    """Allocation variants: the value-norm signal kernel timed on a large zone,
+    then the main run's final output MSE under each allocation of the budget."""
+    from synth import WORKLOADS, make_batch
+    dev = torch.device("cuda:0")
+    # timed: the static signal over a llama3-8b-shaped compress zone, N(0, 1)
+    # values (the generator's value distribution) drawn on the device
+    w3 = WORKLOADS[3]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    V = torch.randn((w3.P, w3.Z, w3.d), generator=gen, device=dev, dtype=torch.float32)
+    sig = torch.empty(w3.P, dtype=torch.float64, device=dev)
+    ws = torch.empty(K.value_norms_workspace_bytes(w3.P, w3.Z), dtype=torch.uint8, device=dev)
+    ctx = K.Context()
+    for _ in range(args.warmup):
+        K.kvs_value_norms(ctx, w3.P, w3.Z, w3.d, V, sig, ws)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(args.steps, 10)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(reps):
+        K.kvs_value_norms(ctx, w3.P, w3.Z, w3.d, V, sig, ws)
+    e1.record(st)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg_s = e0.elapsed_time(e1) / reps / 1e3
+    nbytes = float(w3.P) * w3.Z * w3.d * 4
+    roofline = {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(nbytes / avg_s / PEAK_HBM, 4),
+                "traffic": traffic_for("value_norms"), "kernel": "value_norms (+ final sum)",
+                "launches": reps, "avg_us": round(avg_s * 1e6, 2)}
+    del V
+    # quality: pilot at uniform k, then the main run under each allocation
+    w = WORKLOADS[args.config]
+    T = w.T if args.iters is None else args.iters
+    log(f"[bench] generating {w.name}: P={w.P} layers={w.layers} heads={w.kv_heads}")
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Q, Kz, Vz = (torch.from_numpy(b[key]).to(dev) for key in ("Q", "Kz", "Vz"))
+    K_total = w.k0 * P
+    bt0 = K.Batch(P, d, w.Z, n, k=[w.k0] * P, scale=b["scale"])
+    pm = torch.empty(P, dtype=torch.float32, device=dev)
+    o = K.opts(iters=T)
+    need = max(K.workspace_bytes(K.Batch(P, d, w.Z, n, k=[w.Z] * P, scale=b["scale"]), o), 256)
+    wsm = torch.empty(need, dtype=torch.uint8, device=dev)
+    K.kvs_pilot_allocate(ctx, bt0, K.opts(iters=w.pilot or 60), w.pilot or 60, 0.5, 1, w.Z, Q, Kz,
+                         Vz, pm, wsm)
+    pilot = pm.cpu().numpy().astype(np.float64)
+    wsn = torch.empty(K.value_norms_workspace_bytes(P, w.Z), dtype=torch.uint8, device=dev)
+    vsig = torch.empty(P, dtype=torch.float64, device=dev)
+    K.kvs_value_norms(ctx, P, w.Z, d, Vz, vsig, wsn)
+    allocs = {
+        "uniform": np.full(P, w.k0, dtype=np.int32),
+        "pilot_sqrt_flat": K.kvs_allocate_budget(pilot, K_total, 0.5, 1, w.Z),
+        "pilot_sqrt_two_level": K.kvs_allocate_budget_two_level(pilot, w.layers, w.kv_heads,
+                                                                K_total, 0.5, 1, w.Z),
+        "pilot_mse_flat_alpha1": K.kvs_allocate_budget(pilot, K_total, 1.0, 1, w.Z),
+        "value_norm_static": K.kvs_allocate_budget(vsig.cpu().numpy(), K_total, 1.0, 1, w.Z),
+    }
+    quality = {}
+    for name, ks in allocs.items():
+        bt = K.Batch(P, d, w.Z, n, k=ks, scale=b["scale"])
+        Kc = torch.empty((int(ks.sum()), d), dtype=torch.float32, device=dev)
+        Vc = torch.empty_like(Kc)
+        loss, mse, l0 = (torch.empty(P, dtype=torch.float32, device=dev) for _ in range(3))
+        flags = torch.zeros(P, dtype=torch.int32, device=dev)
+        K.kvs_compress(ctx, bt, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, wsm)
+        m = mse.cpu().numpy().astype(np.float64)
+        quality[name] = {"mean_mse": float(m.mean()), "max_mse": float(m.max()),
+                         "k_min": int(ks.min()), "k_max": int(ks.max())}
+        log(f"[bench] {name:22s} mean final MSE {m.mean():.4e} max {m.max():.4e} "
+            f"k in [{ks.min()}, {ks.max()}]")
+    base = quality["uniform"]["mean_mse"]
+    out = {
+        "metric": "value-norm allocation signal: zone rows reduced/sec (HBM); allocation variants' final MSE",
+        "value": round(w3.P * w3.Z * reps / elapsed, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": reps, "warmup": args.warmup, "ms_per_step": round(1e3 * elapsed / reps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32 (sums f64)",
+        "data": "synthetic",
+        "config": {"workload": f"signal: {w3.name} zone ({w3.P} x {w3.Z} x {w3.d}); quality: {w.name}",
+                   "row": "alloc", "iters": T,
+                   "mean_mse_over_uniform": {k: round(v["mean_mse"] / base, 4) for k, v in quality.items()},
+                   "quality": quality},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,18 +515,18 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--row", choices=["compress", "queries", "use", "adam", "restarts"],
+    ap.add_argument("--row", choices=["compress", "queries", "use", "adam", "restarts", "alloc"],
                     default="compress",
                     help="compress: the optimizer (default); queries: training-query "
                          "construction; use: use-side evaluation; adam / restarts: the "
-                         "optimizer ablations")
+                         "optimizer ablations; alloc: allocation variants")
     ap.add_argument("--adam-lr", type=float, default=1e-2)
     ap.add_argument("--restarts", type=int, default=100)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run plain device copies of this size (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.config is None:
-        args.config = 2 if args.row in ("queries", "use") else 1
+        args.config = 2 if args.row in ("queries", "use", "alloc") else 1
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the problems of a batch are independent and this build "
             "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
@@ -455,6 +549,9 @@ def main():
         return
     if args.row == "restarts":
         bench_restarts(args, torch, K)
+        return
+    if args.row == "alloc":
+        bench_alloc(args, torch, K)
         return
 
     w = WORKLOADS[args.config]

@@ -235,6 +235,31 @@ kvs_status kvs_pilot_allocate(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o
 kvs_status kvs_allocate_budget(const double* mse, int32_t P, int64_t K_total, double alpha,
                                int32_t k_min, int32_t k_max, int32_t* k_out);
 
+/* Two-level budget split (gist page, "Adaptive Budget Allocation":
+ * allocation is performed at the layer and the KV-head level), pure host,
+ * IEEE double, bit-reproducible like kvs_allocate_budget.  Problem
+ * p = layer * heads + head.  A layer's signal is the mean of its heads' mse
+ * (summed in head order, divided by heads); the layer budgets split K_total
+ * by kvs_allocate_budget with bounds [heads k_min, min(heads k_max,
+ * K_total)], then each layer's budget is split over its heads by
+ * kvs_allocate_budget on their own mse, same alpha at both levels.  mse and
+ * k_out are HOST arrays of layers * heads entries.  Errors as for
+ * kvs_allocate_budget, and KVS_ERR_INVALID if a per-layer bound exceeds
+ * INT32_MAX. */
+kvs_status kvs_allocate_budget_two_level(const double* mse, int32_t layers, int32_t heads,
+                                         int64_t K_total, double alpha, int32_t k_min,
+                                         int32_t k_max, int32_t* k_out);
+
+/* Static allocation signal (gist page, section 4 "Budget Allocation": static
+ * signals such as value norms, compared with the pilot MSE): signal[p] = mean
+ * over the Z rows of Vz [P][Z][d] of their Euclidean norm, accumulated in
+ * float64 in a fixed order.  signal is DEVICE double[P]; the workspace holds
+ * kvs_value_norms_workspace_bytes(P, Z) bytes (256-byte aligned).  Feeding
+ * signal to kvs_allocate_budget with alpha = 1 gives the static allocation. */
+size_t kvs_value_norms_workspace_bytes(int32_t P, int32_t Z);
+kvs_status kvs_value_norms(kvs_ctx ctx, int32_t P, int32_t Z, int32_t d, const float* Vz,
+                           double* signal, void* ws, size_t ws_bytes);
+
 /* Training queries (gist page, section 2 "Training Query Construction": real
  * queries of the recent context plus synthetic future queries whose content
  * is taken from the context by undoing RoPE and embedded again at future

@@ -144,6 +144,26 @@ def test_allocator_cpp_equals_oracle_bit_for_bit(K):
         assert got.tolist() == want, (it, P, kmin, kmax, K_total)
 
 
+def test_two_level_allocator_cpp_equals_oracle_bit_for_bit(K):
+    rng = np.random.default_rng(21)
+    for it in range(3000):
+        L, H = int(rng.integers(1, 33)), int(rng.integers(1, 9))
+        P = L * H
+        mse = np.exp(rng.normal(0, 3, size=P)) * rng.choice([1e-6, 1.0, 1e3])
+        if it % 5 == 0:
+            mse[rng.integers(0, P)] = 0.0
+        kmax = int(rng.integers(1, 4000))
+        kmin = int(rng.integers(1, kmax + 1))
+        K_total = int(rng.integers(P * kmin, P * kmax + 1))
+        alpha = [0.5, 1.0, 0.75][it % 3]
+        want = O.allocate_budget_two_level(list(mse), L, H, K_total, alpha, kmin, kmax)
+        got = K.kvs_allocate_budget_two_level(mse, L, H, K_total, alpha, kmin, kmax)
+        assert got.tolist() == want, (it, L, H, kmin, kmax, K_total)
+    with pytest.raises(K.KvsError):
+        K.kvs_allocate_budget_two_level([1.0, 2.0, 3.0, 4.0], 2, 2, 100, 0.5, 1, 4)
+    assert K.value_norms_workspace_bytes(0, 10) == 0 and K.value_norms_workspace_bytes(4, 100) >= 32
+
+
 def test_allocator_rejects_bad_requests(K):
     with pytest.raises(K.KvsError):
         K.kvs_allocate_budget([1.0, 2.0], 10, 0.5, 1, 4)
