@@ -4,8 +4,9 @@
 // Euclidean norm of each problem's compress-zone value rows.
 //
 // HBM-bound reduction.  A row is read by d/4 lanes with 16-byte loads
-// (coalesced), its squared norm summed in float64 across those lanes, and
-// the row norms accumulated per workgroup over a chunk of rows; chunk
+// (coalesced, eight rows per thread in flight), its squared norm summed in
+// float64 across those lanes, and the row norms accumulated per workgroup
+// over a chunk of rows; chunk
 // partials are summed per problem in chunk order by a second kernel, so the
 // result does not depend on scheduling.
 #include "kvs_internal.h"
@@ -21,13 +22,26 @@ __global__ __launch_bounds__(256) void value_norm_kernel(VnormArgs a) {
   const int len = (a.Z + a.C - 1) / a.C;
   const int r0 = c * len, r1 = min(a.Z, r0 + len);
   const int lane = tid % TPR;
+  const float* base = a.V + (long long)p * a.Z * D + 4 * lane;
   double acc = 0.0;
-  for (int r = r0 + tid / TPR; r < r1; r += RPI) {
-    const f32x4 v = *(const f32x4*)(a.V + ((long long)p * a.Z + r) * D + 4 * lane);
-    double s = (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
+  // U rows per thread in flight; rows past the chunk are read clamped and
+  // not counted
+  constexpr int U = 8;
+  for (int rb = r0 + tid / TPR; rb < r1; rb += RPI * U) {
+    f32x4 v[U];
 #pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) acc += sqrt(s);
+    for (int u = 0; u < U; ++u) {
+      const int r = min(rb + u * RPI, r1 - 1);
+      v[u] = *(const f32x4*)(base + (long long)r * D);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      double s = (double)v[u].x * v[u].x + (double)v[u].y * v[u].y + (double)v[u].z * v[u].z +
+                 (double)v[u].w * v[u].w;
+#pragma unroll
+      for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0 && rb + u * RPI < r1) acc += sqrt(s);
+    }
   }
   __shared__ double red[256];
   red[tid] = acc;

@@ -474,6 +474,13 @@ def bench_alloc(args, torch, K):
         "pilot_mse_flat_alpha1": K.kvs_allocate_budget(pilot, K_total, 1.0, 1, w.Z),
         "value_norm_static": K.kvs_allocate_budget(vsig.cpu().numpy(), K_total, 1.0, 1, w.Z),
     }
+    # held-out queries for the use-side error of each allocation
+    from synth import make_use_batch
+    u = make_use_batch(w, 0, per_head=128)
+    nh = u["Qh"].shape[1]
+    Qh, Kr, Vr = (torch.from_numpy(u[key]).to(dev) for key in ("Qh", "Kr", "Vr"))
+    umse = torch.empty(P, dtype=torch.float32, device=dev)
+    urel = torch.empty(P, dtype=torch.float32, device=dev)
     quality = {}
     for name, ks in allocs.items():
         bt = K.Batch(P, d, w.Z, n, k=ks, scale=b["scale"])
@@ -483,11 +490,19 @@ def bench_alloc(args, torch, K):
         flags = torch.zeros(P, dtype=torch.int32, device=dev)
         K.kvs_compress(ctx, bt, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, wsm)
         m = mse.cpu().numpy().astype(np.float64)
+        bu = K.Batch(P, d, w.Z, nh, k=ks, scale=b["scale"])
+        wsu = torch.empty(K.use_eval_workspace_bytes(bu, w.m), dtype=torch.uint8, device=dev)
+        K.kvs_use_eval(ctx, bu, w.m, Qh, Kz, Vz, Kr, Vr, Kc, Vc, None, None, umse, urel, wsu)
+        um = umse.cpu().numpy().astype(np.float64)
         quality[name] = {"mean_mse": float(m.mean()), "max_mse": float(m.max()),
+                         "use_mean_mse": float(um.mean()),
+                         "use_mean_rel": float(urel.cpu().numpy().astype(np.float64).mean()),
                          "k_min": int(ks.min()), "k_max": int(ks.max())}
-        log(f"[bench] {name:22s} mean final MSE {m.mean():.4e} max {m.max():.4e} "
-            f"k in [{ks.min()}, {ks.max()}]")
+        log(f"[bench] {name:22s} mean final MSE {m.mean():.4e} max {m.max():.4e}; held-out "
+            f"use-side MSE {um.mean():.4e}; k in [{ks.min()}, {ks.max()}]")
+        del wsu
     base = quality["uniform"]["mean_mse"]
+    ubase = quality["uniform"]["use_mean_mse"]
     out = {
         "metric": "value-norm allocation signal: zone rows reduced/sec (HBM); allocation variants' final MSE",
         "value": round(w3.P * w3.Z * reps / elapsed, 1), "unit": "rows/s", "n_gpus": 1,
@@ -497,6 +512,8 @@ def bench_alloc(args, torch, K):
         "config": {"workload": f"signal: {w3.name} zone ({w3.P} x {w3.Z} x {w3.d}); quality: {w.name}",
                    "row": "alloc", "iters": T,
                    "mean_mse_over_uniform": {k: round(v["mean_mse"] / base, 4) for k, v in quality.items()},
+                   "use_mse_over_uniform": {k: round(v["use_mean_mse"] / ubase, 4)
+                                            for k, v in quality.items()},
                    "quality": quality},
         "roofline": roofline,
         "cpu_baseline": None,
