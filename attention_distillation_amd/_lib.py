@@ -335,7 +335,7 @@ def kvs_value_norms(ctx, P, Z, d, Vz, signal, ws):
 
 PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",
                    "hist_dots", "direction", "importance", "ref_attn_fwd", "merge",
-                   "build_queries", "use_attn_fwd")
+                   "build_queries", "use_attn_fwd", "attn_pv")
 
 
 def kvs_profile_enable(ctx, enable=True, kernels=None):

@@ -17,11 +17,11 @@
 namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
-  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_NCLASS
+  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
-    "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd"};
+    "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -193,22 +193,33 @@ void run_reference(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
 // Forward at keys K (+ alpha * dir when dir != NULL) for problems selected by
 // (st, mask): stores shifted scores, merges, writes G / e / crow and the loss
 // partials, then finalises per-problem losses in the given mode.
+// reuse_scores: the keys have not moved since the last forward of every
+// selected problem stored its scores (only the values changed), so the
+// scores are read back instead of formed again.
 void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Y,
                  const float* lse, const float* K, const float* V, LbState* st,
                  int mask, int fin_mode, float* loss, float* mse, const kvs_opts* o, void* ws,
-                 const std::vector<int>* hs = nullptr, int want = 0) {
+                 const std::vector<int>* hs = nullptr, int want = 0, bool reuse_scores = false) {
   FwdArgs f{};
   f.Q = Q; f.K = K; f.V = V; f.st = st; f.active_mask = mask;
-  f.shift = lse; f.St = at<float>(ws, pl.r_St);
+  f.shift = lse;
+  f.St = reuse_scores ? nullptr : at<float>(ws, pl.r_St);
+  f.Sload = reuse_scores ? at<float>(ws, pl.r_St) : nullptr;
   f.Opart = at<float>(ws, pl.r_Opart); f.Mpart = at<float>(ws, pl.r_Mpart); f.Lpart = at<float>(ws, pl.r_Lpart);
   f.info = at<ProbInfo>(ws, pl.r_info); f.P = pl.P; f.n = pl.n; f.C = pl.C; f.kuni = 0; f.kmax = pl.kmax;
   f.scale = b->scale;
   {
     const double ks = sum_k(pl, hs, want);
     const double np = hs ? 0 : pl.P;
-    Prof pr(ctx, PROF_FWD, 4.0 * pl.n * pl.d * ks,
-            4.0 * (ks * pl.d * 2.0 + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
-    launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+    if (reuse_scores) {
+      Prof pr(ctx, PROF_PV, 2.0 * pl.n * pl.d * ks,
+              4.0 * (ks * pl.d + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
+      launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+    } else {
+      Prof pr(ctx, PROF_FWD, 4.0 * pl.n * pl.d * ks,
+              4.0 * (ks * pl.d * 2.0 + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
+      launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+    }
   }
   MergeArgs m{};
   m.Opart = f.Opart; m.Mpart = f.Mpart; m.Lpart = f.Lpart; m.st = st; m.active_mask = mask;
@@ -359,8 +370,9 @@ void lb_dots(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const LbBuffers& B
 // L-BFGS bookkeeping: prep_mode 1 keeps the history, 2 clears it.
 void lb_eval_at_x(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o, const float* Q,
                   const float* Y, const float* lse, float* Kc, const float* Vc, const LbBuffers& B,
-                  int prep_mode, float* loss_out, float* mse_out, void* ws) {
-  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws);
+                  int prep_mode, float* loss_out, float* mse_out, void* ws, bool reuse_scores = false) {
+  run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, B.st, kAll, 2, loss_out, mse_out, o, ws, nullptr, 0,
+              reuse_scores);
   run_backward(ctx, pl, b, Q, Vc, B.st, kAll, ws);
   lb_dots(ctx, pl, b, B, ws, prep_mode, kAll, true, Kc);
 }
@@ -496,7 +508,8 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
   LbBuffers B = lb_in_ws(pl, ws);
   launch_state_init(B.st, pl.P, 1, ctx->stream);
   run_init(ctx, pl, b, Q, Kz, Yr, lr, Kc, Vc, nullptr, B.st, keys_given, ws);
-  lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws);
+  // the init's forward stored the scores at these keys
+  lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws, true);
   bool refreshed = true;
   if (kvs_status s = status_buffers(ctx, pl.P); s != KVS_OK) return s;
   int* hbuf[2] = {ctx->hstat, ctx->hstat + pl.P};
@@ -541,7 +554,9 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
         run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, 1 << ST_DONE_FAIL, 2, nullptr, nullptr, o,
                     ws);
       run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws);
-      lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 1, nullptr, mse, ws);
+      // the value solve used the stored scores at the current keys: valid for
+      // every problem, so the loss at the new values reads them back
+      lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 1, nullptr, mse, ws, true);
       refreshed = true;
     }
   }
@@ -577,8 +592,12 @@ kvs_status adam_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_
   aa.info = at<ProbInfo>(ws, pl.r_info); aa.P = pl.P; aa.d = pl.d;
   aa.b1 = (float)ad->beta1; aa.b2 = (float)ad->beta2; aa.eps = (float)ad->eps;
   double p1 = 1.0, p2 = 1.0;
+  bool fresh = false;   // scores stored at the current keys before a value solve
   for (int t = 1; t <= o->iters; ++t) {
-    if (t > 1) run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, o, ws);
+    if (t > 1)
+      run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, o, ws, nullptr, 0,
+                  fresh);
+    fresh = false;
     run_backward(ctx, pl, b, Q, Vc, nullptr, 0, ws);
     GradUpdArgs ga = grad_args(pl, b, ws, nullptr, 0, 2);
     ga.gout = g;
@@ -591,9 +610,10 @@ kvs_status adam_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_
     if (t % o->vc_every == 0) {
       run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, o, ws);
       run_value_solve(ctx, pl, b, Yr, Vc, flags, nullptr, kAllStates, ws);
+      fresh = true;
     }
   }
-  run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, loss, mse, o, ws);
+  run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, loss, mse, o, ws, nullptr, 0, fresh);
   return KVS_OK;
 }
 

@@ -217,8 +217,126 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Forward at keys whose shifted scores are already stored: the keys have not
+// moved since the forward that stored them, only the values have (the loss
+// after a value re-solve).  The scores are read from St instead of formed on
+// MFMA; staging, softmax and P V are the forward's, in the same layout (F64:
+// the layout of the fp64 score product).  A stored score is exactly the float
+// that product rounded to, so the partials equal the full forward's bit for bit.
+template <int D, bool F64>
+__global__ __launch_bounds__(256) void attn_pv_kernel(FwdArgs a) {
+  const int p = blockIdx.y, c = blockIdx.z;
+  const int k = a.info[p].k, koff = a.info[p].koff;
+  const long long soff = a.info[p].soff;
+  if (a.st && (!((1 << a.st[p].status) & a.active_mask) || k < 0)) return;
+  const int n = a.n;
+  const int npad = (n + 3) & ~3;
+  const int chunk = (((k + a.C - 1) / a.C) + 63) & ~63;
+  const int kbeg = c * chunk;
+  const int kend = min(k, kbeg + chunk);
+
+  __shared__ float Vt[D][64 + 4];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, lq = lane & 15;
+  const int q = blockIdx.x * 64 + wave * 16 + lq;
+  const bool qok = q < n;
+  const size_t prow = (size_t)p * n;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int NL = 64 * (D / 4) / 256;     // float4 of V per thread per tile
+  const float* Vp = a.V + (size_t)koff * D;
+  const float* Sp = a.Sload + soff;
+  for (int kt = kbeg; kt < kend; kt += 64) {
+    // this lane's scores (query q, keys of the score layout); rows past kend
+    // are -inf, queries past n 0 (as the forward forms them).  The bound
+    // between the PV products and these loads is the MFMA work and the
+    // partial outputs, not the scores' 64-byte segments.
+    float sv[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt + 16 * b + out_row<F64>(g, r);
+        sv[b][r] = key >= kend ? -INFINITY : (qok ? Sp[(size_t)key * npad + q] : 0.f);
+      }
+    __syncthreads();
+    f32x4 vv[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vv[u][j] = Vp[(unsigned)(min(kt + vt_key<F64>(vg, j), kend - 1) * D + dim)];
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
+      *(f32x4*)&Vt[dim][16 * (vg >> 2) + 4 * (vg & 3)] = vv[u];
+    }
+    __syncthreads();
+
+    float tmax = sv[0][0];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sv[b][r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);   // finite: the tile holds a valid key
+    const float corr = expf(m_run - m_new);
+    l_run *= corr;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[b][r] = expf(sv[b][r] - m_new);
+        l_run += sv[b][r];
+      }
+    m_run = m_new;
+
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const f32x4 vv4 = *(const f32x4*)&Vt[16 * db + lq][16 * b + 4 * g];
+        oacc[db] = mfma_f32(vv4.x, sv[b][0], oacc[db]);
+        oacc[db] = mfma_f32(vv4.y, sv[b][1], oacc[db]);
+        oacc[db] = mfma_f32(vv4.z, sv[b][2], oacc[db]);
+        oacc[db] = mfma_f32(vv4.w, sv[b][3], oacc[db]);
+      }
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (qok) {
+    const size_t orow = (size_t)c * a.P * n + prow + q;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) *(f32x4*)(a.Opart + orow * D + 16 * db + 4 * g) = oacc[db];
+    if (g == 0) {
+      a.Mpart[orow] = m_run;
+      a.Lpart[orow] = l_run;
+    }
+  }
+}
+
 void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s) {
   dim3 grid((a.n + 63) / 64, a.P, a.C);
+  if (a.Sload) {
+#define KVS_PV(DD, FF) hipLaunchKernelGGL((attn_pv_kernel<DD, FF>), grid, dim3(256), 0, s, a)
+    if (d == 128) { if (logit_f64) KVS_PV(128, true); else KVS_PV(128, false); }
+    else { if (logit_f64) KVS_PV(64, true); else KVS_PV(64, false); }
+#undef KVS_PV
+    return;
+  }
   const bool store = a.St != nullptr;
 #define KVS_FWD(DD, SS, FF) hipLaunchKernelGGL((attn_fwd_kernel<DD, SS, FF>), grid, dim3(256), 0, s, a)
   if (d == 128) {

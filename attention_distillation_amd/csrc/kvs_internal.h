@@ -110,6 +110,8 @@ struct FwdArgs {
   int active_mask;         // bit (1 << status) selects the problems processed
   const float* shift;      // [P][n] per-row score shift, NULL = none
   float* St;               // stored shifted scores (NULL = do not store)
+  const float* Sload;      // non-NULL: take the scores from these stored ones
+                           // (keys unchanged since they were stored; needs info)
   float* Opart; float* Mpart; float* Lpart;
   const ProbInfo* info;    // NULL: uniform k = kuni rows at K + p*kuni*d
   int P, n, C, kuni, kmax;

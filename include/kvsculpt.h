@@ -322,7 +322,8 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
  * kvs_profile_enable clears the totals; its argument is 0 (off), -1 (all
  * kernels) or a bitmask over attn_fwd (bit 0), attn_bwd, gram, potrf_panel,
  * trailing, back_subst, hist_dots, direction, importance, ref_attn_fwd,
- * merge, build_queries, use_attn_fwd (bit 12).  kvs_profile_read
+ * merge, build_queries, use_attn_fwd, attn_pv (bit 13: the forward that
+ * reads stored scores after a value re-solve).  kvs_profile_read
  * synchronises the stream and writes up to max entries (kernels with
  * launches) to out. */
 typedef struct {
