@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
       if (part == 0) a.lse_out[row] = lse;
     }
   } else {
-    __shared__ double red[2][256];
+    __shared__ double red[2][4];
     __shared__ int s_last;
     float rr = 0.f, dl = 0.f;
     if (ok) {
@@ -505,22 +505,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
       a.e[row] = e;
       a.crow[row] = -dl + (float)(2.0 * a.lambda) * e;
     }
-    const double lrow = ok ? (double)rr + a.lambda * (double)e * (double)e : 0.0;
-    const double orow = ok ? (double)rr : 0.0;
-    red[0][tid] = (part == 0) ? lrow : 0.0;
-    red[1][tid] = (part == 0) ? orow : 0.0;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-      if (tid < off) {
-        red[0][tid] += red[0][tid + off];
-        red[1][tid] += red[1][tid + off];
-      }
-      __syncthreads();
+    // every lane of a query holds its row terms; a wave holds four queries:
+    // their sum by two xor steps, then the four waves in order
+    double lrow = ok ? (double)rr + a.lambda * (double)e * (double)e : 0.0;
+    double orow = ok ? (double)rr : 0.0;
+    lrow += __shfl_xor(lrow, 16);
+    orow += __shfl_xor(orow, 16);
+    lrow += __shfl_xor(lrow, 32);
+    orow += __shfl_xor(orow, 32);
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = lrow;
+      red[1][tid >> 6] = orow;
     }
+    __syncthreads();
     if (tid == 0) {
       double* dst = a.part + ((size_t)p * gridDim.x + blockIdx.x) * 2;
-      coherent_store(dst, red[0][0]);
-      coherent_store(dst + 1, red[1][0]);
+      coherent_store(dst, ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3]);
+      coherent_store(dst + 1, ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3]);
       wait_own_stores();
       s_last = arrive_last(a.counter + p, gridDim.x);
     }
