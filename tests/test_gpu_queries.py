@@ -116,3 +116,30 @@ def test_built_queries_drive_reference_attention():
         ey, el = rel(Yg[p], Yo), rel(lg[p], lo)
         say(f"   p={p} relY={ey:.2e} rel_lse={el:.2e}")
         assert ey <= 1e-4 and el <= 1e-4
+
+
+def test_degenerate_query_shapes():
+    """No synthetic queries (src NULL) and no retain queries."""
+    import torch
+    rng = np.random.default_rng(9)
+    P, g, N, d = 3, 2, 37, 64
+    Qctx = rng.standard_normal((P, g, N, d)).astype(np.float32)
+    ctx = K.Context()
+    # F = 0: the retain block only, bit-exact copies
+    Q = empty((P, g * 5, d))
+    say("[queries] degenerate F=0 (src NULL), m=5")
+    K.kvs_build_queries(ctx, P, g, N, 5, 0, d, 1e4, to_gpu(Qctx), None, Q, None)
+    Qg = host(Q)
+    for p in range(P):
+        assert np.array_equal(Qg[p], Qctx[p, :, N - 5:].reshape(-1, d))
+    # m = 0: the future block only, one source per head at the first and last position
+    src = np.zeros((P, g, 2), dtype=np.int32)
+    src[:, :, 1] = N - 1
+    Q = empty((P, g * 2, d))
+    say("[queries] degenerate m=0, sources 0 and N-1")
+    K.kvs_build_queries(ctx, P, g, N, 0, 2, d, 1e4, to_gpu(Qctx), to_gpu(src), Q, None)
+    Qg = host(Q).astype(np.float64)
+    for p in range(P):
+        Qo = O.training_queries(Qctx[p], src[p], 0, 1e4)
+        assert np.abs(Qg[p] - Qo).max() <= 1e-6 * np.abs(Qo).max()
+    torch.cuda.synchronize()

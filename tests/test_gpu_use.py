@@ -100,3 +100,20 @@ def test_uncompressed_cache_has_no_use_error_and_outputs_are_optional():
     a = _run(u, [700, 900], Kc2, Vc2, w.m, outputs=True)
     b = _run(u, [700, 900], Kc2, Vc2, w.m, outputs=False)
     assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3])
+
+
+def test_use_eval_single_query_single_pair():
+    """n = 1 held-out query and k = 1 compressed pair per problem."""
+    w = tiny_workload(d=64, N=50, m=6, g=1, F=1, layers=1, kv_heads=3)
+    u = make_use_batch(w, 8, None, 1)
+    P, n, d = u["Qh"].shape
+    assert n == 1
+    ks = [1] * P
+    say(f"[use-eval] degenerate n=1, k=1, P={P}")
+    Kc, Vc = _subset(u, ks, 3)
+    Of, Oc, mse, rl = _run(u, ks, Kc, Vc, w.m)
+    for p in range(P):
+        r = O.use_side_outputs(u["Qh"][p], u["Kz"][p], u["Vz"][p], u["Kr"][p], u["Vr"][p],
+                               Kc[p:p + 1], Vc[p:p + 1], u["scale"])
+        assert rel(Of[p], r["full"]) <= TOL and rel(Oc[p], r["comp"]) <= TOL
+        assert abs(mse[p] - r["mse"]) <= TOL * r["mse"]
