@@ -21,8 +21,8 @@ default to the 56-problem full-cache workload (--config 2).  --row adam runs
 the schedule with Adam on the keys and reports its final output MSE over
 L-BFGS's; --row restarts runs R random restarts of one problem as one batch
 (kvs_compress_from_keys) and reports the single Select+Fit run's final loss
-over the best restart's.  The ablation rows carry no CPU baseline (the
-oracle of the whole schedule is timed by the default row).  --row alloc
+over the best restart's.  Each row times its own oracle on a bounded sample
+beside it.  --row alloc
 times the value-norm signal kernel on a llama3-8b-shaped zone and compares
 the main run's final MSE under uniform, pilot (flat, two-level, alpha 1)
 and value-norm allocations of the same total budget.
@@ -292,6 +292,44 @@ def _fwd_roofline(stats):
             "kernel": "attn_fwd", "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
 
 
+def cpu_adam(w, b, seconds, lr):
+    """Float64 oracle of the Adam schedule on problem 0 (bounded iterations)."""
+    from oracle import kvsculpt as O
+    Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
+    Y, l = O.reference_attention(Q, Kz, Vz, s)
+    t0 = time.perf_counter()
+    O.compress_problem_adam(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=5), O.AdamOptions(lr=lr),
+                            Y=Y, lse=l)
+    t5 = time.perf_counter() - t0
+    iters = int(max(5, min(w.T, 5 * round(seconds / max(t5, 1e-3)))))
+    t0 = time.perf_counter()
+    O.compress_problem_adam(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=iters),
+                            O.AdamOptions(lr=lr), Y=Y, lse=l)
+    el = time.perf_counter() - t0
+    return {"value": iters / el, "unit": "problem-iterations/s", "cores": _threads(),
+            "kind": "oracle", "sample": f"{w.name} problem 0, {iters} Adam iterations with value "
+                                        f"solves every 5 (Select+Fit init included), float64"}
+
+
+def cpu_restart(w, b, K0, seconds):
+    """Float64 oracle of one restart (the schedule from given keys) on problem 0."""
+    from oracle import kvsculpt as O
+    Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
+    Y, l = O.reference_attention(Q, Kz, Vz, s)
+    t0 = time.perf_counter()
+    O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=5), Y=Y, lse=l, init=K0,
+                       init_keys=True)
+    t5 = time.perf_counter() - t0
+    iters = int(max(5, min(w.T, 5 * round(seconds / max(t5, 1e-3)))))
+    t0 = time.perf_counter()
+    O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=iters), Y=Y, lse=l, init=K0,
+                       init_keys=True)
+    el = time.perf_counter() - t0
+    return {"value": iters / el, "unit": "problem-iterations/s", "cores": _threads(),
+            "kind": "oracle", "sample": f"{w.name} problem 0, one restart of {iters} L-BFGS "
+                                        f"iterations from random keys, float64"}
+
+
 def bench_adam(args, torch, K):
     """The schedule with Adam on the keys, and its final MSE against L-BFGS's."""
     from synth import WORKLOADS, make_batch
@@ -332,6 +370,7 @@ def bench_adam(args, torch, K):
     mse_lb = mse.cpu().numpy().copy()
     ratio = [float(x) for x in mse_adam / mse_lb]
     log(f"[bench] final output MSE Adam {mse_adam.tolist()} L-BFGS {mse_lb.tolist()} flags {fl.tolist()}")
+    cpu = None if args.no_cpu_baseline else cpu_adam(w, b, min(args.cpu_seconds, 15.0), args.adam_lr)
     out = {
         "metric": "Adam-on-keys schedule: problem-iterations/sec (ablation of L-BFGS)",
         "value": round(P * T * args.steps / elapsed, 2), "unit": "problem-iterations/s",
@@ -342,7 +381,7 @@ def bench_adam(args, torch, K):
                    "k": w.k0, "iters": T, "vc_every": 5, "lr": args.adam_lr,
                    "mse_adam_over_lbfgs": [round(r, 3) for r in ratio]},
         "roofline": _fwd_roofline(stats),
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -398,6 +437,8 @@ def bench_restarts(args, torch, K):
     best = float(lr_.min())
     log(f"[bench] restart losses min {best:.6g} median {float(np.median(lr_)):.6g} "
         f"max {float(lr_.max()):.6g}; single Select+Fit run {single:.6g}")
+    cpu = None if args.no_cpu_baseline else cpu_restart(w, b, b["Kz"][0][draws[0]],
+                                                        min(args.cpu_seconds, 15.0))
     out = {
         "metric": "random-restart search: problem-iterations/sec over R restarts batched",
         "value": round(R * T * args.steps / elapsed, 2), "unit": "problem-iterations/s",
@@ -408,7 +449,7 @@ def bench_restarts(args, torch, K):
                    "Z": w.Z, "k": w.k0, "iters": T,
                    "single_run_over_best_restart": round(single / best, 4)},
         "roofline": _fwd_roofline(stats),
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -446,6 +487,19 @@ def bench_alloc(args, torch, K):
                 "unit": "GB/s", "frac": round(nbytes / avg_s / PEAK_HBM, 4),
                 "traffic": traffic_for("value_norms"), "kernel": "value_norms (+ final sum)",
                 "launches": reps, "avg_us": round(avg_s * 1e6, 2)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle signal on problems of the same zone, copied to the host
+        from oracle import kvsculpt as O
+        Vh = V[: min(w3.P, 16)].cpu().numpy()
+        done, t0c = 0, time.perf_counter()
+        while time.perf_counter() - t0c < min(args.cpu_seconds, 10.0):
+            O.value_norm_signal(Vh[done % Vh.shape[0]])
+            done += 1
+        elc = time.perf_counter() - t0c
+        cpu = {"value": round(done * w3.Z / elc, 1), "unit": "rows/s", "cores": _threads(),
+               "kind": "oracle", "sample": f"{done} problems' value-norm signals ({w3.Z} x {w3.d} "
+                                           f"zones), float64 NumPy"}
     del V
     # quality: pilot at uniform k, then the main run under each allocation
     w = WORKLOADS[args.config]
@@ -516,7 +570,7 @@ def bench_alloc(args, torch, K):
                                             for k, v in quality.items()},
                    "quality": quality},
         "roofline": roofline,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
