@@ -424,43 +424,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
   const size_t plane = (size_t)a.P * n;
 
   // all chunk maxima and sums first, then the partial outputs four chunks at
-  // a time; loads are branch-free (rows past n read row 0 and are dropped)
+  // a time; loads are branch-free (rows past n read row 0 and are dropped).
+  // The targets of the loss are loaded first so their latency overlaps the
+  // partials'.
   const size_t rrow = ok ? row : (size_t)p * n;
-  float mv[kMaxChunks], lv[kMaxChunks];
+  f32x4 yv[DPT / 4];
+  if constexpr (LOSS) {
+    const float* y = a.Y + rrow * D + part * DPT;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const size_t o = (c < a.C ? c : 0) * plane + rrow;
-    mv[c] = a.Mpart[o];
-    lv[c] = a.Lpart[o];
+    for (int i = 0; i < DPT / 4; ++i) yv[i] = *(const f32x4*)(y + 4 * i);
   }
-  float m = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c)
-    if (c < a.C) m = fmaxf(m, mv[c]);
-  float l = 0.f;
+  float m, l;
   float o[DPT];
+  if (a.C == 1) {
+    // one chunk: its output is already merged (the general path would scale
+    // it by exp(0) = 1, so the result is the same bit for bit)
+    m = a.Mpart[rrow];
+    l = a.Lpart[rrow];
+    const float* src = a.Opart + rrow * D + part * DPT;
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) o[i] = 0.f;
-#pragma unroll
-  for (int c0 = 0; c0 < kMaxChunks; c0 += 4) {
-    if (c0 >= a.C) break;
-    f32x4 ov[4][DPT / 4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int c = c0 + cc < a.C ? c0 + cc : 0;
-      const float* src = a.Opart + (c * plane + rrow) * D + part * DPT;
-#pragma unroll
-      for (int i = 0; i < DPT / 4; ++i) ov[cc][i] = *(const f32x4*)(src + 4 * i);
+    for (int i = 0; i < DPT / 4; ++i) {
+      const f32x4 v = *(const f32x4*)(src + 4 * i);
+      o[4 * i + 0] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
     }
+  } else {
+    float mv[kMaxChunks], lv[kMaxChunks];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int c = c0 + cc;
-      const float w = (c < a.C) ? expf(mv[c] - m) : 0.f;
-      l += w * ((c < a.C) ? lv[c] : 0.f);
+    for (int c = 0; c < kMaxChunks; ++c) {
+      const size_t off = (c < a.C ? c : 0) * plane + rrow;
+      mv[c] = a.Mpart[off];
+      lv[c] = a.Lpart[off];
+    }
+    m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < DPT / 4; ++i) {
-        o[4 * i + 0] += w * ov[cc][i].x; o[4 * i + 1] += w * ov[cc][i].y;
-        o[4 * i + 2] += w * ov[cc][i].z; o[4 * i + 3] += w * ov[cc][i].w;
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < a.C) m = fmaxf(m, mv[c]);
+    l = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < kMaxChunks; c0 += 4) {
+      if (c0 >= a.C) break;
+      f32x4 ov[4][DPT / 4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int c = c0 + cc < a.C ? c0 + cc : 0;
+        const float* src = a.Opart + (c * plane + rrow) * D + part * DPT;
+#pragma unroll
+        for (int i = 0; i < DPT / 4; ++i) ov[cc][i] = *(const f32x4*)(src + 4 * i);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int c = c0 + cc;
+        const float w = (c < a.C) ? expf(mv[c] - m) : 0.f;
+        l += w * ((c < a.C) ? lv[c] : 0.f);
+#pragma unroll
+        for (int i = 0; i < DPT / 4; ++i) {
+          o[4 * i + 0] += w * ov[cc][i].x; o[4 * i + 1] += w * ov[cc][i].y;
+          o[4 * i + 2] += w * ov[cc][i].z; o[4 * i + 3] += w * ov[cc][i].w;
+        }
       }
     }
   }
@@ -481,13 +503,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
     __shared__ int s_last;
     float rr = 0.f, dl = 0.f;
     if (ok) {
-      const float* y = a.Y + row * D + part * DPT;
       float* gout = a.G + row * D + part * DPT;
 #pragma unroll
       for (int i = 0; i < DPT; i += 4) {
-        const f32x4 yv = *(const f32x4*)(y + i);
+        const f32x4 y4 = yv[i / 4];
         f32x4 gv;
-        const float r0 = o[i] - yv.x, r1 = o[i + 1] - yv.y, r2 = o[i + 2] - yv.z, r3 = o[i + 3] - yv.w;
+        const float r0 = o[i] - y4.x, r1 = o[i + 1] - y4.y, r2 = o[i + 2] - y4.z, r3 = o[i + 3] - y4.w;
         rr += r0 * r0 + r1 * r1 + r2 * r2 + r3 * r3;
         gv.x = 2.f * r0; gv.y = 2.f * r1; gv.z = 2.f * r2; gv.w = 2.f * r3;
         dl += gv.x * o[i] + gv.y * o[i + 1] + gv.z * o[i + 2] + gv.w * o[i + 3];
@@ -532,9 +553,102 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
   }
 }
 
+// Loss-mode merge when the forward used one key chunk (its partial output is
+// already the merged one): 64 queries per workgroup, the loads of all four
+// 16-query groups issued before any use, so a workgroup moves enough bytes to
+// cover its fixed cost (status test, partial store, arrival).  The row terms,
+// G, e and crow are those of merge_kernel, bit for bit; the loss partials
+// are summed over four times fewer, larger blocks.
+template <int D>
+__global__ __launch_bounds__(256) void merge1_loss_kernel(MergeArgs a) {
+  const int p = blockIdx.y;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  constexpr int DPT = D / 16, SUB = 4;
+  const int tid = threadIdx.x, qi = tid >> 4, part = tid & 15;
+  const int n = a.n;
+  bool ok[SUB];
+  size_t row[SUB];
+  float mv[SUB], lv[SUB];
+  f32x4 ov[SUB][DPT / 4], yv[SUB][DPT / 4];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    const int q = blockIdx.x * 64 + 16 * u + qi;
+    ok[u] = q < n;
+    row[u] = (size_t)p * n + (ok[u] ? q : 0);
+    mv[u] = a.Mpart[row[u]];
+    lv[u] = a.Lpart[row[u]];
+    const float* src = a.Opart + row[u] * D + part * DPT;
+    const float* y = a.Y + row[u] * D + part * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT / 4; ++i) {
+      ov[u][i] = *(const f32x4*)(src + 4 * i);
+      yv[u][i] = *(const f32x4*)(y + 4 * i);
+    }
+  }
+  double lsum = 0.0, osum = 0.0;
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    const float inv = ok[u] ? 1.f / lv[u] : 0.f;
+    const float e = ok[u] ? mv[u] + logf(lv[u]) : 0.f;   // lhat - l
+    float rr = 0.f, dl = 0.f;
+    float* gout = a.G + row[u] * D + part * DPT;
+#pragma unroll
+    for (int i = 0; i < DPT / 4; ++i) {
+      const float o0 = ov[u][i].x * inv, o1 = ov[u][i].y * inv, o2 = ov[u][i].z * inv, o3 = ov[u][i].w * inv;
+      const float r0 = o0 - yv[u][i].x, r1 = o1 - yv[u][i].y, r2 = o2 - yv[u][i].z, r3 = o3 - yv[u][i].w;
+      rr += r0 * r0 + r1 * r1 + r2 * r2 + r3 * r3;
+      f32x4 gv;
+      gv.x = 2.f * r0; gv.y = 2.f * r1; gv.z = 2.f * r2; gv.w = 2.f * r3;
+      dl += gv.x * o0 + gv.y * o1 + gv.z * o2 + gv.w * o3;
+      if (ok[u]) *(f32x4*)(gout + 4 * i) = gv;
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      rr += __shfl_xor(rr, off);
+      dl += __shfl_xor(dl, off);
+    }
+    if (ok[u] && part == 0) {
+      a.e[row[u]] = e;
+      a.crow[row[u]] = -dl + (float)(2.0 * a.lambda) * e;
+    }
+    lsum += ok[u] ? (double)rr + a.lambda * (double)e * (double)e : 0.0;
+    osum += ok[u] ? (double)rr : 0.0;
+  }
+  // each lane of a query group holds the group's sums; a wave holds four
+  // groups: two xor steps, then the four waves in order
+  __shared__ double red[2][4];
+  __shared__ int s_last;
+  lsum += __shfl_xor(lsum, 16);
+  osum += __shfl_xor(osum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  osum += __shfl_xor(osum, 32);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = lsum;
+    red[1][tid >> 6] = osum;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double* dst = a.part + ((size_t)p * gridDim.x + blockIdx.x) * 2;
+    coherent_store(dst, ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3]);
+    coherent_store(dst + 1, ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3]);
+    wait_own_stores();
+    s_last = arrive_last(a.counter + p, gridDim.x);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  finalize_problem<D>(a, p, gridDim.x);
+  if (tid == 0) a.counter[p] = 0u;
+}
+
 int merge_blocks(int n) { return (n + 15) / 16; }
 
 void launch_merge(const MergeArgs& a, int d, bool loss_mode, hipStream_t s) {
+  if (loss_mode && a.C == 1) {
+    dim3 grid((a.n + 63) / 64, a.P);
+    if (d == 128) hipLaunchKernelGGL((merge1_loss_kernel<128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((merge1_loss_kernel<64>), grid, dim3(256), 0, s, a);
+    return;
+  }
   dim3 grid(merge_blocks(a.n), a.P);
 #define KVS_MERGE(DD, LL) hipLaunchKernelGGL((merge_kernel<DD, LL>), grid, dim3(256), 0, s, a)
   if (d == 128) { if (loss_mode) KVS_MERGE(128, true); else KVS_MERGE(128, false); }

@@ -25,7 +25,9 @@ over the best restart's.  Each row times its own oracle on a bounded sample
 beside it.  --row alloc
 times the value-norm signal kernel on a llama3-8b-shaped zone and compares
 the main run's final MSE under uniform, pilot (flat, two-level, alpha 1)
-and value-norm allocations of the same total budget.
+and value-norm allocations of the same total budget.  --row vector runs 25
+iterations on a 64-problem slice of the llama3-8b-shaped cache, large enough
+for the vector and reduction kernels' HBM rates to be read from a trace.
 
 Printed: one JSON line (stdout).  It carries the live roofline of the
 dominant kernel (HIP events on the library's stream over the timed steps)
@@ -575,6 +577,57 @@ def bench_alloc(args, torch, K):
     print(json.dumps(out), flush=True)
 
 
+def bench_vector(args, torch, K):
+    """The schedule on a 64-problem slice of the llama3-8b-shaped cache: one key
+    chunk and one query split, so the merge, history and direction kernels move
+    hundreds of MB per launch (their HBM fractions come from a kernel trace)."""
+    from synth import WORKLOADS, make_batch
+    w = WORKLOADS[3]
+    P = 64
+    T = 25 if args.iters is None else args.iters
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name} problems 0..{P - 1}: n={w.n} Z={w.Z} k={w.k0} T={T}")
+    b = make_batch(w, 0, problems=list(range(P)))
+    _, n, d = b["Q"].shape
+    Q, Kz, Vz = (torch.from_numpy(b[key]).to(dev) for key in ("Q", "Kz", "Vz"))
+    bt = K.Batch(P, d, w.Z, n, k=[w.k0] * P, scale=b["scale"])
+    o = K.opts(iters=T)
+    ws = torch.empty(K.workspace_bytes(bt, o), dtype=torch.uint8, device=dev)
+    Kc = torch.empty((w.k0 * P, d), dtype=torch.float32, device=dev)
+    Vc = torch.empty_like(Kc)
+    loss, mse, l0 = (torch.empty(P, dtype=torch.float32, device=dev) for _ in range(3))
+    flags = torch.zeros(P, dtype=torch.int32, device=dev)
+    ctx = K.Context()
+
+    def step():
+        K.kvs_compress(ctx, bt, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kvs_profile_enable(ctx, True, kernels=["attn_fwd"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = K.kvs_profile_read(ctx)
+    K.kvs_profile_enable(ctx, False)
+    out = {
+        "metric": "L-BFGS problem-iterations/sec on a 64-problem llama3-8b slice (vector-kernel sizing run)",
+        "value": round(P * T * args.steps / elapsed, 2), "unit": "problem-iterations/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name} problems 0..{P - 1}", "row": "vector", "n": n,
+                   "Z": w.Z, "k": w.k0, "iters": T},
+        "roofline": _fwd_roofline(stats),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -586,11 +639,13 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--row", choices=["compress", "queries", "use", "adam", "restarts", "alloc"],
+    ap.add_argument("--row", choices=["compress", "queries", "use", "adam", "restarts", "alloc",
+                                      "vector"],
                     default="compress",
                     help="compress: the optimizer (default); queries: training-query "
                          "construction; use: use-side evaluation; adam / restarts: the "
-                         "optimizer ablations; alloc: allocation variants")
+                         "optimizer ablations; alloc: allocation variants; vector: the "
+                         "schedule on a 64-problem llama3-8b slice (vector-kernel sizing)")
     ap.add_argument("--adam-lr", type=float, default=1e-2)
     ap.add_argument("--restarts", type=int, default=100)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -623,6 +678,9 @@ def main():
         return
     if args.row == "alloc":
         bench_alloc(args, torch, K)
+        return
+    if args.row == "vector":
+        bench_vector(args, torch, K)
         return
 
     w = WORKLOADS[args.config]
