@@ -362,7 +362,7 @@ void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s) {
 // Fixed-order sum of the per-block partials, then the per-problem decision.
 template <int D>
 __device__ void finalize_problem(const MergeArgs& a, int p, int nblk) {
-  __shared__ double r0[256], r1[256];
+  __shared__ double r0[4], r1[4];
   const int t = threadIdx.x;
   double sL = 0.0, sO = 0.0;
   for (int i = t; i < nblk; i += 256) {
@@ -370,19 +370,20 @@ __device__ void finalize_problem(const MergeArgs& a, int p, int nblk) {
     sL += coherent_load(src);
     sO += coherent_load(src + 1);
   }
-  r0[t] = sL;
-  r1[t] = sO;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) {
-      r0[t] += r0[t + off];
-      r1[t] += r1[t + off];
-    }
-    __syncthreads();
+  // fixed xor tree within each wave, then the four waves in order
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    sL += __shfl_xor(sL, off);
+    sO += __shfl_xor(sO, off);
   }
+  if ((t & 63) == 0) {
+    r0[t >> 6] = sL;
+    r1[t >> 6] = sO;
+  }
+  __syncthreads();
   if (t != 0) return;
-  sL = r0[0];
-  sO = r1[0];
+  sL = ((r0[0] + r0[1]) + r0[2]) + r0[3];
+  sO = ((r1[0] + r1[1]) + r1[2]) + r1[3];
   LbState* st = a.st ? a.st + p : nullptr;
   if (a.fin_mode == 1) {
     st->Ltrial = sL;
