@@ -622,11 +622,13 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
   };
   float dv[16];
   load_dinv(dv, KT - 1);
+  // the two first L blocks of a step (rb = wave, wave + 4) are loaded while
+  // the previous step finishes, into the registers its updates have freed
+  float av0[4][16], av1[4][16];
+  const int rb0 = wave, rb1 = wave + 4;
+  if (rb0 < KT - 1) load_block(av0, KT - 1, rb0);
+  if (rb1 < KT - 1) load_block(av1, KT - 1, rb1);
   for (int i = KT - 1; i >= 0; --i) {
-    float av0[4][16], av1[4][16];
-    const int rb0 = wave, rb1 = wave + 4;
-    if (rb0 < i) load_block(av0, i, rb0);
-    if (rb1 < i) load_block(av1, i, rb1);
     // X_i rows b = 16 wave + (4g + r): sum_a inv(L_ii)[a][b] W_i[a][c]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     {
@@ -655,6 +657,9 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
         update_block(av0, bx, rb);
         if (rb + 4 < i) update_block(av1, bx, rb + 4);
       }
+      // next step's first blocks
+      if (rb0 < i - 1) load_block(av0, i - 1, rb0);
+      if (rb1 < i - 1) load_block(av1, i - 1, rb1);
     }
     __syncthreads();
   }
