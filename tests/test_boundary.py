@@ -127,6 +127,46 @@ def test_use_eval_workspace_and_argument_errors(K):
     assert lib.kvs_destroy(ctx) == 0
 
 
+def test_ablation_and_signal_argument_errors(K):
+    lib = K.load()
+    ctx = ctypes.c_void_p()
+    assert lib.kvs_create(ctypes.byref(ctx), None) == 0
+    fake = ctypes.c_void_p(0x1000)
+    b = K.Batch(1, 64, 224, 96, k=[64])
+    o = K.opts()
+    big = 1 << 40
+    # Adam: options checked before anything else
+    st = lib.kvs_compress_adam(ctx, ctypes.byref(b.c), ctypes.byref(o), None, 0, fake, fake, fake,
+                               fake, fake, fake, None, None, fake, fake, big)
+    assert st == -1 and b"adam" in lib.kvs_last_error(ctx)
+    for bad in (K.adam_opts(lr=0.0), K.adam_opts(beta1=1.0), K.adam_opts(beta2=-0.1),
+                K.adam_opts(eps=0.0)):
+        st = lib.kvs_compress_adam(ctx, ctypes.byref(b.c), ctypes.byref(o), ctypes.byref(bad), 0,
+                                   fake, fake, fake, fake, fake, fake, None, None, fake, fake, big)
+        assert st == -1 and b"lr" in lib.kvs_last_error(ctx)
+    # flags are required for Adam
+    good = K.adam_opts()
+    st = lib.kvs_compress_adam(ctx, ctypes.byref(b.c), ctypes.byref(o), ctypes.byref(good), 0, fake,
+                               fake, fake, fake, fake, fake, None, None, None, fake, big)
+    assert st == -1 and b"flags" in lib.kvs_last_error(ctx)
+    # restarts: the same checks as kvs_compress
+    st = lib.kvs_compress_from_keys(ctx, ctypes.byref(b.c), None, fake, fake, fake, fake, fake, fake,
+                                    None, None, fake, fake, big)
+    assert st == -1 and b"opts" in lib.kvs_last_error(ctx)
+    st = lib.kvs_compress_from_keys(ctx, ctypes.byref(b.c), ctypes.byref(o), fake, fake, fake, fake,
+                                    fake, fake, None, None, fake, fake, 16)
+    assert st == -3
+    # value norms: sizes, pointers, workspace
+    assert lib.kvs_value_norms(ctx, 2, 100, 96, fake, fake, fake, big) == -1
+    assert lib.kvs_value_norms(ctx, 2, 100, 64, fake, None, fake, big) == -1
+    assert lib.kvs_value_norms(ctx, 2, 100, 64, fake, fake, fake, 8) == -3
+    d = K.adam_opts.__defaults__
+    dflt = K._lib.KvsAdamOpts()
+    lib.kvs_default_adam_opts(ctypes.byref(dflt))
+    assert (dflt.lr, dflt.beta1, dflt.beta2, dflt.eps) == d
+    assert lib.kvs_destroy(ctx) == 0
+
+
 def test_allocator_cpp_equals_oracle_bit_for_bit(K):
     rng = np.random.default_rng(20)
     for it in range(10000):
