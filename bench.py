@@ -73,9 +73,9 @@ MEASURED_TRAFFIC = {
     # qwen2.5-1.5b-full-cache training queries: FETCH 53517.7 KiB x 1.99978
     # + WRITE 107520.0 KiB x 1.00000 per dispatch
     "build_queries": {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
-    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 9688.9 KiB x 1.99978
+    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 9626.8 KiB x 1.99978
     # + WRITE 52500.0 KiB x 1.00000 per dispatch
-    "attn_fwd": {"bytes": 73600669, "source": "attn_fwd.hip", "sha": "936fd2a0f2ed272f"},
+    "attn_fwd": {"bytes": 73473514, "source": "attn_fwd.hip", "sha": "b27ce2ca39f20c44"},
 }
 
 
