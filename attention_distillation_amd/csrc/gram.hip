@@ -164,8 +164,164 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
       }
 }
 
+// 128x128 output tiles for batches with many tiles: each staged weight is
+// used by 128 outputs instead of 64, which halves the exp work and the LDS
+// operand reads per flop.  Tile t of a problem with KT2 = ceil(KT / 2)
+// 128-key tiles is (I2, J2) of the lower triangle, then (KT2, J2) for the d
+// value rows of Y^T A (one 128-row tile).  Results go to the same 64-tile
+// layout of M as gram_kernel's; rows and columns past kpad (odd KT) and the
+// strictly upper quadrant of a diagonal tile are not written.
+__device__ __forceinline__ bool gram_tile128(long long t, int KT2, int& I2, int& J2) {
+  const long long tri = (long long)KT2 * (KT2 + 1) / 2;
+  if (t < tri) {
+    int i = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while ((long long)(i + 1) * (i + 2) / 2 <= t) ++i;
+    while ((long long)i * (i + 1) / 2 > t) --i;
+    I2 = i;
+    J2 = (int)(t - (long long)i * (i + 1) / 2);
+    return true;
+  }
+  const long long u = t - tri;
+  if (u >= KT2) return false;
+  I2 = KT2;
+  J2 = (int)u;
+  return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gram128_kernel(GramArgs a) {
+  unsigned bx, by, bz;
+  xcd_block(bx, by, bz);
+  const int p = by;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int KT = pi.kpad / 64, KT2 = (KT + 1) / 2;
+  int I2, J2;
+  if (!gram_tile128(bx, KT2, I2, J2)) return;
+  const int n = a.n, npad = (n + 3) & ~3;
+  const int nq = ((((n + a.Cg - 1) / a.Cg) + 63) / 64) * 64;
+  const int qbeg = bz * nq, qend = min(n, qbeg + nq);
+
+  __shared__ float Ra[128][68];
+  __shared__ float Ca[128][68];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+  const int wr = wave >> 1, wc = wave & 1;     // 64x64 output quadrant of this wave
+  const bool yrows = I2 >= KT2;
+  const bool diag = !yrows && I2 == J2;
+  // quadrants with nothing to write skip their MFMA work (they still stage)
+  const bool idle = (diag && wr == 0 && wc == 1) || (yrows && 64 * wr >= D) ||
+                    (!yrows && 128 * I2 + 64 * wr >= pi.kpad) || (128 * J2 + 64 * wc >= pi.kpad);
+  const float* St = a.St + pi.soff;
+  const float* E = a.e + (size_t)p * n;
+  const float* Y = a.Y + (size_t)p * n * D;
+  const int keyR = 128 * I2, keyC = 128 * J2;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Operand tiles of 64 queries, loads of the next tile issued before the
+  // MFMA work of this one.  Key tiles: element u of a thread (i = tid + 256 u)
+  // is key i / 16, queries 4 (i % 16) .. + 3 (one 16-byte load); value rows:
+  // dim i % 128, queries 4 (i / 128) .. + 3 (four 4-byte loads), landing
+  // transposed with one 16-byte LDS store.  Keys past k read the last key;
+  // queries past qend are zeroed; dims past d are zero.
+  f32x4 pr[8], pc[8], ev;
+  auto prefetch = [&](int qt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ev[j] = E[min(qt + 4 * (tid & 15) + j, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = tid + 256 * u;
+      const int r = i >> 4, q4 = 4 * (i & 15);
+      if (yrows) {
+        const int dim = i & 127, qy = qt + 4 * (i >> 7);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[u][j] = dim < D ? Y[(size_t)min(qy + j, n - 1) * D + dim] : 0.f;
+      } else {
+        pr[u] = *(const f32x4*)(St + (size_t)min(keyR + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
+      }
+      if (!diag) pc[u] = *(const f32x4*)(St + (size_t)min(keyC + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
+    }
+  };
+  auto weights = [&](f32x4 v, int q0) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (q0 + j < qend) ? __expf(v[j] - ev[j]) : 0.f;
+    return w;
+  };
+  if (qbeg < qend) prefetch(qbeg);
+  for (int qt = qbeg; qt < qend; qt += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = tid + 256 * u;
+      const int r = yrows ? (i & 127) : (i >> 4), q4 = yrows ? 4 * (i >> 7) : 4 * (i & 15);
+      f32x4 v;
+      if (yrows) {
+        v = pr[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (qt + q4 + j >= qend) v[j] = 0.f;
+      } else {
+        v = weights(pr[u], qt + q4);
+      }
+      *(f32x4*)&Ra[r][q4] = v;
+      if (!diag) *(f32x4*)&Ca[i >> 4][4 * (i & 15)] = weights(pc[u], qt + 4 * (i & 15));
+    }
+    __syncthreads();
+    if (qt + 64 < qend) prefetch(qt + 64);
+    if (idle) continue;
+    float (*C)[68] = diag ? Ra : Ca;
+#pragma unroll
+    for (int qq = 0; qq < 64; qq += 16) {
+      f32x4 av[4], bv[4];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) av[ib] = *(const f32x4*)&Ra[64 * wr + 16 * ib + lq][qq + 4 * g];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) bv[jb] = *(const f32x4*)&C[64 * wc + 16 * jb + lq][qq + 4 * g];
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          acc[ib][jb] = mfma_g(av[ib].x, bv[jb].x, acc[ib][jb]);
+          acc[ib][jb] = mfma_g(av[ib].y, bv[jb].y, acc[ib][jb]);
+          acc[ib][jb] = mfma_g(av[ib].z, bv[jb].z, acc[ib][jb]);
+          acc[ib][jb] = mfma_g(av[ib].w, bv[jb].w, acc[ib][jb]);
+        }
+    }
+  }
+  if (idle) return;
+
+  float* Mout = a.Mpart + (size_t)bz * a.mtot + pi.moff;
+  const int ld = pi.kpad;
+  const int row0 = yrows ? pi.kpad + 64 * wr : keyR + 64 * wr;
+  const int col0 = keyC + 64 * wc;
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * ib + 4 * g + r;
+        const int col = col0 + 16 * jb + lq;
+        Mout[(size_t)row * ld + col] = acc[ib][jb][r];
+      }
+}
+
 void launch_gram(const GramArgs& a, int d, hipStream_t s) {
   const long long KT = a.kpadmax / 64;
+  // 128-row tiles when the batch has enough of them to fill the chip
+  const long long KT2 = (KT + 1) / 2;
+  const long long T2 = KT2 * (KT2 + 1) / 2 + KT2;
+  if ((long long)a.P * T2 * a.Cg >= 512) {
+    dim3 grid2((unsigned)T2, a.P, a.Cg);
+    if (d == 128) hipLaunchKernelGGL((gram128_kernel<128>), grid2, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gram128_kernel<64>), grid2, dim3(256), 0, s, a);
+    return;
+  }
   const long long T = KT * (KT + 1) / 2 + (long long)(d / 64) * KT;
   dim3 grid((unsigned)T, a.P, a.Cg);
   if (d == 128) hipLaunchKernelGGL((gram_kernel<128>), grid, dim3(256), 0, s, a);

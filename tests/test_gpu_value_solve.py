@@ -45,6 +45,11 @@ CASES = {
     # workgroup's LDS for the first and not for the second
     "llama3-8b-k2381": (WORKLOADS[3], lambda p, Z: 2381, 0.0, [0]),
     "llama3-8b-k2600": (WORKLOADS[3], lambda p, Z: 2600, 0.0, [5]),
+    # twelve full-cache heads with ragged k (odd tile counts, k = 1, k = 64):
+    # a batch large enough for the 128x128 Gram tiles
+    "full-cache-12-ragged": (WORKLOADS[2],
+                             lambda p, Z: [960, 897, 64, 1, 700, 513, 959, 130, 300, 400, 257, 77][p],
+                             0.0, list(range(12))),
 }
 
 
