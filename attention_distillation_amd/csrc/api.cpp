@@ -260,10 +260,18 @@ GradUpdArgs grad_args(const Plan& pl, const kvs_batch* b, void* ws, LbState* st,
   return g;
 }
 
+// Inputs of the forward that the refinement step of a value solve repeats.
+struct RefineIn {
+  const float* Q; const float* lse; const float* Kc;
+};
+
 // Ridge value solve from the last forward's stored scores (St, e): Gram with
 // the A^T Y rows, fixed-order reduction, mu, panel Cholesky, back solve.
+// With ref (every problem active, no state), one refinement step follows:
+// G = 2 (A Vc - Y) from the stored scores, r = -A^T G / 2 - mu Vc in fp64,
+// Vc += (L L^T)^-1 r with the same factor.
 void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Y, float* Vc,
-                     int* flags, LbState* st, int mask, void* ws) {
+                     int* flags, LbState* st, int mask, void* ws, const RefineIn* ref = nullptr) {
   float* M = at<float>(ws, pl.r_M);
   // kernels that read the status only to select problems skip that load
   // when every status is selected
@@ -305,12 +313,28 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
     Prof pr(ctx, PROF_BACK, fl, 0);
     launch_back_subst(bk, pl.d, ctx->stream);
   }
+  if (!ref) return;
+  run_forward(ctx, pl, b, ref->Q, Y, ref->lse, ref->Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr,
+              ws, nullptr, 0, true);
+  RhsArgs ra{};
+  ra.St = g.St; ra.e = g.e; ra.G = at<float>(ws, pl.r_G); ra.info = g.info;
+  ra.Rpart = at<double>(ws, pl.r_R); ra.xtot = pl.kpadtot * pl.d;
+  ra.P = pl.P; ra.n = pl.n; ra.Cr = pl.Crf; ra.kpadmax = pl.kpadmax;
+  launch_resid_rhs(ra, pl.d, ctx->stream);
+  FsubArgs fa{};
+  fa.Rpart = ra.Rpart; fa.xtot = ra.xtot; fa.Cr = ra.Cr; fa.mu = c.mu; fa.Vc = Vc; fa.M = M;
+  fa.Dinv = c.Dinv; fa.X = bk.X; fa.info_out = c.info_out; fa.info = g.info; fa.P = pl.P;
+  fa.kpadmax = pl.kpadmax; fa.lds_max = ctx->lds_max;
+  launch_fwd_subst(fa, pl.d, ctx->stream);
+  bk.accumulate = 1;
+  bk.flags = nullptr;
+  launch_back_subst(bk, pl.d, ctx->stream);
 }
 
 // Select+Fit: importance, top-k, gather, then the ridge fit at the selected keys.
 void run_init_topk(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Kz,
                    const float* Y, const float* lse, int* idx, float* Kc, float* Vc, int* flags,
-                   LbState* st, void* ws) {
+                   LbState* st, void* ws, bool refine = false) {
   ImpArgs ia{};
   ia.Q = Q; ia.Kz = Kz; ia.lse = lse;
   ia.Mpart = at<float>(ws, pl.r_imp);
@@ -326,7 +350,8 @@ void run_init_topk(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
   launch_topk(ta, ctx->stream);
   launch_fill_f32(Vc, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
   run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
-  run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws);
+  const RefineIn rin{Q, lse, Kc};
+  run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws, refine ? &rin : nullptr);
 }
 
 constexpr int kAll = kAllStates;
@@ -723,7 +748,8 @@ kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, cons
   kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
   run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
-  run_value_solve(ctx, pl, b, Y, Vc, flags, nullptr, 0, ws);
+  const RefineIn rin{Q, lse, Kc};
+  run_value_solve(ctx, pl, b, Y, Vc, flags, nullptr, 0, ws, &rin);
   return hip_check(ctx, fn);
 }
 
@@ -742,7 +768,7 @@ kvs_status kvs_init_topk(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
   Plan pl;
   kvs_status s = prepare(ctx, fn, b, nullptr, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
-  run_init_topk(ctx, pl, b, Q, Kz, Y, lse, idx, Kc, Vc, flags, nullptr, ws);
+  run_init_topk(ctx, pl, b, Q, Kz, Y, lse, idx, Kc, Vc, flags, nullptr, ws, true);
   return hip_check(ctx, fn);
 }
 

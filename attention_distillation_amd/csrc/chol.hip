@@ -558,7 +558,8 @@ __global__ __launch_bounds__(256) void back_subst_kernel(BackArgs a) {
   if (ok) {
     for (int e = tid; e < pi.k * 16; e += 256) {
       const int row = e >> 4, c = e & 15;
-      a.Vc[(size_t)(pi.koff + row) * D + dim0 + c] = W[(size_t)row * 16 + c];
+      float* v = a.Vc + (size_t)(pi.koff + row) * D + dim0 + c;
+      *v = a.accumulate ? *v + W[(size_t)row * 16 + c] : W[(size_t)row * 16 + c];
     }
   }
   if (blockIdx.x == 0 && tid == 0 && !ok) {
@@ -668,7 +669,8 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
   if (ok) {
     for (int e = tid; e < pi.k * 16; e += 256) {
       const int row = e >> 4, c = e & 15;
-      a.Vc[(size_t)(pi.koff + row) * D + dim0 + c] = Wl[row * 16 + c];
+      float* v = a.Vc + (size_t)(pi.koff + row) * D + dim0 + c;
+      *v = a.accumulate ? *v + Wl[row * 16 + c] : Wl[row * 16 + c];
     }
   }
   if (blockIdx.x == 0 && tid == 0 && !ok) {

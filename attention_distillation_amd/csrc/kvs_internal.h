@@ -176,10 +176,29 @@ struct BackArgs {
   const float* M; float* X; const float* Dinv; float* Vc; const int* info_out; int* flags;
   LbState* st; int active_mask;
   const ProbInfo* info; int P, d, kpadmax;
-  int lds_max;   // dynamic LDS bytes a workgroup may use (0: solve in global memory)
+  int lds_max;      // dynamic LDS bytes a workgroup may use (0: solve in global memory)
+  int accumulate;   // 0: Vc = X; 1: Vc += X (refinement correction)
 };
 size_t back_subst_lds_bytes(int kpadmax);
 void launch_back_subst(const BackArgs& a, int d, hipStream_t s);
+
+// Refinement step of the value solve: fp64 partials of A^T G per query split
+// ([Cr][kpadtot][d], problem p at xoff), then r and the forward substitution
+// L Z = r, Z written into the A^T Y rows of M.
+struct RhsArgs {
+  const float* St; const float* e; const float* G;
+  const ProbInfo* info; double* Rpart;
+  long long xtot;   // kpadtot * d
+  int P, n, Cr, kpadmax;
+};
+struct FsubArgs {
+  const double* Rpart; long long xtot; int Cr;
+  const double* mu; const float* Vc; float* M; const float* Dinv; float* X;
+  const int* info_out; const ProbInfo* info; int P, kpadmax, lds_max;
+};
+int refine_splits(int P, int kpadmax, int n);
+void launch_resid_rhs(const RhsArgs& a, int d, hipStream_t s);
+void launch_fwd_subst(const FsubArgs& a, int d, hipStream_t s);
 
 struct ImpArgs {
   const float* Q; const float* Kz; const float* lse;

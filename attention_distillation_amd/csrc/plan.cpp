@@ -95,6 +95,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   const long long gtiles = (long long)KT * (KT + 1) / 2 + (long long)(p.d / kTile) * KT;
   p.Cg = split_for((long long)p.P * gtiles, (int)qtiles);
   p.Cq = split_for((long long)p.P * ((p.Z + 63) / 64), (int)qtiles);
+  p.Crf = refine_splits(p.P, p.kpadmax, p.n);
   p.nblk = merge_blocks(p.n);
   p.nchv = vec_chunks((long long)p.kmax * p.d);
   p.nchd = dots_chunks((long long)p.kmax * p.d);
@@ -131,6 +132,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_cinfo, sizeof(int) * p.P);
   take(p.r_X, f * (size_t)p.kpadtot * p.d);
   take(p.r_Dinv, f * (size_t)p.kpadtot * kTile);
+  take(p.r_R, sizeof(double) * (size_t)p.Crf * p.kpadtot * p.d);
   take(p.r_imp, f * 2 * (size_t)p.Cq * p.P * p.Z);
   take(p.r_idx, sizeof(int) * (size_t)p.ktot);
   take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nchd * kDots);

@@ -15,12 +15,12 @@ struct Region {
 struct Plan {
   int P = 0, d = 0, Z = 0, n = 0, npad = 0, kmax = 0, kpadmax = 0, H = 10;
   long long ktot = 0, kpadtot = 0, mtot = 0, stot = 0;
-  int Cref = 1, C = 1, Cn = 1, Cg = 1, Cq = 1, nblk = 1, nchv = 1, nchd = 1;
+  int Cref = 1, C = 1, Cn = 1, Cg = 1, Cq = 1, Crf = 1, nblk = 1, nchv = 1, nchd = 1;
   std::vector<ProbInfo> info;
   // workspace regions
   Region r_info, r_state, r_status, r_yref, r_lseref, r_St, r_Opart, r_Mpart, r_Lpart, r_G, r_e,
       r_crow, r_part, r_dK, r_grad, r_Mg, r_M, r_tr, r_mu, r_cinfo, r_X, r_imp, r_hpart, r_g, r_p, r_Kt,
-      r_S, r_Yh, r_idx, r_flags, r_loss, r_Kc, r_Vc, r_cnt, r_Dinv;
+      r_S, r_Yh, r_idx, r_flags, r_loss, r_Kc, r_Vc, r_cnt, r_Dinv, r_R;
   size_t ws_bytes = 0;
   // persistent L-BFGS state buffer (kvs_lbfgs_* calls)
   Region s_state, s_g, s_p, s_S, s_Yh;

@@ -113,8 +113,8 @@ kvs_status kvs_reference_attn(kvs_ctx ctx, const kvs_batch* b, const float* Q,
  * Initialization).  importance_j = sum_i exp(scale*q_i.kz_j - lse_i); the
  * k_p largest (ties to the lower position) are taken in ascending position
  * order: idx [sum k] int32 (positions within the problem's zone), Kc = Kz[idx],
- * then Vc = ridge solve at Kc (see kvs_value_solve).  flags [P] device int32
- * gets KVS_FLAG_CHOLESKY where the solve failed (Vc then zero). */
+ * then Vc = ridge solve at Kc, refined as in kvs_value_solve.  flags [P]
+ * device int32 gets KVS_FLAG_CHOLESKY where the solve failed (Vc then zero). */
 kvs_status kvs_init_topk(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Kz,
                          const float* Y, const float* lse, int32_t* idx, float* Kc,
                          float* Vc, int32_t* flags, void* ws, size_t ws_bytes);
@@ -131,11 +131,17 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
 /* Closed-form values (gist page, "Optimization Strategy", Value Optimization:
  * ridge regression given the attention weights of the current keys):
  * A = softmax(scale Q Kc^T), mu = ridge_rel * trace(A^T A) / k,
- * (A^T A + mu I) Vc = A^T Y by Cholesky and two triangular solves.
+ * (A^T A + mu I) Vc = A^T Y by Cholesky and two triangular solves, then one
+ * step of iterative refinement: r = A^T (Y - A Vc) - mu Vc accumulated in
+ * fp64 across 64-query tiles, Vc += (L L^T)^-1 r with the same factor (the
+ * fp32 solve alone is off by up to 1e-3 relative when mu is small against
+ * the largest eigenvalue of A^T A, e.g. k close to Z, or k > n).
  * lse [P][n] is only used as a per-row shift of the scores (it does not
  * change A); NULL means no shift.  flags [P] (device, may be NULL) gets
  * KVS_FLAG_CHOLESKY where the factorisation failed; Vc of that problem is
- * left unchanged. */
+ * left unchanged.  The value re-solves inside kvs_compress skip the
+ * refinement step (the loss is first-order insensitive to Vc there, up to
+ * a factor mu). */
 kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
                            const float* lse, const float* Kc, float* Vc, int32_t* flags,
                            void* ws, size_t ws_bytes);

@@ -1,4 +1,9 @@
-"""GPU parity: closed-form ridge value solve through the C ABI (bar 1e-4)."""
+"""GPU parity: closed-form ridge value solve through the C ABI (bar 1e-4).
+
+The call refines its fp32 solve once against an fp64-accumulated residual, so
+the bar holds for ill-conditioned systems too: large k at small mu, and more
+pairs than training queries (A^T A rank deficient, only mu keeps it definite).
+"""
 import numpy as np
 import pytest
 
@@ -46,16 +51,19 @@ CASES = {
     "llama3-8b-k2381": (WORKLOADS[3], lambda p, Z: 2381, 0.0, [0]),
     "llama3-8b-k2600": (WORKLOADS[3], lambda p, Z: 2600, 0.0, [5]),
     # twelve full-cache heads with ragged k (odd tile counts, k = 1, k = 64):
-    # a batch large enough for the 128x128 Gram tiles
+    # a batch large enough for the 128x128 Gram tiles.  Heads 8 and 11 are
+    # ill-conditioned (lambda_max / mu ~ 2e4 .. 6e4): without the refinement step
+    # the fp32 solve is off by 1e-4 .. 3e-4 there
     "full-cache-12-ragged": (WORKLOADS[2],
-                             lambda p, Z: [960, 897, 64, 1, 700, 513, 959, 130, 300, 400, 257, 77][p],
+                             lambda p, Z: [960, 897, 64, 1, 700, 513, 959, 130, 960, 400, 257, 1000][p],
                              0.0, list(range(12))),
+    # the largest k the pilot hands out on this cache (k = Z - 20 and k = Z):
+    # unrefined errors near 1e-3
+    "full-cache-k1900-k1920": (WORKLOADS[2], lambda p, Z: [1900, 1920][p], 0.0, [20, 33]),
 }
 
 
-@pytest.mark.parametrize("name", [pytest.param(c, marks=pytest.mark.xfail(
-    reason="fp32 Cholesky loses accuracy when k > n (rank-deficient Gram)", strict=False))
-    if c == "rank-deficient" else c for c in CASES])
+@pytest.mark.parametrize("name", list(CASES))
 def test_value_solve_matches_oracle(name):
     w, kfun, pert, *sel = CASES[name]
     b, probs = _setup(w, kfun, pert, problems=sel[0] if sel else None)
