@@ -17,7 +17,9 @@ step just before the optimizer); the metric is training queries built per
 second.  With --row use it is one kvs_use_eval call: held-out future
 queries over the full and the compressed cache (the step just after the
 optimizer); the metric is held-out queries evaluated per second.  Both
-default to the 56-problem full-cache workload (--config 2).  --row adam runs
+default to the 56-problem full-cache workload (--config 2), as does --row
+solve: one standalone kvs_value_solve at the Select+Fit keys (Gram,
+Cholesky, triangular solves, the refinement step).  --row adam runs
 the schedule with Adam on the keys and reports its final output MSE over
 L-BFGS's; --row restarts runs R random restarts of one problem as one batch
 (kvs_compress_from_keys) and reports the single Select+Fit run's final loss
@@ -65,17 +67,22 @@ def mixed_fwd_peak():
     return 1.0 / (0.5 / PEAK_FP64_MFMA + 0.5 / PEAK_FP32_MFMA)
 
 
-# HBM bytes per launch of a kernel, from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE on the default bench workload, each scaled by the ratio of a
+# HBM bytes per launch of a kernel on one workload (bench row), from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE, each scaled by the ratio of a
 # plain copy's known bytes to what the same counter reads for it.  Valid only
-# for the kernel source they were taken on (sha256 of that file).
+# for that kernel source (sha256 of the file) and that workload: other
+# workloads report null.
 MEASURED_TRAFFIC = {
-    # qwen2.5-1.5b-full-cache training queries: FETCH 53517.7 KiB x 1.99978
-    # + WRITE 107520.0 KiB x 1.00000 per dispatch
-    "build_queries": {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
-    # qwen2.5-1.5b-one-layer, loss-mode forward: FETCH 9626.8 KiB x 1.99978
-    # + WRITE 52500.0 KiB x 1.00000 per dispatch
-    "attn_fwd": {"bytes": 73473514, "source": "attn_fwd.hip", "sha": "b27ce2ca39f20c44"},
+    # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
+    ("build_queries", "qwen2.5-1.5b-full-cache"):
+        {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
+    # loss-mode forward: FETCH 9626.8 KiB x 1.99978 + WRITE 52500.0 KiB x 1.00000 per dispatch
+    ("attn_fwd", "qwen2.5-1.5b-one-layer"):
+        {"bytes": 73473514, "source": "attn_fwd.hip", "sha": "b27ce2ca39f20c44"},
+    # standalone value solve, 128x128 Gram tiles: FETCH 2386981.1 KiB x 1.99978
+    # + WRITE 134400.0 KiB x 1.00000 per dispatch
+    ("gram", "qwen2.5-1.5b-full-cache solve"):
+        {"bytes": 5025617564, "source": "gram.hip", "sha": "e704efe4848c8b3c"},
 }
 
 
@@ -86,8 +93,8 @@ def source_sha(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(kernel):
-    t = MEASURED_TRAFFIC.get(kernel)
+def traffic_for(kernel, workload):
+    t = MEASURED_TRAFFIC.get((kernel, workload))
     if t is None or source_sha(t["source"]) != t["sha"]:
         return None
     return t["bytes"]
@@ -208,7 +215,7 @@ def bench_queries(args, torch, K):
     achieved = bytes_launch / avg_s
     roofline = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
-                "traffic": traffic_for("build_queries"), "kernel": "build_queries",
+                "traffic": traffic_for("build_queries", w.name), "kernel": "build_queries",
                 "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
     cpu = None if args.no_cpu_baseline else cpu_queries(w, b, min(args.cpu_seconds, 10.0))
     out = {
@@ -279,7 +286,7 @@ def bench_use(args, torch, K):
     peak = mixed_fwd_peak()
     roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic_for("use_attn_fwd"), "kernel": "use_attn_fwd",
+                "traffic": traffic_for("use_attn_fwd", w.name), "kernel": "use_attn_fwd",
                 "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
     log(f"[bench] use-side rel error per problem: {rl.cpu().numpy()[:8].tolist()} ...")
     cpu = None if args.no_cpu_baseline else cpu_use(w, u, Kc, Vc, k, min(args.cpu_seconds, 10.0))
@@ -297,13 +304,91 @@ def bench_use(args, torch, K):
     print(json.dumps(out), flush=True)
 
 
-def _fwd_roofline(stats):
+def cpu_solve(w, hb, Kc, k, seconds):
+    """Float64 oracle of the ridge value solve on whole problems."""
+    from oracle import kvsculpt as O
+    P = hb["Q"].shape[0]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        p = done % P
+        O.ridge_values(hb["Q"][p], hb["Y"][p], Kc[p * k:(p + 1) * k], hb["scale"])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "problem-solves/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{w.name}: {done} problems' ridge solves (n={hb['Q'].shape[1]}, k={k}, "
+                      f"d={w.d}), float64 NumPy/SciPy"}
+
+
+def bench_solve(args, torch, K):
+    """The standalone ridge value solve at the Select+Fit keys: scores, Gram with the
+    A^T Y rows, Cholesky, back substitution and the refinement step."""
+    from synth import WORKLOADS, make_batch
+    w = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {w.name}: P={w.P} n={w.n} Z={w.Z} d={w.d} k0={w.k0}")
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z, k = b["Kz"].shape[1], w.k0
+    Q = torch.from_numpy(b["Q"]).to(dev)
+    Kz = torch.from_numpy(b["Kz"]).to(dev)
+    Vz = torch.from_numpy(b["Vz"]).to(dev)
+    ctx = K.Context()
+    bt = K.Batch(P, d, Z, n, k=[k] * P, scale=b["scale"])
+    ws = torch.empty(K.workspace_bytes(bt), dtype=torch.uint8, device=dev)
+    Y = torch.empty((P, n, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((P, n), dtype=torch.float32, device=dev)
+    K.kvs_reference_attn(ctx, bt, Q, Kz, Vz, Y, lse, ws)
+    idx = torch.empty(P * k, dtype=torch.int32, device=dev)
+    Kc = torch.empty((P * k, d), dtype=torch.float32, device=dev)
+    Vc = torch.empty((P * k, d), dtype=torch.float32, device=dev)
+    flags = torch.zeros(P, dtype=torch.int32, device=dev)
+    K.kvs_init_topk(ctx, bt, Q, Kz, Y, lse, idx, Kc, Vc, flags, ws)
+    log("[bench] Select+Fit keys ready")
+
+    def step():
+        K.kvs_value_solve(ctx, bt, Q, Y, lse, Kc, Vc, flags, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    elapsed = timed_pass(torch, step, args.steps)
+    st = event_pass(torch, K, ctx, ["gram"], step, args.steps)["gram"]
+    avg_s = st["ms"] / st["launches"] / 1e3
+    achieved = st["flops"] / st["launches"] / avg_s
+    roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3),
+                "peak": round(PEAK_FP32_MFMA / 1e12, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": traffic_for("gram", w.name + " solve"),
+                "kernel": "gram", "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
+    log(f"[bench] flags {int(flags.ne(0).sum().item())} of {P} problems set")
+    cpu = None
+    if not args.no_cpu_baseline:
+        hb = {"Q": b["Q"], "Y": Y.cpu().numpy(), "scale": b["scale"]}
+        cpu = cpu_solve(w, hb, Kc.cpu().numpy(), k, min(args.cpu_seconds, 15.0))
+    out = {
+        "metric": "ridge value solves/sec (Gram, Cholesky, triangular solves, one refinement step)",
+        "value": round(P * args.steps / elapsed, 2), "unit": "problem-solves/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (scores f64, residual f64)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "row": "solve", "problems": P, "n": n, "Z": Z, "k": k, "d": d,
+                   "keys": "Select+Fit"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _fwd_roofline(stats, workload):
     st = stats["attn_fwd"]
     avg_s = st["ms"] / st["launches"] / 1e3
     achieved = st["flops"] / st["launches"] / avg_s
     peak = mixed_fwd_peak()
     return {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
-            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_for("attn_fwd"),
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": traffic_for("attn_fwd", workload),
             "kernel": "attn_fwd", "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
 
 
@@ -388,7 +473,7 @@ def bench_adam(args, torch, K):
         "config": {"workload": w.name, "row": "adam", "problems": P, "n": n, "Z": w.Z,
                    "k": w.k0, "iters": T, "vc_every": 5, "lr": args.adam_lr,
                    "mse_adam_over_lbfgs": [round(r, 3) for r in ratio]},
-        "roofline": _fwd_roofline(stats),
+        "roofline": _fwd_roofline(stats, w.name),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -449,7 +534,7 @@ def bench_restarts(args, torch, K):
         "config": {"workload": w.name, "row": "restarts", "problem": 0, "restarts": R, "n": n,
                    "Z": w.Z, "k": w.k0, "iters": T,
                    "single_run_over_best_restart": round(single / best, 4)},
-        "roofline": _fwd_roofline(stats),
+        "roofline": _fwd_roofline(stats, f"{w.name} x{R} restarts"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -486,7 +571,7 @@ def bench_alloc(args, torch, K):
     nbytes = float(w3.P) * w3.Z * w3.d * 4
     roofline = {"bound": "hbm", "achieved": round(nbytes / avg_s / 1e9, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(nbytes / avg_s / PEAK_HBM, 4),
-                "traffic": traffic_for("value_norms"), "kernel": "value_norms (+ final sum)",
+                "traffic": traffic_for("value_norms", "llama3-8b zone"), "kernel": "value_norms (+ final sum)",
                 "launches": reps, "avg_us": round(avg_s * 1e6, 2)}
     cpu = None
     if not args.no_cpu_baseline:
@@ -614,7 +699,7 @@ def bench_vector(args, torch, K):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{w.name} problems 0..{P - 1}", "row": "vector", "n": n,
                    "Z": w.Z, "k": w.k0, "iters": T},
-        "roofline": _fwd_roofline(stats),
+        "roofline": _fwd_roofline(stats, f"{w.name} slice of {P}"),
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -631,11 +716,12 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--row", choices=["compress", "queries", "use", "adam", "restarts", "alloc",
-                                      "vector"],
+    ap.add_argument("--row", choices=["compress", "queries", "use", "solve", "adam", "restarts",
+                                      "alloc", "vector"],
                     default="compress",
                     help="compress: the optimizer (default); queries: training-query "
-                         "construction; use: use-side evaluation; adam / restarts: the "
+                         "construction; use: use-side evaluation; solve: the standalone "
+                         "ridge value solve; adam / restarts: the "
                          "optimizer ablations; alloc: allocation variants; vector: the "
                          "schedule on a 64-problem llama3-8b slice (vector-kernel sizing)")
     ap.add_argument("--adam-lr", type=float, default=1e-2)
@@ -644,7 +730,7 @@ def main():
                     help="only run plain device copies of this size (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.config is None:
-        args.config = 2 if args.row in ("queries", "use", "alloc") else 1
+        args.config = 2 if args.row in ("queries", "use", "solve", "alloc") else 1
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the problems of a batch are independent and this build "
             "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
@@ -661,6 +747,9 @@ def main():
         return
     if args.row == "use":
         bench_use(args, torch, K)
+        return
+    if args.row == "solve":
+        bench_solve(args, torch, K)
         return
     if args.row == "adam":
         bench_adam(args, torch, K)
@@ -773,7 +862,7 @@ def main():
     peak = mixed_fwd_peak() if name == "attn_fwd" else PEAK_FP32_MFMA
     achieved = fl_launch / avg_s
     roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_for(name),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_for(name, w.name if args.ratio is None else None),
                 "kernel": name, "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2),
                 "timed": f"second timed pass of {args.steps} steps with per-launch HIP events "
                          f"({1e3 * elapsed_events / args.steps:.2f} ms per step)"}
