@@ -167,6 +167,10 @@ kvs_status prepare(kvs_ctx ctx, const char* fn, const kvs_batch* b, const kvs_op
     return fail(ctx, KVS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, pl->ws_bytes);
   launch_write_info(at<ProbInfo>(ws, pl->r_info), pl->info.data(), pl->P, ctx->stream);
   launch_fill_i32(at<int>(ws, pl->r_cnt), 0, 2LL * pl->P, ctx->stream);
+  CholArgs c{};
+  c.info = at<ProbInfo>(ws, pl->r_info); c.coff = at<int>(ws, pl->r_coff);
+  c.P = pl->P; c.kpadmax = pl->kpadmax;
+  launch_chol_offsets(c, pl->d, ctx->stream);
   return KVS_OK;
 }
 
@@ -296,12 +300,12 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   CholArgs c{};
   c.M = M; c.Dinv = at<float>(ws, pl.r_Dinv); c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
   c.st = sel; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
-  c.ridge_rel = b->ridge_rel;
+  c.ridge_rel = b->ridge_rel; c.coff = at<int>(ws, pl.r_coff);
   launch_mu(c, ctx->stream);
   const int KT = pl.kpadmax / kTile;
   for (int j = -1; j < KT; ++j) {
     Prof pr(ctx, PROF_POTRF, 0, 0);
-    launch_chol_step(c, pl.d, j, ctx->stream);
+    launch_chol_step(c, pl.d, j, pl.chol_wgs[j + 1], ctx->stream);
   }
   BackArgs bk{};
   bk.M = M; bk.X = at<float>(ws, pl.r_X); bk.Dinv = c.Dinv; bk.Vc = Vc;

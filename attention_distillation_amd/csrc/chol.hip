@@ -115,7 +115,8 @@ __device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (
 
 // Launch j of the right-looking factorisation with look-ahead (j = -1 .. KT-1),
 // all problems of the batch at once:
-//  - panel workgroups: row tile I = j+1+blockIdx.x of column block j.  Each
+//  - panel workgroups: row tile I = j+1+w of column block j (w: the
+//    workgroup's index within its problem's range of the grid).  Each
 //    applies the update of panel j-1 to its tile, solves it against L_jj by
 //    one MFMA product with inv(L_jj) (computed one launch earlier), stores
 //    L_Ij in place and subtracts L_Ij L_Ij^T from its row's diagonal tile
@@ -127,13 +128,27 @@ __device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (
 //    -1 does only this for block 0.
 //  - trailing workgroups: the update of panel j-1 for the tiles (I, J) with
 //    I > J >= j+1 (diagonal tiles are left to the panel workgroups).
+// The grid of launch j lists only the workgroups that have work: problem p
+// owns [coff[j+1][p], coff[j+1][p+1]), its panel rows first, then its
+// trailing tiles (a ragged batch would otherwise launch the largest
+// problem's square of tiles for every problem).
 template <int D>
-__global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int Rmax, int nJ) {
-  const int p = blockIdx.y;
+__global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
+  const int* __restrict__ off = a.coff + (size_t)(j + 1) * (a.P + 1);
+  const int x = blockIdx.x;
+  int lo = 0, hi = a.P;           // largest lo with off[lo] <= x (off[P] > x)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  const int p = lo;
   if (!chol_active(a.st, a.active_mask, p)) return;
   const ProbInfo pi = a.info[p];
   const int KT = pi.kpad / 64, RT = KT + D / 64;
   if (j >= KT) return;
+  const int wid = x - off[p];                      // workgroup within the problem
+  const int npanel = chol_panel_wgs(KT, D / 64, j);
   const int ld = pi.kpad;
   float* __restrict__ Mp = a.M + pi.moff;
   float* __restrict__ Dinv = a.Dinv + (size_t)pi.xoff / D * 64;   // [KT][64][64]
@@ -141,12 +156,26 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
   auto rowof = [&](int I) { return (I < KT) ? 64 * I : pi.kpad + 64 * (I - KT); };
 
-  if ((int)blockIdx.x >= Rmax) {
-    // trailing update from panel j-1
-    if (j <= 0) return;
-    const int t = blockIdx.x - Rmax;
-    const int I = j + 1 + t / nJ, J = j + 1 + t % nJ;
-    if (J >= KT || I >= RT || J >= I) return;   // diagonal tiles: panel workgroups
+  if (wid >= npanel) {
+    // trailing update from panel j-1: strictly lower tiles among the
+    // columns j+1 .. KT-1 row by row, then the value rows (diagonal tiles
+    // are left to the panel workgroups)
+    const int nj = KT - j - 1;
+    const int u = wid - npanel;
+    const int ntri = nj * (nj - 1) / 2;
+    int I, J;
+    if (u < ntri) {
+      int i = (int)((sqrt(8.0 * (double)u + 1.0) + 1.0) * 0.5);   // i (i - 1) / 2 <= u < i (i + 1) / 2
+      while (i * (i - 1) / 2 > u) --i;
+      while (i * (i + 1) / 2 <= u) ++i;
+      I = j + 1 + i;
+      J = j + 1 + (u - i * (i - 1) / 2);
+    } else {
+      const int v = u - ntri;
+      I = KT + v / nj;
+      J = j + 1 + v % nj;
+    }
+    if (J >= KT || I >= RT || J >= I) return;   // not reached: the count lists only these
     f32x4 acc[2][2];
     tile_aat(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
 #pragma unroll
@@ -161,7 +190,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
     return;
   }
 
-  const int I = j + 1 + blockIdx.x;
+  const int I = j + 1 + wid;
   if (I >= RT) return;
   const bool look = (I == j + 1) && (I < KT);
   __shared__ float Tl[64][68];      // panel tile, then L_Ij
@@ -470,14 +499,48 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j, int R
   if (tid == 0 && badcol >= 0 && a.info_out[p] == 0) a.info_out[p] = 64 * I + badcol + 1;
 }
 
-void launch_chol_step(const CholArgs& a, int d, int j, hipStream_t s) {
-  const int KT = a.kpadmax / 64, RT = KT + d / 64;
-  const int Rmax = (j < 0) ? 1 : RT - j - 1;
-  const int nI = RT - j - 1, nJ = KT - j - 1;
-  const int ntrail = (j > 0 && nI > 0 && nJ > 0) ? nI * nJ : 0;
-  dim3 grid(Rmax + ntrail, a.P);
-  if (d == 128) hipLaunchKernelGGL((chol_step_kernel<128>), grid, dim3(256), 0, s, a, j, Rmax, nJ > 0 ? nJ : 1);
-  else hipLaunchKernelGGL((chol_step_kernel<64>), grid, dim3(256), 0, s, a, j, Rmax, nJ > 0 ? nJ : 1);
+// coff rows for every launch j = -1 .. KTmax-1: one workgroup per launch, an
+// exclusive scan of the per-problem workgroup counts (each thread sums a
+// contiguous segment of problems, the segment totals are scanned in LDS).
+template <int D>
+__global__ __launch_bounds__(256) void chol_offsets_kernel(CholArgs a) {
+  const int j = (int)blockIdx.x - 1, tid = threadIdx.x;
+  int* off = a.coff + (size_t)blockIdx.x * (a.P + 1);
+  const int seg = (a.P + 255) / 256;
+  const int p0 = min(a.P, tid * seg), p1 = min(a.P, p0 + seg);
+  auto count = [&](int p) {
+    const int KT = a.info[p].kpad / 64;
+    return chol_panel_wgs(KT, D / 64, j) + chol_trail_wgs(KT, D / 64, j);
+  };
+  int sum = 0;
+  for (int p = p0; p < p1; ++p) sum += count(p);
+  __shared__ int sc[256];
+  sc[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  int run = sc[tid] - sum;          // exclusive prefix of this segment
+  for (int p = p0; p < p1; ++p) {
+    off[p] = run;
+    run += count(p);
+  }
+  if (tid == 255) off[a.P] = sc[255];
+}
+
+void launch_chol_offsets(const CholArgs& a, int d, hipStream_t s) {
+  dim3 grid(a.kpadmax / 64 + 1);
+  if (d == 128) hipLaunchKernelGGL((chol_offsets_kernel<128>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((chol_offsets_kernel<64>), grid, dim3(256), 0, s, a);
+}
+
+void launch_chol_step(const CholArgs& a, int d, int j, int wgs, hipStream_t s) {
+  if (wgs <= 0) return;
+  if (d == 128) hipLaunchKernelGGL((chol_step_kernel<128>), dim3(wgs), dim3(256), 0, s, a, j);
+  else hipLaunchKernelGGL((chol_step_kernel<64>), dim3(wgs), dim3(256), 0, s, a, j);
 }
 
 // Solve L^T X = W for 16 value columns per workgroup, 64-row blocks from the

@@ -168,9 +168,23 @@ struct CholArgs {
   float* M; float* Dinv; const double* trpart; double* mu; int* info_out;
   const LbState* st; int active_mask;
   const ProbInfo* info; int P, kpadmax; double ridge_rel;
+  int* coff;   // [kpadmax/64 + 1][P + 1]: first workgroup of each problem in launch j (row j + 1)
 };
+// Workgroups of Cholesky launch j (-1 .. KT-1) for a problem with KT key
+// tiles and DT value-row tiles: the panel rows of column block j (launch -1:
+// the look-ahead of block 0 only), then the trailing tiles (I, J), I > J > j,
+// that take the update of panel j - 1 (lower triangle, then the value rows).
+__host__ __device__ inline int chol_panel_wgs(int KT, int DT, int j) {
+  return j >= KT ? 0 : (j < 0 ? 1 : KT + DT - j - 1);
+}
+__host__ __device__ inline int chol_trail_wgs(int KT, int DT, int j) {
+  if (j <= 0 || j >= KT) return 0;
+  const int nj = KT - j - 1;
+  return nj * (nj - 1) / 2 + DT * nj;
+}
 void launch_mu(const CholArgs& a, hipStream_t s);
-void launch_chol_step(const CholArgs& a, int d, int panel, hipStream_t s);
+void launch_chol_offsets(const CholArgs& a, int d, hipStream_t s);
+void launch_chol_step(const CholArgs& a, int d, int panel, int wgs, hipStream_t s);
 
 struct BackArgs {
   const float* M; float* X; const float* Dinv; float* Vc; const int* info_out; int* flags;

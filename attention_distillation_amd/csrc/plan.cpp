@@ -96,6 +96,17 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p.Cg = split_for((long long)p.P * gtiles, (int)qtiles);
   p.Cq = split_for((long long)p.P * ((p.Z + 63) / 64), (int)qtiles);
   p.Crf = refine_splits(p.P, p.kpadmax, p.n);
+  {
+    const int KTm = p.kpadmax / kTile, DT = p.d / kTile;
+    p.chol_wgs.assign(KTm + 1, 0);
+    for (int j = -1; j < KTm; ++j) {
+      long long t = 0;
+      for (const ProbInfo& q : p.info)
+        t += chol_panel_wgs(q.kpad / kTile, DT, j) + chol_trail_wgs(q.kpad / kTile, DT, j);
+      if (t > 0x7fffffffLL) return "Cholesky launch has too many tiles";
+      p.chol_wgs[j + 1] = (int)t;
+    }
+  }
   p.nblk = merge_blocks(p.n);
   p.nchv = vec_chunks((long long)p.kmax * p.d);
   p.nchd = dots_chunks((long long)p.kmax * p.d);
@@ -133,6 +144,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_X, f * (size_t)p.kpadtot * p.d);
   take(p.r_Dinv, f * (size_t)p.kpadtot * kTile);
   take(p.r_R, sizeof(double) * (size_t)p.Crf * p.kpadtot * p.d);
+  take(p.r_coff, sizeof(int) * (size_t)(p.kpadmax / kTile + 1) * (p.P + 1));
   take(p.r_imp, f * 2 * (size_t)p.Cq * p.P * p.Z);
   take(p.r_idx, sizeof(int) * (size_t)p.ktot);
   take(p.r_hpart, sizeof(double) * (size_t)p.P * p.nchd * kDots);

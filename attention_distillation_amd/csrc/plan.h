@@ -17,10 +17,11 @@ struct Plan {
   long long ktot = 0, kpadtot = 0, mtot = 0, stot = 0;
   int Cref = 1, C = 1, Cn = 1, Cg = 1, Cq = 1, Crf = 1, nblk = 1, nchv = 1, nchd = 1;
   std::vector<ProbInfo> info;
+  std::vector<int> chol_wgs;   // workgroups of Cholesky launch j = -1 .. kpadmax/64 - 1 (index j + 1)
   // workspace regions
   Region r_info, r_state, r_status, r_yref, r_lseref, r_St, r_Opart, r_Mpart, r_Lpart, r_G, r_e,
       r_crow, r_part, r_dK, r_grad, r_Mg, r_M, r_tr, r_mu, r_cinfo, r_X, r_imp, r_hpart, r_g, r_p, r_Kt,
-      r_S, r_Yh, r_idx, r_flags, r_loss, r_Kc, r_Vc, r_cnt, r_Dinv, r_R;
+      r_S, r_Yh, r_idx, r_flags, r_loss, r_Kc, r_Vc, r_cnt, r_Dinv, r_R, r_coff;
   size_t ws_bytes = 0;
   // persistent L-BFGS state buffer (kvs_lbfgs_* calls)
   Region s_state, s_g, s_p, s_S, s_Yh;
