@@ -169,7 +169,7 @@ kvs_status prepare(kvs_ctx ctx, const char* fn, const kvs_batch* b, const kvs_op
   launch_fill_i32(at<int>(ws, pl->r_cnt), 0, 2LL * pl->P, ctx->stream);
   CholArgs c{};
   c.info = at<ProbInfo>(ws, pl->r_info); c.coff = at<int>(ws, pl->r_coff);
-  c.P = pl->P; c.kpadmax = pl->kpadmax;
+  c.P = pl->P; c.kpadmax = pl->kpadmax; c.S = pl->chol_S;
   launch_chol_offsets(c, pl->d, ctx->stream);
   return KVS_OK;
 }
@@ -300,7 +300,7 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   CholArgs c{};
   c.M = M; c.Dinv = at<float>(ws, pl.r_Dinv); c.trpart = r.trpart; c.mu = at<double>(ws, pl.r_mu); c.info_out = at<int>(ws, pl.r_cinfo);
   c.st = sel; c.active_mask = mask; c.info = g.info; c.P = pl.P; c.kpadmax = pl.kpadmax;
-  c.ridge_rel = b->ridge_rel; c.coff = at<int>(ws, pl.r_coff);
+  c.ridge_rel = b->ridge_rel; c.coff = at<int>(ws, pl.r_coff); c.S = pl.chol_S;
   launch_mu(c, ctx->stream);
   const int KT = pl.kpadmax / kTile;
   for (int j = -1; j < KT; ++j) {

@@ -58,10 +58,11 @@ void launch_mu(const CholArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(mu_kernel, dim3(a.P), dim3(64), 0, s, a);
 }
 
-// 64x64 tile product C -= A B^T (A = rows rowA.., B = rows rowB.., both taking
-// columns col0..col0+63 of M), each wave a 32x32 quarter on 16x16x4 fp32 MFMA.
-// Results: acc[ib][jb][r] belongs to row rb + 16 ib + 4 g + r, column
+// 64x64 tile product acc = A B^T (A = rows rowA.., B = rows rowB.., both taking
+// columns col0..col0+16 NT-1 of M), each wave a 32x32 quarter on 16x16x4 fp32
+// MFMA.  Results: acc[ib][jb][r] belongs to row rb + 16 ib + 4 g + r, column
 // cb + 16 jb + lq of the tile.
+template <int NT>
 __device__ __forceinline__ void tile_aat(const float* __restrict__ Mp, int ld, int rowA, int rowB, int col0,
                                          f32x4 (&acc)[2][2]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
@@ -71,7 +72,7 @@ __device__ __forceinline__ void tile_aat(const float* __restrict__ Mp, int ld, i
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
     f32x4 av[2], bv[2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -114,10 +115,14 @@ __device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (
 }
 
 // Launch j of the right-looking factorisation with look-ahead (j = -1 .. KT-1),
-// all problems of the batch at once:
+// all problems of the batch at once.  With S = 2 (large batches) the
+// trailing matrix takes the panels' updates two at a time: launches
+// j = 2, 4, 6, .. apply panels j-2 and j-1 in one read-modify-write of every
+// trailing tile; with S = 1 every launch j >= 1 applies panel j-1.
 //  - panel workgroups: row tile I = j+1+w of column block j (w: the
 //    workgroup's index within its problem's range of the grid).  Each
-//    applies the update of panel j-1 to its tile, solves it against L_jj by
+//    applies to its tile the panels the trailing passes have not (j-1, or
+//    with S = 2 at even j: j-2 and j-1), solves it against L_jj by
 //    one MFMA product with inv(L_jj) (computed one launch earlier), stores
 //    L_Ij in place and subtracts L_Ij L_Ij^T from its row's diagonal tile
 //    (I, I).  Rows below kpad are the A^T Y rows: their panel solves are the
@@ -126,8 +131,9 @@ __device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (
 //    earlier panels are already applied), factors it and writes
 //    inv(L_{j+1,j+1}) for the next launch and the back substitution.  Launch
 //    -1 does only this for block 0.
-//  - trailing workgroups: the update of panel j-1 for the tiles (I, J) with
-//    I > J >= j+1 (diagonal tiles are left to the panel workgroups).
+//  - trailing workgroups: the update of the pending panels for the tiles
+//    (I, J) with I > J >= j+1 (diagonal tiles are left to the panel
+//    workgroups).
 // The grid of launch j lists only the workgroups that have work: problem p
 // owns [coff[j+1][p], coff[j+1][p+1]), its panel rows first, then its
 // trailing tiles (a ragged batch would otherwise launch the largest
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
   auto rowof = [&](int I) { return (I < KT) ? 64 * I : pi.kpad + 64 * (I - KT); };
 
   if (wid >= npanel) {
-    // trailing update from panel j-1: strictly lower tiles among the
+    // trailing update from the pending panels: strictly lower tiles among the
     // columns j+1 .. KT-1 row by row, then the value rows (diagonal tiles
     // are left to the panel workgroups)
     const int nj = KT - j - 1;
@@ -176,17 +182,26 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
       J = j + 1 + v % nj;
     }
     if (J >= KT || I >= RT || J >= I) return;   // not reached: the count lists only these
-    f32x4 acc[2][2];
-    tile_aat(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
+    // the tile itself is loaded first so its latency overlaps the operands'
+    float cv[2][2][4];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* dst = Mp + (size_t)(rowof(I) + rb + 16 * ib + 4 * g + r) * ld + 64 * J + cb + 16 * jb + lq;
-          *dst -= acc[ib][jb][r];
-        }
+        for (int r = 0; r < 4; ++r)
+          cv[ib][jb][r] = Mp[(size_t)(rowof(I) + rb + 16 * ib + 4 * g + r) * ld + 64 * J + cb + 16 * jb + lq];
+    f32x4 acc[2][2];
+    if (a.S == 2) tile_aat<8>(Mp, ld, rowof(I), 64 * J, 64 * (j - 2), acc);
+    else tile_aat<4>(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Mp[(size_t)(rowof(I) + rb + 16 * ib + 4 * g + r) * ld + 64 * J + cb + 16 * jb + lq] =
+              cv[ib][jb][r] - acc[ib][jb][r];
     return;
   }
 
@@ -206,11 +221,13 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
   float dv[2][2][4];
   if (j >= 0) {
     // every global load of the workgroup is issued here, before any use:
-    // the panel tile (I, j), the diagonal tile (I, I), the panel j-1
-    // operands of the panel tile's update, and inv(L_jj) as MFMA B operand
-    const bool upd = j > 0;
+    // the panel tile (I, j), the diagonal tile (I, I), the operands of the
+    // panel tile's update by its np pending panels, and inv(L_jj) as MFMA B
+    // operand
+    const int np = j <= 0 ? 0 : ((a.S == 2 && !(j & 1)) ? 2 : 1);
+    const bool upd = np > 0;
     float tv[2][2][4], dj[16][2];
-    f32x4 av[4][2], bt[4][2];
+    f32x4 av[8][2], bt[8][2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -222,9 +239,10 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
           dv[ib][jb][r] = diag ? Mp[(size_t)(rowI + rr) * ld + 64 * I + cc] : 0.f;
         }
     if (upd) {
-      const int c0 = 64 * (j - 1);
+      const int c0 = 64 * (j - np);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 8; ++t) {
+        if (t >= 4 * np) break;
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
           av[t][ib] = *(const f32x4*)(Mp + (size_t)(rowI + rb + 16 * ib + lq) * ld + c0 + 16 * t + 4 * g);
@@ -245,7 +263,7 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
         for (int e = 0; e < 4; ++e) dj[4 * t4 + e][jb] = v[e];
       }
 
-    // update of panel j-1: T -= L_{I,j-1} L_{j,j-1}^T
+    // update by the pending panels: T -= sum_p L_{I,p} L_{j,p}^T
     f32x4 accT[2][2];
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -253,13 +271,15 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
       for (int jb = 0; jb < 2; ++jb) accT[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (upd) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 8; ++t) {
+        if (t >= 4 * np) break;
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) accT[ib][jb] = mfma_c(av[t][ib][e], bt[t][jb][e], accT[ib][jb]);
+      }
     }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -510,7 +530,7 @@ __global__ __launch_bounds__(256) void chol_offsets_kernel(CholArgs a) {
   const int p0 = min(a.P, tid * seg), p1 = min(a.P, p0 + seg);
   auto count = [&](int p) {
     const int KT = a.info[p].kpad / 64;
-    return chol_panel_wgs(KT, D / 64, j) + chol_trail_wgs(KT, D / 64, j);
+    return chol_panel_wgs(KT, D / 64, j) + chol_trail_wgs(KT, D / 64, j, a.S);
   };
   int sum = 0;
   for (int p = p0; p < p1; ++p) sum += count(p);

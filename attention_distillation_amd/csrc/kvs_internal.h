@@ -169,16 +169,19 @@ struct CholArgs {
   const LbState* st; int active_mask;
   const ProbInfo* info; int P, kpadmax; double ridge_rel;
   int* coff;   // [kpadmax/64 + 1][P + 1]: first workgroup of each problem in launch j (row j + 1)
+  int S;       // panels per trailing pass (1 or 2)
 };
 // Workgroups of Cholesky launch j (-1 .. KT-1) for a problem with KT key
 // tiles and DT value-row tiles: the panel rows of column block j (launch -1:
 // the look-ahead of block 0 only), then the trailing tiles (I, J), I > J > j,
-// that take the update of panel j - 1 (lower triangle, then the value rows).
+// that take the pending panels' update (lower triangle, then the value
+// rows): panel j - 1 at every j >= 1 with S = 1, panels j - 2 and j - 1 at
+// even j >= 2 with S = 2.
 __host__ __device__ inline int chol_panel_wgs(int KT, int DT, int j) {
   return j >= KT ? 0 : (j < 0 ? 1 : KT + DT - j - 1);
 }
-__host__ __device__ inline int chol_trail_wgs(int KT, int DT, int j) {
-  if (j <= 0 || j >= KT) return 0;
+__host__ __device__ inline int chol_trail_wgs(int KT, int DT, int j, int S) {
+  if (j >= KT || (S == 1 ? j < 1 : (j < 2 || (j & 1)))) return 0;
   const int nj = KT - j - 1;
   return nj * (nj - 1) / 2 + DT * nj;
 }

@@ -18,6 +18,7 @@ struct Plan {
   int Cref = 1, C = 1, Cn = 1, Cg = 1, Cq = 1, Crf = 1, nblk = 1, nchv = 1, nchd = 1;
   std::vector<ProbInfo> info;
   std::vector<int> chol_wgs;   // workgroups of Cholesky launch j = -1 .. kpadmax/64 - 1 (index j + 1)
+  int chol_S = 1;              // panels per trailing pass of the Cholesky
   // workspace regions
   Region r_info, r_state, r_status, r_yref, r_lseref, r_St, r_Opart, r_Mpart, r_Lpart, r_G, r_e,
       r_crow, r_part, r_dK, r_grad, r_Mg, r_M, r_tr, r_mu, r_cinfo, r_X, r_imp, r_hpart, r_g, r_p, r_Kt,

@@ -60,6 +60,10 @@ CASES = {
     # the largest k the pilot hands out on this cache (k = Z - 20 and k = Z):
     # unrefined errors near 1e-3
     "full-cache-k1900-k1920": (WORKLOADS[2], lambda p, Z: [1900, 1920][p], 0.0, [20, 33]),
+    # five large ragged heads: about 20k trailing tiles per solve, enough for
+    # the Cholesky to apply two panels per trailing pass
+    "full-cache-5-large": (WORKLOADS[2], lambda p, Z: [1900, 1920, 1850, 1700, 1600][p], 0.0,
+                           [20, 33, 40, 47, 52]),
 }
 
 
