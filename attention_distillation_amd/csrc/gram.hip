@@ -189,7 +189,7 @@ __device__ __forceinline__ bool gram_tile128(long long t, int KT2, int& I2, int&
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gram128_kernel(GramArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gram128_kernel(GramArgs a) {
   unsigned bx, by, bz;
   xcd_block(bx, by, bz);
   const int p = by;
@@ -205,45 +205,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float Ra[128][68];
   __shared__ float Ca[128][68];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
-  const int wr = wave >> 1, wc = wave & 1;     // 64x64 output quadrant of this wave
+  const int wr = wave >> 2, wc = wave & 3;     // rows 64 wr .. +63, columns 32 wc .. +31 of the tile
   const bool yrows = I2 >= KT2;
   const bool diag = !yrows && I2 == J2;
-  // quadrants with nothing to write skip their MFMA work (they still stage)
-  const bool idle = (diag && wr == 0 && wc == 1) || (yrows && 64 * wr >= D) ||
-                    (!yrows && 128 * I2 + 64 * wr >= pi.kpad) || (128 * J2 + 64 * wc >= pi.kpad);
+  // waves with nothing to write skip their MFMA work (they still stage)
+  const bool idle = (diag && wr == 0 && wc >= 2) || (yrows && 64 * wr >= D) ||
+                    (!yrows && 128 * I2 + 64 * wr >= pi.kpad) || (128 * J2 + 32 * wc >= pi.kpad);
   const float* St = a.St + pi.soff;
   const float* E = a.e + (size_t)p * n;
   const float* Y = a.Y + (size_t)p * n * D;
   const int keyR = 128 * I2, keyC = 128 * J2;
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Operand tiles of 64 queries, loads of the next tile issued before the
-  // MFMA work of this one.  Key tiles: element u of a thread (i = tid + 256 u)
+  // MFMA work of this one.  Key tiles: element u of a thread (i = tid + 512 u)
   // is key i / 16, queries 4 (i % 16) .. + 3 (one 16-byte load); value rows:
   // dim i % 128, queries 4 (i / 128) .. + 3 (four 4-byte loads), landing
   // transposed with one 16-byte LDS store.  Keys past k read the last key;
   // queries past qend are zeroed; dims past d are zero.
-  f32x4 pr[8], pc[8], ev;
+  const int qk4 = 4 * (tid & 15);
+  f32x4 pr[4], pc[4], ev;
   auto prefetch = [&](int qt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ev[j] = E[min(qt + 4 * (tid & 15) + j, n - 1)];
+    for (int j = 0; j < 4; ++j) ev[j] = E[min(qt + qk4 + j, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = tid + 256 * u;
-      const int r = i >> 4, q4 = 4 * (i & 15);
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 512 * u;
       if (yrows) {
         const int dim = i & 127, qy = qt + 4 * (i >> 7);
 #pragma unroll
         for (int j = 0; j < 4; ++j) pr[u][j] = dim < D ? Y[(size_t)min(qy + j, n - 1) * D + dim] : 0.f;
       } else {
-        pr[u] = *(const f32x4*)(St + (size_t)min(keyR + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
+        pr[u] = *(const f32x4*)(St + (size_t)min(keyR + (i >> 4), pi.k - 1) * npad + min(qt + qk4, npad - 4));
       }
-      if (!diag) pc[u] = *(const f32x4*)(St + (size_t)min(keyC + r, pi.k - 1) * npad + min(qt + q4, npad - 4));
+      if (!diag) pc[u] = *(const f32x4*)(St + (size_t)min(keyC + (i >> 4), pi.k - 1) * npad + min(qt + qk4, npad - 4));
     }
   };
   auto weights = [&](f32x4 v, int q0) {
@@ -256,20 +256,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int qt = qbeg; qt < qend; qt += 64) {
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = tid + 256 * u;
-      const int r = yrows ? (i & 127) : (i >> 4), q4 = yrows ? 4 * (i >> 7) : 4 * (i & 15);
-      f32x4 v;
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 512 * u;
       if (yrows) {
-        v = pr[u];
+        const int q4 = 4 * (i >> 7);
+        f32x4 v = pr[u];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (qt + q4 + j >= qend) v[j] = 0.f;
+        *(f32x4*)&Ra[i & 127][q4] = v;
       } else {
-        v = weights(pr[u], qt + q4);
+        *(f32x4*)&Ra[i >> 4][qk4] = weights(pr[u], qt + qk4);
       }
-      *(f32x4*)&Ra[r][q4] = v;
-      if (!diag) *(f32x4*)&Ca[i >> 4][4 * (i & 15)] = weights(pc[u], qt + 4 * (i & 15));
+      if (!diag) *(f32x4*)&Ca[i >> 4][qk4] = weights(pc[u], qt + qk4);
     }
     __syncthreads();
     if (qt + 64 < qend) prefetch(qt + 64);
@@ -277,15 +276,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float (*C)[68] = diag ? Ra : Ca;
 #pragma unroll
     for (int qq = 0; qq < 64; qq += 16) {
-      f32x4 av[4], bv[4];
+      f32x4 av[4], bv[2];
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) av[ib] = *(const f32x4*)&Ra[64 * wr + 16 * ib + lq][qq + 4 * g];
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) bv[jb] = *(const f32x4*)&C[64 * wc + 16 * jb + lq][qq + 4 * g];
+      for (int jb = 0; jb < 2; ++jb) bv[jb] = *(const f32x4*)&C[32 * wc + 16 * jb + lq][qq + 4 * g];
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
+        for (int jb = 0; jb < 2; ++jb) {
           acc[ib][jb] = mfma_g(av[ib].x, bv[jb].x, acc[ib][jb]);
           acc[ib][jb] = mfma_g(av[ib].y, bv[jb].y, acc[ib][jb]);
           acc[ib][jb] = mfma_g(av[ib].z, bv[jb].z, acc[ib][jb]);
@@ -298,11 +297,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float* Mout = a.Mpart + (size_t)bz * a.mtot + pi.moff;
   const int ld = pi.kpad;
   const int row0 = yrows ? pi.kpad + 64 * wr : keyR + 64 * wr;
-  const int col0 = keyC + 64 * wc;
+  const int col0 = keyC + 32 * wc;
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + 16 * ib + 4 * g + r;
@@ -318,8 +317,8 @@ void launch_gram(const GramArgs& a, int d, hipStream_t s) {
   const long long T2 = KT2 * (KT2 + 1) / 2 + KT2;
   if ((long long)a.P * T2 * a.Cg >= 512) {
     dim3 grid2((unsigned)T2, a.P, a.Cg);
-    if (d == 128) hipLaunchKernelGGL((gram128_kernel<128>), grid2, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gram128_kernel<64>), grid2, dim3(256), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((gram128_kernel<128>), grid2, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gram128_kernel<64>), grid2, dim3(512), 0, s, a);
     return;
   }
   const long long T = KT * (KT + 1) / 2 + (long long)(d / 64) * KT;
