@@ -79,10 +79,10 @@ MEASURED_TRAFFIC = {
     # loss-mode forward: FETCH 9626.8 KiB x 1.99978 + WRITE 52500.0 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-1.5b-one-layer"):
         {"bytes": 73473514, "source": "attn_fwd.hip", "sha": "b27ce2ca39f20c44"},
-    # standalone value solve, 128x128 Gram tiles: FETCH 2386981.1 KiB x 1.99978
+    # standalone value solve, 128x128 Gram tiles: FETCH 2606685.1 KiB x 1.99978
     # + WRITE 134400.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-1.5b-full-cache solve"):
-        {"bytes": 5025617564, "source": "gram.hip", "sha": "e704efe4848c8b3c"},
+        {"bytes": 5475519395, "source": "gram.hip", "sha": "0a5a0e05b43b778e"},
 }
 
 
