@@ -185,6 +185,42 @@ def test_compress_cfg1_end_to_end():
         assert fg[p] & ~K.KVS_FLAG_NONDESCENT == 0
 
 
+def test_compress_full_cache_ragged_sampled():
+    """kvs_compress on all 56 full-cache heads at ragged k (336 .. 1920, as the
+    pilot hands out), 20 iterations: the launch shapes of the large batches
+    (128-row Gram tiles, two panels per Cholesky trailing pass, the packed
+    Cholesky grid).  Three sampled heads are run through the oracle's
+    compress_problem: init loss within 1e-4, final loss within 2%."""
+    w = WORKLOADS[2]
+    T = 20
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    ks = [336 + (97 * p) % 1585 for p in range(P)]
+    ks[5] = Z
+    o = K.opts(iters=T)
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt, o))
+    kt = sum(ks)
+    Kc, Vc = empty((kt, d)), empty((kt, d))
+    loss, mse, l0 = empty((P,)), empty((P,)), empty((P,))
+    flags = to_gpu(np.zeros(P, np.int32))
+    say(f"[compress full cache] P={P} n={n} k in [{min(ks)}, {max(ks)}] T={T}")
+    K.kvs_compress(ctx, bt, o, to_gpu(b["Q"]), to_gpu(b["Kz"]), to_gpu(b["Vz"]), Kc, Vc, loss, mse, l0,
+                   flags, ws)
+    lg, l0g, fg = host(loss), host(l0), host(flags)
+    assert np.all(np.isfinite(lg)) and np.all(lg <= l0g)
+    for p in (5, 17, 40):
+        r = O.compress_problem(b["Q"][p], b["Kz"][p], b["Vz"][p], ks[p], b["scale"],
+                               O.CompressOptions(iters=T))
+        say(f"   p={p} k={ks[p]} init gpu={l0g[p]:.6g} oracle={r['init_loss']:.6g}; final gpu={lg[p]:.6g} "
+            f"oracle={r['loss']:.6g} ratio={lg[p] / r['loss']:.4f} flags={fg[p]}")
+        assert abs(l0g[p] - r["init_loss"]) <= 1e-4 * r["init_loss"]
+        assert abs(lg[p] - r["loss"]) <= 0.02 * r["loss"]
+        assert fg[p] & ~K.KVS_FLAG_NONDESCENT == 0
+
+
 def test_pilot_allocation_bit_exact():
     w = tiny_workload(d=64, N=300, m=20, g=2, F=30, layers=3, kv_heads=2, k0=40)
     b = make_batch(w, 0)
