@@ -115,14 +115,13 @@ __device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (
 }
 
 // Launch j of the right-looking factorisation with look-ahead (j = -1 .. KT-1),
-// all problems of the batch at once.  With S = 2 (large batches) the
-// trailing matrix takes the panels' updates two at a time: launches
-// j = 2, 4, 6, .. apply panels j-2 and j-1 in one read-modify-write of every
-// trailing tile; with S = 1 every launch j >= 1 applies panel j-1.
+// all problems of the batch at once.  The trailing matrix takes the panels'
+// updates S at a time (S = 1, 2 or 4 by batch size): launches j = S, 2S, ..
+// apply panels j-S .. j-1 in one read-modify-write of every trailing tile.
 //  - panel workgroups: row tile I = j+1+w of column block j (w: the
 //    workgroup's index within its problem's range of the grid).  Each
-//    applies to its tile the panels the trailing passes have not (j-1, or
-//    with S = 2 at even j: j-2 and j-1), solves it against L_jj by
+//    applies to its tile the panels the trailing passes have not
+//    (chol_pending), solves it against L_jj by
 //    one MFMA product with inv(L_jj) (computed one launch earlier), stores
 //    L_Ij in place and subtracts L_Ij L_Ij^T from its row's diagonal tile
 //    (I, I).  Rows below kpad are the A^T Y rows: their panel solves are the
@@ -192,7 +191,8 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
         for (int r = 0; r < 4; ++r)
           cv[ib][jb][r] = Mp[(size_t)(rowof(I) + rb + 16 * ib + 4 * g + r) * ld + 64 * J + cb + 16 * jb + lq];
     f32x4 acc[2][2];
-    if (a.S == 2) tile_aat<8>(Mp, ld, rowof(I), 64 * J, 64 * (j - 2), acc);
+    if (a.S == 4) tile_aat<16>(Mp, ld, rowof(I), 64 * J, 64 * (j - 4), acc);
+    else if (a.S == 2) tile_aat<8>(Mp, ld, rowof(I), 64 * J, 64 * (j - 2), acc);
     else tile_aat<4>(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -224,7 +224,8 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
     // the panel tile (I, j), the diagonal tile (I, I), the operands of the
     // panel tile's update by its np pending panels, and inv(L_jj) as MFMA B
     // operand
-    const int np = j <= 0 ? 0 : ((a.S == 2 && !(j & 1)) ? 2 : 1);
+    const int np = chol_pending(j, a.S);
+    const int np0 = np < 2 ? np : 2;   // the newest two: loaded with the tiles
     const bool upd = np > 0;
     float tv[2][2][4], dj[16][2];
     f32x4 av[8][2], bt[8][2];
@@ -239,10 +240,10 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
           dv[ib][jb][r] = diag ? Mp[(size_t)(rowI + rr) * ld + 64 * I + cc] : 0.f;
         }
     if (upd) {
-      const int c0 = 64 * (j - np);
+      const int c0 = 64 * (j - np0);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if (t >= 4 * np) break;
+        if (t >= 4 * np0) break;
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
           av[t][ib] = *(const f32x4*)(Mp + (size_t)(rowI + rb + 16 * ib + lq) * ld + c0 + 16 * t + 4 * g);
@@ -272,7 +273,32 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
     if (upd) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if (t >= 4 * np) break;
+        if (t >= 4 * np0) break;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accT[ib][jb] = mfma_c(av[t][ib][e], bt[t][jb][e], accT[ib][jb]);
+      }
+    }
+    // older pending panels (S = 4), two at a time
+    for (int e2 = np0; e2 < np; e2 += 2) {
+      const int nq = np - e2 < 2 ? np - e2 : 2;
+      const int c1 = 64 * (j - np + e2 - np0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t >= 4 * nq) break;
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+          av[t][ib] = *(const f32x4*)(Mp + (size_t)(rowI + rb + 16 * ib + lq) * ld + c1 + 16 * t + 4 * g);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+          bt[t][jb] = *(const f32x4*)(Mp + (size_t)(64 * j + cb + 16 * jb + lq) * ld + c1 + 16 * t + 4 * g);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t >= 4 * nq) break;
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib)
 #pragma unroll

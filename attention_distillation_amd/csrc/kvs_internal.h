@@ -175,13 +175,20 @@ struct CholArgs {
 // tiles and DT value-row tiles: the panel rows of column block j (launch -1:
 // the look-ahead of block 0 only), then the trailing tiles (I, J), I > J > j,
 // that take the pending panels' update (lower triangle, then the value
-// rows): panel j - 1 at every j >= 1 with S = 1, panels j - 2 and j - 1 at
-// even j >= 2 with S = 2.
+// rows): at launches j = S, 2S, 3S, .. the S panels j - S .. j - 1 (S = 1, 2
+// or 4).
+__host__ __device__ inline int chol_pending(int j, int S) {
+  // panels that column block j still lacks at launch j: those after the last
+  // trailing pass before it (all earlier ones when there was none)
+  if (j <= 0) return 0;
+  const int m = (j - 1) / S;
+  return m >= 1 ? j - S * m : j;
+}
 __host__ __device__ inline int chol_panel_wgs(int KT, int DT, int j) {
   return j >= KT ? 0 : (j < 0 ? 1 : KT + DT - j - 1);
 }
 __host__ __device__ inline int chol_trail_wgs(int KT, int DT, int j, int S) {
-  if (j >= KT || (S == 1 ? j < 1 : (j < 2 || (j & 1)))) return 0;
+  if (j >= KT || j < S || j % S != 0) return 0;
   const int nj = KT - j - 1;
   return nj * (nj - 1) / 2 + DT * nj;
 }

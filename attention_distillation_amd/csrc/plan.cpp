@@ -97,9 +97,9 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p.Cq = split_for((long long)p.P * ((p.Z + 63) / 64), (int)qtiles);
   p.Crf = refine_splits(p.P, p.kpadmax, p.n);
   {
-    // Two panels per trailing pass halve the trailing read-modify-write;
-    // they add a second panel product to the critical path of every other
-    // launch, which small batches (latency-bound) do not recover.  (Measured:
+    // Two (four) panels per trailing pass halve (quarter) the trailing
+    // read-modify-write; they add panel products to the critical path of
+    // some launches, which small batches (latency-bound) do not recover.  (Measured:
     // 2 problems at k = 960 slower by ~1 us per launch; 56 ragged problems
     // at k <= 1920 and 256 at k <= 4680 faster, 104 -> 82 ms and
     // 3.95 -> 1.92 s of Cholesky per run.)
@@ -107,7 +107,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     long long trail1 = 0;
     for (const ProbInfo& q : p.info)
       for (int j = 1; j < q.kpad / kTile; ++j) trail1 += chol_trail_wgs(q.kpad / kTile, DT, j, 1);
-    p.chol_S = trail1 >= 16384 ? 2 : 1;
+    p.chol_S = trail1 >= 131072 ? 4 : (trail1 >= 16384 ? 2 : 1);
     p.chol_wgs.assign(KTm + 1, 0);
     for (int j = -1; j < KTm; ++j) {
       long long t = 0;

@@ -64,6 +64,12 @@ CASES = {
     # the Cholesky to apply two panels per trailing pass
     "full-cache-5-large": (WORKLOADS[2], lambda p, Z: [1900, 1920, 1850, 1700, 1600][p], 0.0,
                            [20, 33, 40, 47, 52]),
+    # four llama3-8b heads at the largest k the pilot gives there (up to 4680,
+    # n = 5120): ~210k trailing tiles per solve, four panels per trailing
+    # pass; the right-hand sides no longer fit in LDS (global-memory
+    # substitutions)
+    "llama3-8b-4-large": (WORKLOADS[3], lambda p, Z: [4680, 4500, 4200, 3900][p], 0.0,
+                          [0, 9, 77, 200]),
 }
 
 
