@@ -3,7 +3,7 @@
 Every number stored here comes from ``oracle/`` (float64) run on the seeded
 synthetic inputs of ``synth``; nothing is read from the GPU path.
 
-    python tests/golden/make_golden.py cfg1      # config 1, 300 iterations
+    python tests/golden/make_golden.py qwen2.5-1.5b-one-layer    # 300 iterations
 """
 import json
 import os
@@ -30,16 +30,16 @@ def golden_compress(cid: int, iters: int | None = None, seed: int = 0):
             "p": p, "init_loss": r["init_loss"], "final_loss": r["loss"], "mse": r["mse"],
             "flags": r["flags"], "idx": [int(i) for i in r["idx"]],
             "traj": [float(v) for v in r["traj"]], "seconds": time.time() - t0})
-        print(f"config {cid} problem {p}: {r['init_loss']:.6g} -> {r['loss']:.6g} "
+        print(f"{w.name} problem {p}: {r['init_loss']:.6g} -> {r['loss']:.6g} "
               f"({time.time() - t0:.1f} s)", flush=True)
     return out
 
 
 if __name__ == "__main__":
-    which = sys.argv[1] if len(sys.argv) > 1 else "cfg1"
-    cid = int(which.replace("cfg", ""))
+    name = sys.argv[1] if len(sys.argv) > 1 else "qwen2.5-1.5b-one-layer"
+    cid = next(c for c, w in WORKLOADS.items() if w.name == name)
     res = golden_compress(cid)
-    path = os.path.join(HERE, f"oracle_compress_cfg{cid}.json")
+    path = os.path.join(HERE, f"oracle_compress_{name}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print("wrote", path)

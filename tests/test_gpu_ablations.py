@@ -60,8 +60,8 @@ def test_adam_first_step_matches_oracle():
 
 
 ADAM_CASES = {
-    "cfg0": (WORKLOADS[0], 20),
-    "cfg1-40it": (WORKLOADS[1], 40),
+    "single-head-d64": (WORKLOADS[0], 20),
+    "qwen-one-layer-40it": (WORKLOADS[1], 40),
 }
 
 

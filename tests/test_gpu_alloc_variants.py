@@ -30,7 +30,7 @@ def _norms_gpu(Vz):
 
 
 CASES = {
-    "cfg2": (WORKLOADS[2], None),
+    "qwen-full-cache": (WORKLOADS[2], None),
     "tiny-d64-short-zone": (tiny_workload(d=64, N=40, m=8, g=1, F=4, layers=3, kv_heads=2), None),
     "long-context-2-problems": (WORKLOADS[4], [0, 57]),
 }

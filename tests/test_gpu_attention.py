@@ -19,8 +19,8 @@ TOL = 1e-4
 
 def _cases():
     return {
-        "cfg0": (WORKLOADS[0], None),
-        "cfg1": (WORKLOADS[1], None),
+        "single-head-d64": (WORKLOADS[0], None),
+        "qwen-one-layer": (WORKLOADS[1], None),
         "tiny64-ragged": (tiny_workload(d=64, N=80, m=10, g=1, F=40, layers=3, kv_heads=1), None),
         "tiny128-ragged": (tiny_workload(d=128, N=150, m=6, g=3, F=11, layers=1, kv_heads=2), None),
     }
@@ -62,7 +62,7 @@ def _loss_case(name, state):
         Y, l = O.reference_attention(Q, Kz, Vz, s)
         Y32, l32 = Y.astype(np.float32), l.astype(np.float32)
         Z = Kz.shape[0]
-        k = w.k0 if name in ("cfg0", "cfg1") else [1, 17, Z, 33][p % 4]
+        k = w.k0 if name in ("single-head-d64", "qwen-one-layer") else [1, 17, Z, 33][p % 4]
         k = min(k, Z)
         if state == "init":
             idx, Kc, Vc, ok = O.init_select_fit(Q, Kz, Y32, l32, k, s)
@@ -78,8 +78,8 @@ def _loss_case(name, state):
     return w, b, probs
 
 
-LOSS_CASES = [("cfg0", "init"), ("cfg0", "perturbed"), ("cfg0", "t5"), ("cfg0", "t20"),
-              ("cfg1", "init"), ("tiny64-ragged", "init"), ("tiny128-ragged", "perturbed")]
+LOSS_CASES = [("single-head-d64", "init"), ("single-head-d64", "perturbed"), ("single-head-d64", "t5"), ("single-head-d64", "t20"),
+              ("qwen-one-layer", "init"), ("tiny64-ragged", "init"), ("tiny128-ragged", "perturbed")]
 
 
 @pytest.mark.parametrize("name,state", LOSS_CASES)

@@ -46,8 +46,8 @@ def _check_topk(idx_gpu, logimp, k):
 
 
 INIT_CASES = {
-    "cfg0": (WORKLOADS[0], lambda p, Z: 64),
-    "cfg1": (WORKLOADS[1], lambda p, Z: 960),
+    "single-head-d64": (WORKLOADS[0], lambda p, Z: 64),
+    "qwen-one-layer": (WORKLOADS[1], lambda p, Z: 960),
     "tiny-ragged": (tiny_workload(d=64, N=300, m=20, g=2, F=30, layers=2, kv_heads=2),
                     lambda p, Z: [1, 64, 100, 280][p]),
 }
@@ -86,9 +86,9 @@ def test_init_topk_matches_oracle(name):
         off += k
 
 
-@pytest.mark.parametrize("name,steps", [("cfg0", 8), ("cfg1", 4)])
+@pytest.mark.parametrize("name,steps", [("single-head-d64", 8), ("qwen-one-layer", 4)])
 def test_lbfgs_steps_match_oracle(name, steps):
-    w = WORKLOADS[0 if name == "cfg0" else 1]
+    w = WORKLOADS[0 if name == "single-head-d64" else 1]
     b = make_batch(w, 0)
     P, n, d = b["Q"].shape
     Z = b["Kz"].shape[1]
@@ -133,7 +133,7 @@ def test_lbfgs_steps_match_oracle(name, steps):
         assert ek <= 1e-3
 
 
-def test_compress_cfg0_end_to_end():
+def test_compress_single_head_end_to_end():
     w = WORKLOADS[0]
     b = make_batch(w, 0)
     P, n, d = b["Q"].shape
@@ -149,7 +149,7 @@ def test_compress_cfg0_end_to_end():
                    flags, ws)
     lg, mg, l0g, fg = host(loss), host(mse), host(l0), host(flags)
     r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], w.k0, b["scale"], O.CompressOptions(iters=w.T))
-    say(f"[compress cfg0] init gpu={l0g[0]:.6g} oracle={r['init_loss']:.6g}; "
+    say(f"[compress single-head-d64] init gpu={l0g[0]:.6g} oracle={r['init_loss']:.6g}; "
         f"final gpu={lg[0]:.6g} oracle={r['loss']:.6g}; mse gpu={mg[0]:.4e} oracle={r['mse']:.4e} flags={fg[0]}")
     assert abs(l0g[0] - r["init_loss"]) <= 1e-4 * r["init_loss"]
     assert abs(lg[0] - r["loss"]) <= 0.02 * r["loss"]
@@ -160,8 +160,8 @@ def test_compress_cfg0_end_to_end():
     assert abs(Lchk - lg[0]) <= 1e-3 * Lchk
 
 
-def test_compress_cfg1_end_to_end():
-    path = os.path.join(HERE, "golden", "oracle_compress_cfg1.json")
+def test_compress_qwen_one_layer_end_to_end():
+    path = os.path.join(HERE, "golden", "oracle_compress_qwen2.5-1.5b-one-layer.json")
     gold = json.load(open(path))
     w = WORKLOADS[1]
     b = make_batch(w, gold["seed"])
@@ -178,7 +178,7 @@ def test_compress_cfg1_end_to_end():
                    flags, ws)
     lg, l0g, fg = host(loss), host(l0), host(flags)
     for p, g in enumerate(gold["problems"]):
-        say(f"[compress cfg1] p={p} init gpu={l0g[p]:.6g} oracle={g['init_loss']:.6g}; "
+        say(f"[compress qwen2.5-1.5b-one-layer] p={p} init gpu={l0g[p]:.6g} oracle={g['init_loss']:.6g}; "
             f"final gpu={lg[p]:.6g} oracle={g['final_loss']:.6g} ratio={lg[p] / g['final_loss']:.4f} flags={fg[p]}")
         assert abs(l0g[p] - g["init_loss"]) <= 1e-4 * g["init_loss"]
         assert abs(lg[p] - g["final_loss"]) <= 0.02 * g["final_loss"]

@@ -24,8 +24,8 @@ PLANE_TOL = 1e-6
 
 def _cases():
     return {
-        "cfg0-d64": (WORKLOADS[0], None),
-        "cfg1-d128": (WORKLOADS[1], None),
+        "single-head-d64": (WORKLOADS[0], None),
+        "qwen-one-layer-d128": (WORKLOADS[1], None),
         "long-context-d128": (WORKLOADS[4], [0]),
         "tiny-d8": (tiny_workload(d=8, N=40, m=8, g=2, F=6, layers=2, kv_heads=2), None),
         "tiny-d256-ragged": (tiny_workload(d=256, N=70, m=3, g=5, F=13, layers=1, kv_heads=3),

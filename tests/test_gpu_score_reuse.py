@@ -17,13 +17,13 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,w,T", [
-    ("cfg1", WORKLOADS[1], 10),
+    ("qwen-one-layer", WORKLOADS[1], 10),
     ("ragged-d64", tiny_workload(d=64, N=300, m=20, g=2, F=30, layers=2, kv_heads=2, k0=100), 15),
 ])
 def test_loss_after_value_solve_equals_full_forward(name, w, T):
     b = make_batch(w, 0)
     P, n, d = b["Q"].shape
-    ks = [w.k0] * P if name == "cfg1" else [40, 100, 150, 280]
+    ks = [w.k0] * P if name == "qwen-one-layer" else [40, 100, 150, 280]
     bt = K.Batch(P, d, w.Z, n, k=ks, scale=b["scale"])
     o = K.opts(iters=T)            # T a multiple of 5: the call ends with a value solve
     ctx = K.Context()

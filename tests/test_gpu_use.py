@@ -51,7 +51,7 @@ def _run(u, ks, Kc, Vc, m, outputs=True):
 def _cases():
     t64 = tiny_workload(d=64, N=300, m=20, g=3, F=23, layers=3, kv_heads=1)
     return {
-        "cfg1": (WORKLOADS[1], None, None, None),
+        "qwen-one-layer": (WORKLOADS[1], None, None, None),
         "ragged-d64": (t64, None, [5, 117, 280], None),
         "no-retain-d128": (tiny_workload(d=128, N=200, m=0, g=2, F=40, layers=1, kv_heads=2),
                            None, [33, 150], None),

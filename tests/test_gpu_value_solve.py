@@ -35,9 +35,9 @@ def _setup(w, kfun, perturb=0.0, seed=0, problems=None):
 
 
 CASES = {
-    "cfg0": (WORKLOADS[0], lambda p, Z: 64, 0.0),
-    "cfg0-perturbed": (WORKLOADS[0], lambda p, Z: 64, 1e-2),
-    "cfg1": (WORKLOADS[1], lambda p, Z: 960, 0.0),
+    "single-head-d64": (WORKLOADS[0], lambda p, Z: 64, 0.0),
+    "single-head-d64-perturbed": (WORKLOADS[0], lambda p, Z: 64, 1e-2),
+    "qwen-one-layer": (WORKLOADS[1], lambda p, Z: 960, 0.0),
     "tiny64-ragged": (tiny_workload(d=64, N=80, m=10, g=1, F=40, layers=3), lambda p, Z: [1, 17, 70][p], 0.0),
     "tiny128-ragged": (tiny_workload(d=128, N=330, m=10, g=2, F=40, layers=1, kv_heads=3),
                        lambda p, Z: [100, 3, 96][p], 0.0),
