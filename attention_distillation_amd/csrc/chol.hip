@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256) void back_subst_kernel(BackArgs a) {
 // and inv(L_ii) come from global memory, and the L-block loads of a step are
 // issued before its diagonal solve so their latency overlaps it.
 template <int D>
-__global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
+__global__ __launch_bounds__(512) void back_subst_lds_kernel(BackArgs a) {
   extern __shared__ float Wl[];          // [kpadmax][16], then Xs [64][16]
   const int p = blockIdx.y;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
 
   // W[row][c] = M[kpad + dim0 + c][row]: coalesced float4 reads along the row
-  for (int e = tid; e < pi.kpad * 4; e += 256) {
+  for (int e = tid; e < pi.kpad * 4; e += 512) {
     const int c = e / (pi.kpad / 4), r4 = e % (pi.kpad / 4);
     const f32x4 v = *(const f32x4*)(Mp + (size_t)(pi.kpad + dim0 + c) * ld + 4 * r4);
 #pragma unroll
@@ -730,18 +730,20 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) dv[s2] = Di[(4 * s2 + g) * 64 + 16 * wave + lq];
   };
+  // waves 0..3 solve the diagonal block (16 rows each); all eight update
+  const bool dw = wave < 4;
   float dv[16];
-  load_dinv(dv, KT - 1);
-  // the two first L blocks of a step (rb = wave, wave + 4) are loaded while
+  if (dw) load_dinv(dv, KT - 1);
+  // the two first L blocks of a step (rb = wave, wave + 8) are loaded while
   // the previous step finishes, into the registers its updates have freed
   float av0[4][16], av1[4][16];
-  const int rb0 = wave, rb1 = wave + 4;
+  const int rb0 = wave, rb1 = wave + 8;
   if (rb0 < KT - 1) load_block(av0, KT - 1, rb0);
   if (rb1 < KT - 1) load_block(av1, KT - 1, rb1);
   for (int i = KT - 1; i >= 0; --i) {
     // X_i rows b = 16 wave + (4g + r): sum_a inv(L_ii)[a][b] W_i[a][c]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    {
+    if (dw) {
       float wv[16];
 #pragma unroll
       for (int s2 = 0; s2 < 16; ++s2) wv[s2] = Wl[(64 * i + 4 * s2 + g) * 16 + lq];
@@ -750,22 +752,24 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Xs[(16 * wave + 4 * g + r) * 16 + lq] = x[r];
     }
-    if (i > 0) load_dinv(dv, i - 1);
+    if (dw && i > 0) load_dinv(dv, i - 1);
     __syncthreads();
     // every wave has read W_i: it now holds X_i
+    if (dw) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Wl[(64 * i + 16 * wave + 4 * g + r) * 16 + lq] = x[r];
+      for (int r = 0; r < 4; ++r) Wl[(64 * i + 16 * wave + 4 * g + r) * 16 + lq] = x[r];
+    }
     if (i > 0) {
       float bx[16];
 #pragma unroll
       for (int s2 = 0; s2 < 16; ++s2) bx[s2] = Xs[(4 * s2 + g) * 16 + lq];
       if (rb0 < i) update_block(av0, bx, rb0);
       if (rb1 < i) update_block(av1, bx, rb1);
-      for (int rb = wave + 8; rb < i; rb += 8) {
+      for (int rb = wave + 16; rb < i; rb += 16) {
         load_block(av0, i, rb);
-        if (rb + 4 < i) load_block(av1, i, rb + 4);
+        if (rb + 8 < i) load_block(av1, i, rb + 8);
         update_block(av0, bx, rb);
-        if (rb + 4 < i) update_block(av1, bx, rb + 4);
+        if (rb + 8 < i) update_block(av1, bx, rb + 8);
       }
       // next step's first blocks
       if (rb0 < i - 1) load_block(av0, i - 1, rb0);
@@ -776,7 +780,7 @@ __global__ __launch_bounds__(256) void back_subst_lds_kernel(BackArgs a) {
 
   const bool ok = a.info_out[p] == 0;
   if (ok) {
-    for (int e = tid; e < pi.k * 16; e += 256) {
+    for (int e = tid; e < pi.k * 16; e += 512) {
       const int row = e >> 4, c = e & 15;
       float* v = a.Vc + (size_t)(pi.koff + row) * D + dim0 + c;
       *v = a.accumulate ? *v + Wl[row * 16 + c] : Wl[row * 16 + c];
@@ -794,8 +798,8 @@ void launch_back_subst(const BackArgs& a, int d, hipStream_t s) {
   dim3 grid(d / 16, a.P);
   const size_t lds = back_subst_lds_bytes(a.kpadmax);
   if (lds <= (size_t)a.lds_max) {
-    if (d == 128) hipLaunchKernelGGL((back_subst_lds_kernel<128>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((back_subst_lds_kernel<64>), grid, dim3(256), lds, s, a);
+    if (d == 128) hipLaunchKernelGGL((back_subst_lds_kernel<128>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((back_subst_lds_kernel<64>), grid, dim3(512), lds, s, a);
     return;
   }
   if (d == 128) hipLaunchKernelGGL((back_subst_kernel<128>), grid, dim3(256), 0, s, a);
