@@ -138,9 +138,9 @@ def softmax_rows(S):
 def ridge_values(Q, Y, Kc, scale, ridge_rel=1e-3):
     """Closed-form values for fixed keys.
 
-    [gist] "Optimization Strategy": values are solved in closed form by ridge
-    regression (least squares) given the attention weights of the current
-    keys; [abs] "values are solved in closed form via least squares".
+    [gist] "Optimization Strategy": with the keys held fixed, the values
+    have a closed-form ridge-regression (least-squares) solution given the
+    current keys' attention weights; the arXiv abstract [abs] says the same.
     Reading: A = softmax(Q Kc^T scale) over the k compressed keys, ridge
     constant mu = ridge_rel * trace(A^T A) / k, and
     (A^T A + mu I) Vc = A^T Y solved by Cholesky and two triangular solves.
@@ -519,9 +519,10 @@ def allocate_budget_two_level(mse: Sequence[float], layers: int, heads: int, K_t
 
 def value_norm_signal(Vz):
     """Static allocation signal: the mean Euclidean norm of the compress
-    zone's value rows.  [gist] "Adaptive Budget Allocation" contrasts pilot
-    MSE with static signals "like value norms"; reading: this per-problem
-    mean, used as the allocation weight in place of the pilot MSE."""
+    zone's value rows.  [gist] "Adaptive Budget Allocation" compares the
+    pilot MSE against static per-head signals, value norms among them;
+    reading: this per-problem mean, used as the allocation weight in place of
+    the pilot MSE."""
     V = _f64(Vz)
     return float(np.mean(np.sqrt(np.sum(V * V, axis=1))))
 

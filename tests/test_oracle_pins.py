@@ -314,3 +314,97 @@ def test_allocation_largest_remainder_ties_go_to_lower_index():
 def test_allocation_rejects_infeasible_budget():
     with pytest.raises(ValueError):
         O.allocate_budget([1.0, 2.0], 10, k_max=4)
+
+
+# ---------------------------------------------------------------- pins added for branches no other pin reaches
+
+def test_output_mse_by_hand():
+    """Output MSE = ||Yhat - Y||_F^2 / (n d), the LSE term excluded.
+
+    Two equal keys give every query the weights (1/2, 1/2), so Yhat is the
+    mean of the two value rows whatever the queries; the reference lse is
+    far from lhat, so any LSE contribution would show."""
+    Q = np.array([[0.3, -1.0], [2.0, 0.5]])
+    Kc = np.array([[1.0, 1.0], [1.0, 1.0]])
+    Vc = np.array([[1.0, 0.0], [3.0, 2.0]])          # mean row (2, 1)
+    Y = np.array([[1.0, 2.0], [3.0, 4.0]])           # residuals (1,-1), (-1,-3): squares sum 12
+    lse = np.array([100.0, -100.0])
+    assert O.output_mse(Q, Y, lse, Kc, Vc, 0.7) == pytest.approx(12.0 / 4.0, rel=0, abs=1e-14)
+    # one key: Yhat = v for every query; ||Y||^2 = 30 over n d = 4 entries
+    assert O.output_mse(Q, Y, lse, Kc[:1], np.zeros((1, 2)), 0.7) == pytest.approx(7.5, abs=1e-14)
+    # a rectangular case (n = 3, d = 2): the divisor is n d, not n or d
+    Y3 = np.vstack([Y, [[0.0, 2.0]]])                # third residual (2, -1): 5 more
+    Q3 = np.vstack([Q, [[1.0, 1.0]]])
+    assert O.output_mse(Q3, Y3, np.zeros(3), Kc, Vc, 0.7) == pytest.approx(17.0 / 6.0, abs=1e-14)
+
+
+def test_nondescent_direction_clears_history_and_flags():
+    """A stored pair of negative curvature (which the curvature guard would
+    never admit, planted here) turns the two-loop output into an ascent
+    direction on f = |x|^2 / 2.  The iteration must flag it, drop the
+    history, and take the steepest-descent step with the first step size
+    1/max(1, ||g||); the accepted step then leaves exactly one pair.
+
+    By hand: g = x0 = (1, 2, 3); with s = (1, 0, 0), y = (-1, 0, 0),
+    rho = -1: a = rho s.g = -1, q = g - a y = (0, 2, 3), gamma = s.y / y.y = -1,
+    r = gamma q = (0, -2, -3), b = rho y.r = 0, r += (a - b) s -> (-1, -2, -3),
+    p = -r = g, so g.p = 14 > 0."""
+    f = lambda x: 0.5 * float(x @ x)
+    fg = lambda x: (f(x), x.copy())
+    x0 = np.array([1.0, 2.0, 3.0])
+    s, y = np.array([1.0, 0.0, 0.0]), np.array([-1.0, 0.0, 0.0])
+    np.testing.assert_allclose(O.two_loop(x0, [(s, y, -1.0)]), -x0, rtol=0, atol=1e-15)
+    st = O.LbfgsState(x=x0.copy(), L=f(x0), g=x0.copy(), hist=[(s, y, -1.0)])
+    ok = O.lbfgs_iteration(f, fg, st, O.LbfgsOptions())
+    assert ok
+    assert st.flags == O.FLAG_NONDESCENT
+    a0 = 1.0 / math.sqrt(14.0)
+    assert st.last_alpha == a0 and st.trials == 1       # Armijo holds at once on this quadratic
+    np.testing.assert_allclose(st.x, x0 * (1.0 - a0), rtol=0, atol=1e-15)
+    assert len(st.hist) == 1
+    s_new, y_new, rho_new = st.hist[0]
+    np.testing.assert_allclose(s_new, -a0 * x0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(y_new, s_new, rtol=0, atol=1e-15)     # Hessian = I
+    # an empty history is not a non-descent event: no flag
+    st2 = O.LbfgsState(x=x0.copy(), L=f(x0), g=x0.copy())
+    O.lbfgs_iteration(f, fg, st2, O.LbfgsOptions())
+    assert st2.flags == 0
+
+
+@pytest.mark.parametrize("alpha", [0.5, 1.0])
+def test_pilot_allocate_wiring(alpha):
+    """pilot_allocate = compress_problem for pilot_iters at uniform k0, its
+    output MSE, then the (separately pinned) flat split of K_total = P k0
+    with exponent alpha and bounds [1, Z].  The pilot MSEs differ enough that
+    alpha = 0.5 and alpha = 1 give different budgets, checked by hand from
+    the continuous shares."""
+    w = tiny_workload(d=8, N=40, m=8, g=2, F=6, layers=1, kv_heads=3, k0=6)
+    b = make_batch(w, 0)
+    probs = [(b["Q"][p], b["Kz"][p], b["Vz"][p]) for p in range(3)]
+    # widen the spread: scale the values of problems 1 and 2 up (pilot MSEs
+    # about 0.049, 0.042, 0.025: shares 6.9/6.3/4.8 at alpha 0.5,
+    # 7.7/6.5/3.8 at alpha 1, no bound binds)
+    probs[1] = (probs[1][0], probs[1][1], probs[1][2] * 2.0)
+    probs[2] = (probs[2][0], probs[2][1], probs[2][2] * 2.0)
+    opt = O.CompressOptions()
+    mse, ks, res = O.pilot_allocate(probs, w.k0, b["scale"], opt, pilot_iters=5, alpha=alpha)
+    for p, (Q, Kz, Vz) in enumerate(probs):
+        r = O.compress_problem(Q, Kz, Vz, w.k0, b["scale"], O.CompressOptions(iters=5))
+        assert mse[p] == r["mse"]
+        assert res[p]["traj"] == r["traj"]
+    Z = w.Z
+    assert ks == O.allocate_budget(mse, 3 * w.k0, alpha, 1, Z)
+    assert sum(ks) == 18
+    # by hand: continuous shares 18 w_p / sum w, w = mse**alpha, then floors
+    # and largest remainders (no bound binds at these sizes)
+    wts = [m ** alpha for m in mse]
+    x = [18.0 * v / sum(wts) for v in wts]
+    fl = [math.floor(v) for v in x]
+    left = 18 - sum(fl)
+    for p in sorted(range(3), key=lambda q: (-(x[q] - fl[q]), q))[:left]:
+        fl[p] += 1
+    assert ks == fl
+    assert ks == ([7, 6, 5] if alpha == 0.5 else [8, 6, 4])
+    other = O.pilot_allocate(probs, w.k0, b["scale"], opt, pilot_iters=5,
+                             alpha=1.5 - alpha)[1]
+    assert other != ks
