@@ -129,7 +129,13 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
     st->Sg[lane] = d[5 * lane + 3];
     st->Yg[lane] = d[5 * lane + 4];
   }
-  if (use_dots && tid == 0) st->gg = d[5 * MS];
+  if (use_dots && tid == 0) {
+    st->gg = d[5 * MS];
+    // a fresh loss and gradient (start, accepted step, or after a value
+    // re-solve): record a non-finite one; the problem then keeps failing its
+    // searches and stays where it is
+    if (!(isfinite(st->L) && isfinite(st->gg))) st->flags |= KVS_FLAG_NONFINITE;
+  }
   __syncthreads();
   if (reset && tid == 0) {
     if (mode == 0) st->flags |= KVS_FLAG_LINESEARCH;

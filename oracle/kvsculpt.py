@@ -155,7 +155,8 @@ def ridge_values(Q, Y, Kc, scale, ridge_rel=1e-3):
         c = cho_factor(Gm + mu * np.eye(k), lower=True, check_finite=True)
     except (LinAlgError, ValueError):
         return None, mu, False
-    return cho_solve(c, A.T @ _f64(Y)), mu, True
+    # plain arithmetic: a non-finite right-hand side gives non-finite values
+    return cho_solve(c, A.T @ _f64(Y), check_finite=False), mu, True
 
 
 def init_select_fit(Q, Kz, Y, lse, k, scale, ridge_rel=1e-3):
@@ -355,7 +356,10 @@ def compress_problem(Q, Kz, Vz, k, scale, opt: CompressOptions, Y=None, lse=None
     [gist] "Optimization Strategy".  Reading: one iteration is one L-BFGS
     iteration on Kc with Vc fixed; after iterations vc_every, 2*vc_every, ...
     Vc is re-solved and the loss and gradient are recomputed at the same Kc,
-    keeping the L-BFGS history.  ``init``: None = Select+Fit; a (Kc, Vc)
+    keeping the L-BFGS history.  Flags: FLAG_NONFINITE whenever the loss or
+    gradient at the current keys is not finite (at the start, after an
+    accepted step, after a value re-solve); such a problem then fails every
+    search and does not move.  ``init``: None = Select+Fit; a (Kc, Vc)
     pair; or, with ``init_keys``, starting keys Kc whose values are the ridge
     fit (a failed fit starts from zero values and sets FLAG_CHOLESKY).
     """
@@ -378,9 +382,14 @@ def compress_problem(Q, Kz, Vz, k, scale, opt: CompressOptions, Y=None, lse=None
         return (lambda x: loss(Q, Y, lse, x, Vc_, scale, opt.lam),
                 lambda x: loss_grad(Q, Y, lse, x, Vc_, scale, opt.lam)[:2])
 
+    def finite(L, g):
+        return bool(np.isfinite(L) and np.all(np.isfinite(g)))
+
     f, fg = make_f(Vc)
     L0, g0 = fg(Kc)
     st = LbfgsState(x=Kc, L=L0, g=g0, flags=flags)
+    if not finite(L0, g0):
+        st.flags |= FLAG_NONFINITE
     traj = [L0]
     for t in range(1, opt.iters + 1):
         lbfgs_iteration(f, fg, st, opt.lbfgs)
@@ -392,6 +401,8 @@ def compress_problem(Q, Kz, Vz, k, scale, opt: CompressOptions, Y=None, lse=None
                 st.flags |= FLAG_CHOLESKY
             f, fg = make_f(Vc)
             st.L, st.g = fg(st.x)
+            if not finite(st.L, st.g):
+                st.flags |= FLAG_NONFINITE
         if record:
             traj.append(st.L)
     mse = output_mse(Q, Y, lse, st.x, Vc, scale)

@@ -408,3 +408,23 @@ def test_pilot_allocate_wiring(alpha):
     other = O.pilot_allocate(probs, w.k0, b["scale"], opt, pilot_iters=5,
                              alpha=1.5 - alpha)[1]
     assert other != ks
+
+
+def test_nonfinite_value_row_flags_and_freezes():
+    """One NaN value row makes the zone's output NaN for every query (every
+    weight is positive), so the loss at the start is NaN: FLAG_NONFINITE.
+    Every Armijo test against a NaN loss is false, so every search fails:
+    FLAG_LINESEARCH, and the keys stay at the Select+Fit choice.  The ridge
+    solve passes the NaN right-hand side through instead of raising.  A
+    finite problem keeps flags 0."""
+    w = WORKLOADS[0]
+    b = make_batch(w, 0)
+    Q, Kz = b["Q"][0], b["Kz"][0]
+    Vz = b["Vz"][0].astype(np.float64).copy()
+    Vz[7, :] = np.nan
+    r = O.compress_problem(Q, Kz, Vz, w.k0, b["scale"], O.CompressOptions(iters=10))
+    assert r["flags"] == O.FLAG_NONFINITE | O.FLAG_LINESEARCH
+    assert np.isnan(r["loss"]) and np.isnan(r["init_loss"])
+    np.testing.assert_array_equal(r["Kc"], Kz[r["idx"]].astype(np.float64))
+    assert O.compress_problem(Q, Kz, b["Vz"][0], w.k0, b["scale"],
+                              O.CompressOptions(iters=10))["flags"] == 0
