@@ -21,6 +21,48 @@ KVS_FLAG_LINESEARCH = 4
 KVS_FLAG_NONDESCENT = 8
 KVS_FLAG_BADINDEX = 16
 
+__all__ = [
+    "ENTRY_POINTS",
+    "KVS_FLAG_BADINDEX",
+    "KVS_FLAG_CHOLESKY",
+    "KVS_FLAG_LINESEARCH",
+    "KVS_FLAG_NONDESCENT",
+    "KVS_FLAG_NONFINITE",
+    "Batch",
+    "Context",
+    "KvsBatch",
+    "KvsError",
+    "KvsAdamOpts",
+    "KvsOpts",
+    "KvsQueryGeom",
+    "adam_opts",
+    "kvs_allocate_budget",
+    "kvs_allocate_budget_two_level",
+    "kvs_value_norms",
+    "value_norms_workspace_bytes",
+    "kvs_build_queries",
+    "kvs_compress",
+    "kvs_compress_adam",
+    "kvs_compress_from_keys",
+    "kvs_compress_begin",
+    "kvs_compress_advance",
+    "kvs_init_topk",
+    "kvs_lbfgs_init",
+    "kvs_lbfgs_step",
+    "kvs_loss_grad",
+    "kvs_pilot_allocate",
+    "kvs_profile_enable",
+    "kvs_profile_read",
+    "kvs_reference_attn",
+    "kvs_use_eval",
+    "kvs_value_solve",
+    "lbfgs_state_bytes",
+    "load",
+    "opts",
+    "use_eval_workspace_bytes",
+    "workspace_bytes",
+]
+
 ENTRY_POINTS = (
     "kvs_create", "kvs_destroy", "kvs_status_string", "kvs_last_error", "kvs_default_opts",
     "kvs_workspace_bytes", "kvs_lbfgs_state_bytes", "kvs_reference_attn", "kvs_init_topk",
@@ -28,7 +70,7 @@ ENTRY_POINTS = (
     "kvs_pilot_allocate", "kvs_allocate_budget", "kvs_build_queries", "kvs_use_eval_workspace_bytes",
     "kvs_use_eval", "kvs_compress_from_keys", "kvs_default_adam_opts", "kvs_compress_adam",
     "kvs_allocate_budget_two_level", "kvs_value_norms_workspace_bytes", "kvs_value_norms",
-    "kvs_profile_enable", "kvs_profile_read",
+    "kvs_profile_enable", "kvs_profile_read", "kvs_compress_begin", "kvs_compress_advance",
 )
 
 
@@ -110,6 +152,9 @@ def load(path: str | None = None):
         "kvs_compress_adam": (c_int32, [V, B, O, POINTER(KvsAdamOpts), c_int32, V, V, V, V, V, V, V,
                                         V, V, V, c_size_t]),
         "kvs_use_eval": (c_int32, [V, B, c_int32, V, V, V, V, V, V, V, V, V, V, V, V, c_size_t]),
+        "kvs_compress_begin": (c_int32, [V, B, O, V, V, V, c_int32, V, V, V, V, c_size_t]),
+        "kvs_compress_advance": (c_int32, [V, B, O, V, c_int32, c_int32, V, V, V, V, V, V,
+                                           c_size_t]),
         "kvs_profile_enable": (c_int32, [V, c_int32]),
         "kvs_profile_read": (c_int32, [V, POINTER(KvsKernelStats), c_int32, POINTER(c_int32)]),
     }
@@ -256,6 +301,20 @@ def kvs_compress_from_keys(ctx, batch, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_los
     ctx.check("kvs_compress_from_keys", ctx.lib.kvs_compress_from_keys(
         ctx.handle, ctypes.byref(batch.c), ctypes.byref(o), _ptr(Q), _ptr(Kz), _ptr(Vz), _ptr(Kc),
         _ptr(Vc), _ptr(loss), _ptr(mse), _ptr(init_loss), _ptr(flags), w, nb))
+
+
+def kvs_compress_begin(ctx, batch, o, Q, Kz, Vz, keys_given, Kc, Vc, init_loss, ws):
+    w, nb = _ws(ws)
+    ctx.check("kvs_compress_begin", ctx.lib.kvs_compress_begin(
+        ctx.handle, ctypes.byref(batch.c), ctypes.byref(o), _ptr(Q), _ptr(Kz), _ptr(Vz),
+        int(keys_given), _ptr(Kc), _ptr(Vc), _ptr(init_loss), w, nb))
+
+
+def kvs_compress_advance(ctx, batch, o, Q, t_begin, t_end, Kc, Vc, loss, mse, flags, ws):
+    w, nb = _ws(ws)
+    ctx.check("kvs_compress_advance", ctx.lib.kvs_compress_advance(
+        ctx.handle, ctypes.byref(batch.c), ctypes.byref(o), _ptr(Q), int(t_begin), int(t_end),
+        _ptr(Kc), _ptr(Vc), _ptr(loss), _ptr(mse), _ptr(flags), w, nb))
 
 
 def adam_opts(lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8):

@@ -470,7 +470,7 @@ void lb_slot(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
 
 // Contraction work of the device-driven slots, from the per-problem trial and
 // accept counters (profiling only: one state read-back per call).
-void prof_add_slot_work(kvs_ctx ctx, const Plan& pl, const LbState* st) {
+void prof_add_slot_work(kvs_ctx ctx, const Plan& pl, const LbState* st, const LbState* before) {
   if (!ctx->prof) return;
   std::vector<LbState> h(pl.P);
   if (hipMemcpyAsync(h.data(), st, sizeof(LbState) * pl.P, hipMemcpyDeviceToHost, ctx->stream) != hipSuccess ||
@@ -478,8 +478,8 @@ void prof_add_slot_work(kvs_ctx ctx, const Plan& pl, const LbState* st) {
     return;
   double fw = 0, bw = 0;
   for (int p = 0; p < pl.P; ++p) {
-    fw += (double)h[p].n_trial * pl.info[p].k;
-    bw += (double)h[p].n_accept * pl.info[p].k;
+    fw += (double)(h[p].n_trial - (before ? before[p].n_trial : 0)) * pl.info[p].k;
+    bw += (double)(h[p].n_accept - (before ? before[p].n_accept : 0)) * pl.info[p].k;
   }
   ctx->acc[PROF_FWD].flops += 4.0 * pl.n * pl.d * fw;
   ctx->acc[PROF_BWD].flops += 4.0 * pl.n * pl.d * bw;
@@ -527,10 +527,12 @@ void run_init(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, c
   run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws);
 }
 
-kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
+// Everything before the first iteration: reference attention into the
+// workspace, the starting point, loss and gradient there with an empty
+// history (the state lives in the workspace).
+void compress_begin_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
                          const float* Q, const float* Kz, const float* Vz, float* Kc, float* Vc,
-                         float* loss, float* mse, float* init_loss, int* flags, void* ws,
-                         bool keys_given = false) {
+                         float* init_loss, bool keys_given, void* ws) {
   float* Yr = at<float>(ws, pl.r_yref);
   float* lr = at<float>(ws, pl.r_lseref);
   run_reference(ctx, pl, b, Q, Kz, Vz, Yr, lr, ws);
@@ -539,7 +541,28 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
   run_init(ctx, pl, b, Q, Kz, Yr, lr, Kc, Vc, nullptr, B.st, keys_given, ws);
   // the init's forward stored the scores at these keys
   lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 2, init_loss, nullptr, ws, true);
-  bool refreshed = true;
+}
+
+// Iterations t_begin + 1 .. t_end of the schedule from the state in the
+// workspace (t_begin is 0 or follows a value re-solve, so every problem is
+// ready for a new search).  Ends with loss, flags and, when asked, the
+// output MSE at the current pair.
+kvs_status compress_advance_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
+                                 const float* Q, float* Kc, float* Vc, int t_begin, int t_end,
+                                 float* loss, float* mse, int* flags, void* ws) {
+  float* Yr = at<float>(ws, pl.r_yref);
+  float* lr = at<float>(ws, pl.r_lseref);
+  LbBuffers B = lb_in_ws(pl, ws);
+  // trial and accept counters before this call, for the profile's work totals
+  std::vector<LbState> before;
+  if (ctx->prof) {
+    before.resize(pl.P);
+    if (hipMemcpyAsync(before.data(), B.st, sizeof(LbState) * pl.P, hipMemcpyDeviceToHost, ctx->stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(ctx->stream) != hipSuccess)
+      return fail(ctx, KVS_ERR_HIP, "schedule: %s", hipGetErrorString(hipGetLastError()));
+  }
+  bool refreshed = false;
   if (kvs_status s = status_buffers(ctx, pl.P); s != KVS_OK) return s;
   int* hbuf[2] = {ctx->hstat, ctx->hstat + pl.P};
   auto copy_status = [&](int i) {
@@ -547,9 +570,9 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
                hipSuccess &&
            hipEventRecord(ctx->sev[i], ctx->stream) == hipSuccess;
   };
-  int done = 0;
-  while (done < o->iters) {
-    const int blk = std::min(o->vc_every - done % o->vc_every, o->iters - done);
+  int done = t_begin;
+  while (done < t_end) {
+    const int blk = std::min(o->vc_every - done % o->vc_every, t_end - done);
     int slots = 0;
     for (; slots < blk; ++slots) lb_slot(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, ws, blk);
     bool any_fail = false;
@@ -579,9 +602,11 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
     done += blk;
     refreshed = false;
     if (done % o->vc_every == 0) {
-      if (any_fail)   // stored scores of a failed search belong to a rejected trial
+      if (any_fail) {  // stored scores of a failed search belong to a rejected trial
+        const std::vector<int> hs(hbuf[cur], hbuf[cur] + pl.P);
         run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, 1 << ST_DONE_FAIL, 2, nullptr, nullptr, o,
-                    ws);
+                    ws, &hs, ST_DONE_FAIL);
+      }
       run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws);
       // the value solve used the stored scores at the current keys: valid for
       // every problem, so the loss at the new values reads them back
@@ -589,11 +614,19 @@ kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const 
       refreshed = true;
     }
   }
-  if (!refreshed || o->iters == 0)
+  if (!refreshed)
     run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, kAll, 2, nullptr, mse, o, ws);
   launch_state_flags_out(B.st, flags, loss, pl.P, ctx->stream);
-  prof_add_slot_work(ctx, pl, B.st);
+  prof_add_slot_work(ctx, pl, B.st, before.empty() ? nullptr : before.data());
   return KVS_OK;
+}
+
+kvs_status compress_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_opts* o,
+                         const float* Q, const float* Kz, const float* Vz, float* Kc, float* Vc,
+                         float* loss, float* mse, float* init_loss, int* flags, void* ws,
+                         bool keys_given = false) {
+  compress_begin_impl(ctx, pl, b, o, Q, Kz, Vz, Kc, Vc, init_loss, keys_given, ws);
+  return compress_advance_impl(ctx, pl, b, o, Q, Kc, Vc, 0, o->iters, loss, mse, flags, ws);
 }
 
 // The alternating schedule with Adam on the keys: per iteration loss and
@@ -853,6 +886,41 @@ kvs_status kvs_compress_from_keys(kvs_ctx ctx, const kvs_batch* b, const kvs_opt
   kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
   if (s != KVS_OK) return s;
   s = compress_impl(ctx, pl, b, o, Q, Kz, Vz, Kc, Vc, loss, mse, init_loss, flags, ws, true);
+  if (s != KVS_OK) return s;
+  return hip_check(ctx, fn);
+}
+
+kvs_status kvs_compress_begin(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                              const float* Kz, const float* Vz, int32_t keys_given, float* Kc,
+                              float* Vc, float* init_loss, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_compress_begin";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Kz); KVS_NEED(Vz); KVS_NEED(Kc); KVS_NEED(Vc); KVS_OPT(init_loss);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  compress_begin_impl(ctx, pl, b, o, Q, Kz, Vz, Kc, Vc, init_loss, keys_given != 0, ws);
+  return hip_check(ctx, fn);
+}
+
+kvs_status kvs_compress_advance(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                                int32_t t_begin, int32_t t_end, float* Kc, float* Vc, float* loss,
+                                float* mse, int32_t* flags, void* ws, size_t ws_bytes) {
+  const char* fn = "kvs_compress_advance";
+  if (!ctx) return KVS_ERR_INVALID;
+  if (!o) return fail(ctx, KVS_ERR_INVALID, "%s: opts is NULL", fn);
+  KVS_NEED(Q); KVS_NEED(Kc); KVS_NEED(Vc); KVS_NEED(loss); KVS_OPT(mse); KVS_OPT(flags);
+  // checked before anything is enqueued (vc_every < 1 is reported by the plan)
+  if (t_begin < 0 || t_end < t_begin)
+    return fail(ctx, KVS_ERR_INVALID, "%s: need 0 <= t_begin <= t_end (got %d, %d)", fn, t_begin, t_end);
+  if (o->vc_every >= 1 && t_begin % o->vc_every != 0)
+    return fail(ctx, KVS_ERR_INVALID, "%s: t_begin %d is not a multiple of vc_every %d", fn, t_begin,
+                o->vc_every);
+  Plan pl;
+  kvs_status s = prepare(ctx, fn, b, o, ws, ws_bytes, &pl);
+  if (s != KVS_OK) return s;
+  s = compress_advance_impl(ctx, pl, b, o, Q, Kc, Vc, t_begin, t_end, loss, mse, flags, ws);
   if (s != KVS_OK) return s;
   return hip_check(ctx, fn);
 }

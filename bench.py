@@ -1,14 +1,26 @@
 """Throughput of the KVSculpt optimizer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
 
-A step is one whole kvs_compress call on one batch of synthetic problems:
-compress-zone reference attention, Select+Fit init (importance, top-k, ridge
-fit), then T L-BFGS iterations (direction, Armijo trials, loss/gradient) with
-the ridge value re-solve every 5 iterations.  With --config 2..4 the step
-also runs the 60-iteration pilot and the budget reallocation before the main
-run at ragged k.  The metric is problem-iterations per second,
-P * T * K / (wall time of the K timed steps), inputs resident in HBM.
+Default (the compress row): the long-context Qwen2.5-7B-shaped cache, all
+112 (layer, KV-head) problems, N = 32768, n = 17920 training queries per
+problem.  The run is the whole method: the 60-iteration pilot at uniform k0,
+the budget reallocation, reference attention and Select+Fit at the new
+ragged k, then the 150-iteration main run.  A step is one block of 5 main-run
+iterations of every problem (direction, Armijo trials, loss and gradient,
+history update, then the ridge value re-solve and the loss/gradient after
+it), driven through kvs_compress_begin / kvs_compress_advance.  W blocks are
+warm-up, the next K are timed (inputs resident in HBM, synchronised before
+and after), the rest finish the main run; the metric is problem-iterations
+per second, P * 5 * K / (wall time of the K blocks).  The whole-model
+compress latency (pilot through iteration T) is measured in the same run.
+--config 0..3 runs the other workloads the same way (configs 0 and 1 have
+no pilot).
+
+The roofline comes from HIP events on the library's stream around every
+launch of the timed kernels during the timed blocks (kvs_profile_enable):
+the contraction kernel with the most time is the dominant one.  The float64
+oracle is timed on a bounded sample on the host CPU (one block of problem 0).
 
 With --row queries the step is instead one kvs_build_queries call over the
 workload's problems: retain queries copied and synthetic future queries
@@ -30,13 +42,8 @@ the main run's final MSE under uniform, pilot (flat, two-level, alpha 1)
 and value-norm allocations of the same total budget.  --row vector runs 25
 iterations on a 64-problem slice of the llama3-8b-shaped cache, large enough
 for the vector and reduction kernels' HBM rates to be read from a trace.
-
-Printed: one JSON line (stdout).  The throughput comes from a timed pass
-with nothing recorded on the stream; the roofline of the dominant kernel
-comes from a second timed pass of the same steps with a HIP event pair on
-the library's stream around each of its launches (events cost about 2 us
-per launch).  The float64 oracle is timed on a bounded sample on the host
-CPU.
+These rows time whole calls and take a second, event-timed pass for their
+roofline.
 """
 from __future__ import annotations
 
@@ -117,32 +124,6 @@ def _threads():
         return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
         return os.cpu_count() or 1
-
-
-def cpu_baseline(w, b, seconds):
-    """Float64 oracle on problem 0 of the same workload (host cores)."""
-    from oracle import kvsculpt as O
-    threads = _threads()
-    Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
-    Y, l = O.reference_attention(Q, Kz, Vz, s)
-    t0 = time.perf_counter()
-    O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=0), Y=Y, lse=l)
-    t_init = time.perf_counter() - t0
-    # size the sample to roughly `seconds` of iteration work (multiple of 5: whole value-solve periods)
-    t0 = time.perf_counter()
-    O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=5), Y=Y, lse=l)
-    t5 = time.perf_counter() - t0 - t_init
-    iters = int(max(5, min(w.T, 5 * round(seconds / max(t5, 1e-3)))))
-    if iters > 5:
-        t0 = time.perf_counter()
-        O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=iters), Y=Y, lse=l)
-        t_it = time.perf_counter() - t0 - t_init
-    else:
-        t_it = t5
-    return {"value": iters / t_it, "unit": "problem-iterations/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{w.name} problem 0 of {w.P}, {iters} L-BFGS iterations with value "
-                      f"solves every 5 (Select+Fit init excluded), float64 NumPy/SciPy"}
 
 
 def timed_pass(torch, step, steps):
@@ -705,13 +686,233 @@ def bench_vector(args, torch, K):
     print(json.dumps(out), flush=True)
 
 
+# kernels whose launches are timed with HIP events during the timed blocks
+TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "attn_pv", "potrf_panel", "back_subst", "merge",
+                 "hist_dots", "direction"]
+# contraction kernels (MFMA roofline) and their peaks: the loss forward forms
+# its scores on fp64 MFMA (half its flops) and A Vc on fp32 MFMA (the other
+# half); the others are fp32 MFMA only
+CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "attn_pv")
+
+
+def kernel_rows(stats):
+    """Per-kernel time, launches and roofline fractions from event totals."""
+    rows = {}
+    for name, st in stats.items():
+        if st["launches"] == 0:
+            continue
+        sec = st["ms"] / 1e3
+        row = {"launches": st["launches"], "ms": round(st["ms"], 3),
+               "avg_us": round(1e6 * sec / st["launches"], 2)}
+        if name in CONTRACTIONS and st["flops"] > 0:
+            fl = st["flops"]
+            row["tflops"] = round(fl / sec / 1e12, 2)
+            if name == "attn_fwd":
+                # t_min = (fl/2)/fp64 peak + (fl/2)/fp32 peak, the MFMA pipes being shared
+                tmin = 0.5 * fl / PEAK_FP64_MFMA + 0.5 * fl / PEAK_FP32_MFMA
+                row["frac_mfma_mixed"] = round(tmin / sec, 4)
+                row["frac_fp64_part"] = round(0.5 * fl / sec / PEAK_FP64_MFMA, 4)
+                row["frac_fp32_part"] = round(0.5 * fl / sec / PEAK_FP32_MFMA, 4)
+            else:
+                row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
+        rows[name] = row
+    return rows
+
+
+def cpu_baseline_block(w, b):
+    """The float64 oracle on problem 0 of the workload, timed on one block of
+    the main run: 5 L-BFGS iterations at uniform k0 from the Select+Fit start,
+    the value re-solve and the loss/gradient after it (the unit the GPU's
+    step is made of).  The reference attention, Select+Fit and the loss at
+    the start are set-up, not timed.  Then the work of one iteration (a
+    trial loss and a loss/gradient) with the BLAS pool held to one thread."""
+    from oracle import kvsculpt as O
+    threads = _threads()
+    Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
+    t0 = time.perf_counter()
+    Y, l = O.reference_attention(Q, Kz, Vz, s)
+    idx, Kc, Vc, ok = O.init_select_fit(Q, Kz, Y, l, w.k0, s)
+    t_setup = time.perf_counter() - t0
+    log(f"[bench] oracle set-up (reference attention, Select+Fit) {t_setup:.1f} s")
+    t0 = time.perf_counter()
+    O.loss_grad(Q, Y, l, Kc, Vc, s)
+    t_eval = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r = O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=5), Y=Y, lse=l, init=(Kc, Vc))
+    t_blk = time.perf_counter() - t0 - t_eval       # less the start's loss/gradient
+    log(f"[bench] oracle block of 5 iterations {t_blk:.1f} s on {threads} threads")
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.loss(Q, Y, l, r["Kc"], r["Vc"], s)
+            t_f1 = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            O.loss_grad(Q, Y, l, r["Kc"], r["Vc"], s)
+            t_g1 = time.perf_counter() - t0
+        one = {"value": round(1.0 / (t_f1 + t_g1), 4), "unit": "problem-iterations/s", "cores": 1,
+               "sample": f"{w.name} problem 0 at the block's end point, BLAS held to 1 thread: one "
+                         f"trial loss ({t_f1:.2f} s) plus one loss and gradient ({t_g1:.2f} s), the "
+                         f"work of an iteration whose first trial is accepted, without the value "
+                         f"re-solve's share"}
+        log(f"[bench] oracle iteration work on 1 thread {t_f1 + t_g1:.2f} s")
+    except Exception as e:  # threadpoolctl missing: report the multi-thread figure only
+        log(f"[bench] one-thread oracle run skipped: {e}")
+    return {"value": round(5.0 / t_blk, 4), "unit": "problem-iterations/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{w.name} problem 0 at k0={w.k0}: one block of 5 L-BFGS iterations "
+                      f"with its value re-solve and the loss/gradient after it, from the Select+Fit start, float64 NumPy/SciPy; "
+                      f"reference attention and Select+Fit ({t_setup:.0f} s) not timed",
+            "one_thread": one}
+
+
+def bench_compress(args, torch, K):
+    """The optimizer on a whole cache: pilot, reallocation, then the main run
+    at ragged k, timed in blocks of 5 iterations (one step = one block for
+    all problems, ending with the value re-solve and the loss/gradient after
+    it).  The whole-model compress latency (pilot, reallocation, reference
+    attention, Select+Fit, all T iterations) is measured in the same run."""
+    from synth import WORKLOADS, make_batch
+    w = WORKLOADS[args.config]
+    if args.ratio is not None:
+        w = w.with_ratio(args.ratio)
+    T = w.T if args.iters is None else args.iters
+    VC = 5
+    if T % VC:
+        raise SystemExit("--iters must be a multiple of 5 (a step is a block of 5 iterations)")
+    W, Kst = args.warmup, args.steps
+    nblk_T = T // VC
+    nblk = max(nblk_T, W + Kst)
+    workers = min(16, os.cpu_count() or 1)
+    log(f"[bench] generating {w.name}: P={w.P} n={w.n} Z={w.Z} d={w.d} k0={w.k0} T={T} "
+        f"pilot={w.pilot} ({workers} processes)")
+    t0 = time.perf_counter()
+    b = make_batch(w, 0, workers=workers if w.P > 8 else 1)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    Q = torch.from_numpy(b["Q"]).to(dev)
+    Kz = torch.from_numpy(b["Kz"]).to(dev)
+    Vz = torch.from_numpy(b["Vz"]).to(dev)
+    ctx = K.Context()
+    o = K.opts(iters=T)
+    pilot = w.pilot or 0
+    loss, mse, l0 = (torch.empty(P, dtype=torch.float32, device=dev) for _ in range(3))
+    flags = torch.zeros(P, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs in HBM ({(b['Q'].nbytes + 2 * b['Kz'].nbytes) / 2**30:.2f} GiB)")
+
+    # ---- whole-model compress: everything from here to the end of iteration T
+    t_start = time.perf_counter()
+    ks = [w.k0] * P
+    t_pilot = 0.0
+    if pilot:
+        bt0 = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+        ws0 = torch.empty(K.workspace_bytes(bt0, K.opts(iters=pilot)), dtype=torch.uint8, device=dev)
+        pm = torch.empty(P, dtype=torch.float32, device=dev)
+        ks = list(K.kvs_pilot_allocate(ctx, bt0, K.opts(iters=pilot), pilot, 0.5, 1, Z, Q, Kz, Vz, pm,
+                                       ws0))
+        t_pilot = time.perf_counter() - t_start
+        del ws0
+        log(f"[bench] pilot ({pilot} iterations) + reallocation {t_pilot:.2f} s: k in "
+            f"[{min(ks)}, {max(ks)}], sum {sum(ks)}")
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    ws = torch.empty(K.workspace_bytes(bt, o), dtype=torch.uint8, device=dev)
+    Kc = torch.empty((sum(ks), d), dtype=torch.float32, device=dev)
+    Vc = torch.empty_like(Kc)
+    t_b = time.perf_counter()
+    K.kvs_compress_begin(ctx, bt, o, Q, Kz, Vz, 0, Kc, Vc, l0, ws)
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter() - t_b
+    log(f"[bench] reference attention + Select+Fit at the new k: {t_begin:.2f} s; main run: "
+        f"{nblk} blocks of {VC} (warmup {W}, timed {Kst})")
+    t_timed = t_latency = None
+    stats = None
+    for i in range(nblk):
+        if i == W:
+            torch.cuda.synchronize()
+            K.kvs_profile_enable(ctx, True, kernels=TIMED_KERNELS)
+            t1 = time.perf_counter()
+        K.kvs_compress_advance(ctx, bt, o, Q, VC * i, VC * (i + 1), Kc, Vc, loss, mse, flags, ws)
+        if i == W + Kst - 1:
+            torch.cuda.synchronize()
+            t_timed = time.perf_counter() - t1
+            stats = K.kvs_profile_read(ctx)
+            K.kvs_profile_enable(ctx, False)
+        if i == nblk_T - 1:
+            torch.cuda.synchronize()
+            t_latency = time.perf_counter() - t_start
+        if i % 5 == 4 or i == nblk - 1:
+            log(f"[bench] block {i + 1}/{nblk} done ({time.perf_counter() - t_start:.1f} s since the "
+                f"pilot started)")
+    torch.cuda.synchronize()
+    lg, l0g, fg = loss.cpu().numpy(), l0.cpu().numpy(), flags.cpu().numpy()
+    log(f"[bench] final/start loss ratio: median {np.median(lg / l0g):.4f} min {np.min(lg / l0g):.4f} "
+        f"max {np.max(lg / l0g):.4f}; flagged problems {int(np.count_nonzero(fg))}")
+
+    value = P * VC * Kst / t_timed
+    rows = kernel_rows(stats)
+    name = max((k for k in rows if k in CONTRACTIONS), key=lambda k: rows[k]["ms"])
+    st = stats[name]
+    avg_s = st["ms"] / st["launches"] / 1e3
+    fl_launch = st["flops"] / st["launches"]
+    achieved = fl_launch / avg_s
+    if name == "attn_fwd":
+        peak = 1.0 / (0.5 / PEAK_FP64_MFMA + 0.5 / PEAK_FP32_MFMA)
+        peak_note = "harmonic mix of the fp64 (scores) and fp32 (A Vc) MFMA peaks"
+    else:
+        peak = PEAK_FP32_MFMA
+        peak_note = "fp32 MFMA"
+    tot_ms = sum(r["ms"] for r in rows.values())
+    for k2, r in sorted(rows.items(), key=lambda kv: -kv[1]["ms"]):
+        log(f"[bench] {k2:12s} launches={r['launches']:6d} ms={r['ms']:10.2f} avg_us={r['avg_us']:9.1f} "
+            + " ".join(f"{kk}={vv}" for kk, vv in r.items() if kk.startswith(("tflops", "frac"))))
+    roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_for(name, w.name if args.ratio is None else None),
+                "kernel": name, "peak_kind": peak_note, "launches": st["launches"],
+                "avg_us": round(avg_s * 1e6, 2),
+                "timed": f"HIP events on the library stream around every launch of the timed "
+                         f"kernels during the {Kst} timed blocks ({tot_ms / Kst:.1f} ms of "
+                         f"event-timed kernels per {1e3 * t_timed / Kst:.1f} ms step)"}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        cpu = cpu_baseline_block(w, b)
+    out = {
+        "metric": "KVSculpt L-BFGS iterations/sec over all layer×KV-head problems; % fp32 MFMA",
+        "value": round(value, 2), "unit": "problem-iterations/s", "n_gpus": 1,
+        "steps": Kst, "warmup": W, "ms_per_step": round(1e3 * t_timed / Kst, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "problems": P, "d": d, "n": n, "Z": Z, "k0": w.k0,
+                   "k_range": [int(min(ks)), int(max(ks))], "k_total": int(sum(ks)),
+                   "iters": T, "vc_every": VC, "history": 10, "pilot": pilot,
+                   "step": f"one block of {VC} L-BFGS iterations of all {P} problems with the value "
+                           f"re-solve and loss/gradient after it (main run at the pilot's ragged k)",
+                   "logits": "fp64 MFMA (stored fp32)", "contractions": "fp32 MFMA"},
+        "latency": {"whole_model_compress_s": round(t_latency, 3), "pilot_and_allocation_s": round(t_pilot, 3),
+                    "reference_and_select_fit_s": round(t_begin, 3),
+                    "note": f"pilot ({pilot} iterations at k0) + reallocation + reference attention + "
+                            f"Select+Fit at the new k + {T} main-run iterations, wall clock, inputs in HBM"},
+        "kernels": rows,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (compress: blocks of 5 iterations, default 20; other rows: 5)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (compress 5, others 1)")
     ap.add_argument("--config", type=int, default=None,
-                    help="workload (default 1; 2 for --row queries / use)")
+                    help="workload (compress: default 4, the long-context cache; 2 for the "
+                         "queries / use / solve / alloc rows)")
     ap.add_argument("--ratio", type=float, default=None, help="compression ratio r (configs 2..4)")
     ap.add_argument("--iters", type=int, default=None, help="override T (profiling runs only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -730,7 +931,11 @@ def main():
                     help="only run plain device copies of this size (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.config is None:
-        args.config = 2 if args.row in ("queries", "use", "solve", "alloc") else 1
+        args.config = {"compress": 4, "adam": 1, "restarts": 1, "vector": 3}.get(args.row, 2)
+    if args.steps is None:
+        args.steps = 20 if args.row == "compress" else 5
+    if args.warmup is None:
+        args.warmup = 5 if args.row == "compress" else 1
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU: the problems of a batch are independent and this build "
             "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
@@ -764,132 +969,7 @@ def main():
         bench_vector(args, torch, K)
         return
 
-    w = WORKLOADS[args.config]
-    if args.ratio is not None:
-        w = w.with_ratio(args.ratio)
-    T = w.T if args.iters is None else args.iters
-    dev = torch.device("cuda:0")
-    log(f"[bench] generating {w.name}: P={w.P} n={w.n} Z={w.Z} d={w.d} k0={w.k0} T={T}")
-    b = make_batch(w, 0)
-    log("[bench] inputs ready")
-    P, n, d = b["Q"].shape
-    Z = b["Kz"].shape[1]
-    Q = torch.from_numpy(b["Q"]).to(dev)
-    Kz = torch.from_numpy(b["Kz"]).to(dev)
-    Vz = torch.from_numpy(b["Vz"]).to(dev)
-
-    ctx = K.Context()
-    o = K.opts(iters=T)
-    pilot = w.pilot if w.pilot else 0
-    kmax_bytes = 0
-    if pilot:
-        # budget the workspace for the widest ragged split the allocator can return
-        bt_pilot = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
-        kmax_bytes = K.workspace_bytes(bt_pilot, K.opts(iters=pilot))
-    bt = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
-    ktot = w.k0 * P
-
-    def alloc(batch):
-        nb = max(K.workspace_bytes(batch, o), kmax_bytes)
-        return torch.empty(nb, dtype=torch.uint8, device=dev)
-
-    ws = alloc(bt)
-    Kc = torch.empty((ktot, d), dtype=torch.float32, device=dev)
-    Vc = torch.empty((ktot, d), dtype=torch.float32, device=dev)
-    loss = torch.empty(P, dtype=torch.float32, device=dev)
-    mse = torch.empty(P, dtype=torch.float32, device=dev)
-    l0 = torch.empty(P, dtype=torch.float32, device=dev)
-    flags = torch.zeros(P, dtype=torch.int32, device=dev)
-    pm = torch.empty(P, dtype=torch.float32, device=dev)
-    state = {"ws": ws, "k": None}
-
-    def step():
-        batch = bt
-        if pilot:
-            k_out = K.kvs_pilot_allocate(ctx, bt, K.opts(iters=pilot), pilot, 0.5, 1, Z, Q, Kz, Vz, pm,
-                                         state["ws"])
-            batch = K.Batch(P, d, Z, n, k=k_out, scale=b["scale"])
-            need = K.workspace_bytes(batch, o)
-            if need > state["ws"].numel():
-                state["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
-            state["k"] = k_out
-            log(f"[bench] pilot done: k in [{min(k_out)}, {max(k_out)}], sum {sum(k_out)}")
-        flags.zero_()
-        K.kvs_compress(ctx, batch, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, state["ws"])
-        if pilot:
-            torch.cuda.synchronize()
-            log("[bench] main run done")
-
-    for i in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region 1: throughput, with no instrumentation on the stream
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    # timed region 2: the same steps again with a HIP event pair on the
-    # library's stream around every launch of the dominant contraction
-    # kernels (the kernel durations for the roofline).  The events add about
-    # 2 us per launch, so the throughput is taken from region 1.
-    dominant = ["attn_fwd", "attn_bwd"]
-    K.kvs_profile_enable(ctx, True, kernels=dominant)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed_events = time.perf_counter() - t1
-    stats = K.kvs_profile_read(ctx)
-    K.kvs_profile_enable(ctx, False)
-
-    # per-kernel breakdown of one further (untimed) step
-    K.kvs_profile_enable(ctx, True)
-    step()
-    breakdown = K.kvs_profile_read(ctx)
-    K.kvs_profile_enable(ctx, False)
-    lg, l0g, fg = loss.cpu().numpy(), l0.cpu().numpy(), flags.cpu().numpy()
-
-    iters_total = P * T * args.steps
-    value = iters_total / elapsed
-    ms_step = 1e3 * elapsed / args.steps
-    # dominant kernel = the contraction kernel with the most time in the timed region
-    name = max(stats, key=lambda k: stats[k]["ms"])
-    st = stats[name]
-    avg_s = st["ms"] / st["launches"] / 1e3
-    fl_launch = st["flops"] / st["launches"]
-    peak = mixed_fwd_peak() if name == "attn_fwd" else PEAK_FP32_MFMA
-    achieved = fl_launch / avg_s
-    roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_for(name, w.name if args.ratio is None else None),
-                "kernel": name, "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2),
-                "timed": f"second timed pass of {args.steps} steps with per-launch HIP events "
-                         f"({1e3 * elapsed_events / args.steps:.2f} ms per step)"}
-    for k2 in breakdown:
-        bd = breakdown[k2]
-        log(f"[bench] {k2:14s} launches={bd['launches']:6d} ms={bd['ms']:9.3f} "
-            f"TF/s={bd['flops'] / max(bd['ms'], 1e-9) / 1e9:8.2f}")
-    log(f"[bench] loss init={l0g.tolist()} final={lg.tolist()} flags={fg.tolist()} k={state['k']}")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the float64 oracle on the host")
-        cpu = cpu_baseline(w, b, args.cpu_seconds)
-
-    out = {
-        "metric": "KVSculpt L-BFGS iterations/sec over all layer×KV-head problems; % fp32 MFMA",
-        "value": round(value, 2), "unit": "problem-iterations/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "problems": P, "d": d, "n": n, "Z": Z, "k": w.k0,
-                   "iters": T, "vc_every": 5, "history": 10, "pilot": pilot,
-                   "logits": "fp64 MFMA (stored fp32)", "contractions": "fp32 MFMA"},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    bench_compress(args, torch, K)
 
 
 if __name__ == "__main__":

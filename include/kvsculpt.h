@@ -192,6 +192,33 @@ kvs_status kvs_compress_from_keys(kvs_ctx ctx, const kvs_batch* b, const kvs_opt
                                   float* Vc, float* loss, float* mse, float* init_loss,
                                   int32_t* flags, void* ws, size_t ws_bytes);
 
+/* kvs_compress in stages, for callers that drive the schedule in pieces
+ * (progress reports, early stopping, timing a block of iterations); the
+ * same schedule (arXiv abstract; gist page, "Optimization Strategy") with
+ * the same kernels, so begin followed by advance(0, iters) gives the bits of
+ * kvs_compress.
+ * kvs_compress_begin: reference attention over the zone, the start
+ * (Select+Fit, or with keys_given != 0 the caller's keys in Kc and their
+ * ridge values), loss and gradient there, empty history.  The reference
+ * outputs and the L-BFGS state stay in ws; init_loss [P] (device, may be
+ * NULL) gets the loss at the start.
+ * kvs_compress_advance: iterations t = t_begin + 1 .. t_end, with the
+ * value re-solve after every t that is a multiple of vc_every, from the
+ * state in ws.  t_begin must be 0 or a multiple of vc_every (a stage ends
+ * anywhere, but only a stage that ended after a value re-solve can be
+ * continued) and equal to the previous stage's t_end; 0 <= t_begin <= t_end.
+ * b, o, Q, Kc, Vc and ws must be those of the begin call and of the earlier
+ * stages (o->iters is not used).  On return loss [P] holds the loss at the
+ * current pair, mse [P] (may be NULL) its output MSE, flags [P] (may be
+ * NULL) the flags accumulated since begin.  Errors: KVS_ERR_INVALID for a
+ * bad t_begin / t_end, otherwise as kvs_compress. */
+kvs_status kvs_compress_begin(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                              const float* Kz, const float* Vz, int32_t keys_given, float* Kc,
+                              float* Vc, float* init_loss, void* ws, size_t ws_bytes);
+kvs_status kvs_compress_advance(kvs_ctx ctx, const kvs_batch* b, const kvs_opts* o, const float* Q,
+                                int32_t t_begin, int32_t t_end, float* Kc, float* Vc, float* loss,
+                                float* mse, int32_t* flags, void* ws, size_t ws_bytes);
+
 /* The schedule with Adam in place of L-BFGS on the keys (gist page, section 4
  * "Optimizer Efficacy": the ablation that replaces L-BFGS by Adam; section 2
  * "Optimization Strategy": first-order methods get trapped).  Per iteration

@@ -274,14 +274,51 @@ def problem_list(w: Workload, problems: Iterable[int] | None = None) -> list:
     return list(range(P)) if problems is None else [int(p) for p in problems]
 
 
+def _heads_f32(args):
+    """Worker of :func:`make_batch`: float32 arrays of some problems."""
+    w, seed, plist, keys = args
+    temps = layer_temperatures(w, seed)
+    out = {k: [] for k in keys}
+    for p in plist:
+        layer, head = divmod(p, w.kv_heads)
+        hd = make_head(w, layer, head, seed, float(temps[layer]))
+        for k in keys:
+            out[k].append(hd[k].astype(np.float32))
+    return out
+
+
 def make_batch(w: Workload, seed: int = 0, problems: Sequence[int] | None = None,
-               with_retain: bool = False) -> dict:
+               with_retain: bool = False, workers: int = 1) -> dict:
     """Stack problems p = layer * kv_heads + head into float32 arrays.
 
     Q [P, n, d], Kz [P, Z, d], Vz [P, Z, d] (+ Kr, Vr [P, m, d] if asked).
+    ``workers`` > 1 builds the heads in that many processes (same arrays:
+    every head has its own seeded stream).
     """
     temps = layer_temperatures(w, seed)
     plist = problem_list(w, problems)
+    if workers > 1 and len(plist) > 1:
+        import concurrent.futures as cf
+        keys = ("Q", "Kz", "Vz") + (("Kr", "Vr") if with_retain else ())
+        nw = min(workers, len(plist))
+        chunks = [plist[i::nw] for i in range(nw)]
+        res = {k: [None] * len(plist) for k in keys}
+        where = {p: i for i, p in enumerate(plist)}
+        with cf.ProcessPoolExecutor(nw) as ex:
+            for chunk, part in zip(chunks, ex.map(_heads_f32, [(w, seed, c, keys) for c in chunks])):
+                for k in keys:
+                    for p, a in zip(chunk, part[k]):
+                        res[k][where[p]] = a
+        out = {}
+        for k in keys:
+            arr = np.empty((len(plist),) + res[k][0].shape, dtype=np.float32)
+            for i, a in enumerate(res[k]):
+                arr[i] = a
+                res[k][i] = None
+            out[k] = arr
+        out["problems"] = np.array(plist, dtype=np.int64)
+        out["scale"] = 1.0 / math.sqrt(w.d)
+        return out
     out = {k: [] for k in ("Q", "Kz", "Vz", "Kr", "Vr")}
     for p in plist:
         layer, head = divmod(p, w.kv_heads)

@@ -244,3 +244,37 @@ def test_pilot_allocation_bit_exact():
     assert sum(k_out) == w.k0 * P
     for a, bb in zip(mg, mse):
         assert abs(a - bb) <= 0.02 * bb
+
+
+def test_staged_compress_equals_one_call():
+    """kvs_compress_begin + kvs_compress_advance over (0, 5), (5, 10),
+    (10, 13) gives the bits of one kvs_compress with 13 iterations (same
+    kernels in the same order); a stage that does not start after a value
+    re-solve is rejected before anything is enqueued."""
+    w = WORKLOADS[1]
+    b = make_batch(w, 0)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    T = 13
+    o = K.opts(iters=T)
+    bt = K.Batch(P, d, Z, n, k=[w.k0] * P, scale=b["scale"])
+    ctx = K.Context()
+    Q, Kz, Vz = to_gpu(b["Q"]), to_gpu(b["Kz"]), to_gpu(b["Vz"])
+    outs = []
+    for staged in (False, True):
+        ws = workspace(K.workspace_bytes(bt, o))
+        Kc, Vc = empty((w.k0 * P, d)), empty((w.k0 * P, d))
+        loss, mse, l0 = empty((P,)), empty((P,)), empty((P,))
+        flags = to_gpu(np.zeros(P, np.int32))
+        if staged:
+            K.kvs_compress_begin(ctx, bt, o, Q, Kz, Vz, 0, Kc, Vc, l0, ws)
+            for t0, t1 in ((0, 5), (5, 10), (10, 13)):
+                K.kvs_compress_advance(ctx, bt, o, Q, t0, t1, Kc, Vc, loss, mse, flags, ws)
+            with pytest.raises(K.KvsError):
+                K.kvs_compress_advance(ctx, bt, o, Q, 13, 15, Kc, Vc, loss, mse, flags, ws)
+        else:
+            K.kvs_compress(ctx, bt, o, Q, Kz, Vz, Kc, Vc, loss, mse, l0, flags, ws)
+        outs.append([host(x).tobytes() for x in (Kc, Vc, loss, mse, l0, flags)])
+    say(f"[staged] {w.name}: begin + 3 stages vs one call, T={T}")
+    for name, a, c in zip(("Kc", "Vc", "loss", "mse", "init_loss", "flags"), *outs):
+        assert a == c, name
