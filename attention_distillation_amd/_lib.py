@@ -46,6 +46,8 @@ __all__ = [
     "kvs_compress_from_keys",
     "kvs_compress_begin",
     "kvs_compress_advance",
+    "kvs_value_norms_noalloc",
+    "value_norms_noalloc_max_bytes",
     "kvs_init_topk",
     "kvs_lbfgs_init",
     "kvs_lbfgs_step",
@@ -71,6 +73,7 @@ ENTRY_POINTS = (
     "kvs_use_eval", "kvs_compress_from_keys", "kvs_default_adam_opts", "kvs_compress_adam",
     "kvs_allocate_budget_two_level", "kvs_value_norms_workspace_bytes", "kvs_value_norms",
     "kvs_profile_enable", "kvs_profile_read", "kvs_compress_begin", "kvs_compress_advance",
+    "kvs_value_norms_noalloc_max_bytes", "kvs_value_norms_noalloc",
 )
 
 
@@ -155,6 +158,8 @@ def load(path: str | None = None):
         "kvs_compress_begin": (c_int32, [V, B, O, V, V, V, c_int32, V, V, V, V, c_size_t]),
         "kvs_compress_advance": (c_int32, [V, B, O, V, c_int32, c_int32, V, V, V, V, V, V,
                                            c_size_t]),
+        "kvs_value_norms_noalloc_max_bytes": (c_size_t, []),
+        "kvs_value_norms_noalloc": (c_int32, [V, c_int32, c_int32, c_int32, V, V]),
         "kvs_profile_enable": (c_int32, [V, c_int32]),
         "kvs_profile_read": (c_int32, [V, POINTER(KvsKernelStats), c_int32, POINTER(c_int32)]),
     }
@@ -395,6 +400,15 @@ def kvs_value_norms(ctx, P, Z, d, Vz, signal, ws):
 PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",
                    "hist_dots", "direction", "importance", "ref_attn_fwd", "merge",
                    "build_queries", "use_attn_fwd", "attn_pv")
+
+
+def value_norms_noalloc_max_bytes():
+    return int(load().kvs_value_norms_noalloc_max_bytes())
+
+
+def kvs_value_norms_noalloc(ctx, P, Z, d, Vz, signal):
+    ctx.check("kvs_value_norms_noalloc", ctx.lib.kvs_value_norms_noalloc(
+        ctx.handle, int(P), int(Z), int(d), _ptr(Vz), _ptr(signal)))
 
 
 def kvs_profile_enable(ctx, enable=True, kernels=None):

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -49,6 +50,10 @@ struct kvs_ctx_s {
   int* hstat = nullptr;
   int hstat_cap = 0;
   hipEvent_t sev[2] = {nullptr, nullptr};
+  // device address of this device's copy of the static scratch array (null
+  // if it could not be taken; scratch_err says why)
+  void* scratch = nullptr;
+  std::string scratch_err;
   ~kvs_ctx_s() {
     for (auto& r : pending) { pool.push_back(r.a); pool.push_back(r.b); }
     for (auto e : pool) hipEventDestroy(e);
@@ -62,6 +67,32 @@ struct kvs_ctx_s {
 };
 
 namespace kvs {
+
+// Scratch memory of the allocation-free entry point (kvs_value_norms_noalloc):
+// a file-scope device array, one copy per GPU the library runs on, held until
+// the process ends.  In host code its name is only a stand-in: the device
+// address of each GPU's copy is taken once per device with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;        // by device ordinal; null until taken
+
+// Address of the current device's scratch copy (dev must be current).
+hipError_t scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0) return hipErrorInvalidDevice;
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 kvs_status fail(kvs_ctx c, kvs_status code, const char* fmt, ...) {
   if (c) {
@@ -697,6 +728,12 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
   (void)hipGetLastError();
   const char* env = getenv("KVS_LOGITS_FP32");
   c->logit_f64 = !(env && env[0] == '1');
+  // the context's device is current here: take its scratch address once
+  if (hipError_t e = scratch_address(c->device, &c->scratch); e != hipSuccess) {
+    c->scratch = nullptr;
+    c->scratch_err = hipGetErrorString(e);
+    (void)hipGetLastError();
+  }
   *out = c;
   return KVS_OK;
 }
@@ -1125,6 +1162,35 @@ kvs_status kvs_value_norms(kvs_ctx ctx, int32_t P, int32_t Z, int32_t d, const f
     return fail(ctx, KVS_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes, need);
   VnormArgs a{};
   a.V = Vz; a.part = static_cast<double*>(ws); a.out = signal; a.P = P; a.Z = Z;
+  a.C = value_norm_chunks(P, Z);
+  launch_value_norms(a, d, ctx->stream);
+  return hip_check(ctx, fn);
+}
+
+size_t kvs_value_norms_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+kvs_status kvs_value_norms_noalloc(kvs_ctx ctx, int32_t P, int32_t Z, int32_t d, const float* Vz,
+                                   double* signal) {
+  const char* fn = "kvs_value_norms_noalloc";
+  if (!ctx) return KVS_ERR_INVALID;
+  ctx->err.clear();
+  if (P < 1 || Z < 1 || (d != 64 && d != 128))
+    return fail(ctx, KVS_ERR_INVALID, "%s: bad sizes P=%d Z=%d d=%d", fn, P, Z, d);
+  KVS_NEED(Vz);
+  if (!signal) return fail(ctx, KVS_ERR_INVALID, "%s: argument 'signal' is NULL", fn);
+  if (!aligned(signal, 8)) return fail(ctx, KVS_ERR_ALIGN, "%s: 'signal' not 8-byte aligned", fn);
+  const size_t need = kvs_value_norms_workspace_bytes(P, Z);
+  if (need > kNoAllocScratchBytes)
+    return fail(ctx, KVS_ERR_INVALID, "%s: P=%d needs %zu bytes of scratch, above the %zu-byte static array",
+                fn, P, need, kNoAllocScratchBytes);
+  if (!ctx->scratch)
+    return fail(ctx, KVS_ERR_HIP, "%s: no scratch address for device %d: %s", fn, ctx->device,
+                ctx->scratch_err.c_str());
+  // the same kernels as kvs_value_norms; the chunk partials go to this
+  // device's static scratch (fully written before they are read: nothing
+  // to clear between calls)
+  VnormArgs a{};
+  a.V = Vz; a.part = static_cast<double*>(ctx->scratch); a.out = signal; a.P = P; a.Z = Z;
   a.C = value_norm_chunks(P, Z);
   launch_value_norms(a, d, ctx->stream);
   return hip_check(ctx, fn);

@@ -293,6 +293,22 @@ size_t kvs_value_norms_workspace_bytes(int32_t P, int32_t Z);
 kvs_status kvs_value_norms(kvs_ctx ctx, int32_t P, int32_t Z, int32_t d, const float* Vz,
                            double* signal, void* ws, size_t ws_bytes);
 
+/* Allocation-free variant of kvs_value_norms, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same kernels and
+ * the same result bits as kvs_value_norms; the chunk partials live in a
+ * static device array of kvs_value_norms_noalloc_max_bytes() bytes (1 MiB),
+ * one copy per GPU, held by the library until the process ends, so no call
+ * allocates anything.  Sizes needing more scratch than that
+ * (kvs_value_norms_workspace_bytes(P, Z) above the limit: P beyond 2048 at
+ * the most chunked Z) return KVS_ERR_INVALID.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.  KVS_ERR_HIP if the
+ * array's device address could not be taken when the context was created. */
+size_t kvs_value_norms_noalloc_max_bytes(void);
+kvs_status kvs_value_norms_noalloc(kvs_ctx ctx, int32_t P, int32_t Z, int32_t d, const float* Vz,
+                                   double* signal);
+
 /* Training queries (gist page, section 2 "Training Query Construction": real
  * queries of the recent context plus synthetic future queries whose content
  * is taken from the context by undoing RoPE and embedded again at future

@@ -210,3 +210,20 @@ def test_allocator_rejects_bad_requests(K):
     with pytest.raises(K.KvsError):
         K.kvs_allocate_budget([1.0, float("nan")], 4, 0.5, 1, 4)
     assert K.kvs_allocate_budget([0.0, 0.0, 0.0], 7).tolist() == [3, 2, 2]
+
+
+def test_noalloc_value_norms_limit_is_checked_on_the_host(K):
+    """The allocation-free value-norm call states its static scratch size and
+    rejects a batch whose chunk partials would not fit, before any launch."""
+    lib = K.load()
+    assert K.value_norms_noalloc_max_bytes() == 1 << 20
+    ctx = ctypes.c_void_p()
+    assert lib.kvs_create(ctypes.byref(ctx), None) == 0
+    fake = ctypes.c_void_p(0x1000)
+    # 200000 problems of one chunk each: 1.6 MB of float64 partials > 1 MiB
+    assert K.value_norms_workspace_bytes(200000, 64) > (1 << 20)
+    st = lib.kvs_value_norms_noalloc(ctx, 200000, 64, 64, fake, fake)
+    assert st == -1 and b"static array" in lib.kvs_last_error(ctx)
+    assert lib.kvs_value_norms_noalloc(ctx, 4, 64, 96, fake, fake) == -1      # d
+    assert lib.kvs_value_norms_noalloc(ctx, 4, 64, 64, None, fake) == -1      # Vz NULL
+    assert lib.kvs_destroy(ctx) == 0
