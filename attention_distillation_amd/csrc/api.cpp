@@ -123,12 +123,21 @@ hipEvent_t prof_event(kvs_ctx c) {
   return e;
 }
 
-// Fold completed launch timings into the per-class totals (stream must be idle
-// or the events complete).
+// Fold the timings of completed launches into the per-class totals; launches
+// still in flight (the schedule drains right after a status copy while the
+// next slot runs) stay pending until a later drain.
 void prof_drain(kvs_ctx c) {
-  for (auto& r : c->pending) {
+  const hipError_t before = hipPeekAtLastError();
+  size_t keep = 0;
+  for (size_t i = 0; i < c->pending.size(); ++i) {
+    ProfRec r = c->pending[i];
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+    const hipError_t e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e == hipErrorNotReady) {
+      c->pending[keep++] = r;
+      continue;
+    }
+    if (e == hipSuccess) {
       ProfAcc& a = c->acc[r.cls];
       a.launches += 1;
       a.ms += ms;
@@ -138,7 +147,9 @@ void prof_drain(kvs_ctx c) {
     c->pool.push_back(r.a);
     c->pool.push_back(r.b);
   }
-  c->pending.clear();
+  c->pending.resize(keep);
+  // an unfinished event is not an error of the caller's work
+  if (before == hipSuccess && hipPeekAtLastError() == hipErrorNotReady) (void)hipGetLastError();
 }
 
 // RAII timer around one kernel launch on the context stream (no-op unless
