@@ -4,6 +4,12 @@ Every number stored here comes from ``oracle/`` (float64) run on the seeded
 synthetic inputs of ``synth``; nothing is read from the GPU path.
 
     python tests/golden/make_golden.py qwen2.5-1.5b-one-layer    # 300 iterations
+    python tests/golden/make_golden.py states     # one-layer iterates at t = 5 and t = 300
+    python tests/golden/make_golden.py pilot      # full-cache pilot, r = 0.3 / 0.5 / 0.7
+    python tests/golden/make_golden.py e2e-llama  # llama3-8b problem 0, k = 2381 and 4680
+    python tests/golden/make_golden.py e2e-long   # long-context problem 0, k = 3226
+
+The pilot set runs its 168 problems in a process pool (one BLAS thread each).
 """
 import json
 import os
@@ -35,8 +41,96 @@ def golden_compress(cid: int, iters: int | None = None, seed: int = 0):
     return out
 
 
+def golden_states(seed: int = 0, stops=(5, 300)):
+    """The oracle's iterates (Kc, Vc) of both one-layer problems after t
+    iterations of the schedule, rounded to float32 (the per-call parity
+    tests feed them to both sides), with the oracle's loss there."""
+    import numpy as np
+    w = WORKLOADS[1]
+    b = make_batch(w, seed)
+    arrays, meta = {}, {"workload": w.name, "seed": seed, "k": w.k0, "stops": list(stops), "loss": {}}
+    for p in range(b["Q"].shape[0]):
+        for t in stops:
+            t0 = time.time()
+            r = O.compress_problem(b["Q"][p], b["Kz"][p], b["Vz"][p], w.k0, b["scale"],
+                                   O.CompressOptions(iters=t))
+            arrays[f"Kc_t{t}_p{p}"] = r["Kc"].astype(np.float32)
+            arrays[f"Vc_t{t}_p{p}"] = r["Vc"].astype(np.float32)
+            meta["loss"][f"t{t}_p{p}"] = r["loss"]
+            print(f"{w.name} p={p} t={t}: loss {r['loss']:.6g} ({time.time() - t0:.1f} s)", flush=True)
+    return arrays, meta
+
+
+def _pilot_one(args):
+    ratio, p, seed = args
+    w = WORKLOADS[2].with_ratio(ratio)
+    b = make_batch(w, seed, problems=[p])
+    r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], w.k0, b["scale"],
+                           O.CompressOptions(iters=w.pilot))
+    return ratio, p, r["mse"], r["flags"]
+
+
+def golden_pilot(seed: int = 0, ratios=(0.3, 0.5, 0.7), workers: int = 5):
+    """The oracle's 60-iteration pilot on every full-cache problem at each
+    ratio: output MSE per problem and the oracle's own allocation."""
+    import concurrent.futures as cf
+    w0 = WORKLOADS[2]
+    jobs = [(r, p, seed) for r in ratios for p in range(w0.P)]
+    res = {}
+    with cf.ProcessPoolExecutor(workers) as ex:
+        for i, (r, p, mse, fl) in enumerate(ex.map(_pilot_one, jobs)):
+            res[(r, p)] = (mse, fl)
+            if i % 8 == 7:
+                print(f"pilot {i + 1}/{len(jobs)}", flush=True)
+    out = {"workload": w0.name, "seed": seed, "pilot_iters": w0.pilot, "alpha": 0.5, "ratios": {}}
+    for r in ratios:
+        w = w0.with_ratio(r)
+        mse = [res[(r, p)][0] for p in range(w.P)]
+        ks = O.allocate_budget(mse, w.k0 * w.P, 0.5, 1, w.Z)
+        out["ratios"][str(r)] = {"k0": w.k0, "mse": mse, "flags": [res[(r, p)][1] for p in range(w.P)],
+                                 "k": ks}
+    return out
+
+
+def golden_e2e(cid: int, p: int, ks, seed: int = 0):
+    """The oracle's whole schedule (Select+Fit, T iterations) on one problem
+    of a large workload at each given k."""
+    w = WORKLOADS[cid]
+    b = make_batch(w, seed, problems=[p])
+    Y, l = O.reference_attention(b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"])
+    out = {"workload": w.name, "seed": seed, "problem": p, "iters": w.T, "runs": []}
+    for k in ks:
+        t0 = time.time()
+        r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], k, b["scale"],
+                               O.CompressOptions(iters=w.T), Y=Y, lse=l, record=True)
+        out["runs"].append({"k": k, "init_loss": r["init_loss"], "final_loss": r["loss"], "mse": r["mse"],
+                            "flags": r["flags"], "traj": [float(v) for v in r["traj"]],
+                            "seconds": time.time() - t0})
+        print(f"{w.name} p={p} k={k}: {r['init_loss']:.6g} -> {r['loss']:.6g} ({time.time() - t0:.1f} s)",
+              flush=True)
+    return out
+
+
 if __name__ == "__main__":
     name = sys.argv[1] if len(sys.argv) > 1 else "qwen2.5-1.5b-one-layer"
+    if name == "states":
+        import numpy as np
+        arrays, meta = golden_states()
+        np.savez_compressed(os.path.join(HERE, "oracle_states_qwen2.5-1.5b-one-layer.npz"), **arrays)
+        with open(os.path.join(HERE, "oracle_states_qwen2.5-1.5b-one-layer.json"), "w") as f:
+            json.dump(meta, f, indent=1)
+        sys.exit(0)
+    if name == "pilot":
+        res = golden_pilot()
+        with open(os.path.join(HERE, "oracle_pilot_qwen2.5-1.5b-full-cache.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        sys.exit(0)
+    if name in ("e2e-llama", "e2e-long"):
+        cid, ks = (3, [2381, 4680]) if name == "e2e-llama" else (4, [3226])
+        res = golden_e2e(cid, 0, ks)
+        with open(os.path.join(HERE, f"oracle_compress_{WORKLOADS[cid].name}_p0.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        sys.exit(0)
     cid = next(c for c, w in WORKLOADS.items() if w.name == name)
     res = golden_compress(cid)
     path = os.path.join(HERE, f"oracle_compress_{name}.json")

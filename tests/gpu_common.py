@@ -19,6 +19,28 @@ def rel(a, b):
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
+def row_err(a, b, floor=0.1):
+    """Worst row-relative error, max over rows i of
+    ||a_i - b_i|| / max(||b_i||, floor * RMS_j ||b_j||).
+
+    A 2-D array's rows are its last-axis vectors; a 1-D array's elements are
+    rows of one entry.  Rows whose reference norm is below ``floor`` times
+    the RMS row norm are measured against that floor instead (an absolute
+    tolerance there), so an error confined to one element or one tile edge
+    fails the bar instead of vanishing into a whole-array norm."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if b.ndim <= 1:
+        a, b = a.reshape(-1, 1), b.reshape(-1, 1)
+    else:
+        a, b = a.reshape(-1, b.shape[-1]), b.reshape(-1, b.shape[-1])
+    nb = np.linalg.norm(b, axis=1)
+    rms = float(np.sqrt(np.mean(nb * nb))) if nb.size else 0.0
+    den = np.maximum(nb, floor * rms)
+    den[den == 0] = 1.0
+    return float(np.max(np.linalg.norm(a - b, axis=1) / den)) if nb.size else 0.0
+
+
 def say(*args):
     print(*args, flush=True)
     sys.stdout.flush()

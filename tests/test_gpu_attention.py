@@ -1,8 +1,20 @@
 """GPU parity: reference attention and loss/gradient through the C ABI.
 
-Bar (relative Frobenius error against the float64 oracle on identical float32
-inputs): 1e-4 for Y, lse, loss, gradient and output MSE.
+Bar against the float64 oracle on identical float32 inputs: 1e-4 relative
+error for loss and output MSE, and 1e-4 for Y, lse and the gradient row by row
+(worst row-relative error, rows below a tenth of the RMS row norm measured
+against that floor; the whole-array Frobenius error is printed beside it).
+The gradient is held to the Frobenius bar everywhere; its rows to 1e-4
+times max(1, amp / 20), amp = ||Y|| / ||Yhat - Y||: the residual that drives
+the gradient is a difference of float32 outputs, so its rounding grows with
+amp (a plain float32 evaluation of the k = Z start of the tiny ragged case,
+amp 197, has row error 1.7e-3 and Frobenius error 7e-4).
+States: the Select+Fit start, that start with perturbed keys, and the
+oracle's own iterates after 5, 20 (single head) and 5 and 300 (one layer,
+stored by tests/golden/make_golden.py) iterations, where the residual the
+gradient depends on is smaller.
 """
+import os
 import math
 
 import numpy as np
@@ -11,7 +23,7 @@ import pytest
 import attention_distillation_amd as K
 from oracle import kvsculpt as O
 from synth import WORKLOADS, make_batch, tiny_workload
-from tests.gpu_common import empty, host, rel, say, to_gpu, workspace
+from tests.gpu_common import empty, host, rel, row_err, say, to_gpu, workspace
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -45,8 +57,9 @@ def test_reference_attention_matches_oracle(name):
     for p in range(b["Q"].shape[0]):
         Y, l = O.reference_attention(b["Q"][p], b["Kz"][p], b["Vz"][p], b["scale"])
         ey, el = rel(Yg[p], Y), rel(lg[p], l)
-        say(f"   p={p} relY={ey:.2e} rel_lse={el:.2e}")
-        assert ey <= TOL and el <= TOL
+        ry, rl = row_err(Yg[p], Y), row_err(lg[p], l)
+        say(f"   p={p} relY={ey:.2e} rel_lse={el:.2e} rowY={ry:.2e} row_lse={rl:.2e}")
+        assert ry <= TOL and rl <= TOL
 
 
 def _loss_case(name, state):
@@ -64,7 +77,10 @@ def _loss_case(name, state):
         Z = Kz.shape[0]
         k = w.k0 if name in ("single-head-d64", "qwen-one-layer") else [1, 17, Z, 33][p % 4]
         k = min(k, Z)
-        if state == "init":
+        if state in ("t5", "t300") and name == "qwen-one-layer":
+            g = np.load(GOLDEN_STATES)
+            Kc, Vc = g[f"Kc_{state}_p{p}"], g[f"Vc_{state}_p{p}"]
+        elif state == "init":
             idx, Kc, Vc, ok = O.init_select_fit(Q, Kz, Y32, l32, k, s)
         elif state == "perturbed":
             idx, Kc, Vc, ok = O.init_select_fit(Q, Kz, Y32, l32, k, s)
@@ -78,8 +94,12 @@ def _loss_case(name, state):
     return w, b, probs
 
 
-LOSS_CASES = [("single-head-d64", "init"), ("single-head-d64", "perturbed"), ("single-head-d64", "t5"), ("single-head-d64", "t20"),
-              ("qwen-one-layer", "init"), ("tiny64-ragged", "init"), ("tiny128-ragged", "perturbed")]
+LOSS_CASES = [("single-head-d64", "init"), ("single-head-d64", "perturbed"), ("single-head-d64", "t5"),
+              ("single-head-d64", "t20"), ("qwen-one-layer", "init"), ("qwen-one-layer", "perturbed"),
+              ("qwen-one-layer", "t5"), ("qwen-one-layer", "t300"), ("tiny64-ragged", "init"),
+              ("tiny128-ragged", "perturbed")]
+GOLDEN_STATES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                             "oracle_states_qwen2.5-1.5b-one-layer.npz")
 
 
 @pytest.mark.parametrize("name,state", LOSS_CASES)
@@ -106,8 +126,12 @@ def test_loss_grad_matches_oracle(name, state):
         m = aux["out"] / (n * d)
         k = Kc32.shape[0]
         eL, eg, em = rel(lg[p], L), rel(gg[off:off + k], g), rel(mg[p], m)
-        say(f"   p={p} k={k} L={L:.6g} relL={eL:.2e} relgrad={eg:.2e} relmse={em:.2e}")
-        assert eL <= TOL and eg <= TOL and em <= TOL
+        rg = row_err(gg[off:off + k], g)
+        amp = float(np.linalg.norm(Y32) / max(np.linalg.norm(aux["R"]), 1e-300))
+        gtol = TOL * max(1.0, amp / 20.0)
+        say(f"   p={p} k={k} L={L:.6g} relL={eL:.2e} relgrad={eg:.2e} rowgrad={rg:.2e} (bar {gtol:.1e}, "
+            f"amplification {amp:.0f}) relmse={em:.2e}")
+        assert eL <= TOL and eg <= TOL and rg <= gtol and em <= TOL
         off += k
 
 

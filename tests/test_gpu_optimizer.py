@@ -20,7 +20,7 @@ import pytest
 import attention_distillation_amd as K
 from oracle import kvsculpt as O
 from synth import WORKLOADS, make_batch, tiny_workload
-from tests.gpu_common import empty, host, rel, say, to_gpu, workspace
+from tests.gpu_common import empty, host, rel, row_err, say, to_gpu, workspace
 
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,8 +80,8 @@ def test_init_topk_matches_oracle(name):
         nd = _check_topk(sel, li, k)
         np.testing.assert_array_equal(kg[off:off + k], Kz[sel])
         V, _, ok = O.ridge_values(Q, ref[p][0], Kz[sel], b["scale"])
-        ev = rel(vg[off:off + k], V)
-        say(f"   p={p} k={k} tie-swaps={nd} relVc={ev:.2e} flags={fg[p]}")
+        ev = row_err(vg[off:off + k], V)
+        say(f"   p={p} k={k} tie-swaps={nd} rowVc={ev:.2e} (frob {rel(vg[off:off + k], V):.2e}) flags={fg[p]}")
         assert ok and fg[p] == 0 and ev <= 1e-4
         off += k
 

@@ -14,7 +14,7 @@ import pytest
 import attention_distillation_amd as K
 from oracle import kvsculpt as O
 from synth import WORKLOADS, make_use_batch, tiny_workload
-from tests.gpu_common import empty, host, pack, rel, say, to_gpu, workspace
+from tests.gpu_common import empty, host, pack, rel, row_err, say, to_gpu, workspace
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -73,10 +73,10 @@ def test_use_eval_matches_oracle(name):
     for p in range(P):
         r = O.use_side_outputs(u["Qh"][p], u["Kz"][p], u["Vz"][p], u["Kr"][p], u["Vr"][p],
                                Kcs[p], Vcs[p], u["scale"])
-        ef, ec = rel(Of[p], r["full"]), rel(Oc[p], r["comp"])
+        ef, ec = row_err(Of[p], r["full"]), row_err(Oc[p], r["comp"])
         amp = 1.0 / max(r["rel"], 1e-30)
         em, er = abs(mse[p] - r["mse"]) / r["mse"], abs(rl[p] - r["rel"]) / r["rel"]
-        say(f"   p={p} relOf={ef:.2e} relOc={ec:.2e} mse={r['mse']:.3e} rel={r['rel']:.3f} "
+        say(f"   p={p} rowOf={ef:.2e} rowOc={ec:.2e} mse={r['mse']:.3e} rel={r['rel']:.3f} "
             f"(amplification {amp:.1f}) err mse={em:.2e} rel={er:.2e}")
         assert ef <= TOL and ec <= TOL
         assert amp < 20
@@ -115,5 +115,5 @@ def test_use_eval_single_query_single_pair():
     for p in range(P):
         r = O.use_side_outputs(u["Qh"][p], u["Kz"][p], u["Vz"][p], u["Kr"][p], u["Vr"][p],
                                Kc[p:p + 1], Vc[p:p + 1], u["scale"])
-        assert rel(Of[p], r["full"]) <= TOL and rel(Oc[p], r["comp"]) <= TOL
+        assert row_err(Of[p], r["full"]) <= TOL and row_err(Oc[p], r["comp"]) <= TOL
         assert abs(mse[p] - r["mse"]) <= TOL * r["mse"]
