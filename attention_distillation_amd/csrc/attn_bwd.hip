@@ -25,7 +25,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   // one query chunk (same G, Q and score rows) share an XCD
   unsigned bx, by, bz;
   xcd_block(bx, by, bz);
-  const int p = by;
+  // logical slot -> problem: the slots of one XCD carry equal total work
+  const int p = a.info[by].xorder;
   // the problem table is read before the status test, which uses it, so the
   // two loads share one round trip
   const ProbInfo pi = a.info[p];

@@ -190,8 +190,10 @@ __device__ __forceinline__ bool gram_tile128(long long t, int KT2, int& I2, int&
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gram128_kernel(GramArgs a) {
-  unsigned bx, by, bz;
-  xcd_block(bx, by, bz);
+  // plain dispatch order: the tiles of every problem spread over all XCDs,
+  // so ragged batches load them evenly (the tiles share little in L2 either
+  // way: they do not sweep the query axis in step)
+  const unsigned bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   const int p = by;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
   const ProbInfo pi = a.info[p];

@@ -19,7 +19,8 @@ struct ProbInfo {
   int k;        // compressed pairs
   int kpad;     // k rounded up to kTile (Gram / Cholesky edge)
   int koff;     // first row of the problem in packed [sum k][d] arrays
-  int pad0;
+  int xorder;   // problem that kernels grouping a problem's workgroups on one XCD
+                // run at logical slot p (slots ordered so each XCD gets equal work)
   long long soff;   // offset (floats) of the problem's stored scores [k][n]
   long long moff;   // offset (floats) of the problem's augmented Gram [(kpad+d)][kpad]
   long long xoff;   // offset (floats) of the problem's padded solve rows [kpad][d]

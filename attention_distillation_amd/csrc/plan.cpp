@@ -61,7 +61,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     q.k = k;
     q.kpad = (k + kTile - 1) / kTile * kTile;
     q.koff = (int)koff;
-    q.pad0 = 0;
+    q.xorder = i;
     q.soff = soff;
     q.moff = moff;
     q.xoff = xoff;
@@ -73,6 +73,23 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     p.kpadmax = std::max(p.kpadmax, q.kpad);
   }
   if (koff > 0x7fffffffLL) return "sum of k too large";
+  // Slot order for kernels that keep each problem's workgroups on one XCD
+  // (a contiguous range of logical slots per XCD): problems by k, largest
+  // first, dealt to the 8 XCDs in snake order, so every XCD gets about the
+  // same number of problems and the same total k.
+  {
+    std::vector<int> byk(p.P);
+    for (int i = 0; i < p.P; ++i) byk[i] = i;
+    std::stable_sort(byk.begin(), byk.end(), [&](int x, int y) { return p.info[x].k > p.info[y].k; });
+    std::vector<std::vector<int>> bin(8);
+    for (int i = 0; i < p.P; ++i) {
+      const int r = i / 8, c = i % 8;
+      bin[(r & 1) ? 7 - c : c].push_back(byk[i]);
+    }
+    int s = 0;
+    for (const auto& b : bin)
+      for (int prob : b) p.info[s++].xorder = prob;
+  }
   p.ktot = koff; p.stot = soff; p.mtot = moff; p.kpadtot = xoff / p.d;
 
   const long long qtiles = (p.n + 63) / 64;
