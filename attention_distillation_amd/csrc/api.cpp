@@ -560,13 +560,17 @@ kvs_status status_buffers(kvs_ctx ctx, int P) {
 void run_init(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Kz,
               const float* Y, const float* lse, float* Kc, float* Vc, int* flags, LbState* st,
               bool keys_given, void* ws) {
+  // the starting values take the refinement step of the standalone solve
+  // (once per run, so its cost does not matter; the re-solves every
+  // vc_every iterations skip it)
   if (!keys_given) {
-    run_init_topk(ctx, pl, b, Q, Kz, Y, lse, at<int>(ws, pl.r_idx), Kc, Vc, flags, st, ws);
+    run_init_topk(ctx, pl, b, Q, Kz, Y, lse, at<int>(ws, pl.r_idx), Kc, Vc, flags, st, ws, true);
     return;
   }
   launch_fill_f32(Vc, 0.f, (long long)pl.ktot * pl.d, ctx->stream);
   run_forward(ctx, pl, b, Q, Y, lse, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, nullptr, ws);
-  run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws);
+  const RefineIn rin{Q, lse, Kc};
+  run_value_solve(ctx, pl, b, Y, Vc, flags, st, kAllStates, ws, &rin);
 }
 
 // Everything before the first iteration: reference attention into the
