@@ -100,11 +100,15 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   // at least six rounds of them (3072) keeps the last round's tail small,
   // while every workgroup keeps at least four query tiles to amortise its
   // fixed cost.  (Measured on the 56-problem full cache: one split 1.86 s,
-  // two 1.70 s, four 1.63 s, six 1.63 s, eight 1.64 s per main run.)
+  // two 1.70 s, four 1.63 s, six 1.63 s, eight 1.64 s per main run.)  No
+  // workgroup sweeps more than 64 query tiles: long sweeps leave long tails
+  // in the launches of the line-search slots, where only the problems whose
+  // trial was accepted run (long-context cache, 280 query tiles: one split
+  // 82.6 TF/s, five 93.4 TF/s over the timed blocks).
   {
     long long ktiles = 0;
     for (const ProbInfo& q : p.info) ktiles += (q.k + 63) / 64;
-    const long long want = (3072 + ktiles - 1) / std::max(1LL, ktiles);
+    const long long want = std::max((3072 + ktiles - 1) / std::max(1LL, ktiles), (qtiles + 63) / 64);
     const long long cap = std::max(1LL, qtiles / 4);
     p.Cn = (int)std::max(1LL, std::min(want, cap));
   }
