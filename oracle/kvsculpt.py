@@ -346,6 +346,11 @@ class CompressOptions:
     lam: float = 1.0
     ridge_rel: float = 1e-3
     lbfgs: LbfgsOptions = dataclasses.field(default_factory=LbfgsOptions)
+    # sensitivity variant: round the keys to float32 at the start and after
+    # every iteration (the loss and gradient are then taken at the rounded
+    # keys).  Not part of the method; it measures how far the schedule's
+    # result moves under perturbations of float32 size.
+    keys_f32: bool = False
 
 
 def compress_problem(Q, Kz, Vz, k, scale, opt: CompressOptions, Y=None, lse=None,
@@ -376,6 +381,8 @@ def compress_problem(Q, Kz, Vz, k, scale, opt: CompressOptions, Y=None, lse=None
         idx, (Kc, Vc), ok = None, init, True
     flags = 0 if ok else FLAG_CHOLESKY
     Kc = _f64(Kc).copy()
+    if opt.keys_f32:
+        Kc = Kc.astype(np.float32).astype(np.float64)
     Vc = _f64(Vc).copy() if Vc is not None else np.zeros_like(Kc)
 
     def make_f(Vc_):
@@ -393,6 +400,11 @@ def compress_problem(Q, Kz, Vz, k, scale, opt: CompressOptions, Y=None, lse=None
     traj = [L0]
     for t in range(1, opt.iters + 1):
         lbfgs_iteration(f, fg, st, opt.lbfgs)
+        if opt.keys_f32:
+            xr = st.x.astype(np.float32).astype(np.float64)
+            if not np.array_equal(xr, st.x):
+                st.x = xr
+                st.L, st.g = fg(st.x)
         if t % opt.vc_every == 0:
             Vn, _, ok = ridge_values(Q, Y, st.x, scale, opt.ridge_rel)
             if ok:

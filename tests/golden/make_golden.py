@@ -10,6 +10,9 @@ synthetic inputs of ``synth``; nothing is read from the GPU path.
     python tests/golden/make_golden.py e2e-long   # long-context problem 0, k = 3226
 
 The pilot set runs its 168 problems in a process pool (one BLAS thread each).
+Each run is stored with the final loss of the same schedule run with its
+keys kept at float32 (the oracle's sensitivity variant); ``--reuse`` keeps
+the plain runs of an existing file and computes only those.
 """
 import json
 import os
@@ -62,24 +65,37 @@ def golden_states(seed: int = 0, stops=(5, 300)):
 
 
 def _pilot_one(args):
-    ratio, p, seed = args
+    ratio, p, seed, plain = args
     w = WORKLOADS[2].with_ratio(ratio)
     b = make_batch(w, seed, problems=[p])
+    Y, l = O.reference_attention(b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"])
+    r32 = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], w.k0, b["scale"],
+                             O.CompressOptions(iters=w.pilot, keys_f32=True), Y=Y, lse=l)
+    if plain is not None:
+        return ratio, p, plain[0], plain[1], plain[2], r32["loss"]
     r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], w.k0, b["scale"],
-                           O.CompressOptions(iters=w.pilot))
-    return ratio, p, r["mse"], r["flags"]
+                           O.CompressOptions(iters=w.pilot), Y=Y, lse=l)
+    return ratio, p, r["mse"], r["flags"], r["loss"], r32["loss"]
 
 
-def golden_pilot(seed: int = 0, ratios=(0.3, 0.5, 0.7), workers: int = 5):
+def golden_pilot(seed: int = 0, ratios=(0.3, 0.5, 0.7), workers: int = 6, previous=None):
     """The oracle's 60-iteration pilot on every full-cache problem at each
-    ratio: output MSE per problem and the oracle's own allocation."""
+    ratio: final loss and output MSE per problem, the oracle's own
+    allocation, and the final loss of the same run with its keys kept at
+    float32 (the sensitivity variant).  ``previous``: a stored result whose
+    plain runs are reused (only the float32-key runs are computed)."""
     import concurrent.futures as cf
     w0 = WORKLOADS[2]
-    jobs = [(r, p, seed) for r in ratios for p in range(w0.P)]
+    def plain(r, p):
+        if previous is None:
+            return None
+        g = previous["ratios"][str(r)]
+        return (g["mse"][p], g["flags"][p], g["loss"][p])
+    jobs = [(r, p, seed, plain(r, p)) for r in ratios for p in range(w0.P)]
     res = {}
     with cf.ProcessPoolExecutor(workers) as ex:
-        for i, (r, p, mse, fl) in enumerate(ex.map(_pilot_one, jobs)):
-            res[(r, p)] = (mse, fl)
+        for i, (r, p, mse, fl, loss, loss32) in enumerate(ex.map(_pilot_one, jobs)):
+            res[(r, p)] = (mse, fl, loss, loss32)
             if i % 8 == 7:
                 print(f"pilot {i + 1}/{len(jobs)}", flush=True)
     out = {"workload": w0.name, "seed": seed, "pilot_iters": w0.pilot, "alpha": 0.5, "ratios": {}}
@@ -88,26 +104,35 @@ def golden_pilot(seed: int = 0, ratios=(0.3, 0.5, 0.7), workers: int = 5):
         mse = [res[(r, p)][0] for p in range(w.P)]
         ks = O.allocate_budget(mse, w.k0 * w.P, 0.5, 1, w.Z)
         out["ratios"][str(r)] = {"k0": w.k0, "mse": mse, "flags": [res[(r, p)][1] for p in range(w.P)],
-                                 "k": ks}
+                                 "loss": [res[(r, p)][2] for p in range(w.P)],
+                                 "loss_f32keys": [res[(r, p)][3] for p in range(w.P)], "k": ks}
     return out
 
 
-def golden_e2e(cid: int, p: int, ks, seed: int = 0):
+def golden_e2e(cid: int, p: int, ks, seed: int = 0, previous=None):
     """The oracle's whole schedule (Select+Fit, T iterations) on one problem
-    of a large workload at each given k."""
+    of a large workload at each given k, and the final loss of the same run
+    with its keys kept at float32.  ``previous``: a stored result whose plain
+    runs are reused."""
     w = WORKLOADS[cid]
     b = make_batch(w, seed, problems=[p])
     Y, l = O.reference_attention(b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"])
     out = {"workload": w.name, "seed": seed, "problem": p, "iters": w.T, "runs": []}
     for k in ks:
         t0 = time.time()
-        r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], k, b["scale"],
-                               O.CompressOptions(iters=w.T), Y=Y, lse=l, record=True)
-        out["runs"].append({"k": k, "init_loss": r["init_loss"], "final_loss": r["loss"], "mse": r["mse"],
-                            "flags": r["flags"], "traj": [float(v) for v in r["traj"]],
-                            "seconds": time.time() - t0})
-        print(f"{w.name} p={p} k={k}: {r['init_loss']:.6g} -> {r['loss']:.6g} ({time.time() - t0:.1f} s)",
-              flush=True)
+        old = next((x for x in (previous or {}).get("runs", []) if x["k"] == k), None)
+        if old is None:
+            r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], k, b["scale"],
+                                   O.CompressOptions(iters=w.T), Y=Y, lse=l, record=True)
+            old = {"k": k, "init_loss": r["init_loss"], "final_loss": r["loss"], "mse": r["mse"],
+                   "flags": r["flags"], "traj": [float(v) for v in r["traj"]], "seconds": time.time() - t0}
+        r32 = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], k, b["scale"],
+                                 O.CompressOptions(iters=w.T, keys_f32=True), Y=Y, lse=l)
+        old["final_loss_f32keys"] = r32["loss"]
+        out["runs"].append(old)
+        r = {"init_loss": old["init_loss"], "loss": old["final_loss"]}
+        print(f"{w.name} p={p} k={k}: {r['init_loss']:.6g} -> {r['loss']:.6g} (float32 keys "
+              f"{old['final_loss_f32keys']:.6g}; {time.time() - t0:.1f} s)", flush=True)
     return out
 
 
@@ -120,14 +145,17 @@ if __name__ == "__main__":
         with open(os.path.join(HERE, "oracle_states_qwen2.5-1.5b-one-layer.json"), "w") as f:
             json.dump(meta, f, indent=1)
         sys.exit(0)
+    reuse = "--reuse" in sys.argv
     if name == "pilot":
-        res = golden_pilot()
+        path = os.path.join(HERE, "oracle_pilot_qwen2.5-1.5b-full-cache.json")
+        res = golden_pilot(previous=json.load(open(path)) if reuse else None)
         with open(os.path.join(HERE, "oracle_pilot_qwen2.5-1.5b-full-cache.json"), "w") as f:
             json.dump(res, f, indent=1)
         sys.exit(0)
     if name in ("e2e-llama", "e2e-long"):
         cid, ks = (3, [2381, 4680]) if name == "e2e-llama" else (4, [3226])
-        res = golden_e2e(cid, 0, ks)
+        path = os.path.join(HERE, f"oracle_compress_{WORKLOADS[cid].name}_p0.json")
+        res = golden_e2e(cid, 0, ks, previous=json.load(open(path)) if reuse else None)
         with open(os.path.join(HERE, f"oracle_compress_{WORKLOADS[cid].name}_p0.json"), "w") as f:
             json.dump(res, f, indent=1)
         sys.exit(0)

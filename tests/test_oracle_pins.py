@@ -428,3 +428,19 @@ def test_nonfinite_value_row_flags_and_freezes():
     np.testing.assert_array_equal(r["Kc"], Kz[r["idx"]].astype(np.float64))
     assert O.compress_problem(Q, Kz, b["Vz"][0], w.k0, b["scale"],
                               O.CompressOptions(iters=10))["flags"] == 0
+
+
+def test_keys_f32_variant_is_the_schedule_at_float32_keys():
+    """The sensitivity variant keeps every iterate float32-representable and
+    reports the loss at those keys; with it off the schedule is unchanged."""
+    w = WORKLOADS[0]
+    b = make_batch(w, 0)
+    Q, Kz, Vz, s = b["Q"][0], b["Kz"][0], b["Vz"][0], b["scale"]
+    plain = O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=7))
+    again = O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=7, keys_f32=False))
+    assert plain["loss"] == again["loss"]
+    r = O.compress_problem(Q, Kz, Vz, w.k0, s, O.CompressOptions(iters=7, keys_f32=True))
+    assert np.array_equal(r["Kc"], r["Kc"].astype(np.float32).astype(np.float64))
+    Y, l = O.reference_attention(Q, Kz, Vz, s)
+    assert r["loss"] == O.loss(Q, Y, l, r["Kc"], r["Vc"], s)
+    assert abs(r["loss"] / plain["loss"] - 1) < 0.05
