@@ -60,39 +60,45 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   for (int i = 0; i < D / 16; ++i) dk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const size_t prow = (size_t)p * n;
-  const float* strow = a.St + pi.soff + (size_t)(kok ? key : 0) * npad;
 
   // Software-pipelined over query tiles: the global loads of tile t+1 (G, Q,
   // the stored scores and the row terms) are issued inside the MFMA work of
-  // tile t.  Rows past qend read the last valid row; their dS is zero, so
-  // they never count.  G is staged row-major; Q transposed: lane l of a quad
-  // covering rows 4 m .. 4 m + 3 and dims 4 c .. 4 c + 3 reads dim 4 c + l of
-  // the four rows (coalesced 4-byte loads across the quads of a wave) and
-  // writes them as one 16-byte row segment of Qt.
+  // tile t.  They go through buffer resources: G, Q and the row terms over
+  // the rows qt .. qend-1 of the tile, so rows past qend read zero (their dS
+  // is zero anyway), and the scores over this wave's 16 key rows, so keys
+  // past k read zero; the lane offsets are fixed.  G is staged row-major; Q
+  // transposed: lane l of a quad covering rows 4 m .. 4 m + 3 and dims
+  // 4 c .. 4 c + 3 reads dim 4 c + l of the four rows (coalesced 4-byte loads
+  // across the quads of a wave) and writes them as one 16-byte row segment
+  // of Qt.
   constexpr int NL = 64 * (D / 4) / 256;   // float4 of G (and of Q) per thread per tile
   const float* Gp = a.G + prow * D;
   const float* Qp = a.Q + prow * D;
+  // first key row of this wave (uniform across it: the resource base needs that)
+  const int kw = kt0 + 16 * __builtin_amdgcn_readfirstlane(wave);
+  const auto rS = buf_rsrc(a.St + pi.soff + (size_t)kw * npad, (long long)min(16, k - kw) * npad * 4);
+  const int soff_l = (lq * npad + 4 * g) * 4;
   f32x4 gpre[NL], qpre[NL], spre[4];
   float epre = 0.f, cpre = 0.f;
   auto prefetch = [&](int qt) {
+    const long long rows = qend - qt;
+    const auto rG = buf_rsrc(Gp + (size_t)qt * D, rows * D * 4);
+    const auto rQ = buf_rsrc(Qp + (size_t)qt * D, rows * D * 4);
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int i = tid + 256 * u;
       const int rg = i / (D / 4), cg = i % (D / 4);
-      gpre[u] = *(const f32x4*)(Gp + (unsigned)(min(qt + rg, qend - 1) * D + 4 * cg));
+      gpre[u] = buf_load4(rG, (rg * D + 4 * cg) * 4);
       const int rq = 4 * (i / (4 * (D / 4))), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qpre[u][j] = Qp[(unsigned)(min(qt + rq + j, qend - 1) * D + dq)];
+      for (int j = 0; j < 4; ++j) qpre[u][j] = buf_load1(rQ, ((rq + j) * D + dq) * 4);
     }
+    const int so = soff_l + qt * 4;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int qrow = qt + 16 * qb + 4 * g;
-      spre[qb] = *(const f32x4*)(strow + (qrow < qend ? qrow : 0));
-    }
+    for (int qb = 0; qb < 4; ++qb) spre[qb] = buf_load4(rS, so + 64 * qb);
     if (tid < 64) {
-      const int qq = min(qt + tid, qend - 1);
-      epre = a.e[prow + qq];
-      cpre = a.crow[prow + qq];
+      epre = buf_load1(buf_rsrc(a.e + prow + qt, rows * 4), tid * 4);
+      cpre = buf_load1(buf_rsrc(a.crow + prow + qt, rows * 4), tid * 4);
     }
   };
   if (qbeg < qend) prefetch(qbeg);
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int li = 16 * qb + 4 * g + r;
         const bool ok = kok && (qt + li) < qend;
-        ds[r] = ok ? expf(sv[r] - es[li]) * (acc[r] + cs[li]) : 0.f;
+        ds[r] = ok ? __expf(sv[r] - es[li]) * (acc[r] + cs[li]) : 0.f;
       }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {

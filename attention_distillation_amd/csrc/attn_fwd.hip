@@ -100,14 +100,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   // K/V tile staging: the loads of a batch of NB float4 per thread are issued
   // together, then written to LDS; two batches keep the registers of one
-  // batch small enough for two waves per SIMD.  Rows past kend read the last
-  // valid row: their scores are replaced by -inf, so their softmax weights
-  // are exactly zero and the values they carry never count.
+  // batch small enough for two waves per SIMD.  The loads go through buffer
+  // resources over the rows kt .. kend-1 at fixed lane offsets: rows past
+  // kend read zero, their scores are replaced by -inf, so their softmax
+  // weights are exactly zero and the values they carry never count.
   constexpr int NL = 64 * (D / 4) / 256;     // float4 of K (and V) per thread per tile
   constexpr int NB = NL >= 4 ? NL / 2 : NL;  // per batch
   const float* Kp = a.K + (size_t)koff * D;
   const float* Vp = a.V + (size_t)koff * D;
+  // stored scores: row (key) kt + 16 b + out_row(g, r) of this lane's query;
+  // the lane's part of the offset is fixed, the row part is uniform
+  const int st_lane = (F64 ? g : 4 * g) * npad + q;
   for (int kt = kbeg; kt < kend; kt += 64) {
+    const long long rows = kend - kt;
+    const auto rK = buf_rsrc(Kp + (size_t)kt * D, rows * D * 4);
+    const auto rV = buf_rsrc(Vp + (size_t)kt * D, rows * D * 4);
     __syncthreads();
 #pragma unroll
     for (int u0 = 0; u0 < NL; u0 += NB) {
@@ -116,13 +123,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int u = 0; u < NB; ++u) {
         const int i = tid + 256 * (u0 + u);
         const int row = i / (D / 4), c4 = i % (D / 4);
-        kv[u] = *(const f32x4*)(Kp + (unsigned)(min(kt + row, kend - 1) * D + 4 * c4));
+        kv[u] = buf_load4(rK, (row * D + 4 * c4) * 4);
         // V: lane l of quad i / 4 reads dim 4 c4v + l of the quad's four keys
         // (four coalesced 4-byte loads), i.e. one 16-byte row segment of Vt
         const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vv[u][j] = Vp[(unsigned)(min(kt + vt_key<F64>(vg, j), kend - 1) * D + dim)];
+        for (int j = 0; j < 4; ++j) vv[u][j] = buf_load1(rV, (vt_key<F64>(vg, j) * D + dim) * 4);
       }
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
@@ -179,7 +185,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (key >= kend) {
           sv[b][r] = -INFINITY;
         } else if (STORE && qok) {
-          a.St[soff + (size_t)key * npad + q] = sv[b][r];
+          float* srow = a.St + soff + (size_t)(kt + 16 * b + (F64 ? 4 * r : r)) * npad;
+          srow[st_lane] = sv[b][r];
         }
       }
     }

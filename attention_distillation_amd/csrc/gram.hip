@@ -166,40 +166,38 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
 
 // 128x128 output tiles for batches with many tiles: each staged weight is
 // used by 128 outputs instead of 64, which halves the exp work and the LDS
-// operand reads per flop.  Tile t of a problem with KT2 = ceil(KT / 2)
-// 128-key tiles is (I2, J2) of the lower triangle, then (KT2, J2) for the d
-// value rows of Y^T A (one 128-row tile).  Results go to the same 64-tile
-// layout of M as gram_kernel's; rows and columns past kpad (odd KT) and the
-// strictly upper quadrant of a diagonal tile are not written.
-__device__ __forceinline__ bool gram_tile128(long long t, int KT2, int& I2, int& J2) {
-  const long long tri = (long long)KT2 * (KT2 + 1) / 2;
-  if (t < tri) {
-    int i = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-    while ((long long)(i + 1) * (i + 2) / 2 <= t) ++i;
-    while ((long long)i * (i + 1) / 2 > t) --i;
-    I2 = i;
-    J2 = (int)(t - (long long)i * (i + 1) / 2);
-    return true;
-  }
-  const long long u = t - tri;
-  if (u >= KT2) return false;
-  I2 = KT2;
-  J2 = (int)u;
-  return true;
-}
-
+// operand reads per flop.  A problem with KT2 = ceil(KT / 2) 128-key tiles
+// has the tiles (I2, J2) of the lower triangle plus (KT2, J2) for the d value
+// rows of Y^T A (one 128-row tile).  Results go to the same 64-tile layout of
+// M as gram_kernel's; rows and columns past kpad (odd KT) and the strictly
+// upper quadrant of a diagonal tile are not written.
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gram128_kernel(GramArgs a) {
-  // plain dispatch order: the tiles of every problem spread over all XCDs,
-  // so ragged batches load them evenly (the tiles share little in L2 either
-  // way: they do not sweep the query axis in step)
-  const unsigned bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-  const int p = by;
+  // Workgroup L runs on XCD L % 8 (hardware round-robin) as that XCD's
+  // (L / 8)-th workgroup, and an XCD holds 64 of these (two per CU).  The
+  // flat tile order (problems in order, each in gram_queue_tile's 8x8-block
+  // order) is cut into rounds of 64 tiles dealt to the XCDs in turn, so the
+  // tiles that run together on one XCD come from one or two blocks: they
+  // start together, sweep the query axis at the same pace and share their
+  // score strips in that XCD's L2.  Every XCD gets the same number of
+  // rounds, give or take one.
+  const unsigned L = blockIdx.x, bz = blockIdx.z;
+  const unsigned slot = L >> 3;
+  const long long f = ((long long)(slot >> 6) * 8 + (L & 7)) * 64 + (slot & 63);
+  if (f >= a.gtot) return;
+  // problem of flat tile f: the last one whose first tile is <= f
+  int lo = 0, hi = a.P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.info[mid].gtoff <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  const int p = lo;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
   const ProbInfo pi = a.info[p];
   const int KT = pi.kpad / 64, KT2 = (KT + 1) / 2;
   int I2, J2;
-  if (!gram_tile128(bx, KT2, I2, J2)) return;
+  if (!gram_queue_tile(f - pi.gtoff, KT2, I2, J2)) return;
   const int n = a.n, npad = (n + 3) & ~3;
   const int nq = ((((n + a.Cg - 1) / a.Cg) + 63) / 64) * 64;
   const int qbeg = bz * nq, qend = min(n, qbeg + nq);
@@ -228,24 +226,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // MFMA work of this one.  Key tiles: element u of a thread (i = tid + 512 u)
   // is key i / 16, queries 4 (i % 16) .. + 3 (one 16-byte load); value rows:
   // dim i % 128, queries 4 (i / 128) .. + 3 (four 4-byte loads), landing
-  // transposed with one 16-byte LDS store.  Keys past k read the last key;
-  // queries past qend are zeroed; dims past d are zero.
+  // transposed with one 16-byte LDS store.  The loads go through buffer
+  // resources over the tile's score rows (keys past k read zero; those rows
+  // and columns are replaced by the identity later), the problem's e and Y
+  // rows (queries past n read zero); queries past qend are zeroed; dims past
+  // d are zero.  Every offset that the range check needs is in the lane
+  // offset.
   const int qk4 = 4 * (tid & 15);
+  const auto rE = buf_rsrc(E, (long long)n * 4);
+  const auto rY = buf_rsrc(Y, (long long)n * D * 4);
+  const auto rR = buf_rsrc(St + (size_t)keyR * npad, (long long)min(128, pi.k - keyR) * npad * 4);
+  const auto rC = buf_rsrc(St + (size_t)keyC * npad, (long long)min(128, pi.k - keyC) * npad * 4);
   f32x4 pr[4], pc[4], ev;
   auto prefetch = [&](int qt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ev[j] = E[min(qt + qk4 + j, n - 1)];
+    ev = buf_load4(rE, (qt + qk4) * 4);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = tid + 512 * u;
       if (yrows) {
         const int dim = i & 127, qy = qt + 4 * (i >> 7);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pr[u][j] = dim < D ? Y[(size_t)min(qy + j, n - 1) * D + dim] : 0.f;
+        for (int j = 0; j < 4; ++j) pr[u][j] = dim < D ? buf_load1(rY, ((qy + j) * D + dim) * 4) : 0.f;
       } else {
-        pr[u] = *(const f32x4*)(St + (size_t)min(keyR + (i >> 4), pi.k - 1) * npad + min(qt + qk4, npad - 4));
+        pr[u] = buf_load4(rR, ((i >> 4) * npad + qt + qk4) * 4);
       }
-      if (!diag) pc[u] = *(const f32x4*)(St + (size_t)min(keyC + (i >> 4), pi.k - 1) * npad + min(qt + qk4, npad - 4));
+      if (!diag) pc[u] = buf_load4(rC, ((i >> 4) * npad + qt + qk4) * 4);
     }
   };
   auto weights = [&](f32x4 v, int q0) {
@@ -318,7 +323,9 @@ void launch_gram(const GramArgs& a, int d, hipStream_t s) {
   const long long KT2 = (KT + 1) / 2;
   const long long T2 = KT2 * (KT2 + 1) / 2 + KT2;
   if ((long long)a.P * T2 * a.Cg >= 512) {
-    dim3 grid2((unsigned)T2, a.P, a.Cg);
+    // whole rounds of 64 tiles on each of the 8 XCDs
+    const long long rounds = (a.gtot + 64 * 8 - 1) / (64 * 8);
+    dim3 grid2((unsigned)(rounds * 64 * 8), 1, a.Cg);
     if (d == 128) hipLaunchKernelGGL((gram128_kernel<128>), grid2, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gram128_kernel<64>), grid2, dim3(512), 0, s, a);
     return;

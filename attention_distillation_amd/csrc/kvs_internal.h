@@ -14,6 +14,22 @@ constexpr int kHistMax = 16;            // L-BFGS pairs kept at most
 constexpr int kSlots = kHistMax + 1;    // ring slots (history + one staging slot)
 constexpr int kTile = 64;               // key/query tile edge used across kernels
 
+// Raw buffer resource over `bytes` bytes from `base` (both uniform across the
+// wave).  Loads through it at byte offsets at or past `bytes` return zero, so
+// the loads of a tile that runs past the end of its range need no clamping.
+// The last descriptor word selects untyped 32-bit access on gfx9 parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, long long bytes) {
+  const int nr = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, 0x00020000);
+}
+// 16 (4) bytes at byte offset `off` of the resource, as floats
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // Per-problem geometry, uploaded once per call into the workspace.
 struct ProbInfo {
   int k;        // compressed pairs
@@ -24,6 +40,8 @@ struct ProbInfo {
   long long soff;   // offset (floats) of the problem's stored scores [k][n]
   long long moff;   // offset (floats) of the problem's augmented Gram [(kpad+d)][kpad]
   long long xoff;   // offset (floats) of the problem's padded solve rows [kpad][d]
+  int gtoff;        // first tile of the problem in the flat order of the 128x128 Gram tiles
+  int pad1;
 };
 
 // L-BFGS / line-search status of one problem.
@@ -156,8 +174,55 @@ struct GramArgs {
   float* Mpart;            // [Cg][sum M]
   const ProbInfo* info;
   int P, n, Cg, kpadmax; long long mtot;
+  long long gtot;          // 128x128 tiles of all problems (flat order, see gram_queue_tile)
 };
 void launch_gram(const GramArgs& a, int d, hipStream_t s);
+
+// 128x128 Gram tiles of a problem with KT2 = ceil(kpad / 128) key tiles: the
+// lower triangle of key rows plus one row of value tiles (Y^T A).
+__host__ __device__ inline long long gram128_tiles(int KT2) {
+  return (long long)KT2 * (KT2 + 1) / 2 + KT2;
+}
+
+// Tile u (0 .. gram128_tiles(KT2) - 1) of a problem in its operand-sharing
+// order -> tile row I2 (KT2: the value row) and column J2.  The tile grid
+// (rows 0..KT2, columns 0..KT2-1, J2 <= I2 for key rows) is cut into 8x8
+// blocks taken row by row, tiles row by row inside a block, so that 64
+// consecutive tiles read at most 16 row strips of the stored scores instead
+// of up to 128.
+__host__ __device__ inline bool gram_queue_tile(long long u, int KT2, int& I2, int& J2) {
+  const int NBr = (KT2 + 8) / 8, NBc = (KT2 + 7) / 8;
+  for (int BI = 0; BI < NBr; ++BI) {
+    const int r0 = 8 * BI, r1 = (r0 + 8 < KT2 + 1) ? r0 + 8 : KT2 + 1;
+    const int nbj = (BI + 1 < NBc) ? BI + 1 : NBc;
+    for (int BJ = 0; BJ < nbj; ++BJ) {
+      const int c0 = 8 * BJ, c1 = (c0 + 8 < KT2) ? c0 + 8 : KT2;
+      long long cnt;
+      if (BI > BJ) {
+        cnt = (long long)(r1 - r0) * (c1 - c0);
+      } else {
+        // diagonal block: key row r takes columns c0..r, the value row all
+        const int m = (r1 < KT2) ? r1 : KT2, t = m - r0;
+        cnt = (long long)t * (t + 1) / 2 + (KT2 < r1 ? c1 - c0 : 0);
+      }
+      if (u >= cnt) {
+        u -= cnt;
+        continue;
+      }
+      for (int r = r0; r < r1; ++r) {
+        const int cn = (r == KT2) ? c1 - c0 : ((r + 1 < c1 ? r + 1 : c1) - c0);
+        if (u < cn) {
+          I2 = r;
+          J2 = c0 + (int)u;
+          return true;
+        }
+        u -= cn;
+      }
+      return false;
+    }
+  }
+  return false;
+}
 
 struct GramReduceArgs {
   const float* Mpart; float* M; double* trpart; const LbState* st; int active_mask;

@@ -36,6 +36,8 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   if (b->d != 64 && b->d != 128) return "d must be 64 or 128";
   if (b->Z < 1) return "Z must be >= 1";
   if (b->n < 1) return "n must be >= 1";
+  // tile loads address up to 128 rows of the stored scores with 32-bit byte offsets
+  if (b->n > (1 << 22)) return "n must be <= 4194304";
   if (!(b->scale > 0.0)) return "scale must be > 0";
   if (!(b->lambda >= 0.0)) return "lambda must be >= 0";
   if (!(b->ridge_rel >= 0.0)) return "ridge_rel must be >= 0";
@@ -53,7 +55,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p = Plan();
   p.P = b->P; p.d = b->d; p.Z = b->Z; p.n = b->n; p.npad = (b->n + 3) & ~3; p.H = H;
   p.info.resize(p.P);
-  long long koff = 0, soff = 0, moff = 0, xoff = 0;
+  long long koff = 0, soff = 0, moff = 0, xoff = 0, gtoff = 0;
   for (int i = 0; i < p.P; ++i) {
     int k = b->k ? b->k[i] : b->Z;
     if (k < 1 || k > b->Z) return "k[p] must be in [1, Z]";
@@ -65,6 +67,9 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     q.soff = soff;
     q.moff = moff;
     q.xoff = xoff;
+    q.gtoff = (int)gtoff;
+    q.pad1 = 0;
+    gtoff += gram128_tiles((q.kpad / kTile + 1) / 2);
     koff += k;
     soff += (long long)k * p.npad;
     moff += (long long)(q.kpad + p.d) * q.kpad;
@@ -73,6 +78,8 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     p.kpadmax = std::max(p.kpadmax, q.kpad);
   }
   if (koff > 0x7fffffffLL) return "sum of k too large";
+  if (gtoff > 0x7fffffffLL / 2) return "too many Gram tiles";
+  p.gtot = gtoff;
   // Slot order for kernels that keep each problem's workgroups on one XCD
   // (a contiguous range of logical slots per XCD): problems by k, largest
   // first, dealt to the 8 XCDs in snake order, so every XCD gets about the
