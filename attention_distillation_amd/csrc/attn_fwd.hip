@@ -109,12 +109,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const float* Kp = a.K + (size_t)koff * D;
   const float* Vp = a.V + (size_t)koff * D;
   // stored scores: row (key) kt + 16 b + out_row(g, r) of this lane's query;
-  // the lane's part of the offset is fixed, the row part is uniform
-  const int st_lane = (F64 ? g : 4 * g) * npad + q;
+  // the lane's part of the byte offset is fixed, the row part is uniform
+  const int st_lane = ((F64 ? g : 4 * g) * npad + q) * 4;
   for (int kt = kbeg; kt < kend; kt += 64) {
     const long long rows = kend - kt;
     const auto rK = buf_rsrc(Kp + (size_t)kt * D, rows * D * 4);
     const auto rV = buf_rsrc(Vp + (size_t)kt * D, rows * D * 4);
+    const auto rSt = buf_rsrc(STORE ? a.St + soff + (size_t)kt * npad : nullptr, STORE ? rows * npad * 4 : 0);
+    const bool tail = kt + 64 > kend;   // the chunk's last tile may hold keys past kend
     __syncthreads();
 #pragma unroll
     for (int u0 = 0; u0 < NL; u0 += NB) {
@@ -181,12 +183,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kt + 16 * b + out_row<F64>(g, r);
-        if (key >= kend) {
+        if (tail && kt + 16 * b + out_row<F64>(g, r) >= kend) {
           sv[b][r] = -INFINITY;
         } else if (STORE && qok) {
-          float* srow = a.St + soff + (size_t)(kt + 16 * b + (F64 ? 4 * r : r)) * npad;
-          srow[st_lane] = sv[b][r];
+          buf_store1(rSt, st_lane, (16 * b + (F64 ? 4 * r : r)) * npad * 4, sv[b][r]);
         }
       }
     }
@@ -199,15 +199,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);   // finite: the tile holds a valid key
-    const float corr = expf(m_run - m_new);
-    l_run *= corr;
+    // The running sums are rescaled only when some query's maximum moved (a
+    // factor of exactly 1 elsewhere); exponentials in the hardware exp2 form
+    // of arguments relative to the running maximum, so only weights far below
+    // the largest carry its product rounding.
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const float corr = __expf(m_run - m_new);
+      l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+      for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sv[b][r] = expf(sv[b][r] - m_new);
+        sv[b][r] = __expf(sv[b][r] - m_new);
         l_run += sv[b][r];
       }
     m_run = m_new;
@@ -270,29 +276,36 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(FwdArgs a) {
 
   constexpr int NL = 64 * (D / 4) / 256;     // float4 of V per thread per tile
   const float* Vp = a.V + (size_t)koff * D;
-  const float* Sp = a.Sload + soff;
+  // this lane's scores: fixed lane part of the byte offset, uniform row part
+  const int st_lane = ((F64 ? g : 4 * g) * npad + q) * 4;
   for (int kt = kbeg; kt < kend; kt += 64) {
+    const long long rows = kend - kt;
+    const auto rS = buf_rsrc(a.Sload + soff + (size_t)kt * npad, rows * npad * 4);
+    const auto rV = buf_rsrc(Vp + (size_t)kt * D, rows * D * 4);
+    const bool tail = kt + 64 > kend;
     // this lane's scores (query q, keys of the score layout); rows past kend
-    // are -inf, queries past n 0 (as the forward forms them).  The bound
-    // between the PV products and these loads is the MFMA work and the
-    // partial outputs, not the scores' 64-byte segments.
+    // are -inf, queries past n 0 (as the forward forms them), neither is
+    // loaded.  The bound between the PV products and these loads is the MFMA
+    // work and the partial outputs, not the scores' 64-byte segments.
     float sv[4][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kt + 16 * b + out_row<F64>(g, r);
-        sv[b][r] = key >= kend ? -INFINITY : (qok ? Sp[(size_t)key * npad + q] : 0.f);
+        if (tail && kt + 16 * b + out_row<F64>(g, r) >= kend) sv[b][r] = -INFINITY;
+        else sv[b][r] = qok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                  rS, st_lane, (16 * b + (F64 ? 4 * r : r)) * npad * 4, 0))
+                            : 0.f;
       }
     __syncthreads();
+    // V rows past kend read zero (their weights are exactly zero)
     f32x4 vv[NL];
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int i = tid + 256 * u;
       const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vv[u][j] = Vp[(unsigned)(min(kt + vt_key<F64>(vg, j), kend - 1) * D + dim)];
+      for (int j = 0; j < 4; ++j) vv[u][j] = buf_load1(rV, (vt_key<F64>(vg, j) * D + dim) * 4);
     }
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
@@ -310,15 +323,21 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(FwdArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float m_new = fmaxf(m_run, tmax);   // finite: the tile holds a valid key
-    const float corr = expf(m_run - m_new);
-    l_run *= corr;
+    // The running sums are rescaled only when some query's maximum moved (a
+    // factor of exactly 1 elsewhere); exponentials in the hardware exp2 form
+    // of arguments relative to the running maximum, so only weights far below
+    // the largest carry its product rounding.
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const float corr = __expf(m_run - m_new);
+      l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+      for (int i = 0; i < D / 16; ++i) oacc[i] *= corr;
+    }
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sv[b][r] = expf(sv[b][r] - m_new);
+        sv[b][r] = __expf(sv[b][r] - m_new);
         l_run += sv[b][r];
       }
     m_run = m_new;

@@ -29,6 +29,11 @@ __device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// 4 bytes to byte offset voff + soff of the resource (soff uniform); callers
+// store only in range
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, int voff, int soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, voff, soff, 0);
+}
 
 // Per-problem geometry, uploaded once per call into the workspace.
 struct ProbInfo {
