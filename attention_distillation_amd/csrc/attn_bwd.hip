@@ -20,7 +20,9 @@ __device__ __forceinline__ f32x4 mfma_f32b(float a, float b, f32x4 c) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
+// two waves per SIMD (its LDS tiles allow two workgroups per CU); the
+// register budget that leaves is 256
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_kernel(BwdArgs a) {
   // logical block: key tile bx of problem p, query chunk bz; the key tiles of
   // one query chunk (same G, Q and score rows) share an XCD
   unsigned bx, by, bz;
@@ -41,7 +43,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
 
   __shared__ float Gs[64][D + 4];
   __shared__ float Qt[D][64 + 4];
-  __shared__ float es[64], cs[64];
+  __shared__ __align__(16) float es[64];
+  __shared__ __align__(16) float cs[64];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lq = lane & 15;
@@ -126,6 +129,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
       // the next tile's loads are issued inside the MFMA work of this one
       if (qb == 1 && qt + 64 < qend) prefetch(qt + 64);
       const f32x4 sv = svv[qb];
+      // row terms of this lane's four query rows, read ahead of the dA chain
+      const f32x4 e4 = *(const f32x4*)&es[16 * qb + 4 * g];
+      const f32x4 c4 = *(const f32x4*)&cs[16 * qb + 4 * g];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) {
@@ -135,12 +141,14 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
         acc = mfma_f32b(gv.z, vr[4 * j + 2], acc);
         acc = mfma_f32b(gv.w, vr[4 * j + 3], acc);
       }
+      // dS without branches; rows past qend are selected away (their stored
+      // scores may be padding).  Keys past k need no mask: a key's dS only
+      // reaches its own row of dK, and those rows are not written.
       float ds[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int li = 16 * qb + 4 * g + r;
-        const bool ok = kok && (qt + li) < qend;
-        ds[r] = ok ? __expf(sv[r] - es[li]) * (acc[r] + cs[li]) : 0.f;
+        const float v = __expf(sv[r] - e4[r]) * (acc[r] + c4[r]);
+        ds[r] = (qt + 16 * qb + 4 * g + r < qend) ? v : 0.f;
       }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {

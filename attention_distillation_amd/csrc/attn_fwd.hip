@@ -98,50 +98,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K/V tile staging: the loads of a batch of NB float4 per thread are issued
-  // together, then written to LDS; two batches keep the registers of one
-  // batch small enough for two waves per SIMD.  The loads go through buffer
-  // resources over the rows kt .. kend-1 at fixed lane offsets: rows past
-  // kend read zero, their scores are replaced by -inf, so their softmax
-  // weights are exactly zero and the values they carry never count.
+  // K/V tile staging, pipelined over the two phases of a tile: the next
+  // tile's K is loaded into registers during this tile's score products and
+  // written to LDS once every wave has finished reading K; its V is loaded
+  // during the P V products and written once every wave has finished reading
+  // V.  Two barriers per tile separate the phases, and only LDS stores sit
+  // between them.  The loads go through buffer resources that end at kend:
+  // rows past kend read zero, their scores are replaced by -inf, so their
+  // softmax weights are exactly zero and the values they carry never count.
+  // Every load of a thread uses one lane offset: K batch u (RPU rows) has a
+  // resource of its own, V batch u is an immediate offset.
   constexpr int NL = 64 * (D / 4) / 256;     // float4 of K (and V) per thread per tile
-  constexpr int NB = NL >= 4 ? NL / 2 : NL;  // per batch
+  constexpr int RPU = 1024 / D;              // K rows per batch of 256 float4
   const float* Kp = a.K + (size_t)koff * D;
   const float* Vp = a.V + (size_t)koff * D;
+  const int k_lane = ((tid / (D / 4)) * D + 4 * (tid % (D / 4))) * 4;
+  auto load_k = [&](int kt, f32x4 (&kr)[NL]) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int r0 = kt + RPU * u;
+      kr[u] = buf_load4(buf_rsrc(Kp + (size_t)r0 * D, (long long)(kend - r0) * D * 4), k_lane);
+    }
+  };
+  auto store_k = [&](const f32x4 (&kr)[NL]) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) *(f32x4*)&Ks[RPU * u + tid / (D / 4)][4 * (tid % (D / 4))] = kr[u];
+  };
+  // V: wave w stages keys 16 w .. 16 w + 15, lane l key 16 w + (l & 15) and
+  // dims 16 u + 4 (l >> 4) .. + 3 of batch u (one 16-byte load); the four
+  // floats go to the four Vt rows of those dims, in the column that vt_col
+  // gives the key (the 64 lanes of each store hit 64 different banks)
+  const int v_key = 16 * (tid >> 6) + (lane & 15);
+  const int v_lane = (v_key * D + 4 * (lane >> 4)) * 4;
+  const int v_col = 16 * (tid >> 6) + vt_col<F64>(lane & 15);
+  auto load_v = [&](int kt, f32x4 (&vr)[NL]) {
+    const auto rV = buf_rsrc(Vp + (size_t)kt * D, (long long)(kend - kt) * D * 4);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) vr[u] = buf_load4(rV, v_lane + 64 * u);
+  };
+  auto store_v = [&](const f32x4 (&vr)[NL]) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Vt[16 * u + 4 * (lane >> 4) + j][v_col] = vr[u][j];
+  };
   // stored scores: row (key) kt + 16 b + out_row(g, r) of this lane's query;
   // the lane's part of the byte offset is fixed, the row part is uniform
   const int st_lane = ((F64 ? g : 4 * g) * npad + q) * 4;
+  f32x4 kpre[NL], vpre[NL];
+  if (kbeg < kend) {
+    load_k(kbeg, kpre);
+    load_v(kbeg, vpre);
+    store_k(kpre);
+    store_v(vpre);
+  }
+  __syncthreads();
   for (int kt = kbeg; kt < kend; kt += 64) {
-    const long long rows = kend - kt;
-    const auto rK = buf_rsrc(Kp + (size_t)kt * D, rows * D * 4);
-    const auto rV = buf_rsrc(Vp + (size_t)kt * D, rows * D * 4);
-    const auto rSt = buf_rsrc(STORE ? a.St + soff + (size_t)kt * npad : nullptr, STORE ? rows * npad * 4 : 0);
-    const bool tail = kt + 64 > kend;   // the chunk's last tile may hold keys past kend
-    __syncthreads();
-#pragma unroll
-    for (int u0 = 0; u0 < NL; u0 += NB) {
-      f32x4 kv[NB], vv[NB];
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int i = tid + 256 * (u0 + u);
-        const int row = i / (D / 4), c4 = i % (D / 4);
-        kv[u] = buf_load4(rK, (row * D + 4 * c4) * 4);
-        // V: lane l of quad i / 4 reads dim 4 c4v + l of the quad's four keys
-        // (four coalesced 4-byte loads), i.e. one 16-byte row segment of Vt
-        const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vv[u][j] = buf_load1(rV, (vt_key<F64>(vg, j) * D + dim) * 4);
-      }
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int i = tid + 256 * (u0 + u);
-        const int row = i / (D / 4), c4 = i % (D / 4);
-        *(f32x4*)&Ks[row][4 * c4] = kv[u];
-        const int q4 = i >> 2, vg = q4 / (D / 4), dim = 4 * (q4 % (D / 4)) + (i & 3);
-        *(f32x4*)&Vt[dim][16 * (vg >> 2) + 4 * (vg & 3)] = vv[u];
-      }
-    }
-    __syncthreads();
+    const bool more = kt + 64 < kend;
+    const bool tail = !more && kt + 64 > kend;   // the chunk's last tile may hold keys past kend
+    if (more) load_k(kt + 64, kpre);
 
     float sv[4][4];
     if constexpr (F64) {
@@ -181,14 +196,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[b][r] = (float)((double)acc[r] * a.scale - shift);
       }
+    }
+    // the scores of the tile's keys go to St (queries past n have no row);
+    // keys past kend are not stored and get -inf
+    if (STORE && qok) {
+      const auto rSt = buf_rsrc(a.St + soff + (size_t)kt * npad, (long long)(kend - kt) * npad * 4);
+      if (!tail) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (tail && kt + 16 * b + out_row<F64>(g, r) >= kend) {
-          sv[b][r] = -INFINITY;
-        } else if (STORE && qok) {
-          buf_store1(rSt, st_lane, (16 * b + (F64 ? 4 * r : r)) * npad * 4, sv[b][r]);
-        }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) buf_store1(rSt, st_lane, (16 * b + (F64 ? 4 * r : r)) * npad * 4, sv[b][r]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kt + 16 * b + out_row<F64>(g, r) < kend)
+              buf_store1(rSt, st_lane, (16 * b + (F64 ? 4 * r : r)) * npad * 4, sv[b][r]);
       }
+    }
+    if (tail) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kt + 16 * b + out_row<F64>(g, r) >= kend) sv[b][r] = -INFINITY;
+    }
+    __syncthreads();   // every wave is done with this tile's K
+    if (more) {
+      store_k(kpre);
+      load_v(kt + 64, vpre);
     }
 
     float tmax = sv[0][0];
@@ -228,6 +265,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         oacc[db] = mfma_f32(vv.z, sv[b][2], oacc[db]);
         oacc[db] = mfma_f32(vv.w, sv[b][3], oacc[db]);
       }
+    __syncthreads();   // every wave is done with this tile's V (and the next K is in)
+    if (more) store_v(vpre);
   }
 
   l_run += __shfl_xor(l_run, 16);
