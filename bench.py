@@ -81,12 +81,12 @@ def mixed_fwd_peak():
 # workloads report null.
 MEASURED_TRAFFIC = {
     # long-context default bench, the timed blocks' dispatches:
-    # loss-mode forward: FETCH 7170787.7 KiB x 1.99980 + WRITE 18557011.6 KiB x 1.00000 per dispatch
+    # loss-mode forward: FETCH 7378330.0 KiB x 1.99980 + WRITE 18403829.8 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
-        {"bytes": 33686659251, "source": "attn_fwd.hip", "sha": "84890aef4602e063"},
-    # Gram: FETCH 359793248.8 KiB x 1.99980 + WRITE 2764448.0 KiB x 1.00000 per dispatch
+        {"bytes": 33954818883, "source": "attn_fwd.hip", "sha": "0731476bccde8379"},
+    # Gram: FETCH 324121861.5 KiB x 1.99980 + WRITE 2763232.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-7b-long-context"):
-        {"bytes": 739612419087, "source": "gram.hip", "sha": "f4648aa32ec46fb8"},
+        {"bytes": 666564236367, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
     # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
     ("build_queries", "qwen2.5-1.5b-full-cache"):
         {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
