@@ -93,10 +93,10 @@ MEASURED_TRAFFIC = {
     # loss-mode forward: FETCH 9626.8 KiB x 1.99978 + WRITE 52500.0 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-1.5b-one-layer"):
         {"bytes": 73473514, "source": "attn_fwd.hip", "sha": "b27ce2ca39f20c44"},
-    # standalone value solve, 128x128 Gram tiles: FETCH 2606685.1 KiB x 1.99978
+    # standalone value solve, 128x128 Gram tiles: FETCH 2483836.3 KiB x 1.99980
     # + WRITE 134400.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-1.5b-full-cache solve"):
-        {"bytes": 5475519395, "source": "gram.hip", "sha": "0a5a0e05b43b778e"},
+        {"bytes": 5224009779, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
 }
 
 
