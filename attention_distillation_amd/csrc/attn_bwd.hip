@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   f32x4 gpre[NL], qpre[NL], spre[4];
   float epre = 0.f, cpre = 0.f;
   auto prefetch = [&](int qt) {
-    const long long rows = qend - qt;
+    const long long rows = min(64, qend - qt);   // the tile's rows
     const auto rG = buf_rsrc(Gp + (size_t)qt * D, rows * D * 4);
     const auto rQ = buf_rsrc(Qp + (size_t)qt * D, rows * D * 4);
 #pragma unroll

@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // rows past kend read zero, their scores are replaced by -inf, so their
   // softmax weights are exactly zero and the values they carry never count.
   // Every load of a thread uses one lane offset: K batch u (RPU rows) has a
-  // resource of its own, V batch u is an immediate offset.
+  // resource of its own, V batch u is an immediate offset.  Each resource
+  // covers one tile (or batch), so its range stays far below 2^31 bytes.
   constexpr int NL = 64 * (D / 4) / 256;     // float4 of K (and V) per thread per tile
   constexpr int RPU = 1024 / D;              // K rows per batch of 256 float4
   const float* Kp = a.K + (size_t)koff * D;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
       const int r0 = kt + RPU * u;
-      kr[u] = buf_load4(buf_rsrc(Kp + (size_t)r0 * D, (long long)(kend - r0) * D * 4), k_lane);
+      kr[u] = buf_load4(buf_rsrc(Kp + (size_t)r0 * D, (long long)min(RPU, kend - r0) * D * 4), k_lane);
     }
   };
   auto store_k = [&](const f32x4 (&kr)[NL]) {
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int v_lane = (v_key * D + 4 * (lane >> 4)) * 4;
   const int v_col = 16 * (tid >> 6) + vt_col<F64>(lane & 15);
   auto load_v = [&](int kt, f32x4 (&vr)[NL]) {
-    const auto rV = buf_rsrc(Vp + (size_t)kt * D, (long long)(kend - kt) * D * 4);
+    const auto rV = buf_rsrc(Vp + (size_t)kt * D, (long long)min(64, kend - kt) * D * 4);
 #pragma unroll
     for (int u = 0; u < NL; ++u) vr[u] = buf_load4(rV, v_lane + 64 * u);
   };
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     // the scores of the tile's keys go to St (queries past n have no row);
     // keys past kend are not stored and get -inf
     if (STORE && qok) {
-      const auto rSt = buf_rsrc(a.St + soff + (size_t)kt * npad, (long long)(kend - kt) * npad * 4);
+      const auto rSt = buf_rsrc(a.St + soff + (size_t)kt * npad, (long long)min(64, kend - kt) * npad * 4);
       if (!tail) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(FwdArgs a) {
   // this lane's scores: fixed lane part of the byte offset, uniform row part
   const int st_lane = ((F64 ? g : 4 * g) * npad + q) * 4;
   for (int kt = kbeg; kt < kend; kt += 64) {
-    const long long rows = kend - kt;
+    const long long rows = min(64, kend - kt);
     const auto rS = buf_rsrc(a.Sload + soff + (size_t)kt * npad, rows * npad * 4);
     const auto rV = buf_rsrc(Vp + (size_t)kt * D, rows * D * 4);
     const bool tail = kt + 64 > kend;

@@ -17,7 +17,10 @@ constexpr int kTile = 64;               // key/query tile edge used across kerne
 // Raw buffer resource over `bytes` bytes from `base` (both uniform across the
 // wave).  Loads through it at byte offsets at or past `bytes` return zero, so
 // the loads of a tile that runs past the end of its range need no clamping.
-// The last descriptor word selects untyped 32-bit access on gfx9 parts.
+// The range is a 32-bit count: callers keep it below 2^31 bytes (with at most
+// 2^21 training queries per problem every range in the kernels is a tile's
+// rows, at most 1 GiB).  The last descriptor word selects untyped 32-bit
+// access on gfx9 parts.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, long long bytes) {
   const int nr = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nr, 0x00020000);

@@ -36,8 +36,9 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   if (b->d != 64 && b->d != 128) return "d must be 64 or 128";
   if (b->Z < 1) return "Z must be >= 1";
   if (b->n < 1) return "n must be >= 1";
-  // tile loads address up to 128 rows of the stored scores with 32-bit byte offsets
-  if (b->n > (1 << 22)) return "n must be <= 4194304";
+  // tile loads address up to 128 rows of the stored scores (and a problem's
+  // n rows of targets) through 32-bit byte ranges and offsets
+  if (b->n > (1 << 21)) return "n must be <= 2097152";
   if (!(b->scale > 0.0)) return "scale must be > 0";
   if (!(b->lambda >= 0.0)) return "lambda must be >= 0";
   if (!(b->ridge_rel >= 0.0)) return "ridge_rel must be >= 0";

@@ -71,9 +71,9 @@ const char* kvs_status_string(kvs_status s);
 const char* kvs_last_error(kvs_ctx ctx);
 
 /* Problem batch description.  k points to HOST int32[P].  d is 64 or 128;
- * 1 <= n <= 4194304 training queries per problem (kernels address a tile's
- * rows with 32-bit byte offsets); every call rejects other values with
- * KVS_ERR_INVALID. */
+ * 1 <= n <= 2097152 training queries per problem (kernels address a tile's
+ * rows with 32-bit byte ranges and offsets); every call rejects other values
+ * with KVS_ERR_INVALID. */
 typedef struct {
   int32_t P, d, Z, n;
   const int32_t* k;     /* HOST [P], 1 <= k[p] <= Z (ragged)                    */

@@ -45,9 +45,9 @@ def test_workspace_and_state_sizes(K):
     assert K.workspace_bytes(bad, o) == 0
     bad2 = K.Batch(2, 128, 100, 64, k=[10, 101])     # k > Z
     assert K.workspace_bytes(bad2, o) == 0
-    # n past 2^22: tile rows are addressed with 32-bit byte offsets
-    assert K.workspace_bytes(K.Batch(1, 128, 100, 1 << 22, k=[10]), o) > 0
-    assert K.workspace_bytes(K.Batch(1, 128, 100, (1 << 22) + 1, k=[10]), o) == 0
+    # n past 2^21: tile rows are addressed with 32-bit byte ranges and offsets
+    assert K.workspace_bytes(K.Batch(1, 128, 100, 1 << 21, k=[10]), o) > 0
+    assert K.workspace_bytes(K.Batch(1, 128, 100, (1 << 21) + 1, k=[10]), o) == 0
 
 
 def test_argument_errors_are_reported_before_any_launch(K):
