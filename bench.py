@@ -81,12 +81,22 @@ def mixed_fwd_peak():
 # workloads report null.
 MEASURED_TRAFFIC = {
     # long-context default bench, the timed blocks' dispatches:
-    # loss-mode forward: FETCH 7378330.0 KiB x 1.99980 + WRITE 18403829.8 KiB x 1.00000 per dispatch
+    # loss-mode forward: FETCH 7799359.8 KiB x 1.99980 + WRITE 18418784.9 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
-        {"bytes": 33954818883, "source": "attn_fwd.hip", "sha": "0731476bccde8379"},
-    # Gram: FETCH 324121861.5 KiB x 1.99980 + WRITE 2763232.0 KiB x 1.00000 per dispatch
+        {"bytes": 34832320146, "source": "attn_fwd.hip", "sha": "57a6e7757b787957"},
+    # Gram: FETCH 323936206.5 KiB x 1.99980 + WRITE 2763232.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-7b-long-context"):
-        {"bytes": 666564236367, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
+        {"bytes": 666184264092, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
+    # L-BFGS vector passes and the merge of the same runs (each operand streamed once):
+    # inner products FETCH 1581258.0 KiB x 1.99980 + WRITE 395589.0 KiB, direction FETCH
+    # 1103026.3 KiB x 1.99980 + WRITE 223827.9 KiB, merge FETCH 736886.0 KiB x 1.99980 +
+    # WRITE 747236.2 KiB per dispatch
+    ("hist_dots", "qwen2.5-7b-long-context"):
+        {"bytes": 3643174188, "source": "lbfgs.hip", "sha": "1a77ca1dc4de04ae"},
+    ("direction", "qwen2.5-7b-long-context"):
+        {"bytes": 2487970706, "source": "lbfgs.hip", "sha": "1a77ca1dc4de04ae"},
+    ("merge", "qwen2.5-7b-long-context"):
+        {"bytes": 2274160829, "source": "attn_fwd.hip", "sha": "57a6e7757b787957"},
     # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
     ("build_queries", "qwen2.5-1.5b-full-cache"):
         {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
@@ -884,6 +894,20 @@ def bench_compress(args, torch, K):
                 "timed": f"HIP events on the library stream around every launch of the timed "
                          f"kernels during the {Kst} timed blocks ({tot_ms / Kst:.1f} ms of "
                          f"event-timed kernels per {1e3 * t_timed / Kst:.1f} ms step)"}
+    # HBM rate of the L-BFGS vector passes and the merge (measured bytes per
+    # dispatch over the event-timed average)
+    vec = {}
+    for nm in ("hist_dots", "direction", "merge"):
+        r = rows.get(nm)
+        if not r:
+            continue
+        bts = traffic_for(nm, w.name if args.ratio is None else None)
+        e = {"launches": r["launches"], "avg_us": r["avg_us"], "bytes_per_launch": bts}
+        if bts:
+            rate = bts / (r["avg_us"] * 1e-6)
+            e["GB/s"] = round(rate / 1e9, 1)
+            e["frac_hbm"] = round(rate / PEAK_HBM, 4)
+        vec[nm] = e
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host")
@@ -906,6 +930,10 @@ def bench_compress(args, torch, K):
                             f"Select+Fit at the new k + {T} main-run iterations, wall clock, inputs in HBM"},
         "kernels": rows,
         "roofline": roofline,
+        "vector_phases": {"kernels": vec, "peak_GB/s": PEAK_HBM / 1e9,
+                          "bytes": "HBM bytes per dispatch measured by FETCH_SIZE / WRITE_SIZE over the timed "
+                                   "blocks (copy-calibrated; null once the kernel source changed); these "
+                                   "kernels stream each operand once"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
