@@ -58,42 +58,9 @@ void launch_mu(const CholArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(mu_kernel, dim3(a.P), dim3(64), 0, s, a);
 }
 
-// 64x64 tile product acc = A B^T (A = rows rowA.., B = rows rowB.., both taking
-// columns col0..col0+16 NT-1 of M), each wave a 32x32 quarter on 16x16x4 fp32
-// MFMA.  Results: acc[ib][jb][r] belongs to row rb + 16 ib + 4 g + r, column
-// cb + 16 jb + lq of the tile.
-template <int NT>
-__device__ __forceinline__ void tile_aat(const float* __restrict__ Mp, int ld, int rowA, int rowB, int col0,
-                                         f32x4 (&acc)[2][2]) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
-  const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    f32x4 av[2], bv[2];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-      av[ib] = *(const f32x4*)(Mp + (size_t)(rowA + rb + 16 * ib + lq) * ld + col0 + 16 * t + 4 * g);
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-      bv[jb] = *(const f32x4*)(Mp + (size_t)(rowB + cb + 16 * jb + lq) * ld + col0 + 16 * t + 4 * g);
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        acc[ib][jb] = mfma_c(av[ib].x, bv[jb].x, acc[ib][jb]);
-        acc[ib][jb] = mfma_c(av[ib].y, bv[jb].y, acc[ib][jb]);
-        acc[ib][jb] = mfma_c(av[ib].z, bv[jb].z, acc[ib][jb]);
-        acc[ib][jb] = mfma_c(av[ib].w, bv[jb].w, acc[ib][jb]);
-      }
-  }
-}
-
-// acc += A B^T for 64x64 tiles held in LDS ([64][68], row-major); same
-// result layout as tile_aat.  Operands are read four k at a time: step t
+// acc += A B^T for 64x64 tiles held in LDS ([64][68], row-major): each wave
+// a 32x32 quarter, acc[ib][jb][r] at row rb + 16 ib + 4 g + r, column
+// cb + 16 jb + lq of the tile.  Operands are read four k at a time: step t
 // takes k = 16 (t / 4) + 4 g + t % 4 on both sides.
 __device__ __forceinline__ void tile_abt_acc(const float (*A)[68], const float (*B)[68], f32x4 (&acc)[2][2]) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
@@ -160,6 +127,8 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
   const int rb = 32 * (wave >> 1), cb = 32 * (wave & 1);
   auto rowof = [&](int I) { return (I < KT) ? 64 * I : pi.kpad + 64 * (I - KT); };
+  __shared__ float Tl[64][68];      // panel tile, then L_Ij (trailing: a panel block of row I)
+  __shared__ float Dl[64][68];      // diagonal tile of the look-ahead, then its factor (trailing: of row J)
 
   if (wid >= npanel) {
     // trailing update from the pending panels: strictly lower tiles among the
@@ -190,10 +159,38 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           cv[ib][jb][r] = Mp[(size_t)(rowof(I) + rb + 16 * ib + 4 * g + r) * ld + 64 * J + cb + 16 * jb + lq];
+    // T -= sum over the pending panels of L_{I,p} L_{J,p}^T: each panel's two
+    // 64x64 blocks are staged in LDS once for the four waves (each wave would
+    // otherwise read its own 32 rows of both from L2), the next panel's
+    // blocks loaded during the current panel's products
     f32x4 acc[2][2];
-    if (a.S == 4) tile_aat<16>(Mp, ld, rowof(I), 64 * J, 64 * (j - 4), acc);
-    else if (a.S == 2) tile_aat<8>(Mp, ld, rowof(I), 64 * J, 64 * (j - 2), acc);
-    else tile_aat<4>(Mp, ld, rowof(I), 64 * J, 64 * (j - 1), acc);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int rA = rowof(I), rB = 64 * J, c00 = 64 * (j - a.S);
+    f32x4 pa[4], pb[4];
+    auto load_blocks = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * u, r = i >> 4, c4 = 4 * (i & 15);
+        pa[u] = *(const f32x4*)(Mp + (size_t)(rA + r) * ld + c0 + c4);
+        pb[u] = *(const f32x4*)(Mp + (size_t)(rB + r) * ld + c0 + c4);
+      }
+    };
+    load_blocks(c00);
+    for (int pn = 0; pn < a.S; ++pn) {
+      __syncthreads();   // the previous panel's blocks are read
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = tid + 256 * u, r = i >> 4, c4 = 4 * (i & 15);
+        *(f32x4*)&Tl[r][c4] = pa[u];
+        *(f32x4*)&Dl[r][c4] = pb[u];
+      }
+      __syncthreads();
+      if (pn + 1 < a.S) load_blocks(c00 + 64 * (pn + 1));
+      tile_abt_acc(Tl, Dl, acc);
+    }
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
@@ -208,8 +205,6 @@ __global__ __launch_bounds__(256) void chol_step_kernel(CholArgs a, int j) {
   const int I = j + 1 + wid;
   if (I >= RT) return;
   const bool look = (I == j + 1) && (I < KT);
-  __shared__ float Tl[64][68];      // panel tile, then L_Ij
-  __shared__ float Dl[64][68];      // diagonal tile of the look-ahead, then its factor
   __shared__ float Xr[4][16][20];   // inverses of the factor's 16x16 diagonal blocks
 
   const int rowI = rowof(I);
