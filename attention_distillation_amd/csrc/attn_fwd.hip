@@ -51,7 +51,9 @@ template <int D, bool STORE, bool F64>
 // interleaved score accumulators of d = 128 fill (its LDS tiles allow two
 // workgroups per CU)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(FwdArgs a) {
-  const int p = blockIdx.y, c = blockIdx.z;
+  // grid row -> problem: largest k first (a workgroup's work grows with k)
+  const int p = a.info ? a.info[blockIdx.y].korder : (int)blockIdx.y;
+  const int c = blockIdx.z;
   // the problem table and the state are read before the status test, which
   // uses both, so the two loads share one round trip
   int k, koff;
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 // that product rounded to, so the partials equal the full forward's bit for bit.
 template <int D, bool F64>
 __global__ __launch_bounds__(256) void attn_pv_kernel(FwdArgs a) {
-  const int p = blockIdx.y, c = blockIdx.z;
+  const int p = a.info[blockIdx.y].korder, c = blockIdx.z;   // largest k first
   const int k = a.info[p].k, koff = a.info[p].koff;
   const long long soff = a.info[p].soff;
   if (a.st && (!((1 << a.st[p].status) & a.active_mask) || k < 0)) return;

@@ -49,7 +49,7 @@ struct ProbInfo {
   long long moff;   // offset (floats) of the problem's augmented Gram [(kpad+d)][kpad]
   long long xoff;   // offset (floats) of the problem's padded solve rows [kpad][d]
   int gtoff;        // first tile of the problem in the flat order of the 128x128 Gram tiles
-  int pad1;
+  int korder;       // problem that the forwards run at grid row p (largest k first)
 };
 
 // L-BFGS / line-search status of one problem.

@@ -69,7 +69,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     q.moff = moff;
     q.xoff = xoff;
     q.gtoff = (int)gtoff;
-    q.pad1 = 0;
+    q.korder = i;
     gtoff += gram128_tiles((q.kpad / kTile + 1) / 2);
     koff += k;
     soff += (long long)k * p.npad;
@@ -97,6 +97,15 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     int s = 0;
     for (const auto& b : bin)
       for (int prob : b) p.info[s++].xorder = prob;
+  }
+  // Grid rows of the forwards: a workgroup's work grows with its problem's k,
+  // so the largest problems are dispatched first and the last round of
+  // workgroups is the shortest.
+  {
+    std::vector<int> byk(p.P);
+    for (int i = 0; i < p.P; ++i) byk[i] = i;
+    std::stable_sort(byk.begin(), byk.end(), [&](int x, int y) { return p.info[x].k > p.info[y].k; });
+    for (int i = 0; i < p.P; ++i) p.info[i].korder = byk[i];
   }
   p.ktot = koff; p.stot = soff; p.mtot = moff; p.kpadtot = xoff / p.d;
 
