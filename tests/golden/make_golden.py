@@ -8,6 +8,7 @@ synthetic inputs of ``synth``; nothing is read from the GPU path.
     python tests/golden/make_golden.py pilot      # full-cache pilot, r = 0.3 / 0.5 / 0.7
     python tests/golden/make_golden.py e2e-llama  # llama3-8b problem 0, k = 2381 and 4680
     python tests/golden/make_golden.py e2e-long   # long-context problem 0, k = 3226
+    python tests/golden/make_golden.py e2e-ragged # llama3-8b, 8 seeded problems at ragged k
 
 The pilot set runs its 168 problems in a process pool (one BLAS thread each).
 Each run is stored with the final loss of the same schedule run with its
@@ -136,6 +137,50 @@ def golden_e2e(cid: int, p: int, ks, seed: int = 0, previous=None):
     return out
 
 
+def ragged_budgets(P: int, lo: int, hi: int, seed: int):
+    """Seeded ragged budgets, log-uniform in [lo, hi]: test inputs with the
+    spread a reallocation produces (on the llama3-8b cache the pilot hands out
+    about 700 to 4700 pairs), independent of either side's pilot."""
+    import numpy as np
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 8317]))
+    return [int(round(float(np.exp(v)))) for v in rng.uniform(np.log(lo), np.log(hi), size=P)]
+
+
+def _ragged_one(args):
+    cid, p, k, seed, f32 = args
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        w = WORKLOADS[cid]
+        b = make_batch(w, seed, problems=[p])
+        t0 = time.time()
+        r = O.compress_problem(b["Q"][0], b["Kz"][0], b["Vz"][0], k, b["scale"],
+                               O.CompressOptions(iters=w.T, keys_f32=f32))
+        return p, f32, r["init_loss"], r["loss"], r["flags"], time.time() - t0
+
+
+def golden_ragged(cid: int = 3, seed: int = 0, nsample: int = 8, workers: int = 8):
+    """The oracle's whole schedule (Select+Fit at the problem's budget, T
+    iterations) on a seeded sample of problems of a large workload whose
+    problems all have seeded ragged budgets, plain and with the keys kept at
+    float32 (the sensitivity variant)."""
+    import concurrent.futures as cf
+    import numpy as np
+    w = WORKLOADS[cid]
+    ks = ragged_budgets(w.P, 700, 4680, seed)
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 4471]))
+    sample = sorted(int(p) for p in rng.choice(w.P, size=nsample, replace=False))
+    jobs = [(cid, p, ks[p], seed, f32) for p in sample for f32 in (False, True)]
+    res = {}
+    with cf.ProcessPoolExecutor(workers) as ex:
+        for p, f32, l0, loss, flags, sec in ex.map(_ragged_one, jobs):
+            res[(p, f32)] = (l0, loss, flags)
+            print(f"{w.name} p={p} k={ks[p]} {'float32 keys' if f32 else 'float64'}: {l0:.6g} -> {loss:.6g} "
+                  f"({sec:.0f} s)", flush=True)
+    runs = [{"p": p, "k": ks[p], "init_loss": res[(p, False)][0], "final_loss": res[(p, False)][1],
+             "flags": res[(p, False)][2], "final_loss_f32keys": res[(p, True)][1]} for p in sample]
+    return {"workload": w.name, "seed": seed, "iters": w.T, "k": ks, "runs": runs}
+
+
 if __name__ == "__main__":
     name = sys.argv[1] if len(sys.argv) > 1 else "qwen2.5-1.5b-one-layer"
     if name == "states":
@@ -157,6 +202,11 @@ if __name__ == "__main__":
         path = os.path.join(HERE, f"oracle_compress_{WORKLOADS[cid].name}_p0.json")
         res = golden_e2e(cid, 0, ks, previous=json.load(open(path)) if reuse else None)
         with open(os.path.join(HERE, f"oracle_compress_{WORKLOADS[cid].name}_p0.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        sys.exit(0)
+    if name == "e2e-ragged":
+        res = golden_ragged()
+        with open(os.path.join(HERE, f"oracle_compress_{WORKLOADS[3].name}_ragged.json"), "w") as f:
             json.dump(res, f, indent=1)
         sys.exit(0)
     cid = next(c for c, w in WORKLOADS.items() if w.name == name)

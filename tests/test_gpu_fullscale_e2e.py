@@ -31,6 +31,9 @@ oracle runs stored by tests/golden/make_golden.py (oracle only).
   spread that the two one-rounding perturbations above give that problem,
   whichever is larger; llama3-8b problem 0 also alone at k = 4680, the
   largest budget the pilot hands out on that cache.
+- kvs_compress on the whole llama3-8b batch at seeded ragged budgets (the main
+  run after a reallocation), eight seeded problems against the oracle, each
+  to the single-problem bar.
 """
 import json
 import math
@@ -195,4 +198,41 @@ def test_compress_full_schedule(name):
     assert abs(l0g[0] - run["init_loss"]) <= 1e-4 * run["init_loss"]
     assert dev <= max(0.02, 2.0 * spread)
     assert fg[0] & ~K.KVS_FLAG_NONDESCENT == 0 and run["flags"] & ~O.FLAG_NONDESCENT == 0
+    assert np.all(np.isfinite(lg))
+
+
+def test_compress_ragged_batch():
+    """kvs_compress on the whole llama3-8b-shaped batch (256 problems) at
+    seeded ragged budgets (log-uniform in [700, 4680], the spread a
+    reallocation produces there), T = 200; eight seeded problems against the
+    oracle's runs of the same schedule: Select+Fit loss within 1e-4, final
+    loss within max(2%, twice the problem's spread), the spread measured as
+    for the single-problem runs (the oracle with float32 keys, the GPU with
+    one-ulp queries)."""
+    gold = json.load(open(os.path.join(GOLD, "oracle_compress_llama3-8b-cache_ragged.json")))
+    w = WORKLOADS[3]
+    ks, T = gold["k"], gold["iters"]
+    b = make_batch(w, gold["seed"], workers=16)
+    P = b["Q"].shape[0]
+    assert len(ks) == P
+    say(f"[ragged batch] {w.name}: P={P} k {min(ks)}..{max(ks)} (sum {sum(ks)}) T={T}")
+    lg, l0g, fg = _compress(b, ks, T)
+    lu, _, _ = _compress(b, ks, T, Q=ulp_perturbed(b["Q"]))
+    devs = []
+    for run in gold["runs"]:
+        p = run["p"]
+        lo, l32 = run["final_loss"], run["final_loss_f32keys"]
+        dev = abs(lg[p] - lo) / lo
+        spread = max(abs(l32 - lo) / lo, abs(lu[p] - lg[p]) / lg[p])
+        devs.append(dev)
+        say(f"   p={p} k={ks[p]} init gpu={l0g[p]:.7g} oracle={run['init_loss']:.7g}; final gpu={lg[p]:.7g} "
+            f"oracle={lo:.7g} (float32 keys {l32:.7g}; gpu with one-ulp queries {lu[p]:.7g}) deviation "
+            f"{dev:.2e} spread {spread:.2e}; flags={fg[p]}")
+        assert abs(l0g[p] - run["init_loss"]) <= 1e-4 * run["init_loss"]
+        assert dev <= max(0.02, 2.0 * spread)
+        assert fg[p] & ~K.KVS_FLAG_NONDESCENT == 0 and run["flags"] & ~O.FLAG_NONDESCENT == 0
+    ub = np.abs(lu - lg) / lg
+    say(f"   sampled deviations median {np.median(devs):.2e} max {max(devs):.2e}; batch final/init median "
+        f"{np.median(lg / l0g):.4f}, one-ulp spread over the batch median {np.median(ub):.2e} max {ub.max():.2e}, "
+        f"flagged {int(np.count_nonzero(fg))}")
     assert np.all(np.isfinite(lg))
