@@ -10,7 +10,8 @@
 //                       y = g_new - g (into the staging slot), g <- g_new;
 //                       then, one workgroup per chunk, the five inner products of
 //                       every history slot with the staged pair and g, kept
-//                       in registers; the last workgroup of each problem
+//                       in registers and reduced per wave after each of the
+//                       chunk's sub-chunks; the last workgroup of each problem
 //                       (arrival counter) reduces them in chunk order and runs
 //                       the scalar logic (curvature test, ring update, two-loop
 //                       coefficients, descent check, first step) on a copy of
@@ -27,7 +28,8 @@ namespace kvs {
 static_assert(sizeof(LbState) % 8 == 0, "state is copied to LDS in 8-byte words");
 
 constexpr int kVec4PerWG = 256;     // float4 per workgroup in the streaming passes
-constexpr int kDotVec4PerWG = 256;  // float4 per workgroup in the dot pass (one per thread)
+constexpr int kDotSub = 2;          // 256-float4 sub-chunks per workgroup in the dot pass
+constexpr int kDotVec4PerWG = 256 * kDotSub;  // float4 per workgroup in the dot pass
 
 int vec_chunks(long long kmax_d) {
   const long long v4 = (kmax_d + 3) / 4;
@@ -274,13 +276,17 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
   __syncthreads();
 }
 
-// One workgroup per 256-float4 chunk of a problem's vectors, one float4 per
-// thread.  The five inner products are taken per ring slot (not per history
-// position), so no vector load waits for the history order: the problem
-// table and the state header are read together, then every vector load of
-// the thread is issued at once.  The last workgroup of the problem sums the
-// chunk partials in a fixed order and runs the scalar logic.  MS bounds the
-// ring slots in use (history + 1).
+// One workgroup per chunk of kDotSub 256-float4 sub-chunks of a problem's
+// vectors, one float4 per thread per sub-chunk.  The five inner products are
+// taken per ring slot (not per history position), so no vector load waits for
+// the history order: the problem table and the state header are read
+// together, then every vector load of the thread for a sub-chunk is issued at
+// once.  Each sub-chunk's products are reduced across the wave and added to
+// the lane's running total (the two waves of a SIMD overlap one's loads with
+// the other's arithmetic, and the partial store and arrival are paid once per
+// chunk).  The last workgroup of the problem sums the chunk partials in a
+// fixed order and runs the scalar logic.  MS bounds the ring slots in use
+// (history + 1).
 template <int MS>
 __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   constexpr int E = 5 * MS + 2;            // partial entries per chunk
@@ -304,111 +310,121 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   __shared__ int s_last;
 
   if (compute) {
-    const long long e = (long long)blockIdx.x * 256 + tid;
-    const bool ok = e < n4;
-    const long long ec = ok ? e : 0;       // in-range index for the loads of idle lanes
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
-    const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
-    f32x4 sj[MS], yj[MS];
+    // per-lane running totals of the wave-reduced values over the sub-chunks
+    double tot[NV];
 #pragma unroll
-    for (int t = 0; t < MS; ++t) {
-      const bool use = t < nslot;
-      sj[t] = use ? S[(size_t)t * stride4 + ec] : z;
-      yj[t] = use ? Yv[(size_t)t * stride4 + ec] : z;
-    }
-    f32x4 gv = z, sv = z, yv = z;
-    if (a.grad) {
-      // gradient from the split partials (fixed order), then the accepted
-      // step and its (s, y) pair, staged in slot stg
-      const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
-      f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
-      f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
-      const f32x4 go = G[ec];
-      const f32x4 xv = accept ? X[ec] : z;
-      const f32x4 pv = accept ? reinterpret_cast<const f32x4*>(a.pdir)[base4 + ec] : z;
-      f32x4 t0[8];
+    for (int gi = 0; gi < NV; ++gi) tot[gi] = 0.0;
+    for (int sub = 0; sub < kDotSub; ++sub) {
+      const long long e0 = ((long long)blockIdx.x * kDotSub + sub) * 256;
+      if (e0 >= n4) break;                 // uniform across the workgroup
+      const long long e = e0 + tid;
+      const bool ok = e < n4;
+      const long long ec = ok ? e : 0;       // in-range index for the loads of idle lanes
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4* S = reinterpret_cast<const f32x4*>(a.S) + base4;
+      const f32x4* Yv = reinterpret_cast<const f32x4*>(a.Yh) + base4;
+      f32x4 sj[MS], yj[MS];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) t0[j] = dK[(size_t)(j < a.Cn ? j : 0) * stride4 + ec];
-      f32x4 gn = t0[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j)
-        if (j < a.Cn) gn += t0[j];
-      for (int c0 = 8; c0 < a.Cn; c0 += 8) {
-        f32x4 t[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + ec];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (c0 + j < a.Cn) gn += t[j];
+      for (int t = 0; t < MS; ++t) {
+        const bool use = t < nslot;
+        sj[t] = use ? S[(size_t)t * stride4 + ec] : z;
+        yj[t] = use ? Yv[(size_t)t * stride4 + ec] : z;
       }
-      gn *= (float)a.gscale;
-      if (ok) {
-        if (accept) {
-          f32x4 xn;
-          xn.x = __fmaf_rn(alpha, pv.x, xv.x);
-          xn.y = __fmaf_rn(alpha, pv.y, xv.y);
-          xn.z = __fmaf_rn(alpha, pv.z, xv.z);
-          xn.w = __fmaf_rn(alpha, pv.w, xv.w);
-          X[e] = xn;
-          sv = xn - xv;
-          yv = gn - go;
-          reinterpret_cast<f32x4*>(a.S)[(size_t)stg * stride4 + base4 + e] = sv;
-          reinterpret_cast<f32x4*>(a.Yh)[(size_t)stg * stride4 + base4 + e] = yv;
+      f32x4 gv = z, sv = z, yv = z;
+      if (a.grad) {
+        // gradient from the split partials (fixed order), then the accepted
+        // step and its (s, y) pair, staged in slot stg
+        const f32x4* dK = reinterpret_cast<const f32x4*>(a.dKpart) + base4;
+        f32x4* G = reinterpret_cast<f32x4*>(a.g) + base4;
+        f32x4* X = reinterpret_cast<f32x4*>(a.x) + base4;
+        const f32x4 go = G[ec];
+        const f32x4 xv = accept ? X[ec] : z;
+        const f32x4 pv = accept ? reinterpret_cast<const f32x4*>(a.pdir)[base4 + ec] : z;
+        f32x4 t0[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t0[j] = dK[(size_t)(j < a.Cn ? j : 0) * stride4 + ec];
+        f32x4 gn = t0[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+          if (j < a.Cn) gn += t0[j];
+        for (int c0 = 8; c0 < a.Cn; c0 += 8) {
+          f32x4 t[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + ec];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j < a.Cn) gn += t[j];
         }
-        G[e] = gn;
-        gv = gn;
-      }
-    } else {
-      gv = ok ? reinterpret_cast<const f32x4*>(a.g)[base4 + e] : z;
-      sv = (ok && accept) ? S[(size_t)stg * stride4 + e] : z;
-      yv = (ok && accept) ? Yv[(size_t)stg * stride4 + e] : z;
-    }
-    if (!ok) {
-#pragma unroll
-      for (int t = 0; t < MS; ++t) sj[t] = yj[t] = z;
-    }
-    // the staged slot holds the new pair (its loads above may predate the
-    // stores): take it from registers
-#pragma unroll
-    for (int t = 0; t < MS; ++t)
-      if (accept && t == stg) {
-        sj[t] = sv;
-        yj[t] = yv;
-      }
-    // all E values of this lane, padded to a multiple of 64, then a
-    // butterfly reduction per group of 64: at each level a lane keeps one
-    // half of its values and adds the partner's copy of that half, so lane l
-    // ends with the wave total of value l of the group (63 exchanges per
-    // group instead of a full reduction per value)
-    double v[64 * NV];
-#pragma unroll
-    for (int t = 0; t < MS; ++t) {
-      v[5 * t + 0] = dot4(sv, yj[t]);   // s_new . y_t
-      v[5 * t + 1] = dot4(sj[t], yv);   // s_t . y_new
-      v[5 * t + 2] = dot4(yv, yj[t]);   // y_new . y_t
-      v[5 * t + 3] = dot4(gv, sj[t]);   // g . s_t
-      v[5 * t + 4] = dot4(gv, yj[t]);   // g . y_t
-    }
-    v[5 * MS] = dot4(gv, gv);
-    v[5 * MS + 1] = dot4(sv, sv);
-#pragma unroll
-    for (int i = E; i < 64 * NV; ++i) v[i] = 0.0;
-#pragma unroll
-    for (int gi = 0; gi < NV; ++gi) {
-      double* w = v + 64 * gi;
-#pragma unroll
-      for (int L = 32; L > 0; L >>= 1) {
-        const bool hi = (lane & L) != 0;
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
-          const double send = hi ? w[i] : w[i + L];
-          const double keep = hi ? w[i + L] : w[i];
-          w[i] = keep + __shfl_xor(send, L);
+        gn *= (float)a.gscale;
+        if (ok) {
+          if (accept) {
+            f32x4 xn;
+            xn.x = __fmaf_rn(alpha, pv.x, xv.x);
+            xn.y = __fmaf_rn(alpha, pv.y, xv.y);
+            xn.z = __fmaf_rn(alpha, pv.z, xv.z);
+            xn.w = __fmaf_rn(alpha, pv.w, xv.w);
+            X[e] = xn;
+            sv = xn - xv;
+            yv = gn - go;
+            reinterpret_cast<f32x4*>(a.S)[(size_t)stg * stride4 + base4 + e] = sv;
+            reinterpret_cast<f32x4*>(a.Yh)[(size_t)stg * stride4 + base4 + e] = yv;
+          }
+          G[e] = gn;
+          gv = gn;
         }
+      } else {
+        gv = ok ? reinterpret_cast<const f32x4*>(a.g)[base4 + e] : z;
+        sv = (ok && accept) ? S[(size_t)stg * stride4 + e] : z;
+        yv = (ok && accept) ? Yv[(size_t)stg * stride4 + e] : z;
       }
-      red[wave][64 * gi + lane] = w[0];
+      if (!ok) {
+#pragma unroll
+        for (int t = 0; t < MS; ++t) sj[t] = yj[t] = z;
+      }
+      // the staged slot holds the new pair (its loads above may predate the
+      // stores): take it from registers
+#pragma unroll
+      for (int t = 0; t < MS; ++t)
+        if (accept && t == stg) {
+          sj[t] = sv;
+          yj[t] = yv;
+        }
+      // all E values of this lane, padded to a multiple of 64, then a
+      // butterfly reduction per group of 64: at each level a lane keeps one
+      // half of its values and adds the partner's copy of that half, so lane l
+      // ends with the wave total of value l of the group (63 exchanges per
+      // group instead of a full reduction per value)
+      double v[64 * NV];
+#pragma unroll
+      for (int t = 0; t < MS; ++t) {
+        v[5 * t + 0] = dot4(sv, yj[t]);   // s_new . y_t
+        v[5 * t + 1] = dot4(sj[t], yv);   // s_t . y_new
+        v[5 * t + 2] = dot4(yv, yj[t]);   // y_new . y_t
+        v[5 * t + 3] = dot4(gv, sj[t]);   // g . s_t
+        v[5 * t + 4] = dot4(gv, yj[t]);   // g . y_t
+      }
+      v[5 * MS] = dot4(gv, gv);
+      v[5 * MS + 1] = dot4(sv, sv);
+#pragma unroll
+      for (int i = E; i < 64 * NV; ++i) v[i] = 0.0;
+#pragma unroll
+      for (int gi = 0; gi < NV; ++gi) {
+        double* w = v + 64 * gi;
+#pragma unroll
+        for (int L = 32; L > 0; L >>= 1) {
+          const bool hi = (lane & L) != 0;
+#pragma unroll
+          for (int i = 0; i < L; ++i) {
+            const double send = hi ? w[i] : w[i + L];
+            const double keep = hi ? w[i + L] : w[i];
+            w[i] = keep + __shfl_xor(send, L);
+          }
+        }
+        tot[gi] += w[0];
+      }
     }
+#pragma unroll
+    for (int gi = 0; gi < NV; ++gi) red[wave][64 * gi + lane] = tot[gi];
     __syncthreads();
     if (tid < E) coherent_store(out + tid, ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
   }

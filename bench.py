@@ -81,22 +81,22 @@ def mixed_fwd_peak():
 # workloads report null.
 MEASURED_TRAFFIC = {
     # long-context default bench, the timed blocks' dispatches:
-    # loss-mode forward: FETCH 3084954.2 KiB x 1.99980 + WRITE 18402113.3 KiB x 1.00000 per dispatch
+    # loss-mode forward: FETCH 3073914.7 KiB x 1.99980 + WRITE 18401623.2 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
-        {"bytes": 25161107510, "source": "attn_fwd.hip", "sha": "6579d1690010fdff"},
-    # Gram: FETCH 324225649.8 KiB x 1.99980 + WRITE 2763232.0 KiB x 1.00000 per dispatch
+        {"bytes": 25137999042, "source": "attn_fwd.hip", "sha": "6579d1690010fdff"},
+    # Gram: FETCH 324390230.5 KiB x 1.99980 + WRITE 2763232.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-7b-long-context"):
-        {"bytes": 666776140128, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
+        {"bytes": 667113167294, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
     # L-BFGS vector passes and the merge of the same runs (each operand streamed once):
-    # inner products FETCH 1581255.4 KiB x 1.99980 + WRITE 395589.0 KiB, direction FETCH
-    # 1103026.2 KiB x 1.99980 + WRITE 223827.9 KiB, merge FETCH 736888.8 KiB x 1.99980 +
-    # WRITE 747243.0 KiB per dispatch
+    # inner products FETCH 1574937.8 KiB x 1.99980 + WRITE 383034.0 KiB, direction FETCH
+    # 1103026.1 KiB x 1.99980 + WRITE 223827.9 KiB, merge FETCH 736886.5 KiB x 1.99980 +
+    # WRITE 747215.0 KiB per dispatch
     ("hist_dots", "qwen2.5-7b-long-context"):
-        {"bytes": 3643164853, "source": "lbfgs.hip", "sha": "1a77ca1dc4de04ae"},
+        {"bytes": 3617371325, "source": "lbfgs.hip", "sha": "69bc1b284c639763"},
     ("direction", "qwen2.5-7b-long-context"):
-        {"bytes": 2487967584, "source": "lbfgs.hip", "sha": "1a77ca1dc4de04ae"},
+        {"bytes": 2487967394, "source": "lbfgs.hip", "sha": "69bc1b284c639763"},
     ("merge", "qwen2.5-7b-long-context"):
-        {"bytes": 2274171481, "source": "attn_fwd.hip", "sha": "6579d1690010fdff"},
+        {"bytes": 2274138305, "source": "attn_fwd.hip", "sha": "6579d1690010fdff"},
     # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
     ("build_queries", "qwen2.5-1.5b-full-cache"):
         {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
