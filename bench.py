@@ -143,6 +143,17 @@ def _threads():
         return os.cpu_count() or 1
 
 
+def _blas():
+    """The BLAS library NumPy/SciPy use, its version and thread pool size."""
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                         for i in libs) or None
+    except Exception:
+        return None
+
+
 def timed_pass(torch, step, steps):
     """Wall time of `steps` calls with nothing recorded on the stream."""
     torch.cuda.synchronize()
@@ -781,6 +792,7 @@ def cpu_baseline_block(w, b):
             "sample": f"{w.name} problem 0 at k0={w.k0}: one block of 5 L-BFGS iterations "
                       f"with its value re-solve and the loss/gradient after it, from the Select+Fit start, float64 NumPy/SciPy; "
                       f"reference attention and Select+Fit ({t_setup:.0f} s) not timed",
+            "host_cpus": os.cpu_count(), "blas": _blas(),
             "one_thread": one}
 
 
