@@ -18,11 +18,12 @@
 namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
-  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_NCLASS
+  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_DIGITS, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
-    "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv"};
+    "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv",
+    "key_digits"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -39,7 +40,8 @@ struct kvs_ctx_s {
   std::string err;
   int device = 0;
   int lds_max = 0;          // dynamic LDS bytes per workgroup on this device
-  bool logit_f64 = true;
+  int logit_mode = kvs::LOGIT_I8;   // score arithmetic of the loss forwards
+  bool refine_resolves = true;      // refinement step after the schedule's value re-solves
   bool prof = false;
   int prof_mask = 0;
   std::vector<hipEvent_t> pool;
@@ -228,7 +230,7 @@ void run_reference(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float*
   f.info = nullptr; f.P = pl.P; f.n = pl.n; f.C = pl.Cref; f.kuni = pl.Z; f.kmax = pl.Z; f.scale = b->scale;
   {
     Prof pr(ctx, PROF_REF, 4.0 * pl.n * pl.Z * pl.d * pl.P, 4.0 * pl.P * (2.0 * pl.n * pl.d + 2.0 * pl.Z * pl.d));
-    launch_attn_fwd(f, pl.d, false, ctx->stream);
+    launch_attn_fwd(f, pl.d, LOGIT_F32, ctx->stream);
   }
   MergeArgs m{};
   m.Opart = f.Opart; m.Mpart = f.Mpart; m.Lpart = f.Lpart; m.st = nullptr; m.active_mask = 0;
@@ -260,11 +262,17 @@ void run_forward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q
     if (reuse_scores) {
       Prof pr(ctx, PROF_PV, 2.0 * pl.n * pl.d * ks,
               4.0 * (ks * pl.d + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
-      launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+      launch_attn_fwd(f, pl.d, ctx->logit_mode, ctx->stream);
     } else {
+      if (ctx->logit_mode == LOGIT_I8) {
+        // digit planes of the keys (all rows; only the selected problems read them)
+        f.K8 = at<int>(ws, pl.r_K8); f.Kscl = at<float>(ws, pl.r_Kscl); f.k8rows = pl.ktot;
+        Prof pr(ctx, PROF_DIGITS, 0.0, (double)pl.ktot * pl.d * (4.0 + kDigits) + 4.0 * pl.ktot);
+        launch_digit_rows(K, pl.ktot, pl.d, const_cast<int*>(f.K8), const_cast<float*>(f.Kscl), ctx->stream);
+      }
       Prof pr(ctx, PROF_FWD, 4.0 * pl.n * pl.d * ks,
               4.0 * (ks * pl.d * 2.0 + ks * pl.npad + (np ? np : 1) * pl.n * pl.d));
-      launch_attn_fwd(f, pl.d, ctx->logit_f64, ctx->stream);
+      launch_attn_fwd(f, pl.d, ctx->logit_mode, ctx->stream);
     }
   }
   MergeArgs m{};
@@ -560,9 +568,8 @@ kvs_status status_buffers(kvs_ctx ctx, int P) {
 void run_init(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* Q, const float* Kz,
               const float* Y, const float* lse, float* Kc, float* Vc, int* flags, LbState* st,
               bool keys_given, void* ws) {
-  // the starting values take the refinement step of the standalone solve
-  // (once per run, so its cost does not matter; the re-solves every
-  // vc_every iterations skip it)
+  // the starting values take the refinement step of the standalone solve,
+  // as do the re-solves every vc_every iterations
   if (!keys_given) {
     run_init_topk(ctx, pl, b, Q, Kz, Y, lse, at<int>(ws, pl.r_idx), Kc, Vc, flags, st, ws, true);
     return;
@@ -653,7 +660,10 @@ kvs_status compress_advance_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b
         run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, B.st, 1 << ST_DONE_FAIL, 2, nullptr, nullptr, o,
                     ws, &hs, ST_DONE_FAIL);
       }
-      run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws);
+      // every problem is re-solved (the stored scores are at its current
+      // keys), with the refinement step of the standalone solve
+      const RefineIn rin{Q, lr, Kc};
+      run_value_solve(ctx, pl, b, Yr, Vc, nullptr, B.st, kAll, ws, ctx->refine_resolves ? &rin : nullptr);
       // the value solve used the stored scores at the current keys: valid for
       // every problem, so the loss at the new values reads them back
       lb_eval_at_x(ctx, pl, b, o, Q, Yr, lr, Kc, Vc, B, 1, nullptr, mse, ws, true);
@@ -741,8 +751,14 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
   if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) == hipSuccess)
     c->lds_max = lds;
   (void)hipGetLastError();
-  const char* env = getenv("KVS_LOGITS_FP32");
-  c->logit_f64 = !(env && env[0] == '1');
+  // score arithmetic of the loss forwards, for comparisons: KVS_LOGITS=fp32
+  // or fp64 (the default is the exact integer products)
+  if (const char* env = getenv("KVS_LOGITS")) {
+    if (!strcmp(env, "fp32")) c->logit_mode = kvs::LOGIT_F32;
+    else if (!strcmp(env, "fp64")) c->logit_mode = kvs::LOGIT_F64;
+  }
+  // the schedule's value re-solves without their refinement step, for comparisons
+  if (const char* env = getenv("KVS_RESOLVE_REFINE")) c->refine_resolves = env[0] != '0';
   // the context's device is current here: take its scratch address once
   if (hipError_t e = scratch_address(c->device, &c->scratch); e != hipSuccess) {
     c->scratch = nullptr;
@@ -1127,7 +1143,7 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
     f.info = info; f.P = u.P; f.n = u.n; f.C = C; f.kuni = kuni; f.kmax = kmax;
     f.scale = b->scale;
     Prof pr(ctx, PROF_USE, 4.0 * u.n * u.d * keys, 4.0 * (keys * u.d * 2.0 + (double)pn * u.d));
-    launch_attn_fwd(f, u.d, ctx->logit_f64, ctx->stream);
+    launch_attn_fwd(f, u.d, ctx->logit_mode == LOGIT_F32 ? LOGIT_F32 : LOGIT_F64, ctx->stream);
   };
   chunk_fwd(Kz, Vz, nullptr, u.Z, u.Z, u.Cz, 0, (double)u.P * u.Z);
   if (u.Cr) chunk_fwd(Kr, Vr, nullptr, m, m, u.Cr, u.Cz, (double)u.P * m);

@@ -8,12 +8,29 @@
 // are staged in LDS; V transposed, with the key order inside each 16-key
 // block permuted to match the score layout of the MFMA variant in use.
 //
-// Scores (logits) optionally run on fp64 MFMA and are shifted by a per-row
-// value (the target log-sum-exp) before rounding to fp32: the stored
+// Scores (logits) run on fp32 MFMA, on fp64 MFMA, or as exact integer
+// products on int8 MFMA, and are shifted by a per-row value (the target
+// log-sum-exp) in fp64 before rounding to fp32: the stored
 // St = scale*q.k - shift keeps small magnitudes, so the exp() of later
 // kernels sees a well-conditioned argument.  Softmax is online (running max
 // per query, per-lane partial sums), partial O / max / sum per key chunk are
 // merged by merge_kernel.
+//
+// Integer scores.  Every query row and key row is scaled by a power of two
+// 2^-e (e: the exponent of its largest magnitude, so each scaled element x
+// lies in (-1, 1)) and written as five base-128 digits,
+//     x = a_0/128 + a_1/128^2 + ... + a_4/128^5 + r,   0 <= r < 128^-5,
+// a_0 in [-128, 127] and a_1..a_4 in [0, 127] (int8).  Then
+//     sum_j x_j y_j = sum_{s,t} 128^-(s+t+2) sum_j a_s,j b_t,j + O(128^-5),
+// every digit product sum_j a_s,j b_t,j is an int8 MFMA with exact int32
+// accumulation, products of one weight s + t share an accumulator, and the
+// 19 products with s + t <= 5 are kept (the dropped ones add less than
+// 2^-33 * 2^(e_q + e_k) at d = 128).  The sums are combined in fp64 and
+// scaled by 2^(e_q + e_k), so a score carries only the truncation of each
+// input element below 2^-35 of its row's largest magnitude: far below the
+// accumulation rounding of fp32 MFMA, whose error grows with the partial
+// sums of the outlier channels.  (The splitting of floating-point products
+// into exact integer ones is the scheme of Ozaki, Ogita, Oishi and Rump.)
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -23,6 +40,74 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 }
 __device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+// 16x16x64 int8 product: lane (g, lq) supplies row lq of A and column lq of
+// B, bytes b of both being the same contraction index (any order that A and
+// B share), and receives C[4 g + r][lq]
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// The five digits of x * 128 (|x * 128| < 128), packed into byte c of w[0..4].
+__device__ __forceinline__ void put_digits(float t, int c, unsigned (&w)[kDigits]) {
+#pragma unroll
+  for (int s = 0; s < kDigits; ++s) {
+    const float a = floorf(t);
+    w[s] |= ((unsigned)(int)a & 0xffu) << (8 * c);
+    t = (t - a) * 128.f;
+  }
+}
+
+// Byte order of a row's digits, shared by the key planes and the query
+// operands: the 16-byte chunk 4 h + g holds dims 16 (4 h + j) + 4 g + c at
+// byte 4 j + c (j, c = 0..3), which is what lane group g supplies to the
+// integer product over dims 64 h .. 64 h + 63.  Dword of the four dims
+// 4 c4 .. 4 c4 + 3 inside a row:
+__device__ __forceinline__ int digit_dword(int c4) {
+  const int j = c4 >> 2, g = c4 & 3;
+  return (4 * (j >> 2) + g) * 4 + (j & 3);
+}
+
+// One thread per float4 of X (D / 4 threads per row, consecutive lanes):
+// the row's largest magnitude by lane exchange, its exponent e (that
+// magnitude < 2^e; 0 for a zero row), the digits of x = X * 2^-e into the
+// five planes, and scl = 2^e (NaN if the row has a non-finite element).
+template <int D>
+__global__ __launch_bounds__(256) void digit_rows_kernel(const float* X, long long rows, int* planes, float* scl) {
+  const long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = i4 / (D / 4);
+  const int c4 = (int)(i4 % (D / 4));
+  const bool ok = row < rows;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (ok) v = reinterpret_cast<const f32x4*>(X)[i4];
+  float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  int bad = !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
+#pragma unroll
+  for (int o = 1; o < D / 4; o <<= 1) {
+    m = fmaxf(m, __shfl_xor(m, o));
+    bad |= __shfl_xor(bad, o);
+  }
+  int e = 0;
+  if (!bad) frexpf(m, &e);
+  unsigned w[kDigits] = {0u, 0u, 0u, 0u, 0u};
+  if (!bad) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) put_digits(ldexpf(v[c], 7 - e), c, w);
+  }
+  if (ok) {
+    const int dw = digit_dword(c4);
+#pragma unroll
+    for (int s = 0; s < kDigits; ++s) planes[((size_t)s * rows + row) * (D / 4) + dw] = (int)w[s];
+    if (c4 == 0) scl[row] = bad ? __builtin_nanf("") : ldexpf(1.f, e);
+  }
+}
+
+void launch_digit_rows(const float* X, long long rows, int d, int* planes, float* scl, hipStream_t s) {
+  const long long n4 = rows * (d / 4);
+  if (n4 <= 0) return;
+  dim3 grid((unsigned)((n4 + 255) / 256));
+  if (d == 128) hipLaunchKernelGGL((digit_rows_kernel<128>), grid, dim3(256), 0, s, X, rows, planes, scl);
+  else hipLaunchKernelGGL((digit_rows_kernel<64>), grid, dim3(256), 0, s, X, rows, planes, scl);
 }
 
 // Key (row) index held in register r by lane group g of a 16x16 MFMA result.
@@ -46,11 +131,13 @@ __device__ __forceinline__ int vt_key(int vg, int j) {
   return 16 * (vg >> 2) + (F64 ? (vg & 3) + 4 * j : 4 * (vg & 3) + j);
 }
 
-template <int D, bool STORE, bool F64>
+template <int D, bool STORE, int SM>
 // waves_per_eu(2): at least two waves per SIMD, whose register budget the
 // interleaved score accumulators of d = 128 fill (its LDS tiles allow two
 // workgroups per CU)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(FwdArgs a) {
+  // score arithmetic; the integer scores come out in the fp32 product's layout
+  constexpr bool F64 = SM == LOGIT_F64, I8 = SM == LOGIT_I8;
   // grid row -> problem: largest k first (a workgroup's work grows with k)
   const int p = a.info ? a.info[blockIdx.y].korder : (int)blockIdx.y;
   const int c = blockIdx.z;
@@ -70,8 +157,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int kbeg = c * chunk;
   const int kend = min(k, kbeg + chunk);
 
-  __shared__ float Ks[64][D + 4];
+  __shared__ float Ks[I8 ? 1 : 64][D + 4];
   __shared__ float Vt[D][64 + 4];
+  // integer scores: the key tile's digit planes (a row's D bytes with its
+  // 16-byte chunks permuted by the row, so that the 16 rows one lane group
+  // reads fall in distinct banks) and the keys' scales
+  __shared__ __align__(16) int Ks8[I8 ? kDigits : 1][I8 ? 64 : 1][D / 4];
+  __shared__ __align__(16) float Kscl[I8 ? 64 : 4];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, lq = lane & 15;
@@ -92,6 +184,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   if constexpr (F64) {
 #pragma unroll
     for (int i = 0; i < D / 4; ++i) qd[i] = (double)qf[i];
+  }
+  // integer scores: this lane's query digits as B operands (digit s, dims
+  // 64 h .. 64 h + 63 in the shared byte order: dword j of half h holds dims
+  // 16 (4 h + j) + 4 g + c, i.e. qf[16 h + 4 j + c]) and the query's factor
+  // scale * 2^(e_q - 49); a query with a non-finite element gets NaN scores
+  i32x4 qb[I8 ? kDigits : 1][I8 ? D / 64 : 1];
+  double qfac = 0.0;
+  if constexpr (I8) {
+    float m = 0.f;
+    int bad = 0;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      m = fmaxf(m, fabsf(qf[i]));
+      bad |= !isfinite(qf[i]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    bad |= __shfl_xor(bad, 16);
+    bad |= __shfl_xor(bad, 32);
+    int e = 0;
+    if (!bad) frexpf(m, &e);
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        unsigned w[kDigits] = {0u, 0u, 0u, 0u, 0u};
+        if (!bad) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) put_digits(ldexpf(qf[16 * h + 4 * j + c], 7 - e), c, w);
+        }
+#pragma unroll
+        for (int sd = 0; sd < kDigits; ++sd) qb[sd][h][j] = (int)w[sd];
+      }
+    qfac = bad ? __builtin_nan("") : ldexp(a.scale, e - 49);
   }
   const double shift = (a.shift && qok) ? (double)a.shift[prow + q] : 0.0;
 
@@ -127,6 +253,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
     for (int u = 0; u < NL; ++u) *(f32x4*)&Ks[RPU * u + tid / (D / 4)][4 * (tid % (D / 4))] = kr[u];
   };
+  // integer scores: 16-byte chunk u of a thread is chunk tid % (D / 16) of
+  // row r of digit plane s (a plane's tile is 64 rows of D bytes, one
+  // resource per plane over the tile's rows; rows past kend read zero), and
+  // the first 64 threads take the keys' scales
+  constexpr int CPP = 64 * (D / 16) / 256;   // chunks per thread per plane
+  constexpr int NL8 = kDigits * CPP;
+  const int ch8 = tid % (D / 16);
+  auto k8_row = [&](int u) { return (tid + 256 * (u % CPP)) / (D / 16); };
+  auto load_k8 = [&](int kt, i32x4 (&kr)[NL8], float& ks) {
+    const long long rows = min(64, kend - kt);
+#pragma unroll
+    for (int sd = 0; sd < kDigits; ++sd) {
+      const auto rK = buf_rsrc(a.K8 + ((size_t)sd * a.k8rows + koff + kt) * (D / 4), rows * D);
+#pragma unroll
+      for (int v = 0; v < CPP; ++v) kr[sd * CPP + v] = buf_load4i(rK, k8_row(v) * D + 16 * ch8);
+    }
+    if (tid < 64) ks = buf_load1(buf_rsrc(a.Kscl + koff + kt, rows * 4), tid * 4);
+  };
+  auto store_k8 = [&](const i32x4 (&kr)[NL8], float ks) {
+#pragma unroll
+    for (int u = 0; u < NL8; ++u) {
+      const int r = k8_row(u);
+      *(i32x4*)&Ks8[u / CPP][r][4 * (ch8 ^ ((r / (256 / D)) & (D / 16 - 1)))] = kr[u];
+    }
+    if (tid < 64) Kscl[tid] = ks;
+  };
   // V: wave w stages keys 16 w .. 16 w + 15, lane l key 16 w + (l & 15) and
   // dims 16 u + 4 (l >> 4) .. + 3 of batch u (one 16-byte load); the four
   // floats go to the four Vt rows of those dims, in the column that vt_col
@@ -149,20 +301,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // the lane's part of the byte offset is fixed, the row part is uniform
   const int st_lane = ((F64 ? g : 4 * g) * npad + q) * 4;
   f32x4 kpre[NL], vpre[NL];
+  i32x4 kpre8[I8 ? NL8 : 1];
+  float kspre = 0.f;
   if (kbeg < kend) {
-    load_k(kbeg, kpre);
+    if constexpr (I8) load_k8(kbeg, kpre8, kspre);
+    else load_k(kbeg, kpre);
     load_v(kbeg, vpre);
-    store_k(kpre);
+    if constexpr (I8) store_k8(kpre8, kspre);
+    else store_k(kpre);
     store_v(vpre);
   }
   __syncthreads();
   for (int kt = kbeg; kt < kend; kt += 64) {
     const bool more = kt + 64 < kend;
     const bool tail = !more && kt + 64 > kend;   // the chunk's last tile may hold keys past kend
-    if (more) load_k(kt + 64, kpre);
+    if (more) {
+      if constexpr (I8) load_k8(kt + 64, kpre8, kspre);
+      else load_k(kt + 64, kpre);
+    }
 
     float sv[4][4];
-    if constexpr (F64) {
+    if constexpr (I8) {
+      // per 16-key block: the 19 digit products into six accumulators by
+      // weight s + t, pairs of weights joined exactly in int32 (each below
+      // 2^31), the three pairs in fp64, then the scale 2^(e_q + e_k - 49)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        i32x4 acc[6];
+#pragma unroll
+        for (int w = 0; w < 6; ++w) acc[w] = i32x4{0, 0, 0, 0};
+        const int row = 16 * b + lq;
+#pragma unroll
+        for (int h = 0; h < D / 64; ++h) {
+          const int ch = (4 * h + g) ^ ((row / (256 / D)) & (D / 16 - 1));
+#pragma unroll
+          for (int sd = 0; sd < kDigits; ++sd) {
+            const i32x4 av = *(const i32x4*)&Ks8[sd][row][4 * ch];
+#pragma unroll
+            for (int t = 0; t < kDigits; ++t)
+              if (sd + t <= 5) acc[sd + t] = mfma_i8(av, qb[t][h], acc[sd + t]);
+          }
+        }
+        const f32x4 ks = *(const f32x4*)&Kscl[16 * b + 4 * g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hi = acc[0][r] * 128 + acc[1][r];
+          const int mid = acc[2][r] * 128 + acc[3][r];
+          const int lo = acc[4][r] * 128 + acc[5][r];
+          const double v = fma(fma((double)hi, 16384.0, (double)mid), 16384.0, (double)lo);
+          sv[b][r] = (float)fma(v, qfac * (double)ks[r], -shift);
+        }
+      }
+    } else if constexpr (F64) {
       // the four 16-key blocks' score products interleaved: each column
       // group of K is read from LDS once for 16 products (3% faster than
       // block by block on the long-context heads)
@@ -186,7 +376,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      if constexpr (!F64) {
+      if constexpr (!F64 && !I8) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
@@ -227,7 +417,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     __syncthreads();   // every wave is done with this tile's K
     if (more) {
-      store_k(kpre);
+      if constexpr (I8) store_k8(kpre8, kspre);
+      else store_k(kpre);
       load_v(kt + 64, vpre);
     }
 
@@ -409,24 +600,33 @@ __global__ __launch_bounds__(256) void attn_pv_kernel(FwdArgs a) {
   }
 }
 
-void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s) {
+void launch_attn_fwd(const FwdArgs& a, int d, int logit_mode, hipStream_t s) {
   dim3 grid((a.n + 63) / 64, a.P, a.C);
   if (a.Sload) {
+    // the stored scores are in the layout of the product that formed them
+    const bool f64 = logit_mode == LOGIT_F64;
 #define KVS_PV(DD, FF) hipLaunchKernelGGL((attn_pv_kernel<DD, FF>), grid, dim3(256), 0, s, a)
-    if (d == 128) { if (logit_f64) KVS_PV(128, true); else KVS_PV(128, false); }
-    else { if (logit_f64) KVS_PV(64, true); else KVS_PV(64, false); }
+    if (d == 128) { if (f64) KVS_PV(128, true); else KVS_PV(128, false); }
+    else { if (f64) KVS_PV(64, true); else KVS_PV(64, false); }
 #undef KVS_PV
     return;
   }
   const bool store = a.St != nullptr;
-#define KVS_FWD(DD, SS, FF) hipLaunchKernelGGL((attn_fwd_kernel<DD, SS, FF>), grid, dim3(256), 0, s, a)
+#define KVS_FWD(DD, SS, MM) hipLaunchKernelGGL((attn_fwd_kernel<DD, SS, MM>), grid, dim3(256), 0, s, a)
+#define KVS_FWD_M(DD, SS)                                           \
+  do {                                                              \
+    if (logit_mode == LOGIT_I8) KVS_FWD(DD, SS, LOGIT_I8);          \
+    else if (logit_mode == LOGIT_F64) KVS_FWD(DD, SS, LOGIT_F64);   \
+    else KVS_FWD(DD, SS, LOGIT_F32);                                \
+  } while (0)
   if (d == 128) {
-    if (store) { if (logit_f64) KVS_FWD(128, true, true); else KVS_FWD(128, true, false); }
-    else { if (logit_f64) KVS_FWD(128, false, true); else KVS_FWD(128, false, false); }
+    if (store) KVS_FWD_M(128, true);
+    else KVS_FWD_M(128, false);
   } else {
-    if (store) { if (logit_f64) KVS_FWD(64, true, true); else KVS_FWD(64, true, false); }
-    else { if (logit_f64) KVS_FWD(64, false, true); else KVS_FWD(64, false, false); }
+    if (store) KVS_FWD_M(64, true);
+    else KVS_FWD_M(64, false);
   }
+#undef KVS_FWD_M
 #undef KVS_FWD
 }
 

@@ -9,6 +9,7 @@ namespace kvs {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHistMax = 16;            // L-BFGS pairs kept at most
 constexpr int kSlots = kHistMax + 1;    // ring slots (history + one staging slot)
@@ -28,6 +29,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, lon
 // 16 (4) bytes at byte offset `off` of the resource, as floats
 __device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ i32x4 buf_load4i(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 __device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
@@ -143,8 +147,18 @@ struct FwdArgs {
   const ProbInfo* info;    // NULL: uniform k = kuni rows at K + p*kuni*d
   int P, n, C, kuni, kmax;
   double scale;
+  // integer score products (mode LOGIT_I8): digit planes of the keys and their
+  // row scales, as written by launch_digit_rows for the rows of K
+  const int* K8; const float* Kscl; long long k8rows;
 };
-void launch_attn_fwd(const FwdArgs& a, int d, bool logit_f64, hipStream_t s);
+// Score (logit) arithmetic of the forward: fp32 MFMA, fp64 MFMA, or exact
+// integer products of base-128 digits on int8 MFMA.
+enum { LOGIT_F32 = 0, LOGIT_F64 = 1, LOGIT_I8 = 2 };
+constexpr int kDigits = 5;   // base-128 digits per element of the integer scores
+void launch_attn_fwd(const FwdArgs& a, int d, int logit_mode, hipStream_t s);
+// Digit planes of `rows` rows of X (d floats each) for LOGIT_I8 forwards:
+// planes [5][rows][d] bytes, scales [rows].
+void launch_digit_rows(const float* X, long long rows, int d, int* planes, float* scl, hipStream_t s);
 
 struct MergeArgs {
   const float* Opart; const float* Mpart; const float* Lpart;

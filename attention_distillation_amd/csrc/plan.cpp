@@ -199,6 +199,9 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   take(p.r_g, f * (size_t)p.ktot * p.d);
   take(p.r_p, f * (size_t)p.ktot * p.d);
   take(p.r_Kt, f * (size_t)p.ktot * p.d);
+  // digit planes of the keys and their scales (integer score products)
+  take(p.r_K8, (size_t)kDigits * p.ktot * p.d);
+  take(p.r_Kscl, f * (size_t)p.ktot);
   take(p.r_S, f * (size_t)(H + 1) * p.ktot * p.d);
   take(p.r_Yh, f * (size_t)(H + 1) * p.ktot * p.d);
   take(p.r_Kc, f * (size_t)p.ktot * p.d);

@@ -23,7 +23,7 @@ struct Plan {
   // workspace regions
   Region r_info, r_state, r_status, r_yref, r_lseref, r_St, r_Opart, r_Mpart, r_Lpart, r_G, r_e,
       r_crow, r_part, r_dK, r_grad, r_Mg, r_M, r_tr, r_mu, r_cinfo, r_X, r_imp, r_hpart, r_g, r_p, r_Kt,
-      r_S, r_Yh, r_idx, r_flags, r_loss, r_Kc, r_Vc, r_cnt, r_Dinv, r_R, r_coff;
+      r_S, r_Yh, r_idx, r_flags, r_loss, r_Kc, r_Vc, r_cnt, r_Dinv, r_R, r_coff, r_K8, r_Kscl;
   size_t ws_bytes = 0;
   // persistent L-BFGS state buffer (kvs_lbfgs_* calls)
   Region s_state, s_g, s_p, s_S, s_Yh;

@@ -62,16 +62,45 @@ sys.path.insert(0, ROOT)
 # MI355X published dense peaks
 PEAK_FP32_MFMA = 157.3e12
 PEAK_FP64_MFMA = 78.6e12
+PEAK_INT8_MFMA = 5.0e15
 PEAK_HBM = 8.0e12
+# the integer scores of the loss forward: digit products per score (five
+# base-128 digits per element, the pairs of weight s + t <= 5)
+INT8_PRODUCTS = 19
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def mixed_fwd_peak():
-    """Forward kernel: half its flops (Q Kc^T) on fp64 MFMA, half (A Vc) on fp32."""
-    return 1.0 / (0.5 / PEAK_FP64_MFMA + 0.5 / PEAK_FP32_MFMA)
+LOGIT_NOTES = {
+    "int8": "exact integer products of five base-128 digits per element on int8 MFMA "
+            f"({INT8_PRODUCTS} products, int32 sums), shifted in fp64, stored fp32",
+    "fp64": "fp64 MFMA, shifted in fp64, stored fp32",
+    "fp32": "fp32 MFMA, shifted in fp64, stored fp32"}
+
+
+def logit_mode():
+    """Score arithmetic of the library's loss forwards (KVS_LOGITS, default int8)."""
+    m = os.environ.get("KVS_LOGITS", "int8")
+    return m if m in ("fp32", "fp64") else "int8"
+
+
+def score_time_per_flop(mode):
+    """Seconds at peak per algorithmic flop of Q Kc^T: fp32 or fp64 MFMA, or
+    INT8_PRODUCTS int8 digit products per multiply-add."""
+    if mode == "fp64":
+        return 1.0 / PEAK_FP64_MFMA
+    if mode == "fp32":
+        return 1.0 / PEAK_FP32_MFMA
+    return INT8_PRODUCTS / PEAK_INT8_MFMA
+
+
+def mixed_fwd_peak(mode=None):
+    """Forward kernel: half its algorithmic flops (Q Kc^T) on the score
+    arithmetic's unit, half (A Vc) on fp32 MFMA; the peak is the harmonic
+    mix (the MFMA pipes are shared)."""
+    return 1.0 / (0.5 * score_time_per_flop(mode or logit_mode()) + 0.5 / PEAK_FP32_MFMA)
 
 
 # HBM bytes per launch of a kernel on one workload (bench row), from
@@ -292,7 +321,8 @@ def bench_use(args, torch, K):
     st = event_pass(torch, K, ctx, ["use_attn_fwd"], step, args.steps)["use_attn_fwd"]
     avg_s = st["ms"] / st["launches"] / 1e3
     achieved = st["flops"] / st["launches"] / avg_s
-    peak = mixed_fwd_peak()
+    # the use-side forwards form their scores on fp64 MFMA (fp32 if asked)
+    peak = mixed_fwd_peak("fp32" if logit_mode() == "fp32" else "fp64")
     roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3), "peak": round(peak / 1e12, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_for("use_attn_fwd", w.name), "kernel": "use_attn_fwd",
@@ -380,7 +410,8 @@ def bench_solve(args, torch, K):
         "value": round(P * args.steps / elapsed, 2), "unit": "problem-solves/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(1e3 * elapsed / args.steps, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (scores f64, residual f64)",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (scores " + {"int8": "exact int8 digit products", "fp64": "f64",
+                                     "fp32": "f32"}[logit_mode()] + ", residual f64)",
         "data": "synthetic",
         "config": {"workload": w.name, "row": "solve", "problems": P, "n": n, "Z": Z, "k": k, "d": d,
                    "keys": "Select+Fit"},
@@ -716,7 +747,7 @@ def bench_vector(args, torch, K):
 
 # kernels whose launches are timed with HIP events during the timed blocks
 TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "attn_pv", "potrf_panel", "back_subst", "merge",
-                 "hist_dots", "direction"]
+                 "hist_dots", "direction", "key_digits"]
 # contraction kernels (MFMA roofline) and their peaks: the loss forward forms
 # its scores on fp64 MFMA (half its flops) and A Vc on fp32 MFMA (the other
 # half); the others are fp32 MFMA only
@@ -736,11 +767,14 @@ def kernel_rows(stats):
             fl = st["flops"]
             row["tflops"] = round(fl / sec / 1e12, 2)
             if name == "attn_fwd":
-                # t_min = (fl/2)/fp64 peak + (fl/2)/fp32 peak, the MFMA pipes being shared
-                tmin = 0.5 * fl / PEAK_FP64_MFMA + 0.5 * fl / PEAK_FP32_MFMA
-                row["frac_mfma_mixed"] = round(tmin / sec, 4)
-                row["frac_fp64_part"] = round(0.5 * fl / sec / PEAK_FP64_MFMA, 4)
+                # t_min = (fl/2) on the score unit + (fl/2)/fp32 peak, the MFMA pipes being shared
+                mode = logit_mode()
+                ts = 0.5 * fl * score_time_per_flop(mode)
+                row["frac_mfma_mixed"] = round((ts + 0.5 * fl / PEAK_FP32_MFMA) / sec, 4)
+                row[f"frac_{mode}_scores_part"] = round(ts / sec, 4)
                 row["frac_fp32_part"] = round(0.5 * fl / sec / PEAK_FP32_MFMA, 4)
+                # the algorithmic rate against the fp32 MFMA peak
+                row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
             else:
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
         rows[name] = row
@@ -889,8 +923,11 @@ def bench_compress(args, torch, K):
     fl_launch = st["flops"] / st["launches"]
     achieved = fl_launch / avg_s
     if name == "attn_fwd":
-        peak = 1.0 / (0.5 / PEAK_FP64_MFMA + 0.5 / PEAK_FP32_MFMA)
-        peak_note = "harmonic mix of the fp64 (scores) and fp32 (A Vc) MFMA peaks"
+        peak = mixed_fwd_peak()
+        peak_note = {"fp64": "harmonic mix of the fp64 (scores) and fp32 (A Vc) MFMA peaks",
+                     "fp32": "fp32 MFMA",
+                     "int8": f"harmonic mix of the int8 MFMA peak over {INT8_PRODUCTS} digit products "
+                             f"(scores) and the fp32 MFMA peak (A Vc)"}[logit_mode()]
     else:
         peak = PEAK_FP32_MFMA
         peak_note = "fp32 MFMA"
@@ -935,7 +972,7 @@ def bench_compress(args, torch, K):
                    "iters": T, "vc_every": VC, "history": 10, "pilot": pilot,
                    "step": f"one block of {VC} L-BFGS iterations of all {P} problems with the value "
                            f"re-solve and loss/gradient after it (main run at the pilot's ragged k)",
-                   "logits": "fp64 MFMA (stored fp32)", "contractions": "fp32 MFMA"},
+                   "logits": LOGIT_NOTES[logit_mode()], "contractions": "fp32 MFMA"},
         "latency": {"whole_model_compress_s": round(t_latency, 3), "pilot_and_allocation_s": round(t_pilot, 3),
                     "reference_and_select_fit_s": round(t_begin, 3),
                     "note": f"pilot ({pilot} iterations at k0) + reallocation + reference attention + "
