@@ -18,12 +18,13 @@
 namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
-  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_DIGITS, PROF_NCLASS
+  PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_DIGITS, PROF_RESID, PROF_FSUB,
+  PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
     "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv",
-    "key_digits"};
+    "key_digits", "resid_rhs", "fwd_subst"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -374,12 +375,22 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   ra.St = g.St; ra.e = g.e; ra.G = at<float>(ws, pl.r_G); ra.info = g.info;
   ra.Rpart = at<double>(ws, pl.r_R); ra.xtot = pl.kpadtot * pl.d;
   ra.P = pl.P; ra.n = pl.n; ra.Cr = pl.Crf; ra.kpadmax = pl.kpadmax;
-  launch_resid_rhs(ra, pl.d, ctx->stream);
+  {
+    double ks = 0;
+    for (const auto& q : pl.info) ks += q.k;
+    Prof pr(ctx, PROF_RESID, 2.0 * pl.n * pl.d * ks, 4.0 * (ks * pl.npad + (double)pl.P * pl.n * (pl.d + 1)));
+    launch_resid_rhs(ra, pl.d, ctx->stream);
+  }
   FsubArgs fa{};
   fa.Rpart = ra.Rpart; fa.xtot = ra.xtot; fa.Cr = ra.Cr; fa.mu = c.mu; fa.Vc = Vc; fa.M = M;
   fa.Dinv = c.Dinv; fa.X = bk.X; fa.info_out = c.info_out; fa.info = g.info; fa.P = pl.P;
   fa.kpadmax = pl.kpadmax; fa.lds_max = ctx->lds_max;
-  launch_fwd_subst(fa, pl.d, ctx->stream);
+  {
+    double fl = 0;
+    for (const auto& q : pl.info) fl += 1.0 * q.kpad * q.kpad * pl.d;
+    Prof pr(ctx, PROF_FSUB, fl, 0);
+    launch_fwd_subst(fa, pl.d, ctx->stream);
+  }
   bk.accumulate = 1;
   bk.flags = nullptr;
   launch_back_subst(bk, pl.d, ctx->stream);

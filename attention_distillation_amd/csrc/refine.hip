@@ -26,25 +26,31 @@ __device__ __forceinline__ f32x4 mfma_r(float a, float b, f32x4 c) {
 }
 
 // Rpart[c][xoff + key * D + dim] = sum over the queries q of split c of
-// A[q][key] G[q][dim], A = exp(St - e).  Keys past k read the last key (their
-// rows are ignored by the substitution); queries past the split are zero.
+// A[q][key] G[q][dim], A = exp(St - e).  One workgroup = 4 wave64s = 64 keys
+// (16 per wave) x one query split.  The layout is the backward's with dS
+// replaced by A: a lane's stored scores (key kw + lq, queries 16 qb + 4 g ..
+// + 3 of a 64-query tile) are the A operand of the product as they are
+// loaded, G is staged transposed in LDS as the B operand.  The loads of the
+// next query tile (G, scores, e) are issued inside the MFMA work of this one
+// through buffer resources: G and e over the tile's rows (queries past the
+// split's end read zero), the scores over the wave's 16 key rows (keys past
+// k read zero and weigh zero; their rows are ignored by the substitution).
+// Products are summed in fp32 within a tile and in fp64 across tiles.
 template <int D>
-__global__ __launch_bounds__(256) void resid_rhs_kernel(RhsArgs a) {
-  const int p = blockIdx.y, kt = blockIdx.x, c = blockIdx.z;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void resid_rhs_kernel(RhsArgs a) {
+  const int p = blockIdx.y, kt0 = 64 * blockIdx.x, c = blockIdx.z;
   const ProbInfo pi = a.info[p];
-  if (64 * kt >= pi.kpad) return;
+  if (kt0 >= pi.kpad) return;
   const int n = a.n, npad = (n + 3) & ~3;
   const int nq = ((((n + a.Cr - 1) / a.Cr) + 63) / 64) * 64;
   const int qbeg = c * nq, qend = min(n, qbeg + nq);
   constexpr int DB = D / 16;
 
-  __shared__ float As[64][68];   // [key][query]
-  __shared__ float Gt[D][68];    // [dim][query]
+  __shared__ float Gt[D][64 + 4];    // [dim][query]
+  __shared__ __align__(16) float es[64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
-  const float* St = a.St + pi.soff;
-  const float* E = a.e + (size_t)p * n;
-  const float* Gq = a.G + (size_t)p * n * D;
-  const int krow = 64 * kt;
+  const size_t prow = (size_t)p * n;
+  const float* Gp = a.G + prow * D;
 
   double acc64[DB][4];
 #pragma unroll
@@ -52,61 +58,83 @@ __global__ __launch_bounds__(256) void resid_rhs_kernel(RhsArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc64[db][r] = 0.0;
 
+  // G transposed: lane l of a quad covering queries 4 m .. 4 m + 3 and dims
+  // 4 c .. 4 c + 3 reads dim 4 c + l of the four queries (coalesced 4-byte
+  // loads across the quads of a wave) and writes them as one 16-byte row
+  // segment of Gt
+  constexpr int NL = 64 * (D / 4) / 256;
+  // first key row of this wave (uniform across it: the resource base needs that)
+  const int kw = kt0 + 16 * __builtin_amdgcn_readfirstlane(wave);
+  const auto rS = buf_rsrc(a.St + pi.soff + (size_t)kw * npad, (long long)max(0, min(16, pi.k - kw)) * npad * 4);
+  const int soff_l = (lq * npad + 4 * g) * 4;
+  const bool kok = kw + lq < pi.k;     // this lane's key (rows past k stay zero)
+  f32x4 gpre[NL], spre[4];
+  float epre = 0.f;
+  auto prefetch = [&](int qt) {
+    const long long rows = min(64, qend - qt);
+    const auto rG = buf_rsrc(Gp + (size_t)qt * D, rows * D * 4);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int rq = 4 * (i / (4 * (D / 4))), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gpre[u][j] = buf_load1(rG, ((rq + j) * D + dq) * 4);
+    }
+    const int so = soff_l + qt * 4;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) spre[qb] = buf_load4(rS, so + 64 * qb);
+    if (tid < 64) epre = buf_load1(buf_rsrc(a.e + prow + qt, rows * 4), tid * 4);
+  };
+  if (qbeg < qend) prefetch(qbeg);
   for (int qt = qbeg; qt < qend; qt += 64) {
-    // weights: key i >> 4, queries 4 (i % 16) .. + 3 (one 16-byte load)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + 256 * u;
-      const int r = i >> 4, q0 = qt + 4 * (i & 15);
-      const f32x4 v = *(const f32x4*)(St + (size_t)min(krow + r, pi.k - 1) * npad + min(q0, npad - 4));
-      f32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (q0 + j < qend) ? __expf(v[j] - E[min(q0 + j, n - 1)]) : 0.f;
-      *(f32x4*)&As[r][4 * (i & 15)] = w;
-    }
-    // G transposed: dim i % D, queries 4 (i / D) .. + 3 (consecutive lanes,
-    // consecutive dims)
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-      const int i = tid + 256 * u;
-      const int dim = i % D, q4 = 4 * (i / D);
-      f32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = qt + q4 + j;
-        w[j] = q < qend ? Gq[(size_t)q * D + dim] : 0.f;
-      }
-      *(f32x4*)&Gt[dim][q4] = w;
-    }
     __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int rq = 4 * (i / (4 * (D / 4))), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
+      *(f32x4*)&Gt[dq][rq] = gpre[u];
+    }
+    if (tid < 64) es[tid] = epre;
+    f32x4 svv[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) svv[qb] = spre[qb];
+    __syncthreads();
+    if (qt + 64 < qend) prefetch(qt + 64);
+
     f32x4 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int qq = 0; qq < 64; qq += 16) {
-      const f32x4 av = *(const f32x4*)&As[16 * wave + lq][qq + 4 * g];
+    for (int qb = 0; qb < 4; ++qb) {
+      const f32x4 e4 = *(const f32x4*)&es[16 * qb + 4 * g];
+      float w[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = __expf(svv[qb][r] - e4[r]);
+        w[r] = (kok && qt + 16 * qb + 4 * g + r < qend) ? v : 0.f;
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const f32x4 bv = *(const f32x4*)&Gt[16 * db + lq][qq + 4 * g];
-        acc[db] = mfma_r(av.x, bv.x, acc[db]);
-        acc[db] = mfma_r(av.y, bv.y, acc[db]);
-        acc[db] = mfma_r(av.z, bv.z, acc[db]);
-        acc[db] = mfma_r(av.w, bv.w, acc[db]);
+        const f32x4 gv = *(const f32x4*)&Gt[16 * db + lq][16 * qb + 4 * g];
+        acc[db] = mfma_r(w[0], gv.x, acc[db]);
+        acc[db] = mfma_r(w[1], gv.y, acc[db]);
+        acc[db] = mfma_r(w[2], gv.z, acc[db]);
+        acc[db] = mfma_r(w[3], gv.w, acc[db]);
       }
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc64[db][r] += (double)acc[db][r];
-    __syncthreads();
   }
 
+  // acc64[db][r] = sum A[q][key = kt0 + 16 wave + 4 g + r] G[q][dim = 16 db + lq]
   double* out = a.Rpart + (size_t)c * a.xtot + pi.xoff;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      out[(size_t)(krow + 16 * wave + 4 * g + r) * D + 16 * db + lq] = acc64[db][r];
+      out[(size_t)(kt0 + 16 * wave + 4 * g + r) * D + 16 * db + lq] = acc64[db][r];
 }
 
 // r = -1/2 sum_c Rpart[c] - mu Vc (rows < k; 0 below), then L Z = r for 16
@@ -195,11 +223,13 @@ __global__ __launch_bounds__(256) void fwd_subst_kernel(FsubArgs a) {
 }  // namespace
 
 int refine_splits(int P, int kpadmax, int n) {
-  // about four workgroups per CU over the key tiles, each split at least two
+  // about four workgroups per CU over the key tiles and no split longer than
+  // 64 query tiles (long sweeps leave long tails), each split at least two
   // query tiles long, at most 16 splits
   const long long tiles = (long long)P * (kpadmax / 64);
   const long long qtiles = (n + 63) / 64;
   long long c = tiles > 0 ? (1024 + tiles - 1) / tiles : 1;
+  c = std::max(c, (qtiles + 63) / 64);
   c = std::min(c, std::max(1LL, qtiles / 2));
   c = std::min(c, 16LL);
   return (int)std::max(1LL, c);

@@ -747,11 +747,11 @@ def bench_vector(args, torch, K):
 
 # kernels whose launches are timed with HIP events during the timed blocks
 TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "attn_pv", "potrf_panel", "back_subst", "merge",
-                 "hist_dots", "direction", "key_digits"]
+                 "hist_dots", "direction", "key_digits", "resid_rhs", "fwd_subst"]
 # contraction kernels (MFMA roofline) and their peaks: the loss forward forms
 # its scores on fp64 MFMA (half its flops) and A Vc on fp32 MFMA (the other
 # half); the others are fp32 MFMA only
-CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "attn_pv")
+CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "attn_pv", "resid_rhs")
 
 
 def kernel_rows(stats):
