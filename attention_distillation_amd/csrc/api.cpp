@@ -393,7 +393,12 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   }
   bk.accumulate = 1;
   bk.flags = nullptr;
-  launch_back_subst(bk, pl.d, ctx->stream);
+  {
+    double fl = 0;
+    for (const auto& q : pl.info) fl += 1.0 * q.kpad * q.kpad * pl.d;
+    Prof pr(ctx, PROF_BACK, fl, 0);
+    launch_back_subst(bk, pl.d, ctx->stream);
+  }
 }
 
 // Select+Fit: importance, top-k, gather, then the ridge fit at the selected keys.
