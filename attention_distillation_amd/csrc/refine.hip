@@ -142,9 +142,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
 // Z_i = inv(L_ii) W_i, then W_r -= L_ri Z_i for every r > i.  W is held in
 // LDS ([kpad][16]) while it fits, else in the per-slab buffer in X.  The
 // contraction index of an MFMA step s in lane group g is 16 g + s, so every
-// lane reads 16 consecutive floats of a row of L (four 16-byte loads).
+// lane reads 16 consecutive floats of a row of L (four 16-byte loads).  Eight
+// waves: waves 0..3 solve the diagonal block (16 rows each, inv(L_ii) loaded
+// one step ahead), all eight share the step's block updates, and the first
+// two L blocks a wave updates in a step are loaded while the previous step
+// finishes.
 template <int D, bool INLDS>
-__global__ __launch_bounds__(256) void fwd_subst_kernel(FsubArgs a) {
+__global__ __launch_bounds__(512) void fwd_subst_kernel(FsubArgs a) {
   extern __shared__ float dyn[];        // INLDS: W [kpadmax][16], then Xs [64][16]
   const int p = blockIdx.y;
   const ProbInfo pi = a.info[p];
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256) void fwd_subst_kernel(FsubArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
 
   const double mu = a.mu[p];
-  for (int e = tid; e < pi.kpad * 16; e += 256) {
+  for (int e = tid; e < pi.kpad * 16; e += 512) {
     const int row = e >> 4, c = e & 15;
     float v = 0.f;
     if (row < k) {
@@ -169,52 +173,89 @@ __global__ __launch_bounds__(256) void fwd_subst_kernel(FsubArgs a) {
     }
     W[e] = v;
   }
+
+  // -L_{rb,i} as A operands: rows 64 rb + 16 q + lq, columns 64 i + 16 g + s
+  auto load_block = [&](float (&lv)[4][16], int rb, int i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* Lr = Mp + (size_t)(64 * rb + 16 * q + lq) * ld + 64 * i + 16 * g;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 v = *(const f32x4*)(Lr + 4 * t);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lv[q][4 * t + u] = -v[u];
+      }
+    }
+  };
+  // W_rb -= L_{rb,i} Z_i, accumulator seeded with W_rb
+  auto update_block = [&](const float (&lv)[4][16], const float (&bz)[16], int rb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = W[(64 * rb + 16 * q + 4 * g + r) * 16 + lq];
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) acc = mfma_r(lv[q][s2], bz[s2], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) W[(64 * rb + 16 * q + 4 * g + r) * 16 + lq] = acc[r];
+    }
+  };
+  // inv(L_ii) rows 16 wave + lq, columns 16 g + s
+  auto load_dinv = [&](float (&dv)[16], int i) {
+    const float* Di = Dinv + (size_t)i * 64 * 64 + (16 * wave + lq) * 64 + 16 * g;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 v = *(const f32x4*)(Di + 4 * t);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) dv[4 * t + u] = v[u];
+    }
+  };
+  const bool dw = wave < 4;
+  float dv[16];
+  if (dw) load_dinv(dv, 0);
+  float l0[4][16], l1[4][16];
+  if (1 + wave < KT) load_block(l0, 1 + wave, 0);
+  if (9 + wave < KT) load_block(l1, 9 + wave, 0);
   __syncthreads();
 
   for (int i = 0; i < KT; ++i) {
     // Z_i rows b = 16 wave + 4 g + r: sum_a inv(L_ii)[b][a] W_i[a][c]
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    {
-      const float* Di = Dinv + (size_t)i * 64 * 64 + (16 * wave + lq) * 64 + 16 * g;
-      f32x4 d4[4];
+    if (dw) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) d4[t] = *(const f32x4*)(Di + 4 * t);
-#pragma unroll
-      for (int s = 0; s < 16; ++s) x = mfma_r(d4[s >> 2][s & 3], W[(64 * i + 16 * g + s) * 16 + lq], x);
+      for (int s2 = 0; s2 < 16; ++s2) x = mfma_r(dv[s2], W[(64 * i + 16 * g + s2) * 16 + lq], x);
 #pragma unroll
       for (int r = 0; r < 4; ++r) Xs[(16 * wave + 4 * g + r) * 16 + lq] = x[r];
+      if (i + 1 < KT) load_dinv(dv, i + 1);
     }
     __syncthreads();
     // every wave has read W_i: it now holds Z_i
+    if (dw) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) W[(64 * i + 16 * wave + 4 * g + r) * 16 + lq] = x[r];
+      for (int r = 0; r < 4; ++r) W[(64 * i + 16 * wave + 4 * g + r) * 16 + lq] = x[r];
+    }
     if (i + 1 < KT) {
       float bz[16];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) bz[s] = Xs[(16 * g + s) * 16 + lq];
-      // W_rb -= L_{rb,i} Z_i; wave w owns the blocks rb = i + 1 + w, + 4, ...
-      for (int rb = i + 1 + wave; rb < KT; rb += 4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float* Lr = Mp + (size_t)(64 * rb + 16 * q + lq) * ld + 64 * i + 16 * g;
-          f32x4 l4[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) l4[t] = *(const f32x4*)(Lr + 4 * t);
-          f32x4 acc;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = W[(64 * rb + 16 * q + 4 * g + r) * 16 + lq];
-#pragma unroll
-          for (int s = 0; s < 16; ++s) acc = mfma_r(-l4[s >> 2][s & 3], bz[s], acc);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) W[(64 * rb + 16 * q + 4 * g + r) * 16 + lq] = acc[r];
-        }
+      for (int s2 = 0; s2 < 16; ++s2) bz[s2] = Xs[(16 * g + s2) * 16 + lq];
+      const int r0 = i + 1 + wave, r1 = r0 + 8;
+      if (r0 < KT) update_block(l0, bz, r0);
+      if (r1 < KT) update_block(l1, bz, r1);
+      for (int rb = r0 + 16; rb < KT; rb += 16) {
+        load_block(l0, rb, i);
+        if (rb + 8 < KT) load_block(l1, rb + 8, i);
+        update_block(l0, bz, rb);
+        if (rb + 8 < KT) update_block(l1, bz, rb + 8);
       }
+      // the next step's first blocks
+      if (r0 + 1 < KT) load_block(l0, r0 + 1, i + 1);
+      if (r1 + 1 < KT) load_block(l1, r1 + 1, i + 1);
     }
     __syncthreads();
   }
 
   // Z into the A^T Y rows of M: M[kpad + dim0 + c][row] = Z[row][c]
-  for (int e = tid; e < pi.kpad * 16; e += 256) {
+  for (int e = tid; e < pi.kpad * 16; e += 512) {
     const int c = e / pi.kpad, row = e % pi.kpad;
     Mp[(size_t)(pi.kpad + dim0 + c) * ld + row] = W[row * 16 + c];
   }
@@ -245,13 +286,13 @@ void launch_fwd_subst(const FsubArgs& a, int d, hipStream_t s) {
   dim3 grid(d / 16, a.P);
   const size_t lds = back_subst_lds_bytes(a.kpadmax);
   if (lds <= (size_t)a.lds_max) {
-    if (d == 128) hipLaunchKernelGGL((fwd_subst_kernel<128, true>), grid, dim3(256), lds, s, a);
-    else hipLaunchKernelGGL((fwd_subst_kernel<64, true>), grid, dim3(256), lds, s, a);
+    if (d == 128) hipLaunchKernelGGL((fwd_subst_kernel<128, true>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((fwd_subst_kernel<64, true>), grid, dim3(512), lds, s, a);
     return;
   }
   const size_t xs = 64 * 16 * sizeof(float);
-  if (d == 128) hipLaunchKernelGGL((fwd_subst_kernel<128, false>), grid, dim3(256), xs, s, a);
-  else hipLaunchKernelGGL((fwd_subst_kernel<64, false>), grid, dim3(256), xs, s, a);
+  if (d == 128) hipLaunchKernelGGL((fwd_subst_kernel<128, false>), grid, dim3(512), xs, s, a);
+  else hipLaunchKernelGGL((fwd_subst_kernel<64, false>), grid, dim3(512), xs, s, a);
 }
 
 }  // namespace kvs
