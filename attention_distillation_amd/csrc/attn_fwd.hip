@@ -18,9 +18,12 @@
 //
 // Integer scores.  Every query row and key row is scaled by a power of two
 // 2^-e (e: the exponent of its largest magnitude, so each scaled element x
-// lies in (-1, 1)) and written as five base-128 digits,
-//     x = a_0/128 + a_1/128^2 + ... + a_4/128^5 + r,   0 <= r < 128^-5,
-// a_0 in [-128, 127] and a_1..a_4 in [0, 127] (int8).  Then
+// lies in (-1, 1)) and written as five base-128 digits of its magnitude,
+// each carrying the element's sign,
+//     x = sign(x) (a_0/128 + a_1/128^2 + ... + a_4/128^5 + r),   0 <= r < 128^-5,
+// a_0..a_4 in [0, 127], so every signed digit fits int8 (peeling the digits
+// of |x| is exact: the fraction of a non-negative float is representable,
+// which a floor of a negative value close to zero would not keep).  Then
 //     sum_j x_j y_j = sum_{s,t} 128^-(s+t+2) sum_j a_s,j b_t,j + O(128^-5),
 // every digit product sum_j a_s,j b_t,j is an int8 MFMA with exact int32
 // accumulation, products of one weight s + t share an accumulator, and the
@@ -48,13 +51,17 @@ __device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// The five digits of x * 128 (|x * 128| < 128), packed into byte c of w[0..4].
+// The five digits of t = x * 128 (|t| < 128), each with the sign of t,
+// packed into byte c of w[0..4].
 __device__ __forceinline__ void put_digits(float t, int c, unsigned (&w)[kDigits]) {
+  const bool neg = t < 0.f;
+  float u = fabsf(t);
 #pragma unroll
   for (int s = 0; s < kDigits; ++s) {
-    const float a = floorf(t);
-    w[s] |= ((unsigned)(int)a & 0xffu) << (8 * c);
-    t = (t - a) * 128.f;
+    const float a = floorf(u);
+    const int q = (int)a;
+    w[s] |= ((unsigned)(neg ? -q : q) & 0xffu) << (8 * c);
+    u = (u - a) * 128.f;
   }
 }
 

@@ -160,3 +160,69 @@ def test_loss_grad_zero_at_compress_zone():
     Lg = float(host(loss)[0])
     say(f"[zero] L={Lg:.3e} |Y|^2={float((Y ** 2).sum()):.3e}")
     assert 0 <= Lg <= 1e-9 * float((Y ** 2).sum())
+
+
+def _edge_rows(X, rng):
+    """Rows whose digits exercise the integer score products: a zero row, a
+    row with one nonzero element, rows scaled by 2^-40 and 2^5, a row whose
+    elements span 2^-63 .. 1 of its largest magnitude, and a row of equal
+    magnitudes with alternating signs (the leading digit at both ends of its
+    range)."""
+    X = X.copy()
+    d = X.shape[1]
+    X[0] = 0.0
+    X[1] = 0.0
+    X[1, int(rng.integers(d))] = 3.0
+    X[2] *= np.float32(2.0 ** -40)
+    X[3] *= np.float32(2.0 ** 5)
+    X[4] = X[4] * np.exp2(-np.arange(d) * 63.0 / (d - 1)).astype(np.float32)
+    X[5] = np.where(np.arange(d) % 2 == 0, 1.0, -1.0).astype(np.float32) * np.float32(0.75)
+    return X.astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", ["int8", "fp64"])
+@pytest.mark.parametrize("name", ["single-head-d64", "qwen-one-layer"])
+def test_loss_grad_edge_rows(name, mode, monkeypatch):
+    """Loss and gradient at the Select+Fit start with six key rows and six
+    query rows replaced by _edge_rows, for the integer score products (the
+    default) and the fp64 ones (KVS_LOGITS=fp64), against the oracle on the
+    same float32 arrays (its targets recomputed from the edited queries)."""
+    monkeypatch.setenv("KVS_LOGITS", mode)
+    w, b, probs = _loss_case(name, "init")
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    s = b["scale"]
+    rng = np.random.default_rng(11)
+    Qs, cases = [], []
+    for p, (Q, _, _, Kc32, Vc32) in enumerate(probs):
+        Qe = Q.copy()
+        Qe[:6] = _edge_rows(Q[:6], rng)
+        Ke = _edge_rows(Kc32, rng)
+        Y, l = O.reference_attention(Qe, b["Kz"][p], b["Vz"][p], s)
+        Qs.append(Qe)
+        cases.append((Qe, Y.astype(np.float32), l.astype(np.float32), Ke, Vc32))
+    ks = [c[3].shape[0] for c in cases]
+    say(f"[edge rows] case={name} mode={mode} P={P} n={n} d={d} k={ks}")
+    bt = K.Batch(P, d, Z, n, k=ks, scale=s)
+    ctx = K.Context()
+    ws = workspace(K.workspace_bytes(bt))
+    loss, mse = empty((P,)), empty((P,))
+    grad = empty((sum(ks), d))
+    K.kvs_loss_grad(ctx, bt, to_gpu(np.stack(Qs)), to_gpu(np.stack([c[1] for c in cases])),
+                    to_gpu(np.stack([c[2] for c in cases])), to_gpu(np.concatenate([c[3] for c in cases])),
+                    to_gpu(np.concatenate([c[4] for c in cases])), loss, grad, mse, ws)
+    lg, gg, mg = host(loss), host(grad), host(mse)
+    off = 0
+    for p, (Qe, Y32, l32, Ke, Vc32) in enumerate(cases):
+        L, g, aux = O.loss_grad(Qe, Y32, l32, Ke, Vc32, s)
+        m = aux["out"] / (n * d)
+        k = Ke.shape[0]
+        eL, eg, em = rel(lg[p], L), rel(gg[off:off + k], g), rel(mg[p], m)
+        rg = row_err(gg[off:off + k], g)
+        amp = float(np.linalg.norm(Y32) / max(np.linalg.norm(aux["R"]), 1e-300))
+        gtol = TOL * max(1.0, amp / 20.0)
+        say(f"   p={p} k={k} L={L:.6g} relL={eL:.2e} relgrad={eg:.2e} rowgrad={rg:.2e} (bar {gtol:.1e}) "
+            f"relmse={em:.2e}")
+        assert np.isfinite(lg[p]) and np.all(np.isfinite(gg[off:off + k]))
+        assert eL <= TOL and eg <= TOL and em <= TOL and rg <= gtol
+        off += k

@@ -28,9 +28,12 @@ oracle runs stored by tests/golden/make_golden.py (oracle only).
   k0: 256 llama3-8b problems, T = 200; 112 long-context problems, T = 150):
   problem 0's Select+Fit loss within 1e-4 of the oracle's, its final loss
   within 2% of the oracle's run of the same schedule, or within twice the
-  spread that the two one-rounding perturbations above give that problem,
-  whichever is larger; llama3-8b problem 0 also alone at k = 4680, the
-  largest budget the pilot hands out on that cache.
+  problem's spread, whichever is larger; llama3-8b problem 0 also alone at
+  k = 4680, the largest budget the pilot hands out on that cache.  For a
+  single problem one perturbation samples its spread once, so here the
+  GPU's part of the spread is the largest move under three one-rounding
+  perturbations (the queries by one ulp in either alternating pattern, the
+  compress-zone keys in one), beside the oracle's float32-key run.
 - kvs_compress on the whole llama3-8b batch at seeded ragged budgets (the main
   run after a reallocation), eight seeded problems against the oracle, each
   to the single-problem bar.
@@ -57,12 +60,12 @@ def band_err(x, a, b):
     return 0.0 if lo <= x <= hi else (lo - x) / lo if x < lo else (x - hi) / hi
 
 
-def ulp_perturbed(x):
+def ulp_perturbed(x, phase=0):
     """x with every element moved by one float32 ulp, up at even flat
-    positions and down at odd ones: a perturbation at the level of one
-    float32 rounding."""
+    positions and down at odd ones (phase 1: the other way round): a
+    perturbation at the level of one float32 rounding."""
     f = np.asarray(x, dtype=np.float32).ravel().copy()
-    up = np.arange(f.size) % 2 == 0
+    up = np.arange(f.size) % 2 == phase
     f[up] = np.nextafter(f[up], np.float32(np.inf))
     f[~up] = np.nextafter(f[~up], np.float32(-np.inf))
     return f.reshape(np.shape(x))
@@ -150,7 +153,7 @@ def test_pilot_full_cache(ratio):
     assert int(k_out.sum()) == Kt and k_out.min() >= 1 and k_out.max() <= Z
 
 
-def _compress(b, ks, T, Q=None):
+def _compress(b, ks, T, Q=None, Kz=None):
     P, n, d = b["Q"].shape
     Z = b["Kz"].shape[1]
     o = K.opts(iters=T)
@@ -161,9 +164,21 @@ def _compress(b, ks, T, Q=None):
     Kc, Vc = empty((kt, d)), empty((kt, d))
     loss, mse, l0 = empty((P,)), empty((P,)), empty((P,))
     flags = to_gpu(np.zeros(P, np.int32))
-    K.kvs_compress(ctx, bt, o, to_gpu(b["Q"] if Q is None else Q), to_gpu(b["Kz"]), to_gpu(b["Vz"]), Kc, Vc,
-                   loss, mse, l0, flags, ws)
+    K.kvs_compress(ctx, bt, o, to_gpu(b["Q"] if Q is None else Q), to_gpu(b["Kz"] if Kz is None else Kz),
+                   to_gpu(b["Vz"]), Kc, Vc, loss, mse, l0, flags, ws)
     return host(loss).astype(np.float64), host(l0).astype(np.float64), host(flags)
+
+
+def _gpu_spread(b, ks, T, lg):
+    """Per problem, the largest relative move of the GPU's final loss under
+    three one-rounding perturbations of its inputs (the queries moved by one
+    ulp in either alternating pattern, the compress-zone keys in one): one
+    perturbation samples a chaotic head's spread once, three bound it more
+    tightly.  Returns (spread, losses of the first perturbation)."""
+    runs = [_compress(b, ks, T, Q=ulp_perturbed(b["Q"]))[0],
+            _compress(b, ks, T, Q=ulp_perturbed(b["Q"], 1))[0],
+            _compress(b, ks, T, Kz=ulp_perturbed(b["Kz"]))[0]]
+    return np.max([np.abs(r - lg) / lg for r in runs], axis=0), runs[0]
 
 
 E2E = {
@@ -184,17 +199,17 @@ def test_compress_full_schedule(name):
     P = b["Q"].shape[0]
     say(f"[full schedule] {name}: P={P} k={k} T={T}")
     lg, l0g, fg = _compress(b, [k] * P, T)
-    lu, _, _ = _compress(b, [k] * P, T, Q=ulp_perturbed(b["Q"]))
+    ub, lu = _gpu_spread(b, [k] * P, T, lg)
     lo, l32 = run["final_loss"], run["final_loss_f32keys"]
     dev = abs(lg[0] - lo) / lo
-    spread = max(abs(l32 - lo) / lo, abs(lu[0] - lg[0]) / lg[0])
+    spread = max(abs(l32 - lo) / lo, ub[0])
     be = band_err(lg[0], lo, l32)
-    ub = np.abs(lu - lg) / lg
     say(f"   p=0 init gpu={l0g[0]:.7g} oracle={run['init_loss']:.7g}; final gpu={lg[0]:.7g} "
-        f"oracle={lo:.7g} (float32 keys {l32:.7g}; gpu with one-ulp queries {lu[0]:.7g}) deviation {dev:.2e}, "
-        f"spread {spread:.2e}, distance to the float64 / float32-key interval {be:.2e}; flags={fg[0]}; batch "
-        f"final/init median {np.median(lg / l0g):.4f}, one-ulp spread over the batch median {np.median(ub):.2e} "
-        f"max {ub.max():.2e}, flagged {int(np.count_nonzero(fg))}")
+        f"oracle={lo:.7g} (float32 keys {l32:.7g}; gpu with one-ulp queries {lu[0]:.7g}; GPU spread over three "
+        f"one-rounding perturbations {ub[0]:.2e}) deviation {dev:.2e}, spread {spread:.2e}, distance to the "
+        f"float64 / float32-key interval {be:.2e}; flags={fg[0]}; batch final/init median "
+        f"{np.median(lg / l0g):.4f}, GPU spread over the batch median {np.median(ub):.2e} max {ub.max():.2e}, "
+        f"flagged {int(np.count_nonzero(fg))}")
     assert abs(l0g[0] - run["init_loss"]) <= 1e-4 * run["init_loss"]
     assert dev <= max(0.02, 2.0 * spread)
     assert fg[0] & ~K.KVS_FLAG_NONDESCENT == 0 and run["flags"] & ~O.FLAG_NONDESCENT == 0
@@ -217,13 +232,13 @@ def test_compress_ragged_batch():
     assert len(ks) == P
     say(f"[ragged batch] {w.name}: P={P} k {min(ks)}..{max(ks)} (sum {sum(ks)}) T={T}")
     lg, l0g, fg = _compress(b, ks, T)
-    lu, _, _ = _compress(b, ks, T, Q=ulp_perturbed(b["Q"]))
+    ub, lu = _gpu_spread(b, ks, T, lg)
     devs, bad = [], []
     for run in gold["runs"]:
         p = run["p"]
         lo, l32 = run["final_loss"], run["final_loss_f32keys"]
         dev = abs(lg[p] - lo) / lo
-        spread = max(abs(l32 - lo) / lo, abs(lu[p] - lg[p]) / lg[p])
+        spread = max(abs(l32 - lo) / lo, ub[p])
         devs.append(dev)
         say(f"   p={p} k={ks[p]} init gpu={l0g[p]:.7g} oracle={run['init_loss']:.7g}; final gpu={lg[p]:.7g} "
             f"oracle={lo:.7g} (float32 keys {l32:.7g}; gpu with one-ulp queries {lu[p]:.7g}) deviation "
@@ -234,9 +249,8 @@ def test_compress_ragged_batch():
             bad.append((p, "final"))
         if not (fg[p] & ~K.KVS_FLAG_NONDESCENT == 0 and run["flags"] & ~O.FLAG_NONDESCENT == 0):
             bad.append((p, "flags"))
-    ub = np.abs(lu - lg) / lg
     say(f"   sampled deviations median {np.median(devs):.2e} max {max(devs):.2e}; batch final/init median "
-        f"{np.median(lg / l0g):.4f}, one-ulp spread over the batch median {np.median(ub):.2e} max {ub.max():.2e}, "
+        f"{np.median(lg / l0g):.4f}, GPU spread over the batch median {np.median(ub):.2e} max {ub.max():.2e}, "
         f"flagged {int(np.count_nonzero(fg))}")
     assert not bad, bad
     assert np.all(np.isfinite(lg))
