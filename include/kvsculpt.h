@@ -126,7 +126,12 @@ kvs_status kvs_init_topk(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
  * loss[p] = sum_i ||Yhat_i - Y_i||^2 + lambda * sum_i (lhat_i - lse_i)^2 with
  * Yhat = softmax(scale Q Kc^T) Vc and lhat its log-sum-exp; grad = dL/dKc
  * [sum k][d] (NULL to skip); mse[p] = ||Yhat - Y||_F^2 / (n d) (NULL to skip).
- * loss and mse are device float[P]. */
+ * loss and mse are device float[P].  The scores q.k are exact integer
+ * products of base-128 digits of the rows (scaled by powers of two), shifted
+ * by lse in float64 before rounding to float32: each carries the truncation
+ * of its inputs below 2^-35 of their row maxima (the environment variable
+ * KVS_LOGITS=fp64 or fp32, read when the context is created, selects those
+ * products instead).  The same holds for every loss forward below. */
 kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
                          const float* lse, const float* Kc, const float* Vc, float* loss,
                          float* grad, float* mse, void* ws, size_t ws_bytes);
@@ -142,9 +147,8 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
  * lse [P][n] is only used as a per-row shift of the scores (it does not
  * change A); NULL means no shift.  flags [P] (device, may be NULL) gets
  * KVS_FLAG_CHOLESKY where the factorisation failed; Vc of that problem is
- * left unchanged.  The value re-solves inside kvs_compress skip the
- * refinement step (the loss is first-order insensitive to Vc there, up to
- * a factor mu). */
+ * left unchanged.  The value re-solves inside kvs_compress take the same
+ * refinement step. */
 kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
                            const float* lse, const float* Kc, float* Vc, int32_t* flags,
                            void* ws, size_t ws_bytes);
@@ -357,7 +361,7 @@ kvs_status kvs_build_queries(kvs_ctx ctx, const kvs_query_geom* q, const float* 
  * retain zone (m >= 0; may be NULL when m == 0); Kc, Vc packed [sum k][d].
  * Ofull, Ocomp [P][n][d] are optional outputs (NULL: kept in the
  * workspace); mse [P] is required, rel [P] optional (device float).  Scores
- * are formed as for the loss (float64 products), outputs accumulate in
+ * are float64 products (float32 with KVS_LOGITS=fp32), outputs accumulate in
  * float32, the norms in float64 in a fixed order.  The workspace is
  * kvs_use_eval_workspace_bytes(b, m) bytes (0: invalid batch or m). */
 size_t kvs_use_eval_workspace_bytes(const kvs_batch* b, int32_t m);
