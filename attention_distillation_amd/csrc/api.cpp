@@ -742,8 +742,10 @@ kvs_status adam_impl(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const kvs_
     aa.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(1.0 - p2));
     launch_adam(aa, pl.kmax, ctx->stream);
     if (t % o->vc_every == 0) {
+      // scores at the moved keys for every problem, then the refined solve
       run_forward(ctx, pl, b, Q, Yr, lr, Kc, Vc, nullptr, 0, 0, nullptr, nullptr, o, ws);
-      run_value_solve(ctx, pl, b, Yr, Vc, flags, nullptr, kAllStates, ws);
+      const RefineIn rin{Q, lr, Kc};
+      run_value_solve(ctx, pl, b, Yr, Vc, flags, nullptr, kAllStates, ws, ctx->refine_resolves ? &rin : nullptr);
       fresh = true;
     }
   }

@@ -6,7 +6,7 @@
 // at once); see chol_step_kernel.  The panel solves of the rows below kpad
 // (the Y^T A rows) are the forward substitution L W = A^T Y.  The inverted
 // diagonal blocks serve the panel solves and the back substitution;
-// back_subst_kernel solves L^T X = W for 16 value columns per workgroup,
+// back_subst_lds_kernel solves L^T X = W for 16 value columns per workgroup,
 // 64-row blocks from the bottom up, every block step on MFMA.
 #include "../../include/kvsculpt.h"
 #include "kvs_internal.h"
@@ -587,98 +587,15 @@ void launch_chol_step(const CholArgs& a, int d, int j, int wgs, hipStream_t s) {
 // Solve L^T X = W for 16 value columns per workgroup, 64-row blocks from the
 // bottom up, right-looking: X_i = inv(L_ii)^T W_i, then W_r -= L_ir^T X_i for
 // every r < i.  W starts as the A^T Y rows left in M by the factorisation
-// (forward substitution) and is updated in place in the per-slab solve
-// buffer [d/16][kpad][16]; Vc rows < k are written at the end.
-template <int D>
-__global__ __launch_bounds__(256) void back_subst_kernel(BackArgs a) {
-  const int p = blockIdx.y;
-  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
-  const ProbInfo pi = a.info[p];
-  const int KT = pi.kpad / 64, ld = pi.kpad;
-  const float* __restrict__ Mp = a.M + pi.moff;
-  const int dim0 = 16 * blockIdx.x;
-  float* __restrict__ W = a.X + pi.xoff + (size_t)blockIdx.x * pi.kpad * 16;
-  const float* __restrict__ Dinv = a.Dinv + (size_t)pi.xoff / D / 64 * 64 * 64;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
-  __shared__ float Xs[64][17];
-
-  // W[row][c] = M[kpad + dim0 + c][row]
-  for (int e = tid; e < pi.kpad * 16; e += 256) {
-    const int row = e >> 4, c = e & 15;
-    W[e] = Mp[(size_t)(pi.kpad + dim0 + c) * ld + row];
-  }
-  __syncthreads();
-
-  for (int i = KT - 1; i >= 0; --i) {
-    // X_i rows b = 16 wave + (4g + r): sum_a inv(L_ii)[a][b] W_i[a][c]
-    {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* Di = Dinv + (size_t)i * 64 * 64;
-      float av[16], bv[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int arow = 4 * s + g;
-        av[s] = Di[arow * 64 + 16 * wave + lq];
-        bv[s] = W[(size_t)(64 * i + arow) * 16 + lq];
-      }
-#pragma unroll
-      for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], bv[s], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Xs[16 * wave + 4 * g + r][lq] = acc[r];
-    }
-    __syncthreads();
-    // store X_i and update W_r (r < i): block (r, wave) rows 64r + 16 wave + ..
-#pragma unroll
-    for (int r = 0; r < 4; ++r) W[(size_t)(64 * i + 16 * wave + 4 * g + r) * 16 + lq] = Xs[16 * wave + 4 * g + r][lq];
-    if (i > 0) {
-      // W_rb -= L_{i,rb}^T X_i for rb < i; wave w owns the blocks rb = w, w+4, ...
-      float bv[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) bv[s] = Xs[4 * s + g][lq];
-      for (int rb = wave; rb < i; rb += 4) {
-        float av[4][16], wv[4][4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int s = 0; s < 16; ++s)
-            av[q][s] = Mp[(size_t)(64 * i + 4 * s + g) * ld + 64 * rb + 16 * q + lq];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) wv[q][r] = W[(size_t)(64 * rb + 16 * q + 4 * g + r) * 16 + lq];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q][s], bv[s], acc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) W[(size_t)(64 * rb + 16 * q + 4 * g + r) * 16 + lq] = wv[q][r] - acc[r];
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  const bool ok = a.info_out[p] == 0;
-  if (ok) {
-    for (int e = tid; e < pi.k * 16; e += 256) {
-      const int row = e >> 4, c = e & 15;
-      float* v = a.Vc + (size_t)(pi.koff + row) * D + dim0 + c;
-      *v = a.accumulate ? *v + W[(size_t)row * 16 + c] : W[(size_t)row * 16 + c];
-    }
-  }
-  if (blockIdx.x == 0 && tid == 0 && !ok) {
-    if (a.flags) a.flags[p] |= KVS_FLAG_CHOLESKY;
-    if (a.st) a.st[p].flags |= KVS_FLAG_CHOLESKY;
-  }
-}
-
-// Same solve with the right-hand side W held in LDS ([kpad][16] floats,
-// dynamic shared memory) for the whole back substitution: only the L blocks
-// and inv(L_ii) come from global memory, and the L-block loads of a step are
+// (forward substitution); Vc rows < k are written at the end.  Eight waves:
+// four solve the diagonal block, all share the block updates.  W is held in
+// LDS ([kpad][16] floats, dynamic shared memory) while it fits (INLDS), else
+// in the per-slab solve buffer [d/16][kpad][16] in X: only the L blocks and
+// inv(L_ii) come from global memory, and the L-block loads of a step are
 // issued before its diagonal solve so their latency overlaps it.
-template <int D>
+template <int D, bool INLDS>
 __global__ __launch_bounds__(512) void back_subst_lds_kernel(BackArgs a) {
-  extern __shared__ float Wl[];          // [kpadmax][16], then Xs [64][16]
+  extern __shared__ float dyn[];         // INLDS: W [kpadmax][16], then Xs [64][16]
   const int p = blockIdx.y;
   if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
   const ProbInfo pi = a.info[p];
@@ -686,7 +603,8 @@ __global__ __launch_bounds__(512) void back_subst_lds_kernel(BackArgs a) {
   const float* __restrict__ Mp = a.M + pi.moff;
   const int dim0 = 16 * blockIdx.x;
   const float* __restrict__ Dinv = a.Dinv + (size_t)pi.xoff / D / 64 * 64 * 64;
-  float* Xs = Wl + (size_t)a.kpadmax * 16;
+  float* Wl = INLDS ? dyn : a.X + pi.xoff + (size_t)blockIdx.x * pi.kpad * 16;
+  float* Xs = INLDS ? dyn + (size_t)a.kpadmax * 16 : dyn;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
 
   // W[row][c] = M[kpad + dim0 + c][row]: coalesced float4 reads along the row
@@ -793,12 +711,13 @@ void launch_back_subst(const BackArgs& a, int d, hipStream_t s) {
   dim3 grid(d / 16, a.P);
   const size_t lds = back_subst_lds_bytes(a.kpadmax);
   if (lds <= (size_t)a.lds_max) {
-    if (d == 128) hipLaunchKernelGGL((back_subst_lds_kernel<128>), grid, dim3(512), lds, s, a);
-    else hipLaunchKernelGGL((back_subst_lds_kernel<64>), grid, dim3(512), lds, s, a);
+    if (d == 128) hipLaunchKernelGGL((back_subst_lds_kernel<128, true>), grid, dim3(512), lds, s, a);
+    else hipLaunchKernelGGL((back_subst_lds_kernel<64, true>), grid, dim3(512), lds, s, a);
     return;
   }
-  if (d == 128) hipLaunchKernelGGL((back_subst_kernel<128>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((back_subst_kernel<64>), grid, dim3(256), 0, s, a);
+  const size_t xs = 64 * 16 * sizeof(float);
+  if (d == 128) hipLaunchKernelGGL((back_subst_lds_kernel<128, false>), grid, dim3(512), xs, s, a);
+  else hipLaunchKernelGGL((back_subst_lds_kernel<64, false>), grid, dim3(512), xs, s, a);
 }
 
 }  // namespace kvs
