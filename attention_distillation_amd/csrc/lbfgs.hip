@@ -284,9 +284,12 @@ __device__ void lbfgs_scalar(LbState* st, const double* d, int mode, int H, doub
 // once.  Each sub-chunk's products are reduced across the wave and added to
 // the lane's running total (the two waves of a SIMD overlap one's loads with
 // the other's arithmetic, and the partial store and arrival are paid once per
-// chunk).  The last workgroup of the problem sums the chunk partials in a
-// fixed order and runs the scalar logic.  MS bounds the ring slots in use
-// (history + 1).
+// chunk).  The history slots and the gradient partials are read once per
+// iteration, with non-temporal loads (3.5% faster on the long-context heads,
+// the direction pass after it reading the slots 2% slower), and only the
+// Cn partials that exist.  The last workgroup of the problem sums the chunk
+// partials in a fixed order and runs the scalar logic.  MS bounds the ring
+// slots in use (history + 1).
 template <int MS>
 __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
   constexpr int E = 5 * MS + 2;            // partial entries per chunk
@@ -327,8 +330,8 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
 #pragma unroll
       for (int t = 0; t < MS; ++t) {
         const bool use = t < nslot;
-        sj[t] = use ? S[(size_t)t * stride4 + ec] : z;
-        yj[t] = use ? Yv[(size_t)t * stride4 + ec] : z;
+        sj[t] = use ? __builtin_nontemporal_load(S + (size_t)t * stride4 + ec) : z;
+        yj[t] = use ? __builtin_nontemporal_load(Yv + (size_t)t * stride4 + ec) : z;
       }
       f32x4 gv = z, sv = z, yv = z;
       if (a.grad) {
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
         const f32x4 pv = accept ? reinterpret_cast<const f32x4*>(a.pdir)[base4 + ec] : z;
         f32x4 t0[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t0[j] = dK[(size_t)(j < a.Cn ? j : 0) * stride4 + ec];
+        for (int j = 0; j < 8; ++j) t0[j] = j < a.Cn ? __builtin_nontemporal_load(dK + (size_t)j * stride4 + ec) : z;
         f32x4 gn = t0[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j)
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256) void dots_kernel(DotsArgs a) {
         for (int c0 = 8; c0 < a.Cn; c0 += 8) {
           f32x4 t[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) t[j] = dK[(size_t)(c0 + j < a.Cn ? c0 + j : 0) * stride4 + ec];
+          for (int j = 0; j < 8; ++j) t[j] = c0 + j < a.Cn ? __builtin_nontemporal_load(dK + (size_t)(c0 + j) * stride4 + ec) : z;
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             if (c0 + j < a.Cn) gn += t[j];

@@ -110,22 +110,22 @@ def mixed_fwd_peak(mode=None):
 # workloads report null.
 MEASURED_TRAFFIC = {
     # long-context default bench, the timed blocks' dispatches:
-    # loss-mode forward (integer scores): FETCH 3460285.3 KiB x 1.99980 + WRITE 18407876.8 KiB x 1.00000 per dispatch
+    # loss-mode forward (integer scores): FETCH 3382536.0 KiB x 1.99980 + WRITE 18403157.5 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
-        {"bytes": 25935609406, "source": "attn_fwd.hip", "sha": "9fd7e14b7d1af0ae"},
-    # Gram: FETCH 326243512.2 KiB x 1.99980 + WRITE 2766768.0 KiB x 1.00000 per dispatch
+        {"bytes": 25771562413, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
+    # Gram: FETCH 323944473.5 KiB x 1.99980 + WRITE 2760720.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-7b-long-context"):
-        {"bytes": 670911922871, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
+        {"bytes": 666197777536, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
     # L-BFGS vector passes and the merge of the same runs (each operand streamed once):
-    # inner products FETCH 1574932.0 KiB x 1.99980 + WRITE 383001.2 KiB, direction FETCH
-    # 1103236.5 KiB x 1.99980 + WRITE 224038.0 KiB, merge FETCH 762582.6 KiB x 1.99980 +
-    # WRITE 773309.8 KiB per dispatch
+    # inner products FETCH 1582571.8 KiB x 1.99980 + WRITE 384944.2 KiB, direction FETCH
+    # 1108513.4 KiB x 1.99980 + WRITE 224538.6 KiB, merge FETCH 762430.6 KiB x 1.99980 +
+    # WRITE 773140.1 KiB per dispatch
     ("hist_dots", "qwen2.5-7b-long-context"):
-        {"bytes": 3617325974, "source": "lbfgs.hip", "sha": "69bc1b284c639763"},
+        {"bytes": 3634960180, "source": "lbfgs.hip", "sha": "f883507a64090751"},
     ("direction", "qwen2.5-7b-long-context"):
-        {"bytes": 2488613477, "source": "lbfgs.hip", "sha": "69bc1b284c639763"},
+        {"bytes": 2499932105, "source": "lbfgs.hip", "sha": "f883507a64090751"},
     ("merge", "qwen2.5-7b-long-context"):
-        {"bytes": 2353479488, "source": "attn_fwd.hip", "sha": "9fd7e14b7d1af0ae"},
+        {"bytes": 2352994533, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
     # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
     ("build_queries", "qwen2.5-1.5b-full-cache"):
         {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
