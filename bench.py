@@ -129,9 +129,9 @@ MEASURED_TRAFFIC = {
     # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
     ("build_queries", "qwen2.5-1.5b-full-cache"):
         {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
-    # loss-mode forward (integer scores): FETCH 10107.42 KiB x 1.99980 + WRITE 47697.87 KiB x 1.00000 per dispatch
+    # loss-mode forward (integer scores): FETCH 10318.44 KiB x 1.99980 + WRITE 48582.10 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-1.5b-one-layer"):
-        {"bytes": 69540526, "source": "attn_fwd.hip", "sha": "9fd7e14b7d1af0ae"},
+        {"bytes": 70878108, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
     # standalone value solve, 128x128 Gram tiles: FETCH 2483836.3 KiB x 1.99980
     # + WRITE 134400.0 KiB x 1.00000 per dispatch
     ("gram", "qwen2.5-1.5b-full-cache solve"):
