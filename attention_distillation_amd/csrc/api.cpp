@@ -19,12 +19,12 @@ namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
   PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_DIGITS, PROF_RESID, PROF_FSUB,
-  PROF_NCLASS
+  PROF_GRAM_SPLIT, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
     "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv",
-    "key_digits", "resid_rhs", "fwd_subst"};
+    "key_digits", "resid_rhs", "fwd_subst", "gram_split"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -43,6 +43,7 @@ struct kvs_ctx_s {
   int lds_max = 0;          // dynamic LDS bytes per workgroup on this device
   int logit_mode = kvs::LOGIT_I8;   // score arithmetic of the loss forwards
   bool refine_resolves = true;      // refinement step after the schedule's value re-solves
+  bool gram_split3 = true;          // 128x128 Gram tiles on bf16 MFMA over exact three-piece splits
   bool prof = false;
   int prof_mask = 0;
   std::vector<hipEvent_t> pool;
@@ -335,13 +336,14 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   g.St = at<float>(ws, pl.r_St); g.e = at<float>(ws, pl.r_e); g.Y = Y; g.st = sel; g.active_mask = mask;
   g.Mpart = pl.Cg > 1 ? at<float>(ws, pl.r_Mg) : M; g.info = at<ProbInfo>(ws, pl.r_info);
   g.P = pl.P; g.n = pl.n; g.Cg = pl.Cg; g.kpadmax = pl.kpadmax; g.mtot = pl.mtot; g.gtot = pl.gtot;
+  g.split3 = ctx->gram_split3 ? 1 : 0;
   {
     double fl = 0, by = 0;
     for (const auto& q : pl.info) {
       fl += (double)pl.n * q.k * (q.k + 1) + 2.0 * pl.n * q.k * pl.d;
       by += 4.0 * ((double)q.k * pl.npad + (double)pl.n * pl.d + (double)(q.kpad + pl.d) * q.kpad * pl.Cg);
     }
-    Prof pr(ctx, PROF_GRAM, fl, by);
+    Prof pr(ctx, gram_split_products(g) ? PROF_GRAM_SPLIT : PROF_GRAM, fl, by);
     launch_gram(g, pl.d, ctx->stream);
   }
   GramReduceArgs r{};
@@ -777,6 +779,8 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
   }
   // the schedule's value re-solves without their refinement step, for comparisons
   if (const char* env = getenv("KVS_RESOLVE_REFINE")) c->refine_resolves = env[0] != '0';
+  // the Gram's products in fp32 MFMA instead of the split bf16 ones, for comparisons
+  if (const char* env = getenv("KVS_GRAM")) c->gram_split3 = strcmp(env, "fp32") != 0;
   // the context's device is current here: take its scratch address once
   if (hipError_t e = scratch_address(c->device, &c->scratch); e != hipSuccess) {
     c->scratch = nullptr;

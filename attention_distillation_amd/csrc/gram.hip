@@ -1,5 +1,10 @@
 // Normal equations of the ridge value solve, gfx950.
 //
+// Three kernels form them: gram_kernel (64x64 tiles, fp32 MFMA; small
+// batches), gram128_kernel (128x128 tiles, fp32 MFMA) and gram128s_kernel
+// (128x128 tiles, bf16 MFMA over exact three-piece splits of the operands;
+// the default for large batches, KVS_GRAM=fp32 selects gram128_kernel).
+//
 // The softmax weights are rebuilt from the stored shifted scores while the
 // Gram tiles are staged (the scores themselves stay untouched).
 //
@@ -9,7 +14,7 @@
 //         [ Y^T A ]   rows kpad..kpad+d-1
 // so that a Cholesky factorisation of the top block, carried through the
 // bottom rows, also performs the forward substitution L W = A^T Y.
-// Tiles are 64x64; 4 waves each compute a 32x32 quarter with 16x16x4 fp32
+// gram_kernel: 64x64 tiles; 4 waves each compute a 32x32 quarter with 16x16x4 fp32
 // MFMA, operands staged in LDS along the query (contraction) axis.  The
 // query axis can be split over gridDim.z; partial tiles are then summed in
 // a fixed order by gram_reduce_kernel, which also pads rows/columns k..kpad-1
@@ -317,15 +322,212 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats as a pair of bf16 rounded to nearest even (element 0 in the low
+// half); the two halves back as floats.
+__device__ __forceinline__ uint32_t pk_bf16(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){x0, x1}, bf16x2));
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// x = h + m + l for two floats, each piece a bf16: h = bf16(x), m = bf16(x - h),
+// l = bf16(x - h - m).  Both differences are exact in fp32 (each piece keeps
+// the leading 8 bits of what is left), so |x - h - m - l| <= 2^-24 |x| up to
+// the underflow of l.
+__device__ __forceinline__ void split3_pair(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = pk_bf16(x0, x1);
+  const float r0 = x0 - bf_lo(h), r1 = x1 - bf_hi(h);
+  m = pk_bf16(r0, r1);
+  l = pk_bf16(r0 - bf_lo(m), r1 - bf_hi(m));
+}
+
+__device__ __forceinline__ f32x4 mfma_b(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// gram128_kernel's tiles and tile order with the products on bf16 MFMA: every
+// staged operand x (a softmax weight, or an element of Y for the value rows)
+// is split into three bf16 pieces h + m + l (|x - h - m - l| <= 2^-24 |x|),
+// and a product x y is taken as the six piece products of weight at most 2,
+//     hh + hm + mh + hl + lh + mm,
+// which differ from x y by at most about 2^-22 |x y| (the dropped ml, lm, ll
+// terms and the two residuals, of either sign), the size of a few fp32
+// roundings.  Each 16x16x32 product sums 32 queries into the fp32
+// accumulator, so a 32-query step rounds the accumulator 6 times where the
+// fp32 16x16x4 products round it 8 times.  The six products take 6 x 16 = 96
+// matrix-pipe cycles per 16x16x32 block against 256 for fp32.
+// Operand strips of 32 queries (planes h, m, l of 128 rows, 20 words a row:
+// 16 bf16 pairs and 4 words of padding so that the 16-byte operand reads of
+// 16 rows fall on distinct banks).
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gram128s_kernel(GramArgs a) {
+  const unsigned L = blockIdx.x, bz = blockIdx.z;
+  const unsigned slot = L >> 3;
+  const long long f = ((long long)(slot >> 6) * 8 + (L & 7)) * 64 + (slot & 63);
+  if (f >= a.gtot) return;
+  int lo = 0, hi = a.P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.info[mid].gtoff <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  const int p = lo;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int KT = pi.kpad / 64, KT2 = (KT + 1) / 2;
+  int I2, J2;
+  if (!gram_queue_tile(f - pi.gtoff, KT2, I2, J2)) return;
+  const int n = a.n, npad = (n + 3) & ~3;
+  const int nq = ((((n + a.Cg - 1) / a.Cg) + 63) / 64) * 64;
+  const int qbeg = bz * nq, qend = min(n, qbeg + nq);
+
+  constexpr int LW = 20;
+  __shared__ __align__(16) uint32_t Rs[3][128][LW];
+  __shared__ __align__(16) uint32_t Cs[3][128][LW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+  const int wr = wave >> 2, wc = wave & 3;
+  const bool yrows = I2 >= KT2;
+  const bool diag = !yrows && I2 == J2;
+  const bool idle = (diag && wr == 0 && wc >= 2) || (yrows && 64 * wr >= D) ||
+                    (!yrows && 128 * I2 + 64 * wr >= pi.kpad) || (128 * J2 + 32 * wc >= pi.kpad);
+  const float* St = a.St + pi.soff;
+  const float* E = a.e + (size_t)p * n;
+  const float* Y = a.Y + (size_t)p * n * D;
+  const int keyR = 128 * I2, keyC = 128 * J2;
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Staging of a 32-query step: element u of a thread (i = tid + 512 u) is,
+  // for a key strip, key i / 8 and queries 4 (i % 8) .. + 3 (one 16-byte
+  // load); for the value rows, dim i % 128 and queries 4 (i / 128) .. + 3
+  // (four 4-byte loads).  Resources and range checks as in gram128_kernel.
+  const int qk4 = 4 * (tid & 7);
+  const auto rE = buf_rsrc(E, (long long)n * 4);
+  const auto rY = buf_rsrc(Y, (long long)n * D * 4);
+  const auto rR = buf_rsrc(St + (size_t)keyR * npad, (long long)min(128, pi.k - keyR) * npad * 4);
+  const auto rC = buf_rsrc(St + (size_t)keyC * npad, (long long)min(128, pi.k - keyC) * npad * 4);
+  f32x4 pr[2], pc[2], ev;
+  auto prefetch = [&](int qt) {
+    ev = buf_load4(rE, (qt + qk4) * 4);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 512 * u;
+      if (yrows) {
+        const int dim = i & 127, qy = qt + 4 * (i >> 7);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[u][j] = dim < D ? buf_load1(rY, ((qy + j) * D + dim) * 4) : 0.f;
+      } else {
+        pr[u] = buf_load4(rR, ((i >> 3) * npad + qt + qk4) * 4);
+      }
+      if (!diag) pc[u] = buf_load4(rC, ((i >> 3) * npad + qt + qk4) * 4);
+    }
+  };
+  auto weights = [&](f32x4 v, int q0) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (q0 + j < qend) ? __expf(v[j] - ev[j]) : 0.f;
+    return w;
+  };
+  // the three pieces of four consecutive queries of one row, as 8-byte stores
+  auto stage = [&](uint32_t (*S)[128][LW], int row, int q4, f32x4 v) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3_pair(v[0], v[1], h0, m0, l0);
+    split3_pair(v[2], v[3], h1, m1, l1);
+    *(u32x2*)&S[0][row][q4 / 2] = u32x2{h0, h1};
+    *(u32x2*)&S[1][row][q4 / 2] = u32x2{m0, m1};
+    *(u32x2*)&S[2][row][q4 / 2] = u32x2{l0, l1};
+  };
+  if (qbeg < qend) prefetch(qbeg);
+  for (int qt = qbeg; qt < qend; qt += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 512 * u;
+      if (yrows) {
+        const int q4 = 4 * (i >> 7);
+        f32x4 v = pr[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (qt + q4 + j >= qend) v[j] = 0.f;
+        stage(Rs, i & 127, q4, v);
+      } else {
+        stage(Rs, i >> 3, qk4, weights(pr[u], qt + qk4));
+      }
+      if (!diag) stage(Cs, i >> 3, qk4, weights(pc[u], qt + qk4));
+    }
+    __syncthreads();
+    if (qt + 32 < qend) prefetch(qt + 32);
+    if (idle) continue;
+    uint32_t (*C)[128][LW] = diag ? Rs : Cs;
+    i32x4 bv[2][3];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int s = 0; s < 3; ++s) bv[jb][s] = *(const i32x4*)&C[s][32 * wc + 16 * jb + lq][4 * g];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) {
+      i32x4 av[3];
+#pragma unroll
+      for (int s = 0; s < 3; ++s) av[s] = *(const i32x4*)&Rs[s][64 * wr + 16 * ib + lq][4 * g];
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        f32x4 c = acc[ib][jb];
+        c = mfma_b(av[1], bv[jb][1], c);   // mm
+        c = mfma_b(av[2], bv[jb][0], c);   // lh
+        c = mfma_b(av[0], bv[jb][2], c);   // hl
+        c = mfma_b(av[1], bv[jb][0], c);   // mh
+        c = mfma_b(av[0], bv[jb][1], c);   // hm
+        c = mfma_b(av[0], bv[jb][0], c);   // hh
+        acc[ib][jb] = c;
+      }
+    }
+  }
+  if (idle) return;
+
+  float* Mout = a.Mpart + (size_t)bz * a.mtot + pi.moff;
+  const int ld = pi.kpad;
+  const int row0 = yrows ? pi.kpad + 64 * wr : keyR + 64 * wr;
+  const int col0 = keyC + 32 * wc;
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * ib + 4 * g + r;
+        const int col = col0 + 16 * jb + lq;
+        Mout[(size_t)row * ld + col] = acc[ib][jb][r];
+      }
+}
+
+// 128-row tiles when the batch has enough of them to fill the chip
+static bool gram_big_tiles(const GramArgs& a) {
+  const long long KT2 = (a.kpadmax / 64 + 1) / 2;
+  const long long T2 = KT2 * (KT2 + 1) / 2 + KT2;
+  return (long long)a.P * T2 * a.Cg >= 512;
+}
+
+bool gram_split_products(const GramArgs& a) { return a.split3 && gram_big_tiles(a); }
+
 void launch_gram(const GramArgs& a, int d, hipStream_t s) {
   const long long KT = a.kpadmax / 64;
-  // 128-row tiles when the batch has enough of them to fill the chip
-  const long long KT2 = (KT + 1) / 2;
-  const long long T2 = KT2 * (KT2 + 1) / 2 + KT2;
-  if ((long long)a.P * T2 * a.Cg >= 512) {
+  if (gram_big_tiles(a)) {
     // whole rounds of 64 tiles on each of the 8 XCDs
     const long long rounds = (a.gtot + 64 * 8 - 1) / (64 * 8);
     dim3 grid2((unsigned)(rounds * 64 * 8), 1, a.Cg);
+    if (a.split3) {
+      if (d == 128) hipLaunchKernelGGL((gram128s_kernel<128>), grid2, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((gram128s_kernel<64>), grid2, dim3(512), 0, s, a);
+      return;
+    }
     if (d == 128) hipLaunchKernelGGL((gram128_kernel<128>), grid2, dim3(512), 0, s, a);
     else hipLaunchKernelGGL((gram128_kernel<64>), grid2, dim3(512), 0, s, a);
     return;

@@ -62,6 +62,7 @@ struct ProbInfo {
 enum : int { ST_READY = 0, ST_SEARCH = 1, ST_ACCEPT = 2, ST_FAIL = 3, ST_DONE = 4, ST_DONE_FAIL = 5 };
 constexpr int kAllStates = 0x3F;   // active_mask selecting every status
 constexpr int kMaxChunks = 16;     // key chunks of the split forward (merge unrolls over them)
+constexpr int kMaxRefineSplits = 16;   // query splits of the refinement residual (summed unrolled)
 
 // Per-problem optimizer state, kept in device memory between kernels.
 struct LbState {
@@ -197,8 +198,11 @@ struct GramArgs {
   const ProbInfo* info;
   int P, n, Cg, kpadmax; long long mtot;
   long long gtot;          // 128x128 tiles of all problems (flat order, see gram_queue_tile)
+  int split3;              // 128x128 tiles: products of exact three-piece bf16 splits (else fp32)
 };
 void launch_gram(const GramArgs& a, int d, hipStream_t s);
+// whether launch_gram takes the 128x128 tiles with split bf16 products
+bool gram_split_products(const GramArgs& a);
 
 // 128x128 Gram tiles of a problem with KT2 = ceil(kpad / 128) key tiles: the
 // lower triangle of key rows plus one row of value tiles (Y^T A).

@@ -161,17 +161,39 @@ __global__ __launch_bounds__(512) void fwd_subst_kernel(FsubArgs a) {
   float* Xs = INLDS ? dyn + (size_t)a.kpadmax * 16 : dyn;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
 
+  // every partial of an element is loaded before the first addition (a
+  // dependent load per partial left this prologue latency-bound at small
+  // batches); the sum keeps the split order
   const double mu = a.mu[p];
-  for (int e = tid; e < pi.kpad * 16; e += 512) {
-    const int row = e >> 4, c = e & 15;
-    float v = 0.f;
-    if (row < k) {
+  const int Cr = a.Cr;
+  constexpr int EU = 2;                 // elements per thread per round
+  for (int e0 = tid; e0 < pi.kpad * 16; e0 += EU * 512) {
+    double part[EU][kMaxRefineSplits];
+    float vc[EU];
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int e = e0 + 512 * u, row = e >> 4, c = e & 15;
+      const bool live = e < pi.kpad * 16 && row < k;
       const size_t o = pi.xoff + (size_t)row * D + dim0 + c;
-      double s = 0.0;
-      for (int cc = 0; cc < a.Cr; ++cc) s += a.Rpart[(size_t)cc * a.xtot + o];
-      v = (float)(-0.5 * s - mu * (double)a.Vc[(size_t)(pi.koff + row) * D + dim0 + c]);
+#pragma unroll
+      for (int cc = 0; cc < kMaxRefineSplits; ++cc)
+        part[u][cc] = (live && cc < Cr) ? a.Rpart[(size_t)cc * a.xtot + o] : 0.0;
+      vc[u] = live ? a.Vc[(size_t)(pi.koff + row) * D + dim0 + c] : 0.f;
     }
-    W[e] = v;
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+      const int e = e0 + 512 * u, row = e >> 4;
+      if (e >= pi.kpad * 16) break;
+      float v = 0.f;
+      if (row < k) {
+        double s = 0.0;
+#pragma unroll
+        for (int cc = 0; cc < kMaxRefineSplits; ++cc)
+          if (cc < Cr) s += part[u][cc];
+        v = (float)(-0.5 * s - mu * (double)vc[u]);
+      }
+      W[e] = v;
+    }
   }
 
   // -L_{rb,i} as A operands: rows 64 rb + 16 q + lq, columns 64 i + 16 g + s
@@ -272,7 +294,7 @@ int refine_splits(int P, int kpadmax, int n) {
   long long c = tiles > 0 ? (1024 + tiles - 1) / tiles : 1;
   c = std::max(c, (qtiles + 63) / 64);
   c = std::min(c, std::max(1LL, qtiles / 2));
-  c = std::min(c, 16LL);
+  c = std::min(c, (long long)kMaxRefineSplits);
   return (int)std::max(1LL, c);
 }
 

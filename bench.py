@@ -63,7 +63,12 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA = 157.3e12
 PEAK_FP64_MFMA = 78.6e12
 PEAK_INT8_MFMA = 5.0e15
+PEAK_BF16_MFMA = 2.5e15
 PEAK_HBM = 8.0e12
+# the Gram's 128x128 tiles: bf16 MFMA products per multiply-add (every operand
+# split exactly into three bf16 pieces, the six piece products of weight <= 2)
+GRAM_SPLIT_PRODUCTS = 6
+PEAK_GRAM_SPLIT = PEAK_BF16_MFMA / GRAM_SPLIT_PRODUCTS
 # the integer scores of the loss forward: digit products per score (five
 # base-128 digits per element, the pairs of weight s + t <= 5)
 INT8_PRODUCTS = 19
@@ -113,9 +118,9 @@ MEASURED_TRAFFIC = {
     # loss-mode forward (integer scores): FETCH 3382536.0 KiB x 1.99980 + WRITE 18403157.5 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
         {"bytes": 25771562413, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
-    # Gram: FETCH 323944473.5 KiB x 1.99980 + WRITE 2760720.0 KiB x 1.00000 per dispatch
-    ("gram", "qwen2.5-7b-long-context"):
-        {"bytes": 666197777536, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
+    # Gram, 128x128 tiles on split bf16 products: FETCH 329460930.9 KiB x 1.99980 + WRITE 2765168.1 KiB x 1.00000 per dispatch
+    ("gram_split", "qwen2.5-7b-long-context"):
+        {"bytes": 677500045019, "source": "gram.hip", "sha": "cae0c7dcc2b67ff1"},
     # L-BFGS vector passes and the merge of the same runs (each operand streamed once):
     # inner products FETCH 1582571.8 KiB x 1.99980 + WRITE 384944.2 KiB, direction FETCH
     # 1108513.4 KiB x 1.99980 + WRITE 224538.6 KiB, merge FETCH 762430.6 KiB x 1.99980 +
@@ -132,10 +137,6 @@ MEASURED_TRAFFIC = {
     # loss-mode forward (integer scores): FETCH 10318.44 KiB x 1.99980 + WRITE 48582.10 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-1.5b-one-layer"):
         {"bytes": 70878108, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
-    # standalone value solve, 128x128 Gram tiles: FETCH 2483836.3 KiB x 1.99980
-    # + WRITE 134400.0 KiB x 1.00000 per dispatch
-    ("gram", "qwen2.5-1.5b-full-cache solve"):
-        {"bytes": 5224009779, "source": "gram.hip", "sha": "7ca50c814bf02aac"},
 }
 
 
@@ -393,13 +394,17 @@ def bench_solve(args, torch, K):
         step()
     torch.cuda.synchronize()
     elapsed = timed_pass(torch, step, args.steps)
-    st = event_pass(torch, K, ctx, ["gram"], step, args.steps)["gram"]
+    ev = event_pass(torch, K, ctx, ["gram", "gram_split"], step, args.steps)
+    gname = gram_kernel_of(ev)
+    st = ev[gname]
     avg_s = st["ms"] / st["launches"] / 1e3
     achieved = st["flops"] / st["launches"] / avg_s
+    peak, peak_note = contraction_peak(gname)
     roofline = {"bound": "mfma", "achieved": round(achieved / 1e12, 3),
-                "peak": round(PEAK_FP32_MFMA / 1e12, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": traffic_for("gram", w.name + " solve"),
-                "kernel": "gram", "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
+                "peak": round(peak / 1e12, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "frac_fp32_mfma": round(achieved / PEAK_FP32_MFMA, 4),
+                "traffic": traffic_for(gname, w.name + " solve"), "kernel": gname, "peak_kind": peak_note,
+                "launches": st["launches"], "avg_us": round(avg_s * 1e6, 2)}
     log(f"[bench] flags {int(flags.ne(0).sum().item())} of {P} problems set")
     cpu = None
     if not args.no_cpu_baseline:
@@ -746,12 +751,28 @@ def bench_vector(args, torch, K):
 
 
 # kernels whose launches are timed with HIP events during the timed blocks
-TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "attn_pv", "potrf_panel", "back_subst", "merge",
-                 "hist_dots", "direction", "key_digits", "resid_rhs", "fwd_subst"]
+TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "potrf_panel", "back_subst",
+                 "merge", "hist_dots", "direction", "key_digits", "resid_rhs", "fwd_subst"]
 # contraction kernels (MFMA roofline) and their peaks: the loss forward forms
-# its scores on fp64 MFMA (half its flops) and A Vc on fp32 MFMA (the other
-# half); the others are fp32 MFMA only
-CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "attn_pv", "resid_rhs")
+# its scores on the score arithmetic's unit (half its flops) and A Vc on fp32
+# MFMA (the other half); the split-product Gram runs on bf16 MFMA, six
+# products per multiply-add; the others are fp32 MFMA only
+CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "resid_rhs")
+
+
+def gram_kernel_of(stats):
+    """The Gram's profile name in these stats: the split-product kernel when
+    its launches ran (large batches), else the fp32 one."""
+    return "gram_split" if stats.get("gram_split", {}).get("launches", 0) else "gram"
+
+
+def contraction_peak(name):
+    """(peak flop rate, description) of a contraction kernel other than the
+    loss forward."""
+    if name == "gram_split":
+        return PEAK_GRAM_SPLIT, (f"bf16 MFMA over {GRAM_SPLIT_PRODUCTS} products per multiply-add "
+                                 f"(exact three-piece bf16 splits of both operands)")
+    return PEAK_FP32_MFMA, "fp32 MFMA"
 
 
 def kernel_rows(stats):
@@ -776,9 +797,18 @@ def kernel_rows(stats):
                 # the algorithmic rate against the fp32 MFMA peak
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
             else:
+                if name == "gram_split":
+                    row["frac_split_bf16_mfma"] = round(fl / sec / PEAK_GRAM_SPLIT, 4)
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
         rows[name] = row
     return rows
+
+
+def contractions_note(stats):
+    if gram_kernel_of(stats) == "gram_split":
+        return (f"fp32 MFMA; the Gram's 128x128 tiles on bf16 MFMA over exact three-piece bf16 splits "
+                f"({GRAM_SPLIT_PRODUCTS} products per multiply-add, fp32 accumulation)")
+    return "fp32 MFMA"
 
 
 def cpu_baseline_block(w, b):
@@ -929,8 +959,7 @@ def bench_compress(args, torch, K):
                      "int8": f"harmonic mix of the int8 MFMA peak over {INT8_PRODUCTS} digit products "
                              f"(scores) and the fp32 MFMA peak (A Vc)"}[logit_mode()]
     else:
-        peak = PEAK_FP32_MFMA
-        peak_note = "fp32 MFMA"
+        peak, peak_note = contraction_peak(name)
     tot_ms = sum(r["ms"] for r in rows.values())
     for k2, r in sorted(rows.items(), key=lambda kv: -kv[1]["ms"]):
         log(f"[bench] {k2:12s} launches={r['launches']:6d} ms={r['ms']:10.2f} avg_us={r['avg_us']:9.1f} "
@@ -972,7 +1001,7 @@ def bench_compress(args, torch, K):
                    "iters": T, "vc_every": VC, "history": 10, "pilot": pilot,
                    "step": f"one block of {VC} L-BFGS iterations of all {P} problems with the value "
                            f"re-solve and loss/gradient after it (main run at the pilot's ragged k)",
-                   "logits": LOGIT_NOTES[logit_mode()], "contractions": "fp32 MFMA"},
+                   "logits": LOGIT_NOTES[logit_mode()], "contractions": contractions_note(stats)},
         "latency": {"whole_model_compress_s": round(t_latency, 3), "pilot_and_allocation_s": round(t_pilot, 3),
                     "reference_and_select_fit_s": round(t_begin, 3),
                     "note": f"pilot ({pilot} iterations at k0) + reallocation + reference attention + "

@@ -381,7 +381,9 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
  * merge, build_queries, use_attn_fwd, attn_pv (bit 13: the forward that
  * reads stored scores after a value re-solve), key_digits (bit 14: the digit
  * planes of the keys for the integer score products), resid_rhs and
- * fwd_subst (bits 15, 16: the refinement step of a value solve).
+ * fwd_subst (bits 15, 16: the refinement step of a value solve) and
+ * gram_split (bit 17: the Gram's launches whose 128x128 tiles take the
+ * products of exact three-piece bf16 splits; "gram" counts the fp32 ones).
  * kvs_profile_read
  * synchronises the stream and writes up to max entries (kernels with
  * launches) to out. */

@@ -120,3 +120,52 @@ def test_value_solve_flags_nonfinite_keys_and_keeps_vc():
     assert np.all(Vg[20:] == 7.0)
     V0, _, _ = O.ridge_values(b["Q"][0], probs[0][1], probs[0][3], b["scale"])
     assert row_err(Vg[:20], V0) <= TOL
+
+
+def test_split_gram_and_fp32_gram_both_match_oracle():
+    """The 128x128 Gram tiles take the split bf16 products by default and the
+    fp32 ones under KVS_GRAM=fp32 (read when a context is created): both
+    solves meet the bar, and the profile shows which kernel ran."""
+    import os
+    w, kfun, _, sel = CASES["full-cache-12-ragged"]
+    b, probs = _setup(w, kfun, 0.0, problems=sel)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    ks = [pr[3].shape[0] for pr in probs]
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    Qg, Yg = to_gpu(b["Q"]), to_gpu(np.stack([p[1] for p in probs]))
+    lg, Kg = to_gpu(np.stack([p[2] for p in probs])), to_gpu(np.concatenate([p[3] for p in probs]))
+    out = {}
+    for mode in ("split", "fp32"):
+        old = os.environ.pop("KVS_GRAM", None)
+        if mode == "fp32":
+            os.environ["KVS_GRAM"] = "fp32"
+        try:
+            ctx = K.Context()
+        finally:
+            os.environ.pop("KVS_GRAM", None)
+            if old is not None:
+                os.environ["KVS_GRAM"] = old
+        ws = workspace(K.workspace_bytes(bt))
+        Vc = empty((sum(ks), d))
+        flags = to_gpu(np.zeros(P, np.int32))
+        K.kvs_profile_enable(ctx, True, kernels=["gram", "gram_split"])
+        K.kvs_value_solve(ctx, bt, Qg, Yg, lg, Kg, Vc, flags, ws)
+        st = K.kvs_profile_read(ctx)
+        K.kvs_profile_enable(ctx, False)
+        ran = {k2: v["launches"] for k2, v in st.items()}
+        say(f"[split-gram] mode={mode} gram launches {ran}")
+        assert ran == ({"gram_split": 1} if mode == "split" else {"gram": 1})
+        out[mode] = (host(Vc), host(flags))
+    off, worst = 0, {"split": 0.0, "fp32": 0.0}
+    for p, (Q, Y32, l32, Kc) in enumerate(probs):
+        k = Kc.shape[0]
+        V, mu, ok = O.ridge_values(Q, Y32, Kc, b["scale"])
+        for mode, (Vg, fg) in out.items():
+            assert ok and fg[p] == 0
+            worst[mode] = max(worst[mode], row_err(Vg[off:off + k], V))
+        off += k
+    mutual = row_err(out["split"][0], out["fp32"][0])
+    say(f"   worst row error vs the oracle: split {worst['split']:.2e} fp32 {worst['fp32']:.2e}; "
+        f"split vs fp32 {mutual:.2e}")
+    assert worst["split"] <= TOL and worst["fp32"] <= TOL
