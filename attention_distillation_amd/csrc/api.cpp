@@ -43,7 +43,8 @@ struct kvs_ctx_s {
   int lds_max = 0;          // dynamic LDS bytes per workgroup on this device
   int logit_mode = kvs::LOGIT_I8;   // score arithmetic of the loss forwards
   bool refine_resolves = true;      // refinement step after the schedule's value re-solves
-  bool gram_split3 = true;          // 128x128 Gram tiles on bf16 MFMA over exact three-piece splits
+  bool gram_split3 = true;          // large-batch Gram tiles on bf16 MFMA over exact three-piece splits
+  int gram_tile256 = 1;             // those tiles 256x256: 0 never, 1 for >= 2048 of them, 2 always
   bool prof = false;
   int prof_mask = 0;
   std::vector<hipEvent_t> pool;
@@ -336,7 +337,9 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   g.St = at<float>(ws, pl.r_St); g.e = at<float>(ws, pl.r_e); g.Y = Y; g.st = sel; g.active_mask = mask;
   g.Mpart = pl.Cg > 1 ? at<float>(ws, pl.r_Mg) : M; g.info = at<ProbInfo>(ws, pl.r_info);
   g.P = pl.P; g.n = pl.n; g.Cg = pl.Cg; g.kpadmax = pl.kpadmax; g.mtot = pl.mtot; g.gtot = pl.gtot;
+  g.gtot4 = pl.gtot4;
   g.split3 = ctx->gram_split3 ? 1 : 0;
+  g.tile256 = ctx->gram_tile256;
   {
     double fl = 0, by = 0;
     for (const auto& q : pl.info) {
@@ -779,8 +782,15 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
   }
   // the schedule's value re-solves without their refinement step, for comparisons
   if (const char* env = getenv("KVS_RESOLVE_REFINE")) c->refine_resolves = env[0] != '0';
-  // the Gram's products in fp32 MFMA instead of the split bf16 ones, for comparisons
-  if (const char* env = getenv("KVS_GRAM")) c->gram_split3 = strcmp(env, "fp32") != 0;
+  // the Gram's large-batch kernel, for comparisons: KVS_GRAM=fp32 (128x128
+  // tiles, fp32 products), split128 or split256 (split bf16 products on
+  // 128x128 or 256x256 tiles); the default takes the split products on
+  // 256x256 tiles when a batch has at least 2048 of them, else on 128x128
+  if (const char* env = getenv("KVS_GRAM")) {
+    if (!strcmp(env, "fp32")) c->gram_split3 = false;
+    else if (!strcmp(env, "split128")) c->gram_tile256 = 0;
+    else if (!strcmp(env, "split256")) c->gram_tile256 = 2;
+  }
   // the context's device is current here: take its scratch address once
   if (hipError_t e = scratch_address(c->device, &c->scratch); e != hipSuccess) {
     c->scratch = nullptr;

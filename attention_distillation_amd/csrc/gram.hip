@@ -508,6 +508,180 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       }
 }
 
+// gram128s_kernel's products on 256x256 tiles: a tile sweeps two 256-key
+// strips, so each staged score feeds 256 outputs instead of 128 and the
+// strips are read half as often per flop.  One workgroup of eight waves per
+// CU (the two split strips take 120 KB of LDS); wave (wr, wc) owns rows
+// 64 wr .. + 63 and columns 128 wc .. + 127 of the tile as two 64-column
+// halves (4 x 4 blocks of 16x16 each).  A half is skipped when it lies past
+// kpad or strictly above the diagonal (64-tile granularity, as the 64-tile
+// layout of M stores); the value tile (Y^T A, d rows) leaves the waves of
+// rows past d idle.  Tiles are dealt to the XCDs in rounds of 32 (one per CU).
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gram256s_kernel(GramArgs a) {
+  const unsigned L = blockIdx.x, bz = blockIdx.z;
+  const unsigned slot = L >> 3;
+  const long long f = ((long long)(slot >> 5) * 8 + (L & 7)) * 32 + (slot & 31);
+  if (f >= a.gtot4) return;
+  int lo = 0, hi = a.P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.info[mid].gtoff4 <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  const int p = lo;
+  if (a.st && !((1 << a.st[p].status) & a.active_mask)) return;
+  const ProbInfo pi = a.info[p];
+  const int KT = pi.kpad / 64, KT4 = (KT + 3) / 4;
+  int I4, J4;
+  if (!gram_queue_tile(f - pi.gtoff4, KT4, I4, J4)) return;
+  const int n = a.n, npad = (n + 3) & ~3;
+  const int nq = ((((n + a.Cg - 1) / a.Cg) + 63) / 64) * 64;
+  const int qbeg = bz * nq, qend = min(n, qbeg + nq);
+
+  constexpr int LW = 20;
+  __shared__ __align__(16) uint32_t Rs[3][256][LW];
+  __shared__ __align__(16) uint32_t Cs[3][256][LW];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+  const int wr = wave >> 1, wc = wave & 1;
+  const bool yrows = I4 >= KT4;
+  const bool diag = !yrows && I4 == J4;
+  const int keyR = 256 * I4, keyC = 256 * J4;
+  // 64-tile row and column of the wave's halves
+  const int trow = 4 * I4 + wr;
+  const bool rows_live = yrows ? 64 * wr < D : 64 * trow < pi.kpad;
+  bool live[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tcol = 4 * J4 + 2 * wc + h;
+    live[h] = rows_live && 64 * tcol < pi.kpad && !(diag && tcol > trow);
+  }
+  const bool idle = !live[0] && !live[1];
+  const float* St = a.St + pi.soff;
+  const float* E = a.e + (size_t)p * n;
+  const float* Y = a.Y + (size_t)p * n * D;
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Staging of a 32-query step: element u of a thread (i = tid + 512 u) is,
+  // for a key strip, key i / 8 and queries 4 (i % 8) .. + 3 (one 16-byte
+  // load); for the value rows (u < 2 only), dim i % 128 and queries
+  // 4 (i / 128) .. + 3 (four 4-byte loads).
+  const int qk4 = 4 * (tid & 7);
+  const auto rE = buf_rsrc(E, (long long)n * 4);
+  const auto rY = buf_rsrc(Y, (long long)n * D * 4);
+  const auto rR = buf_rsrc(St + (size_t)keyR * npad, (long long)min(256, pi.k - keyR) * npad * 4);
+  const auto rC = buf_rsrc(St + (size_t)keyC * npad, (long long)min(256, pi.k - keyC) * npad * 4);
+  f32x4 pr[4], pc[4], ev;
+  auto prefetch = [&](int qt) {
+    ev = buf_load4(rE, (qt + qk4) * 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 512 * u;
+      if (yrows) {
+        if (u < 2) {
+          const int dim = i & 127, qy = qt + 4 * (i >> 7);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pr[u][j] = dim < D ? buf_load1(rY, ((qy + j) * D + dim) * 4) : 0.f;
+        }
+      } else {
+        pr[u] = buf_load4(rR, ((i >> 3) * npad + qt + qk4) * 4);
+      }
+      if (!diag) pc[u] = buf_load4(rC, ((i >> 3) * npad + qt + qk4) * 4);
+    }
+  };
+  auto weights = [&](f32x4 v, int q0) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (q0 + j < qend) ? __expf(v[j] - ev[j]) : 0.f;
+    return w;
+  };
+  auto stage = [&](uint32_t (*S)[256][LW], int row, int q4, f32x4 v) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3_pair(v[0], v[1], h0, m0, l0);
+    split3_pair(v[2], v[3], h1, m1, l1);
+    *(u32x2*)&S[0][row][q4 / 2] = u32x2{h0, h1};
+    *(u32x2*)&S[1][row][q4 / 2] = u32x2{m0, m1};
+    *(u32x2*)&S[2][row][q4 / 2] = u32x2{l0, l1};
+  };
+  if (qbeg < qend) prefetch(qbeg);
+  for (int qt = qbeg; qt < qend; qt += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 512 * u;
+      if (yrows) {
+        if (u < 2) {
+          const int q4 = 4 * (i >> 7);
+          f32x4 v = pr[u];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (qt + q4 + j >= qend) v[j] = 0.f;
+          stage(Rs, i & 127, q4, v);
+        }
+      } else {
+        stage(Rs, i >> 3, qk4, weights(pr[u], qt + qk4));
+      }
+      if (!diag) stage(Cs, i >> 3, qk4, weights(pc[u], qt + qk4));
+    }
+    __syncthreads();
+    if (qt + 32 < qend) prefetch(qt + 32);
+    if (idle) continue;
+    uint32_t (*C)[256][LW] = diag ? Rs : Cs;
+    i32x4 av[4][3];
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int s = 0; s < 3; ++s) av[ib][s] = *(const i32x4*)&Rs[s][64 * wr + 16 * ib + lq][4 * g];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (!live[h]) continue;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int jb = 4 * h + j4;
+        i32x4 bv[3];
+#pragma unroll
+        for (int s = 0; s < 3; ++s) bv[s] = *(const i32x4*)&C[s][128 * wc + 16 * jb + lq][4 * g];
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+          f32x4 c = acc[ib][jb];
+          c = mfma_b(av[ib][1], bv[1], c);   // mm
+          c = mfma_b(av[ib][2], bv[0], c);   // lh
+          c = mfma_b(av[ib][0], bv[2], c);   // hl
+          c = mfma_b(av[ib][1], bv[0], c);   // mh
+          c = mfma_b(av[ib][0], bv[1], c);   // hm
+          c = mfma_b(av[ib][0], bv[0], c);   // hh
+          acc[ib][jb] = c;
+        }
+      }
+    }
+  }
+  if (idle) return;
+
+  float* Mout = a.Mpart + (size_t)bz * a.mtot + pi.moff;
+  const int ld = pi.kpad;
+  const int row0 = yrows ? pi.kpad + 64 * wr : keyR + 64 * wr;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (!live[h]) continue;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jb = 4 * h + j4;
+          const int row = row0 + 16 * ib + 4 * g + r;
+          const int col = keyC + 128 * wc + 16 * jb + lq;
+          Mout[(size_t)row * ld + col] = acc[ib][jb][r];
+        }
+  }
+}
+
 // 128-row tiles when the batch has enough of them to fill the chip
 static bool gram_big_tiles(const GramArgs& a) {
   const long long KT2 = (a.kpadmax / 64 + 1) / 2;
@@ -519,6 +693,19 @@ bool gram_split_products(const GramArgs& a) { return a.split3 && gram_big_tiles(
 
 void launch_gram(const GramArgs& a, int d, hipStream_t s) {
   const long long KT = a.kpadmax / 64;
+  // 256x256 tiles when there are at least eight per CU (one workgroup per
+  // CU: with fewer, the 128x128 tiles' two workgroups per CU hide more; the
+  // full cache at k = 960 has three); n <= 2^20 keeps the lane offsets of a
+  // 256-row strip below 2^31 bytes
+  const bool t256 = a.tile256 == 2 || (a.tile256 == 1 && a.gtot4 * a.Cg >= 2048);
+  if (gram_big_tiles(a) && a.split3 && t256 && a.n <= (1 << 20)) {
+    // whole rounds of 32 tiles on each of the 8 XCDs
+    const long long rounds = (a.gtot4 + 32 * 8 - 1) / (32 * 8);
+    dim3 grid4((unsigned)(rounds * 32 * 8), 1, a.Cg);
+    if (d == 128) hipLaunchKernelGGL((gram256s_kernel<128>), grid4, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((gram256s_kernel<64>), grid4, dim3(512), 0, s, a);
+    return;
+  }
   if (gram_big_tiles(a)) {
     // whole rounds of 64 tiles on each of the 8 XCDs
     const long long rounds = (a.gtot + 64 * 8 - 1) / (64 * 8);

@@ -54,6 +54,7 @@ struct ProbInfo {
   long long xoff;   // offset (floats) of the problem's padded solve rows [kpad][d]
   int gtoff;        // first tile of the problem in the flat order of the 128x128 Gram tiles
   int korder;       // problem that the forwards run at grid row p (largest k first)
+  int gtoff4;       // first tile of the problem in the flat order of the 256x256 Gram tiles
 };
 
 // L-BFGS / line-search status of one problem.
@@ -198,7 +199,9 @@ struct GramArgs {
   const ProbInfo* info;
   int P, n, Cg, kpadmax; long long mtot;
   long long gtot;          // 128x128 tiles of all problems (flat order, see gram_queue_tile)
-  int split3;              // 128x128 tiles: products of exact three-piece bf16 splits (else fp32)
+  long long gtot4;         // 256x256 tiles of all problems (same order over 256-key tiles)
+  int split3;              // products of exact three-piece bf16 splits (else fp32)
+  int tile256;             // split products on 256x256 tiles: 0 never, 1 with >= 2048 of them, 2 always
 };
 void launch_gram(const GramArgs& a, int d, hipStream_t s);
 // whether launch_gram takes the 128x128 tiles with split bf16 products

@@ -56,7 +56,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   p = Plan();
   p.P = b->P; p.d = b->d; p.Z = b->Z; p.n = b->n; p.npad = (b->n + 3) & ~3; p.H = H;
   p.info.resize(p.P);
-  long long koff = 0, soff = 0, moff = 0, xoff = 0, gtoff = 0;
+  long long koff = 0, soff = 0, moff = 0, xoff = 0, gtoff = 0, gtoff4 = 0;
   for (int i = 0; i < p.P; ++i) {
     int k = b->k ? b->k[i] : b->Z;
     if (k < 1 || k > b->Z) return "k[p] must be in [1, Z]";
@@ -69,8 +69,10 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
     q.moff = moff;
     q.xoff = xoff;
     q.gtoff = (int)gtoff;
+    q.gtoff4 = (int)gtoff4;
     q.korder = i;
     gtoff += gram128_tiles((q.kpad / kTile + 1) / 2);
+    gtoff4 += gram128_tiles((q.kpad / kTile + 3) / 4);
     koff += k;
     soff += (long long)k * p.npad;
     moff += (long long)(q.kpad + p.d) * q.kpad;
@@ -81,6 +83,7 @@ std::string make_plan(const kvs_batch* b, const kvs_opts* o, Plan* pl) {
   if (koff > 0x7fffffffLL) return "sum of k too large";
   if (gtoff > 0x7fffffffLL / 2) return "too many Gram tiles";
   p.gtot = gtoff;
+  p.gtot4 = gtoff4;
   // Slot order for kernels that keep each problem's workgroups on one XCD
   // (a contiguous range of logical slots per XCD): problems by k, largest
   // first, dealt to the 8 XCDs in snake order, so every XCD gets about the

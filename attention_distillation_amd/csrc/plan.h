@@ -16,6 +16,7 @@ struct Plan {
   int P = 0, d = 0, Z = 0, n = 0, npad = 0, kmax = 0, kpadmax = 0, H = 10;
   long long ktot = 0, kpadtot = 0, mtot = 0, stot = 0;
   long long gtot = 0;          // 128x128 Gram tiles of all problems
+  long long gtot4 = 0;         // 256x256 Gram tiles of all problems
   int Cref = 1, C = 1, Cn = 1, Cg = 1, Cq = 1, Crf = 1, nblk = 1, nchv = 1, nchd = 1;
   std::vector<ProbInfo> info;
   std::vector<int> chol_wgs;   // workgroups of Cholesky launch j = -1 .. kpadmax/64 - 1 (index j + 1)

@@ -115,28 +115,32 @@ def mixed_fwd_peak(mode=None):
 # workloads report null.
 MEASURED_TRAFFIC = {
     # long-context default bench, the timed blocks' dispatches:
-    # loss-mode forward (integer scores): FETCH 3382536.0 KiB x 1.99980 + WRITE 18403157.5 KiB x 1.00000 per dispatch
+    # loss-mode forward (integer scores): FETCH 3393086.5 KiB x 1.99980 + WRITE 18157940.8 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
-        {"bytes": 25771562413, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
-    # Gram, 128x128 tiles on split bf16 products: FETCH 329460930.9 KiB x 1.99980 + WRITE 2765168.1 KiB x 1.00000 per dispatch
+        {"bytes": 25542077627, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
+    # Gram, 256x256 tiles on split bf16 products: FETCH 141733727.5 KiB x 1.99980 + WRITE 2765207.7 KiB x 1.00000 per dispatch
     ("gram_split", "qwen2.5-7b-long-context"):
-        {"bytes": 677500045019, "source": "gram.hip", "sha": "cae0c7dcc2b67ff1"},
+        {"bytes": 293073219537, "source": "gram.hip", "sha": "8175c6117de39252"},
     # L-BFGS vector passes and the merge of the same runs (each operand streamed once):
-    # inner products FETCH 1582571.8 KiB x 1.99980 + WRITE 384944.2 KiB, direction FETCH
-    # 1108513.4 KiB x 1.99980 + WRITE 224538.6 KiB, merge FETCH 762430.6 KiB x 1.99980 +
-    # WRITE 773140.1 KiB per dispatch
+    # inner products FETCH 1552134.5 KiB x 1.99980 + WRITE 377476.8 KiB, direction FETCH
+    # 1085940.2 KiB x 1.99980 + WRITE 220762.4 KiB, merge FETCH 754083.2 KiB x 1.99980 +
+    # WRITE 764748.1 KiB per dispatch
     ("hist_dots", "qwen2.5-7b-long-context"):
-        {"bytes": 3634960180, "source": "lbfgs.hip", "sha": "f883507a64090751"},
+        {"bytes": 3564989822, "source": "lbfgs.hip", "sha": "f883507a64090751"},
     ("direction", "qwen2.5-7b-long-context"):
-        {"bytes": 2499932105, "source": "lbfgs.hip", "sha": "f883507a64090751"},
+        {"bytes": 2449843827, "source": "lbfgs.hip", "sha": "f883507a64090751"},
     ("merge", "qwen2.5-7b-long-context"):
-        {"bytes": 2352994533, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
+        {"bytes": 2327310012, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
     # training queries: FETCH 53517.7 KiB x 1.99978 + WRITE 107520.0 KiB x 1.00000 per dispatch
     ("build_queries", "qwen2.5-1.5b-full-cache"):
         {"bytes": 219692476, "source": "queries.hip", "sha": "b2221c837c63d711"},
     # loss-mode forward (integer scores): FETCH 10318.44 KiB x 1.99980 + WRITE 48582.10 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-1.5b-one-layer"):
         {"bytes": 70878108, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
+    # standalone value solve, 128x128 Gram tiles on split bf16 products:
+    # FETCH 2628652.75 KiB x 1.99980 + WRITE 134400.0 KiB x 1.00000 per dispatch
+    ("gram_split", "qwen2.5-1.5b-full-cache solve"):
+        {"bytes": 5520568084, "source": "gram.hip", "sha": "8175c6117de39252"},
 }
 
 

@@ -148,7 +148,13 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
  * change A); NULL means no shift.  flags [P] (device, may be NULL) gets
  * KVS_FLAG_CHOLESKY where the factorisation failed; Vc of that problem is
  * left unchanged.  The value re-solves inside kvs_compress take the same
- * refinement step. */
+ * refinement step.  On batches with enough Gram tiles (at least 512 of
+ * 128x128) each product of A^T A and Y^T A is taken as six bf16 products
+ * of exact three-piece splits of both operands (h = bf16(x),
+ * m = bf16(x - h), l = bf16(x - h - m); the terms of weight <= 2), within
+ * about 2^-22 of the product, with fp32 accumulation; KVS_GRAM=fp32, read
+ * when the context is created, selects fp32 products instead (split128 /
+ * split256 force a tile shape). */
 kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
                            const float* lse, const float* Kc, float* Vc, int32_t* flags,
                            void* ws, size_t ws_bytes);
@@ -382,8 +388,9 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
  * reads stored scores after a value re-solve), key_digits (bit 14: the digit
  * planes of the keys for the integer score products), resid_rhs and
  * fwd_subst (bits 15, 16: the refinement step of a value solve) and
- * gram_split (bit 17: the Gram's launches whose 128x128 tiles take the
- * products of exact three-piece bf16 splits; "gram" counts the fp32 ones).
+ * gram_split (bit 17: the Gram's launches whose 128x128 or 256x256 tiles
+ * take the products of exact three-piece bf16 splits; "gram" counts the
+ * fp32 ones).
  * kvs_profile_read
  * synchronises the stream and writes up to max entries (kernels with
  * launches) to out. */

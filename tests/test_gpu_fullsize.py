@@ -134,7 +134,11 @@ def test_degenerate_shapes_match_oracle():
         assert worst <= TOL
 
 
-TOPK_FULL = {"llama3-8b-p0": (WORKLOADS[3], 0), "qwen2.5-7b-long-p0": (WORKLOADS[4], 0)}
+# the first and the last head of each cache: the last long-context head has
+# its own heavy-tailed keys and outlier channels (importance scores with the
+# widest range)
+TOPK_FULL = {"llama3-8b-p0": (WORKLOADS[3], 0), "llama3-8b-p255": (WORKLOADS[3], 255),
+             "qwen2.5-7b-long-p0": (WORKLOADS[4], 0), "qwen2.5-7b-long-p111": (WORKLOADS[4], 111)}
 
 
 @pytest.mark.parametrize("name", list(TOPK_FULL))
