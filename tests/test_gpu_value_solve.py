@@ -122,14 +122,26 @@ def test_value_solve_flags_nonfinite_keys_and_keeps_vc():
     assert row_err(Vg[:20], V0) <= TOL
 
 
-def test_split_gram_and_fp32_gram_both_match_oracle():
+# batches with enough 128x128 Gram tiles for the large-batch kernels: the
+# ragged full-cache heads (d = 128) and twelve d = 64 heads at k = 960 from
+# 1040 training queries each, whose value tiles leave the waves of rows past
+# d idle
+SPLIT_CASES = {
+    "full-cache-12-ragged-d128": CASES["full-cache-12-ragged"],
+    "small-12-d64-k960": (tiny_workload(d=64, N=1000, m=40, g=1, F=1000, layers=6, kv_heads=2),
+                          lambda p, Z: 960, 0.0, None),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_gram_and_fp32_gram_both_match_oracle(name):
     """The large-batch Gram takes split bf16 products (on 128x128 or 256x256
     tiles) by default and fp32 ones under KVS_GRAM=fp32 (read when a context
     is created).  Every variant meets the bar; the two split tile shapes sum
     the same products in the same order, so their solves agree bit for bit;
     the profile shows which product kind ran."""
     import os
-    w, kfun, _, sel = CASES["full-cache-12-ragged"]
+    w, kfun, _, sel = SPLIT_CASES[name]
     b, probs = _setup(w, kfun, 0.0, problems=sel)
     P, n, d = b["Q"].shape
     Z = b["Kz"].shape[1]
@@ -155,7 +167,7 @@ def test_split_gram_and_fp32_gram_both_match_oracle():
         st = K.kvs_profile_read(ctx)
         K.kvs_profile_enable(ctx, False)
         ran = {k2: v["launches"] for k2, v in st.items()}
-        say(f"[split-gram] mode={mode} gram launches {ran}")
+        say(f"[split-gram] case={name} P={P} d={d} k={ks[0]}.. mode={mode} gram launches {ran}")
         assert ran == ({"gram": 1} if mode == "fp32" else {"gram_split": 1})
         out[mode] = (host(Vc), host(flags))
     assert out["split128"][0].tobytes() == out["split256"][0].tobytes()
