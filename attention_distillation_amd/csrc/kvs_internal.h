@@ -204,7 +204,8 @@ struct GramArgs {
   int tile256;             // split products on 256x256 tiles: 0 never, 1 with >= 2048 of them, 2 always
 };
 void launch_gram(const GramArgs& a, int d, hipStream_t s);
-// whether launch_gram takes the 128x128 tiles with split bf16 products
+// whether launch_gram takes its large-batch tiles (128x128 or 256x256) with
+// the split bf16 products
 bool gram_split_products(const GramArgs& a);
 
 // 128x128 Gram tiles of a problem with KT2 = ceil(kpad / 128) key tiles: the
