@@ -1054,8 +1054,8 @@ def main():
     if args.warmup is None:
         args.warmup = 5 if args.row == "compress" else 1
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        log("bench.py measures one GPU: the problems of a batch are independent and this build "
-            "runs them all on a single MI355X; multi-GPU runs are not part of it (--gpus 1).")
+        log("bench.py measures one GPU: the problems of a batch are independent and the library "
+            "runs them all on a single MI355X; multi-GPU runs are not supported (use --gpus 1).")
         sys.exit(2)
 
     import torch
