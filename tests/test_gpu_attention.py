@@ -4,7 +4,7 @@ Bar against the float64 oracle on identical float32 inputs: 1e-4 relative
 error for loss and output MSE, and 1e-4 for Y, lse and the gradient row by row
 (worst row-relative error, rows below a tenth of the RMS row norm measured
 against that floor; the whole-array Frobenius error is printed beside it).
-The gradient is held to the Frobenius bar everywhere; at the judged states
+The gradient is held to the Frobenius bar everywhere; at the row-checked states
 (start, perturbed start, t = 5) its rows too, to 1e-4 times
 max(1, amp / 20), amp = ||Y|| / ||Yhat - Y||: the residual that drives
 the gradient is a difference of float32 outputs, so its rounding grows with
@@ -99,11 +99,11 @@ LOSS_CASES = [("single-head-d64", "init"), ("single-head-d64", "perturbed"), ("s
               ("single-head-d64", "t20"), ("qwen-one-layer", "init"), ("qwen-one-layer", "perturbed"),
               ("qwen-one-layer", "t5"), ("qwen-one-layer", "t300"), ("tiny64-ragged", "init"),
               ("tiny128-ragged", "perturbed")]
-# the per-call bar is judged at the start, the perturbed start and after 5
+# the per-call row bar is checked at the start, the perturbed start and after 5
 # iterations; at later iterates (t = 20, 300) the gradient is near a
 # stationary point, a small sum of much larger terms, so its rows are
 # reported and only its Frobenius error is held to the bar
-JUDGED = ("init", "perturbed", "t5")
+ROW_CHECKED = ("init", "perturbed", "t5")
 GOLDEN_STATES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                              "oracle_states_qwen2.5-1.5b-one-layer.npz")
 
@@ -138,7 +138,7 @@ def test_loss_grad_matches_oracle(name, state):
         say(f"   p={p} k={k} L={L:.6g} relL={eL:.2e} relgrad={eg:.2e} rowgrad={rg:.2e} (bar {gtol:.1e}, "
             f"amplification {amp:.0f}) relmse={em:.2e}")
         assert eL <= TOL and eg <= TOL and em <= TOL
-        if state in JUDGED:
+        if state in ROW_CHECKED:
             assert rg <= gtol
         off += k
 
