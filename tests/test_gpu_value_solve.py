@@ -124,12 +124,16 @@ def test_value_solve_flags_nonfinite_keys_and_keeps_vc():
 
 # batches with enough 128x128 Gram tiles for the large-batch kernels: the
 # ragged full-cache heads (d = 128) and twelve d = 64 heads at k = 960 from
-# 1040 training queries each, whose value tiles leave the waves of rows past
-# d idle
+# 1040 (or 1041) training queries each, whose value tiles leave the waves of
+# rows past d idle
 SPLIT_CASES = {
     "full-cache-12-ragged-d128": CASES["full-cache-12-ragged"],
     "small-12-d64-k960": (tiny_workload(d=64, N=1000, m=40, g=1, F=1000, layers=6, kv_heads=2),
                           lambda p, Z: 960, 0.0, None),
+    # n = 1041, not a multiple of 4: the stored score rows carry padding
+    # columns, which the staged weights must mask
+    "small-12-d64-k960-n1041": (tiny_workload(d=64, N=1000, m=40, g=1, F=1001, layers=6, kv_heads=2),
+                                lambda p, Z: 960, 0.0, None),
 }
 
 
