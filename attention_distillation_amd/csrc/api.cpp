@@ -19,12 +19,12 @@ namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
   PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_DIGITS, PROF_RESID, PROF_FSUB,
-  PROF_GRAM_SPLIT, PROF_NCLASS
+  PROF_GRAM_SPLIT, PROF_RESID_SPLIT, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
     "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv",
-    "key_digits", "resid_rhs", "fwd_subst", "gram_split"};
+    "key_digits", "resid_rhs", "fwd_subst", "gram_split", "resid_rhs_split"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -45,6 +45,7 @@ struct kvs_ctx_s {
   bool refine_resolves = true;      // refinement step after the schedule's value re-solves
   bool gram_split3 = true;          // large-batch Gram tiles on bf16 MFMA over exact three-piece splits
   int gram_tile256 = 1;             // those tiles 256x256: 0 never, 1 for >= 2048 of them, 2 always
+  bool resid_split3 = true;         // refinement residual A^T G on split bf16 products
   bool prof = false;
   int prof_mask = 0;
   std::vector<hipEvent_t> pool;
@@ -380,10 +381,12 @@ void run_value_solve(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const floa
   ra.St = g.St; ra.e = g.e; ra.G = at<float>(ws, pl.r_G); ra.info = g.info;
   ra.Rpart = at<double>(ws, pl.r_R); ra.xtot = pl.kpadtot * pl.d;
   ra.P = pl.P; ra.n = pl.n; ra.Cr = pl.Crf; ra.kpadmax = pl.kpadmax;
+  ra.split3 = ctx->resid_split3 ? 1 : 0;
   {
     double ks = 0;
     for (const auto& q : pl.info) ks += q.k;
-    Prof pr(ctx, PROF_RESID, 2.0 * pl.n * pl.d * ks, 4.0 * (ks * pl.npad + (double)pl.P * pl.n * (pl.d + 1)));
+    Prof pr(ctx, ra.split3 ? PROF_RESID_SPLIT : PROF_RESID, 2.0 * pl.n * pl.d * ks,
+            4.0 * (ks * pl.npad + (double)pl.P * pl.n * (pl.d + 1)));
     launch_resid_rhs(ra, pl.d, ctx->stream);
   }
   FsubArgs fa{};
@@ -791,6 +794,8 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
     else if (!strcmp(env, "split128")) c->gram_tile256 = 0;
     else if (!strcmp(env, "split256")) c->gram_tile256 = 2;
   }
+  // the refinement residual A^T G on fp32 products instead of split bf16 ones, for comparisons
+  if (const char* env = getenv("KVS_RESID")) c->resid_split3 = strcmp(env, "fp32") != 0;
   // the context's device is current here: take its scratch address once
   if (hipError_t e = scratch_address(c->device, &c->scratch); e != hipSuccess) {
     c->scratch = nullptr;

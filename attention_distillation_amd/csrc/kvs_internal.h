@@ -310,6 +310,7 @@ struct RhsArgs {
   const ProbInfo* info; double* Rpart;
   long long xtot;   // kpadtot * d
   int P, n, Cr, kpadmax;
+  int split3;       // products of exact three-piece bf16 splits (else fp32)
 };
 struct FsubArgs {
   const double* Rpart; long long xtot; int Cr;

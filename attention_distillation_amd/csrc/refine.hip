@@ -137,6 +137,157 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
       out[(size_t)(kt0 + 16 * wave + 4 * g + r) * D + 16 * db + lq] = acc64[db][r];
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_bf16r(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float __attribute__((ext_vector_type(2)))){x0, x1}, bf16x2));
+}
+// x = h + m + l for two floats (bf16 pieces, round to nearest even, the
+// differences exact in fp32)
+__device__ __forceinline__ void split3_pair_r(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = pk_bf16r(x0, x1);
+  const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+  m = pk_bf16r(r0, r1);
+  l = pk_bf16r(r0 - __uint_as_float(m << 16), r1 - __uint_as_float(m & 0xffff0000u));
+}
+__device__ __forceinline__ f32x4 mfma_rb(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// resid_rhs_kernel with the products of the Gram's large-batch kernels: the
+// weights and G split into three bf16 pieces each, six piece products per
+// multiply-add on 16x16x32 bf16 MFMA, fp32 sums within a 64-query tile and
+// fp64 across tiles as before.  G is split once per tile while it is staged
+// (three planes, [dim][query position], 36 words a row); a 32-query product
+// t takes, in K slot s of lane group g, query 16 (2t + s / 4) + 4 g + s % 4,
+// so the weights a lane already holds (key lq, queries 16 qb + 4 g .. + 3 of
+// each 16-query block qb) form its A operand as they are, and the planes
+// store query 16 qb + 4 g + r at position 32 (qb / 2) + 8 g + 4 (qb % 2) + r,
+// making each lane's eight B values one 16-byte read per plane.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void resid_rhs_split_kernel(RhsArgs a) {
+  const int p = blockIdx.y, kt0 = 64 * blockIdx.x, c = blockIdx.z;
+  const ProbInfo pi = a.info[p];
+  if (kt0 >= pi.kpad) return;
+  const int n = a.n, npad = (n + 3) & ~3;
+  const int nq = ((((n + a.Cr - 1) / a.Cr) + 63) / 64) * 64;
+  const int qbeg = c * nq, qend = min(n, qbeg + nq);
+  constexpr int DB = D / 16;
+  constexpr int QW = 36;
+
+  __shared__ __align__(16) uint32_t Gs3[3][D][QW];   // pieces of G^T, permuted query positions
+  __shared__ __align__(16) float es[64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lq = lane & 15;
+  const size_t prow = (size_t)p * n;
+  const float* Gp = a.G + prow * D;
+
+  double acc64[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc64[db][r] = 0.0;
+
+  constexpr int NL = 64 * (D / 4) / 256;
+  const int kw = kt0 + 16 * __builtin_amdgcn_readfirstlane(wave);
+  const auto rS = buf_rsrc(a.St + pi.soff + (size_t)kw * npad, (long long)max(0, min(16, pi.k - kw)) * npad * 4);
+  const int soff_l = (lq * npad + 4 * g) * 4;
+  const bool kok = kw + lq < pi.k;
+  f32x4 gpre[NL], spre[4];
+  float epre = 0.f;
+  auto prefetch = [&](int qt) {
+    const long long rows = min(64, qend - qt);
+    const auto rG = buf_rsrc(Gp + (size_t)qt * D, rows * D * 4);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      const int rq = 4 * (i / (4 * (D / 4))), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gpre[u][j] = buf_load1(rG, ((rq + j) * D + dq) * 4);
+    }
+    const int so = soff_l + qt * 4;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) spre[qb] = buf_load4(rS, so + 64 * qb);
+    if (tid < 64) epre = buf_load1(buf_rsrc(a.e + prow + qt, rows * 4), tid * 4);
+  };
+  if (qbeg < qend) prefetch(qbeg);
+  for (int qt = qbeg; qt < qend; qt += 64) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int i = tid + 256 * u;
+      // queries 4 m .. 4 m + 3 (m = 4 qb + gg) of dim dq
+      const int m = i / (4 * (D / 4)), dq = 4 * ((i >> 2) % (D / 4)) + (i & 3);
+      const int qb = m >> 2, gg = m & 3;
+      const int wpos = 16 * (qb >> 1) + 4 * gg + 2 * (qb & 1);
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3_pair_r(gpre[u][0], gpre[u][1], h0, m0, l0);
+      split3_pair_r(gpre[u][2], gpre[u][3], h1, m1, l1);
+      *(u32x2*)&Gs3[0][dq][wpos] = u32x2{h0, h1};
+      *(u32x2*)&Gs3[1][dq][wpos] = u32x2{m0, m1};
+      *(u32x2*)&Gs3[2][dq][wpos] = u32x2{l0, l1};
+    }
+    if (tid < 64) es[tid] = epre;
+    f32x4 svv[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) svv[qb] = spre[qb];
+    __syncthreads();
+    if (qt + 64 < qend) prefetch(qt + 64);
+
+    f32x4 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // this lane's weights at queries 16 (2t + h) + 4 g + r, h = 0, 1
+      float w[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int qb = 2 * t + hh;
+        const f32x4 e4 = *(const f32x4*)&es[16 * qb + 4 * g];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = __expf(svv[qb][r] - e4[r]);
+          w[4 * hh + r] = (kok && qt + 16 * qb + 4 * g + r < qend) ? v : 0.f;
+        }
+      }
+      uint32_t ah[4], am[4], al[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) split3_pair_r(w[2 * j], w[2 * j + 1], ah[j], am[j], al[j]);
+      const i32x4 Ah = {(int)ah[0], (int)ah[1], (int)ah[2], (int)ah[3]};
+      const i32x4 Am = {(int)am[0], (int)am[1], (int)am[2], (int)am[3]};
+      const i32x4 Al = {(int)al[0], (int)al[1], (int)al[2], (int)al[3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = 16 * db + lq, wo = 16 * t + 4 * g;
+        const i32x4 Bh = *(const i32x4*)&Gs3[0][row][wo];
+        const i32x4 Bm = *(const i32x4*)&Gs3[1][row][wo];
+        const i32x4 Bl = *(const i32x4*)&Gs3[2][row][wo];
+        f32x4 cc = acc[db];
+        cc = mfma_rb(Am, Bm, cc);
+        cc = mfma_rb(Al, Bh, cc);
+        cc = mfma_rb(Ah, Bl, cc);
+        cc = mfma_rb(Am, Bh, cc);
+        cc = mfma_rb(Ah, Bm, cc);
+        cc = mfma_rb(Ah, Bh, cc);
+        acc[db] = cc;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc64[db][r] += (double)acc[db][r];
+  }
+
+  double* out = a.Rpart + (size_t)c * a.xtot + pi.xoff;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      out[(size_t)(kt0 + 16 * wave + 4 * g + r) * D + 16 * db + lq] = acc64[db][r];
+}
+
 // r = -1/2 sum_c Rpart[c] - mu Vc (rows < k; 0 below), then L Z = r for 16
 // value columns per workgroup.  Top down, right-looking:
 // Z_i = inv(L_ii) W_i, then W_r -= L_ri Z_i for every r > i.  W is held in
@@ -300,6 +451,11 @@ int refine_splits(int P, int kpadmax, int n) {
 
 void launch_resid_rhs(const RhsArgs& a, int d, hipStream_t s) {
   dim3 grid(a.kpadmax / 64, a.P, a.Cr);
+  if (a.split3) {
+    if (d == 128) hipLaunchKernelGGL((resid_rhs_split_kernel<128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((resid_rhs_split_kernel<64>), grid, dim3(256), 0, s, a);
+    return;
+  }
   if (d == 128) hipLaunchKernelGGL((resid_rhs_kernel<128>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((resid_rhs_kernel<64>), grid, dim3(256), 0, s, a);
 }

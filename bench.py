@@ -118,6 +118,9 @@ MEASURED_TRAFFIC = {
     # loss-mode forward (integer scores): FETCH 3393086.5 KiB x 1.99980 + WRITE 18157940.8 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
         {"bytes": 25542077627, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
+    # backward: FETCH 11502934.7 KiB x 1.99980 + WRITE 521123.1 KiB x 1.00000 per dispatch
+    ("attn_bwd", "qwen2.5-7b-long-context"):
+        {"bytes": 24089284519, "source": "attn_bwd.hip", "sha": "e5236c87a419db06"},
     # Gram, 256x256 tiles on split bf16 products: FETCH 141733727.5 KiB x 1.99980 + WRITE 2765207.7 KiB x 1.00000 per dispatch
     ("gram_split", "qwen2.5-7b-long-context"):
         {"bytes": 293073219537, "source": "gram.hip", "sha": "8175c6117de39252"},
@@ -756,12 +759,13 @@ def bench_vector(args, torch, K):
 
 # kernels whose launches are timed with HIP events during the timed blocks
 TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "potrf_panel", "back_subst",
-                 "merge", "hist_dots", "direction", "key_digits", "resid_rhs", "fwd_subst"]
+                 "merge", "hist_dots", "direction", "key_digits", "resid_rhs", "resid_rhs_split",
+                 "fwd_subst"]
 # contraction kernels (MFMA roofline) and their peaks: the loss forward forms
 # its scores on the score arithmetic's unit (half its flops) and A Vc on fp32
-# MFMA (the other half); the split-product Gram runs on bf16 MFMA, six
-# products per multiply-add; the others are fp32 MFMA only
-CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "resid_rhs")
+# MFMA (the other half); the split-product Gram and refinement residual run
+# on bf16 MFMA, six products per multiply-add; the others are fp32 MFMA only
+CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "resid_rhs", "resid_rhs_split")
 
 
 def gram_kernel_of(stats):
@@ -773,7 +777,7 @@ def gram_kernel_of(stats):
 def contraction_peak(name):
     """(peak flop rate, description) of a contraction kernel other than the
     loss forward."""
-    if name == "gram_split":
+    if name in ("gram_split", "resid_rhs_split"):
         return PEAK_GRAM_SPLIT, (f"bf16 MFMA over {GRAM_SPLIT_PRODUCTS} products per multiply-add "
                                  f"(exact three-piece bf16 splits of both operands)")
     return PEAK_FP32_MFMA, "fp32 MFMA"
@@ -801,7 +805,7 @@ def kernel_rows(stats):
                 # the algorithmic rate against the fp32 MFMA peak
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
             else:
-                if name == "gram_split":
+                if name in ("gram_split", "resid_rhs_split"):
                     row["frac_split_bf16_mfma"] = round(fl / sec / PEAK_GRAM_SPLIT, 4)
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
         rows[name] = row
@@ -809,10 +813,15 @@ def kernel_rows(stats):
 
 
 def contractions_note(stats):
+    parts = []
     if gram_kernel_of(stats) == "gram_split":
-        return (f"fp32 MFMA; the Gram's 128x128 tiles on bf16 MFMA over exact three-piece bf16 splits "
-                f"({GRAM_SPLIT_PRODUCTS} products per multiply-add, fp32 accumulation)")
-    return "fp32 MFMA"
+        parts.append("the Gram's large tiles")
+    if stats.get("resid_rhs_split", {}).get("launches", 0):
+        parts.append("the refinement residual A^T G")
+    if not parts:
+        return "fp32 MFMA"
+    return (f"fp32 MFMA; {' and '.join(parts)} on bf16 MFMA over exact three-piece bf16 splits "
+            f"({GRAM_SPLIT_PRODUCTS} products per multiply-add, fp32 accumulation)")
 
 
 def cpu_baseline_block(w, b):

@@ -154,7 +154,9 @@ kvs_status kvs_loss_grad(kvs_ctx ctx, const kvs_batch* b, const float* Q, const 
  * m = bf16(x - h), l = bf16(x - h - m); the terms of weight <= 2), within
  * about 2^-22 of the product, with fp32 accumulation; KVS_GRAM=fp32, read
  * when the context is created, selects fp32 products instead (split128 /
- * split256 force a tile shape). */
+ * split256 force a tile shape).  The refinement residual A^T G takes the
+ * same split products (fp32 sums within 64-query tiles, fp64 across them);
+ * KVS_RESID=fp32 selects fp32 products. */
 kvs_status kvs_value_solve(kvs_ctx ctx, const kvs_batch* b, const float* Q, const float* Y,
                            const float* lse, const float* Kc, float* Vc, int32_t* flags,
                            void* ws, size_t ws_bytes);
@@ -390,7 +392,8 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
  * fwd_subst (bits 15, 16: the refinement step of a value solve) and
  * gram_split (bit 17: the Gram's launches whose 128x128 or 256x256 tiles
  * take the products of exact three-piece bf16 splits; "gram" counts the
- * fp32 ones).
+ * fp32 ones) and resid_rhs_split (bit 18: the refinement residual on those
+ * products; "resid_rhs" counts the fp32 one).
  * kvs_profile_read
  * synchronises the stream and writes up to max entries (kernels with
  * launches) to out. */

@@ -140,10 +140,12 @@ SPLIT_CASES = {
 @pytest.mark.parametrize("name", list(SPLIT_CASES))
 def test_split_gram_and_fp32_gram_both_match_oracle(name):
     """The large-batch Gram takes split bf16 products (on 128x128 or 256x256
-    tiles) by default and fp32 ones under KVS_GRAM=fp32 (read when a context
-    is created).  Every variant meets the bar; the two split tile shapes sum
-    the same products in the same order, so their solves agree bit for bit;
-    the profile shows which product kind ran."""
+    tiles) by default and fp32 ones under KVS_GRAM=fp32; the refinement
+    residual A^T G takes split products by default and fp32 ones under
+    KVS_RESID=fp32 (both read when a context is created).  Every variant
+    meets the bar; the two split tile shapes sum the same products in the
+    same order, so their solves agree bit for bit; the profile shows which
+    product kind ran."""
     import os
     w, kfun, _, sel = SPLIT_CASES[name]
     b, probs = _setup(w, kfun, 0.0, problems=sel)
@@ -153,26 +155,30 @@ def test_split_gram_and_fp32_gram_both_match_oracle(name):
     bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
     Qg, Yg = to_gpu(b["Q"]), to_gpu(np.stack([p[1] for p in probs]))
     lg, Kg = to_gpu(np.stack([p[2] for p in probs])), to_gpu(np.concatenate([p[3] for p in probs]))
+    modes = {"split128": {"KVS_GRAM": "split128"}, "split256": {"KVS_GRAM": "split256"},
+             "fp32": {"KVS_GRAM": "fp32", "KVS_RESID": "fp32"}}
+    kinds = ["gram", "gram_split", "resid_rhs", "resid_rhs_split"]
     out = {}
-    for mode in ("split128", "split256", "fp32"):
-        old = os.environ.pop("KVS_GRAM", None)
-        os.environ["KVS_GRAM"] = mode
+    for mode, env in modes.items():
+        old = {v: os.environ.pop(v, None) for v in ("KVS_GRAM", "KVS_RESID")}
+        os.environ.update(env)
         try:
             ctx = K.Context()
         finally:
-            os.environ.pop("KVS_GRAM", None)
-            if old is not None:
-                os.environ["KVS_GRAM"] = old
+            for v, x in old.items():
+                os.environ.pop(v, None)
+                if x is not None:
+                    os.environ[v] = x
         ws = workspace(K.workspace_bytes(bt))
         Vc = empty((sum(ks), d))
         flags = to_gpu(np.zeros(P, np.int32))
-        K.kvs_profile_enable(ctx, True, kernels=["gram", "gram_split"])
+        K.kvs_profile_enable(ctx, True, kernels=kinds)
         K.kvs_value_solve(ctx, bt, Qg, Yg, lg, Kg, Vc, flags, ws)
         st = K.kvs_profile_read(ctx)
         K.kvs_profile_enable(ctx, False)
         ran = {k2: v["launches"] for k2, v in st.items()}
-        say(f"[split-gram] case={name} P={P} d={d} k={ks[0]}.. mode={mode} gram launches {ran}")
-        assert ran == ({"gram": 1} if mode == "fp32" else {"gram_split": 1})
+        say(f"[split-gram] case={name} P={P} d={d} k={ks[0]}.. mode={mode} launches {ran}")
+        assert ran == ({"gram": 1, "resid_rhs": 1} if mode == "fp32" else {"gram_split": 1, "resid_rhs_split": 1})
         out[mode] = (host(Vc), host(flags))
     assert out["split128"][0].tobytes() == out["split256"][0].tobytes()
     off, worst = 0, {m: 0.0 for m in out}
