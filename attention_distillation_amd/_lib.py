@@ -400,7 +400,7 @@ def kvs_value_norms(ctx, P, Z, d, Vz, signal, ws):
 PROFILE_CLASSES = ("attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst",
                    "hist_dots", "direction", "importance", "ref_attn_fwd", "merge",
                    "build_queries", "use_attn_fwd", "attn_pv", "key_digits", "resid_rhs", "fwd_subst",
-                   "gram_split", "resid_rhs_split")
+                   "gram_split", "resid_rhs_split", "attn_bwd_split")
 
 
 def value_norms_noalloc_max_bytes():

@@ -19,12 +19,12 @@ namespace kvs {
 enum ProfClass {
   PROF_FWD, PROF_BWD, PROF_GRAM, PROF_POTRF, PROF_TRAIL, PROF_BACK, PROF_HIST, PROF_DIR,
   PROF_IMP, PROF_REF, PROF_MERGE, PROF_QUERIES, PROF_USE, PROF_PV, PROF_DIGITS, PROF_RESID, PROF_FSUB,
-  PROF_GRAM_SPLIT, PROF_RESID_SPLIT, PROF_NCLASS
+  PROF_GRAM_SPLIT, PROF_RESID_SPLIT, PROF_BWD_SPLIT, PROF_NCLASS
 };
 const char* const kProfNames[PROF_NCLASS] = {
     "attn_fwd", "attn_bwd", "gram", "potrf_panel", "trailing", "back_subst", "hist_dots",
     "direction", "importance", "ref_attn_fwd", "merge", "build_queries", "use_attn_fwd", "attn_pv",
-    "key_digits", "resid_rhs", "fwd_subst", "gram_split", "resid_rhs_split"};
+    "key_digits", "resid_rhs", "fwd_subst", "gram_split", "resid_rhs_split", "attn_bwd_split"};
 struct ProfRec {
   int cls;
   hipEvent_t a, b;
@@ -46,6 +46,7 @@ struct kvs_ctx_s {
   bool gram_split3 = true;          // large-batch Gram tiles on bf16 MFMA over exact three-piece splits
   int gram_tile256 = 1;             // those tiles 256x256: 0 never, 1 for >= 2048 of them, 2 always
   bool resid_split3 = true;         // refinement residual A^T G on split bf16 products
+  bool bwd_split3 = true;           // backward on split bf16 products
   bool prof = false;
   int prof_mask = 0;
   std::vector<hipEvent_t> pool;
@@ -303,9 +304,10 @@ void run_backward(kvs_ctx ctx, const Plan& pl, const kvs_batch* b, const float* 
   bw.crow = at<float>(ws, pl.r_crow); bw.K = nullptr; bw.V = V; bw.st = st; bw.active_mask = mask;
   bw.dKpart = at<float>(ws, pl.r_dK); bw.info = at<ProbInfo>(ws, pl.r_info);
   bw.P = pl.P; bw.n = pl.n; bw.Cn = pl.Cn; bw.kmax = pl.kmax; bw.ktot = (int)pl.ktot;
+  bw.split3 = ctx->bwd_split3 ? 1 : 0;
   {
     const double ks = sum_k(pl, hs, want);
-    Prof pr(ctx, PROF_BWD, 4.0 * pl.n * pl.d * ks, 4.0 * (ks * pl.npad + ks * pl.d * (1.0 + pl.Cn)));
+    Prof pr(ctx, bw.split3 ? PROF_BWD_SPLIT : PROF_BWD, 4.0 * pl.n * pl.d * ks, 4.0 * (ks * pl.npad + ks * pl.d * (1.0 + pl.Cn)));
     launch_attn_bwd(bw, pl.d, ctx->stream);
   }
 }
@@ -796,6 +798,8 @@ kvs_status kvs_create(kvs_ctx* out, void* hip_stream) {
   }
   // the refinement residual A^T G on fp32 products instead of split bf16 ones, for comparisons
   if (const char* env = getenv("KVS_RESID")) c->resid_split3 = strcmp(env, "fp32") != 0;
+  // the backward on fp32 products instead of split bf16 ones, for comparisons
+  if (const char* env = getenv("KVS_BWD")) c->bwd_split3 = strcmp(env, "fp32") != 0;
   // the context's device is current here: take its scratch address once
   if (hipError_t e = scratch_address(c->device, &c->scratch); e != hipSuccess) {
     c->scratch = nullptr;

@@ -189,6 +189,7 @@ struct BwdArgs {
   float* dKpart;           // [Cn][sum k][d]
   const ProbInfo* info;
   int P, n, Cn, kmax, ktot;
+  int split3;              // products of exact three-piece bf16 splits (else fp32)
 };
 void launch_attn_bwd(const BwdArgs& a, int d, hipStream_t s);
 

@@ -118,9 +118,6 @@ MEASURED_TRAFFIC = {
     # loss-mode forward (integer scores): FETCH 3393086.5 KiB x 1.99980 + WRITE 18157940.8 KiB x 1.00000 per dispatch
     ("attn_fwd", "qwen2.5-7b-long-context"):
         {"bytes": 25542077627, "source": "attn_fwd.hip", "sha": "d786fa10287fbda0"},
-    # backward: FETCH 11502934.7 KiB x 1.99980 + WRITE 521123.1 KiB x 1.00000 per dispatch
-    ("attn_bwd", "qwen2.5-7b-long-context"):
-        {"bytes": 24089284519, "source": "attn_bwd.hip", "sha": "e5236c87a419db06"},
     # Gram, 256x256 tiles on split bf16 products: FETCH 141733727.5 KiB x 1.99980 + WRITE 2765207.7 KiB x 1.00000 per dispatch
     ("gram_split", "qwen2.5-7b-long-context"):
         {"bytes": 293073219537, "source": "gram.hip", "sha": "8175c6117de39252"},
@@ -758,14 +755,18 @@ def bench_vector(args, torch, K):
 
 
 # kernels whose launches are timed with HIP events during the timed blocks
-TIMED_KERNELS = ["attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "potrf_panel", "back_subst",
+TIMED_KERNELS = ["attn_fwd", "attn_bwd", "attn_bwd_split", "gram", "gram_split", "attn_pv", "potrf_panel",
+                 "back_subst",
                  "merge", "hist_dots", "direction", "key_digits", "resid_rhs", "resid_rhs_split",
                  "fwd_subst"]
 # contraction kernels (MFMA roofline) and their peaks: the loss forward forms
 # its scores on the score arithmetic's unit (half its flops) and A Vc on fp32
-# MFMA (the other half); the split-product Gram and refinement residual run
-# on bf16 MFMA, six products per multiply-add; the others are fp32 MFMA only
-CONTRACTIONS = ("attn_fwd", "attn_bwd", "gram", "gram_split", "attn_pv", "resid_rhs", "resid_rhs_split")
+# MFMA (the other half); the split-product Gram, refinement residual and
+# backward run on bf16 MFMA, six products per multiply-add; the others are
+# fp32 MFMA only
+CONTRACTIONS = ("attn_fwd", "attn_bwd", "attn_bwd_split", "gram", "gram_split", "attn_pv", "resid_rhs",
+                "resid_rhs_split")
+SPLIT_KERNELS = ("gram_split", "resid_rhs_split", "attn_bwd_split")
 
 
 def gram_kernel_of(stats):
@@ -777,7 +778,7 @@ def gram_kernel_of(stats):
 def contraction_peak(name):
     """(peak flop rate, description) of a contraction kernel other than the
     loss forward."""
-    if name in ("gram_split", "resid_rhs_split"):
+    if name in SPLIT_KERNELS:
         return PEAK_GRAM_SPLIT, (f"bf16 MFMA over {GRAM_SPLIT_PRODUCTS} products per multiply-add "
                                  f"(exact three-piece bf16 splits of both operands)")
     return PEAK_FP32_MFMA, "fp32 MFMA"
@@ -805,7 +806,7 @@ def kernel_rows(stats):
                 # the algorithmic rate against the fp32 MFMA peak
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
             else:
-                if name in ("gram_split", "resid_rhs_split"):
+                if name in SPLIT_KERNELS:
                     row["frac_split_bf16_mfma"] = round(fl / sec / PEAK_GRAM_SPLIT, 4)
                 row["frac_fp32_mfma"] = round(fl / sec / PEAK_FP32_MFMA, 4)
         rows[name] = row
@@ -818,6 +819,8 @@ def contractions_note(stats):
         parts.append("the Gram's large tiles")
     if stats.get("resid_rhs_split", {}).get("launches", 0):
         parts.append("the refinement residual A^T G")
+    if stats.get("attn_bwd_split", {}).get("launches", 0):
+        parts.append("the backward (G Vc^T, dS^T Q)")
     if not parts:
         return "fp32 MFMA"
     return (f"fp32 MFMA; {' and '.join(parts)} on bf16 MFMA over exact three-piece bf16 splits "

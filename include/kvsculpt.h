@@ -392,8 +392,9 @@ kvs_status kvs_use_eval(kvs_ctx ctx, const kvs_batch* b, int32_t m, const float*
  * fwd_subst (bits 15, 16: the refinement step of a value solve) and
  * gram_split (bit 17: the Gram's launches whose 128x128 or 256x256 tiles
  * take the products of exact three-piece bf16 splits; "gram" counts the
- * fp32 ones) and resid_rhs_split (bit 18: the refinement residual on those
- * products; "resid_rhs" counts the fp32 one).
+ * fp32 ones), resid_rhs_split (bit 18: the refinement residual on those
+ * products; "resid_rhs" counts the fp32 one) and attn_bwd_split (bit 19:
+ * the backward on those products; "attn_bwd" counts the fp32 one).
  * kvs_profile_read
  * synchronises the stream and writes up to max entries (kernels with
  * launches) to out. */

@@ -226,3 +226,57 @@ def test_loss_grad_edge_rows(name, mode, monkeypatch):
         assert np.isfinite(lg[p]) and np.all(np.isfinite(gg[off:off + k]))
         assert eL <= TOL and eg <= TOL and em <= TOL and rg <= gtol
         off += k
+
+
+@pytest.mark.parametrize("name", ["qwen-one-layer", "tiny128-ragged"])
+def test_split_and_fp32_backward_both_match_oracle(name):
+    """The backward takes split bf16 products (G Vc^T and dS^T Q as six
+    piece products of exact three-piece splits) by default and fp32 ones
+    under KVS_BWD=fp32 (read when a context is created): both gradients meet
+    the per-call bar row by row at the start, and the profile shows which
+    kernel ran."""
+    import os
+    state = "init" if name == "qwen-one-layer" else "perturbed"
+    w, b, probs = _loss_case(name, state)
+    P, n, d = b["Q"].shape
+    Z = b["Kz"].shape[1]
+    ks = [pr[3].shape[0] for pr in probs]
+    bt = K.Batch(P, d, Z, n, k=ks, scale=b["scale"])
+    Kc = to_gpu(np.concatenate([pr[3] for pr in probs]))
+    Vc = to_gpu(np.concatenate([pr[4] for pr in probs]))
+    Yt = to_gpu(np.stack([pr[1] for pr in probs]))
+    lt = to_gpu(np.stack([pr[2] for pr in probs]))
+    Qg = to_gpu(b["Q"])
+    grads = {}
+    for mode in ("split", "fp32"):
+        old = os.environ.pop("KVS_BWD", None)
+        if mode == "fp32":
+            os.environ["KVS_BWD"] = "fp32"
+        try:
+            ctx = K.Context()
+        finally:
+            os.environ.pop("KVS_BWD", None)
+            if old is not None:
+                os.environ["KVS_BWD"] = old
+        ws = workspace(K.workspace_bytes(bt))
+        loss, mse = empty((P,)), empty((P,))
+        grad = empty((sum(ks), d))
+        K.kvs_profile_enable(ctx, True, kernels=["attn_bwd", "attn_bwd_split"])
+        K.kvs_loss_grad(ctx, bt, Qg, Yt, lt, Kc, Vc, loss, grad, mse, ws)
+        st = K.kvs_profile_read(ctx)
+        K.kvs_profile_enable(ctx, False)
+        ran = {k2: v["launches"] for k2, v in st.items()}
+        say(f"[backward kinds] case={name} mode={mode} launches {ran}")
+        assert ran == ({"attn_bwd_split": 1} if mode == "split" else {"attn_bwd": 1})
+        grads[mode] = host(grad)
+    off = 0
+    for p, (Q, Y32, l32, Kc32, Vc32) in enumerate(probs):
+        L, g, aux = O.loss_grad(Q, Y32, l32, Kc32, Vc32, b["scale"])
+        k = Kc32.shape[0]
+        amp = float(np.linalg.norm(Y32) / max(np.linalg.norm(aux["R"]), 1e-300))
+        gtol = TOL * max(1.0, amp / 20.0)
+        for mode, gg in grads.items():
+            rg, eg = row_err(gg[off:off + k], g), rel(gg[off:off + k], g)
+            say(f"   p={p} k={k} mode={mode} relgrad={eg:.2e} rowgrad={rg:.2e} (bar {gtol:.1e})")
+            assert eg <= TOL and rg <= gtol
+        off += k
