@@ -558,7 +558,7 @@ void prof_add_slot_work(kvs_ctx ctx, const Plan& pl, const LbState* st, const Lb
     bw += (double)(h[p].n_accept - (before ? before[p].n_accept : 0)) * pl.info[p].k;
   }
   ctx->acc[PROF_FWD].flops += 4.0 * pl.n * pl.d * fw;
-  ctx->acc[PROF_BWD].flops += 4.0 * pl.n * pl.d * bw;
+  ctx->acc[ctx->bwd_split3 ? PROF_BWD_SPLIT : PROF_BWD].flops += 4.0 * pl.n * pl.d * bw;
 }
 
 // Two pinned status buffers of P entries and their events.
